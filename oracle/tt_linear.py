@@ -1,0 +1,148 @@
+"""fp64 oracle for the TT-linear layer with rank-control diagonals.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Notation (CoMERA project page, "Learn the ranks while training"; NeurIPS 2024
+poster page, figure caption on the TT / TTM network structures):
+
+* ``cores[k]`` is G_{k+1} with shape (r_k, n_{k+1}, r_{k+1}); r_0 = r_d = 1.
+* ``D[k]`` is the diagonal on the link between ``cores[k]`` and ``cores[k+1]``
+  (length r_{k+1}); there are d-1 of them, none at the chain ends.
+* The full chain tensor T[j_1, ..., j_d] = G_1[0, j_1, :] D_1 G_2[:, j_2, :]
+  ... D_{d-1} G_d[:, j_d, 0], flattened row-major (first mode most
+  significant).
+* A weight W (N_out x N_in) is that tensor reshaped: with the output modes
+  first in the chain, W = T.reshape(N_out, N_in); with the input modes first,
+  W = T.reshape(N_in, N_out)^T.  Y = x W^T (no bias).
+
+Readings where the pages are silent (each is listed in the design doc): the order
+of the modes in the chain is a parameter (``in_first``); index linearisation
+is row-major mixed radix; D is a real-valued scale, not only a 0/1 mask.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _check_chain(cores, D):
+    d = len(cores)
+    if d < 1:
+        raise ValueError("a chain needs at least one core")
+    if len(D) != d - 1:
+        raise ValueError("a chain of d cores has d-1 link diagonals")
+    if _f64(cores[0]).shape[0] != 1 or _f64(cores[-1]).shape[2] != 1:
+        raise ValueError("boundary ranks must be 1")
+    for k in range(d - 1):
+        rk = _f64(cores[k]).shape[2]
+        if _f64(cores[k + 1]).shape[0] != rk or _f64(D[k]).shape != (rk,):
+            raise ValueError(f"rank mismatch on link {k + 1}")
+
+
+def chain_prefix(cores, D, k: int) -> np.ndarray:
+    """Product of the cores left of core ``k`` with their links' diagonals.
+
+    Returns P of shape (prod(n_1..n_k), r_k): P = G_1 D_1 G_2 ... G_k D_k with
+    the mode indices flattened row-major, i.e. the part of the chain product
+    (project page, "Learn the ranks while training") to the left of G_{k+1}.
+    For k = 0 it is the 1x1 identity.
+    """
+    M = np.ones((1, 1))
+    for j in range(k):
+        G = _f64(cores[j])
+        r0, n, r1 = G.shape
+        M = (M @ G.reshape(r0, n * r1)).reshape(-1, r1)
+        M = M * _f64(D[j])[None, :]
+    return M
+
+
+def chain_suffix(cores, D, k: int) -> np.ndarray:
+    """Product of the cores right of core ``k`` with their links' diagonals.
+
+    Returns S of shape (r_{k+1}, prod(n_{k+2}..n_d)): S = D_{k+1} G_{k+2} ...
+    D_{d-1} G_d, mode indices flattened row-major.  For the last core it is
+    the 1x1 identity.
+    """
+    d = len(cores)
+    M = np.ones((1, 1))
+    for j in range(d - 1, k, -1):
+        G = _f64(cores[j])
+        r0, n, r1 = G.shape
+        M = (G.reshape(r0 * n, r1) @ M).reshape(r0, -1)
+        M = _f64(D[j - 1])[:, None] * M
+    return M
+
+
+def chain_tensor(cores, D) -> np.ndarray:
+    """The full chain tensor, flattened row-major (length prod(n_k)).
+
+    Definition of the TT format with a rank-control diagonal on every link
+    (project page, "Learn the ranks while training", figure of the tensor-train
+    layer with rank-control diagonals).
+    """
+    _check_chain(cores, D)
+    d = len(cores)
+    M = chain_prefix(cores, D, d - 1)          # (prod n_<d, r_{d-1})
+    G = _f64(cores[d - 1])
+    r0, n, _ = G.shape
+    return (M @ G.reshape(r0, n)).reshape(-1)
+
+
+def dense_weight(out_modes, in_modes, cores, D, in_first: bool = False) -> np.ndarray:
+    """Dense W (N_out x N_in) reconstructed from the cores in fp64."""
+    n_out = int(np.prod(out_modes))
+    n_in = int(np.prod(in_modes))
+    modes = list(in_modes) + list(out_modes) if in_first else list(out_modes) + list(in_modes)
+    got = [int(_f64(c).shape[1]) for c in cores]
+    if got != modes:
+        raise ValueError(f"core modes {got} do not match the chain {modes}")
+    T = chain_tensor(cores, D)
+    if in_first:
+        return T.reshape(n_in, n_out).T.copy()
+    return T.reshape(n_out, n_in)
+
+
+def chain_core_grads(dT, cores, D) -> list:
+    """Gradient of <dT, T(G, D)> with respect to every core (D held fixed).
+
+    T is linear in each core: T = P_k . G_k . S_k with P_k the prefix and S_k
+    the suffix of core k, so
+        dG_k[a, m, b] = sum_{alpha, beta} P_k[alpha, a] dT[alpha, m, beta] S_k[b, beta]
+    where dT is viewed as (prod n_<k, n_k, prod n_>k).
+    """
+    _check_chain(cores, D)
+    dT = _f64(dT).reshape(-1)
+    d = len(cores)
+    grads = []
+    for k in range(d):
+        G = _f64(cores[k])
+        P = chain_prefix(cores, D, k)
+        S = chain_suffix(cores, D, k)
+        dTk = dT.reshape(P.shape[0], G.shape[1], S.shape[1])
+        grads.append(np.einsum("xa,xmy,by->amb", P, dTk, S))
+    return grads
+
+
+def tt_linear_forward(x, out_modes, in_modes, cores, D, in_first: bool = False) -> np.ndarray:
+    """Y = x W^T for a batch of tokens x (T x N_in)."""
+    W = dense_weight(out_modes, in_modes, cores, D, in_first)
+    return _f64(x) @ W.T
+
+
+def tt_linear_backward(x, dy, out_modes, in_modes, cores, D, in_first: bool = False):
+    """Input gradient and core gradients of the TT-linear layer.
+
+    dX = dY W, dW = dY^T x, and dG_k = d<dW, W>/dG_k, i.e. the gradient of
+    <dY, x W^T> with respect to each core with D fixed.  Returns (dX, [dG_k]).
+    """
+    W = dense_weight(out_modes, in_modes, cores, D, in_first)
+    x = _f64(x)
+    dy = _f64(dy)
+    dX = dy @ W
+    dW = dy.T @ x
+    dT = dW.T if in_first else dW           # back to the chain's own layout
+    return dX, chain_core_grads(dT.reshape(-1), cores, D)

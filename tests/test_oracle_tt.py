@@ -1,0 +1,254 @@
+"""Pins for the fp64 TT-linear oracle, each independent of the oracle's own code.
+
+* brute-force index sums over every rank index (the TT definition written as
+  explicit nested sums);
+* closed forms: all ranks 1 gives a Kronecker product; two cores give the
+  textbook low-rank product G_1 diag(D) G_2;
+* TT-SVD (Oseledets 2011) of a random dense W at full ranks rebuilds W;
+* the loss <dY, x W^T> is linear in each core, so probing it with unit
+  tensors gives every gradient entry exactly;
+* a zero D entry is the same as deleting the matching slices of both
+  neighbouring cores (project page, "Learn the ranks while training");
+* a hand-worked two-core example under tests/golden/.
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_chain(rng, modes, ranks, zero_frac=0.0):
+    cores = [rng.standard_normal((ranks[k], modes[k], ranks[k + 1])) for k in range(len(modes))]
+    D = []
+    for k in range(1, len(modes)):
+        v = rng.uniform(0.5, 1.5, ranks[k])
+        nz = int(np.floor(zero_frac * ranks[k]))
+        v[rng.permutation(ranks[k])[:nz]] = 0.0
+        D.append(v)
+    return cores, D
+
+
+def _digits(idx, modes):
+    out = []
+    for n in reversed(modes):
+        out.append(idx % n)
+        idx //= n
+    return out[::-1]
+
+
+def _brute_entry(cores, D, js):
+    """Sum over every tuple of rank indices of the product of core entries and D."""
+    d = len(cores)
+    ranks = [c.shape[0] for c in cores] + [1]
+    total = 0.0
+    for a in itertools.product(*[range(r) for r in ranks[1:d]]):
+        a = (0,) + a + (0,)
+        term = 1.0
+        for k in range(d):
+            term *= cores[k][a[k], js[k], a[k + 1]]
+            if k < d - 1:
+                term *= D[k][a[k + 1]]
+        total += term
+    return total
+
+
+def _brute_W(out_modes, in_modes, cores, D, in_first=False):
+    n_out, n_in = int(np.prod(out_modes)), int(np.prod(in_modes))
+    W = np.zeros((n_out, n_in))
+    for i in range(n_out):
+        for j in range(n_in):
+            di, dj = _digits(i, out_modes), _digits(j, in_modes)
+            js = dj + di if in_first else di + dj
+            W[i, j] = _brute_entry(cores, D, js)
+    return W
+
+
+@pytest.mark.parametrize("in_first", [False, True])
+def test_W_matches_brute_force(in_first):
+    rng = np.random.default_rng(1)
+    out_modes, in_modes = (2, 3), (3, 2)
+    ranks = [1, 2, 3, 2, 1]
+    modes = list(in_modes) + list(out_modes) if in_first else list(out_modes) + list(in_modes)
+    cores, D = _rand_chain(rng, modes, ranks, zero_frac=0.34)
+    W = oracle.dense_weight(out_modes, in_modes, cores, D, in_first)
+    Wb = _brute_W(out_modes, in_modes, cores, D, in_first)
+    assert np.max(np.abs(W - Wb)) <= 1e-13 * max(1.0, np.max(np.abs(Wb)))
+
+
+def test_W_matches_brute_force_six_cores():
+    rng = np.random.default_rng(2)
+    out_modes, in_modes = (2, 3, 2), (3, 2, 2)
+    ranks = [1, 2, 3, 4, 3, 2, 1]
+    cores, D = _rand_chain(rng, list(out_modes) + list(in_modes), ranks, zero_frac=0.3)
+    W = oracle.dense_weight(out_modes, in_modes, cores, D)
+    Wb = _brute_W(out_modes, in_modes, cores, D)
+    assert np.max(np.abs(W - Wb)) <= 1e-13 * max(1.0, np.max(np.abs(Wb)))
+
+
+@pytest.mark.parametrize("in_first", [False, True])
+def test_rank_one_is_kronecker(in_first):
+    rng = np.random.default_rng(3)
+    out_modes, in_modes = (3, 4, 2), (2, 5)
+    modes = list(in_modes) + list(out_modes) if in_first else list(out_modes) + list(in_modes)
+    vecs = [rng.standard_normal(n) for n in modes]
+    cores = [v.reshape(1, -1, 1) for v in vecs]
+    D = [np.array([s]) for s in rng.uniform(0.5, 1.5, len(modes) - 1)]
+    scale = np.prod([v[0] for v in D])
+    if in_first:
+        kin = np.kron(vecs[0], vecs[1])
+        kout = np.kron(np.kron(vecs[2], vecs[3]), vecs[4])
+    else:
+        kout = np.kron(np.kron(vecs[0], vecs[1]), vecs[2])
+        kin = np.kron(vecs[3], vecs[4])
+    want = np.outer(kout, kin) * scale
+    W = oracle.dense_weight(out_modes, in_modes, cores, D, in_first)
+    np.testing.assert_allclose(W, want, rtol=1e-14, atol=1e-14)
+
+
+def test_two_cores_is_low_rank_product():
+    rng = np.random.default_rng(4)
+    n1, n2, r = 7, 5, 4
+    G1 = rng.standard_normal((1, n1, r))
+    G2 = rng.standard_normal((r, n2, 1))
+    Dv = rng.uniform(0.5, 1.5, r)
+    Dv[1] = 0.0
+    want = G1[0] @ np.diag(Dv) @ G2[:, :, 0]
+    W = oracle.dense_weight((n1,), (n2,), [G1, G2], [Dv])
+    np.testing.assert_allclose(W, want, rtol=1e-14, atol=1e-14)
+
+
+def test_tt_svd_full_rank_round_trip():
+    rng = np.random.default_rng(5)
+    out_modes, in_modes = (3, 4), (2, 5)
+    W = rng.standard_normal((12, 10))
+    cores = oracle.tt_svd(W, list(out_modes) + list(in_modes))
+    D = [np.ones(c.shape[2]) for c in cores[:-1]]
+    W2 = oracle.dense_weight(out_modes, in_modes, cores, D)
+    assert np.max(np.abs(W2 - W)) <= 1e-12
+
+
+def test_forward_and_input_grad_against_loops():
+    rng = np.random.default_rng(6)
+    out_modes, in_modes = (2, 3), (3, 2)
+    cores, D = _rand_chain(rng, [2, 3, 3, 2], [1, 3, 2, 3, 1], zero_frac=0.34)
+    Wb = _brute_W(out_modes, in_modes, cores, D)
+    x = rng.standard_normal((5, 6))
+    dy = rng.standard_normal((5, 6))
+    Y = oracle.tt_linear_forward(x, out_modes, in_modes, cores, D)
+    dX, _ = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D)
+    Yb = np.zeros((5, 6))
+    dXb = np.zeros((5, 6))
+    for t in range(5):
+        for i in range(6):
+            for j in range(6):
+                Yb[t, i] += x[t, j] * Wb[i, j]
+                dXb[t, j] += dy[t, i] * Wb[i, j]
+    np.testing.assert_allclose(Y, Yb, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dX, dXb, rtol=1e-13, atol=1e-13)
+    # adjoint identity <dY, x W^T> = <dY W, x>
+    assert abs(np.sum(dy * Y) - np.sum(dX * x)) <= 1e-12 * np.sum(np.abs(dy * Y))
+
+
+def _loss(x, dy, out_modes, in_modes, cores, D, in_first=False):
+    Wb = _brute_W(out_modes, in_modes, cores, D, in_first)
+    return float(np.sum(dy * (x @ Wb.T)))
+
+
+@pytest.mark.parametrize("in_first", [False, True])
+def test_core_grads_by_unit_probes(in_first):
+    """f(G) = <dY, x W(G)^T> is linear in each core: f(G_k = e_amb) = dG_k[a,m,b]."""
+    rng = np.random.default_rng(7)
+    out_modes, in_modes = (2, 3), (2, 2)
+    modes = list(in_modes) + list(out_modes) if in_first else list(out_modes) + list(in_modes)
+    ranks = [1, 2, 3, 2, 1]
+    cores, D = _rand_chain(rng, modes, ranks, zero_frac=0.34)
+    x = rng.standard_normal((4, 4))
+    dy = rng.standard_normal((4, 6))
+    _, dG = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D, in_first)
+    for k in range(len(cores)):
+        probe = np.zeros_like(cores[k])
+        for idx in np.ndindex(*cores[k].shape):
+            probe[...] = 0.0
+            probe[idx] = 1.0
+            trial = list(cores)
+            trial[k] = probe
+            want = _loss(x, dy, out_modes, in_modes, trial, D, in_first)
+            assert abs(dG[k][idx] - want) <= 1e-12 * (1.0 + abs(want)), (k, idx)
+
+
+def test_core_grads_finite_difference_random_direction():
+    rng = np.random.default_rng(8)
+    out_modes, in_modes = (3, 2, 2), (2, 3, 2)
+    ranks = [1, 3, 4, 3, 4, 3, 1]
+    cores, D = _rand_chain(rng, list(out_modes) + list(in_modes), ranks, zero_frac=0.25)
+    x = rng.standard_normal((6, 12))
+    dy = rng.standard_normal((6, 12))
+    _, dG = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D)
+    f0 = _loss(x, dy, out_modes, in_modes, cores, D)
+    for k in range(len(cores)):
+        E = rng.standard_normal(cores[k].shape)
+        trial = list(cores)
+        trial[k] = cores[k] + E
+        df = _loss(x, dy, out_modes, in_modes, trial, D) - f0
+        assert abs(df - np.sum(dG[k] * E)) <= 1e-10 * (1.0 + abs(df))
+
+
+def test_zero_D_entry_equals_deleting_slices():
+    rng = np.random.default_rng(9)
+    out_modes, in_modes = (3, 4), (2, 5)
+    ranks = [1, 4, 5, 3, 1]
+    cores, D = _rand_chain(rng, [3, 4, 2, 5], ranks)
+    link, b = 2, 3  # zero D_2[3]: drop slice 3 of G_2's last axis and G_3's first axis
+    D[link - 1][b] = 0.0
+    x = rng.standard_normal((7, 10))
+    dy = rng.standard_normal((7, 12))
+    W = oracle.dense_weight(out_modes, in_modes, cores, D)
+    keep = [i for i in range(ranks[link]) if i != b]
+    cores_s = list(cores)
+    cores_s[link - 1] = cores[link - 1][:, :, keep]
+    cores_s[link] = cores[link][keep, :, :]
+    D_s = list(D)
+    D_s[link - 1] = D[link - 1][keep]
+    W_s = oracle.dense_weight(out_modes, in_modes, cores_s, D_s)
+    assert np.max(np.abs(W - W_s)) <= 1e-15 * np.max(np.abs(W)) * 10
+    _, dG = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D)
+    assert np.all(dG[link - 1][:, :, b] == 0.0)
+    assert np.all(dG[link][b, :, :] == 0.0)
+
+
+def test_all_zero_link_removes_layer():
+    rng = np.random.default_rng(10)
+    out_modes, in_modes = (2, 3), (3, 2)
+    cores, D = _rand_chain(rng, [2, 3, 3, 2], [1, 3, 3, 3, 1])
+    D[1][:] = 0.0
+    x = rng.standard_normal((4, 6))
+    dy = rng.standard_normal((4, 6))
+    Y = oracle.tt_linear_forward(x, out_modes, in_modes, cores, D)
+    dX, dG = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D)
+    assert np.all(Y == 0.0) and np.all(dX == 0.0)
+    # cores adjacent to the dead link see an exactly-zero D factor in every term
+    assert np.all(dG[1] == 0.0) and np.all(dG[2] == 0.0)
+
+
+def test_hand_worked_golden():
+    with open(os.path.join(GOLDEN, "tt_two_core_worked.json")) as f:
+        g = json.load(f)
+    cores = [np.array(c, dtype=np.float64) for c in g["cores"]]
+    D = [np.array(v, dtype=np.float64) for v in g["D"]]
+    x = np.array(g["x"], dtype=np.float64)
+    dy = np.array(g["dy"], dtype=np.float64)
+    W = oracle.dense_weight(g["out_modes"], g["in_modes"], cores, D)
+    Y = oracle.tt_linear_forward(x, g["out_modes"], g["in_modes"], cores, D)
+    dX, dG = oracle.tt_linear_backward(x, dy, g["out_modes"], g["in_modes"], cores, D)
+    assert np.array_equal(W, np.array(g["W"]))
+    assert np.array_equal(Y, np.array(g["Y"]))
+    assert np.array_equal(dX, np.array(g["dX"]))
+    for k in range(2):
+        assert np.array_equal(dG[k], np.array(g["dG"][k]))
