@@ -1,0 +1,216 @@
+/*
+ * ttc.h - C ABI of the tensor-train compressed layer library (HIP, gfx950).
+ *
+ * The library computes the data-parallel hot path of rank-adaptive
+ * tensor-compressed training as described for CoMERA ("CoMERA: Computing- and
+ * Memory-Efficient Training via Rank-Adaptive Tensor Optimization", NeurIPS
+ * 2024, project page):
+ *
+ *   - a linear layer whose weight W (N_out x N_in) is stored as a tensor train:
+ *     cores G_k of shape (r_{k-1}, n_k, r_k), r_0 = r_d = 1, with a diagonal
+ *     D_k on every link (section "Learn the ranks while training"); the
+ *     forward Y = x W^T, the input gradient dX = dY W and the core gradients
+ *     dG_k, evaluated in the contraction order of section "Making small tensor
+ *     operations fast on GPUs" (multiply the output-side cores together and the
+ *     input-side cores together, contract the input through them, keep the
+ *     intermediate for the backward pass);
+ *   - an embedding table in tensor-train-matrix (TTM) format, cores F_k of
+ *     shape (r_{k-1}, m_k, n_k, r_k) (same section; NeurIPS poster page, figure
+ *     on the TT and TTM structures), looked up for a batch of ids with
+ *     deduplication and pairwise core contraction (section "Making small tensor
+ *     operations fast on GPUs", embedding lookup without repeated work), and
+ *     its backward into the core gradients.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer to caller-owned, contiguous,
+ *     row-major memory, unless the comment says "host".  The library never
+ *     allocates or frees device memory in these calls and never synchronises
+ *     the stream; all work is enqueued on `stream` (0 = the null stream), so
+ *     the calls may be captured into a HIP graph.
+ *   - Arrays of per-core pointers (G, D, dG, F, dF) are HOST arrays holding
+ *     device pointers.
+ *   - Row and column indices of W and of the TTM table are mixed-radix over
+ *     their modes, first mode most significant.
+ *   - The tensor train's chain lists the output modes first, then the input
+ *     modes (in_first = 0), or the input modes first (in_first = 1); W is the
+ *     chain tensor reshaped to (N_out, N_in), or the transpose of its
+ *     (N_in, N_out) reshape.
+ *   - D_k is a real-valued scale (fp32) on link k; an entry that is exactly 0
+ *     removes the matching slice of both neighbouring cores, and the results
+ *     are then exactly those of the smaller chain (dead-slice core gradients
+ *     are exactly 0).  D is read on the device at every call.
+ *   - Errors are returned synchronously, before anything is enqueued; on a
+ *     non-zero status nothing was launched.  T = 0 is a valid no-op.
+ */
+#ifndef TTC_H
+#define TTC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* ttc_stream_t; /* a hipStream_t */
+
+typedef enum {
+  TTC_OK = 0,
+  TTC_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  TTC_ERR_SHAPE = 2,       /* mode counts / modes / T out of range                */
+  TTC_ERR_RANK = 3,        /* ranks inconsistent (r_0, r_d != 1, r_k < 1)          */
+  TTC_ERR_DTYPE = 4,       /* unknown dtype                                        */
+  TTC_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                     */
+  TTC_ERR_WORKSPACE = 6,   /* saved / scratch buffer smaller than required         */
+  TTC_ERR_UNSUPPORTED = 7, /* valid but not implemented (path, size limits)        */
+  TTC_ERR_HIP = 8          /* a HIP runtime call failed                            */
+} ttc_status;
+
+typedef enum { TTC_F32 = 0, TTC_BF16 = 1 } ttc_dtype;
+
+typedef enum {
+  TTC_PATH_AUTO = 0,       /* planner picks                                        */
+  TTC_PATH_MERGED = 1,     /* merge each half of the chain, two skinny GEMMs       */
+  TTC_PATH_SEQUENTIAL = 2, /* core-by-core sweep (costed by the planner only)      */
+  TTC_PATH_DENSE = 3       /* materialise W (costed by the planner only)           */
+} ttc_path;
+
+#define TTC_MAX_HALF_MODES 8 /* at most 8 output and 8 input modes */
+#define TTC_MAX_RANK 128     /* every r_k <= 128 */
+
+/* TT-linear layer descriptor (host memory). */
+typedef struct {
+  int32_t p;                              /* number of output modes, >= 1          */
+  int32_t q;                              /* number of input modes, >= 1           */
+  int32_t out_modes[TTC_MAX_HALF_MODES];  /* n of each output mode, >= 1           */
+  int32_t in_modes[TTC_MAX_HALF_MODES];   /* n of each input mode, >= 1            */
+  int32_t ranks[2 * TTC_MAX_HALF_MODES + 1]; /* r_0..r_{p+q} in chain order      */
+  int32_t in_first;                       /* 0: chain = out modes, in modes; 1: in, out */
+  int32_t act_dtype;                      /* ttc_dtype of x, y, dy, dx              */
+  int32_t path;                           /* ttc_path                               */
+} tt_linear_desc;
+
+/*
+ * Bytes of the two caller-provided device buffers for T tokens.
+ *   saved   - written by tt_linear_fwd, read by tt_linear_bwd: the merged halves
+ *             of the chain and the T x r intermediate Z = x A^T kept from the
+ *             forward pass.  Must outlive the fwd -> bwd pair, with the same
+ *             cores, D and x.
+ *   scratch - temporary space of one call (partial reductions).
+ * Host-only; launches nothing.
+ */
+ttc_status tt_linear_workspace(const tt_linear_desc* desc, int64_t T,
+                               size_t* saved_bytes, size_t* scratch_bytes);
+
+/*
+ * Forward: y = x W^T.
+ *   x  - T x N_in  (act_dtype)
+ *   G  - host array of p+q device pointers, core k is fp32 (r_{k-1}, n_k, r_k)
+ *   D  - host array of p+q-1 device pointers, fp32 vectors of length r_k
+ *   y  - T x N_out (act_dtype), overwritten
+ *   saved / scratch - device buffers of at least tt_linear_workspace() bytes,
+ *        16-byte aligned.
+ * fp32 activations are computed with fp32 MFMA; bf16 activations with bf16
+ * MFMA operands and fp32 accumulation (y rounded to nearest-even).
+ */
+ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const void* x,
+                         const float* const* G, const float* const* D, void* y,
+                         void* saved, size_t saved_bytes, void* scratch,
+                         size_t scratch_bytes, ttc_stream_t stream);
+
+/*
+ * Backward: dX = dY W (skipped when dx == NULL) and dG_k = d<dY, x W^T>/dG_k.
+ *   x, G, D, saved - exactly as passed to the matching tt_linear_fwd
+ *   dy - T x N_out (act_dtype)
+ *   dx - T x N_in  (act_dtype), overwritten, or NULL
+ *   dG - host array of p+q device pointers, fp32, shapes of the cores,
+ *        overwritten
+ */
+ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const void* x,
+                         const void* dy, const float* const* G,
+                         const float* const* D, const void* saved,
+                         size_t saved_bytes, void* dx, float* const* dG,
+                         void* scratch, size_t scratch_bytes,
+                         ttc_stream_t stream);
+
+/*
+ * Planner report (host-only): writes a NUL-terminated text into buf (at most
+ * n bytes) with the chosen path and the modelled flops / bytes of the merged,
+ * sequential and dense paths for T tokens.
+ */
+ttc_status tt_linear_explain(const tt_linear_desc* desc, int64_t T, char* buf,
+                             size_t n);
+
+/* Modelled multiply-adds of one path for T tokens (forward + backward),
+ * host-only; *out is set to -1 when the path does not apply. */
+ttc_status tt_linear_path_cost(const tt_linear_desc* desc, int64_t T,
+                               int32_t path, double* macs, double* bytes);
+
+/* TTM embedding descriptor (host memory). */
+#define TTC_TTM_MAX_MODES 8
+typedef struct {
+  int32_t d;                              /* number of cores, 1..8                   */
+  int32_t vocab_modes[TTC_TTM_MAX_MODES]; /* m_k; vocabulary = prod m_k < 2^31       */
+  int32_t dim_modes[TTC_TTM_MAX_MODES];   /* n_k; embedding dim = prod n_k           */
+  int32_t ranks[TTC_TTM_MAX_MODES + 1];   /* r_0..r_d, r_0 = r_d = 1                 */
+  int32_t accumulate;                     /* bwd: 1 = add into dF, 0 = overwrite     */
+} ttm_embed_desc;
+
+/*
+ * Bytes of the saved / scratch buffers for a lookup of T ids.  `saved` is
+ * written by ttm_embed_fwd and read by ttm_embed_bwd; its first part has a
+ * documented layout (see TTM_SAVED_* below) so that the integer results can
+ * be inspected.  Host-only.
+ */
+ttc_status ttm_embed_workspace(const ttm_embed_desc* desc, int64_t T,
+                               size_t* saved_bytes, size_t* scratch_bytes);
+
+/*
+ * Forward lookup: out[t] = E[ids[t]] for t < T.
+ *   ids - T int64 ids, each in [0, prod m_k); an id out of range gives a zero
+ *         row and sets the device error flag (see ttm_embed_status)
+ *   F   - host array of d device pointers, fp32 cores (r_{k-1}, m_k, n_k, r_k)
+ *   D   - host array of d-1 device pointers (fp32 length r_k), or NULL for the
+ *         identity on every link
+ *   out - T x prod n_k fp32, overwritten
+ * saved layout (int32 words, U = number of distinct ids):
+ *   [0]                 U
+ *   [1]                 error flag (0 = ok, 1 = an id out of range)
+ *   [2 .. 2+T)          order: token positions sorted by (id, position)
+ *   [2+T .. 2+2T)       inverse: index into the unique list of each token
+ *   [2+2T .. 2+3T)      unique ids, ascending (first U used)
+ *   [2+3T .. 3+4T)      segment offsets into order (first U+1 used)
+ *   [3+4T .. 3+5T)      first digit... no: digits of each unique id follow in
+ *                       the rest of the buffer, which is private.
+ */
+ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T,
+                         const int64_t* ids, const float* const* F,
+                         const float* const* D, float* out, void* saved,
+                         size_t saved_bytes, void* scratch, size_t scratch_bytes,
+                         ttc_stream_t stream);
+
+/*
+ * Backward: dF_k = d( sum_t <dout[t], E[ids[t]]> ) / dF_k.
+ *   ids, F, D, saved - as passed to the matching ttm_embed_fwd
+ *   dout - T x prod n_k fp32
+ *   dF   - host array of d device pointers, fp32, shapes of the cores;
+ *          overwritten, or added to when desc->accumulate
+ */
+ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T,
+                         const int64_t* ids, const float* dout,
+                         const float* const* F, const float* const* D,
+                         const void* saved, size_t saved_bytes,
+                         float* const* dF, void* scratch, size_t scratch_bytes,
+                         ttc_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ttc_status_str(ttc_status s);
+
+/* Library version string (static storage). */
+const char* ttc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTC_H */

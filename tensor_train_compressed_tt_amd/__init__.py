@@ -1,0 +1,224 @@
+"""Python binding of libttc (the C ABI declared in include/ttc.h).
+
+Argument marshalling only: every step of the TT-linear and TTM-embedding
+computations runs in the HIP kernels of libttc.so.  PyTorch supplies device
+memory and the current stream.  Importing this module does not need a GPU;
+loading the library does need the built ``libttc.so`` (``python -m
+tensor_train_compressed_tt_amd.build``) and fails loudly without it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libttc.so")
+
+TTC_F32, TTC_BF16 = 0, 1
+TTC_PATH_AUTO, TTC_PATH_MERGED, TTC_PATH_SEQUENTIAL, TTC_PATH_DENSE = 0, 1, 2, 3
+MAX_HALF_MODES = 8
+TTM_MAX_MODES = 8
+
+STATUS = {
+    0: "TTC_OK",
+    1: "TTC_ERR_NULL",
+    2: "TTC_ERR_SHAPE",
+    3: "TTC_ERR_RANK",
+    4: "TTC_ERR_DTYPE",
+    5: "TTC_ERR_ALIGN",
+    6: "TTC_ERR_WORKSPACE",
+    7: "TTC_ERR_UNSUPPORTED",
+    8: "TTC_ERR_HIP",
+}
+
+# every symbol include/ttc.h declares
+EXPORTS = [
+    "tt_linear_workspace",
+    "tt_linear_fwd",
+    "tt_linear_bwd",
+    "tt_linear_explain",
+    "tt_linear_path_cost",
+    "ttm_embed_workspace",
+    "ttm_embed_fwd",
+    "ttm_embed_bwd",
+    "ttc_status_str",
+    "ttc_version",
+]
+
+
+class TTCError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class TTLinearDesc(ctypes.Structure):
+    _fields_ = [
+        ("p", ctypes.c_int32),
+        ("q", ctypes.c_int32),
+        ("out_modes", ctypes.c_int32 * MAX_HALF_MODES),
+        ("in_modes", ctypes.c_int32 * MAX_HALF_MODES),
+        ("ranks", ctypes.c_int32 * (2 * MAX_HALF_MODES + 1)),
+        ("in_first", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+    ]
+
+
+class TTMEmbedDesc(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32),
+        ("vocab_modes", ctypes.c_int32 * TTM_MAX_MODES),
+        ("dim_modes", ctypes.c_int32 * TTM_MAX_MODES),
+        ("ranks", ctypes.c_int32 * (TTM_MAX_MODES + 1)),
+        ("accumulate", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libttc.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m tensor_train_compressed_tt_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    D = ctypes.POINTER(TTLinearDesc)
+    E = ctypes.POINTER(TTMEmbedDesc)
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "tt_linear_workspace": [D, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
+        "tt_linear_fwd": [D, _I64, _P, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
+        "tt_linear_bwd": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P],
+        "tt_linear_explain": [D, _I64, ctypes.c_char_p, _SZ],
+        "tt_linear_path_cost": [D, _I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double)],
+        "ttm_embed_workspace": [E, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
+        "ttm_embed_fwd": [E, _I64, _P, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
+        "ttm_embed_bwd": [E, _I64, _P, _P, pp, pp, _P, _SZ, pp, _P, _SZ, _P],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.ttc_status_str.argtypes = [ctypes.c_int]
+    L.ttc_status_str.restype = ctypes.c_char_p
+    L.ttc_version.argtypes = []
+    L.ttc_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise TTCError(fn, code)
+
+
+def _ptrs(addrs: Sequence[int] | None):
+    if addrs is None:
+        return None
+    arr = (ctypes.c_void_p * max(1, len(addrs)))(*[ctypes.c_void_p(int(a)) for a in addrs])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), arr
+
+
+def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=False, path=TTC_PATH_AUTO):
+    d = TTLinearDesc()
+    d.p, d.q = len(out_modes), len(in_modes)
+    for i, n in enumerate(out_modes):
+        d.out_modes[i] = int(n)
+    for i, n in enumerate(in_modes):
+        d.in_modes[i] = int(n)
+    for i, r in enumerate(ranks):
+        d.ranks[i] = int(r)
+    d.in_first = int(bool(in_first))
+    d.act_dtype = int(act_dtype)
+    d.path = int(path)
+    return d
+
+
+def make_ttm_desc(vocab_modes, dim_modes, ranks, accumulate=False):
+    d = TTMEmbedDesc()
+    d.d = len(vocab_modes)
+    for i, n in enumerate(vocab_modes):
+        d.vocab_modes[i] = int(n)
+    for i, n in enumerate(dim_modes):
+        d.dim_modes[i] = int(n)
+    for i, r in enumerate(ranks):
+        d.ranks[i] = int(r)
+    d.accumulate = int(bool(accumulate))
+    return d
+
+
+# ---- raw entry points (same names as the C ABI, integer addresses) -------------
+
+def tt_linear_workspace(desc: TTLinearDesc, T: int):
+    s, c = _SZ(0), _SZ(0)
+    _check("tt_linear_workspace", lib().tt_linear_workspace(ctypes.byref(desc), T, ctypes.byref(s), ctypes.byref(c)))
+    return s.value, c.value
+
+
+def tt_linear_fwd(desc, T, x, G, D, y, saved, saved_bytes, scratch, scratch_bytes, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    code = lib().tt_linear_fwd(ctypes.byref(desc), T, x, g, dd, y, saved, saved_bytes, scratch, scratch_bytes, stream)
+    _check("tt_linear_fwd", code)
+
+
+def tt_linear_bwd(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, scratch, scratch_bytes, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    dg, _dga = _ptrs(dG)
+    code = lib().tt_linear_bwd(ctypes.byref(desc), T, x, dy, g, dd, saved, saved_bytes, dx, dg, scratch,
+                               scratch_bytes, stream)
+    _check("tt_linear_bwd", code)
+
+
+def tt_linear_explain(desc: TTLinearDesc, T: int) -> str:
+    buf = ctypes.create_string_buffer(1024)
+    _check("tt_linear_explain", lib().tt_linear_explain(ctypes.byref(desc), T, buf, 1024))
+    return buf.value.decode()
+
+
+def tt_linear_path_cost(desc: TTLinearDesc, T: int, path: int):
+    m, b = ctypes.c_double(0), ctypes.c_double(0)
+    _check("tt_linear_path_cost", lib().tt_linear_path_cost(ctypes.byref(desc), T, path, ctypes.byref(m),
+                                                            ctypes.byref(b)))
+    return m.value, b.value
+
+
+def ttm_embed_workspace(desc: TTMEmbedDesc, T: int):
+    s, c = _SZ(0), _SZ(0)
+    _check("ttm_embed_workspace", lib().ttm_embed_workspace(ctypes.byref(desc), T, ctypes.byref(s), ctypes.byref(c)))
+    return s.value, c.value
+
+
+def ttm_embed_fwd(desc, T, ids, F, D, out, saved, saved_bytes, scratch, scratch_bytes, stream=0):
+    f, _fa = _ptrs(F)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    code = lib().ttm_embed_fwd(ctypes.byref(desc), T, ids, f, dd, out, saved, saved_bytes, scratch, scratch_bytes,
+                               stream)
+    _check("ttm_embed_fwd", code)
+
+
+def ttm_embed_bwd(desc, T, ids, dout, F, D, saved, saved_bytes, dF, scratch, scratch_bytes, stream=0):
+    f, _fa = _ptrs(F)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    df, _dfa = _ptrs(dF)
+    code = lib().ttm_embed_bwd(ctypes.byref(desc), T, ids, dout, f, dd, saved, saved_bytes, df, scratch,
+                               scratch_bytes, stream)
+    _check("ttm_embed_bwd", code)
+
+
+def version() -> str:
+    return lib().ttc_version().decode()
+
+
+from .torch_api import TTLinear, TTMEmbedding  # noqa: E402,F401

@@ -1,0 +1,59 @@
+// Host-side plan of one TT-linear call: validated shapes, the split of the
+// chain into its output-side and input-side halves, launch shapes and the
+// byte layout of the caller's `saved` and `scratch` buffers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ttc.h"
+
+namespace ttc {
+
+constexpr int kMaxCores = 2 * TTC_MAX_HALF_MODES;
+constexpr int kTileT = 64;  // tokens per tile of the streaming kernels
+
+struct LinearPlan {
+  // ---- shape, chain order -------------------------------------------------
+  int p, q, d;
+  int in_first;
+  int act;                 // TTC_F32 / TTC_BF16
+  int modes[kMaxCores];    // n_k in chain order
+  int ranks[kMaxCores + 1];
+  int s;                   // cores in the left half of the chain
+  int rs;                  // rank of the link between the halves
+  int Rpad;                // rs rounded up to 32 (MFMA tile multiple)
+  int NR;                  // Rpad / 16
+  int64_t NL, NRt;         // prod of the left / right half's modes
+  int64_t N_out, N_in;
+  int64_t T;
+  // prefix products M_k (k < s-1) and suffix products N_k (k > s), fp32,
+  // offsets in floats inside the chain area of `saved`
+  int64_t chain_off[kMaxCores];
+  int64_t chain_floats;
+  // merge work items: left rows of M_k (k < s) and right columns of N_k (k >= s)
+  int64_t item_off[kMaxCores + 1];  // per core k: first item; item_off[d] = total
+  // ---- launch shapes ---------------------------------------------------------
+  int ntiles;              // ceil(T / kTileT)
+  int cwc;                 // 64-column chunks per work-group in the backward passes (max)
+  int dy_gc, dy_gt, dy_ncc, dy_tpg;  // dY pass: column groups, token groups, chunks/group, tiles/group
+  int dx_gc, dx_gt, dx_ncc, dx_tpg;  // dX pass
+  // ---- saved layout (bytes) ----------------------------------------------------
+  size_t sv_meta, sv_Ac, sv_AcT, sv_Bc, sv_BcT, sv_chain, sv_Z, sv_total;
+  // ---- scratch layout (bytes) ----------------------------------------------------
+  size_t sc_dZp, sc_dBp, sc_dAp, sc_dL, sc_dR, sc_w0, sc_w1, sc_total;
+  int64_t wl_floats, wr_floats;  // size of one left / right ping-pong buffer
+};
+
+// saved meta block (int32 words)
+constexpr int kMetaLive = 0;    // live[j]: link index of the j-th nonzero D entry, -1 past r_eff
+constexpr int kMetaPos = 128;   // pos[b]: compact index of link entry b, -1 when D[b] == 0
+constexpr int kMetaReff = 256;  // r_eff
+constexpr size_t kMetaBytes = 1088;
+
+ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P);
+
+// multiply-adds and bytes of one forward+backward for each path (planner model)
+void linear_path_costs(const LinearPlan& P, double macs[4], double bytes[4]);
+
+}  // namespace ttc

@@ -1,0 +1,118 @@
+// Device-side helpers shared by the HIP kernels: element types, the MFMA
+// fragments used for gfx950, guarded 16-byte row loads and bf16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 activations are carried as raw 16-bit patterns.
+struct bf16_t {
+  unsigned short bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+  return __uint_as_float(((unsigned int)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+// One MFMA "k-step": each lane supplies 16 bytes of one row of A and of one
+// column of B.  Lane l = 16*g + c holds row/column c and the 16-byte group g,
+// so a k-step spans 4 groups x (16 bytes / element size) k-values.  The order
+// of k inside a step is the same for both operands, so any assignment of
+// memory columns to (g, element) pairs gives the same dot products.
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16_t> {
+  static constexpr int EPV = 8;    // elements per lane per k-step
+  static constexpr int KSTEP = 32; // k-values per k-step
+  typedef u16x8 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0}; }
+  __device__ __forceinline__ static unsigned short from_f32(float f) { return f32_to_bf16(f); }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int EPV = 4;
+  static constexpr int KSTEP = 16;
+  typedef f32x4 frag;
+  // four 16x16x4 fp32 MFMAs; MFMA e takes element e of every lane
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+  }
+  __device__ __forceinline__ static frag zero() { return frag{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ static float from_f32(float f) { return f; }
+};
+
+// storage element of an activation type
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> { typedef unsigned short type; };
+template <> struct Elem<float> { typedef float type; };
+
+template <typename T>
+__device__ __forceinline__ float elem_to_f32(typename Elem<T>::type v);
+template <>
+__device__ __forceinline__ float elem_to_f32<bf16_t>(unsigned short v) { return bf16_to_f32(v); }
+template <>
+__device__ __forceinline__ float elem_to_f32<float>(float v) { return v; }
+
+// Load the 16-byte group of row `row` starting at column `col` of a row-major
+// matrix (leading dimension ld elements).  Elements outside [0,nrows) x
+// [0,ncols) read as zero.  `vec` says that rows are 16-byte aligned.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag load_frag(const typename Elem<T>::type* __restrict__ base,
+                                                           int64_t row, int64_t nrows, int64_t col,
+                                                           int64_t ncols, int64_t ld, bool vec) {
+  typedef typename Mma<T>::frag frag;
+  constexpr int EPV = Mma<T>::EPV;
+  if (row >= nrows || col >= ncols) return Mma<T>::zero();
+  const typename Elem<T>::type* p = base + row * ld + col;
+  if (vec && col + EPV <= ncols) return *reinterpret_cast<const frag*>(p);
+  frag f = Mma<T>::zero();
+#pragma unroll
+  for (int e = 0; e < EPV; ++e)
+    if (col + e < ncols) f[e] = p[e];
+  return f;
+}
+
+// Same from LDS (always in range, 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag lds_frag(const typename Elem<T>::type* p) {
+  return *reinterpret_cast<const typename Mma<T>::frag*>(p);
+}
+
+// Column fragment from LDS: EPV consecutive rows of one column.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag lds_col_frag(const typename Elem<T>::type* p, int ld) {
+  typename Mma<T>::frag f;
+#pragma unroll
+  for (int e = 0; e < Mma<T>::EPV; ++e) f[e] = p[e * ld];
+  return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace ttc

@@ -1,0 +1,169 @@
+"""Torch-tensor front end of libttc: checks shapes, allocates the caller-owned
+buffers with torch and passes device addresses and the current HIP stream to
+the C entry points.  No arithmetic happens here."""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (
+    TTC_BF16,
+    TTC_F32,
+    TTC_PATH_AUTO,
+    make_linear_desc,
+    make_ttm_desc,
+    tt_linear_bwd,
+    tt_linear_fwd,
+    tt_linear_workspace,
+    ttm_embed_bwd,
+    ttm_embed_fwd,
+    ttm_embed_workspace,
+)
+
+_ACT = {torch.float32: TTC_F32, torch.bfloat16: TTC_BF16}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class TTLinear:
+    """A TT-linear layer y = x W^T with W given by cores and link diagonals.
+
+    ``ranks`` lists r_0..r_d in chain order (output modes first unless
+    ``in_first``).  Cores are fp32 (r_{k-1}, n_k, r_k); D is a list of d-1 fp32
+    vectors; activations are fp32 or bf16.
+    """
+
+    def __init__(self, out_modes, in_modes, ranks, dtype=torch.float32, in_first=False, path=TTC_PATH_AUTO):
+        self.out_modes = tuple(int(n) for n in out_modes)
+        self.in_modes = tuple(int(n) for n in in_modes)
+        self.ranks = tuple(int(r) for r in ranks)
+        self.in_first = bool(in_first)
+        self.dtype = dtype
+        self.n_out = math.prod(self.out_modes)
+        self.n_in = math.prod(self.in_modes)
+        self.desc = make_linear_desc(self.out_modes, self.in_modes, self.ranks, _ACT[dtype], in_first, path)
+        modes = list(self.in_modes) + list(self.out_modes) if in_first else list(self.out_modes) + list(self.in_modes)
+        self.core_shapes = [(self.ranks[k], modes[k], self.ranks[k + 1]) for k in range(len(modes))]
+
+    def workspace(self, T: int):
+        return tt_linear_workspace(self.desc, T)
+
+    def alloc(self, T: int, device="cuda"):
+        """Fresh (saved, scratch) byte buffers for T tokens."""
+        sb, cb = self.workspace(T)
+        return (torch.empty(max(sb, 256), dtype=torch.uint8, device=device),
+                torch.empty(max(cb, 256), dtype=torch.uint8, device=device))
+
+    def _check_chain(self, cores, D):
+        if len(cores) != len(self.core_shapes) or len(D) != len(self.core_shapes) - 1:
+            raise ValueError("wrong number of cores / diagonals")
+        for k, (c, s) in enumerate(zip(cores, self.core_shapes)):
+            _need(c, f"core {k}", torch.float32, s)
+        for k, v in enumerate(D):
+            _need(v, f"D {k}", torch.float32, (self.core_shapes[k][2],))
+
+    def forward(self, x, cores, D, out=None, saved=None):
+        T = int(x.shape[0])
+        _need(x, "x", self.dtype, (T, self.n_in))
+        self._check_chain(cores, D)
+        if out is None:
+            out = torch.empty((T, self.n_out), dtype=self.dtype, device=x.device)
+        _need(out, "out", self.dtype, (T, self.n_out))
+        sb, _ = self.workspace(T)
+        if saved is None:
+            saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=x.device)
+        tt_linear_fwd(self.desc, T, x.data_ptr(), [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
+                      out.data_ptr(), saved.data_ptr(), saved.numel(), None, 0, _stream())
+        return out, saved
+
+    def backward(self, x, dy, cores, D, saved, want_dx=True, dx=None, dG=None, scratch=None):
+        T = int(x.shape[0])
+        _need(x, "x", self.dtype, (T, self.n_in))
+        _need(dy, "dy", self.dtype, (T, self.n_out))
+        self._check_chain(cores, D)
+        _, cb = self.workspace(T)
+        if scratch is None:
+            scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=x.device)
+        if want_dx and dx is None:
+            dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
+        if dG is None:
+            dG = [torch.empty(s, dtype=torch.float32, device=x.device) for s in self.core_shapes]
+        tt_linear_bwd(self.desc, T, x.data_ptr(), dy.data_ptr(), [c.data_ptr() for c in cores],
+                      [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
+                      dx.data_ptr() if want_dx else None, [g.data_ptr() for g in dG], scratch.data_ptr(),
+                      scratch.numel(), _stream())
+        return (dx if want_dx else None), dG
+
+
+class TTMEmbedding:
+    """A TTM embedding table: cores F_k (r_{k-1}, m_k, n_k, r_k) fp32."""
+
+    def __init__(self, vocab_modes, dim_modes, ranks):
+        self.vocab_modes = tuple(int(n) for n in vocab_modes)
+        self.dim_modes = tuple(int(n) for n in dim_modes)
+        self.ranks = tuple(int(r) for r in ranks)
+        self.vocab = math.prod(self.vocab_modes)
+        self.dim = math.prod(self.dim_modes)
+        self.core_shapes = [(self.ranks[k], self.vocab_modes[k], self.dim_modes[k], self.ranks[k + 1])
+                            for k in range(len(self.vocab_modes))]
+
+    def desc(self, accumulate=False):
+        return make_ttm_desc(self.vocab_modes, self.dim_modes, self.ranks, accumulate)
+
+    def workspace(self, T: int):
+        return ttm_embed_workspace(self.desc(), T)
+
+    def _check(self, cores, D):
+        if len(cores) != len(self.core_shapes):
+            raise ValueError("wrong number of cores")
+        for k, (c, s) in enumerate(zip(cores, self.core_shapes)):
+            _need(c, f"core {k}", torch.float32, s)
+        if D is not None:
+            for k, v in enumerate(D):
+                _need(v, f"D {k}", torch.float32, (self.ranks[k + 1],))
+
+    def forward(self, ids, cores, D=None, out=None, saved=None, scratch=None):
+        T = int(ids.shape[0])
+        _need(ids, "ids", torch.int64, (T,))
+        self._check(cores, D)
+        sb, cb = self.workspace(T)
+        if out is None:
+            out = torch.empty((T, self.dim), dtype=torch.float32, device=ids.device)
+        if saved is None:
+            saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=ids.device)
+        if scratch is None:
+            scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=ids.device)
+        ttm_embed_fwd(self.desc(), T, ids.data_ptr(), [c.data_ptr() for c in cores],
+                      None if D is None else [v.data_ptr() for v in D], out.data_ptr(), saved.data_ptr(),
+                      saved.numel(), scratch.data_ptr(), scratch.numel(), _stream())
+        return out, saved
+
+    def backward(self, ids, dout, cores, D, saved, dF=None, accumulate=False, scratch=None):
+        T = int(ids.shape[0])
+        _need(ids, "ids", torch.int64, (T,))
+        _need(dout, "dout", torch.float32, (T, self.dim))
+        self._check(cores, D)
+        _, cb = self.workspace(T)
+        if scratch is None:
+            scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=ids.device)
+        if dF is None:
+            dF = [torch.empty(s, dtype=torch.float32, device=ids.device) for s in self.core_shapes]
+        ttm_embed_bwd(self.desc(accumulate), T, ids.data_ptr(), dout.data_ptr(), [c.data_ptr() for c in cores],
+                      None if D is None else [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
+                      [g.data_ptr() for g in dF], scratch.data_ptr(), scratch.numel(), _stream())
+        return dF

@@ -1,0 +1,179 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, validates descriptors and sizes buffers, and its planner's
+cost model agrees with an independent operation count.  No GPU needed: none
+of these calls launches work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_train_compressed_tt_amd as ttc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "ttc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:ttc_status|const char\s*\*)\s+(\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ttc.lib()
+    names = _header_functions()
+    assert set(names) == set(ttc.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert ttc.version().startswith("ttc")
+
+
+def _desc(**kw):
+    base = dict(out_modes=(12, 8, 8), in_modes=(12, 8, 8), ranks=[1, 30, 30, 30, 30, 30, 1], act_dtype=ttc.TTC_BF16)
+    base.update(kw)
+    return ttc.make_linear_desc(**base)
+
+
+def test_workspace_sizes_scale_with_tokens():
+    d = _desc()
+    s0, c0 = ttc.tt_linear_workspace(d, 0)
+    s1, c1 = ttc.tt_linear_workspace(d, 16384)
+    # the kept intermediate Z is T x 32 fp32
+    assert s1 - s0 >= 16384 * 32 * 4
+    assert c1 > c0
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(ranks=[2, 30, 30, 30, 30, 30, 1]), 3),
+        (dict(ranks=[1, 30, 30, 0, 30, 30, 1]), 3),
+        (dict(ranks=[1, 30, 30, 129, 30, 30, 1]), 3),
+        (dict(act_dtype=7), 4),
+        (dict(out_modes=(12, 0, 8)), 2),
+        (dict(path=ttc.TTC_PATH_DENSE), 7),
+        (dict(path=ttc.TTC_PATH_SEQUENTIAL), 7),
+    ],
+)
+def test_bad_descriptors_are_rejected(kw, code):
+    d = _desc(**kw)
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_workspace(d, 64)
+    assert e.value.code == code
+
+
+def test_too_many_modes_rejected():
+    d = _desc()
+    d.p = 9
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_workspace(d, 64)
+    assert e.value.code == 2
+
+
+def test_negative_tokens_rejected():
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_workspace(_desc(), -1)
+    assert e.value.code == 2
+
+
+def test_fwd_errors_before_launch():
+    """Argument errors come back synchronously and nothing is launched."""
+    d = _desc()
+    sb, cb = ttc.tt_linear_workspace(d, 64)
+    G = [16] * 6  # never dereferenced: validation fails first
+    D = [16] * 5
+    # null x
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd(d, 64, None, G, D, 16, 16, sb, None, 0)
+    assert e.value.code == 1
+    # misaligned x
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd(d, 64, 18, G, D, 16, 16, sb, None, 0)
+    assert e.value.code == 5
+    # saved too small
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd(d, 64, 16, G, D, 16, 16, sb - 1, None, 0)
+    assert e.value.code == 6
+    # null core pointer
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd(d, 64, 16, [16, 16, 0, 16, 16, 16], D, 16, 16, sb, None, 0)
+    assert e.value.code == 1
+    # T = 0 is a no-op that succeeds without touching anything
+    ttc.tt_linear_fwd(d, 0, None, G, D, None, None, 0, None, 0)
+
+
+def test_bwd_errors_before_launch():
+    d = _desc()
+    sb, cb = ttc.tt_linear_workspace(d, 64)
+    G = [16] * 6
+    D = [16] * 5
+    dG = [16] * 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd(d, 64, 16, 16, G, D, 16, sb, 16, dG, 16, cb - 1)
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd(d, 64, 16, 16, G, D, 16, sb, 16, [16] * 5 + [0], 16, cb)
+    assert e.value.code == 1
+
+
+def _merged_macs(out_modes, in_modes, r, T):
+    """Independent count: skinny GEMMs of the merged order plus the half merges."""
+    n_out, n_in = 1, 1
+    for n in out_modes:
+        n_out *= n
+    for n in in_modes:
+        n_in *= n
+
+    def half(modes):
+        # chain product built one core at a time: (rows x r) (r x n r)
+        tot, rows = 0, modes[0]
+        for n in modes[1:]:
+            tot += rows * r * n * r
+            rows *= n
+        return tot
+
+    merge = half(list(out_modes)) + half(list(reversed(in_modes)))
+    return 3 * T * r * (n_in + n_out) + 3 * merge
+
+
+def _sequential_macs(out_modes, in_modes, r, T):
+    """Independent count of the core-by-core sweep over x (forward f, total 3 f)."""
+    f = 0
+    lead = 1
+    for n in in_modes:
+        lead *= n
+    ranks_in = [r] * len(in_modes) + [1]  # rank left of each input core, then the end
+    for k in range(len(in_modes) - 1, -1, -1):
+        f += T * lead * ranks_in[k + 1] * ranks_in[k]
+        lead //= in_modes[k]
+    ranks_out = [1] + [r] * len(out_modes)
+    trail = 1
+    for k in range(len(out_modes) - 1, -1, -1):
+        trail *= out_modes[k]
+        f += T * trail * ranks_out[k + 1] * ranks_out[k]
+    return 3 * f
+
+
+@pytest.mark.parametrize("T", [1, 64, 4096])
+@pytest.mark.parametrize("shape", [((12, 8, 8), (12, 8, 8)), ((12, 16, 16), (12, 8, 8)), ((2, 3), (3, 2))])
+def test_planner_cost_model_matches_independent_count(T, shape):
+    out_modes, in_modes = shape
+    r = 30 if len(out_modes) == 3 else 3
+    ranks = [1] + [r] * (len(out_modes) + len(in_modes) - 1) + [1]
+    d = ttc.make_linear_desc(out_modes, in_modes, ranks, ttc.TTC_F32)
+    m1, _ = ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_MERGED)
+    m2, _ = ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_SEQUENTIAL)
+    assert m1 == pytest.approx(_merged_macs(out_modes, in_modes, r, T), rel=1e-12)
+    assert m2 == pytest.approx(_sequential_macs(out_modes, in_modes, r, T), rel=1e-12)
+
+
+def test_merged_order_wins_at_large_batch_and_loses_at_batch_one():
+    """Project page, one contraction order for both passes: close to the fewest
+    operations for large batches (Proposition 4.1); at batch 1 the core-by-core
+    sweep is cheaper, so a crossover exists."""
+    d = ttc.make_linear_desc((12, 8, 8), (12, 8, 8), [1, 30, 30, 30, 30, 30, 1], ttc.TTC_F32)
+    for T in (64, 4096, 16384):
+        assert ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_MERGED)[0] < ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_SEQUENTIAL)[0]
+    assert ttc.tt_linear_path_cost(d, 1, ttc.TTC_PATH_SEQUENTIAL)[0] < ttc.tt_linear_path_cost(d, 1, ttc.TTC_PATH_MERGED)[0]
+    assert "path=merged" in ttc.tt_linear_explain(d, 4096)

@@ -1,0 +1,190 @@
+"""GPU parity of the TT-linear forward and backward against the fp64 oracle.
+
+Every case draws seeded inputs (synth), runs the HIP path through the C ABI
+and compares each output tensor with the oracle by relative L2 error
+||gpu - ref|| / ||ref||: at most 1e-5 for fp32 activations, 2e-2 for bf16
+storage with fp32 accumulation.  Gradient slices whose link diagonal entry is
+zero must be exactly 0.0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def _ttc():
+    import tensor_train_compressed_tt_amd as ttc
+    return ttc
+
+
+def _rel(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    nr = np.linalg.norm(ref)
+    if nr == 0.0:
+        return 0.0 if np.all(got == 0) else np.inf
+    return float(np.linalg.norm(got - ref) / nr)
+
+
+def _to_dev(layer, dtype):
+    dev = torch.device("cuda:0")
+    cores = [torch.from_numpy(np.ascontiguousarray(c)).to(dev) for c in layer["cores"]]
+    D = [torch.from_numpy(np.ascontiguousarray(v)).to(dev) for v in layer["D"]]
+    if dtype == "bf16":
+        x = torch.from_numpy(layer["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        dy = torch.from_numpy(layer["dy_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        x = torch.from_numpy(layer["x"]).to(dev)
+        dy = torch.from_numpy(layer["dy"]).to(dev)
+    return cores, D, x, dy
+
+
+def _run(spec, layer, dtype, want_dx=True):
+    ttc = _ttc()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
+    cores, D, x, dy = _to_dev(layer, dtype)
+    y, saved = mod.forward(x, cores, D)
+    dx, dG = mod.backward(x, dy, cores, D, saved, want_dx=want_dx)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    return f(y), (f(dx) if dx is not None else None), [f(g) for g in dG]
+
+
+def _check(spec, layer, dtype, want_dx=True):
+    y, dx, dG = _run(spec, layer, dtype, want_dx)
+    x = layer["x"].astype(np.float64)
+    dy = layer["dy"].astype(np.float64)
+    Yr = oracle.tt_linear_forward(x, spec.out_modes, spec.in_modes, layer["cores"], layer["D"], spec.in_first)
+    dXr, dGr = oracle.tt_linear_backward(x, dy, spec.out_modes, spec.in_modes, layer["cores"], layer["D"],
+                                         spec.in_first)
+    tol = TOL[dtype]
+    errs = {"Y": _rel(y, Yr)}
+    if want_dx:
+        errs["dX"] = _rel(dx, dXr)
+    for k in range(len(dG)):
+        errs[f"dG{k}"] = _rel(dG[k], dGr[k])
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"rel-L2 above {tol}: {bad} (all: {errs})"
+    # dead slices are exactly zero
+    for k, v in enumerate(layer["D"]):
+        dead = np.flatnonzero(v == 0)
+        if dead.size:
+            assert np.all(dG[k][:, :, dead] == 0.0), f"dG{k} dead slice not exactly 0"
+            assert np.all(dG[k + 1][dead, :, :] == 0.0), f"dG{k + 1} dead slice not exactly 0"
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_config0_single_layer(dtype):
+    spec = synth.config_layers(0)[0]
+    layer = synth.make_tt_layer(0, 0, spec, 64, 0.25, dtype)
+    print(_check(spec, layer, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("in_first", [False, True])
+@pytest.mark.parametrize("T", [1, 70, 200])
+def test_tiny_odd_shapes(dtype, in_first, T):
+    spec = synth.LayerSpec("tiny", (2, 3), (3, 2), 3, in_first)
+    layer = synth.make_tt_layer(100, T, spec, T, 0.34, dtype)
+    _check(spec, layer, dtype)
+
+
+@pytest.mark.parametrize("modes", [((5,), (7,)), ((2, 2, 2, 2), (3,)), ((4,), (2, 3, 2, 2, 1))])
+def test_chain_lengths(modes):
+    spec = synth.LayerSpec("chain", modes[0], modes[1], 5)
+    layer = synth.make_tt_layer(101, len(modes[0]) * 10 + len(modes[1]), spec, 130, 0.2, "f32")
+    _check(spec, layer, "f32")
+
+
+@pytest.mark.parametrize("rank", [1, 8, 16, 30, 33, 64, 100, 128])
+def test_rank_range(rank):
+    spec = synth.LayerSpec("r", (4, 6), (6, 4), rank)
+    layer = synth.make_tt_layer(102, rank, spec, 150, 0.3, "f32")
+    _check(spec, layer, "f32")
+
+
+@pytest.mark.parametrize("li", range(6))
+def test_config1_layers_fp32(li):
+    spec = synth.config_layers(1)[li]
+    layer = synth.make_tt_layer(1, li, spec, 333, 0.25, "f32")
+    _check(spec, layer, "f32")
+
+
+@pytest.mark.parametrize("rank", [8, 16, 30, 64])
+@pytest.mark.parametrize("li", [0, 4, 5])
+def test_config2_layers_bf16(rank, li):
+    spec = synth.config_layers(2, rank)[li]
+    layer = synth.make_tt_layer(2, 10 * rank + li, spec, 257, 0.40, "bf16")
+    _check(spec, layer, "bf16")
+
+
+def test_config1_full_tokens_one_layer():
+    spec = synth.config_layers(1)[0]
+    layer = synth.make_tt_layer(1, 0, spec, 4096, 0.25, "f32")
+    print(_check(spec, layer, "f32"))
+
+
+def test_config2_full_tokens_ffn1_r30():
+    spec = synth.config_layers(2, 30)[4]
+    layer = synth.make_tt_layer(2, 4, spec, 16384, 0.40, "bf16")
+    print(_check(spec, layer, "bf16"))
+
+
+def test_skip_dx():
+    spec = synth.config_layers(0)[0]
+    layer = synth.make_tt_layer(0, 1, spec, 100, 0.25, "f32")
+    _check(spec, layer, "f32", want_dx=False)
+
+
+def test_all_zero_link_removes_layer():
+    spec = synth.LayerSpec("dead", (4, 6), (6, 4), 8)
+    layer = synth.make_tt_layer(103, 0, spec, 90, 0.0, "f32")
+    layer["D"][1][:] = 0.0
+    y, dx, dG = _run(spec, layer, "f32")
+    assert np.all(y == 0.0) and np.all(dx == 0.0)
+    # both cores next to the dead link get exactly-zero gradients
+    assert np.all(dG[1] == 0.0) and np.all(dG[2] == 0.0)
+
+
+def test_split_link_all_dead():
+    spec = synth.LayerSpec("deadsplit", (4, 6), (6, 4), 8)
+    layer = synth.make_tt_layer(104, 0, spec, 90, 0.0, "bf16")
+    layer["D"][1][:] = 0.0  # link 2 is the split between output and input modes
+    y, dx, dG = _run(spec, layer, "bf16")
+    assert np.all(y == 0.0) and np.all(dx == 0.0)
+    for g in dG:
+        assert np.all(g == 0.0)
+
+
+def test_zero_tokens():
+    ttc = _ttc()
+    spec = synth.config_layers(0)[0]
+    layer = synth.make_tt_layer(0, 2, spec, 0, 0.25, "f32")
+    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, torch.float32)
+    cores, D, x, dy = _to_dev(layer, "f32")
+    y, saved = mod.forward(x, cores, D)
+    dG = [torch.full(s, 7.0, device="cuda") for s in mod.core_shapes]
+    mod.backward(x, dy, cores, D, saved, dG=dG)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 768)
+    for g in dG:
+        assert torch.all(g == 0.0)
+
+
+def test_bitwise_deterministic():
+    spec = synth.config_layers(2, 30)[5]
+    layer = synth.make_tt_layer(2, 5, spec, 1000, 0.40, "bf16")
+    a = _run(spec, layer, "bf16")
+    b = _run(spec, layer, "bf16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    for g1, g2 in zip(a[2], b[2]):
+        assert np.array_equal(g1, g2)
