@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""TT-linear fwd+bwd throughput on one MI355X.
+
+One step = the forward pass of six TT-linear layers shaped like one encoder of
+the CoMERA pages' six-encoder transformer (Q, K, V, O 768->768 with modes
+(12,8,8)x(12,8,8); FFN 768->3072 and 3072->768 with 3072 = (12,16,16)),
+followed by their backward passes in reverse order (input gradients and core
+gradients), over T = 128 x 128 = 16384 tokens, bf16 activations with fp32
+accumulation, TT rank 30 with 40% of every link diagonal zeroed.  Inputs are
+seeded synthetic data already resident in HBM.
+
+Prints one JSON line (see the design doc for every field).  Only rank 0 of a single
+GPU runs; --gpus above 1 is refused.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TT-linear fwd+bwd tokens/sec at d=768 r=30; achieved HBM GB/s % of peak"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 4])
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="config 4 only: number of encoder layers")
+    ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    return ap.parse_args()
+
+
+def step_bytes(layers, T, es):
+    """Algorithmic HBM bytes of one fwd+bwd per layer (kernel-level split).
+
+    fwd:    read x, write Y, write Z (T x r_eff fp32)
+    bwd_dy: read dY, read Z
+    bwd_dx: read x, write dX
+    """
+    out = []
+    for L in layers:
+        s = L["spec"]
+        r_eff = int((L["D"][len(s.out_modes) - 1 if not s.in_first else len(s.in_modes) - 1] != 0).sum())
+        out.append({
+            "fwd": T * (s.n_in + s.n_out) * es + T * r_eff * 4,
+            "bwd_dy": T * s.n_out * es + T * r_eff * 4,
+            "bwd_dx": T * 2 * s.n_in * es,
+            "r_eff": r_eff,
+        })
+    return out
+
+
+def cpu_baseline(layers_host, T_cpu):
+    """The fp64 oracle, as it stands, on the first T_cpu tokens of every layer."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    for L in layers_host:
+        s = L["spec"]
+        x = L["x"][:T_cpu].astype(np.float64)
+        dy = L["dy"][:T_cpu].astype(np.float64)
+        oracle.tt_linear_forward(x, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
+        oracle.tt_linear_backward(x, dy, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
+    dt = time.perf_counter() - t0
+    return {"value": T_cpu / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd of all {len(layers_host)} layers on the first {T_cpu} tokens "
+                      f"({dt:.1f} s wall)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import tensor_train_compressed_tt_amd as ttc
+
+    cfg = args.config
+    rank = args.rank if args.rank is not None else (64 if cfg == 4 else 30)
+    T = synth.CONFIG_TOKENS[cfg]
+    zf = synth.CONFIG_ZERO_FRAC[cfg]
+    dt = synth.CONFIG_DTYPE[cfg]
+    specs = synth.config_layers(cfg, rank)
+    if cfg == 4 and args.layers is not None:
+        specs = specs[: 6 * args.layers]
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    es = 2 if dt == "bf16" else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM ------------------------------------------------
+    layers, host = [], []
+    max_scratch = 0
+    for li, spec in enumerate(specs):
+        L = synth.make_tt_layer(cfg, li, spec, T, zf, dt)
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
+        cores = [torch.from_numpy(c).to(dev) for c in L["cores"]]
+        D = [torch.from_numpy(v).to(dev) for v in L["D"]]
+        if dt == "bf16":
+            x = torch.from_numpy(L["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+            dy = torch.from_numpy(L["dy_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(L["x"]).to(dev)
+            dy = torch.from_numpy(L["dy"]).to(dev)
+        sb, cb = mod.workspace(T)
+        max_scratch = max(max_scratch, cb)
+        layers.append({
+            "spec": spec, "mod": mod, "cores": cores, "D": D, "x": x, "dy": dy,
+            "y": torch.empty((T, spec.n_out), dtype=tdt, device=dev),
+            "dx": torch.empty((T, spec.n_in), dtype=tdt, device=dev),
+            "dG": [torch.empty(s, dtype=torch.float32, device=dev) for s in mod.core_shapes],
+            "saved": torch.empty(sb, dtype=torch.uint8, device=dev),
+        })
+        keep = {"spec": spec, "cores": L["cores"], "D": L["D"]}
+        if not args.no_cpu_baseline and len(host) < 6:
+            keep["x"] = L["x"][: args.cpu_tokens].copy()
+            keep["dy"] = L["dy"][: args.cpu_tokens].copy()
+        host.append(keep)
+        del L
+    scratch = torch.empty(max_scratch, dtype=torch.uint8, device=dev)
+    sizes = step_bytes(host, T, es)
+
+    def step():
+        for L in layers:
+            L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"])
+        for L in reversed(layers):
+            L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
+                              scratch=scratch)
+
+    # ---- warm-up, optional graph capture --------------------------------------------
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+
+    # ---- timed region -----------------------------------------------------------------
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tokens_per_s = T / (ms_per_step / 1e3)
+    bytes_per_step = sum(s["fwd"] + s["bwd_dy"] + s["bwd_dx"] for s in sizes)
+    step_gbps = bytes_per_step / (ms_per_step / 1e3) / 1e9
+
+    # ---- per-kernel durations: the same steps, launched eagerly with HIP events
+    # recorded by the library around every kernel on its launch stream -----------------
+    ttc.trace_start()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ttc.trace_stop()
+    recs = ttc.trace_records()
+    per = {}
+    # launch order of one step: per layer merge, fwd; then per layer (reversed)
+    # bwd_dy, bwd_dx, reduce, core_step x n
+    expect = []
+    for li in range(len(layers)):
+        expect += [("merge", li), ("fwd", li)]
+    for li in reversed(range(len(layers))):
+        s = layers[li]["spec"]
+        n_sweep = max(len(s.out_modes), len(s.in_modes))
+        expect += [("bwd_dy", li), ("bwd_dx", li), ("reduce", li)] + [("core_step", li)] * n_sweep
+    assert len(recs) == len(expect) * args.steps, (len(recs), len(expect))
+    for i, (name, ms) in enumerate(recs):
+        ename, li = expect[i % len(expect)]
+        assert name == ename, (i, name, ename)
+        d = per.setdefault(name, {"ms": 0.0, "bytes": 0.0, "launches": 0})
+        d["ms"] += ms
+        d["launches"] += 1
+        d["bytes"] += sizes[li].get(name, 0)
+    for d in per.values():
+        d["avg_us"] = 1e3 * d["ms"] / d["launches"]
+        d["gbps"] = d["bytes"] / (d["ms"] / 1e3) / 1e9 if d["bytes"] else None
+        d["ms_per_step"] = d["ms"] / args.steps
+    stream_kernels = ["fwd", "bwd_dy", "bwd_dx"]
+    dom = max(stream_kernels, key=lambda k: per[k]["ms"])
+    roof = {
+        "bound": "hbm",
+        "kernel": dom,
+        "achieved": round(per[dom]["gbps"], 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(per[dom]["gbps"] / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "avg_launch_us": round(per[dom]["avg_us"], 2),
+        "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host[:6], args.cpu_tokens)
+
+    wl = {1: "config 1", 2: "config 2", 4: "config 4"}[cfg]
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl}: {len(specs)} TT-linear layers (fwd then bwd in reverse), "
+                        f"{'4x 768->768, 768->3072, 3072->768' if cfg != 4 else '24x (4x 1024->1024, 1024->4096, 4096->1024)'}, "
+                        f"{dt} activations, fp32 accumulate, T={T} tokens, TT rank {rank}, "
+                        f"{int(zf * 100)}% of each link diagonal zeroed",
+            "tokens": T,
+            "rank": rank,
+            "layers": len(specs),
+            "launch": "eager" if graph is None else "hip_graph_replay",
+        },
+        "hbm_gbps_step": round(step_gbps, 1),
+        "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": bytes_per_step,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in per.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,4 +12,8 @@ from .workloads import (  # noqa: F401
     make_tt_layer,
     make_ttm,
     CONFIG_TOKENS,
+    CONFIG_ZERO_FRAC,
+    CONFIG_DTYPE,
+    make_link_diagonals,
+    zipf_ids,
 )

@@ -45,6 +45,10 @@ EXPORTS = [
     "ttm_embed_bwd",
     "ttc_status_str",
     "ttc_version",
+    "ttc_trace_start",
+    "ttc_trace_stop",
+    "ttc_trace_count",
+    "ttc_trace_get",
 ]
 
 
@@ -113,6 +117,13 @@ def lib() -> ctypes.CDLL:
     L.ttc_status_str.restype = ctypes.c_char_p
     L.ttc_version.argtypes = []
     L.ttc_version.restype = ctypes.c_char_p
+    for name in ("ttc_trace_start", "ttc_trace_stop"):
+        getattr(L, name).argtypes = []
+        getattr(L, name).restype = ctypes.c_int
+    L.ttc_trace_count.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    L.ttc_trace_count.restype = ctypes.c_int
+    L.ttc_trace_get.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+    L.ttc_trace_get.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -215,6 +226,27 @@ def ttm_embed_bwd(desc, T, ids, dout, F, D, saved, saved_bytes, dF, scratch, scr
     code = lib().ttm_embed_bwd(ctypes.byref(desc), T, ids, dout, f, dd, saved, saved_bytes, df, scratch,
                                scratch_bytes, stream)
     _check("ttm_embed_bwd", code)
+
+
+def trace_start():
+    _check("ttc_trace_start", lib().ttc_trace_start())
+
+
+def trace_stop():
+    _check("ttc_trace_stop", lib().ttc_trace_stop())
+
+
+def trace_records():
+    """[(kernel name, milliseconds)] of the launches recorded since trace_start."""
+    n = ctypes.c_int32(0)
+    _check("ttc_trace_count", lib().ttc_trace_count(ctypes.byref(n)))
+    out = []
+    name = ctypes.c_char_p()
+    ms = ctypes.c_float()
+    for i in range(n.value):
+        _check("ttc_trace_get", lib().ttc_trace_get(i, ctypes.byref(name), ctypes.byref(ms)))
+        out.append((name.value.decode(), ms.value))
+    return out
 
 
 def version() -> str:

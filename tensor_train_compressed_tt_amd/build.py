@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libttc.so")
 
-SOURCES = ["tt_plan.cpp", "tt_linear.hip", "ttm_embed.hip"]
+SOURCES = ["tt_plan.cpp", "ttc_trace.cpp", "tt_linear.hip", "ttm_embed.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

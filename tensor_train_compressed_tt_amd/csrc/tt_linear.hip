@@ -36,6 +36,7 @@
 
 #include "tt_plan.hpp"
 #include "ttc_device.hpp"
+#include "ttc_trace.hpp"
 
 namespace ttc {
 
@@ -720,9 +721,14 @@ static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y,
   typedef typename Elem<T>::type E;
   const size_t lds = size_t(4) * 64 * 16 * NR * sizeof(float);
   auto kern = k_fwd<T, NR>;
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static bool lds_set = false;  // set once, before any graph capture can see it
+  if (!lds_set) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    lds_set = true;
+  }
   const int vin = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x);
   const int vout = (P.N_out % 4) == 0 && aligned16(y);
+  TraceScope ts("fwd", st);
   hipLaunchKernelGGL(kern, dim3(P.ntiles), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
                      (const E*)(saved + P.sv_Bc), (float*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, vin,
                      vout);
@@ -733,10 +739,14 @@ static void launch_bwd_main(const LinearPlan& P, const void* x, const void* dy, 
                             char* scratch, hipStream_t st) {
   typedef typename Elem<T>::type E;
   const int vout = (P.N_out % Mma<T>::EPV) == 0 && aligned16(dy);
-  hipLaunchKernelGGL((k_bwd_dy<T, NR>), dim3(P.dy_gc, P.dy_gt), dim3(256), 0, st, (const E*)dy,
+  {
+    TraceScope ts("bwd_dy", st);
+    hipLaunchKernelGGL((k_bwd_dy<T, NR>), dim3(P.dy_gc, P.dy_gt), dim3(256), 0, st, (const E*)dy,
                      (const E*)(saved + P.sv_BcT), (const float*)(saved + P.sv_Z), (float*)(scratch + P.sc_dZp),
                      (float*)(scratch + P.sc_dBp), P.T, P.N_out, P.dy_ncc, P.dy_tpg, P.ntiles, vout);
+  }
   const int vin = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x) && (dx == nullptr || aligned16(dx));
+  TraceScope ts("bwd_dx", st);
   hipLaunchKernelGGL((k_bwd_dx<T, NR>), dim3(P.dx_gc, P.dx_gt), dim3(256), 0, st, (const E*)x,
                      (const E*)(saved + P.sv_AcT), (const float*)(scratch + P.sc_dZp), P.dy_gc,
                      (float*)(scratch + P.sc_dAp), (E*)dx, P.T, P.N_in, P.dx_ncc, P.dx_tpg, P.ntiles, vin);
@@ -820,10 +830,13 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   m.Bc = sv + P.sv_Bc;
   m.BcT = sv + P.sv_BcT;
   m.chain = reinterpret_cast<float*>(sv + P.sv_chain);
-  if (P.act == TTC_BF16)
-    hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(128), 0, s, m);
-  else
-    hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(128), 0, s, m);
+  {
+    TraceScope ts("merge", s);
+    if (P.act == TTC_BF16)
+      hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(128), 0, s, m);
+    else
+      hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(128), 0, s, m);
+  }
   const bool ok = P.act == TTC_BF16 ? dispatch_fwd<bf16_t>(P, x, sv, y, s) : dispatch_fwd<float>(P, x, sv, y, s);
   if (!ok) return TTC_ERR_UNSUPPORTED;
   return hip_status();
@@ -845,6 +858,7 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
   if (T == 0) {
     for (int k = 0; k < P.d; ++k) {
       const int64_t n = (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
+      TraceScope ts("zero", s);
       hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>(1024, (n + 255) / 256)), dim3(256), 0, s, dG[k], n);
     }
     return hip_status();
@@ -862,6 +876,7 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
   {
     const int64_t n = (int64_t)P.rs * (P.N_out + P.N_in);
     const unsigned blocks = (unsigned)std::min<int64_t>(2048, (n + 255) / 256);
+    TraceScope ts("reduce", s);
     hipLaunchKernelGGL(k_reduce, dim3(blocks), dim3(256), 0, s, (const float*)(sc + P.sc_dBp), P.dy_gt,
                        (const float*)(sc + P.sc_dAp), P.dx_gt, (const int*)(sv + P.sv_meta), D[P.s - 1],
                        (float*)(sc + P.sc_dL), (float*)(sc + P.sc_dR), P.N_out, P.N_in, P.rs, P.Rpad, P.in_first);
@@ -904,7 +919,10 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
       if (k < P.d - 1) total += (int64_t)P.ranks[k + 1] * (colsR / P.modes[k]);
     }
     const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(4096, (total + 255) / 256));
-    hipLaunchKernelGGL(k_core_step, dim3(blocks), dim3(256), 0, s, a);
+    {
+      TraceScope ts("core_step", s);
+      hipLaunchKernelGGL(k_core_step, dim3(blocks), dim3(256), 0, s, a);
+    }
     if (a.kL >= 0) {
       curL = a.dMn;
       rowsL /= P.modes[a.kL];
