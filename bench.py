@@ -198,8 +198,11 @@ def main():
         expect += [("merge", li), ("fwd", li)]
     for li in reversed(range(len(layers))):
         s = layers[li]["spec"]
-        n_sweep = max(len(s.out_modes), len(s.in_modes))
-        expect += [("bwd_dy", li), ("bwd_dx", li), ("reduce", li)] + [("core_step", li)] * n_sweep
+        plan = dict(kv.split("=") for kv in ttc.tt_linear_explain(layers[li]["mod"].desc, T).split())
+        ndy = int(plan["dy_grid"].split("x")[0])
+        halves = [len(s.out_modes), len(s.in_modes)]
+        expect += [("bwd_dy", li)] + ([("dz_sum", li)] if ndy > 1 else []) + [("bwd_dx", li), ("reduce", li)]
+        expect += [("core", li)] * (max(halves) - 1)
     assert len(recs) == len(expect) * args.steps, (len(recs), len(expect))
     for i, (name, ms) in enumerate(recs):
         ename, li = expect[i % len(expect)]

@@ -40,7 +40,8 @@
  *     are then exactly those of the smaller chain (dead-slice core gradients
  *     are exactly 0).  D is read on the device at every call.
  *   - Errors are returned synchronously, before anything is enqueued; on a
- *     non-zero status nothing was launched.  T = 0 is a valid no-op.
+ *     non-zero status nothing was launched.  T = 0 is valid: the forward does
+ *     nothing and the backward writes zero core gradients.
  */
 #ifndef TTC_H
 #define TTC_H
@@ -125,6 +126,7 @@ ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const void* x,
  *   dx - T x N_in  (act_dtype), overwritten, or NULL
  *   dG - host array of p+q device pointers, fp32, shapes of the cores,
  *        overwritten
+ * Every reduction runs in a fixed order: results are bitwise reproducible.
  */
 ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const void* x,
                          const void* dy, const float* const* G,

@@ -31,7 +31,7 @@ ttc_status ttc_trace_count(int32_t* n);
 
 /*
  * Record i (0-based, in launch order): the kernel's name (static storage, one
- * of "merge", "fwd", "bwd_dy", "bwd_dx", "reduce", "core_step", "zero",
+ * of "merge", "fwd", "bwd_dy", "dz_sum", "bwd_dx", "reduce", "core", "zero",
  * "ttm_sort", "ttm_rows", "ttm_bwd_seg", "ttm_bwd_core") and its duration in
  * milliseconds.  Waits for the record's end event.
  */

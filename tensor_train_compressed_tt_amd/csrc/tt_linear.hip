@@ -1,4 +1,4 @@
-// TT-linear layer on gfx950: merged-halves contraction order, fused streaming
+// TT-linear layer on gfx950: merged-halves contraction order, streaming
 // kernels with MFMA on the dense (tokens x modes) . (modes x rank) products.
 //
 // Method (CoMERA project page, "Learn the ranks while training" and "Making
@@ -13,22 +13,28 @@
 //             then the core gradients by a reverse sweep through each half.
 // Rank adaptivity: the entries of D_s that are exactly zero are dropped on the
 // device (the live slices are compacted), so the skinny products run over the
-// live rank only; zero entries of the inner links zero their slices by plain
-// multiplication.
+// live rank; zero entries of the inner links zero their slices by plain
+// multiplication, which keeps dead-slice gradients exactly 0.
 //
 // Kernels (one stream, no host synchronisation, no allocation):
-//   k_merge      one work-group per row of a left prefix product / column of
-//                a right suffix product; writes the compacted A, B (and
-//                transposes) in the activation dtype plus the fp32 prefix and
-//                suffix products used by the backward sweep
+//   k_merge      one wave per row of a left prefix product / column of a right
+//                suffix product; writes the compacted A, B (and transposes) in
+//                the activation dtype plus the fp32 prefix / suffix products
+//                the backward sweep needs
 //   k_fwd        per 64-token tile: Z = x A^T with the K range split over the
-//                4 waves, Z summed in LDS and saved, then Y^T = B Z^T
-//   k_bwd_dy     per (column group, token group): dZ partials over its column
-//                range, dB^T partials over its token range, dY read once
-//   k_bwd_dx     per (column group, token group): dZ = sum of partials,
-//                dX^T = A^T dZ^T, dA partials; x read once, dX written once
+//                4 waves (unrolled, many loads in flight), Z summed in LDS and
+//                kept, then Y^T = B Z^T with the B fragments prefetched
+//   k_bwd_dy     per (column group, token group): 64 x 256-byte slabs of dY
+//                stream through LDS with register prefetch; dZ (or its
+//                partials over the column groups), dB^T partials over the
+//                token group
+//   k_dz_sum     sums the dZ partials of the column groups in group order
+//   k_bwd_dx     per (column group, token group): slabs of x stream through
+//                LDS; dX^T = A^T dZ^T written per slab, dA partials
 //   k_reduce     sums the partials into the gradients of the two half products
-//   k_core_step  one step of the reverse sweep on both halves at once
+//   k_sweep      one level of the reverse sweep through both halves: the
+//                small GEMMs of that level as 32 x 32 fp32-MFMA tiles spread
+//                over work-groups (one launch per level)
 #include <stdio.h>
 #include <string.h>
 
@@ -50,7 +56,7 @@ struct ChainPtrs {
 // ------------------------------------------------------------------------------
 struct MergeArgs {
   ChainPtrs c;
-  int d, s, rs, Rpad, in_first;
+  int d, s, rs, Rpad, in_first, max_rank;
   int modes[kMaxCores];
   int ranks[kMaxCores + 1];
   int64_t item_off[kMaxCores + 1];
@@ -64,36 +70,83 @@ struct MergeArgs {
   float* chain;
 };
 
+// core slice G[:, dig, :] (r0 x rn) into LDS, eight independent loads per lane
+// per round
+__device__ __forceinline__ void stage_slice(float* gsl, const float* G, int r0, int rn, int n, int dig, int lane) {
+  const int tot = r0 * rn;
+  for (int e0 = lane; e0 < tot; e0 += 512) {
+    float vals[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 64 * u;
+      const bool ok = e < tot;
+      const int aa = ok ? e / rn : 0, b = ok ? e % rn : 0;
+      vals[u] = G[((int64_t)aa * n + dig) * rn + b];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (e0 + 64 * u < tot) gsl[e0 + 64 * u] = vals[u];
+  }
+}
+
+// sum_i v[i] * m[i * stride] over LDS operands, eight terms per block so the
+// reads of a block are in flight together (fixed order: deterministic)
+__device__ __forceinline__ float dot_col(const float* v, const float* m, int len, int stride) {
+  float acc0 = 0.f, acc1 = 0.f;
+  int i = 0;
+  for (; i + 8 <= len; i += 8) {
+    float a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = v[i + u];
+      b[u] = m[(i + u) * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      acc0 += a[u] * b[u];
+      acc1 += a[u + 1] * b[u + 1];
+    }
+  }
+  for (; i < len; ++i) acc0 += v[i] * m[i * stride];
+  return acc0 + acc1;
+}
+
+// One wave (64 lanes) per item; vectors of length <= 128 live in LDS, each
+// step stages the core slice G_t[:, digit, :] in LDS and does one
+// vector-matrix product.
 template <typename T>
-__global__ __launch_bounds__(128) void k_merge(MergeArgs a) {
+__global__ __launch_bounds__(64) void k_merge(MergeArgs a) {
   typedef typename Elem<T>::type E;
+  extern __shared__ float gsl[];  // max_rank x max_rank core slice
   __shared__ float v[TTC_MAX_RANK];
   __shared__ float w[TTC_MAX_RANK];
   __shared__ int live[TTC_MAX_RANK];
-  __shared__ int reff_s;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int64_t item = blockIdx.x;
   const int d = a.d, s = a.s;
 
   // live entries of the split link's diagonal, in increasing link index
   const float* Ds = a.c.D[s - 1];
-  if (tid == 0) {
-    int cnt = 0;
-    for (int b = 0; b < a.rs; ++b)
-      if (Ds[b] != 0.0f) live[cnt++] = b;
-    reff_s = cnt;
-    for (int j = cnt; j < TTC_MAX_RANK; ++j) live[j] = -1;
-  }
+  const bool f0 = lane < a.rs && Ds[lane] != 0.0f;
+  const bool f1 = lane + 64 < a.rs && Ds[lane + 64] != 0.0f;
+  const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int c0 = __popcll(m0);
+  const int reff = c0 + __popcll(m1);
+  live[lane] = -1;
+  live[lane + 64] = -1;
   __syncthreads();
-  const int reff = reff_s;
+  if (f0) live[__popcll(m0 & below)] = lane;
+  if (f1) live[c0 + __popcll(m1 & below)] = lane + 64;
+  __syncthreads();
   if (item == 0) {
-    for (int j = tid; j < TTC_MAX_RANK; j += blockDim.x) {
+    for (int j = lane; j < TTC_MAX_RANK; j += 64) {
       a.meta[kMetaLive + j] = live[j];
       a.meta[kMetaPos + j] = -1;
     }
     __syncthreads();
-    for (int j = tid; j < reff; j += blockDim.x) a.meta[kMetaPos + live[j]] = j;
-    if (tid == 0) a.meta[kMetaReff] = reff;
+    for (int j = lane; j < reff; j += 64) a.meta[kMetaPos + live[j]] = j;
+    if (lane == 0) a.meta[kMetaReff] = reff;
   }
 
   // which core's item range holds this item
@@ -101,13 +154,13 @@ __global__ __launch_bounds__(128) void k_merge(MergeArgs a) {
   for (int kk = 0; kk < d; ++kk) {
     int64_t hi;
     if (kk < s)
-      hi = (kk + 1 < s) ? a.item_off[kk + 1] : (s < d ? a.item_off[d - 1] : a.item_off[d]);
+      hi = (kk + 1 < s) ? a.item_off[kk + 1] : a.item_off[d - 1];
     else
       hi = (kk - 1 >= s) ? a.item_off[kk - 1] : a.item_off[d];
     if (item >= a.item_off[kk] && item < hi) k = kk;
   }
   if (k < 0) return;
-  int64_t idx = item - a.item_off[k];
+  const int64_t idx = item - a.item_off[k];
 
   if (k < s) {
     // row idx of the prefix product M_k = G_0 D_0 G_1 ... G_k (digits j_0..j_k)
@@ -118,28 +171,27 @@ __global__ __launch_bounds__(128) void k_merge(MergeArgs a) {
       rem /= a.modes[t];
     }
     const int r1 = a.ranks[1];
-    if (tid < r1) v[tid] = a.c.G[0][(int64_t)dig[0] * r1 + tid];
-    __syncthreads();
+    for (int b = lane; b < r1; b += 64) v[b] = a.c.G[0][(int64_t)dig[0] * r1 + b];
     for (int t = 1; t <= k; ++t) {
       const int r0 = a.ranks[t], rn = a.ranks[t + 1], n = a.modes[t];
       const float* G = a.c.G[t];
       const float* D = a.c.D[t - 1];
-      if (tid < rn) {
-        float acc = 0.f;
-        for (int aa = 0; aa < r0; ++aa) acc += (v[aa] * D[aa]) * G[((int64_t)aa * n + dig[t]) * rn + tid];
-        w[tid] = acc;
-      }
+      stage_slice(gsl, G, r0, rn, n, dig[t], lane);
+      for (int aa = lane; aa < r0; aa += 64) v[aa] *= D[aa];
       __syncthreads();
-      if (tid < rn) v[tid] = w[tid];
+      for (int b = lane; b < rn; b += 64) w[b] = dot_col(v, gsl + b, r0, rn);
+      __syncthreads();
+      for (int b = lane; b < rn; b += 64) v[b] = w[b];
       __syncthreads();
     }
+    __syncthreads();
     const int rk = a.ranks[k + 1];
     if (k < s - 1) {
-      if (tid < rk) a.chain[a.chain_off[k] + idx * rk + tid] = v[tid];
+      for (int b = lane; b < rk; b += 64) a.chain[a.chain_off[k] + idx * rk + b] = v[b];
       return;
     }
     // a row of L (length rs)
-    for (int j = tid; j < a.Rpad; j += blockDim.x) {
+    for (int j = lane; j < a.Rpad; j += 64) {
       const int b = j < reff ? live[j] : -1;
       if (!a.in_first) {  // B row idx
         const E val = (E)Mma<T>::from_f32(b >= 0 ? v[b] : 0.f);
@@ -160,31 +212,29 @@ __global__ __launch_bounds__(128) void k_merge(MergeArgs a) {
       rem /= a.modes[t];
     }
     const int rl = a.ranks[d - 1];
-    if (tid < rl) v[tid] = a.c.G[d - 1][(int64_t)tid * a.modes[d - 1] + dig[d - 1]];
-    __syncthreads();
+    for (int b = lane; b < rl; b += 64) v[b] = a.c.G[d - 1][(int64_t)b * a.modes[d - 1] + dig[d - 1]];
     for (int t = d - 2; t >= k; --t) {
       const int r0 = a.ranks[t], rn = a.ranks[t + 1], n = a.modes[t];
       const float* G = a.c.G[t];
       const float* D = a.c.D[t];
-      if (tid < r0) {
-        const float* row = G + ((int64_t)tid * n + dig[t]) * rn;
-        float acc = 0.f;
-        for (int b = 0; b < rn; ++b) acc += row[b] * (D[b] * v[b]);
-        w[tid] = acc;
-      }
+      stage_slice(gsl, G, r0, rn, n, dig[t], lane);
+      for (int b = lane; b < rn; b += 64) v[b] *= D[b];
       __syncthreads();
-      if (tid < r0) v[tid] = w[tid];
+      for (int aa = lane; aa < r0; aa += 64) w[aa] = dot_col(v, gsl + aa * rn, rn, 1);
+      __syncthreads();
+      for (int aa = lane; aa < r0; aa += 64) v[aa] = w[aa];
       __syncthreads();
     }
+    __syncthreads();
     const int rk = a.ranks[k];
     if (k > s) {
       int64_t cols = 1;
       for (int t = k; t < d; ++t) cols *= a.modes[t];
-      if (tid < rk) a.chain[a.chain_off[k] + (int64_t)tid * cols + idx] = v[tid];
+      for (int b = lane; b < rk; b += 64) a.chain[a.chain_off[k] + (int64_t)b * cols + idx] = v[b];
       return;
     }
     // a column of R (length rs)
-    for (int j = tid; j < a.Rpad; j += blockDim.x) {
+    for (int j = lane; j < a.Rpad; j += 64) {
       const int b = j < reff ? live[j] : -1;
       if (!a.in_first) {  // A column idx
         const E val = (E)Mma<T>::from_f32(b >= 0 ? Ds[b] * v[b] : 0.f);
@@ -200,24 +250,8 @@ __global__ __launch_bounds__(128) void k_merge(MergeArgs a) {
 }
 
 // ------------------------------------------------------------------------------
-// shared tile helpers
+// shared helpers of the streaming kernels
 // ------------------------------------------------------------------------------
-// 64 x 64 tile of a row-major matrix into LDS (leading dimension LD), zeros
-// outside [0,nrows) x [0,ncols).
-template <typename T, int LD>
-__device__ __forceinline__ void load_tile64(typename Elem<T>::type* lds, const typename Elem<T>::type* src,
-                                            int64_t r0, int64_t nrows, int64_t c0, int64_t ncols, int64_t ld,
-                                            bool vec) {
-  typedef typename Mma<T>::frag frag;
-  constexpr int EPV = Mma<T>::EPV;
-  constexpr int PER_ROW = 64 / EPV;  // 16-byte groups per row
-  for (int i = threadIdx.x; i < 64 * PER_ROW; i += 256) {
-    const int rr = i / PER_ROW, pp = i % PER_ROW;
-    frag f = load_frag<T>(src, r0 + rr, nrows, c0 + pp * EPV, ncols, ld, vec);
-    *reinterpret_cast<frag*>(lds + rr * LD + pp * EPV) = f;
-  }
-}
-
 // store 4 consecutive values of one row; `vec` says the 4-element group is
 // aligned and fully in range
 template <typename T>
@@ -241,25 +275,98 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v, int valid, bool
   }
 }
 
-template <int NR>
-struct BwdShape {
-  static constexpr int CWC = (16 / NR) > 8 ? 8 : ((16 / NR) < 1 ? 1 : 16 / NR);
+// Geometry shared by the two backward passes for activation type T and NR
+// rank tiles of 16.
+template <typename T, int NR>
+struct Bwd {
+  typedef typename Elem<T>::type E;
+  static constexpr int ES = sizeof(E);
+  static constexpr int EPV = Mma<T>::EPV;
+  static constexpr int KSTEP = Mma<T>::KSTEP;
+  static constexpr int Rpad = 16 * NR;
+  static constexpr int SW = 256 / ES;        // slab columns
+  static constexpr int SLD = SW + 16 / ES;   // slab row stride (elements), 16-byte pad
+  static constexpr int CTW = SW / 64;        // 16-column tiles per wave per slab
+  static constexpr int ZLD = 64 + 16 / ES;   // row stride of a rank-major 64-token tile
+  static constexpr int RLD = Rpad + 16 / ES; // row stride of a token-major rank tile
+  static constexpr int SLAB = 64 * SLD;      // elements of one slab buffer
+  static constexpr int PER = 4;              // 16-byte slab groups per thread
+  static constexpr int ZG = Rpad * ES / 16;  // 16-byte groups per row of a rank tile
+  static constexpr int ZPER = (64 * ZG + 255) / 256;
 };
+
+// prefetch one 64 x SW slab of a row-major matrix into registers
+template <typename T, int NR, bool VEC>
+__device__ __forceinline__ void slab_fetch(typename Mma<T>::frag* r, const typename Elem<T>::type* src,
+                                           int64_t t0, int64_t T_, int64_t c0, int64_t ncols) {
+  typedef Bwd<T, NR> B;
+#pragma unroll
+  for (int q = 0; q < B::PER; ++q) {
+    const int gi = threadIdx.x + 256 * q;
+    const int row = gi >> 4, part = gi & 15;
+    r[q] = ld_frag<T, VEC>(src, t0 + row, T_, c0 + part * B::EPV, ncols, ncols);
+  }
+}
+
+template <typename T, int NR>
+__device__ __forceinline__ void slab_store(typename Elem<T>::type* lds, const typename Mma<T>::frag* r) {
+  typedef Bwd<T, NR> B;
+#pragma unroll
+  for (int q = 0; q < B::PER; ++q) {
+    const int gi = threadIdx.x + 256 * q;
+    const int row = gi >> 4, part = gi & 15;
+    *reinterpret_cast<typename Mma<T>::frag*>(lds + row * B::SLD + part * B::EPV) = r[q];
+  }
+}
+
+// prefetch a 64-token x Rpad tile (row-major, act dtype) into registers
+template <typename T, int NR>
+__device__ __forceinline__ void rank_fetch(typename Mma<T>::frag* r, const typename Elem<T>::type* src,
+                                           int64_t t0, int64_t T_) {
+  typedef Bwd<T, NR> B;
+#pragma unroll
+  for (int q = 0; q < B::ZPER; ++q) {
+    const int gi = threadIdx.x + 256 * q;
+    const int row = gi / B::ZG, part = gi % B::ZG;
+    r[q] = load_frag_v<T>(src, gi < 64 * B::ZG ? t0 + row : T_, T_, part * B::EPV, B::Rpad, B::Rpad);
+  }
+}
+
+// write a prefetched rank tile rank-major (transposed) and optionally token-major
+template <typename T, int NR>
+__device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename Elem<T>::type* rm,
+                                           const typename Mma<T>::frag* r) {
+  typedef Bwd<T, NR> B;
+#pragma unroll
+  for (int q = 0; q < B::ZPER; ++q) {
+    const int gi = threadIdx.x + 256 * q;
+    if (gi < 64 * B::ZG) {
+      const int row = gi / B::ZG, part = gi % B::ZG;
+#pragma unroll
+      for (int e = 0; e < B::EPV; ++e) tr[(part * B::EPV + e) * B::ZLD + row] = r[q][e];
+      if (rm) *reinterpret_cast<typename Mma<T>::frag*>(rm + row * B::RLD + part * B::EPV) = r[q];
+    }
+  }
+}
 
 // ------------------------------------------------------------------------------
 // forward
 // ------------------------------------------------------------------------------
-template <typename T, int NR>
+template <typename T, int NR, bool VEC>
 __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __restrict__ x,
                                              const typename Elem<T>::type* __restrict__ Ac,
                                              const typename Elem<T>::type* __restrict__ Bc,
-                                             float* __restrict__ Z, typename Elem<T>::type* __restrict__ y,
-                                             int64_t T_, int64_t N_in, int64_t N_out, int vin, int vout) {
+                                             typename Elem<T>::type* __restrict__ Z,
+                                             typename Elem<T>::type* __restrict__ y, int64_t T_, int64_t N_in,
+                                             int64_t N_out, int vin, int vout) {
   typedef typename Elem<T>::type E;
   typedef typename Mma<T>::frag frag;
   constexpr int Rpad = 16 * NR;
   constexpr int EPV = Mma<T>::EPV, KSTEP = Mma<T>::KSTEP;
-  constexpr int ZLD = Rpad + 8;
+  constexpr int ZLD = Rpad + 16 / (int)sizeof(E);
+  constexpr int UNR = NR <= 2 ? 4 : (NR <= 4 ? 2 : 1);  // k-steps per batch of loads
+  constexpr int KS = Rpad / KSTEP;
+  constexpr int UO = 4;                                  // output tiles per batch
   extern __shared__ __align__(16) char smem[];
   float* zred = reinterpret_cast<float*>(smem);  // [4 waves][64 tokens][Rpad]
   E* zl = reinterpret_cast<E*>(smem);            // [64][ZLD], reuses zred after the sum
@@ -274,18 +381,25 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
 #pragma unroll
     for (int n = 0; n < NR; ++n) acc[u][n] = zero4();
 
+  // Z = x A^T: M = token, N = rank, K = input column; wave w takes the
+  // k-steps w, w+4, ... so the four waves read adjacent 64-byte pieces
   const int nks = (int)((N_in + KSTEP - 1) / KSTEP);
-  for (int ks = w; ks < nks; ks += 4) {
-    const int64_t col = (int64_t)ks * KSTEP + g * EPV;
-    frag fa[4], fb[NR];
+  for (int kb = 0; kb < nks; kb += 4 * UNR) {
+    frag fa[UNR][4], fb[UNR][NR];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fa[u] = load_frag<T>(x, t0 + 16 * u + c, T_, col, N_in, N_in, vin);
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t col = (int64_t)(kb + 4 * u + w) * KSTEP + g * EPV;
 #pragma unroll
-    for (int n = 0; n < NR; ++n) fb[n] = load_frag<T>(Ac, 16 * n + c, Rpad, col, N_in, N_in, vin);
+      for (int tt = 0; tt < 4; ++tt) fa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int n = 0; n < NR; ++n) fb[u][n] = ld_frag<T, VEC>(Ac, 16 * n + c, Rpad, col, N_in, N_in);
+    }
 #pragma unroll
-      for (int n = 0; n < NR; ++n) acc[u][n] = Mma<T>::mma(fa[u], fb[n], acc[u][n]);
+    for (int u = 0; u < UNR; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) acc[tt][n] = Mma<T>::mma(fa[u][tt], fb[u][n], acc[tt][n]);
   }
   // lane (g, c) holds Z rows 4g+v of token tile u, rank column 16n+c
 #pragma unroll
@@ -307,33 +421,41 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   for (int i = 0; i < PER; ++i) {
     const int idx = threadIdx.x + 256 * i;
     const int tt = idx / Rpad, j = idx % Rpad;
-    if (t0 + tt < T_) Z[(t0 + tt) * Rpad + j] = zs[i];
-    zl[tt * ZLD + j] = (E)Mma<T>::from_f32(zs[i]);
+    const E e = (E)Mma<T>::from_f32(zs[i]);
+    if (t0 + tt < T_) Z[(t0 + tt) * Rpad + j] = e;
+    zl[tt * ZLD + j] = e;
   }
   __syncthreads();
 
   // Y^T = B Z^T: M = output column, N = token, K = rank
   const int not_ = (int)((N_out + 15) / 16);
-  for (int ot = w; ot < not_; ot += 4) {
-    f32x4 acc2[4];
+  for (int ob = w; ob < not_; ob += 4 * UO) {
+    frag fa[UO][KS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc2[u] = zero4();
+    for (int uo = 0; uo < UO; ++uo)
 #pragma unroll
-    for (int ks = 0; ks < Rpad / KSTEP; ++ks) {
-      const int kc = ks * KSTEP + g * EPV;
-      const frag fa = load_frag<T>(Bc, (int64_t)ot * 16 + c, N_out, kc, Rpad, Rpad, true);
+      for (int ks = 0; ks < KS; ++ks)
+        fa[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + 4 * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const frag fz = lds_frag<T>(zl + (16 * u + c) * ZLD + kc);
-        acc2[u] = Mma<T>::mma(fa, fz, acc2[u]);
+    for (int uo = 0; uo < UO; ++uo) {
+      const int ot = ob + 4 * uo;
+      if (ot < not_) {
+        f32x4 acc2[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc2[u] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc2[u] = Mma<T>::mma(fa[uo][ks], lds_frag<T>(zl + (16 * u + c) * ZLD + ks * KSTEP + g * EPV), acc2[u]);
+        const int64_t o0 = (int64_t)ot * 16 + 4 * g;
+        const int valid = (int)std::min<int64_t>(4, N_out - o0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t t = t0 + 16 * u + c;
+          if (t < T_ && valid > 0) store4<T>(y + t * N_out + o0, acc2[u], valid, vout);
+        }
       }
-    }
-    const int64_t o0 = (int64_t)ot * 16 + 4 * g;
-    const int valid = (int)std::min<int64_t>(4, N_out - o0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t t = t0 + 16 * u + c;
-      if (t < T_ && valid > 0) store4<T>(y + t * N_out + o0, acc2[u], valid, vout);
     }
   }
 }
@@ -341,197 +463,307 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
 // ------------------------------------------------------------------------------
 // backward, dY pass
 // ------------------------------------------------------------------------------
-template <typename T, int NR>
-__global__ __launch_bounds__(256) void k_bwd_dy(const typename Elem<T>::type* __restrict__ dy,
-                                                const typename Elem<T>::type* __restrict__ BcT,
-                                                const float* __restrict__ Z, float* __restrict__ dZp,
-                                                float* __restrict__ dBp, int64_t T_, int64_t N_out, int ncc,
-                                                int tpg, int ntiles, int vout) {
-  typedef typename Elem<T>::type E;
-  typedef typename Mma<T>::frag frag;
-  constexpr int Rpad = 16 * NR;
-  constexpr int CWC = BwdShape<NR>::CWC;
-  constexpr int EPV = Mma<T>::EPV, KSTEP = Mma<T>::KSTEP;
-  constexpr int LD = 64 + 8;
-  __shared__ __align__(16) E dyl[64 * LD];
-  __shared__ __align__(16) E ztl[Rpad * LD];
+template <typename T>
+struct DyArgs {
+  const typename Elem<T>::type* dy;
+  const typename Elem<T>::type* BcT;  // Rpad x N_out
+  const typename Elem<T>::type* Z;    // T x Rpad
+  float* dZp;                         // gc x T x Rpad partials (gc > 1)
+  typename Elem<T>::type* dZ;         // T x Rpad
+  float* dBp;                         // gt x Rpad x N_out partials (rows < r_eff)
+  const int* meta;
+  int64_t T_, N_out;
+  int nsl, tpg, ntiles, gc_n, vec;
+};
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+template <typename T, int NR, bool VEC>
+__global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
+  typedef Bwd<T, NR> B;
+  typedef typename B::E E;
+  typedef typename Mma<T>::frag frag;
+  constexpr int NSM = bwd_max_slabs(B::ES, NR);
+  constexpr int BLD = NSM * B::SW + 16 / B::ES;
+  extern __shared__ __align__(16) char smem[];
+  E* btl = reinterpret_cast<E*>(smem);            // [Rpad][BLD]: B^T for the column range
+  E* slab = btl + B::Rpad * BLD;                  // [2][64][SLD]
+  E* ztl = slab + 2 * B::SLAB;                    // [Rpad][ZLD]: Z^T of the current tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int gc = blockIdx.x, gt = blockIdx.y;
-  const int64_t col_lo = (int64_t)gc * ncc * 64;
+  const int64_t c0 = (int64_t)gc * a.nsl * B::SW;
+  const int nsl = (int)std::min<int64_t>(a.nsl, (a.N_out - c0 + B::SW - 1) / B::SW);
+  const int reff = a.meta[kMetaReff];
 
-  f32x4 accB[CWC][NR];
-#pragma unroll
-  for (int cc = 0; cc < CWC; ++cc)
-#pragma unroll
-    for (int n = 0; n < NR; ++n) accB[cc][n] = zero4();
-
-  const int tt_lo = gt * tpg;
-  const int tt_hi = min(ntiles, tt_lo + tpg);
-  for (int tt = tt_lo; tt < tt_hi; ++tt) {
-    const int64_t t0 = (int64_t)tt * 64;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * Rpad; idx += 256) {
-      const int tl = idx / Rpad, j = idx % Rpad;
-      const float z = (t0 + tl < T_) ? Z[(t0 + tl) * Rpad + j] : 0.f;
-      ztl[j * LD + tl] = (E)Mma<T>::from_f32(z);
+  // B^T rows for this column range
+  {
+    const int gpr = nsl * B::SW / B::EPV;
+    for (int gi = tid; gi < B::Rpad * gpr; gi += 256) {
+      const int j = gi / gpr, part = gi % gpr;
+      *reinterpret_cast<frag*>(btl + j * BLD + part * B::EPV) =
+          ld_frag<T, VEC>(a.BcT, j, B::Rpad, c0 + part * B::EPV, a.N_out, a.N_out);
     }
-    f32x4 accZ[NR];
-#pragma unroll
-    for (int n = 0; n < NR; ++n) accZ[n] = zero4();
-#pragma unroll
-    for (int cc = 0; cc < CWC; ++cc) {
-      const int64_t ob = col_lo + cc * 64;
-      if (cc < ncc && ob < N_out) {
-        if (cc > 0) __syncthreads();
-        load_tile64<T, LD>(dyl, dy, t0, T_, ob, N_out, N_out, vout);
-        __syncthreads();
-        // dZ: M = token (tile w), N = rank, K = column
-#pragma unroll
-        for (int ks = 0; ks < 64 / KSTEP; ++ks) {
-          const int kc = ks * KSTEP + g * EPV;
-          const frag fa = lds_frag<T>(dyl + (16 * w + c) * LD + kc);
-#pragma unroll
-          for (int n = 0; n < NR; ++n) {
-            const frag fb = load_frag<T>(BcT, 16 * n + c, Rpad, ob + kc, N_out, N_out, vout);
-            accZ[n] = Mma<T>::mma(fa, fb, accZ[n]);
-          }
-        }
-        // dB^T: M = rank, N = column (tile w of the chunk), K = token
-#pragma unroll
-        for (int ks = 0; ks < 64 / KSTEP; ++ks) {
-          const int kt = ks * KSTEP + g * EPV;
-          const frag fb = lds_col_frag<T>(dyl + kt * LD + 16 * w + c, LD);
-#pragma unroll
-          for (int n = 0; n < NR; ++n) {
-            const frag fa = lds_frag<T>(ztl + (16 * n + c) * LD + kt);
-            accB[cc][n] = Mma<T>::mma(fa, fb, accB[cc][n]);
-          }
-        }
-      }
-    }
-    // dZ partial of this column group: tokens t0+16w+4g+v, rank 16n+c
-#pragma unroll
-    for (int n = 0; n < NR; ++n)
-#pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int64_t t = t0 + 16 * w + 4 * g + vv;
-        if (t < T_) dZp[((int64_t)gc * T_ + t) * Rpad + 16 * n + c] = accZ[n][vv];
-      }
   }
-  // dB^T partial of this token group: rank 16n+4g+v, column ob+16w+c
+
+  f32x4 accB[NSM][B::CTW][NR];
 #pragma unroll
-  for (int cc = 0; cc < CWC; ++cc) {
-    const int64_t o = col_lo + cc * 64 + 16 * w + c;
-    if (cc < ncc && o < N_out) {
+  for (int s = 0; s < NSM; ++s)
+#pragma unroll
+    for (int ct = 0; ct < B::CTW; ++ct)
+#pragma unroll
+      for (int n = 0; n < NR; ++n) accB[s][ct][n] = zero4();
+  f32x4 accZ[NR];
+
+  const int tt0 = gt * a.tpg;
+  const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
+  const int nitems = ntt * nsl;
+  frag sr[B::PER], zr[B::ZPER];
+  if (nitems > 0) {
+    slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tt0 * 64, a.T_, c0, a.N_out);
+    rank_fetch<T, NR>(zr, a.Z, (int64_t)tt0 * 64, a.T_);
+  }
+  int buf = 0;
+  for (int it = 0; it < nitems; ++it) {
+    const int tt = tt0 + it / nsl, sb = it % nsl;
+    const int64_t t0 = (int64_t)tt * 64;
+    if (sb == 0) {
+      __syncthreads();  // readers of the previous tile's Z^T are done
+      rank_store<T, NR>(ztl, nullptr, zr);
+#pragma unroll
+      for (int n = 0; n < NR; ++n) accZ[n] = zero4();
+    }
+    E* sl = slab + buf * B::SLAB;
+    slab_store<T, NR>(sl, sr);
+    if (it + 1 < nitems) {
+      const int tn = tt0 + (it + 1) / nsl, sn = (it + 1) % nsl;
+      slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_out);
+      if (sn == 0) rank_fetch<T, NR>(zr, a.Z, (int64_t)tn * 64, a.T_);
+    }
+    __syncthreads();
+    // dZ: M = token (16-row tile w), N = rank, K = column of the slab
+#pragma unroll
+    for (int ks = 0; ks < B::SW / B::KSTEP; ++ks) {
+      const int kc = ks * B::KSTEP + g * B::EPV;
+      const frag fa = lds_frag<T>(sl + (16 * w + c) * B::SLD + kc);
 #pragma unroll
       for (int n = 0; n < NR; ++n)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
-          dBp[((int64_t)gt * Rpad + 16 * n + 4 * g + vv) * N_out + o] = accB[cc][n][vv];
+        accZ[n] = Mma<T>::mma(fa, lds_frag<T>(btl + (16 * n + c) * BLD + sb * B::SW + kc), accZ[n]);
     }
+    // dB^T: M = rank, N = column (tiles ct*4+w of the slab), K = token
+#pragma unroll
+    for (int s = 0; s < NSM; ++s) {
+      if (s == sb) {
+#pragma unroll
+        for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
+          const int kt = ks * B::KSTEP + g * B::EPV;
+          frag fb[B::CTW];
+#pragma unroll
+          for (int ct = 0; ct < B::CTW; ++ct)
+            fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
+#pragma unroll
+          for (int n = 0; n < NR; ++n) {
+            const frag fa = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
+#pragma unroll
+            for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fa, fb[ct], accB[s][ct][n]);
+          }
+        }
+      }
+    }
+    if (sb == nsl - 1) {
+      // tokens t0+16w+4g+v, rank column 16n+c
+      if (a.gc_n == 1) {
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const int64_t t = t0 + 16 * w + 4 * g + vv;
+            if (t < a.T_) a.dZ[t * B::Rpad + 16 * n + c] = (E)Mma<T>::from_f32(accZ[n][vv]);
+          }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const int64_t t = t0 + 16 * w + 4 * g + vv;
+            if (t < a.T_) a.dZp[((int64_t)gc * a.T_ + t) * B::Rpad + 16 * n + c] = accZ[n][vv];
+          }
+      }
+    }
+    buf ^= 1;
+  }
+  // dB^T partial of this token group: rank 16n+4g+v, column c0+s*SW+(ct*4+w)*16+c
+#pragma unroll
+  for (int s = 0; s < NSM; ++s) {
+    if (s < nsl) {
+#pragma unroll
+      for (int ct = 0; ct < B::CTW; ++ct) {
+        const int64_t o = c0 + (int64_t)s * B::SW + (ct * 4 + w) * 16 + c;
+        if (o < a.N_out) {
+#pragma unroll
+          for (int n = 0; n < NR; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+              const int j = 16 * n + 4 * g + vv;
+              if (j < reff) a.dBp[((int64_t)gt * B::Rpad + j) * a.N_out + o] = accB[s][ct][n][vv];
+            }
+        }
+      }
+    }
+  }
+}
+
+// dZ = sum of the column groups' partials, in group order (deterministic)
+template <typename T>
+__global__ __launch_bounds__(256) void k_dz_sum(const float* __restrict__ dZp, typename Elem<T>::type* __restrict__ dZ,
+                                                int ngc, int64_t n4) {
+  typedef typename Elem<T>::type E;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    f32x4 sum = zero4();
+    for (int q = 0; q < ngc; ++q) sum += *reinterpret_cast<const f32x4*>(dZp + ((int64_t)q * n4 + i) * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dZ[i * 4 + e] = (E)Mma<T>::from_f32(sum[e]);
   }
 }
 
 // ------------------------------------------------------------------------------
 // backward, dX pass
 // ------------------------------------------------------------------------------
-template <typename T, int NR>
-__global__ __launch_bounds__(256) void k_bwd_dx(const typename Elem<T>::type* __restrict__ x,
-                                                const typename Elem<T>::type* __restrict__ AcT,
-                                                const float* __restrict__ dZp, int ngc, float* __restrict__ dAp,
-                                                typename Elem<T>::type* __restrict__ dx, int64_t T_, int64_t N_in,
-                                                int ncc, int tpg, int ntiles, int vin) {
-  typedef typename Elem<T>::type E;
-  typedef typename Mma<T>::frag frag;
-  constexpr int Rpad = 16 * NR;
-  constexpr int CWC = BwdShape<NR>::CWC;
-  constexpr int EPV = Mma<T>::EPV, KSTEP = Mma<T>::KSTEP;
-  constexpr int LD = 64 + 8;
-  constexpr int ZLD = Rpad + 8;
-  __shared__ __align__(16) E xl[64 * LD];
-  __shared__ __align__(16) E dzl[64 * ZLD];
-  __shared__ __align__(16) E dztl[Rpad * LD];
+template <typename T>
+struct DxArgs {
+  const typename Elem<T>::type* x;
+  const typename Elem<T>::type* AcT;  // N_in x Rpad
+  const typename Elem<T>::type* dZ;   // T x Rpad
+  float* dAp;                         // gt x Rpad x N_in partials (rows < r_eff)
+  typename Elem<T>::type* dx;         // T x N_in or null
+  const int* meta;
+  int64_t T_, N_in;
+  int nsl, tpg, ntiles, vec;
+};
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+template <typename T, int NR, bool VEC>
+__global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
+  typedef Bwd<T, NR> B;
+  typedef typename B::E E;
+  typedef typename Mma<T>::frag frag;
+  constexpr int NSM = dx_max_slabs(B::ES, NR);
+  extern __shared__ __align__(16) char smem[];
+  E* atl = reinterpret_cast<E*>(smem);            // [NSM*SW][RLD]: A^T rows of the column range
+  E* slab = atl + NSM * B::SW * B::RLD;           // [2][64][SLD]
+  E* dzl = slab + 2 * B::SLAB;                    // [64][RLD]: dZ, token-major
+  E* dztl = dzl + 64 * B::RLD;                    // [Rpad][ZLD]: dZ^T
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int gc = blockIdx.x, gt = blockIdx.y;
-  const int64_t col_lo = (int64_t)gc * ncc * 64;
+  const int64_t c0 = (int64_t)gc * a.nsl * B::SW;
+  const int nsl = (int)std::min<int64_t>(a.nsl, (a.N_in - c0 + B::SW - 1) / B::SW);
+  const int reff = a.meta[kMetaReff];
 
-  f32x4 accA[CWC][NR];
-#pragma unroll
-  for (int cc = 0; cc < CWC; ++cc)
-#pragma unroll
-    for (int n = 0; n < NR; ++n) accA[cc][n] = zero4();
-
-  const int tt_lo = gt * tpg;
-  const int tt_hi = min(ntiles, tt_lo + tpg);
-  for (int tt = tt_lo; tt < tt_hi; ++tt) {
-    const int64_t t0 = (int64_t)tt * 64;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * Rpad; idx += 256) {
-      const int tl = idx / Rpad, j = idx % Rpad;
-      float z = 0.f;
-      if (t0 + tl < T_)
-        for (int q = 0; q < ngc; ++q) z += dZp[((int64_t)q * T_ + t0 + tl) * Rpad + j];
-      const E e = (E)Mma<T>::from_f32(z);
-      dzl[tl * ZLD + j] = e;
-      dztl[j * LD + tl] = e;
+  {
+    constexpr int gpr = B::Rpad / B::EPV;
+    for (int gi = tid; gi < nsl * B::SW * gpr; gi += 256) {
+      const int i = gi / gpr, part = gi % gpr;
+      *reinterpret_cast<frag*>(atl + i * B::RLD + part * B::EPV) =
+          load_frag_v<T>(a.AcT, c0 + i, a.N_in, part * B::EPV, B::Rpad, B::Rpad);
     }
+  }
+
+  f32x4 accA[NSM][B::CTW][NR];
 #pragma unroll
-    for (int cc = 0; cc < CWC; ++cc) {
-      const int64_t ib = col_lo + cc * 64;
-      if (cc < ncc && ib < N_in) {
-        if (cc > 0) __syncthreads();
-        load_tile64<T, LD>(xl, x, t0, T_, ib, N_in, N_in, vin);
-        __syncthreads();
-        if (dx) {
-          // dX^T = A^T dZ^T: M = input column (tile w), N = token, K = rank
-          f32x4 accX[4];
+  for (int s = 0; s < NSM; ++s)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) accX[u] = zero4();
+    for (int ct = 0; ct < B::CTW; ++ct)
 #pragma unroll
-          for (int ks = 0; ks < Rpad / KSTEP; ++ks) {
-            const int kc = ks * KSTEP + g * EPV;
-            const frag fa = load_frag<T>(AcT, ib + 16 * w + c, N_in, kc, Rpad, Rpad, true);
+      for (int n = 0; n < NR; ++n) accA[s][ct][n] = zero4();
+
+  const int tt0 = gt * a.tpg;
+  const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
+  const int nitems = ntt * nsl;
+  frag sr[B::PER], zr[B::ZPER];
+  if (nitems > 0) {
+    slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tt0 * 64, a.T_, c0, a.N_in);
+    rank_fetch<T, NR>(zr, a.dZ, (int64_t)tt0 * 64, a.T_);
+  }
+  int buf = 0;
+  for (int it = 0; it < nitems; ++it) {
+    const int tt = tt0 + it / nsl, sb = it % nsl;
+    const int64_t t0 = (int64_t)tt * 64;
+    if (sb == 0) {
+      __syncthreads();
+      rank_store<T, NR>(dztl, dzl, zr);
+    }
+    E* sl = slab + buf * B::SLAB;
+    slab_store<T, NR>(sl, sr);
+    if (it + 1 < nitems) {
+      const int tn = tt0 + (it + 1) / nsl, sn = (it + 1) % nsl;
+      slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_in);
+      if (sn == 0) rank_fetch<T, NR>(zr, a.dZ, (int64_t)tn * 64, a.T_);
+    }
+    __syncthreads();
+    if (a.dx) {
+      // dX^T = A^T dZ^T: M = input column (tiles ct*4+w of the slab), N = token, K = rank
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const frag fz = lds_frag<T>(dzl + (16 * u + c) * ZLD + kc);
-              accX[u] = Mma<T>::mma(fa, fz, accX[u]);
-            }
-          }
-          const int64_t i0 = ib + 16 * w + 4 * g;
-          const int valid = (int)std::min<int64_t>(4, N_in - i0);
+      for (int ct = 0; ct < B::CTW; ++ct) {
+        const int colt = (ct * 4 + w) * 16;
+        f32x4 accX[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int64_t t = t0 + 16 * u + c;
-            if (t < T_ && valid > 0) store4<T>(dx + t * N_in + i0, accX[u], valid, vin);
-          }
+        for (int u = 0; u < 4; ++u) accX[u] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < B::Rpad / B::KSTEP; ++ks) {
+          const int kc = ks * B::KSTEP + g * B::EPV;
+          const frag fa = lds_frag<T>(atl + (sb * B::SW + colt + c) * B::RLD + kc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) accX[u] = Mma<T>::mma(fa, lds_frag<T>(dzl + (16 * u + c) * B::RLD + kc), accX[u]);
         }
-        // dA: M = rank, N = input column (tile w of the chunk), K = token
+        const int64_t i0 = c0 + (int64_t)sb * B::SW + colt + 4 * g;
+        const int valid = (int)std::min<int64_t>(4, a.N_in - i0);
 #pragma unroll
-        for (int ks = 0; ks < 64 / KSTEP; ++ks) {
-          const int kt = ks * KSTEP + g * EPV;
-          const frag fb = lds_col_frag<T>(xl + kt * LD + 16 * w + c, LD);
+        for (int u = 0; u < 4; ++u) {
+          const int64_t t = t0 + 16 * u + c;
+          if (t < a.T_ && valid > 0) store4<T>(a.dx + t * a.N_in + i0, accX[u], valid, VEC);
+        }
+      }
+    }
+    // dA: M = rank, N = input column, K = token
+#pragma unroll
+    for (int s = 0; s < NSM; ++s) {
+      if (s == sb) {
+#pragma unroll
+        for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
+          const int kt = ks * B::KSTEP + g * B::EPV;
+          frag fb[B::CTW];
+#pragma unroll
+          for (int ct = 0; ct < B::CTW; ++ct)
+            fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
 #pragma unroll
           for (int n = 0; n < NR; ++n) {
-            const frag fa = lds_frag<T>(dztl + (16 * n + c) * LD + kt);
-            accA[cc][n] = Mma<T>::mma(fa, fb, accA[cc][n]);
+            const frag fa = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
+#pragma unroll
+            for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fa, fb[ct], accA[s][ct][n]);
           }
         }
       }
     }
+    buf ^= 1;
   }
 #pragma unroll
-  for (int cc = 0; cc < CWC; ++cc) {
-    const int64_t i = col_lo + cc * 64 + 16 * w + c;
-    if (cc < ncc && i < N_in) {
+  for (int s = 0; s < NSM; ++s) {
+    if (s < nsl) {
 #pragma unroll
-      for (int n = 0; n < NR; ++n)
+      for (int ct = 0; ct < B::CTW; ++ct) {
+        const int64_t i = c0 + (int64_t)s * B::SW + (ct * 4 + w) * 16 + c;
+        if (i < a.N_in) {
 #pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
-          dAp[((int64_t)gt * Rpad + 16 * n + 4 * g + vv) * N_in + i] = accA[cc][n][vv];
+          for (int n = 0; n < NR; ++n)
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+              const int j = 16 * n + 4 * g + vv;
+              if (j < reff) a.dAp[((int64_t)gt * B::Rpad + j) * a.N_in + i] = accA[s][ct][n][vv];
+            }
+        }
+      }
     }
   }
 }
@@ -539,148 +771,294 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const typename Elem<T>::type* __
 // ------------------------------------------------------------------------------
 // partial sums -> gradients of the two half products (full rank, fp32)
 // ------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ dBp, int gtB, const float* __restrict__ dAp,
-                                                int gtA, const int* __restrict__ meta,
-                                                const float* __restrict__ Ds, float* __restrict__ dL,
-                                                float* __restrict__ dR, int64_t N_out, int64_t N_in, int rs,
-                                                int Rpad, int in_first) {
-  const int64_t nB = (int64_t)rs * N_out, nA = (int64_t)rs * N_in;
+struct ReduceArgs {
+  const float* dBp;
+  const float* dAp;
+  int gtB, gtA;
+  const int* meta;
+  const float* Ds;
+  float* dL;
+  float* dR;
+  int64_t N_out, N_in;
+  int rs, Rpad, in_first;
+};
+
+// Each thread sums four consecutive columns of one rank row over all token
+// groups (float4 loads when aligned) and scatters them into the layout of the
+// half product's gradient.
+__global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
+  const int64_t qB = (a.N_out + 3) / 4, qA = (a.N_in + 3) / 4;
+  const int64_t nB = (int64_t)a.rs * qB, nA = (int64_t)a.rs * qA;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nB + nA;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    if (idx < nB) {
-      const int b = (int)(idx / N_out);
-      const int64_t o = idx % N_out;
-      const int j = meta[kMetaPos + b];
-      float acc = 0.f;
-      if (j >= 0)
-        for (int q = 0; q < gtB; ++q) acc += dBp[((int64_t)q * Rpad + j) * N_out + o];
-      if (!in_first)
-        dL[o * rs + b] = acc;
-      else
-        dR[(int64_t)b * N_out + o] = acc;
-    } else {
-      const int64_t id2 = idx - nB;
-      const int b = (int)(id2 / N_in);
-      const int64_t i = id2 % N_in;
-      const int j = meta[kMetaPos + b];
-      float acc = 0.f;
-      if (j >= 0) {
-        for (int q = 0; q < gtA; ++q) acc += dAp[((int64_t)q * Rpad + j) * N_in + i];
-        acc *= Ds[b];
+    const bool isB = idx < nB;
+    const int64_t id = isB ? idx : idx - nB;
+    const int64_t N = isB ? a.N_out : a.N_in;
+    const int64_t nq = isB ? qB : qA;
+    const int b = (int)(id / nq);
+    const int64_t r0 = (id % nq) * 4;
+    const int j = a.meta[kMetaPos + b];
+    const float* src = isB ? a.dBp : a.dAp;
+    const int gtn = isB ? a.gtB : a.gtA;
+    f32x4 acc = zero4();
+    if (j >= 0) {
+      if ((N & 3) == 0) {
+        f32x4 acc1 = zero4();
+        int q = 0;
+        for (; q + 16 <= gtn; q += 16) {
+          f32x4 v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + ((int64_t)(q + u) * a.Rpad + j) * N + r0);
+#pragma unroll
+          for (int u = 0; u < 16; u += 2) {
+            acc += v[u];
+            acc1 += v[u + 1];
+          }
+        }
+        for (; q < gtn; ++q) acc += *reinterpret_cast<const f32x4*>(src + ((int64_t)q * a.Rpad + j) * N + r0);
+        acc += acc1;
+      } else {
+        for (int q = 0; q < gtn; ++q)
+          for (int e = 0; e < 4; ++e)
+            if (r0 + e < N) acc[e] += src[((int64_t)q * a.Rpad + j) * N + r0 + e];
       }
-      if (!in_first)
-        dR[(int64_t)b * N_in + i] = acc;
-      else
-        dL[i * rs + b] = acc;
+      if (!isB) acc *= a.Ds[b];
+    }
+    // B side feeds L (out first) or R (in first); A side the other one
+    const bool toL = isB != (a.in_first != 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (r0 + e < N) {
+        if (toL)
+          a.dL[(r0 + e) * a.rs + b] = acc[e];
+        else
+          a.dR[(int64_t)b * N + r0 + e] = acc[e];
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------------------
-// reverse sweep for the core gradients
+// reverse sweep for the core gradients as small GEMMs
 // ------------------------------------------------------------------------------
-struct StepArgs {
-  ChainPtrs c;
-  float* dG[kMaxCores];
-  int d;
-  int modes[kMaxCores];
-  int ranks[kMaxCores + 1];
-  int64_t chain_off[kMaxCores];
-  const float* chain;
-  int kL, kR;          // cores of this step on the left / right half, -1 = none
-  const float* dM;     // gradient of the left prefix M_kL (rowsL x r_{kL+1})
-  float* dMn;          // gradient of M_{kL-1}
-  const float* dN;     // gradient of the right suffix N_kR (r_kR x colsR)
-  float* dNn;          // gradient of N_{kR+1}
-  int64_t rowsL, colsR;
+// C(i, j) = rowscale(i) * colscale(j) * sum_k A(i, k) B(k, j) with
+// A(i, k) = A[i*sAi + k*sAk], B(k, j) = B[k*sBk + j*sBj], C(i, j) at
+// C[i*sCi + j*sCj]; scales are optional (null = 1).
+struct Gemm {
+  const float* A;
+  int64_t sAi, sAk;
+  const float* B;
+  int64_t sBk, sBj;
+  const float* rs_;
+  const float* cs_;
+  float* C;
+  int64_t sCi, sCj;
+  int M, N, K;
 };
 
-// Left core k, M_k[(alpha, m), c] = sum_a P[alpha, a] G_k[a, m, c] with
-// P = M_{k-1} diag(D_{k-1}):
-//   dG_k[a, m, c]   = sum_alpha P[alpha, a] dM_k[(alpha, m), c]
-//   dM_{k-1}[alpha, a] = D_{k-1}[a] sum_{m, c} dM_k[(alpha, m), c] G_k[a, m, c]
-// Right core k, N_k[a, (m, beta)] = sum_c G_k[a, m, c] Q[c, beta] with
-// Q = diag(D_k) N_{k+1}:
-//   dG_k[a, m, c]   = sum_beta dN_k[a, (m, beta)] Q[c, beta]
-//   dN_{k+1}[c, beta] = D_k[c] sum_{a, m} G_k[a, m, c] dN_k[a, (m, beta)]
-__global__ __launch_bounds__(256) void k_core_step(StepArgs a) {
-  int64_t nL1 = 0, nL2 = 0, nR1 = 0, nR2 = 0;
-  if (a.kL >= 0) {
-    const int k = a.kL;
-    nL1 = (int64_t)a.ranks[k] * a.modes[k] * a.ranks[k + 1];
-    if (k > 0) nL2 = (a.rowsL / a.modes[k]) * a.ranks[k];
-  }
-  if (a.kR >= 0) {
-    const int k = a.kR;
-    nR1 = (int64_t)a.ranks[k] * a.modes[k] * a.ranks[k + 1];
-    if (k < a.d - 1) nR2 = (int64_t)a.ranks[k + 1] * (a.colsR / a.modes[k]);
-  }
-  const int64_t total = nL1 + nL2 + nR1 + nR2;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    if (idx < nL1 + nL2) {
-      const int k = a.kL;
-      const int n = a.modes[k], r0 = a.ranks[k], r1 = a.ranks[k + 1];
-      const int64_t alphas = a.rowsL / n;
-      if (idx < nL1) {
-        const int cc = (int)(idx % r1);
-        const int m = (int)((idx / r1) % n);
-        const int aa = (int)(idx / ((int64_t)r1 * n));
-        float acc = 0.f;
-        if (k == 0) {
-          acc = a.dM[(int64_t)m * r1 + cc];
-        } else {
-          const float* Mp = a.chain + a.chain_off[k - 1];
-          const float dk = a.c.D[k - 1][aa];
-          for (int64_t al = 0; al < alphas; ++al)
-            acc += (Mp[al * r0 + aa] * dk) * a.dM[(al * n + m) * r1 + cc];
-        }
-        a.dG[k][idx] = acc;
-      } else {
-        const int64_t id2 = idx - nL1;
-        const int aa = (int)(id2 % r0);
-        const int64_t al = id2 / r0;
-        const float* Gk = a.c.G[k];
-        float acc = 0.f;
-        for (int m = 0; m < n; ++m) {
-          const float* dm = a.dM + (al * n + m) * r1;
-          const float* gk = Gk + ((int64_t)aa * n + m) * r1;
-          for (int cc = 0; cc < r1; ++cc) acc += dm[cc] * gk[cc];
-        }
-        a.dMn[al * r0 + aa] = a.c.D[k - 1][aa] * acc;
+__host__ __device__ inline int gemm_tiles(const Gemm& g) { return ((g.M + 31) / 32) * ((g.N + 31) / 32); }
+
+constexpr int kGKC = 128;          // k-chunk staged per round
+constexpr int kGLong = kGKC + 4;   // row stride when a whole chunk of k is contiguous
+constexpr int kGShort = 48;        // row stride when 32 tile entries are contiguous
+constexpr int kGStage = kGKC * kGShort > 32 * kGLong ? kGKC * kGShort : 32 * kGLong;
+
+// One 32 x 32 output tile by 256 threads with fp32 MFMA 16x16x4: operands
+// staged in 128-deep k-chunks in LDS, each in the orientation that keeps its
+// global reads coalesced (strides chosen so that neither the staging writes nor
+// the fragment reads conflict on LDS banks); the four waves split the k-steps
+// of a chunk and their partial tiles are summed in wave order at the end.
+__device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gq = lane >> 4, c = lane & 15;
+  const int ntj = (g.N + 31) / 32;
+  const int64_t i0 = (int64_t)(tile / ntj) * 32, j0 = (int64_t)(tile % ntj) * 32;
+  float* As = lds;
+  float* Bs = lds + kGStage;
+  const bool a_kfast = g.sAk == 1, b_jfast = g.sBj == 1;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[p][q] = zero4();
+  for (int k0 = 0; k0 < g.K; k0 += kGKC) {
+    __syncthreads();
+    float ra[16], rb[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int le = tid + 256 * e;
+      const int i = a_kfast ? le / kGKC : le % 32;
+      const int k = a_kfast ? le % kGKC : le / 32;
+      const bool ok = i0 + i < g.M && k0 + k < g.K;
+      const float v = g.A[ok ? (i0 + i) * g.sAi + (k0 + k) * g.sAk : 0];
+      ra[e] = ok ? v : 0.f;
+      const int j = b_jfast ? le % 32 : le / kGKC;
+      const int k2 = b_jfast ? le / 32 : le % kGKC;
+      const bool ok2 = j0 + j < g.N && k0 + k2 < g.K;
+      const float v2 = g.B[ok2 ? (k0 + k2) * g.sBk + (j0 + j) * g.sBj : 0];
+      rb[e] = ok2 ? v2 : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int le = tid + 256 * e;
+      if (a_kfast)
+        As[(le / kGKC) * kGLong + le % kGKC] = ra[e];
+      else
+        As[(le / 32) * kGShort + le % 32] = ra[e];
+      if (b_jfast)
+        Bs[(le / 32) * kGShort + le % 32] = rb[e];
+      else
+        Bs[(le / kGKC) * kGLong + le % kGKC] = rb[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < kGKC / 16; ++st) {
+      const int kk = (4 * st + w) * 4 + gq;  // k-step 4*st+w of this wave
+      float fa[2], fb[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int i = 16 * p + c;
+        fa[p] = a_kfast ? As[i * kGLong + kk] : As[kk * kGShort + i];
+        fb[p] = b_jfast ? Bs[kk * kGShort + i] : Bs[i * kGLong + kk];
       }
-    } else {
-      const int64_t id3 = idx - nL1 - nL2;
-      const int k = a.kR;
-      const int n = a.modes[k], r0 = a.ranks[k], r1 = a.ranks[k + 1];
-      const int64_t betas = a.colsR / n;
-      if (id3 < nR1) {
-        const int cc = (int)(id3 % r1);
-        const int m = (int)((id3 / r1) % n);
-        const int aa = (int)(id3 / ((int64_t)r1 * n));
-        float acc = 0.f;
-        if (k == a.d - 1) {
-          acc = a.dN[(int64_t)aa * a.colsR + m];
-        } else {
-          const float* Nn = a.chain + a.chain_off[k + 1];
-          const float dk = a.c.D[k][cc];
-          const float* dn = a.dN + (int64_t)aa * a.colsR + (int64_t)m * betas;
-          for (int64_t be = 0; be < betas; ++be) acc += dn[be] * (dk * Nn[(int64_t)cc * betas + be]);
-        }
-        a.dG[k][id3] = acc;
-      } else {
-        const int64_t id4 = id3 - nR1;
-        const int64_t be = id4 % betas;
-        const int cc = (int)(id4 / betas);
-        const float* Gk = a.c.G[k];
-        float acc = 0.f;
-        for (int aa = 0; aa < r0; ++aa)
-          for (int m = 0; m < n; ++m)
-            acc += Gk[((int64_t)aa * n + m) * r1 + cc] * a.dN[(int64_t)aa * a.colsR + (int64_t)m * betas + be];
-        a.dNn[(int64_t)cc * betas + be] = a.c.D[k][cc] * acc;
-      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[p], fb[q], acc[p][q], 0, 0, 0);
     }
   }
+  __syncthreads();
+  // lane (gq, c) of sub-tile (p, q) holds rows 16p+4gq+v, column 16q+c
+  float* red = lds;  // [4 waves][32][33]
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(w * 32 + 16 * p + 4 * gq + v) * 33 + 16 * q + c] = acc[p][q][v];
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e;
+    const int i = idx >> 5, j = idx & 31;
+    const int64_t gi = i0 + i, gj = j0 + j;
+    if (gi < g.M && gj < g.N) {
+      const float sum = ((red[i * 33 + j] + red[(32 + i) * 33 + j]) + red[(64 + i) * 33 + j]) + red[(96 + i) * 33 + j];
+      const float rsc = g.rs_ ? g.rs_[gi] : 1.f;
+      const float csc = g.cs_ ? g.cs_[gj] : 1.f;
+      g.C[gi * g.sCi + gj * g.sCj] = (sum * rsc) * csc;
+    }
+  }
+}
+
+// One level of the reverse sweep: up to four independent GEMMs (per half, the
+// core gradient and the gradient passed on to the next core), one 32 x 32
+// tile per work-group.
+struct SweepArgs {
+  Gemm g[4];
+  int tiles[4];
+  int ng;
+};
+
+__global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
+  __shared__ __align__(16) float lds[2 * kGStage];
+  int t = blockIdx.x, q = 0;
+  while (q < a.ng - 1 && t >= a.tiles[q]) {
+    t -= a.tiles[q];
+    ++q;
+  }
+  gemm_tile32(a.g[q], t, lds);
+}
+
+// Left core k, gradient dM_k of the prefix M_k (rows prod_{j<=k} n_j, r_{k+1}
+// cols), M_k[(alpha, m), c] = sum_a (M_{k-1} diag(D_{k-1}))[alpha, a] G_k[a, m, c]:
+//   dG_k = P^T dM_k'         with P = M_{k-1} diag(D_{k-1}), dM_k' = dM_k as (alpha, (m, c))
+//   dM_{k-1} = (dM_k' G_k'^T) diag(D_{k-1})
+static Gemm left_dG(const LinearPlan& P, const float* chain, const float* const* D, float* dGk, int k,
+                    const float* dMk, int64_t rows) {
+  const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
+  Gemm g;
+  g.A = chain + P.chain_off[k - 1];
+  g.sAi = 1;
+  g.sAk = r0;
+  g.rs_ = D[k - 1];
+  g.B = dMk;
+  g.sBk = (int64_t)n * r1;
+  g.sBj = 1;
+  g.cs_ = nullptr;
+  g.C = dGk;
+  g.sCi = (int64_t)n * r1;
+  g.sCj = 1;
+  g.M = r0;
+  g.N = n * r1;
+  g.K = (int)(rows / n);
+  return g;
+}
+static Gemm left_dM(const LinearPlan& P, const float* const* G, const float* const* D, int k, const float* dMk,
+                    int64_t rows, float* out) {
+  const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
+  Gemm g;
+  g.A = dMk;
+  g.sAi = (int64_t)n * r1;
+  g.sAk = 1;
+  g.rs_ = nullptr;
+  g.B = G[k];
+  g.sBk = 1;
+  g.sBj = (int64_t)n * r1;
+  g.cs_ = D[k - 1];
+  g.C = out;
+  g.sCi = r0;
+  g.sCj = 1;
+  g.M = (int)(rows / n);
+  g.N = r0;
+  g.K = n * r1;
+  return g;
+}
+// Right core k, gradient dN_k of the suffix N_k (r_k rows, cols = prod_{j>=k}
+// n_j), N_k[a, (m, beta)] = sum_c G_k[a, m, c] (diag(D_k) N_{k+1})[c, beta]:
+//   dG_k = dN_k'' Q^T        with Q = diag(D_k) N_{k+1}, dN_k'' = dN_k as ((a, m), beta)
+//   dN_{k+1} = diag(D_k) G_k''^T dN_k''
+static Gemm right_dG(const LinearPlan& P, const float* chain, const float* const* D, float* dGk, int k,
+                     const float* dNk, int64_t cols) {
+  const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
+  const int64_t be = cols / n;
+  Gemm g;
+  g.A = dNk;
+  g.sAi = be;
+  g.sAk = 1;
+  g.rs_ = nullptr;
+  g.B = chain + P.chain_off[k + 1];
+  g.sBk = 1;
+  g.sBj = be;
+  g.cs_ = D[k];
+  g.C = dGk;
+  g.sCi = r1;
+  g.sCj = 1;
+  g.M = r0 * n;
+  g.N = r1;
+  g.K = (int)be;
+  return g;
+}
+static Gemm right_dN(const LinearPlan& P, const float* const* G, const float* const* D, int k, const float* dNk,
+                     int64_t cols, float* out) {
+  const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
+  const int64_t be = cols / n;
+  Gemm g;
+  g.A = G[k];
+  g.sAi = 1;
+  g.sAk = r1;
+  g.rs_ = D[k];
+  g.B = dNk;
+  g.sBk = be;
+  g.sBj = 1;
+  g.cs_ = nullptr;
+  g.C = out;
+  g.sCi = be;
+  g.sCj = 1;
+  g.M = r1;
+  g.N = (int)be;
+  g.K = r0 * n;
+  return g;
 }
 
 __global__ void k_zero(float* p, int64_t n) {
@@ -716,40 +1094,110 @@ static ttc_status hip_status() {
   return e == hipSuccess ? TTC_OK : TTC_ERR_HIP;
 }
 
-template <typename T, int NR>
-static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
+// dynamic LDS above 64 KB must be enabled per kernel; done once per kernel,
+// before any graph capture can see it
+static void allow_lds(const void* kern, size_t bytes) {
+  if (bytes > 65536) (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename T, int NR, bool VEC>
+static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
   typedef typename Elem<T>::type E;
   const size_t lds = size_t(4) * 64 * 16 * NR * sizeof(float);
-  auto kern = k_fwd<T, NR>;
-  static bool lds_set = false;  // set once, before any graph capture can see it
+  auto kern = k_fwd<T, NR, VEC>;
+  static bool lds_set = false;
   if (!lds_set) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    allow_lds((const void*)kern, lds);
     lds_set = true;
   }
-  const int vin = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x);
   const int vout = (P.N_out % 4) == 0 && aligned16(y);
   TraceScope ts("fwd", st);
   hipLaunchKernelGGL(kern, dim3(P.ntiles), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
-                     (const E*)(saved + P.sv_Bc), (float*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, vin,
-                     vout);
+                     (const E*)(saved + P.sv_Bc), (E*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, (int)VEC, vout);
+}
+
+template <typename T, int NR>
+static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
+  if ((P.N_in % Mma<T>::EPV) == 0 && aligned16(x))
+    launch_fwd_v<T, NR, true>(P, x, saved, y, st);
+  else
+    launch_fwd_v<T, NR, false>(P, x, saved, y, st);
+}
+
+template <typename T, int NR, bool VY, bool VX>
+static void launch_bwd_v(const LinearPlan& P, const void* x, const void* dy, const char* saved, void* dx,
+                            char* scratch, hipStream_t st) {
+  typedef Bwd<T, NR> B;
+  typedef typename B::E E;
+  {
+    DyArgs<T> a;
+    a.dy = (const E*)dy;
+    a.BcT = (const E*)(saved + P.sv_BcT);
+    a.Z = (const E*)(saved + P.sv_Z);
+    a.dZp = (float*)(scratch + P.sc_dZp);
+    a.dZ = (E*)(scratch + P.sc_dZ);
+    a.dBp = (float*)(scratch + P.sc_dBp);
+    a.meta = (const int*)(saved + P.sv_meta);
+    a.T_ = P.T;
+    a.N_out = P.N_out;
+    a.nsl = P.dy_nsl;
+    a.tpg = P.dy_tpg;
+    a.ntiles = P.ntiles;
+    a.gc_n = P.dy_gc;
+    a.vec = (P.N_out % B::EPV) == 0 && aligned16(dy);
+    constexpr int NSM = bwd_max_slabs(B::ES, NR);
+    const size_t lds = size_t(B::Rpad) * (NSM * B::SW + 16 / B::ES) * B::ES + 2 * B::SLAB * B::ES +
+                       size_t(B::Rpad) * B::ZLD * B::ES;
+    static bool lds_set = false;
+    if (!lds_set) {
+      allow_lds((const void*)k_bwd_dy<T, NR, VY>, lds);
+      lds_set = true;
+    }
+    TraceScope ts("bwd_dy", st);
+    hipLaunchKernelGGL((k_bwd_dy<T, NR, VY>), dim3(P.dy_gc, P.dy_gt), dim3(256), lds, st, a);
+  }
+  if (P.dy_gc > 1) {
+    const int64_t n4 = P.T * B::Rpad / 4;
+    TraceScope ts("dz_sum", st);
+    hipLaunchKernelGGL(k_dz_sum<T>, dim3((unsigned)std::min<int64_t>(4096, (n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)(scratch + P.sc_dZp), (E*)(scratch + P.sc_dZ), P.dy_gc, n4);
+  }
+  {
+    DxArgs<T> a;
+    a.x = (const E*)x;
+    a.AcT = (const E*)(saved + P.sv_AcT);
+    a.dZ = (const E*)(scratch + P.sc_dZ);
+    a.dAp = (float*)(scratch + P.sc_dAp);
+    a.dx = (E*)dx;
+    a.meta = (const int*)(saved + P.sv_meta);
+    a.T_ = P.T;
+    a.N_in = P.N_in;
+    a.nsl = P.dx_nsl;
+    a.tpg = P.dx_tpg;
+    a.ntiles = P.ntiles;
+    a.vec = (P.N_in % B::EPV) == 0 && aligned16(x) && (dx == nullptr || aligned16(dx));
+    constexpr int NSM = dx_max_slabs(B::ES, NR);
+    const size_t lds = size_t(NSM) * B::SW * B::RLD * B::ES + 2 * B::SLAB * B::ES + size_t(64) * B::RLD * B::ES +
+                       size_t(B::Rpad) * B::ZLD * B::ES;
+    static bool lds_set = false;
+    if (!lds_set) {
+      allow_lds((const void*)k_bwd_dx<T, NR, VX>, lds);
+      lds_set = true;
+    }
+    TraceScope ts("bwd_dx", st);
+    hipLaunchKernelGGL((k_bwd_dx<T, NR, VX>), dim3(P.dx_gc, P.dx_gt), dim3(256), lds, st, a);
+  }
 }
 
 template <typename T, int NR>
 static void launch_bwd_main(const LinearPlan& P, const void* x, const void* dy, const char* saved, void* dx,
                             char* scratch, hipStream_t st) {
-  typedef typename Elem<T>::type E;
-  const int vout = (P.N_out % Mma<T>::EPV) == 0 && aligned16(dy);
-  {
-    TraceScope ts("bwd_dy", st);
-    hipLaunchKernelGGL((k_bwd_dy<T, NR>), dim3(P.dy_gc, P.dy_gt), dim3(256), 0, st, (const E*)dy,
-                     (const E*)(saved + P.sv_BcT), (const float*)(saved + P.sv_Z), (float*)(scratch + P.sc_dZp),
-                     (float*)(scratch + P.sc_dBp), P.T, P.N_out, P.dy_ncc, P.dy_tpg, P.ntiles, vout);
-  }
-  const int vin = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x) && (dx == nullptr || aligned16(dx));
-  TraceScope ts("bwd_dx", st);
-  hipLaunchKernelGGL((k_bwd_dx<T, NR>), dim3(P.dx_gc, P.dx_gt), dim3(256), 0, st, (const E*)x,
-                     (const E*)(saved + P.sv_AcT), (const float*)(scratch + P.sc_dZp), P.dy_gc,
-                     (float*)(scratch + P.sc_dAp), (E*)dx, P.T, P.N_in, P.dx_ncc, P.dx_tpg, P.ntiles, vin);
+  const bool vy = (P.N_out % Mma<T>::EPV) == 0 && aligned16(dy);
+  const bool vx = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x) && (dx == nullptr || aligned16(dx));
+  if (vy && vx)
+    launch_bwd_v<T, NR, true, true>(P, x, dy, saved, dx, scratch, st);
+  else
+    launch_bwd_v<T, NR, false, false>(P, x, dy, saved, dx, scratch, st);
 }
 
 template <typename T>
@@ -773,6 +1221,10 @@ static bool dispatch_bwd(const LinearPlan& P, const void* x, const void* dy, con
     case 8: launch_bwd_main<T, 8>(P, x, dy, saved, dx, scratch, st); return true;
   }
   return false;
+}
+
+static unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(cap, (n + per_block - 1) / per_block));
 }
 
 }  // namespace ttc
@@ -814,6 +1266,7 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   m.rs = P.rs;
   m.Rpad = P.Rpad;
   m.in_first = P.in_first;
+  m.max_rank = P.max_rank;
   for (int k = 0; k < P.d; ++k) {
     m.modes[k] = P.modes[k];
     m.chain_off[k] = P.chain_off[k];
@@ -831,11 +1284,18 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   m.BcT = sv + P.sv_BcT;
   m.chain = reinterpret_cast<float*>(sv + P.sv_chain);
   {
+    const size_t lds = size_t(P.max_rank) * P.max_rank * sizeof(float);
+    static bool lds_set[2] = {false, false};
+    const void* kern = P.act == TTC_BF16 ? (const void*)k_merge<bf16_t> : (const void*)k_merge<float>;
+    if (!lds_set[P.act]) {
+      allow_lds(kern, size_t(TTC_MAX_RANK) * TTC_MAX_RANK * sizeof(float));
+      lds_set[P.act] = true;
+    }
     TraceScope ts("merge", s);
     if (P.act == TTC_BF16)
-      hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(128), 0, s, m);
+      hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
     else
-      hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(128), 0, s, m);
+      hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
   }
   const bool ok = P.act == TTC_BF16 ? dispatch_fwd<bf16_t>(P, x, sv, y, s) : dispatch_fwd<float>(P, x, sv, y, s);
   if (!ok) return TTC_ERR_UNSUPPORTED;
@@ -859,7 +1319,7 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
     for (int k = 0; k < P.d; ++k) {
       const int64_t n = (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
       TraceScope ts("zero", s);
-      hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>(1024, (n + 255) / 256)), dim3(256), 0, s, dG[k], n);
+      hipLaunchKernelGGL(k_zero, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, dG[k], n);
     }
     return hip_status();
   }
@@ -872,64 +1332,69 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
   const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s)
                                     : dispatch_bwd<float>(P, x, dy, sv, dx, sc, s);
   if (!ok) return TTC_ERR_UNSUPPORTED;
-  // partial sums -> dL, dR
+  // partial sums -> gradients of the two half products; a half made of one
+  // core receives its gradient directly
+  float* dL = P.s == 1 ? dG[0] : (float*)(sc + P.sc_dL);
+  float* dR = P.d - P.s == 1 ? dG[P.d - 1] : (float*)(sc + P.sc_dR);
   {
-    const int64_t n = (int64_t)P.rs * (P.N_out + P.N_in);
-    const unsigned blocks = (unsigned)std::min<int64_t>(2048, (n + 255) / 256);
+    ReduceArgs r;
+    r.dBp = (const float*)(sc + P.sc_dBp);
+    r.dAp = (const float*)(sc + P.sc_dAp);
+    r.gtB = P.dy_gt;
+    r.gtA = P.dx_gt;
+    r.meta = (const int*)(sv + P.sv_meta);
+    r.Ds = D[P.s - 1];
+    r.dL = dL;
+    r.dR = dR;
+    r.N_out = P.N_out;
+    r.N_in = P.N_in;
+    r.rs = P.rs;
+    r.Rpad = P.Rpad;
+    r.in_first = P.in_first;
+    const int64_t n = (int64_t)P.rs * ((P.N_out + 3) / 4 + (P.N_in + 3) / 4);
     TraceScope ts("reduce", s);
-    hipLaunchKernelGGL(k_reduce, dim3(blocks), dim3(256), 0, s, (const float*)(sc + P.sc_dBp), P.dy_gt,
-                       (const float*)(sc + P.sc_dAp), P.dx_gt, (const int*)(sv + P.sv_meta), D[P.s - 1],
-                       (float*)(sc + P.sc_dL), (float*)(sc + P.sc_dR), P.N_out, P.N_in, P.rs, P.Rpad, P.in_first);
+    hipLaunchKernelGGL(k_reduce, dim3(grid_for(n, 256, 4096)), dim3(256), 0, s, r);
   }
-  // reverse sweep through both halves
-  StepArgs a;
-  memset(&a, 0, sizeof(a));
-  a.c = chain_ptrs(P, G, D);
-  for (int k = 0; k < P.d; ++k) {
-    a.dG[k] = dG[k];
-    a.modes[k] = P.modes[k];
-    a.chain_off[k] = P.chain_off[k];
-  }
-  for (int k = 0; k <= P.d; ++k) a.ranks[k] = P.ranks[k];
-  a.d = P.d;
-  a.chain = reinterpret_cast<const float*>(sv + P.sv_chain);
-  const float* curL = reinterpret_cast<const float*>(sc + P.sc_dL);
-  const float* curR = reinterpret_cast<const float*>(sc + P.sc_dR);
-  int64_t rowsL = P.NL, colsR = P.NRt;
-  const int steps = std::max(P.s, P.d - P.s);
-  for (int i = 0; i < steps; ++i) {
-    float* buf = reinterpret_cast<float*>(sc + ((i & 1) ? P.sc_w1 : P.sc_w0));
-    a.kL = (P.s - 1 - i >= 0) ? P.s - 1 - i : -1;
-    a.kR = (P.s + i < P.d) ? P.s + i : -1;
-    a.dM = curL;
-    a.dMn = buf;
-    a.dN = curR;
-    a.dNn = buf + P.wl_floats;
-    a.rowsL = rowsL;
-    a.colsR = colsR;
-    int64_t total = 0;
-    if (a.kL >= 0) {
-      const int k = a.kL;
-      total += (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
-      if (k > 0) total += (rowsL / P.modes[k]) * P.ranks[k];
-    }
-    if (a.kR >= 0) {
-      const int k = a.kR;
-      total += (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
-      if (k < P.d - 1) total += (int64_t)P.ranks[k + 1] * (colsR / P.modes[k]);
-    }
-    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(4096, (total + 255) / 256));
-    {
-      TraceScope ts("core_step", s);
-      hipLaunchKernelGGL(k_core_step, dim3(blocks), dim3(256), 0, s, a);
-    }
-    if (a.kL >= 0) {
-      curL = a.dMn;
-      rowsL /= P.modes[a.kL];
-    }
-    if (a.kR >= 0) {
-      curR = a.dNn;
-      colsR /= P.modes[a.kR];
+  // reverse sweep through both halves, one launch per level
+  {
+    const float* chain = reinterpret_cast<const float*>(sv + P.sv_chain);
+    float* wL[2] = {(float*)(sc + P.sc_w0), (float*)(sc + P.sc_w1)};
+    float* wR[2] = {(float*)(sc + P.sc_w0) + P.wl_floats, (float*)(sc + P.sc_w1) + P.wl_floats};
+    const float* curL = dL;
+    const float* curR = dR;
+    int64_t rowsL = P.NL, colsR = P.NRt;
+    for (int lvl = 0;; ++lvl) {
+      const int kL = P.s - 1 - lvl, kR = P.s + lvl;
+      const bool hasL = kL >= 1, hasR = kR <= P.d - 2;
+      if (!hasL && !hasR) break;
+      SweepArgs a;
+      memset(&a, 0, sizeof(a));
+      float* outL = nullptr;
+      float* outR = nullptr;
+      if (hasL) {
+        outL = kL - 1 == 0 ? dG[0] : wL[lvl & 1];
+        a.g[a.ng++] = left_dG(P, chain, D, dG[kL], kL, curL, rowsL);
+        a.g[a.ng++] = left_dM(P, G, D, kL, curL, rowsL, outL);
+      }
+      if (hasR) {
+        outR = kR + 1 == P.d - 1 ? dG[P.d - 1] : wR[lvl & 1];
+        a.g[a.ng++] = right_dG(P, chain, D, dG[kR], kR, curR, colsR);
+        a.g[a.ng++] = right_dN(P, G, D, kR, curR, colsR, outR);
+      }
+      int total = 0;
+      for (int q = 0; q < a.ng; ++q) total += (a.tiles[q] = gemm_tiles(a.g[q]));
+      {
+        TraceScope ts("core", s);
+        hipLaunchKernelGGL(k_sweep, dim3(total), dim3(256), 0, s, a);
+      }
+      if (hasL) {
+        curL = outL;
+        rowsL /= P.modes[kL];
+      }
+      if (hasR) {
+        curR = outR;
+        colsR /= P.modes[kR];
+      }
     }
   }
   return hip_status();
@@ -945,15 +1410,17 @@ extern "C" ttc_status tt_linear_explain(const tt_linear_desc* desc, int64_t T, c
   snprintf(buf, n,
            "path=merged split=%d rank=%d rpad=%d N_out=%lld N_in=%lld T=%lld "
            "merged_macs=%.6g merged_bytes=%.6g sequential_macs=%.6g sequential_bytes=%.6g "
-           "dense_macs=%.6g dense_bytes=%.6g dy_grid=%dx%d dx_grid=%dx%d saved=%zu scratch=%zu",
+           "dense_macs=%.6g dense_bytes=%.6g dy_grid=%dx%d dy_slabs=%d dx_grid=%dx%d dx_slabs=%d saved=%zu "
+           "scratch=%zu",
            P.s, P.rs, P.Rpad, (long long)P.N_out, (long long)P.N_in, (long long)T, macs[1], bytes[1], macs[2],
-           bytes[2], macs[3], bytes[3], P.dy_gc, P.dy_gt, P.dx_gc, P.dx_gt, P.sv_total, P.sc_total);
+           bytes[2], macs[3], bytes[3], P.dy_gc, P.dy_gt, P.dy_nsl, P.dx_gc, P.dx_gt, P.dx_nsl, P.sv_total,
+           P.sc_total);
   return TTC_OK;
 }
 
 extern "C" ttc_status tt_linear_path_cost(const tt_linear_desc* desc, int64_t T, int32_t path, double* macs,
                                           double* bytes) {
-  if (!macs || !bytes) return TTC_ERR_NULL;
+  if (!macs || !bytes || !desc) return TTC_ERR_NULL;
   if (path < TTC_PATH_MERGED || path > TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
   // cost the path regardless of whether it is implemented
   tt_linear_desc dd = *desc;
@@ -983,4 +1450,4 @@ extern "C" const char* ttc_status_str(ttc_status s) {
   return "unknown status";
 }
 
-extern "C" const char* ttc_version(void) { return "ttc 0.1 gfx950"; }
+extern "C" const char* ttc_version(void) { return "ttc 0.2 gfx950"; }

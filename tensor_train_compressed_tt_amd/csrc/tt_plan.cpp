@@ -66,6 +66,9 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->NL = desc->in_first ? nin : nout;
   P->NRt = desc->in_first ? nout : nin;
   P->T = T;
+  P->es = desc->act_dtype == TTC_BF16 ? 2 : 4;
+  P->max_rank = 1;
+  for (int k = 0; k <= d; ++k) P->max_rank = std::max(P->max_rank, P->ranks[k]);
 
   // chain area: M_k (rows prod_{j<=k} n_j, r_{k+1} cols) for k < s-1 and
   // N_k (r_k rows, prod_{j>=k} n_j cols) for k > s
@@ -84,7 +87,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
     off += cols * P->ranks[k];
   }
   P->chain_floats = off;
-  // merge items: one per row of every left prefix M_k (k < s) and one per
+  // merge work items: one per row of every left prefix M_k (k < s) and one per
   // column of every right suffix N_k (k >= s)
   int64_t items = 0;
   rows = 1;
@@ -102,47 +105,50 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->item_off[d] = items;
 
   // ---- launch shapes of the two backward streaming passes ---------------------
-  // A work-group owns a range of columns and a range of token tiles.  Splitting
-  // the columns costs partial sums of the T x r intermediate; splitting the
-  // tokens costs partial sums of the r x N weight-side gradient.  Pick the split
-  // with the fewest partial bytes that still yields about 256 work-groups.
+  // A work-group owns a range of columns (whole 256-byte slabs) and a range of
+  // token tiles.  Splitting the columns of the dY pass costs partial sums of
+  // the T x r intermediate dZ (and the dX pass re-reads dZ once per column
+  // group); splitting the tokens costs partial sums of the r x N weight-side
+  // gradients.  Pick the split with the fewest extra bytes that still gives
+  // about one work-group per CU.
   P->ntiles = (int)((T + kTileT - 1) / kTileT);
   const int nt = std::max(1, P->ntiles);
-  P->cwc = std::max(1, std::min(8, 16 / P->NR));
+  P->sw = slab_cols(P->es);
   const int target = 256;
-  auto choose = [&](int64_t ncols, bool partial_t, int* gc, int* gt, int* ncc, int* tpg) {
-    const int chunks = (int)((ncols + 63) / 64);
-    const int gc_min = (chunks + P->cwc - 1) / P->cwc;
+  auto choose = [&](int64_t ncols, int maxs, bool dy, int* gc, int* gt, int* nsl, int* tpg) {
+    const int chunks = (int)std::max<int64_t>(1, (ncols + P->sw - 1) / P->sw);
+    const int gc_min = (chunks + maxs - 1) / maxs;
     double best = 1e300;
     int bgc = gc_min, bgt = 1;
     for (int g = gc_min; g <= chunks; ++g) {
       int t_groups = std::max(1, std::min(nt, (target + g - 1) / g));
-      int per = (nt + t_groups - 1) / t_groups;
+      const int per = (nt + t_groups - 1) / t_groups;
       t_groups = (nt + per - 1) / per;
       const double wgs = double(g) * t_groups;
-      // partial bytes: token-split partials of the r x N side; column-split
-      // partials of the T x r side are written (dY pass) or re-read (dX pass)
-      double bytes = 4.0 * P->Rpad * (double(t_groups) * ncols * 2.0 + double(g) * T * (partial_t ? 2.0 : 1.0));
-      // under-filled GPU: the streaming part slows down in proportion
-      const double stream = double(T) * ncols * (P->act == TTC_BF16 ? 2 : 4) * (partial_t ? 1.0 : 3.0);
+      double extra = 8.0 * t_groups * ncols * P->rs;  // weight-side partials, written and read
+      if (dy)
+        extra += (g > 1 ? 8.0 * g * double(T) * P->Rpad : 0.0);
+      else
+        extra += double(g) * T * P->Rpad * P->es;  // dZ re-read per column group
+      const double stream = double(T) * ncols * P->es * (dy ? 1.0 : 2.0);
       const double fill = std::min(1.0, wgs / target);
-      const double cost = stream / fill + bytes;
+      const double cost = stream / fill + extra;
       if (cost < best) {
         best = cost;
         bgc = g;
         bgt = t_groups;
       }
     }
-    *ncc = (chunks + bgc - 1) / bgc;
-    *gc = (chunks + *ncc - 1) / *ncc;  // no empty column groups
+    *nsl = (chunks + bgc - 1) / bgc;
+    *gc = (chunks + *nsl - 1) / *nsl;  // no empty column groups
     *tpg = (nt + bgt - 1) / bgt;
     *gt = (nt + *tpg - 1) / *tpg;
   };
-  choose(nout, true, &P->dy_gc, &P->dy_gt, &P->dy_ncc, &P->dy_tpg);
-  choose(nin, false, &P->dx_gc, &P->dx_gt, &P->dx_ncc, &P->dx_tpg);
+  choose(nout, bwd_max_slabs(P->es, P->NR), true, &P->dy_gc, &P->dy_gt, &P->dy_nsl, &P->dy_tpg);
+  choose(nin, dx_max_slabs(P->es, P->NR), false, &P->dx_gc, &P->dx_gt, &P->dx_nsl, &P->dx_tpg);
 
   // ---- saved layout -----------------------------------------------------------
-  const size_t es = desc->act_dtype == TTC_BF16 ? 2 : 4;
+  const size_t es = P->es;
   size_t o = 0;
   P->sv_meta = o;
   o = align256(o + kMetaBytes);
@@ -157,26 +163,30 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->sv_chain = o;
   o = align256(o + size_t(P->chain_floats) * 4);
   P->sv_Z = o;
-  o = align256(o + size_t(T) * P->Rpad * 4);
+  o = align256(o + size_t(T) * P->Rpad * es);
   P->sv_total = o;
 
   // ---- scratch layout -------------------------------------------------------------
+  // ping-pong buffers for the gradients passed between levels of the sweep:
+  // left dM_k for 1 <= k <= s-2, right dN_k for s+1 <= k <= d-2
   int64_t wl = 0, wr = 0;
   rows = 1;
-  for (int k = 0; k < P->s; ++k) {
+  for (int k = 0; k < P->s - 1; ++k) {
     rows *= P->modes[k];
-    wl = std::max(wl, rows * (int64_t)P->ranks[k + 1]);
+    if (k >= 1) wl = std::max(wl, rows * (int64_t)P->ranks[k + 1]);
   }
   cols = 1;
-  for (int k = d - 1; k >= P->s; --k) {
+  for (int k = d - 1; k > P->s; --k) {
     cols *= P->modes[k];
-    wr = std::max(wr, cols * (int64_t)P->ranks[k]);
+    if (k <= d - 2) wr = std::max(wr, cols * (int64_t)P->ranks[k]);
   }
   P->wl_floats = wl;
   P->wr_floats = wr;
   o = 0;
   P->sc_dZp = o;
-  o = align256(o + size_t(P->dy_gc) * T * P->Rpad * 4);
+  o = align256(o + (P->dy_gc > 1 ? size_t(P->dy_gc) * T * P->Rpad * 4 : 0));
+  P->sc_dZ = o;
+  o = align256(o + size_t(T) * P->Rpad * es);
   P->sc_dBp = o;
   o = align256(o + size_t(P->dy_gt) * P->Rpad * nout * 4);
   P->sc_dAp = o;

@@ -13,11 +13,27 @@ namespace ttc {
 constexpr int kMaxCores = 2 * TTC_MAX_HALF_MODES;
 constexpr int kTileT = 64;  // tokens per tile of the streaming kernels
 
+// Streaming kernels move 64-token x 256-byte slabs: 128 bf16 or 64 fp32 columns.
+constexpr int slab_cols(int act_bytes) { return 256 / act_bytes; }
+// Most 256-byte slabs one work-group of a backward pass keeps accumulators
+// for: bounded so that the per-lane accumulators stay within 64 registers
+// and the work-group's LDS within ~80 KB (two work-groups per CU).
+constexpr int bwd_max_slabs(int act_bytes, int NR) {
+  return (2048 / (NR * act_bytes)) / slab_cols(act_bytes) < 1
+             ? 1
+             : ((2048 / (NR * act_bytes)) / slab_cols(act_bytes) > 8 ? 8
+                                                                     : (2048 / (NR * act_bytes)) / slab_cols(act_bytes));
+}
+constexpr int dx_max_slabs(int act_bytes, int NR) {
+  return bwd_max_slabs(act_bytes, NR) / 2 < 1 ? 1 : bwd_max_slabs(act_bytes, NR) / 2;
+}
+
 struct LinearPlan {
   // ---- shape, chain order -------------------------------------------------
   int p, q, d;
   int in_first;
   int act;                 // TTC_F32 / TTC_BF16
+  int es;                  // bytes per activation element
   int modes[kMaxCores];    // n_k in chain order
   int ranks[kMaxCores + 1];
   int s;                   // cores in the left half of the chain
@@ -33,15 +49,16 @@ struct LinearPlan {
   int64_t chain_floats;
   // merge work items: left rows of M_k (k < s) and right columns of N_k (k >= s)
   int64_t item_off[kMaxCores + 1];  // per core k: first item; item_off[d] = total
+  int max_rank;
   // ---- launch shapes ---------------------------------------------------------
   int ntiles;              // ceil(T / kTileT)
-  int cwc;                 // 64-column chunks per work-group in the backward passes (max)
-  int dy_gc, dy_gt, dy_ncc, dy_tpg;  // dY pass: column groups, token groups, chunks/group, tiles/group
-  int dx_gc, dx_gt, dx_ncc, dx_tpg;  // dX pass
+  int sw;                  // slab width in elements
+  int dy_gc, dy_gt, dy_nsl, dy_tpg;  // dY pass: column groups, token groups, slabs/group, tiles/group
+  int dx_gc, dx_gt, dx_nsl, dx_tpg;  // dX pass
   // ---- saved layout (bytes) ----------------------------------------------------
   size_t sv_meta, sv_Ac, sv_AcT, sv_Bc, sv_BcT, sv_chain, sv_Z, sv_total;
   // ---- scratch layout (bytes) ----------------------------------------------------
-  size_t sc_dZp, sc_dBp, sc_dAp, sc_dL, sc_dR, sc_w0, sc_w1, sc_total;
+  size_t sc_dZp, sc_dZ, sc_dBp, sc_dAp, sc_dL, sc_dR, sc_w0, sc_w1, sc_total;
   int64_t wl_floats, wr_floats;  // size of one left / right ping-pong buffer
 };
 

@@ -98,6 +98,31 @@ __device__ __forceinline__ typename Mma<T>::frag load_frag(const typename Elem<T
   return f;
 }
 
+// Branch-free variant for 16-byte-aligned rows whose length is a multiple of
+// the group size: the address is clamped into the matrix and the value
+// replaced by zero when out of range, so consecutive calls issue their loads
+// back to back instead of waiting at a branch each.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag load_frag_v(const typename Elem<T>::type* __restrict__ base,
+                                                             int64_t row, int64_t nrows, int64_t col,
+                                                             int64_t ncols, int64_t ld) {
+  typedef typename Mma<T>::frag frag;
+  const bool ok = row < nrows && col < ncols;
+  const frag f = *reinterpret_cast<const frag*>(base + (ok ? row * ld + col : 0));
+  return ok ? f : Mma<T>::zero();
+}
+
+// compile-time choice between the two
+template <typename T, bool VEC>
+__device__ __forceinline__ typename Mma<T>::frag ld_frag(const typename Elem<T>::type* __restrict__ base,
+                                                         int64_t row, int64_t nrows, int64_t col, int64_t ncols,
+                                                         int64_t ld) {
+  if constexpr (VEC)
+    return load_frag_v<T>(base, row, nrows, col, ncols, ld);
+  else
+    return load_frag<T>(base, row, nrows, col, ncols, ld, false);
+}
+
 // Same from LDS (always in range, 16-byte aligned).
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag lds_frag(const typename Elem<T>::type* p) {

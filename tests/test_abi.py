@@ -39,8 +39,8 @@ def test_workspace_sizes_scale_with_tokens():
     d = _desc()
     s0, c0 = ttc.tt_linear_workspace(d, 0)
     s1, c1 = ttc.tt_linear_workspace(d, 16384)
-    # the kept intermediate Z is T x 32 fp32
-    assert s1 - s0 >= 16384 * 32 * 4
+    # the kept intermediate Z is T x 32 in the activation dtype (bf16 here)
+    assert s1 - s0 >= 16384 * 32 * 2
     assert c1 > c0
 
 
