@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="config 4 only: number of encoder layers")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying a HIP graph")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="run merges and core-gradient tails on the main stream too (no overlap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     return ap.parse_args()
@@ -130,6 +132,7 @@ def main():
         sb, cb = mod.workspace(T)
         max_scratch = max(max_scratch, cb)
         layers.append({
+            "scratch": torch.empty(cb, dtype=torch.uint8, device=dev) if not args.single_stream else None,
             "spec": spec, "mod": mod, "cores": cores, "D": D, "x": x, "dy": dy,
             "y": torch.empty((T, spec.n_out), dtype=tdt, device=dev),
             "dx": torch.empty((T, spec.n_in), dtype=tdt, device=dev),
@@ -142,15 +145,40 @@ def main():
             keep["dy"] = L["dy"][: args.cpu_tokens].copy()
         host.append(keep)
         del L
-    scratch = torch.empty(max_scratch, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(max_scratch, dtype=torch.uint8, device=dev) if args.single_stream else None
     sizes = step_bytes(host, T, es)
+    side = torch.cuda.Stream()  # default priority
 
-    def step():
+    def step_single():
         for L in layers:
             L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"])
         for L in reversed(layers):
             L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
                               scratch=scratch)
+
+    def step_overlap():
+        # The merges depend only on the cores and D, the core-gradient tails
+        # produce only dG: both go to a side stream.  The main stream carries
+        # the dependent chain of streaming passes (forward over the layers,
+        # then dX backward through them in reverse order).
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        ready = []
+        with torch.cuda.stream(side):
+            for L in layers:
+                L["mod"].prepare(T, L["cores"], L["D"], saved=L["saved"])
+                e = torch.cuda.Event()
+                e.record(side)
+                ready.append(e)
+        for L, e in zip(layers, ready):
+            main.wait_event(e)
+            L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"], prepared=True)
+        for L in reversed(layers):
+            L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
+                              scratch=L["scratch"], grad_stream=side)
+        main.wait_stream(side)
+
+    step = step_single if args.single_stream else step_overlap
 
     # ---- warm-up, optional graph capture --------------------------------------------
     for _ in range(max(1, args.warmup)):
@@ -194,8 +222,11 @@ def main():
     # launch order of one step: per layer merge, fwd; then per layer (reversed)
     # bwd_dy, bwd_dx, reduce, core_step x n
     expect = []
-    for li in range(len(layers)):
-        expect += [("merge", li), ("fwd", li)]
+    if args.single_stream:
+        for li in range(len(layers)):
+            expect += [("merge", li), ("fwd", li)]
+    else:
+        expect += [("merge", li) for li in range(len(layers))] + [("fwd", li) for li in range(len(layers))]
     for li in reversed(range(len(layers))):
         s = layers[li]["spec"]
         plan = dict(kv.split("=") for kv in ttc.tt_linear_explain(layers[li]["mod"].desc, T).split())
@@ -256,6 +287,7 @@ def main():
             "rank": rank,
             "layers": len(specs),
             "launch": "eager" if graph is None else "hip_graph_replay",
+            "streams": 1 if args.single_stream else 2,
         },
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),

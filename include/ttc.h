@@ -89,7 +89,12 @@ typedef struct {
   int32_t in_first;                       /* 0: chain = out modes, in modes; 1: in, out */
   int32_t act_dtype;                      /* ttc_dtype of x, y, dy, dx              */
   int32_t path;                           /* ttc_path                               */
+  int32_t flags;                          /* TTC_FLAG_* bits, 0 by default          */
 } tt_linear_desc;
+
+/* tt_linear_fwd: `saved` already holds the merged halves written by
+ * tt_linear_prepare for these cores and D; skip the merge. */
+#define TTC_FLAG_PREPARED 1
 
 /*
  * Bytes of the two caller-provided device buffers for T tokens.
@@ -120,6 +125,20 @@ ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const void* x,
                          size_t scratch_bytes, ttc_stream_t stream);
 
 /*
+ * Merge step of the forward pass alone: multiplies each half of the chain
+ * (with its link diagonals, the zero entries of the split link's diagonal
+ * dropped) into `saved`.  It depends only on G and D, so it can run on a
+ * stream of its own, ahead of the forward pass; tt_linear_fwd called with
+ * desc->flags & TTC_FLAG_PREPARED then launches only the streaming kernel.
+ * The caller orders the two (e.g. an event).  T sizes `saved` as for
+ * tt_linear_workspace.
+ */
+ttc_status tt_linear_prepare(const tt_linear_desc* desc, int64_t T,
+                             const float* const* G, const float* const* D,
+                             void* saved, size_t saved_bytes,
+                             ttc_stream_t stream);
+
+/*
  * Backward: dX = dY W (skipped when dx == NULL) and dG_k = d<dY, x W^T>/dG_k.
  *   x, G, D, saved - exactly as passed to the matching tt_linear_fwd
  *   dy - T x N_out (act_dtype)
@@ -134,6 +153,24 @@ ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const void* x,
                          size_t saved_bytes, void* dx, float* const* dG,
                          void* scratch, size_t scratch_bytes,
                          ttc_stream_t stream);
+
+/*
+ * tt_linear_bwd with the core-gradient tail moved to a second stream.  The
+ * passes over dY and x (which produce dX) run on `stream`; the reduction of
+ * their partial sums and the reverse sweep through the chain (which produce
+ * only dG) are enqueued on `grad_stream` behind an event recorded on `stream`,
+ * so they overlap whatever the caller enqueues on `stream` next.  dX is
+ * complete when `stream` passes the call, dG when `grad_stream` does; scratch
+ * stays in use until then.  grad_stream == stream is exactly tt_linear_bwd.
+ * Works under HIP graph capture (the event becomes a graph edge).
+ */
+ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
+                               const void* x, const void* dy,
+                               const float* const* G, const float* const* D,
+                               const void* saved, size_t saved_bytes, void* dx,
+                               float* const* dG, void* scratch,
+                               size_t scratch_bytes, ttc_stream_t stream,
+                               ttc_stream_t grad_stream);
 
 /*
  * Planner report (host-only): writes a NUL-terminated text into buf (at most

@@ -39,6 +39,8 @@ EXPORTS = [
     "tt_linear_fwd",
     "tt_linear_bwd",
     "tt_linear_explain",
+    "tt_linear_prepare",
+    "tt_linear_bwd_split",
     "tt_linear_path_cost",
     "ttm_embed_workspace",
     "ttm_embed_fwd",
@@ -68,7 +70,11 @@ class TTLinearDesc(ctypes.Structure):
         ("in_first", ctypes.c_int32),
         ("act_dtype", ctypes.c_int32),
         ("path", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
+
+
+TTC_FLAG_PREPARED = 1
 
 
 class TTMEmbedDesc(ctypes.Structure):
@@ -102,6 +108,8 @@ def lib() -> ctypes.CDLL:
         "tt_linear_workspace": [D, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
         "tt_linear_fwd": [D, _I64, _P, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
         "tt_linear_bwd": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P],
+        "tt_linear_bwd_split": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P, _P],
+        "tt_linear_prepare": [D, _I64, pp, pp, _P, _SZ, _P],
         "tt_linear_explain": [D, _I64, ctypes.c_char_p, _SZ],
         "tt_linear_path_cost": [D, _I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                 ctypes.POINTER(ctypes.c_double)],
@@ -140,7 +148,7 @@ def _ptrs(addrs: Sequence[int] | None):
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), arr
 
 
-def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=False, path=TTC_PATH_AUTO):
+def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=False, path=TTC_PATH_AUTO, flags=0):
     d = TTLinearDesc()
     d.p, d.q = len(out_modes), len(in_modes)
     for i, n in enumerate(out_modes):
@@ -152,6 +160,7 @@ def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=Fal
     d.in_first = int(bool(in_first))
     d.act_dtype = int(act_dtype)
     d.path = int(path)
+    d.flags = int(flags)
     return d
 
 
@@ -190,6 +199,22 @@ def tt_linear_bwd(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, scratch, scr
     code = lib().tt_linear_bwd(ctypes.byref(desc), T, x, dy, g, dd, saved, saved_bytes, dx, dg, scratch,
                                scratch_bytes, stream)
     _check("tt_linear_bwd", code)
+
+
+def tt_linear_bwd_split(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, scratch, scratch_bytes, stream=0,
+                        grad_stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    dg, _dga = _ptrs(dG)
+    code = lib().tt_linear_bwd_split(ctypes.byref(desc), T, x, dy, g, dd, saved, saved_bytes, dx, dg, scratch,
+                                     scratch_bytes, stream, grad_stream)
+    _check("tt_linear_bwd_split", code)
+
+
+def tt_linear_prepare(desc, T, G, D, saved, saved_bytes, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    _check("tt_linear_prepare", lib().tt_linear_prepare(ctypes.byref(desc), T, g, dd, saved, saved_bytes, stream))
 
 
 def tt_linear_explain(desc: TTLinearDesc, T: int) -> str:

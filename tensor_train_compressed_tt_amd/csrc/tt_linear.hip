@@ -39,6 +39,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "tt_plan.hpp"
 #include "ttc_device.hpp"
@@ -352,7 +353,7 @@ __device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename 
 // ------------------------------------------------------------------------------
 // forward
 // ------------------------------------------------------------------------------
-template <typename T, int NR, bool VEC>
+template <typename T, int NR, bool VEC, int TT>
 __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __restrict__ x,
                                              const typename Elem<T>::type* __restrict__ Ac,
                                              const typename Elem<T>::type* __restrict__ Bc,
@@ -368,16 +369,17 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   constexpr int KS = Rpad / KSTEP;
   constexpr int UO = 4;                                  // output tiles per batch
   extern __shared__ __align__(16) char smem[];
-  float* zred = reinterpret_cast<float*>(smem);  // [4 waves][64 tokens][Rpad]
-  E* zl = reinterpret_cast<E*>(smem);            // [64][ZLD], reuses zred after the sum
+  constexpr int TM = 16 * TT;                     // tokens per work-group
+  float* zred = reinterpret_cast<float*>(smem);  // [4 waves][TM tokens][Rpad]
+  E* zl = reinterpret_cast<E*>(smem);            // [TM][ZLD], reuses zred after the sum
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int64_t t0 = (int64_t)blockIdx.x * TM;
 
-  f32x4 acc[4][NR];
+  f32x4 acc[TT][NR];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < TT; ++u)
 #pragma unroll
     for (int n = 0; n < NR; ++n) acc[u][n] = zero4();
 
@@ -385,36 +387,36 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   // k-steps w, w+4, ... so the four waves read adjacent 64-byte pieces
   const int nks = (int)((N_in + KSTEP - 1) / KSTEP);
   for (int kb = 0; kb < nks; kb += 4 * UNR) {
-    frag fa[UNR][4], fb[UNR][NR];
+    frag fa[UNR][TT], fb[UNR][NR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t col = (int64_t)(kb + 4 * u + w) * KSTEP + g * EPV;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) fa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
+      for (int tt = 0; tt < TT; ++tt) fa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
 #pragma unroll
       for (int n = 0; n < NR; ++n) fb[u][n] = ld_frag<T, VEC>(Ac, 16 * n + c, Rpad, col, N_in, N_in);
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int n = 0; n < NR; ++n) acc[tt][n] = Mma<T>::mma(fa[u][tt], fb[u][n], acc[tt][n]);
   }
   // lane (g, c) holds Z rows 4g+v of token tile u, rank column 16n+c
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < TT; ++u)
 #pragma unroll
     for (int n = 0; n < NR; ++n)
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) zred[(w * 64 + 16 * u + 4 * g + vv) * Rpad + 16 * n + c] = acc[u][n][vv];
+      for (int vv = 0; vv < 4; ++vv) zred[(w * TM + 16 * u + 4 * g + vv) * Rpad + 16 * n + c] = acc[u][n][vv];
   __syncthreads();
-  constexpr int PER = 64 * Rpad / 256;
+  constexpr int PER = TM * Rpad / 256;
   float zs[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int idx = threadIdx.x + 256 * i;
-    zs[i] = ((zred[idx] + zred[64 * Rpad + idx]) + zred[2 * 64 * Rpad + idx]) + zred[3 * 64 * Rpad + idx];
+    zs[i] = ((zred[idx] + zred[TM * Rpad + idx]) + zred[2 * TM * Rpad + idx]) + zred[3 * TM * Rpad + idx];
   }
   __syncthreads();
 #pragma unroll
@@ -440,18 +442,18 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     for (int uo = 0; uo < UO; ++uo) {
       const int ot = ob + 4 * uo;
       if (ot < not_) {
-        f32x4 acc2[4];
+        f32x4 acc2[TT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc2[u] = zero4();
+        for (int u = 0; u < TT; ++u) acc2[u] = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < TT; ++u)
             acc2[u] = Mma<T>::mma(fa[uo][ks], lds_frag<T>(zl + (16 * u + c) * ZLD + ks * KSTEP + g * EPV), acc2[u]);
         const int64_t o0 = (int64_t)ot * 16 + 4 * g;
         const int valid = (int)std::min<int64_t>(4, N_out - o0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < TT; ++u) {
           const int64_t t = t0 + 16 * u + c;
           if (t < T_ && valid > 0) store4<T>(y + t * N_out + o0, acc2[u], valid, vout);
         }
@@ -518,13 +520,17 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
   const int tt0 = gt * a.tpg;
   const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
   const int nitems = ntt * nsl;
-  frag sr[B::PER], zr[B::ZPER];
-  if (nitems > 0) {
-    slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tt0 * 64, a.T_, c0, a.N_out);
-    rank_fetch<T, NR>(zr, a.Z, (int64_t)tt0 * 64, a.T_);
-  }
-  int buf = 0;
-  for (int it = 0; it < nitems; ++it) {
+  // two register sets: the slab (and, at a tile start, the Z tile) of item
+  // it+2 is fetched while item it is computed from LDS
+  frag srA[B::PER], srB[B::PER], zrA[B::ZPER], zrB[B::ZPER];
+  auto fetch = [&](int it, frag* sr, frag* zr) {
+    if (it < nitems) {
+      const int tn = tt0 + it / nsl, sn = it % nsl;
+      slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_out);
+      if (sn == 0) rank_fetch<T, NR>(zr, a.Z, (int64_t)tn * 64, a.T_);
+    }
+  };
+  auto body = [&](int it, frag* sr, frag* zr, int buf) {
     const int tt = tt0 + it / nsl, sb = it % nsl;
     const int64_t t0 = (int64_t)tt * 64;
     if (sb == 0) {
@@ -535,11 +541,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
-    if (it + 1 < nitems) {
-      const int tn = tt0 + (it + 1) / nsl, sn = (it + 1) % nsl;
-      slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_out);
-      if (sn == 0) rank_fetch<T, NR>(zr, a.Z, (int64_t)tn * 64, a.T_);
-    }
+    fetch(it + 2, sr, zr);
     __syncthreads();
     // dZ: M = token (16-row tile w), N = rank, K = column of the slab
 #pragma unroll
@@ -590,7 +592,12 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
           }
       }
     }
-    buf ^= 1;
+  };
+  fetch(0, srA, zrA);
+  fetch(1, srB, zrB);
+  for (int it = 0; it < nitems; it += 2) {
+    body(it, srA, zrA, 0);
+    if (it + 1 < nitems) body(it + 1, srB, zrB, 1);
   }
   // dB^T partial of this token group: rank 16n+4g+v, column c0+s*SW+(ct*4+w)*16+c
 #pragma unroll
@@ -681,13 +688,16 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
   const int tt0 = gt * a.tpg;
   const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
   const int nitems = ntt * nsl;
-  frag sr[B::PER], zr[B::ZPER];
-  if (nitems > 0) {
-    slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tt0 * 64, a.T_, c0, a.N_in);
-    rank_fetch<T, NR>(zr, a.dZ, (int64_t)tt0 * 64, a.T_);
-  }
-  int buf = 0;
-  for (int it = 0; it < nitems; ++it) {
+  frag srA[B::PER], srB[B::PER], zrA[B::ZPER], zrB[B::ZPER];
+  auto fetch = [&](int it, frag* sr, frag* zr) {
+    if (it < nitems) {
+      const int tn = tt0 + it / nsl, sn = it % nsl;
+      slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_in);
+      if (sn == 0) rank_fetch<T, NR>(zr, a.dZ, (int64_t)tn * 64, a.T_);
+    }
+  };
+  auto body = [&](int it, frag* sr, frag* zr, int buf) {
+
     const int tt = tt0 + it / nsl, sb = it % nsl;
     const int64_t t0 = (int64_t)tt * 64;
     if (sb == 0) {
@@ -696,11 +706,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
-    if (it + 1 < nitems) {
-      const int tn = tt0 + (it + 1) / nsl, sn = (it + 1) % nsl;
-      slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_in);
-      if (sn == 0) rank_fetch<T, NR>(zr, a.dZ, (int64_t)tn * 64, a.T_);
-    }
+    fetch(it + 2, sr, zr);
     __syncthreads();
     if (a.dx) {
       // dX^T = A^T dZ^T: M = input column (tiles ct*4+w of the slab), N = token, K = rank
@@ -746,7 +752,12 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
         }
       }
     }
-    buf ^= 1;
+  };
+  fetch(0, srA, zrA);
+  fetch(1, srB, zrB);
+  for (int it = 0; it < nitems; it += 2) {
+    body(it, srA, zrA, 0);
+    if (it + 1 < nitems) body(it + 1, srB, zrB, 1);
   }
 #pragma unroll
   for (int s = 0; s < NSM; ++s) {
@@ -1100,28 +1111,32 @@ static void allow_lds(const void* kern, size_t bytes) {
   if (bytes > 65536) (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <typename T, int NR, bool VEC>
+template <typename T, int NR, bool VEC, int TT>
 static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
   typedef typename Elem<T>::type E;
-  const size_t lds = size_t(4) * 64 * 16 * NR * sizeof(float);
-  auto kern = k_fwd<T, NR, VEC>;
+  const size_t lds = size_t(4) * 16 * TT * 16 * NR * sizeof(float);
+  auto kern = k_fwd<T, NR, VEC, TT>;
   static bool lds_set = false;
   if (!lds_set) {
     allow_lds((const void*)kern, lds);
     lds_set = true;
   }
   const int vout = (P.N_out % 4) == 0 && aligned16(y);
+  const unsigned grid = (unsigned)((P.T + 16 * TT - 1) / (16 * TT));
   TraceScope ts("fwd", st);
-  hipLaunchKernelGGL(kern, dim3(P.ntiles), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
                      (const E*)(saved + P.sv_Bc), (E*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, (int)VEC, vout);
 }
 
+// 32-token work-groups until there are enough 64-token ones to give every CU two
 template <typename T, int NR>
 static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
-  if ((P.N_in % Mma<T>::EPV) == 0 && aligned16(x))
-    launch_fwd_v<T, NR, true>(P, x, saved, y, st);
-  else
-    launch_fwd_v<T, NR, false>(P, x, saved, y, st);
+  const bool vec = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x);
+  const bool big = P.ntiles >= 512;
+  if (vec && big) launch_fwd_v<T, NR, true, 4>(P, x, saved, y, st);
+  else if (vec) launch_fwd_v<T, NR, true, 2>(P, x, saved, y, st);
+  else if (big) launch_fwd_v<T, NR, false, 4>(P, x, saved, y, st);
+  else launch_fwd_v<T, NR, false, 2>(P, x, saved, y, st);
 }
 
 template <typename T, int NR, bool VY, bool VX>
@@ -1242,22 +1257,8 @@ extern "C" ttc_status tt_linear_workspace(const tt_linear_desc* desc, int64_t T,
   return TTC_OK;
 }
 
-extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const void* x, const float* const* G,
-                                    const float* const* D, void* y, void* saved, size_t saved_bytes, void* scratch,
-                                    size_t scratch_bytes, ttc_stream_t stream) {
-  (void)scratch;
-  (void)scratch_bytes;
-  LinearPlan P;
-  ttc_status st = make_linear_plan(desc, T, &P);
-  if (st != TTC_OK) return st;
-  if ((st = check_chain(P, G, D)) != TTC_OK) return st;
-  if (T == 0) return TTC_OK;
-  if (!x || !y || !saved) return TTC_ERR_NULL;
-  if (!aligned16(x) || !aligned16(y) || !aligned16(saved)) return TTC_ERR_ALIGN;
-  if (saved_bytes < P.sv_total) return TTC_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  char* sv = static_cast<char*>(saved);
+namespace ttc {
+static void launch_merge(const LinearPlan& P, const float* const* G, const float* const* D, char* sv, hipStream_t s) {
   MergeArgs m;
   memset(&m, 0, sizeof(m));
   m.c = chain_ptrs(P, G, D);
@@ -1283,20 +1284,59 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   m.Bc = sv + P.sv_Bc;
   m.BcT = sv + P.sv_BcT;
   m.chain = reinterpret_cast<float*>(sv + P.sv_chain);
-  {
-    const size_t lds = size_t(P.max_rank) * P.max_rank * sizeof(float);
-    static bool lds_set[2] = {false, false};
-    const void* kern = P.act == TTC_BF16 ? (const void*)k_merge<bf16_t> : (const void*)k_merge<float>;
-    if (!lds_set[P.act]) {
-      allow_lds(kern, size_t(TTC_MAX_RANK) * TTC_MAX_RANK * sizeof(float));
-      lds_set[P.act] = true;
-    }
-    TraceScope ts("merge", s);
-    if (P.act == TTC_BF16)
-      hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
-    else
-      hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
-  }
+  const size_t lds = size_t(P.max_rank) * P.max_rank * sizeof(float);
+  TraceScope ts("merge", s);
+  if (P.act == TTC_BF16)
+    hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
+  else
+    hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
+}
+
+// one event orders the two streams of a split backward; a wait captures the
+// event's state when it is enqueued, so the event can be recorded again
+// right away
+static hipEvent_t split_event() {
+  static std::mutex mu;
+  static hipEvent_t ev = nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ev && hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) ev = nullptr;
+  return ev;
+}
+static std::mutex g_split_mu;
+}  // namespace ttc
+
+extern "C" ttc_status tt_linear_prepare(const tt_linear_desc* desc, int64_t T, const float* const* G,
+                                        const float* const* D, void* saved, size_t saved_bytes,
+                                        ttc_stream_t stream) {
+  LinearPlan P;
+  ttc_status st = make_linear_plan(desc, T, &P);
+  if (st != TTC_OK) return st;
+  if ((st = check_chain(P, G, D)) != TTC_OK) return st;
+  if (!saved) return TTC_ERR_NULL;
+  if (!aligned16(saved)) return TTC_ERR_ALIGN;
+  if (saved_bytes < P.sv_total) return TTC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  launch_merge(P, G, D, static_cast<char*>(saved), reinterpret_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const void* x, const float* const* G,
+                                    const float* const* D, void* y, void* saved, size_t saved_bytes, void* scratch,
+                                    size_t scratch_bytes, ttc_stream_t stream) {
+  (void)scratch;
+  (void)scratch_bytes;
+  LinearPlan P;
+  ttc_status st = make_linear_plan(desc, T, &P);
+  if (st != TTC_OK) return st;
+  if ((st = check_chain(P, G, D)) != TTC_OK) return st;
+  if (T == 0) return TTC_OK;
+  if (!x || !y || !saved) return TTC_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(saved)) return TTC_ERR_ALIGN;
+  if (saved_bytes < P.sv_total) return TTC_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  char* sv = static_cast<char*>(saved);
+  if (!(desc->flags & TTC_FLAG_PREPARED)) launch_merge(P, G, D, sv, s);
   const bool ok = P.act == TTC_BF16 ? dispatch_fwd<bf16_t>(P, x, sv, y, s) : dispatch_fwd<float>(P, x, sv, y, s);
   if (!ok) return TTC_ERR_UNSUPPORTED;
   return hip_status();
@@ -1306,6 +1346,14 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
                                     const float* const* G, const float* const* D, const void* saved,
                                     size_t saved_bytes, void* dx, float* const* dG, void* scratch,
                                     size_t scratch_bytes, ttc_stream_t stream) {
+  return tt_linear_bwd_split(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, scratch, scratch_bytes, stream,
+                             stream);
+}
+
+extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T, const void* x, const void* dy,
+                                          const float* const* G, const float* const* D, const void* saved,
+                                          size_t saved_bytes, void* dx, float* const* dG, void* scratch,
+                                          size_t scratch_bytes, ttc_stream_t stream, ttc_stream_t grad_stream) {
   LinearPlan P;
   ttc_status st = make_linear_plan(desc, T, &P);
   if (st != TTC_OK) return st;
@@ -1313,7 +1361,8 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
   if (!dG) return TTC_ERR_NULL;
   for (int k = 0; k < P.d; ++k)
     if (!dG[k]) return TTC_ERR_NULL;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t s_main = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t s = reinterpret_cast<hipStream_t>(grad_stream);  // the core-gradient tail
   (void)hipGetLastError();
   if (T == 0) {
     for (int k = 0; k < P.d; ++k) {
@@ -1329,9 +1378,15 @@ extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const
   if (saved_bytes < P.sv_total || scratch_bytes < P.sc_total) return TTC_ERR_WORKSPACE;
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
-  const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s)
-                                    : dispatch_bwd<float>(P, x, dy, sv, dx, sc, s);
+  const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s_main)
+                                    : dispatch_bwd<float>(P, x, dy, sv, dx, sc, s_main);
   if (!ok) return TTC_ERR_UNSUPPORTED;
+  if (s != s_main) {
+    hipEvent_t ev = split_event();
+    if (!ev) return TTC_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_split_mu);
+    if (hipEventRecord(ev, s_main) != hipSuccess || hipStreamWaitEvent(s, ev, 0) != hipSuccess) return TTC_ERR_HIP;
+  }
   // partial sums -> gradients of the two half products; a half made of one
   // core receives its gradient directly
   float* dL = P.s == 1 ? dG[0] : (float*)(sc + P.sc_dL);

@@ -30,6 +30,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   if (desc->in_first != 0 && desc->in_first != 1) return TTC_ERR_SHAPE;
   if (desc->path < TTC_PATH_AUTO || desc->path > TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
   if (desc->path == TTC_PATH_SEQUENTIAL || desc->path == TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
+  if (desc->flags & ~TTC_FLAG_PREPARED) return TTC_ERR_UNSUPPORTED;
   const int d = p + q;
   P->p = p;
   P->q = q;
@@ -114,7 +115,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->ntiles = (int)((T + kTileT - 1) / kTileT);
   const int nt = std::max(1, P->ntiles);
   P->sw = slab_cols(P->es);
-  const int target = 256;
+  const int target = 512;  // two work-groups per CU
   auto choose = [&](int64_t ncols, int maxs, bool dy, int* gc, int* gt, int* nsl, int* tpg) {
     const int chunks = (int)std::max<int64_t>(1, (ncols + P->sw - 1) / P->sw);
     const int gc_min = (chunks + maxs - 1) / maxs;

@@ -11,11 +11,13 @@ import torch
 from . import (
     TTC_BF16,
     TTC_F32,
+    TTC_FLAG_PREPARED,
     TTC_PATH_AUTO,
     make_linear_desc,
     make_ttm_desc,
-    tt_linear_bwd,
+    tt_linear_bwd_split,
     tt_linear_fwd,
+    tt_linear_prepare,
     tt_linear_workspace,
     ttm_embed_bwd,
     ttm_embed_fwd,
@@ -57,6 +59,8 @@ class TTLinear:
         self.n_out = math.prod(self.out_modes)
         self.n_in = math.prod(self.in_modes)
         self.desc = make_linear_desc(self.out_modes, self.in_modes, self.ranks, _ACT[dtype], in_first, path)
+        self.desc_prepared = make_linear_desc(self.out_modes, self.in_modes, self.ranks, _ACT[dtype], in_first, path,
+                                              TTC_FLAG_PREPARED)
         modes = list(self.in_modes) + list(self.out_modes) if in_first else list(self.out_modes) + list(self.in_modes)
         self.core_shapes = [(self.ranks[k], modes[k], self.ranks[k + 1]) for k in range(len(modes))]
 
@@ -77,7 +81,17 @@ class TTLinear:
         for k, v in enumerate(D):
             _need(v, f"D {k}", torch.float32, (self.core_shapes[k][2],))
 
-    def forward(self, x, cores, D, out=None, saved=None):
+    def prepare(self, T, cores, D, saved=None):
+        """Merge the cores into `saved` on the current stream (see tt_linear_prepare)."""
+        self._check_chain(cores, D)
+        sb, _ = self.workspace(T)
+        if saved is None:
+            saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=cores[0].device)
+        tt_linear_prepare(self.desc, T, [c.data_ptr() for c in cores], [v.data_ptr() for v in D], saved.data_ptr(),
+                          saved.numel(), _stream())
+        return saved
+
+    def forward(self, x, cores, D, out=None, saved=None, prepared=False):
         T = int(x.shape[0])
         _need(x, "x", self.dtype, (T, self.n_in))
         self._check_chain(cores, D)
@@ -86,12 +100,16 @@ class TTLinear:
         _need(out, "out", self.dtype, (T, self.n_out))
         sb, _ = self.workspace(T)
         if saved is None:
+            if prepared:
+                raise ValueError("prepared=True needs the saved buffer filled by prepare()")
             saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=x.device)
-        tt_linear_fwd(self.desc, T, x.data_ptr(), [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
+        desc = self.desc_prepared if prepared else self.desc
+        tt_linear_fwd(desc, T, x.data_ptr(), [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
                       out.data_ptr(), saved.data_ptr(), saved.numel(), None, 0, _stream())
         return out, saved
 
-    def backward(self, x, dy, cores, D, saved, want_dx=True, dx=None, dG=None, scratch=None):
+    def backward(self, x, dy, cores, D, saved, want_dx=True, dx=None, dG=None, scratch=None, grad_stream=None):
+        """dX on the current stream; dG on `grad_stream` (a torch.cuda.Stream) when given."""
         T = int(x.shape[0])
         _need(x, "x", self.dtype, (T, self.n_in))
         _need(dy, "dy", self.dtype, (T, self.n_out))
@@ -103,10 +121,12 @@ class TTLinear:
             dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
         if dG is None:
             dG = [torch.empty(s, dtype=torch.float32, device=x.device) for s in self.core_shapes]
-        tt_linear_bwd(self.desc, T, x.data_ptr(), dy.data_ptr(), [c.data_ptr() for c in cores],
-                      [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
-                      dx.data_ptr() if want_dx else None, [g.data_ptr() for g in dG], scratch.data_ptr(),
-                      scratch.numel(), _stream())
+        main = _stream()
+        gs = main if grad_stream is None else grad_stream.cuda_stream
+        tt_linear_bwd_split(self.desc, T, x.data_ptr(), dy.data_ptr(), [c.data_ptr() for c in cores],
+                            [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
+                            dx.data_ptr() if want_dx else None, [g.data_ptr() for g in dG], scratch.data_ptr(),
+                            scratch.numel(), main, gs)
         return (dx if want_dx else None), dG
 
 

@@ -188,3 +188,100 @@ def test_bitwise_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     for g1, g2 in zip(a[2], b[2]):
         assert np.array_equal(g1, g2)
+
+
+def test_prepared_and_split_stream_match_single_stream():
+    """tt_linear_prepare + TTC_FLAG_PREPARED forward and the backward with a
+    separate grad stream give bitwise the same results as the plain calls."""
+    ttc = _ttc()
+    spec = synth.config_layers(2, 30)[4]
+    layer = synth.make_tt_layer(2, 77, spec, 700, 0.40, "bf16")
+    ref = _run(spec, layer, "bf16")
+    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, torch.bfloat16)
+    cores, D, x, dy = _to_dev(layer, "bf16")
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        saved = mod.prepare(700, cores, D)
+        ev = torch.cuda.Event()
+        ev.record(side)
+    main.wait_event(ev)
+    y, _ = mod.forward(x, cores, D, saved=saved, prepared=True)
+    dx, dG = mod.backward(x, dy, cores, D, saved, grad_stream=side)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy()
+    assert np.array_equal(f(y), ref[0]) and np.array_equal(f(dx), ref[1])
+    for g, r in zip(dG, ref[2]):
+        assert np.array_equal(f(g), r)
+
+
+def test_graph_replay_two_streams_matches_eager():
+    """A captured two-layer step (merges and core-gradient tails on a side
+    stream) replayed several times, with eager work and synchronisation in
+    between, reproduces the eager results every time."""
+    ttc = _ttc()
+    specs = synth.config_layers(2, 16)[3:5]
+    T = 300
+    mods, data = [], []
+    for i, spec in enumerate(specs):
+        layer = synth.make_tt_layer(2, 200 + i, spec, T, 0.40, "bf16")
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, torch.bfloat16)
+        cores, D, x, dy = _to_dev(layer, "bf16")
+        sb, cb = mod.workspace(T)
+        bufs = dict(saved=torch.empty(sb, dtype=torch.uint8, device="cuda"),
+                    scratch=torch.empty(cb, dtype=torch.uint8, device="cuda"),
+                    y=torch.empty((T, spec.n_out), dtype=torch.bfloat16, device="cuda"),
+                    dx=torch.empty((T, spec.n_in), dtype=torch.bfloat16, device="cuda"),
+                    dG=[torch.empty(s, device="cuda") for s in mod.core_shapes])
+        mods.append(mod)
+        data.append((cores, D, x, dy, bufs))
+    side = torch.cuda.Stream()
+
+    def step():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        evs = []
+        with torch.cuda.stream(side):
+            for mod, (cores, D, x, dy, b) in zip(mods, data):
+                mod.prepare(T, cores, D, saved=b["saved"])
+                e = torch.cuda.Event()
+                e.record(side)
+                evs.append(e)
+        for mod, e, (cores, D, x, dy, b) in zip(mods, evs, data):
+            main.wait_event(e)
+            mod.forward(x, cores, D, out=b["y"], saved=b["saved"], prepared=True)
+        for mod, (cores, D, x, dy, b) in reversed(list(zip(mods, data))):
+            mod.backward(x, dy, cores, D, b["saved"], dx=b["dx"], dG=b["dG"], scratch=b["scratch"], grad_stream=side)
+        main.wait_stream(side)
+
+    def snapshot():
+        out = []
+        for _, (_, _, _, _, b) in zip(mods, data):
+            out += [b["y"].float().cpu(), b["dx"].float().cpu()] + [g.cpu().clone() for g in b["dG"]]
+        return out
+
+    step()
+    torch.cuda.synchronize()
+    want = snapshot()
+    g = torch.cuda.CUDAGraph()
+    s0 = torch.cuda.Stream()
+    s0.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s0):
+        step()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for _, (_, _, _, _, b) in zip(mods, data):  # eager work between replays
+            b["y"].zero_()
+            b["dx"].zero_()
+            for t in b["dG"]:
+                t.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for a, b2 in zip(got, want):
+            assert torch.equal(a, b2), f"replay {rep} differs"
