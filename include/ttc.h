@@ -187,40 +187,54 @@ ttc_status tt_linear_path_cost(const tt_linear_desc* desc, int64_t T,
 
 /* TTM embedding descriptor (host memory). */
 #define TTC_TTM_MAX_MODES 8
+#define TTC_TTM_MAX_IDS 16384 /* ids per call (the sort runs in one work-group) */
 typedef struct {
   int32_t d;                              /* number of cores, 1..8                   */
   int32_t vocab_modes[TTC_TTM_MAX_MODES]; /* m_k; vocabulary = prod m_k < 2^31       */
-  int32_t dim_modes[TTC_TTM_MAX_MODES];   /* n_k; embedding dim = prod n_k           */
-  int32_t ranks[TTC_TTM_MAX_MODES + 1];   /* r_0..r_d, r_0 = r_d = 1                 */
+  int32_t dim_modes[TTC_TTM_MAX_MODES];   /* n_k; embedding dim = prod n_k <= 2^24   */
+  int32_t ranks[TTC_TTM_MAX_MODES + 1];   /* r_0..r_d, r_0 = r_d = 1, r_k <= 128     */
   int32_t accumulate;                     /* bwd: 1 = add into dF, 0 = overwrite     */
 } ttm_embed_desc;
 
 /*
- * Bytes of the saved / scratch buffers for a lookup of T ids.  `saved` is
- * written by ttm_embed_fwd and read by ttm_embed_bwd; its first part has a
- * documented layout (see TTM_SAVED_* below) so that the integer results can
- * be inspected.  Host-only.
+ * Bytes of the saved / scratch buffers for a lookup of T ids (host-only).
+ * `saved` is written by ttm_embed_fwd and read by ttm_embed_bwd; `scratch`
+ * is only used during a call.  TTC_ERR_UNSUPPORTED when T > TTC_TTM_MAX_IDS
+ * or when one level's prefix product and core slice exceed 64 KB of LDS.
+ *
+ * The head of `saved` has a fixed layout, so that the integer results of the
+ * deduplication can be read back (all int32; U = number of distinct valid
+ * ids; Tv = number of valid ids):
+ *   word 0            U
+ *   word 1            1 if some id was outside [0, prod m_k), else 0
+ *   word 2            number of pieces (private)
+ *   word 3            Tv
+ *   words 4 .. 4+d    number of distinct digit prefixes (v_1..v_l), l = 1..d
+ *   at byte 128                 order[T]: token positions sorted by (id, position);
+ *                               the Tv valid ones first
+ *   at byte 128 + A             inverse[T]: index of each token's id in the
+ *                               distinct list, -1 for an invalid id
+ *   at byte 128 + 2A            uids[T]: the distinct valid ids, ascending (U used)
+ *   at byte 128 + 3A            seg[T+1]: segment offsets into order (U+1 used)
+ * where A = 4*T rounded up to a multiple of 256.  The rest is private.
  */
 ttc_status ttm_embed_workspace(const ttm_embed_desc* desc, int64_t T,
                                size_t* saved_bytes, size_t* scratch_bytes);
 
 /*
- * Forward lookup: out[t] = E[ids[t]] for t < T.
- *   ids - T int64 ids, each in [0, prod m_k); an id out of range gives a zero
- *         row and sets the device error flag (see ttm_embed_status)
+ * Forward lookup: out[t] = E[ids[t]] for t < T, where
+ *   E[(v_1..v_d), (c_1..c_d)] = F_1[0,v_1,c_1,:] D_1 F_2[:,v_2,c_2,:] ... F_d[:,v_d,c_d,0]
+ * (NeurIPS 2024 poster page of CoMERA, figure on the TT and TTM structures).
+ * Each distinct id is evaluated once and each distinct digit prefix once
+ * (project page, "Making small tensor operations fast on GPUs", embedding
+ * lookup without repeated work); repeated ids get bitwise-identical rows.
+ *   ids - T int64 ids; an id outside [0, prod m_k) gives a zero row and sets
+ *         word 1 of `saved`
  *   F   - host array of d device pointers, fp32 cores (r_{k-1}, m_k, n_k, r_k)
  *   D   - host array of d-1 device pointers (fp32 length r_k), or NULL for the
  *         identity on every link
  *   out - T x prod n_k fp32, overwritten
- * saved layout (int32 words, U = number of distinct ids):
- *   [0]                 U
- *   [1]                 error flag (0 = ok, 1 = an id out of range)
- *   [2 .. 2+T)          order: token positions sorted by (id, position)
- *   [2+T .. 2+2T)       inverse: index into the unique list of each token
- *   [2+2T .. 2+3T)      unique ids, ascending (first U used)
- *   [2+3T .. 3+4T)      segment offsets into order (first U+1 used)
- *   [3+4T .. 3+5T)      first digit... no: digits of each unique id follow in
- *                       the rest of the buffer, which is private.
+ * out, saved and scratch must be 16-byte aligned (TTC_ERR_ALIGN).
  */
 ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T,
                          const int64_t* ids, const float* const* F,
@@ -229,11 +243,15 @@ ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T,
                          ttc_stream_t stream);
 
 /*
- * Backward: dF_k = d( sum_t <dout[t], E[ids[t]]> ) / dF_k.
- *   ids, F, D, saved - as passed to the matching ttm_embed_fwd
- *   dout - T x prod n_k fp32
+ * Backward: dF_k = d( sum_t <dout[t], E[ids[t]]> ) / dF_k, D held fixed.
+ * The output gradients of equal ids are summed along their sorted segment
+ * (no floating-point atomics; the result is bitwise reproducible).
+ *   ids  - not read (the sorted structure comes from `saved`); may be NULL
+ *   F, D, saved - as passed to the matching ttm_embed_fwd; saved unchanged
+ *   dout - T x prod n_k fp32, 16-byte aligned
  *   dF   - host array of d device pointers, fp32, shapes of the cores;
  *          overwritten, or added to when desc->accumulate
+ * Invalid ids contribute nothing.  T = 0 zeroes dF (unless accumulate).
  */
 ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T,
                          const int64_t* ids, const float* dout,

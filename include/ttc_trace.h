@@ -32,7 +32,8 @@ ttc_status ttc_trace_count(int32_t* n);
 /*
  * Record i (0-based, in launch order): the kernel's name (static storage, one
  * of "merge", "fwd", "bwd_dy", "dz_sum", "bwd_dx", "reduce", "core", "zero",
- * "ttm_sort", "ttm_rows", "ttm_bwd_seg", "ttm_bwd_core") and its duration in
+ * "ttm_sort", "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level",
+ * "ttm_reduce") and its duration in
  * milliseconds.  Waits for the record's end event.
  */
 ttc_status ttc_trace_get(int32_t i, const char** name, float* ms);

@@ -177,3 +177,69 @@ def test_merged_order_wins_at_large_batch_and_loses_at_batch_one():
         assert ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_MERGED)[0] < ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_SEQUENTIAL)[0]
     assert ttc.tt_linear_path_cost(d, 1, ttc.TTC_PATH_SEQUENTIAL)[0] < ttc.tt_linear_path_cost(d, 1, ttc.TTC_PATH_MERGED)[0]
     assert "path=merged" in ttc.tt_linear_explain(d, 4096)
+
+
+# ---- TTM embedding -------------------------------------------------------------
+
+def _ttm(vocab=(32, 32, 32), dims=(12, 8, 8), ranks=(1, 16, 16, 1), accumulate=False):
+    return ttc.make_ttm_desc(vocab, dims, ranks, accumulate)
+
+
+def test_ttm_workspace_holds_documented_head_and_products():
+    T = 16384
+    sb, cb = ttc.ttm_embed_workspace(_ttm(), T)
+    A = ((4 * T + 255) // 256) * 256
+    # header, order, inverse, distinct ids, segment offsets come first
+    assert sb >= 128 + 3 * A + 4 * (T + 1)
+    # the level-1 prefix products: at most 32*32 prefixes of 96 x 16 floats
+    assert sb >= 1024 * 96 * 16 * 4
+    # scratch: the backward's piece sums are at most T rows of 768 floats
+    assert cb >= T * 768 * 4
+    s1, c1 = ttc.ttm_embed_workspace(_ttm(), 1000)
+    assert s1 < sb and c1 < cb
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ranks=(2, 16, 16, 1)), 3),          # r_0 != 1
+    (dict(ranks=(1, 0, 16, 1)), 3),           # r_k < 1
+    (dict(ranks=(1, 200, 16, 1)), 3),         # r_k > 128
+    (dict(vocab=(32, 0, 32)), 2),             # empty mode
+    (dict(vocab=(2048, 2048, 2048), dims=(2, 2, 2)), 2),  # vocabulary >= 2^31
+])
+def test_ttm_bad_descriptors(kw, code):
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_workspace(_ttm(**kw), 64)
+    assert e.value.code == code
+
+
+def test_ttm_limits():
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_workspace(_ttm(), 16385)
+    assert e.value.code == 7
+    # one level's product and core slice must fit 64 KB of LDS
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_workspace(_ttm(vocab=(4, 4), dims=(64, 64), ranks=(1, 128, 1)), 64)
+    assert e.value.code == 7
+
+
+def test_ttm_errors_before_launch():
+    d = _ttm()
+    sb, cb = ttc.ttm_embed_workspace(d, 64)
+    F = [16] * 3
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_fwd(d, 64, None, F, None, 16, 16, sb, 16, cb)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_fwd(d, 64, 16, F, None, 24, 16, sb, 16, cb)
+    assert e.value.code == 5
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_fwd(d, 64, 16, F, None, 16, 16, sb - 1, 16, cb)
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_fwd(d, 64, 16, [16, 0, 16], None, 16, 16, sb, 16, cb)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_bwd(d, 64, None, 16, F, None, 16, sb, [16] * 3, 16, cb - 1)
+    assert e.value.code == 6
+    # T = 0 forward is a no-op
+    ttc.ttm_embed_fwd(d, 0, None, F, None, None, None, 0, None, 0)
