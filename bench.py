@@ -1,13 +1,17 @@
 #!/usr/bin/env python3
 """TT-linear fwd+bwd throughput on one MI355X.
 
-One step = the forward pass of six TT-linear layers shaped like one encoder of
-the CoMERA pages' six-encoder transformer (Q, K, V, O 768->768 with modes
+One step = a TTM embedding lookup of the step's T ids (vocabulary 32^3 with
+modes (32,32,32), rows of 768 = (12,8,8), ranks (1,16,16,1), Zipf(1.1) ids),
+the forward pass of six TT-linear layers shaped like one encoder of the
+CoMERA pages' six-encoder transformer (Q, K, V, O 768->768 with modes
 (12,8,8)x(12,8,8); FFN 768->3072 and 3072->768 with 3072 = (12,16,16)),
-followed by their backward passes in reverse order (input gradients and core
-gradients), over T = 128 x 128 = 16384 tokens, bf16 activations with fp32
-accumulation, TT rank 30 with 40% of every link diagonal zeroed.  Inputs are
-seeded synthetic data already resident in HBM.
+their backward passes in reverse order (input gradients and core gradients)
+and the embedding's backward into its core gradients, over T = 128 x 128 =
+16384 tokens; TT-linear activations bf16 with fp32 accumulation, TT rank 30
+with 40% of every link diagonal zeroed; the embedding is fp32.  Inputs are
+seeded synthetic data already resident in HBM.  --no-ttm drops the
+embedding from the step.
 
 Prints one JSON line (see the design doc for every field).  Only rank 0 of a single
 GPU runs; --gpus above 1 is refused.
@@ -41,6 +45,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--single-stream", action="store_true",
                     help="run merges and core-gradient tails on the main stream too (no overlap)")
+    ap.add_argument("--no-ttm", action="store_true", help="time the TT-linear layers only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     return ap.parse_args()
@@ -66,8 +71,9 @@ def step_bytes(layers, T, es):
     return out
 
 
-def cpu_baseline(layers_host, T_cpu):
-    """The fp64 oracle, as it stands, on the first T_cpu tokens of every layer."""
+def cpu_baseline(layers_host, T_cpu, ttm_host=None):
+    """The fp64 oracle, as it stands, on the first T_cpu tokens of every layer
+    (and of the embedding lookup when the step has one)."""
     import numpy as np
 
     import oracle
@@ -85,9 +91,14 @@ def cpu_baseline(layers_host, T_cpu):
         dy = L["dy"][:T_cpu].astype(np.float64)
         oracle.tt_linear_forward(x, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
         oracle.tt_linear_backward(x, dy, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
+    what = f"all {len(layers_host)} TT-linear layers"
+    if ttm_host is not None:
+        oracle.ttm_forward(ttm_host["ids"][:T_cpu], ttm_host["cores"])
+        oracle.ttm_backward(ttm_host["ids"][:T_cpu], ttm_host["dout"][:T_cpu], ttm_host["cores"])
+        what = "the TTM embedding lookup and " + what
     dt = time.perf_counter() - t0
     return {"value": T_cpu / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd of all {len(layers_host)} layers on the first {T_cpu} tokens "
+            "sample": f"fp64 oracle fwd+bwd of {what} on the first {T_cpu} tokens "
                       f"({dt:.1f} s wall)"}
 
 
@@ -147,22 +158,56 @@ def main():
         del L
     scratch = torch.empty(max_scratch, dtype=torch.uint8, device=dev) if args.single_stream else None
     sizes = step_bytes(host, T, es)
+
+    # ---- the embedding lookup of the step's T ids ------------------------------
+    ttm = None
+    ttm_host = None
+    if not args.no_ttm:
+        w = synth.make_ttm(3, T=T)
+        sp = w["spec"]
+        emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks)
+        tsb, tcb = emb.workspace(T)
+        ttm = {"emb": emb, "F": [torch.from_numpy(c).to(dev) for c in w["cores"]],
+               "ids": torch.from_numpy(w["ids"]).to(dev), "dout": torch.from_numpy(w["dout"]).to(dev),
+               "out": torch.empty((T, sp.dim), dtype=torch.float32, device=dev),
+               "dF": [torch.empty(c.shape, dtype=torch.float32, device=dev) for c in w["cores"]],
+               "saved": torch.empty(tsb, dtype=torch.uint8, device=dev),
+               "scratch": torch.empty(tcb, dtype=torch.uint8, device=dev), "d": len(sp.vocab_modes),
+               "dim": sp.dim}
+        if not args.no_cpu_baseline:
+            ttm_host = {"ids": w["ids"][: args.cpu_tokens].copy(), "dout": w["dout"][: args.cpu_tokens].copy(),
+                        "cores": w["cores"]}
+        del w
+
+    def ttm_fwd():
+        if ttm is not None:
+            ttm["emb"].forward(ttm["ids"], ttm["F"], None, out=ttm["out"], saved=ttm["saved"],
+                               scratch=ttm["scratch"])
+
+    def ttm_bwd():
+        if ttm is not None:
+            ttm["emb"].backward(ttm["ids"], ttm["dout"], ttm["F"], None, ttm["saved"], dF=ttm["dF"],
+                                scratch=ttm["scratch"])
     side = torch.cuda.Stream()  # default priority
 
     def step_single():
+        ttm_fwd()
         for L in layers:
             L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"])
         for L in reversed(layers):
             L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
                               scratch=scratch)
+        ttm_bwd()
 
     def step_overlap():
         # The merges depend only on the cores and D, the core-gradient tails
         # produce only dG: both go to a side stream.  The main stream carries
-        # the dependent chain of streaming passes (forward over the layers,
-        # then dX backward through them in reverse order).
+        # the dependent chain of streaming passes (embedding lookup, forward
+        # over the layers, dX backward through them in reverse order, then the
+        # embedding's backward).
         main = torch.cuda.current_stream()
         side.wait_stream(main)
+        ttm_fwd()
         ready = []
         with torch.cuda.stream(side):
             for L in layers:
@@ -176,6 +221,7 @@ def main():
         for L in reversed(layers):
             L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
                               scratch=L["scratch"], grad_stream=side)
+        ttm_bwd()
         main.wait_stream(side)
 
     step = step_single if args.single_stream else step_overlap
@@ -208,6 +254,10 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     tokens_per_s = T / (ms_per_step / 1e3)
     bytes_per_step = sum(s["fwd"] + s["bwd_dy"] + s["bwd_dx"] for s in sizes)
+    # embedding: read the ids, write the rows; read the row gradients
+    ttm_sizes = {} if ttm is None else {"ttm_sort": T * 8, "ttm_gather": T * ttm["dim"] * 4,
+                                        "ttm_seg": T * ttm["dim"] * 4}
+    bytes_per_step += sum(ttm_sizes.values())
     step_gbps = bytes_per_step / (ms_per_step / 1e3) / 1e9
 
     # ---- per-kernel durations: the same steps, launched eagerly with HIP events
@@ -222,6 +272,10 @@ def main():
     # launch order of one step: per layer merge, fwd; then per layer (reversed)
     # bwd_dy, bwd_dx, reduce, core_step x n
     expect = []
+    nlev = 0 if ttm is None else ttm["d"] - 1
+    ttm_f = [] if ttm is None else [("ttm_sort", "ttm")] + [("ttm_level", "ttm")] * nlev + [("ttm_gather", "ttm")]
+    ttm_b = [] if ttm is None else [("ttm_seg", "ttm")] + [("ttm_bwd_level", "ttm")] * nlev + [("ttm_reduce", "ttm")]
+    expect += ttm_f
     if args.single_stream:
         for li in range(len(layers)):
             expect += [("merge", li), ("fwd", li)]
@@ -234,6 +288,7 @@ def main():
         halves = [len(s.out_modes), len(s.in_modes)]
         expect += [("bwd_dy", li)] + ([("dz_sum", li)] if ndy > 1 else []) + [("bwd_dx", li), ("reduce", li)]
         expect += [("core", li)] * (max(halves) - 1)
+    expect += ttm_b
     assert len(recs) == len(expect) * args.steps, (len(recs), len(expect))
     for i, (name, ms) in enumerate(recs):
         ename, li = expect[i % len(expect)]
@@ -241,7 +296,7 @@ def main():
         d = per.setdefault(name, {"ms": 0.0, "bytes": 0.0, "launches": 0})
         d["ms"] += ms
         d["launches"] += 1
-        d["bytes"] += sizes[li].get(name, 0)
+        d["bytes"] += (ttm_sizes if li == "ttm" else sizes[li]).get(name, 0)
     for d in per.values():
         d["avg_us"] = 1e3 * d["ms"] / d["launches"]
         d["gbps"] = d["bytes"] / (d["ms"] / 1e3) / 1e9 if d["bytes"] else None
@@ -260,9 +315,17 @@ def main():
         "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
     }
 
+    ttm_summary = None
+    if ttm is not None:
+        tk = [k for k in per if k.startswith("ttm_")]
+        t_ms = sum(per[k]["ms_per_step"] for k in tk)
+        tb = sum(ttm_sizes.values())
+        ttm_summary = {"kernel_us_per_step": round(1e3 * t_ms, 2), "algorithmic_bytes": tb,
+                       "gbps": round(tb / (t_ms / 1e3) / 1e9, 1)}
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host[:6], args.cpu_tokens)
+        cpu = cpu_baseline(host[:6], args.cpu_tokens, ttm_host)
 
     wl = {1: "config 1", 2: "config 2", 4: "config 4"}[cfg]
     out = {
@@ -279,7 +342,7 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": f"{wl}: {len(specs)} TT-linear layers (fwd then bwd in reverse), "
+            "workload": f"{wl}{'' if ttm is None else ' + config 3 embedding'}: {len(specs)} TT-linear layers (fwd then bwd in reverse), "
                         f"{'4x 768->768, 768->3072, 3072->768' if cfg != 4 else '24x (4x 1024->1024, 1024->4096, 4096->1024)'}, "
                         f"{dt} activations, fp32 accumulate, T={T} tokens, TT rank {rank}, "
                         f"{int(zf * 100)}% of each link diagonal zeroed",
@@ -288,12 +351,15 @@ def main():
             "layers": len(specs),
             "launch": "eager" if graph is None else "hip_graph_replay",
             "streams": 1 if args.single_stream else 2,
+            "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "
+                                                  "fp32, Zipf(1.1) ids",
         },
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": bytes_per_step,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in per.items()},
+        "embedding": ttm_summary,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

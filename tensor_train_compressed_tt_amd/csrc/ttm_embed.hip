@@ -49,6 +49,7 @@ constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kChunk = 32;          // sorted positions per piece chunk
 constexpr int kHdrWords = 32;
 constexpr int kTtmThreads = 256;
+constexpr int kLevelThreads = 128;  // per-node work-groups: many resident per CU
 constexpr size_t kTtmMaxLds = 65536;
 
 // header words of `saved`
@@ -81,6 +82,17 @@ struct TtmPlan {
 // ------------------------------------------------------------------------------
 // the sort work-group
 // ------------------------------------------------------------------------------
+// x / M for x < 2^31 by one 64-bit multiply: (x * magic) >> shift, with
+// shift = 32 + ceil(log2 M) and magic = ceil(2^shift / M); the error term is
+// below 1/(2M), so the floor is exact.
+struct FastDiv {
+  uint64_t magic;
+  int shift;
+};
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
+  return (uint32_t)(((uint64_t)x * f.magic) >> f.shift);
+}
+
 struct SortArgs {
   const int64_t* ids;
   int n;
@@ -88,7 +100,8 @@ struct SortArgs {
   int kbits;
   int d;
   int m[TTC_TTM_MAX_MODES];
-  uint32_t Mgt[TTC_TTM_MAX_MODES];
+  FastDiv div_pre[TTC_TTM_MAX_MODES];  // x / prod m_{>l}
+  FastDiv div_m[TTC_TTM_MAX_MODES];    // x / m_l
   int dbits[TTC_TTM_MAX_MODES];
   int nch;
   int32_t* hdr;
@@ -107,6 +120,14 @@ struct SortArgs {
   int32_t* list_off[TTC_TTM_MAX_MODES];
 };
 
+// Work-group barrier that orders LDS accesses only: global stores issued
+// before it are not waited for (a full __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum of one value per thread over the work-group; *total
 // receives the sum.  Contains barriers: every thread must call it.
 __device__ uint32_t block_exscan(uint32_t v, uint32_t* s_red, uint32_t* total) {
@@ -118,7 +139,7 @@ __device__ uint32_t block_exscan(uint32_t v, uint32_t* s_red, uint32_t* total) {
     if (lane >= off) x += y;
   }
   if (lane == 63) s_red[w] = x;
-  __syncthreads();
+  lds_barrier();
   if (w == 0) {
     const uint32_t t0 = lane < kSortWaves ? s_red[lane] : 0u;
     uint32_t t = t0;
@@ -130,92 +151,162 @@ __device__ uint32_t block_exscan(uint32_t v, uint32_t* s_red, uint32_t* total) {
     if (lane < kSortWaves) s_red[lane] = t - t0;
     if (lane == kSortWaves - 1) s_red[kSortWaves] = t;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t r = s_red[w] + x - v;
   *total = s_red[kSortWaves];
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
-// Stable LSD radix sort of keys[0..n) (with 16-bit payloads) in LDS, 8 bits
-// per pass.  Wave w owns the contiguous range [w*L, (w+1)*L) and walks it in
-// rounds of 64; lanes holding equal digits in one round are found with one
-// ballot per digit bit, so each element's rank among equal digits of its
-// wave is exact and in position order.  Counts are kept per (digit, wave),
-// digit-major, so one exclusive scan over them gives every element's
-// destination: the sort is stable.
+// LDS layout of the sort arrays: one pad word after every 16 keys and two
+// pad halves after every 16 payloads, so that a thread reading its 16
+// consecutive elements and 64 lanes reading 64 consecutive ones both hit
+// distinct banks.
+__device__ __forceinline__ int KI(int i) { return i + (i >> 4); }
+__device__ __forceinline__ int VI(int i) { return i + 2 * (i >> 4); }
+constexpr int kKeyWords = kTtmMaxT + kTtmMaxT / 16;
+constexpr int kValHalves = kTtmMaxT + kTtmMaxT / 8;
+
+// Stable LSD radix sort of keys[0..n) (with 16-bit payloads) in LDS, 4 bits
+// per pass.  Thread t owns the contiguous elements [16 t, 16 t + 16) and
+// counts their digits in two packed 64-bit
+// registers (8 bits per digit), which also gives each element its rank among
+// the thread's equal digits.  The (digit, thread) counts go to LDS
+// digit-major; one exclusive scan over them gives every element's
+// destination, so the sort is stable.
+constexpr int kRadixE = kTtmMaxT / kSortThreads;
+
 __device__ void block_radix_sort(uint32_t* keys, uint16_t* vals, uint16_t* cnt, uint32_t* s_red, int n,
                                  int kbits) {
+  const int tid = threadIdx.x;
+  const int i0 = tid * kRadixE;
+  // padded addresses of the thread's elements and of its counters (linear in
+  // the unrolled index, so they become instruction offsets)
+  const int kt = KI(i0), vt = VI(i0), ct = VI(tid), cs = VI(tid * 16);
+  for (int shift = 0; shift < kbits; shift += 4) {
+    // payloads two per register, ranks four per register
+    uint32_t k[kRadixE], vp[kRadixE / 2], rp[kRadixE / 4];
+    uint64_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < kRadixE / 2; ++e) vp[e] = 0;
+#pragma unroll
+    for (int e = 0; e < kRadixE / 4; ++e) rp[e] = 0;
+#pragma unroll
+    for (int e = 0; e < kRadixE; ++e) {
+      k[e] = 0;
+      if (i0 + e < n) {
+        k[e] = keys[kt + e];
+        vp[e >> 1] |= (uint32_t)vals[vt + e] << (16 * (e & 1));
+        const uint32_t dg = (k[e] >> shift) & 15u;
+        const int sh = (int)(dg & 7u) * 8;
+        rp[e >> 2] |= (uint32_t)(((dg < 8 ? lo : hi) >> sh) & 0xffu) << (8 * (e & 3));
+        if (dg < 8)
+          lo += 1ull << sh;
+        else
+          hi += 1ull << sh;
+      }
+    }
+#pragma unroll
+    for (int dg = 0; dg < 16; ++dg)
+      cnt[ct + dg * (kSortThreads + kSortThreads / 8)] = (uint16_t)(((dg < 8 ? lo : hi) >> ((dg & 7) * 8)) & 0xffu);
+    lds_barrier();
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sum += cnt[cs + q];
+    uint32_t total;
+    uint32_t run = block_exscan(sum, s_red, &total);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t c = cnt[cs + q];
+      cnt[cs + q] = (uint16_t)run;
+      run += c;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < kRadixE; ++e) {
+      if (i0 + e < n) {
+        const uint32_t dg = (k[e] >> shift) & 15u;
+        const int dest = (int)cnt[ct + dg * (kSortThreads + kSortThreads / 8)] + (int)((rp[e >> 2] >> (8 * (e & 3))) & 0xffu);
+        keys[KI(dest)] = k[e];
+        vals[VI(dest)] = (uint16_t)(vp[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// One stable counting-sort pass over keys < 2^nb, nb <= 8 (the last digits
+// of a level's nodes).  Wave w owns the contiguous range [w*L, (w+1)*L) and
+// walks it in rounds of 64 lanes; lanes holding equal keys in a round are
+// found with one ballot per key bit, which ranks each element among equal
+// keys of its wave in position order.  Counts per (key, wave), key-major,
+// are scanned once for the destinations.
+__device__ void block_multisplit(uint32_t* keys, uint16_t* vals, uint16_t* cnt, uint32_t* s_red, int n, int nb) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = ((n + kSortWaves - 1) / kSortWaves + 63) & ~63;
   const int rounds = L >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int shift = 0; shift < kbits; shift += 8) {
-    const int nb = kbits - shift < 8 ? kbits - shift : 8;
-    const int nbins = 1 << nb;
-    const uint32_t dmask = (uint32_t)nbins - 1u;
-    for (int i = tid; i < nbins * kSortWaves; i += kSortThreads) cnt[i] = 0;
-    __syncthreads();
-    uint32_t k[16];
-    uint16_t v[16];
-    uint16_t rk[16];
+  const int nbins = 1 << nb;
+  for (int i = tid; i < nbins * kSortWaves; i += kSortThreads) cnt[i] = 0;
+  lds_barrier();
+  const int kw = KI(w * L + lane), vw = VI(w * L + lane);
+  uint32_t k[16], vp[8], rp[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < rounds) {
-        const int i = w * L + r * 64 + lane;
-        const bool valid = i < n;
-        const uint32_t key = valid ? keys[i] : 0u;
-        const uint32_t dg = (key >> shift) & dmask;
-        uint64_t mask = __ballot(valid);
-        for (int b = 0; b < nb; ++b) {
-          const bool bit = (dg >> b) & 1u;
-          const uint64_t bb = __ballot(valid && bit);
-          mask &= bit ? bb : ~bb;
-        }
-        k[r] = key;
-        v[r] = valid ? vals[i] : (uint16_t)0;
-        if (valid) {
-          const uint32_t pre = cnt[dg * kSortWaves + w];
-          const uint32_t mine = (uint32_t)__popcll(mask & below);
-          rk[r] = (uint16_t)(pre + mine);
-          if (mine == 0) cnt[dg * kSortWaves + w] = (uint16_t)(pre + (uint32_t)__popcll(mask));
-        }
-      }
-    }
-    __syncthreads();
-    // exclusive scan of the nbins * waves counters, 4 per thread
-    const int tot = nbins * kSortWaves;
-    uint32_t c4[4];
-    uint32_t s = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = tid * 4 + e;
-      c4[e] = i < tot ? cnt[i] : 0u;
-      s += c4[e];
-    }
-    uint32_t total;
-    uint32_t run = block_exscan(s, s_red, &total);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = tid * 4 + e;
-      if (i < tot) cnt[i] = (uint16_t)run;
-      run += c4[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < rounds) {
-        const int i = w * L + r * 64 + lane;
-        if (i < n) {
-          const uint32_t dg = (k[r] >> shift) & dmask;
-          const int dest = (int)cnt[dg * kSortWaves + w] + (int)rk[r];
-          keys[dest] = k[r];
-          vals[dest] = v[r];
-        }
-      }
-    }
-    __syncthreads();
+  for (int r = 0; r < 8; ++r) {
+    vp[r] = 0;
+    rp[r] = 0;
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    k[r] = 0;
+    if (r < rounds) {
+      const int i = w * L + r * 64 + lane;
+      const bool valid = i < n;
+      const uint32_t key = valid ? keys[kw + 68 * r] : 0u;
+      uint64_t mask = __ballot(valid);
+      for (int b = 0; b < nb; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t bb = __ballot(valid && bit);
+        mask &= bit ? bb : ~bb;
+      }
+      k[r] = key;
+      if (valid) {
+        vp[r >> 1] |= (uint32_t)vals[vw + 72 * r] << (16 * (r & 1));
+        const uint32_t pre = cnt[key * kSortWaves + w];
+        const uint32_t mine = (uint32_t)__popcll(mask & below);
+        rp[r >> 1] |= (pre + mine) << (16 * (r & 1));
+        if (mine == 0) cnt[key * kSortWaves + w] = (uint16_t)(pre + (uint32_t)__popcll(mask));
+      }
+    }
+  }
+  lds_barrier();
+  const int tot = nbins * kSortWaves;
+  uint32_t c4[4];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = tid * 4 + e;
+    c4[e] = i < tot ? cnt[i] : 0u;
+    sum += c4[e];
+  }
+  uint32_t total;
+  uint32_t run = block_exscan(sum, s_red, &total);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = tid * 4 + e;
+    if (i < tot) cnt[i] = (uint16_t)run;
+    run += c4[e];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < rounds && w * L + r * 64 + lane < n) {
+      const int dest = (int)cnt[k[r] * kSortWaves + w] + (int)((rp[r >> 1] >> (16 * (r & 1))) & 0xffffu);
+      keys[KI(dest)] = k[r];
+      vals[VI(dest)] = (uint16_t)(vp[r >> 1] >> (16 * (r & 1)));
+    }
+  }
+  lds_barrier();
 }
 
 // first index i in [0, n) with keys[i] >= x (keys ascending), n if none
@@ -223,7 +314,7 @@ __device__ int lower_bound_lds(const uint32_t* keys, int n, uint32_t x) {
   int lo = 0, hi = n;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (keys[mid] < x)
+    if (keys[KI(mid)] < x)
       lo = mid + 1;
     else
       hi = mid;
@@ -231,78 +322,126 @@ __device__ int lower_bound_lds(const uint32_t* keys, int n, uint32_t x) {
   return lo;
 }
 
-constexpr int kPer = kTtmMaxT / kSortThreads;  // positions owned per thread in the scans
+// Wave w owns positions [w * kPer * 64, (w + 1) * kPer * 64), visited in
+// rows of 64 consecutive positions; a position's rank among the flagged ones
+// is the popcount of the flag ballot below its lane plus the counts of the
+// rows and waves before it.
+constexpr int kPer = kTtmMaxT / kSortThreads;
 
 __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
-  __shared__ uint32_t s_key[kTtmMaxT];
-  __shared__ uint16_t s_val[kTtmMaxT];
-  __shared__ uint16_t s_cnt[256 * kSortWaves];
+  __shared__ uint32_t s_key[kKeyWords];
+  __shared__ uint16_t s_val[kValHalves];
+  __shared__ uint16_t s_cnt[16 * kSortThreads + 16 * kSortThreads / 8];
   __shared__ uint32_t s_red[kSortWaves + 1];
-  const int tid = threadIdx.x;
+  __shared__ uint32_t s_w[2 * kSortWaves];
+  __shared__ int32_t s_ul[TTC_TTM_MAX_MODES];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t upto = below | (1ull << lane);
   const int n = a.n;
+  const int base = w * kPer * 64;
+  // padded addresses of row 0 of this lane and of the element before it;
+  // row e adds 68 (keys) or 72 (payloads)
+  const int kb = KI(base + lane), kbm = kb - 1 - ((lane & 15) == 0 ? 1 : 0);
+  const int vb = VI(base + lane), vbm = vb - 1 - ((lane & 15) == 0 ? 2 : 0);
 
   // e0: keys; an id outside [0, V) becomes V and sorts after every valid id
-  uint32_t bad = 0;
-  for (int i = tid; i < n; i += kSortThreads) {
-    const int64_t id = a.ids[i];
-    const bool ok = id >= 0 && id < (int64_t)a.V;
-    s_key[i] = ok ? (uint32_t)id : a.V;
-    s_val[i] = (uint16_t)i;
-    bad += ok ? 0u : 1u;
+  {
+    int64_t idv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = base + e * 64 + lane;
+      idv[e] = i < n ? a.ids[i] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = base + e * 64 + lane;
+      if (i < n) {
+        const bool ok = idv[e] >= 0 && idv[e] < (int64_t)a.V;
+        s_key[kb + 68 * e] = ok ? (uint32_t)idv[e] : a.V;
+        s_val[vb + 72 * e] = (uint16_t)i;
+      }
+    }
+    lds_barrier();
   }
-  uint32_t nbad;
-  (void)block_exscan(bad, s_red, &nbad);
-
   // e1: sort by (id, position)
   block_radix_sort(s_key, s_val, s_cnt, s_red, n, a.kbits);
-  const int Tv = n - (int)nbad;
+  // the valid ids are the keys below V
+  int Tv;
+  {
+    uint32_t ok = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = base + e * 64 + lane;
+      ok += (i < n && s_key[kb + 68 * e] < a.V) ? 1u : 0u;
+    }
+    uint32_t tot;
+    (void)block_exscan(ok, s_red, &tot);
+    Tv = (int)tot;
+  }
 
-  // segment starts and piece starts over the positions owned by this thread
-  const int i0 = tid * kPer;
-  uint32_t kk[kPer];
-  uint16_t vv[kPer];
-  uint32_t nseg = 0, npc = 0;
-  const uint32_t kprev0 = (i0 > 0 && i0 - 1 < n) ? s_key[i0 - 1] : 0xffffffffu;
+  // segment starts (fs) and piece starts (ps): counts per wave
+  uint32_t key[kPer];
+  uint16_t val[kPer];
+  uint32_t fsm = 0, psm = 0, cf = 0, cp = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int i = i0 + e;
-    kk[e] = i < n ? s_key[i] : 0u;
-    vv[e] = i < n ? s_val[i] : (uint16_t)0;
+    const int i = base + e * 64 + lane;
+    key[e] = i < n ? s_key[kb + 68 * e] : 0u;
+    val[e] = i < n ? s_val[vb + 72 * e] : (uint16_t)0;
+    const uint32_t kp = (i > 0 && i - 1 < n) ? s_key[kbm + 68 * e] : 0xffffffffu;
+    const bool fs = i < Tv && (i == 0 || key[e] != kp);
+    const bool ps = i < Tv && (fs || (i & (kChunk - 1)) == 0);
+    fsm |= (uint32_t)fs << e;
+    psm |= (uint32_t)ps << e;
+    cf += (uint32_t)__popcll(__ballot(fs));
+    cp += (uint32_t)__popcll(__ballot(ps));
   }
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int i = i0 + e;
-    const uint32_t kp = e == 0 ? kprev0 : kk[e - 1];
-    const bool fs = i < Tv && (i == 0 || kk[e] != kp);
-    const bool ps = i < Tv && (fs || (i % kChunk) == 0);
-    nseg += fs;
-    npc += ps;
+  if (lane == 0) {
+    s_w[w] = cf;
+    s_w[kSortWaves + w] = cp;
   }
-  uint32_t tot2;
-  const uint32_t ex2 = block_exscan(nseg | (npc << 16), s_red, &tot2);
-  const int U = (int)(tot2 & 0xffffu), P = (int)(tot2 >> 16);
-  int u = (int)(ex2 & 0xffffu) - 1, p = (int)(ex2 >> 16) - 1;
+  lds_barrier();
+  int U = 0, P = 0, uu = 0, pp = 0;
+  for (int w2 = 0; w2 < kSortWaves; ++w2) {
+    const int x = (int)s_w[w2], y = (int)s_w[kSortWaves + w2];
+    if (w2 < w) {
+      uu += x;
+      pp += y;
+    }
+    U += x;
+    P += y;
+  }
+  --uu;
+  --pp;
+  // indices, outputs, and the distinct ids compacted into s_key[0..U)
+  // (every read of s_key above happened before the barrier)
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int i = i0 + e;
-    if (i >= n) break;
-    const uint32_t kp = e == 0 ? kprev0 : kk[e - 1];
-    const bool fs = i < Tv && (i == 0 || kk[e] != kp);
-    const bool ps = i < Tv && (fs || (i % kChunk) == 0);
-    u += fs;
-    p += ps;
-    a.order[i] = vv[e];
-    if (vv[e] < n) a.inverse[vv[e]] = i < Tv ? u : -1;
+    const int i = base + e * 64 + lane;
+    const bool fs = (fsm >> e) & 1u;
+    const bool ps = (psm >> e) & 1u;
+    const uint64_t mf = __ballot(fs), mp = __ballot(ps);
+    const int ui = uu + __popcll(mf & upto);
+    const int pi = pp + __popcll(mp & upto);
+    uu += __popcll(mf);
+    pp += __popcll(mp);
+    if (i < n) {
+      a.order[i] = val[e];
+      if (val[e] < n) a.inverse[val[e]] = i < Tv ? ui : -1;
+    }
     if (fs) {
-      a.uids[u] = (int32_t)kk[e];
-      a.seg[u] = i;
-      a.u_piece[u] = p;
+      a.uids[ui] = (int32_t)key[e];
+      a.seg[ui] = i;
+      a.u_piece[ui] = pi;
+      s_key[KI(ui)] = key[e];
+      s_val[VI(ui)] = (uint16_t)ui;
     }
     if (ps) {
-      a.piece_u[p] = u;
-      a.piece_beg[p] = i;
+      a.piece_u[pi] = ui;
+      a.piece_beg[pi] = i;
     }
-    if (i < Tv && (i % kChunk) == 0) a.chunk_piece[i / kChunk] = p;
+    if (i < Tv && (i & (kChunk - 1)) == 0) a.chunk_piece[i / kChunk] = pi;
   }
   const int nchv = (Tv + kChunk - 1) / kChunk;
   for (int c = nchv + tid; c <= a.nch; c += kSortThreads) a.chunk_piece[c] = P;
@@ -310,190 +449,368 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
     a.seg[U] = Tv;
     a.u_piece[U] = P;
     a.piece_beg[P] = Tv;
-    a.hdr[kHdrU] = U;
-    a.hdr[kHdrErr] = nbad ? 1 : 0;
-    a.hdr[kHdrPieces] = P;
-    a.hdr[kHdrTv] = Tv;
-    a.hdr[kHdrUl + a.d - 1] = U;
+    s_ul[a.d - 1] = U;
   }
-  __syncthreads();
-  // distinct ids into s_key[0..U), level d-1 node index of each into s_val
-  {
-    int uu = (int)(ex2 & 0xffffu) - 1;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = i0 + e;
-      const uint32_t kp = e == 0 ? kprev0 : kk[e - 1];
-      const bool fs = i < Tv && (i == 0 || kk[e] != kp);
-      uu += fs;
-      if (fs) {
-        s_key[uu] = kk[e];
-        s_val[uu] = (uint16_t)uu;
-      }
-    }
-  }
-  __syncthreads();
+  lds_barrier();
 
-  // e1 (levels): distinct prefixes of every level, from level d-2 down to 0
+  // e1 (levels): distinct prefixes of every level, from level d-2 down to 0;
+  // s_val[u] holds the level-(l+1) node of distinct id u
   int Unext = U;
   for (int l = a.d - 2; l >= 0; --l) {
-    const uint32_t M = a.Mgt[l];
-    uint32_t cntl = 0;
+    const FastDiv M = a.div_pre[l];
     uint32_t pre[kPer];
-    uint16_t nxt[kPer];
-    const uint32_t pprev0 = (i0 > 0 && i0 - 1 < U) ? s_key[i0 - 1] / M : 0xffffffffu;
-    const uint16_t nprev0 = (i0 > 0 && i0 - 1 < U) ? s_val[i0 - 1] : (uint16_t)0xffff;
+    uint16_t nx[kPer];
+    uint32_t nsm = 0, csm = 0, cnt = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int uu = i0 + e;
-      pre[e] = uu < U ? s_key[uu] / M : 0u;
-      nxt[e] = uu < U ? s_val[uu] : (uint16_t)0;
+      const int u = base + e * 64 + lane;
+      const bool in = u < U;
+      pre[e] = in ? fdiv(s_key[kb + 68 * e], M) : 0u;
+      nx[e] = in ? s_val[vb + 72 * e] : (uint16_t)0;
+      const bool prev = u > 0 && u - 1 < U;
+      const uint32_t pp2 = prev ? fdiv(s_key[kbm + 68 * e], M) : 0xffffffffu;
+      const uint32_t nxp = prev ? (uint32_t)s_val[vbm + 72 * e] : 0xffffffffu;
+      const bool ns = in && (u == 0 || pre[e] != pp2);
+      const bool cs = in && (u == 0 || (uint32_t)nx[e] != nxp);
+      nsm |= (uint32_t)ns << e;
+      csm |= (uint32_t)cs << e;
+      cnt += (uint32_t)__popcll(__ballot(ns));
     }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int uu = i0 + e;
-      const uint32_t pp = e == 0 ? pprev0 : pre[e - 1];
-      cntl += (uu < U && (uu == 0 || pre[e] != pp)) ? 1u : 0u;
+    if (lane == 0) s_w[w] = cnt;
+    lds_barrier();
+    int Ul = 0, jj = 0;
+    for (int w2 = 0; w2 < kSortWaves; ++w2) {
+      const int x = (int)s_w[w2];
+      if (w2 < w) jj += x;
+      Ul += x;
     }
-    uint32_t Ul;
-    int j = (int)block_exscan(cntl, s_red, &Ul) - 1;
-    uint16_t mine[kPer];
+    --jj;
+    uint16_t jx[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int uu = i0 + e;
-      const uint32_t pp = e == 0 ? pprev0 : pre[e - 1];
-      const uint16_t np = e == 0 ? nprev0 : nxt[e - 1];
-      const bool ns = uu < U && (uu == 0 || pre[e] != pp);
-      const bool cs = uu < U && (uu == 0 || nxt[e] != np);  // a node of level l+1 starts here
-      j += ns;
-      mine[e] = (uint16_t)j;
+      const bool ns = (nsm >> e) & 1u;
+      const bool cs = (csm >> e) & 1u;
+      const uint64_t m1 = __ballot(ns);
+      const int j = jj + __popcll(m1 & upto);
+      jj += __popcll(m1);
+      jx[e] = (uint16_t)j;
       if (ns) {
         a.pref[l][j] = (int32_t)pre[e];
-        a.child[l][j] = nxt[e];
+        a.child[l][j] = nx[e];
       }
-      if (cs) a.parent[l + 1][nxt[e]] = j;
+      if (cs) a.parent[l + 1][nx[e]] = j;
     }
     if (tid == 0) {
       a.child[l][Ul] = Unext;
-      a.hdr[kHdrUl + l] = (int32_t)Ul;
+      s_ul[l] = Ul;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (i0 + e < U) s_val[i0 + e] = mine[e];
-    __syncthreads();
-    Unext = (int)Ul;
+    for (int e = 0; e < kPer; ++e) {
+      const int u = base + e * 64 + lane;
+      if (u < U) s_val[vb + 72 * e] = jx[e];
+    }
+    lds_barrier();
+    Unext = Ul;
   }
   // level 0 hangs off the single root
   for (int j = tid; j < Unext; j += kSortThreads) a.parent[0][j] = 0;
-  __syncthreads();
+  if (tid == 0) {
+    a.hdr[kHdrU] = U;
+    a.hdr[kHdrErr] = Tv < n ? 1 : 0;
+    a.hdr[kHdrPieces] = P;
+    a.hdr[kHdrTv] = Tv;
+    for (int l = 0; l < a.d; ++l) a.hdr[kHdrUl + l] = s_ul[l];
+  }
 
-  // lists: the nodes of each level sorted stably by their last digit
-  for (int l = 0; l < a.d; ++l) {
-    const int Ul = l == a.d - 1 ? U : a.hdr[kHdrUl + l];
-    const int32_t* pref = l == a.d - 1 ? a.uids : a.pref[l];
+  // lists: the nodes of each level sorted stably by their last digit.  The
+  // last level's digits come from the distinct ids still in s_key; the other
+  // levels read back the prefixes this work-group stored, so wait for them.
+  __syncthreads();
+  for (int l = a.d - 1; l >= 0; --l) {
+    const int Ul = s_ul[l];
     const uint32_t ml = (uint32_t)a.m[l];
-    __syncthreads();
-    for (int j = tid; j < Ul; j += kSortThreads) {
-      s_key[j] = (uint32_t)pref[j] % ml;
-      s_val[j] = (uint16_t)j;
+    const FastDiv dm = a.div_m[l];
+    if (l == a.d - 1) {
+      for (int j = tid; j < Ul; j += kSortThreads) {
+        const uint32_t x = s_key[KI(j)];
+        s_key[KI(j)] = x - fdiv(x, dm) * ml;
+        s_val[VI(j)] = (uint16_t)j;
+      }
+    } else {
+      uint32_t pv[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int j = base + e * 64 + lane;
+        pv[e] = j < Ul ? (uint32_t)a.pref[l][j] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int j = base + e * 64 + lane;
+        if (j < Ul) {
+          s_key[KI(j)] = pv[e] - fdiv(pv[e], dm) * ml;
+          s_val[VI(j)] = (uint16_t)j;
+        }
+      }
     }
-    __syncthreads();
-    block_radix_sort(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
-    for (int j = tid; j < Ul; j += kSortThreads) a.list[l][j] = s_val[j];
+    lds_barrier();
+    if (a.dbits[l] <= 8)
+      block_multisplit(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
+    else
+      block_radix_sort(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
+    for (int j = tid; j < Ul; j += kSortThreads) a.list[l][j] = s_val[VI(j)];
     for (int v = tid; v <= (int)ml; v += kSortThreads) a.list_off[l][v] = lower_bound_lds(s_key, Ul, (uint32_t)v);
-    __syncthreads();
+    lds_barrier();
   }
 }
 
 // ------------------------------------------------------------------------------
-// forward: prefix products per node, rows per distinct id, token gather
+// per-node products
 // ------------------------------------------------------------------------------
-struct LevelArgs {
-  int l;                 // level (>= 1)
-  int d;
-  int m, nk, ra, rb;     // m_{l+1}, n_{l+1}, r_l, r_{l+1} (1-based core l+1)
-  int64_t R;             // rows of the parent product
-  const int32_t* hdr;
-  const int32_t* pref;   // level l prefixes (digit = pref % m)
-  const int32_t* parent; // level l parents
-  const int32_t* ppref;  // level l-1 prefixes (for a parent that is a slice of F_1)
-  const float* Fpar;     // F_1 when l == 1
-  const float* Ppar;     // P_{l-1} when l >= 2
-  const float* Dpar;     // D on the link into this level, NULL = identity
-  const float* F;        // core F_{l+1}
-  float* out;            // P_l, or the distinct-id rows at the last level
-  int64_t osz;           // floats per node of `out`
-  // backward only
-  const float* src;      // gradient sources of a node: pieces or children's Q
-  const int32_t* src_off;
-  int64_t ssz;           // floats per source row (= osz)
-  float* Cout;           // ra * nk * rb per node
-  float* Qout;           // R * ra per node
+// Flat index e = q * div + r walked with a fixed stride, without divisions.
+struct Walk {
+  int q, r, dq, dr, div;
+  __device__ __forceinline__ Walk(int start, int step, int d) : div(d) {
+    q = start / d;
+    r = start - q * d;
+    dq = step / d;
+    dr = step - dq * d;
+  }
+  __device__ __forceinline__ void next() {
+    r += dr;
+    q += dq;
+    if (r >= div) {
+      r -= div;
+      ++q;
+    }
+  }
 };
 
-// Stage the parent's product with D applied (R x ra) and the core slice
-// F[:, v, :, :] (ra x nk*rb) into LDS.
-__device__ __forceinline__ void stage_parent(const LevelArgs& a, int j, float* sPd, float* sW) {
-  const int p = a.parent[j];
-  const int v = (int)((uint32_t)a.pref[j] % (uint32_t)a.m);
-  const float* Pp = a.l == 1 ? a.Fpar + (int64_t)((uint32_t)a.ppref[p]) * a.R * a.ra : a.Ppar + (int64_t)p * a.R * a.ra;
-  const int64_t np = a.R * a.ra;
-  for (int64_t e = threadIdx.x; e < np; e += blockDim.x) {
-    const int aa = (int)(e % a.ra);
-    sPd[e] = Pp[e] * (a.Dpar ? a.Dpar[aa] : 1.f);
-  }
-  const int64_t blk = (int64_t)a.nk * a.rb;
-  const int64_t nw = (int64_t)a.ra * blk;
-  for (int64_t e = threadIdx.x; e < nw; e += blockDim.x) {
-    const int64_t aa = e / blk, cb = e - aa * blk;
-    sW[e] = a.F[(aa * a.m + v) * blk + cb];
+// A node's gradient is the sum of a range of source rows (off != NULL:
+// rows off[j] .. off[j+1]-1) or a single row j (off == NULL).
+struct Src {
+  const float* p;
+  const int32_t* off;
+  int64_t ld;
+};
+
+struct LevelArgs {
+  int l;                  // level (>= 1)
+  int m, nk, ra, rb, R;   // m_{l+1}, n_{l+1}, r_l, r_{l+1}; R = prod n_{<=l-1}
+  int blk;                // nk * rb
+  const int32_t* hdr;
+  const int32_t* pref;    // level l prefixes (digit = pref % m)
+  const int32_t* parent;  // level l parents
+  const int32_t* ppref;   // level l-1 prefixes (a level-0 product is the slice F_1[0, v])
+  const float* F0;        // F_1
+  const float* Ppar;      // products of level l-1 (l >= 2)
+  const float* Dpar;      // D on the link into level l, NULL = identity
+  const float* F;         // core l+1 (1-based)
+  float* out;             // forward: P_l (or the distinct-id rows at the last level)
+  Src src;                // backward: gradient sources of the level-l nodes
+  float* C;               // backward: ra * blk per level-l node
+  float* Q;               // backward: R * ra per level-l node
+};
+
+// the parent's product with D applied, R x ra
+__device__ __forceinline__ void stage_pd(const LevelArgs& a, int p, float* sPd) {
+  const int np = a.R * a.ra;
+  const float* Pp = a.l == 1 ? a.F0 + (int64_t)((uint32_t)a.ppref[p]) * np : a.Ppar + (int64_t)p * np;
+  Walk wk(threadIdx.x, blockDim.x, a.ra);
+#pragma unroll 4
+  for (int e = threadIdx.x; e < np; e += blockDim.x) {
+    sPd[e] = Pp[e] * (a.Dpar ? a.Dpar[wk.r] : 1.f);
+    wk.next();
   }
 }
 
-__global__ __launch_bounds__(kTtmThreads) void k_ttm_level_fwd(LevelArgs a) {
+// the core slice F[:, v, :, :] of node j, ra x blk, rows padded to blk + 1
+// floats so that lanes reading one column of different rows do not collide
+__device__ __forceinline__ void stage_w(const LevelArgs& a, int j, float* sW) {
+  const int v = (int)((uint32_t)a.pref[j] % (uint32_t)a.m);
+  const int nw = a.ra * a.blk;
+  Walk wk(threadIdx.x, blockDim.x, a.blk);
+#pragma unroll 4
+  for (int e = threadIdx.x; e < nw; e += blockDim.x) {
+    sW[wk.q * (a.blk + 1) + wk.r] = a.F[((int64_t)wk.q * a.m + v) * a.blk + wk.r];
+    wk.next();
+  }
+}
+
+// dot product of n terms x[i * sx] * y[i * sy] in order, loads issued 8 ahead
+__device__ __forceinline__ float dot_lds(const float* x, int sx, const float* y, int sy, int n) {
+  float acc = 0.f;
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    float xv[8], yv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      xv[k] = x[(i + k) * sx];
+      yv[k] = y[(i + k) * sy];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc = fmaf(xv[k], yv[k], acc);
+  }
+  for (; i < n; ++i) acc = fmaf(x[i * sx], y[i * sy], acc);
+  return acc;
+}
+
+// Sum of a node's source rows, element block [e0, e0 + 4) per call for
+// float4-aligned rows: 8 rows are loaded before they are added, in order.
+__device__ __forceinline__ float4 sum_rows4(const float* p, int64_t ld, int s0, int s1, int e) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  int q = s0;
+  for (; q + 8 <= s1; q += 8) {
+    float4 x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = *reinterpret_cast<const float4*>(p + (int64_t)(q + k) * ld + e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc.x += x[k].x;
+      acc.y += x[k].y;
+      acc.z += x[k].z;
+      acc.w += x[k].w;
+    }
+  }
+  for (; q < s1; ++q) {
+    const float4 x = *reinterpret_cast<const float4*>(p + (int64_t)q * ld + e);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float sum_rows1(const float* p, int64_t ld, int s0, int s1, int e) {
+  float acc = 0.f;
+  int q = s0;
+  for (; q + 8 <= s1; q += 8) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = p[(int64_t)(q + k) * ld + e];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += x[k];
+  }
+  for (; q < s1; ++q) acc += p[(int64_t)q * ld + e];
+  return acc;
+}
+
+// the node's gradient, R x blk (ng floats)
+__device__ __forceinline__ void stage_g(const Src& s, int j, int ng, float* sG) {
+  const int s0 = s.off ? s.off[j] : j, s1 = s.off ? s.off[j + 1] : j + 1;
+  if ((ng & 3) == 0 && (s.ld & 3) == 0) {
+    for (int e = 4 * threadIdx.x; e < ng; e += 4 * blockDim.x)
+      *reinterpret_cast<float4*>(sG + e) = sum_rows4(s.p, s.ld, s0, s1, e);
+  } else {
+    for (int e = threadIdx.x; e < ng; e += blockDim.x) sG[e] = sum_rows1(s.p, s.ld, s0, s1, e);
+  }
+}
+
+// forward, one work-group per level-l node:
+//   P_l[j][(c, c_k), b] = sum_a Pd[c, a] F[a, v, c_k, b]
+__global__ __launch_bounds__(kLevelThreads) void k_ttm_level_fwd(LevelArgs a) {
   extern __shared__ float lds[];
   const int Ul = a.hdr[kHdrUl + a.l];
-  const int64_t np = a.R * a.ra;
+  const int np = a.R * a.ra;
+  const int ldw = a.blk + 1;
   float* sPd = lds;
   float* sW = lds + np;
-  const int64_t blk = (int64_t)a.nk * a.rb;
-  const int64_t nout = a.R * blk;
+  const int nout = a.R * a.blk;
   for (int j = blockIdx.x; j < Ul; j += gridDim.x) {
+    stage_pd(a, a.parent[j], sPd);
+    stage_w(a, j, sW);
     __syncthreads();
-    stage_parent(a, j, sPd, sW);
-    __syncthreads();
-    float* o = a.out + (int64_t)j * a.osz;
-    for (int64_t e = threadIdx.x; e < nout; e += blockDim.x) {
-      const int64_t c = e / blk, cb = e - c * blk;
-      const float* pr = sPd + c * a.ra;
-      const float* wc = sW + cb;
-      float acc = 0.f;
-      for (int aa = 0; aa < a.ra; ++aa) acc = fmaf(pr[aa], wc[aa * blk], acc);
-      o[e] = acc;
+    float* o = a.out + (int64_t)j * nout;
+    Walk wk(threadIdx.x, blockDim.x, a.blk);
+    for (int e = threadIdx.x; e < nout; e += blockDim.x) {
+      o[e] = dot_lds(sPd + wk.q * a.ra, 1, sW + wk.r, ldw, a.ra);
+      wk.next();
     }
+    __syncthreads();
+  }
+}
+
+// backward, one work-group per level-l node j: its share of dF,
+//   C_j[a, c_k, b] = sum_c Pd[c, a] G_j[(c, c_k), b],
+// and its contribution to the parent's gradient,
+//   Q_j[c, a] = D[a] sum_{c_k, b} G_j[(c, c_k), b] F[a, v, c_k, b].
+__global__ __launch_bounds__(kLevelThreads) void k_ttm_level_bwd(LevelArgs a) {
+  extern __shared__ float lds[];
+  const int np = a.R * a.ra;
+  const int nw = a.ra * a.blk;
+  const int ng = a.R * a.blk;
+  const int ldw = a.blk + 1;
+  float* sPd = lds;
+  float* sW = sPd + np;
+  float* sG = sW + a.ra * ldw;
+  const int Ul = a.hdr[kHdrUl + a.l];
+  for (int j = blockIdx.x; j < Ul; j += gridDim.x) {
+    stage_pd(a, a.parent[j], sPd);
+    stage_w(a, j, sW);
+    stage_g(a.src, j, ng, sG);
+    __syncthreads();
+    float* C = a.C + (int64_t)j * nw;
+    {
+      Walk wk(threadIdx.x, blockDim.x, a.blk);
+      for (int e = threadIdx.x; e < nw; e += blockDim.x) {
+        C[e] = dot_lds(sPd + wk.q, a.ra, sG + wk.r, a.blk, a.R);
+        wk.next();
+      }
+    }
+    {
+      Walk wk(threadIdx.x, blockDim.x, a.ra);
+      float* Q = a.Q + (int64_t)j * np;
+      for (int e = threadIdx.x; e < np; e += blockDim.x) {
+        const float acc = dot_lds(sG + wk.q * a.blk, 1, sW + wk.r * ldw, 1, a.blk);
+        Q[e] = acc * (a.Dpar ? a.Dpar[wk.r] : 1.f);
+        wk.next();
+      }
+    }
+    __syncthreads();
   }
 }
 
 // out[t] = row of inverse[t] (through `map` when given: the row index of a
-// distinct id); zero for an id that was out of range
+// distinct id); zero for an id that was out of range.  Each wave copies
+// kRowsPerWave rows, loading all of them before storing.
+constexpr int kRowsPerWave = 4;
+
 template <bool VEC>
 __global__ __launch_bounds__(kTtmThreads) void k_ttm_gather(const int32_t* __restrict__ inverse,
                                                             const int32_t* __restrict__ map,
                                                             const float* __restrict__ rows, float* __restrict__ out,
                                                             int64_t T, int64_t N) {
-  const int64_t nv = VEC ? N / 4 : N;
-  const int64_t total = T * nv;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total; g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = g / nv, c = g - t * nv;
-    int u = inverse[t];
-    if (map && u >= 0) u = map[u];
-    if constexpr (VEC) {
-      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (u >= 0) val = reinterpret_cast<const float4*>(rows + (int64_t)u * N)[c];
-      reinterpret_cast<float4*>(out + t * N)[c] = val;
-    } else {
-      out[t * N + c] = u >= 0 ? rows[(int64_t)u * N + c] : 0.f;
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = ((int64_t)blockIdx.x * (kTtmThreads / 64) + (threadIdx.x >> 6)) * kRowsPerWave;
+  int u[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int64_t t = t0 + k;
+    int x = t < T ? inverse[t] : -1;
+    if (map && x >= 0) x = map[x];
+    u[k] = x;
+  }
+  if constexpr (VEC) {
+    const int64_t nv = N / 4;
+    for (int64_t c = lane; c < nv; c += 64) {
+      float4 v[kRowsPerWave];
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k)
+        v[k] = u[k] >= 0 ? reinterpret_cast<const float4*>(rows + (int64_t)u[k] * N)[c]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k)
+        if (t0 + k < T) reinterpret_cast<float4*>(out + (t0 + k) * N)[c] = v[k];
+    }
+  } else {
+    for (int64_t c = lane; c < N; c += 64) {
+      float v[kRowsPerWave];
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k) v[k] = u[k] >= 0 ? rows[(int64_t)u[k] * N + c] : 0.f;
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k)
+        if (t0 + k < T) out[(t0 + k) * N + c] = v[k];
     }
   }
 }
@@ -501,139 +818,152 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_gather(const int32_t* __res
 // ------------------------------------------------------------------------------
 // backward
 // ------------------------------------------------------------------------------
-// e5: per chunk of sorted positions, the sum of the output gradients of each
-// piece's tokens, in position order.
+// e5: per chunk of kChunk sorted positions, the sum of the output gradients
+// of each piece's tokens, in position order.  Rows are loaded 16 at a time
+// ahead of the (piece-ordered) accumulation.
 template <bool VEC>
-__global__ __launch_bounds__(kTtmThreads) void k_ttm_seg(const int32_t* __restrict__ order,
+__global__ __launch_bounds__(kTtmThreads) void k_ttm_seg(const int32_t* __restrict__ hdr,
+                                                         const int32_t* __restrict__ order,
                                                          const int32_t* __restrict__ piece_beg,
                                                          const int32_t* __restrict__ chunk_piece,
                                                          const float* __restrict__ dout, float* __restrict__ PS,
                                                          int64_t N) {
+  __shared__ int32_t s_ord[kChunk];
+  __shared__ int32_t s_pb[kChunk + 1];
   const int c = blockIdx.x;
   const int p0 = chunk_piece[c], p1 = chunk_piece[c + 1];
+  if (p0 == p1) return;
+  const int Tv = hdr[kHdrTv];
+  const int i0 = c * kChunk;
+  const int i1 = (i0 + kChunk < Tv) ? i0 + kChunk : Tv;
+  if (threadIdx.x < kChunk) s_ord[threadIdx.x] = i0 + (int)threadIdx.x < i1 ? order[i0 + threadIdx.x] : 0;
+  if ((int)threadIdx.x <= p1 - p0) s_pb[threadIdx.x] = piece_beg[p0 + threadIdx.x];
+  __syncthreads();
+  constexpr int B = 16;
   const int64_t nv = VEC ? N / 4 : N;
-  for (int p = p0; p < p1; ++p) {
-    const int b = piece_beg[p], e = piece_beg[p + 1];
-    for (int64_t col = threadIdx.x; col < nv; col += blockDim.x) {
-      if constexpr (VEC) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int i = b;
-        for (; i + 4 <= e; i += 4) {
-          float4 x[4];
+  for (int64_t col = threadIdx.x; col < nv; col += blockDim.x) {
+    int pi = 0;
+    int pend = s_pb[1];
+    if constexpr (VEC) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int ib = i0; ib < i1; ib += B) {
+        float4 x[B];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) x[q] = reinterpret_cast<const float4*>(dout + (int64_t)order[i + q] * N)[col];
+        for (int q = 0; q < B; ++q)
+          x[q] = ib + q < i1 ? reinterpret_cast<const float4*>(dout + (int64_t)s_ord[ib + q - i0] * N)[col]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < B; ++q) {
+          if (ib + q < i1) {
             acc.x += x[q].x;
             acc.y += x[q].y;
             acc.z += x[q].z;
             acc.w += x[q].w;
+            if (ib + q + 1 == pend) {
+              reinterpret_cast<float4*>(PS + (int64_t)(p0 + pi) * N)[col] = acc;
+              acc = make_float4(0.f, 0.f, 0.f, 0.f);
+              ++pi;
+              pend = pi < p1 - p0 ? s_pb[pi + 1] : 0x7fffffff;
+            }
           }
         }
-        for (; i < e; ++i) {
-          const float4 x = reinterpret_cast<const float4*>(dout + (int64_t)order[i] * N)[col];
-          acc.x += x.x;
-          acc.y += x.y;
-          acc.z += x.z;
-          acc.w += x.w;
+      }
+    } else {
+      float acc = 0.f;
+      for (int ib = i0; ib < i1; ib += B) {
+        float x[B];
+#pragma unroll
+        for (int q = 0; q < B; ++q) x[q] = ib + q < i1 ? dout[(int64_t)s_ord[ib + q - i0] * N + col] : 0.f;
+#pragma unroll
+        for (int q = 0; q < B; ++q) {
+          if (ib + q < i1) {
+            acc += x[q];
+            if (ib + q + 1 == pend) {
+              PS[(int64_t)(p0 + pi) * N + col] = acc;
+              acc = 0.f;
+              ++pi;
+              pend = pi < p1 - p0 ? s_pb[pi + 1] : 0x7fffffff;
+            }
+          }
         }
-        reinterpret_cast<float4*>(PS + (int64_t)p * N)[col] = acc;
-      } else {
-        float acc = 0.f;
-        for (int i = b; i < e; ++i) acc += dout[(int64_t)order[i] * N + col];
-        PS[(int64_t)p * N + col] = acc;
       }
     }
   }
 }
 
-// e6, one level: per node j, G_j = sum of its sources, then
-//   C_j[a, c_k, b] = sum_c Pd[c, a] G_j[(c, c_k), b]          (its share of dF)
-//   Q_j[c, a]      = D[a] sum_{c_k, b} G_j[(c, c_k), b] F[a, v, c_k, b]
-// (the gradient of the parent's product).
-__global__ __launch_bounds__(kTtmThreads) void k_ttm_level_bwd(LevelArgs a) {
-  extern __shared__ float lds[];
-  const int Ul = a.hdr[kHdrUl + a.l];
-  const int64_t np = a.R * a.ra;
-  const int64_t blk = (int64_t)a.nk * a.rb;
-  const int64_t nw = (int64_t)a.ra * blk;
-  const int64_t ng = a.R * blk;
-  float* sPd = lds;
-  float* sW = sPd + np;
-  float* sG = sW + nw;
-  for (int j = blockIdx.x; j < Ul; j += gridDim.x) {
-    __syncthreads();
-    stage_parent(a, j, sPd, sW);
-    const int s0 = a.src_off[j], s1 = a.src_off[j + 1];
-    for (int64_t e = threadIdx.x; e < ng; e += blockDim.x) {
-      float acc = 0.f;
-      for (int s = s0; s < s1; ++s) acc += a.src[(int64_t)s * a.ssz + e];
-      sG[e] = acc;
-    }
-    __syncthreads();
-    float* C = a.Cout + (int64_t)j * nw;
-    for (int64_t e = threadIdx.x; e < nw; e += blockDim.x) {
-      const int64_t aa = e / blk, cb = e - aa * blk;
-      float acc = 0.f;
-      for (int64_t c = 0; c < a.R; ++c) acc = fmaf(sPd[c * a.ra + aa], sG[c * blk + cb], acc);
-      C[e] = acc;
-    }
-    float* Q = a.Qout + (int64_t)j * np;
-    for (int64_t e = threadIdx.x; e < np; e += blockDim.x) {
-      const int64_t c = e / a.ra, aa = e - c * a.ra;
-      const float* g = sG + c * blk;
-      const float* wv = sW + aa * blk;
-      float acc = 0.f;
-      for (int64_t q = 0; q < blk; ++q) acc = fmaf(g[q], wv[q], acc);
-      Q[e] = acc * (a.Dpar ? a.Dpar[aa] : 1.f);
-    }
-  }
-}
-
-// Final step: every slice dF_{l+1}[a, v, :, :] is the sum, over the level-l
-// nodes whose last digit is v (in node order), of their C; at level 0 a
-// node's C is its gradient G itself, the sum of its sources.
+// Final step: dF_{l+1}[a, v, :, :] is the sum, over the level-l nodes whose
+// last digit is v (in node order), of their C[a, :, :]; at level 0 a node's C
+// is its gradient itself (the sum of its sources).  One work-group per
+// (level, v, a); the list is split over QL lanes, each summing every QL-th
+// entry in order, and the QL partial sums are added by a fixed tree.
 struct ReduceArgs {
   int d;
-  int m[TTC_TTM_MAX_MODES], nk[TTC_TTM_MAX_MODES], ra[TTC_TTM_MAX_MODES], rb[TTC_TTM_MAX_MODES];
-  int item_off[TTC_TTM_MAX_MODES + 1];  // first work item (v) of each level
-  const int32_t* hdr;
+  int m[TTC_TTM_MAX_MODES], blk[TTC_TTM_MAX_MODES], ra[TTC_TTM_MAX_MODES];
+  int item_off[TTC_TTM_MAX_MODES + 1];
   const int32_t* list[TTC_TTM_MAX_MODES];
   const int32_t* list_off[TTC_TTM_MAX_MODES];
-  const float* C[TTC_TTM_MAX_MODES];    // levels >= 1
-  const float* src0;                    // level 0: sources (pieces or level-1 Q)
-  const int32_t* src0_off;
+  const float* C[TTC_TTM_MAX_MODES];
+  Src src0;
   float* dF[TTC_TTM_MAX_MODES];
   int accumulate;
 };
 
 __global__ __launch_bounds__(kTtmThreads) void k_ttm_reduce(ReduceArgs a) {
+  __shared__ float s_red[kTtmThreads];
   const int it = blockIdx.x;
   int l = 0;
   while (l + 1 < a.d && it >= a.item_off[l + 1]) ++l;
-  const int v = it - a.item_off[l];
-  const int m = a.m[l];
-  const int64_t blk = (int64_t)a.nk[l] * a.rb[l];
-  const int64_t nw = (int64_t)a.ra[l] * blk;
+  const int rem = it - a.item_off[l];
+  const int ra = a.ra[l], blk = a.blk[l], m = a.m[l];
+  const int v = rem / ra, aa = rem - v * ra;
   const int b0 = a.list_off[l][v], b1 = a.list_off[l][v + 1];
   const int32_t* lst = a.list[l];
+  int BW = 1;
+  while (BW < blk && BW < kTtmThreads) BW <<= 1;
+  const int QL = kTtmThreads / BW;
+  const int ql = threadIdx.x / BW, cb0 = threadIdx.x - ql * BW;
+  const int nw = ra * blk;
   float* dF = a.dF[l];
-  for (int64_t e = threadIdx.x; e < nw; e += blockDim.x) {
-    const int64_t aa = e / blk, cb = e - aa * blk;
+  for (int cbase = 0; cbase < blk; cbase += BW) {
+    const int cb = cbase + cb0;
     float acc = 0.f;
-    if (l == 0) {
-      // ra == 1: e indexes the node's gradient directly
-      for (int q = b0; q < b1; ++q) {
-        const int j = lst[q];
-        const int s0 = a.src0_off[j], s1 = a.src0_off[j + 1];
-        for (int s = s0; s < s1; ++s) acc += a.src0[(int64_t)s * nw + e];
+    if (cb < blk) {
+      const int e = aa * blk + cb;
+      if (l == 0) {
+        for (int q = b0 + ql; q < b1; q += QL) {
+          const int j = lst[q];
+          acc += sum_rows1(a.src0.p, a.src0.ld, a.src0.off[j], a.src0.off[j + 1], e);
+        }
+      } else {
+        const float* C = a.C[l];
+        int q = b0 + ql;
+        for (; q + 3 * QL < b1; q += 4 * QL) {
+          const float x0 = C[(int64_t)lst[q] * nw + e];
+          const float x1 = C[(int64_t)lst[q + QL] * nw + e];
+          const float x2 = C[(int64_t)lst[q + 2 * QL] * nw + e];
+          const float x3 = C[(int64_t)lst[q + 3 * QL] * nw + e];
+          acc += x0;
+          acc += x1;
+          acc += x2;
+          acc += x3;
+        }
+        for (; q < b1; q += QL) acc += C[(int64_t)lst[q] * nw + e];
       }
-    } else {
-      const float* C = a.C[l];
-      for (int q = b0; q < b1; ++q) acc += C[(int64_t)lst[q] * nw + e];
     }
-    float* o = dF + (aa * m + v) * blk + cb;
-    *o = a.accumulate ? *o + acc : acc;
+    if (QL > 1) {
+      s_red[threadIdx.x] = acc;
+      __syncthreads();
+      for (int sft = QL / 2; sft >= 1; sft >>= 1) {
+        if (ql < sft) s_red[threadIdx.x] += s_red[threadIdx.x + sft * BW];
+        __syncthreads();
+      }
+      acc = s_red[threadIdx.x];
+    }
+    if (ql == 0 && cb < blk) {
+      float* o = dF + ((int64_t)aa * m + v) * blk + cb;
+      *o = a.accumulate ? *o + acc : acc;
+    }
+    __syncthreads();
   }
 }
 
@@ -654,6 +984,16 @@ static int bit_length(uint64_t x) {
     x >>= 1;
   }
   return b;
+}
+
+static FastDiv make_fastdiv(uint32_t M) {
+  int lg = 0;
+  while ((uint64_t(1) << lg) < M) ++lg;
+  FastDiv f;
+  f.shift = 32 + lg;
+  const unsigned __int128 num = (unsigned __int128)1 << f.shift;
+  f.magic = (uint64_t)((num + M - 1) / M);
+  return f;
 }
 
 static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* P) {
@@ -700,7 +1040,7 @@ static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* 
     P->cap[l] = mprod < T ? mprod : T;
     P->psz[l] = nprod * P->r[l + 1];
     const size_t blk = (size_t)P->n[l] * P->r[l + 1];
-    P->lds_fwd[l] = 4 * ((size_t)P->R[l] * P->r[l] + (size_t)P->r[l] * blk);
+    P->lds_fwd[l] = 4 * ((size_t)P->R[l] * P->r[l] + (size_t)P->r[l] * (blk + 1));
     P->lds_bwd[l] = P->lds_fwd[l] + 4 * ((size_t)P->R[l] * blk);
     if (l >= 1 && (P->lds_fwd[l] > kTtmMaxLds || P->lds_bwd[l] > kTtmMaxLds)) return TTC_ERR_UNSUPPORTED;
   }
@@ -750,7 +1090,7 @@ static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* 
 
 static ttc_status hip_ok() { return hipGetLastError() == hipSuccess ? TTC_OK : TTC_ERR_HIP; }
 
-static unsigned grid_nodes(int64_t cap) { return (unsigned)(cap < 1 ? 1 : (cap > 4096 ? 4096 : cap)); }
+static unsigned grid_nodes(int64_t cap) { return (unsigned)(cap < 1 ? 1 : (cap > 16384 ? 16384 : cap)); }
 
 template <typename Ptr>
 static Ptr at(void* base, size_t off) {
@@ -765,20 +1105,35 @@ static void fill_level(const TtmPlan& P, int l, const void* saved, const float* 
                        LevelArgs* a) {
   memset(a, 0, sizeof(*a));
   a->l = l;
-  a->d = P.d;
   a->m = P.m[l];
   a->nk = P.n[l];
   a->ra = P.r[l];
   a->rb = P.r[l + 1];
-  a->R = P.R[l];
+  a->R = (int)P.R[l];
+  a->blk = P.n[l] * P.r[l + 1];
   a->hdr = atc<const int32_t*>(saved, 0);
   a->pref = atc<const int32_t*>(saved, P.sv_pref[l]);
   a->parent = atc<const int32_t*>(saved, P.sv_parent[l]);
   a->ppref = atc<const int32_t*>(saved, P.sv_pref[l - 1]);
-  a->Fpar = F[0];
+  a->F0 = F[0];
   a->Ppar = l >= 2 ? atc<const float*>(saved, P.sv_P[l - 1]) : nullptr;
   a->Dpar = D ? D[l - 1] : nullptr;
   a->F = F[l];
+}
+
+// where the gradient of each level-l node comes from
+static Src level_src(const TtmPlan& P, int l, const void* saved, void* scratch) {
+  Src s;
+  if (l == P.d - 1) {
+    s.p = at<const float*>(scratch, P.sc_PS);
+    s.off = atc<const int32_t*>(saved, P.sv_u_piece);
+    s.ld = P.N;
+  } else {
+    s.p = at<const float*>(scratch, P.sc_Q[l + 1]);
+    s.off = atc<const int32_t*>(saved, P.sv_child[l]);
+    s.ld = P.psz[l];
+  }
+  return s;
 }
 
 static ttc_status check_cores(const TtmPlan& P, const float* const* F, const float* const* D) {
@@ -830,7 +1185,8 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
   sa.nch = (int)P.nch;
   for (int l = 0; l < P.d; ++l) {
     sa.m[l] = P.m[l];
-    sa.Mgt[l] = P.Mgt[l];
+    sa.div_pre[l] = make_fastdiv(P.Mgt[l]);
+    sa.div_m[l] = make_fastdiv((uint32_t)P.m[l]);
     sa.dbits[l] = P.dbits[l];
     sa.pref[l] = at<int32_t*>(saved, P.sv_pref[l]);
     sa.parent[l] = at<int32_t*>(saved, P.sv_parent[l]);
@@ -856,9 +1212,8 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
     LevelArgs a;
     fill_level(P, l, saved, F, D, &a);
     a.out = l == P.d - 1 ? at<float*>(scratch, P.sc_urow) : at<float*>(saved, P.sv_P[l]);
-    a.osz = P.psz[l];
     TraceScope ts("ttm_level", s);
-    hipLaunchKernelGGL(k_ttm_level_fwd, dim3(grid_nodes(P.cap[l])), dim3(kTtmThreads), P.lds_fwd[l], s, a);
+    hipLaunchKernelGGL(k_ttm_level_fwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_fwd[l], s, a);
   }
   // with one core the rows are those of F_1 itself, indexed by the id
   const float* rows = P.d >= 2 ? at<const float*>(scratch, P.sc_urow) : F[0];
@@ -866,8 +1221,8 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
   const int32_t* inv = at<const int32_t*>(saved, P.sv_inverse);
   {
     const bool vec = (P.N % 4) == 0 && al16(rows);
-    const int64_t blocks = (T * (vec ? P.N / 4 : P.N) + kTtmThreads - 1) / kTtmThreads;
-    const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+    const int64_t per_block = (kTtmThreads / 64) * kRowsPerWave;
+    const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
     TraceScope ts("ttm_gather", s);
     if (vec)
       hipLaunchKernelGGL(k_ttm_gather<true>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
@@ -910,25 +1265,24 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
   {
     const bool vec = (P.N % 4) == 0;
     TraceScope ts("ttm_seg", s);
+    const int32_t* hdr = atc<const int32_t*>(saved, 0);
     if (vec)
-      hipLaunchKernelGGL(k_ttm_seg<true>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s,
+      hipLaunchKernelGGL(k_ttm_seg<true>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s, hdr,
                          atc<const int32_t*>(saved, P.sv_order), atc<const int32_t*>(saved, P.sv_piece_beg),
                          atc<const int32_t*>(saved, P.sv_chunk_piece), dout, PS, P.N);
     else
-      hipLaunchKernelGGL(k_ttm_seg<false>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s,
+      hipLaunchKernelGGL(k_ttm_seg<false>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s, hdr,
                          atc<const int32_t*>(saved, P.sv_order), atc<const int32_t*>(saved, P.sv_piece_beg),
                          atc<const int32_t*>(saved, P.sv_chunk_piece), dout, PS, P.N);
   }
   for (int l = P.d - 1; l >= 1; --l) {
     LevelArgs a;
     fill_level(P, l, saved, F, D, &a);
-    a.src = l == P.d - 1 ? PS : at<const float*>(scratch, P.sc_Q[l + 1]);
-    a.src_off = atc<const int32_t*>(saved, P.sv_child[l]);
-    a.ssz = P.psz[l];
-    a.Cout = at<float*>(scratch, P.sc_C[l]);
-    a.Qout = at<float*>(scratch, P.sc_Q[l]);
+    a.src = level_src(P, l, saved, scratch);
+    a.C = at<float*>(scratch, P.sc_C[l]);
+    a.Q = at<float*>(scratch, P.sc_Q[l]);
     TraceScope ts("ttm_bwd_level", s);
-    hipLaunchKernelGGL(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kTtmThreads), P.lds_bwd[l], s, a);
+    hipLaunchKernelGGL(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_bwd[l], s, a);
   }
   ReduceArgs ra;
   memset(&ra, 0, sizeof(ra));
@@ -936,20 +1290,17 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
   int items = 0;
   for (int l = 0; l < P.d; ++l) {
     ra.m[l] = P.m[l];
-    ra.nk[l] = P.n[l];
+    ra.blk[l] = P.n[l] * P.r[l + 1];
     ra.ra[l] = P.r[l];
-    ra.rb[l] = P.r[l + 1];
     ra.item_off[l] = items;
-    items += P.m[l];
+    items += P.m[l] * P.r[l];
     ra.list[l] = atc<const int32_t*>(saved, P.sv_list[l]);
     ra.list_off[l] = atc<const int32_t*>(saved, P.sv_list_off[l]);
     ra.C[l] = l >= 1 ? at<const float*>(scratch, P.sc_C[l]) : nullptr;
     ra.dF[l] = dF[l];
   }
   ra.item_off[P.d] = items;
-  ra.hdr = atc<const int32_t*>(saved, 0);
-  ra.src0 = P.d == 1 ? PS : at<const float*>(scratch, P.sc_Q[1]);
-  ra.src0_off = atc<const int32_t*>(saved, P.sv_child[0]);
+  ra.src0 = level_src(P, 0, saved, scratch);
   ra.accumulate = desc->accumulate ? 1 : 0;
   {
     TraceScope ts("ttm_reduce", s);
