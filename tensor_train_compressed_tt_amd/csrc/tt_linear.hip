@@ -258,11 +258,19 @@ __global__ __launch_bounds__(64) void k_merge(MergeArgs a) {
 template <typename T>
 __device__ __forceinline__ void store4(typename Elem<T>::type* p, f32x4 v, int valid, bool vec);
 
+#ifndef TTC_NT_STORE
+#define TTC_NT_STORE 0
+#endif
 template <>
 __device__ __forceinline__ void store4<bf16_t>(unsigned short* p, f32x4 v, int valid, bool vec) {
   if (vec && valid >= 4) {
-    u16x4 o = {f32_to_bf16(v[0]), f32_to_bf16(v[1]), f32_to_bf16(v[2]), f32_to_bf16(v[3])};
+    const unsigned int lo = f32x2_to_bf16x2(v[0], v[1]), hi = f32x2_to_bf16x2(v[2], v[3]);
+    const u16x4 o = __builtin_bit_cast(u16x4, (uint2){lo, hi});
+#if TTC_NT_STORE
+    __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, o), reinterpret_cast<unsigned long long*>(p));
+#else
     *reinterpret_cast<u16x4*>(p) = o;
+#endif
   } else {
     for (int e = 0; e < 4 && e < valid; ++e) p[e] = f32_to_bf16(v[e]);
   }
@@ -353,6 +361,24 @@ __device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename 
 // ------------------------------------------------------------------------------
 // forward
 // ------------------------------------------------------------------------------
+// LDS of the forward: the Z reduction area (4 waves x 16*TT tokens x Rpad
+// fp32) is dead once Z is summed; the Z tile (16*TT tokens, act dtype) then
+// sits at offset 0 and two staged Y chunks of 16*TT rows x 256 columns
+// follow it, overlaying the rest of the reduction area.
+template <typename T, int NR, int TT>
+constexpr int kFwdStageOff() {
+  return ((16 * TT) * (16 * NR + 16 / (int)sizeof(typename Elem<T>::type)) * (int)sizeof(typename Elem<T>::type) +
+          255) / 256 * 256;
+}
+template <typename T, int NR, int TT>
+constexpr size_t kFwdLdsBytes() {
+  constexpr size_t red = (size_t)4 * 16 * TT * 16 * NR * 4;
+  constexpr size_t stg = (size_t)kFwdStageOff<T, NR, TT>() + 2 * (size_t)(16 * TT) *
+                                                                (256 + 16 / sizeof(typename Elem<T>::type)) *
+                                                                sizeof(typename Elem<T>::type);
+  return red > stg ? red : stg;
+}
+
 template <typename T, int NR, bool VEC, int TT>
 __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __restrict__ x,
                                              const typename Elem<T>::type* __restrict__ Ac,
@@ -383,25 +409,65 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
 #pragma unroll
     for (int n = 0; n < NR; ++n) acc[u][n] = zero4();
 
+  // Loads and stores share one in-order completion counter, so a load issued
+  // after a store cannot be waited for before that store completes.  Every
+  // batch of operands is therefore requested one step ahead, before the
+  // stores of the current step: the first B fragments at the very start,
+  // the next x / A batch before the current batch's MFMAs.
+  const int not_ = (int)((N_out + 15) / 16);
+  frag fo0[UO][KS], fo1[UO][KS], fo2[UO][KS];
+  auto fetch_b = [&](frag (&f)[UO][KS], int ob) {
+#pragma unroll
+    for (int uo = 0; uo < UO; ++uo)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        f[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + 4 * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
+  };
+  // Likewise for B: work-group b visits the 256-column steps of the output
+  // starting at step b mod nsteps.
+  const int nsteps = (not_ + 15) / 16;
+  const int rot2 = (int)(blockIdx.x % (unsigned)nsteps);
+  auto ostep = [&](int sidx) { return ((sidx + rot2) % nsteps) * 16; };
+  fetch_b(fo0, ostep(0) + w);
+  if (nsteps > 1) fetch_b(fo1, ostep(1) + w);
+
   // Z = x A^T: M = token, N = rank, K = input column; wave w takes the
-  // k-steps w, w+4, ... so the four waves read adjacent 64-byte pieces
+  // k-steps w, w+4, ... so the four waves read adjacent 64-byte pieces.
+  // Two register buffers, unrolled by two so that both stay in registers.
   const int nks = (int)((N_in + KSTEP - 1) / KSTEP);
-  for (int kb = 0; kb < nks; kb += 4 * UNR) {
-    frag fa[UNR][TT], fb[UNR][NR];
+  constexpr int KB = 4 * UNR;
+  frag fa0[UNR][TT], fb0[UNR][NR], fa1[UNR][TT], fb1[UNR][NR];
+  auto fetch_x = [&](frag (&xa)[UNR][TT], frag (&xb)[UNR][NR], int kb) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t col = (int64_t)(kb + 4 * u + w) * KSTEP + g * EPV;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) fa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
+      for (int tt = 0; tt < TT; ++tt) xa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
 #pragma unroll
-      for (int n = 0; n < NR; ++n) fb[u][n] = ld_frag<T, VEC>(Ac, 16 * n + c, Rpad, col, N_in, N_in);
+      for (int n = 0; n < NR; ++n) xb[u][n] = ld_frag<T, VEC>(Ac, 16 * n + c, Rpad, col, N_in, N_in);
     }
+  };
+  auto mma_x = [&](const frag (&xa)[UNR][TT], const frag (&xb)[UNR][NR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int n = 0; n < NR; ++n) acc[tt][n] = Mma<T>::mma(fa[u][tt], fb[u][n], acc[tt][n]);
+        for (int n = 0; n < NR; ++n) acc[tt][n] = Mma<T>::mma(xa[u][tt], xb[u][n], acc[tt][n]);
+  };
+  // Every work-group reads the same A; each starts at a different batch so
+  // that concurrent requests for A spread over the L2 channels instead of
+  // queueing on the same lines.
+  const int nkb = (nks + KB - 1) / KB;
+  const int rot1 = (int)(blockIdx.x % (unsigned)nkb);
+  auto kbat = [&](int j) { return ((j + rot1) % nkb) * KB; };
+  fetch_x(fa0, fb0, kbat(0));
+  for (int j = 0; j < nkb; j += 2) {
+    if (j + 1 < nkb) fetch_x(fa1, fb1, kbat(j + 1));
+    mma_x(fa0, fb0);
+    if (j + 1 >= nkb) break;
+    if (j + 2 < nkb) fetch_x(fa0, fb0, kbat(j + 2));
+    mma_x(fa1, fb1);
   }
   // lane (g, c) holds Z rows 4g+v of token tile u, rank column 16n+c
 #pragma unroll
@@ -410,7 +476,7 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     for (int n = 0; n < NR; ++n)
 #pragma unroll
       for (int vv = 0; vv < 4; ++vv) zred[(w * TM + 16 * u + 4 * g + vv) * Rpad + 16 * n + c] = acc[u][n][vv];
-  __syncthreads();
+  lds_barrier();
   constexpr int PER = TM * Rpad / 256;
   float zs[PER];
 #pragma unroll
@@ -418,7 +484,7 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     const int idx = threadIdx.x + 256 * i;
     zs[i] = ((zred[idx] + zred[TM * Rpad + idx]) + zred[2 * TM * Rpad + idx]) + zred[3 * TM * Rpad + idx];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int idx = threadIdx.x + 256 * i;
@@ -427,38 +493,66 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     if (t0 + tt < T_) Z[(t0 + tt) * Rpad + j] = e;
     zl[tt * ZLD + j] = e;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // Y^T = B Z^T: M = output column, N = token, K = rank
-  const int not_ = (int)((N_out + 15) / 16);
-  for (int ob = w; ob < not_; ob += 4 * UO) {
-    frag fa[UO][KS];
-#pragma unroll
-    for (int uo = 0; uo < UO; ++uo)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        fa[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + 4 * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
+  // Y^T = B Z^T: M = output column, N = token, K = rank.  The four waves
+  // cover 16 output tiles (256 columns) per step; the step's Y tile goes
+  // through LDS so that it leaves as whole-row 16-byte stores.
+  constexpr int CW = 256;                       // columns per step
+  constexpr int YLD = CW + 16 / (int)sizeof(E);  // staged row stride
+  E* ys0 = reinterpret_cast<E*>(smem + kFwdStageOff<T, NR, TT>());
+  E* ys1 = ys0 + TM * YLD;
+  constexpr int GPR = CW * (int)sizeof(E) / 16;  // 16-byte groups per staged row
+  auto out_step = [&](const frag (&f)[UO][KS], frag (&fn)[UO][KS], int sidx, E* ys) {
+    const int ob0 = ostep(sidx);
 #pragma unroll
     for (int uo = 0; uo < UO; ++uo) {
-      const int ot = ob + 4 * uo;
-      if (ot < not_) {
-        f32x4 acc2[TT];
+      const int lt = w + 4 * uo;
 #pragma unroll
-        for (int u = 0; u < TT; ++u) acc2[u] = zero4();
+      for (int u = 0; u < TT; ++u) {
+        f32x4 a2 = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
+          a2 = Mma<T>::mma(f[uo][ks], lds_frag<T>(zl + (16 * u + c) * ZLD + ks * KSTEP + g * EPV), a2);
+        E* d = ys + (16 * u + c) * YLD + lt * 16 + 4 * g;
+        if constexpr (sizeof(E) == 2) {
+          const uint2 pk = {f32x2_to_bf16x2(a2[0], a2[1]), f32x2_to_bf16x2(a2[2], a2[3])};
+          *reinterpret_cast<uint2*>(d) = pk;
+        } else {
 #pragma unroll
-          for (int u = 0; u < TT; ++u)
-            acc2[u] = Mma<T>::mma(fa[uo][ks], lds_frag<T>(zl + (16 * u + c) * ZLD + ks * KSTEP + g * EPV), acc2[u]);
-        const int64_t o0 = (int64_t)ot * 16 + 4 * g;
-        const int valid = (int)std::min<int64_t>(4, N_out - o0);
-#pragma unroll
-        for (int u = 0; u < TT; ++u) {
-          const int64_t t = t0 + 16 * u + c;
-          if (t < T_ && valid > 0) store4<T>(y + t * N_out + o0, acc2[u], valid, vout);
+          for (int vv = 0; vv < 4; ++vv) d[vv] = (E)Mma<T>::from_f32(a2[vv]);
         }
       }
     }
+    if (sidx + 2 < nsteps) fetch_b(fn, ostep(sidx + 2) + w);
+    lds_barrier();
+    const int64_t c0 = (int64_t)ob0 * 16;
+    const int64_t ncol = std::min<int64_t>(CW, N_out - c0);
+    if (vout && (ncol % (16 / (int)sizeof(E))) == 0) {
+      const int ngr = (int)(ncol * (int64_t)sizeof(E) / 16);
+      for (int idx = threadIdx.x; idx < TM * GPR; idx += 256) {
+        const int row = idx / GPR, gr = idx - row * GPR;
+        if (gr < ngr && t0 + row < T_)
+          *reinterpret_cast<uint4*>(y + (t0 + row) * N_out + c0 + gr * (16 / (int)sizeof(E))) =
+              *reinterpret_cast<const uint4*>(ys + row * YLD + gr * (16 / (int)sizeof(E)));
+      }
+    } else {
+      for (int idx = threadIdx.x; idx < TM * CW; idx += 256) {
+        const int row = idx / CW, col = idx - row * CW;
+        if (col < ncol && t0 + row < T_) y[(t0 + row) * N_out + c0 + col] = ys[row * YLD + col];
+      }
+    }
+  };
+  // three fragment buffers: the fragments of step s + 2 are requested in
+  // step s, so waiting for them never waits for the stores of step s + 1
+  // staging buffers alternate by step parity: a buffer is rewritten two
+  // steps later, after the barrier of the step in between
+  for (int sidx = 0; sidx < nsteps; sidx += 3) {
+    out_step(fo0, fo2, sidx, (sidx & 1) ? ys1 : ys0);
+    if (sidx + 1 >= nsteps) break;
+    out_step(fo1, fo0, sidx + 1, (sidx & 1) ? ys0 : ys1);
+    if (sidx + 2 >= nsteps) break;
+    out_step(fo2, fo1, sidx + 2, (sidx & 1) ? ys1 : ys0);
   }
 }
 
@@ -534,7 +628,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
     const int tt = tt0 + it / nsl, sb = it % nsl;
     const int64_t t0 = (int64_t)tt * 64;
     if (sb == 0) {
-      __syncthreads();  // readers of the previous tile's Z^T are done
+      lds_barrier();  // readers of the previous tile's Z^T are done
       rank_store<T, NR>(ztl, nullptr, zr);
 #pragma unroll
       for (int n = 0; n < NR; ++n) accZ[n] = zero4();
@@ -542,7 +636,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
     fetch(it + 2, sr, zr);
-    __syncthreads();
+    lds_barrier();
     // dZ: M = token (16-row tile w), N = rank, K = column of the slab
 #pragma unroll
     for (int ks = 0; ks < B::SW / B::KSTEP; ++ks) {
@@ -701,13 +795,13 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
     const int tt = tt0 + it / nsl, sb = it % nsl;
     const int64_t t0 = (int64_t)tt * 64;
     if (sb == 0) {
-      __syncthreads();
+      lds_barrier();
       rank_store<T, NR>(dztl, dzl, zr);
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
     fetch(it + 2, sr, zr);
-    __syncthreads();
+    lds_barrier();
     if (a.dx) {
       // dX^T = A^T dZ^T: M = input column (tiles ct*4+w of the slab), N = token, K = rank
 #pragma unroll
@@ -893,7 +987,7 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[p][q] = zero4();
   for (int k0 = 0; k0 < g.K; k0 += kGKC) {
-    __syncthreads();
+    lds_barrier();
     float ra[16], rb[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -921,7 +1015,7 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
       else
         Bs[(le / kGKC) * kGLong + le % kGKC] = rb[e];
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int st = 0; st < kGKC / 16; ++st) {
       const int kk = (4 * st + w) * 4 + gq;  // k-step 4*st+w of this wave
@@ -938,7 +1032,7 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
         for (int q = 0; q < 2; ++q) acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[p], fb[q], acc[p][q], 0, 0, 0);
     }
   }
-  __syncthreads();
+  lds_barrier();
   // lane (gq, c) of sub-tile (p, q) holds rows 16p+4gq+v, column 16q+c
   float* red = lds;  // [4 waves][32][33]
 #pragma unroll
@@ -947,7 +1041,7 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[(w * 32 + 16 * p + 4 * gq + v) * 33 + 16 * q + c] = acc[p][q][v];
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int idx = tid + 256 * e;
@@ -1114,7 +1208,7 @@ static void allow_lds(const void* kern, size_t bytes) {
 template <typename T, int NR, bool VEC, int TT>
 static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
   typedef typename Elem<T>::type E;
-  const size_t lds = size_t(4) * 16 * TT * 16 * NR * sizeof(float);
+  const size_t lds = kFwdLdsBytes<T, NR, TT>();
   auto kern = k_fwd<T, NR, VEC, TT>;
   static bool lds_set = false;
   if (!lds_set) {
@@ -1132,7 +1226,10 @@ static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* 
 template <typename T, int NR>
 static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
   const bool vec = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x);
-  const bool big = P.ntiles >= 512;
+#ifndef TTC_FWD_BIG_TILES
+#define TTC_FWD_BIG_TILES 512
+#endif
+  const bool big = P.ntiles >= TTC_FWD_BIG_TILES && sizeof(typename Elem<T>::type) == 2;
   if (vec && big) launch_fwd_v<T, NR, true, 4>(P, x, saved, y, st);
   else if (vec) launch_fwd_v<T, NR, true, 2>(P, x, saved, y, st);
   else if (big) launch_fwd_v<T, NR, false, 4>(P, x, saved, y, st);

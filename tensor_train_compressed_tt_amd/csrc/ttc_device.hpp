@@ -21,12 +21,18 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
   return __uint_as_float(((unsigned int)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even (gfx950 converts in hardware:
+// one v_cvt_pk_bf16_f32 per pair of values).
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
-  unsigned int u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  return __builtin_bit_cast(unsigned short, (__bf16)f);
+}
+// two values packed low, high
+__device__ __forceinline__ unsigned int f32x2_to_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
 }
 
 // One MFMA "k-step": each lane supplies 16 bytes of one row of A and of one
@@ -139,5 +145,16 @@ __device__ __forceinline__ typename Mma<T>::frag lds_col_frag(const typename Ele
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Work-group barrier that orders LDS accesses only.  __syncthreads() is a
+// work-group release/acquire fence over all address spaces, which on gfx950
+// waits for every outstanding global load and store of the wave first; a
+// barrier that only hands LDS tiles between waves must not drain the
+// prefetched loads and the pending stores of a streaming kernel.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace ttc

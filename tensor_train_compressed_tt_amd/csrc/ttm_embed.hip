@@ -39,6 +39,7 @@
 #include <string.h>
 
 #include "../../include/ttc.h"
+#include "ttc_device.hpp"
 #include "ttc_trace.hpp"
 
 namespace ttc {
@@ -119,14 +120,6 @@ struct SortArgs {
   int32_t* list[TTC_TTM_MAX_MODES];
   int32_t* list_off[TTC_TTM_MAX_MODES];
 };
-
-// Work-group barrier that orders LDS accesses only: global stores issued
-// before it are not waited for (a full __syncthreads would drain them).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Exclusive prefix sum of one value per thread over the work-group; *total
 // receives the sum.  Contains barriers: every thread must call it.
@@ -720,14 +713,14 @@ __global__ __launch_bounds__(kLevelThreads) void k_ttm_level_fwd(LevelArgs a) {
   for (int j = blockIdx.x; j < Ul; j += gridDim.x) {
     stage_pd(a, a.parent[j], sPd);
     stage_w(a, j, sW);
-    __syncthreads();
+    lds_barrier();
     float* o = a.out + (int64_t)j * nout;
     Walk wk(threadIdx.x, blockDim.x, a.blk);
     for (int e = threadIdx.x; e < nout; e += blockDim.x) {
       o[e] = dot_lds(sPd + wk.q * a.ra, 1, sW + wk.r, ldw, a.ra);
       wk.next();
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -749,7 +742,7 @@ __global__ __launch_bounds__(kLevelThreads) void k_ttm_level_bwd(LevelArgs a) {
     stage_pd(a, a.parent[j], sPd);
     stage_w(a, j, sW);
     stage_g(a.src, j, ng, sG);
-    __syncthreads();
+    lds_barrier();
     float* C = a.C + (int64_t)j * nw;
     {
       Walk wk(threadIdx.x, blockDim.x, a.blk);
@@ -767,7 +760,7 @@ __global__ __launch_bounds__(kLevelThreads) void k_ttm_level_bwd(LevelArgs a) {
         wk.next();
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -838,7 +831,7 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_seg(const int32_t* __restri
   const int i1 = (i0 + kChunk < Tv) ? i0 + kChunk : Tv;
   if (threadIdx.x < kChunk) s_ord[threadIdx.x] = i0 + (int)threadIdx.x < i1 ? order[i0 + threadIdx.x] : 0;
   if ((int)threadIdx.x <= p1 - p0) s_pb[threadIdx.x] = piece_beg[p0 + threadIdx.x];
-  __syncthreads();
+  lds_barrier();
   constexpr int B = 16;
   const int64_t nv = VEC ? N / 4 : N;
   for (int64_t col = threadIdx.x; col < nv; col += blockDim.x) {
@@ -952,10 +945,10 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_reduce(ReduceArgs a) {
     }
     if (QL > 1) {
       s_red[threadIdx.x] = acc;
-      __syncthreads();
+      lds_barrier();
       for (int sft = QL / 2; sft >= 1; sft >>= 1) {
         if (ql < sft) s_red[threadIdx.x] += s_red[threadIdx.x + sft * BW];
-        __syncthreads();
+        lds_barrier();
       }
       acc = s_red[threadIdx.x];
     }
@@ -963,7 +956,7 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_reduce(ReduceArgs a) {
       float* o = dF + ((int64_t)aa * m + v) * blk + cb;
       *o = a.accumulate ? *o + acc : acc;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
