@@ -48,7 +48,43 @@ def parse():
     ap.add_argument("--no-ttm", action="store_true", help="time the TT-linear layers only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device three times (scale for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+
+    n = mib * 1024 * 1024 // 2
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 2, "copies": 3}), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from its committed counter summary
+    (profiles/<kernel>_hbm_traffic.md), or None when that summary was taken on
+    a different version of the kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_hbm_traffic.md")
+    src = os.path.join(ROOT, "tensor_train_compressed_tt_amd", "csrc", "tt_linear.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != digest or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def step_bytes(layers, T, es):
@@ -104,6 +140,9 @@ def cpu_baseline(layers_host, T_cpu, ttm_host=None):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -310,7 +349,7 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(per[dom]["gbps"] / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(dom),
         "avg_launch_us": round(per[dom]["avg_us"], 2),
         "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
     }

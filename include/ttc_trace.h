@@ -1,9 +1,10 @@
 /*
  * ttc_trace.h - optional kernel timing of libttc with HIP events.
  *
- * While tracing is on, every kernel the library enqueues is bracketed by two
- * hipEvents recorded on the same stream as the kernel, so the elapsed time of
- * each launch can be read back afterwards.  Tracing is off by default and
+ * While tracing is on, every kernel the library enqueues is launched with a
+ * start and a stop hipEvent that the runtime stamps when the kernel itself
+ * begins and ends on its stream (hipExtLaunchKernelGGL), so the elapsed time
+ * of each launch can be read back afterwards.  Tracing is off by default and
  * costs nothing then.  It is meant for benchmarks and tests: reading the
  * records synchronises on the recorded events.  Do not trace inside a HIP
  * graph capture.  Not thread-safe against concurrent library calls.

@@ -1218,7 +1218,7 @@ static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* 
   const int vout = (P.N_out % 4) == 0 && aligned16(y);
   const unsigned grid = (unsigned)((P.T + 16 * TT - 1) / (16 * TT));
   TraceScope ts("fwd", st);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
+  TTC_LAUNCH(kern, dim3(grid), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
                      (const E*)(saved + P.sv_Bc), (E*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, (int)VEC, vout);
 }
 
@@ -1266,12 +1266,12 @@ static void launch_bwd_v(const LinearPlan& P, const void* x, const void* dy, con
       lds_set = true;
     }
     TraceScope ts("bwd_dy", st);
-    hipLaunchKernelGGL((k_bwd_dy<T, NR, VY>), dim3(P.dy_gc, P.dy_gt), dim3(256), lds, st, a);
+    TTC_LAUNCH((k_bwd_dy<T, NR, VY>), dim3(P.dy_gc, P.dy_gt), dim3(256), lds, st, a);
   }
   if (P.dy_gc > 1) {
     const int64_t n4 = P.T * B::Rpad / 4;
     TraceScope ts("dz_sum", st);
-    hipLaunchKernelGGL(k_dz_sum<T>, dim3((unsigned)std::min<int64_t>(4096, (n4 + 255) / 256)), dim3(256), 0, st,
+    TTC_LAUNCH(k_dz_sum<T>, dim3((unsigned)std::min<int64_t>(4096, (n4 + 255) / 256)), dim3(256), 0, st,
                        (const float*)(scratch + P.sc_dZp), (E*)(scratch + P.sc_dZ), P.dy_gc, n4);
   }
   {
@@ -1297,7 +1297,7 @@ static void launch_bwd_v(const LinearPlan& P, const void* x, const void* dy, con
       lds_set = true;
     }
     TraceScope ts("bwd_dx", st);
-    hipLaunchKernelGGL((k_bwd_dx<T, NR, VX>), dim3(P.dx_gc, P.dx_gt), dim3(256), lds, st, a);
+    TTC_LAUNCH((k_bwd_dx<T, NR, VX>), dim3(P.dx_gc, P.dx_gt), dim3(256), lds, st, a);
   }
 }
 
@@ -1384,9 +1384,9 @@ static void launch_merge(const LinearPlan& P, const float* const* G, const float
   const size_t lds = size_t(P.max_rank) * P.max_rank * sizeof(float);
   TraceScope ts("merge", s);
   if (P.act == TTC_BF16)
-    hipLaunchKernelGGL(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
+    TTC_LAUNCH(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
   else
-    hipLaunchKernelGGL(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
+    TTC_LAUNCH(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
 }
 
 // one event orders the two streams of a split backward; a wait captures the
@@ -1465,7 +1465,7 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
     for (int k = 0; k < P.d; ++k) {
       const int64_t n = (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
       TraceScope ts("zero", s);
-      hipLaunchKernelGGL(k_zero, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, dG[k], n);
+      TTC_LAUNCH(k_zero, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, dG[k], n);
     }
     return hip_status();
   }
@@ -1505,7 +1505,7 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
     r.in_first = P.in_first;
     const int64_t n = (int64_t)P.rs * ((P.N_out + 3) / 4 + (P.N_in + 3) / 4);
     TraceScope ts("reduce", s);
-    hipLaunchKernelGGL(k_reduce, dim3(grid_for(n, 256, 4096)), dim3(256), 0, s, r);
+    TTC_LAUNCH(k_reduce, dim3(grid_for(n, 256, 4096)), dim3(256), 0, s, r);
   }
   // reverse sweep through both halves, one launch per level
   {
@@ -1537,7 +1537,7 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
       for (int q = 0; q < a.ng; ++q) total += (a.tiles[q] = gemm_tiles(a.g[q]));
       {
         TraceScope ts("core", s);
-        hipLaunchKernelGGL(k_sweep, dim3(total), dim3(256), 0, s, a);
+        TTC_LAUNCH(k_sweep, dim3(total), dim3(256), 0, s, a);
       }
       if (hasL) {
         curL = outL;

@@ -1,5 +1,7 @@
 // Kernel timing with HIP events: a growing pool of event pairs, reused across
-// trace sessions; records are (name, start, end) in launch order.
+// trace sessions; records are (name, start, end) in launch order.  The pair
+// is handed to hipExtLaunchKernelGGL, which stamps the kernel's own start and
+// end.
 #include "ttc_trace.hpp"
 
 #include <mutex>
@@ -23,26 +25,31 @@ size_t g_used = 0;        // records of the current session
 
 bool trace_on() { return g_on; }
 
-void trace_begin(const char* name, hipStream_t s) {
+namespace {
+thread_local const char* t_pending = nullptr;
+}
+
+void trace_set_pending(const char* name) { t_pending = name; }
+
+bool trace_take(hipEvent_t* start, hipEvent_t* stop) {
+  const char* name = t_pending;
+  if (!name) return false;
+  t_pending = nullptr;
   std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return false;
   if (g_used == g_pool.size()) {
     Rec r{name, nullptr, nullptr};
     if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.end) != hipSuccess) {
       g_error = true;
-      return;
+      return false;
     }
     g_pool.push_back(r);
   }
-  Rec& r = g_pool[g_used];
+  Rec& r = g_pool[g_used++];
   r.name = name;
-  if (hipEventRecord(r.start, s) != hipSuccess) g_error = true;
-}
-
-void trace_end(hipStream_t s) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (g_used >= g_pool.size()) return;
-  if (hipEventRecord(g_pool[g_used].end, s) != hipSuccess) g_error = true;
-  ++g_used;
+  *start = r.start;
+  *stop = r.end;
+  return true;
 }
 
 }  // namespace ttc

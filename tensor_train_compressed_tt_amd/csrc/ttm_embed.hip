@@ -1198,7 +1198,7 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
   sa.u_piece = at<int32_t*>(saved, P.sv_u_piece);
   {
     TraceScope ts("ttm_sort", s);
-    hipLaunchKernelGGL(k_ttm_sort, dim3(1), dim3(kSortThreads), 0, s, sa);
+    TTC_LAUNCH(k_ttm_sort, dim3(1), dim3(kSortThreads), 0, s, sa);
   }
   // prefix products, level 1 .. d-1 (level 0 is a slice of F_1)
   for (int l = 1; l < P.d; ++l) {
@@ -1206,7 +1206,7 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
     fill_level(P, l, saved, F, D, &a);
     a.out = l == P.d - 1 ? at<float*>(scratch, P.sc_urow) : at<float*>(saved, P.sv_P[l]);
     TraceScope ts("ttm_level", s);
-    hipLaunchKernelGGL(k_ttm_level_fwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_fwd[l], s, a);
+    TTC_LAUNCH(k_ttm_level_fwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_fwd[l], s, a);
   }
   // with one core the rows are those of F_1 itself, indexed by the id
   const float* rows = P.d >= 2 ? at<const float*>(scratch, P.sc_urow) : F[0];
@@ -1218,9 +1218,9 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
     const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
     TraceScope ts("ttm_gather", s);
     if (vec)
-      hipLaunchKernelGGL(k_ttm_gather<true>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
+      TTC_LAUNCH(k_ttm_gather<true>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
     else
-      hipLaunchKernelGGL(k_ttm_gather<false>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
+      TTC_LAUNCH(k_ttm_gather<false>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
   }
   return hip_ok();
 }
@@ -1243,7 +1243,7 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
       for (int k = 0; k < P.d; ++k) {
         const int64_t n = (int64_t)P.r[k] * P.m[k] * P.n[k] * P.r[k + 1];
         TraceScope ts("zero", s);
-        hipLaunchKernelGGL(k_ttm_zero, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256),
+        TTC_LAUNCH(k_ttm_zero, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)), dim3(256),
                            0, s, dF[k], n);
       }
     }
@@ -1260,11 +1260,11 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
     TraceScope ts("ttm_seg", s);
     const int32_t* hdr = atc<const int32_t*>(saved, 0);
     if (vec)
-      hipLaunchKernelGGL(k_ttm_seg<true>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s, hdr,
+      TTC_LAUNCH(k_ttm_seg<true>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s, hdr,
                          atc<const int32_t*>(saved, P.sv_order), atc<const int32_t*>(saved, P.sv_piece_beg),
                          atc<const int32_t*>(saved, P.sv_chunk_piece), dout, PS, P.N);
     else
-      hipLaunchKernelGGL(k_ttm_seg<false>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s, hdr,
+      TTC_LAUNCH(k_ttm_seg<false>, dim3((unsigned)P.nch), dim3(kTtmThreads), 0, s, hdr,
                          atc<const int32_t*>(saved, P.sv_order), atc<const int32_t*>(saved, P.sv_piece_beg),
                          atc<const int32_t*>(saved, P.sv_chunk_piece), dout, PS, P.N);
   }
@@ -1275,7 +1275,7 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
     a.C = at<float*>(scratch, P.sc_C[l]);
     a.Q = at<float*>(scratch, P.sc_Q[l]);
     TraceScope ts("ttm_bwd_level", s);
-    hipLaunchKernelGGL(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_bwd[l], s, a);
+    TTC_LAUNCH(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_bwd[l], s, a);
   }
   ReduceArgs ra;
   memset(&ra, 0, sizeof(ra));
@@ -1297,7 +1297,7 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
   ra.accumulate = desc->accumulate ? 1 : 0;
   {
     TraceScope ts("ttm_reduce", s);
-    hipLaunchKernelGGL(k_ttm_reduce, dim3((unsigned)items), dim3(kTtmThreads), 0, s, ra);
+    TTC_LAUNCH(k_ttm_reduce, dim3((unsigned)items), dim3(kTtmThreads), 0, s, ra);
   }
   return hip_ok();
 }
