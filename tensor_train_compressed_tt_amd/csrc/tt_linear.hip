@@ -802,31 +802,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
     slab_store<T, NR>(sl, sr);
     fetch(it + 2, sr, zr);
     lds_barrier();
-    if (a.dx) {
-      // dX^T = A^T dZ^T: M = input column (tiles ct*4+w of the slab), N = token, K = rank
-#pragma unroll
-      for (int ct = 0; ct < B::CTW; ++ct) {
-        const int colt = (ct * 4 + w) * 16;
-        f32x4 accX[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) accX[u] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < B::Rpad / B::KSTEP; ++ks) {
-          const int kc = ks * B::KSTEP + g * B::EPV;
-          const frag fa = lds_frag<T>(atl + (sb * B::SW + colt + c) * B::RLD + kc);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) accX[u] = Mma<T>::mma(fa, lds_frag<T>(dzl + (16 * u + c) * B::RLD + kc), accX[u]);
-        }
-        const int64_t i0 = c0 + (int64_t)sb * B::SW + colt + 4 * g;
-        const int valid = (int)std::min<int64_t>(4, a.N_in - i0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t t = t0 + 16 * u + c;
-          if (t < a.T_ && valid > 0) store4<T>(a.dx + t * a.N_in + i0, accX[u], valid, VEC);
-        }
-      }
-    }
-    // dA: M = rank, N = input column, K = token
+    // dA: M = rank, N = input column, K = token (reads the x slab first, so
+    // that the slab buffer can then stage this slab's dX)
 #pragma unroll
     for (int s = 0; s < NSM; ++s) {
       if (s == sb) {
@@ -842,6 +819,69 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
             const frag fa = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
             for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fa, fb[ct], accA[s][ct][n]);
+          }
+        }
+      }
+    }
+    if (a.dx) {
+      // dX^T = A^T dZ^T: M = input column (tiles ct*4+w of the slab), N = token, K = rank
+      f32x4 accX[B::CTW][4];
+#pragma unroll
+      for (int ct = 0; ct < B::CTW; ++ct) {
+        const int colt = (ct * 4 + w) * 16;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) accX[ct][u] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < B::Rpad / B::KSTEP; ++ks) {
+          const int kc = ks * B::KSTEP + g * B::EPV;
+          const frag fa = lds_frag<T>(atl + (sb * B::SW + colt + c) * B::RLD + kc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            accX[ct][u] = Mma<T>::mma(fa, lds_frag<T>(dzl + (16 * u + c) * B::RLD + kc), accX[ct][u]);
+        }
+      }
+      const int64_t cs0 = c0 + (int64_t)sb * B::SW;
+      if constexpr (VEC) {
+        // the slab's dX leaves through the slab buffer as whole 16-byte row
+        // pieces: every wave is done reading the x slab, the tile is staged,
+        // then stored row by row
+        lds_barrier();
+#pragma unroll
+        for (int ct = 0; ct < B::CTW; ++ct) {
+          const int colt = (ct * 4 + w) * 16;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            E* d = sl + (16 * u + c) * B::SLD + colt + 4 * g;
+            if constexpr (sizeof(E) == 2) {
+              const uint2 pk = {f32x2_to_bf16x2(accX[ct][u][0], accX[ct][u][1]),
+                                f32x2_to_bf16x2(accX[ct][u][2], accX[ct][u][3])};
+              *reinterpret_cast<uint2*>(d) = pk;
+            } else {
+              *reinterpret_cast<f32x4*>(d) = accX[ct][u];
+            }
+          }
+        }
+        lds_barrier();
+        constexpr int GPR = B::SW * B::ES / 16;  // 16-byte groups per staged row
+        constexpr int EPG = 16 / B::ES;
+#pragma unroll
+        for (int k = 0; k < 64 * GPR / 256; ++k) {
+          const int idx = tid + 256 * k;
+          const int row = idx / GPR, q = idx % GPR;
+          const int64_t col = cs0 + q * EPG;
+          if (t0 + row < a.T_ && col < a.N_in)
+            *reinterpret_cast<uint4*>(a.dx + (t0 + row) * a.N_in + col) =
+                *reinterpret_cast<const uint4*>(sl + row * B::SLD + q * EPG);
+        }
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < B::CTW; ++ct) {
+          const int64_t i0 = cs0 + (ct * 4 + w) * 16 + 4 * g;
+          const int valid = (int)std::min<int64_t>(4, a.N_in - i0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int64_t t = t0 + 16 * u + c;
+            if (t < a.T_ && valid > 0) store4<T>(a.dx + t * a.N_in + i0, accX[ct][u], valid, false);
           }
         }
       }
