@@ -312,7 +312,8 @@ def main():
     # bwd_dy, bwd_dx, reduce, core_step x n
     expect = []
     nlev = 0 if ttm is None else ttm["d"] - 1
-    ttm_f = [] if ttm is None else [("ttm_sort", "ttm")] + [("ttm_level", "ttm")] * nlev + [("ttm_gather", "ttm")]
+    ttm_f = [] if ttm is None else ([("ttm_sort", "ttm"), ("ttm_lists", "ttm")] + [("ttm_level", "ttm")] * nlev
+                                    + [("ttm_gather", "ttm")])
     ttm_b = [] if ttm is None else [("ttm_seg", "ttm")] + [("ttm_bwd_level", "ttm")] * nlev + [("ttm_reduce", "ttm")]
     expect += ttm_f
     if args.single_stream:

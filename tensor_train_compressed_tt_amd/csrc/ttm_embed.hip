@@ -71,7 +71,7 @@ struct TtmPlan {
   int64_t R[TTC_TTM_MAX_MODES];     // prod n_{<l}: rows of the parent product of level l
   int64_t psz[TTC_TTM_MAX_MODES];   // floats of P_l[j] = prod n_{<=l} * r_{l+1}
   // saved (bytes)
-  size_t sv_order, sv_inverse, sv_uids, sv_seg, sv_piece_u, sv_piece_beg, sv_chunk_piece, sv_u_piece;
+  size_t sv_order, sv_inverse, sv_uids, sv_seg, sv_piece_beg, sv_chunk_piece, sv_u_piece;
   size_t sv_pref[TTC_TTM_MAX_MODES], sv_parent[TTC_TTM_MAX_MODES], sv_child[TTC_TTM_MAX_MODES];
   size_t sv_list[TTC_TTM_MAX_MODES], sv_list_off[TTC_TTM_MAX_MODES], sv_P[TTC_TTM_MAX_MODES];
   size_t sv_total;
@@ -110,7 +110,6 @@ struct SortArgs {
   int32_t* inverse;
   int32_t* uids;
   int32_t* seg;
-  int32_t* piece_u;
   int32_t* piece_beg;
   int32_t* chunk_piece;
   int32_t* u_piece;
@@ -430,10 +429,7 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
       s_key[KI(ui)] = key[e];
       s_val[VI(ui)] = (uint16_t)ui;
     }
-    if (ps) {
-      a.piece_u[pi] = ui;
-      a.piece_beg[pi] = i;
-    }
+    if (ps) a.piece_beg[pi] = i;
     if (i < Tv && (i & (kChunk - 1)) == 0) a.chunk_piece[i / kChunk] = pi;
   }
   const int nchv = (Tv + kChunk - 1) / kChunk;
@@ -515,46 +511,45 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
     a.hdr[kHdrTv] = Tv;
     for (int l = 0; l < a.d; ++l) a.hdr[kHdrUl + l] = s_ul[l];
   }
+}
 
-  // lists: the nodes of each level sorted stably by their last digit.  The
-  // last level's digits come from the distinct ids still in s_key; the other
-  // levels read back the prefixes this work-group stored, so wait for them.
-  __syncthreads();
-  for (int l = a.d - 1; l >= 0; --l) {
-    const int Ul = s_ul[l];
-    const uint32_t ml = (uint32_t)a.m[l];
-    const FastDiv dm = a.div_m[l];
-    if (l == a.d - 1) {
-      for (int j = tid; j < Ul; j += kSortThreads) {
-        const uint32_t x = s_key[KI(j)];
-        s_key[KI(j)] = x - fdiv(x, dm) * ml;
-        s_val[VI(j)] = (uint16_t)j;
-      }
-    } else {
-      uint32_t pv[kPer];
+// Digit lists: the nodes of level l (blockIdx.x) sorted stably by their last
+// digit, so that every slice of a core gradient sums a fixed list in node
+// order.  One work-group per level, all levels at once.
+__global__ __launch_bounds__(kSortThreads) void k_ttm_lists(SortArgs a) {
+  __shared__ uint32_t s_key[kKeyWords];
+  __shared__ uint16_t s_val[kValHalves];
+  __shared__ uint16_t s_cnt[16 * kSortThreads + 16 * kSortThreads / 8];
+  __shared__ uint32_t s_red[kSortWaves + 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int base = w * kPer * 64;
+  const int kb = KI(base + lane), vb = VI(base + lane);
+  const int l = blockIdx.x;
+  const int Ul = a.hdr[kHdrUl + l];
+  const uint32_t ml = (uint32_t)a.m[l];
+  const FastDiv dm = a.div_m[l];
+  const int32_t* pref = l == a.d - 1 ? a.uids : a.pref[l];
+  uint32_t pv[kPer];
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const int j = base + e * 64 + lane;
-        pv[e] = j < Ul ? (uint32_t)a.pref[l][j] : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const int j = base + e * 64 + lane;
-        if (j < Ul) {
-          s_key[KI(j)] = pv[e] - fdiv(pv[e], dm) * ml;
-          s_val[VI(j)] = (uint16_t)j;
-        }
-      }
-    }
-    lds_barrier();
-    if (a.dbits[l] <= 8)
-      block_multisplit(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
-    else
-      block_radix_sort(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
-    for (int j = tid; j < Ul; j += kSortThreads) a.list[l][j] = s_val[VI(j)];
-    for (int v = tid; v <= (int)ml; v += kSortThreads) a.list_off[l][v] = lower_bound_lds(s_key, Ul, (uint32_t)v);
-    lds_barrier();
+  for (int e = 0; e < kPer; ++e) {
+    const int j = base + e * 64 + lane;
+    pv[e] = j < Ul ? (uint32_t)pref[j] : 0u;
   }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int j = base + e * 64 + lane;
+    if (j < Ul) {
+      s_key[kb + 68 * e] = pv[e] - fdiv(pv[e], dm) * ml;
+      s_val[vb + 72 * e] = (uint16_t)j;
+    }
+  }
+  lds_barrier();
+  if (a.dbits[l] <= 8)
+    block_multisplit(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
+  else
+    block_radix_sort(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
+  for (int j = tid; j < Ul; j += kSortThreads) a.list[l][j] = s_val[VI(j)];
+  for (int v = tid; v <= (int)ml; v += kSortThreads) a.list_off[l][v] = lower_bound_lds(s_key, Ul, (uint32_t)v);
 }
 
 // ------------------------------------------------------------------------------
@@ -648,30 +643,48 @@ __device__ __forceinline__ float dot_lds(const float* x, int sx, const float* y,
   return acc;
 }
 
-// Sum of a node's source rows, element block [e0, e0 + 4) per call for
-// float4-aligned rows: 8 rows are loaded before they are added, in order.
+// Sum of a node's source rows, elements [e, e + 4) of each row (float4-aligned
+// rows), in row order.  Rows are requested 8 at a time and the next 8 are in
+// flight while the current 8 are added, so a node with many rows costs about
+// one memory latency plus the issue time of its loads.
+__device__ __forceinline__ void add4(float4& acc, const float4& x) {
+  acc.x += x.x;
+  acc.y += x.y;
+  acc.z += x.z;
+  acc.w += x.w;
+}
+
 __device__ __forceinline__ float4 sum_rows4(const float* p, int64_t ld, int s0, int s1, int e) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto row = [&](int q) { return *reinterpret_cast<const float4*>(p + (int64_t)q * ld + e); };
   int q = s0;
-  for (; q + 8 <= s1; q += 8) {
-    float4 x[8];
+  if (q + 8 <= s1) {
+    float4 x0[8], x1[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = *reinterpret_cast<const float4*>(p + (int64_t)(q + k) * ld + e);
+    for (int k = 0; k < 8; ++k) x0[k] = row(q + k);
+    q += 8;
+    while (true) {
+      const bool more1 = q + 8 <= s1;
+      if (more1) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      acc.x += x[k].x;
-      acc.y += x[k].y;
-      acc.z += x[k].z;
-      acc.w += x[k].w;
+        for (int k = 0; k < 8; ++k) x1[k] = row(q + k);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) add4(acc, x0[k]);
+      if (!more1) break;
+      q += 8;
+      const bool more0 = q + 8 <= s1;
+      if (more0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x0[k] = row(q + k);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) add4(acc, x1[k]);
+      if (!more0) break;
+      q += 8;
     }
   }
-  for (; q < s1; ++q) {
-    const float4 x = *reinterpret_cast<const float4*>(p + (int64_t)q * ld + e);
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
-  }
+  for (; q < s1; ++q) add4(acc, row(q));
   return acc;
 }
 
@@ -812,7 +825,7 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_gather(const int32_t* __res
 // backward
 // ------------------------------------------------------------------------------
 // e5: per chunk of kChunk sorted positions, the sum of the output gradients
-// of each piece's tokens, in position order.  Rows are loaded 16 at a time
+// of each piece's tokens, in position order.  All rows of the chunk are loaded
 // ahead of the (piece-ordered) accumulation.
 template <bool VEC>
 __global__ __launch_bounds__(kTtmThreads) void k_ttm_seg(const int32_t* __restrict__ hdr,
@@ -832,7 +845,7 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_seg(const int32_t* __restri
   if (threadIdx.x < kChunk) s_ord[threadIdx.x] = i0 + (int)threadIdx.x < i1 ? order[i0 + threadIdx.x] : 0;
   if ((int)threadIdx.x <= p1 - p0) s_pb[threadIdx.x] = piece_beg[p0 + threadIdx.x];
   lds_barrier();
-  constexpr int B = 16;
+  constexpr int B = kChunk;  // the whole chunk's rows in flight at once
   const int64_t nv = VEC ? N / 4 : N;
   for (int64_t col = threadIdx.x; col < nv; col += blockDim.x) {
     int pi = 0;
@@ -1048,7 +1061,6 @@ static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* 
   P->sv_inverse = take(T);
   P->sv_uids = take(T);
   P->sv_seg = take(T + 1);
-  P->sv_piece_u = take(T);
   P->sv_piece_beg = take(T + 1);
   P->sv_chunk_piece = take(P->nch + 1);
   P->sv_u_piece = take(T + 1);
@@ -1192,13 +1204,16 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
   sa.inverse = at<int32_t*>(saved, P.sv_inverse);
   sa.uids = at<int32_t*>(saved, P.sv_uids);
   sa.seg = at<int32_t*>(saved, P.sv_seg);
-  sa.piece_u = at<int32_t*>(saved, P.sv_piece_u);
   sa.piece_beg = at<int32_t*>(saved, P.sv_piece_beg);
   sa.chunk_piece = at<int32_t*>(saved, P.sv_chunk_piece);
   sa.u_piece = at<int32_t*>(saved, P.sv_u_piece);
   {
     TraceScope ts("ttm_sort", s);
     TTC_LAUNCH(k_ttm_sort, dim3(1), dim3(kSortThreads), 0, s, sa);
+  }
+  {
+    TraceScope ts("ttm_lists", s);
+    TTC_LAUNCH(k_ttm_lists, dim3((unsigned)P.d), dim3(kSortThreads), 0, s, sa);
   }
   // prefix products, level 1 .. d-1 (level 0 is a slice of F_1)
   for (int l = 1; l < P.d; ++l) {

@@ -285,3 +285,36 @@ def test_graph_replay_two_streams_matches_eager():
         got = snapshot()
         for a, b2 in zip(got, want):
             assert torch.equal(a, b2), f"replay {rep} differs"
+
+
+# ---- config 4: CodeBERT-large-shaped layers (d = 1024, FFN 4096, rank 64, half of D zeroed)
+
+@pytest.mark.parametrize("li", [0, 4, 5])
+def test_config4_layer_shapes(li):
+    """Each of the three config-4 layer shapes, several token tiles and a ragged tail."""
+    spec = synth.config_layers(4)[li]
+    layer = synth.make_tt_layer(4, li, spec, 257, synth.CONFIG_ZERO_FRAC[4], "bf16")
+    print(_check(spec, layer, "bf16"))
+
+
+def test_config4_full_tokens_sampled_rows():
+    """Full config-4 size (T = 16384) for the 1024 -> 4096 layer: Y and dX on
+    seeded token samples (rows are independent, so this is exact), the core
+    gradients in full."""
+    spec = synth.config_layers(4)[4]
+    T = synth.CONFIG_TOKENS[4]
+    layer = synth.make_tt_layer(4, 4, spec, T, synth.CONFIG_ZERO_FRAC[4], "bf16")
+    y, dx, dG = _run(spec, layer, "bf16")
+    rows = np.sort(np.random.default_rng(4).choice(T, 512, replace=False))
+    x = layer["x"].astype(np.float64)
+    dy = layer["dy"].astype(np.float64)
+    W = oracle.dense_weight(spec.out_modes, spec.in_modes, layer["cores"], layer["D"], spec.in_first)
+    assert _rel(y[rows], x[rows] @ W.T) <= TOL["bf16"]
+    assert _rel(dx[rows], dy[rows] @ W) <= TOL["bf16"]
+    _, dGr = oracle.tt_linear_backward(x, dy, spec.out_modes, spec.in_modes, layer["cores"], layer["D"],
+                                       spec.in_first)
+    for k in range(len(dG)):
+        assert _rel(dG[k], dGr[k]) <= TOL["bf16"], k
+    for k, v in enumerate(layer["D"]):
+        dead = np.flatnonzero(v == 0)
+        assert np.all(dG[k][:, :, dead] == 0.0) and np.all(dG[k + 1][dead, :, :] == 0.0)
