@@ -140,9 +140,12 @@ def tt_linear_backward(x, dy, out_modes, in_modes, cores, D, in_first: bool = Fa
     <dY, x W^T> with respect to each core with D fixed.  Returns (dX, [dG_k]).
     """
     W = dense_weight(out_modes, in_modes, cores, D, in_first)
-    x = _f64(x)
-    dy = _f64(dy)
-    dX = dy @ W
-    dW = dy.T @ x
+    dX = _f64(dy) @ W
+    return dX, tt_linear_core_grads(x, dy, cores, D, in_first)
+
+
+def tt_linear_core_grads(x, dy, cores, D, in_first: bool = False) -> list:
+    """The core gradients alone: dW = dY^T x, then dG_k = d<dW, W>/dG_k."""
+    dW = _f64(dy).T @ _f64(x)
     dT = dW.T if in_first else dW           # back to the chain's own layout
-    return dX, chain_core_grads(dT.reshape(-1), cores, D)
+    return chain_core_grads(dT.reshape(-1), cores, D)
