@@ -316,11 +316,20 @@ def main():
                                     + [("ttm_gather", "ttm")])
     ttm_b = [] if ttm is None else [("ttm_seg", "ttm")] + [("ttm_bwd_level", "ttm")] * nlev + [("ttm_reduce", "ttm")]
     expect += ttm_f
+    def merge_launches(li):
+        # one GEMM launch per level of the longer half, then the packing launch
+        s = layers[li]["spec"]
+        split = len(s.in_modes) if s.in_first else len(s.out_modes)
+        d = len(s.in_modes) + len(s.out_modes)
+        return [("merge_level", li)] * max(split - 1, d - 1 - split) + [("merge", li)]
+
     if args.single_stream:
         for li in range(len(layers)):
-            expect += [("merge", li), ("fwd", li)]
+            expect += merge_launches(li) + [("fwd", li)]
     else:
-        expect += [("merge", li) for li in range(len(layers))] + [("fwd", li) for li in range(len(layers))]
+        for li in range(len(layers)):
+            expect += merge_launches(li)
+        expect += [("fwd", li) for li in range(len(layers))]
     for li in reversed(range(len(layers))):
         s = layers[li]["spec"]
         plan = dict(kv.split("=") for kv in ttc.tt_linear_explain(layers[li]["mod"].desc, T).split())

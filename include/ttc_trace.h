@@ -32,7 +32,7 @@ ttc_status ttc_trace_count(int32_t* n);
 
 /*
  * Record i (0-based, in launch order): the kernel's name (static storage, one
- * of "merge", "fwd", "bwd_dy", "dz_sum", "bwd_dx", "reduce", "core", "zero",
+ * of "merge_level", "merge", "fwd", "bwd_dy", "dz_sum", "bwd_dx", "reduce", "core", "zero",
  * "ttm_sort", "ttm_lists", "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level",
  * "ttm_reduce") and its duration in
  * milliseconds.  Waits for the record's end event.

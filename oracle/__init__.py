@@ -38,6 +38,7 @@ from .tt_linear import (  # noqa: F401
     dense_weight,
     tt_linear_forward,
     tt_linear_backward,
+    tt_linear_core_grads,
     chain_core_grads,
 )
 from .ttm_embed import (  # noqa: F401

@@ -17,10 +17,10 @@
 // multiplication, which keeps dead-slice gradients exactly 0.
 //
 // Kernels (one stream, no host synchronisation, no allocation):
-//   k_merge      one wave per row of a left prefix product / column of a right
-//                suffix product; writes the compacted A, B (and transposes) in
-//                the activation dtype plus the fp32 prefix / suffix products
-//                the backward sweep needs
+//   k_sweep      (merge) the prefix / suffix products of both halves, one
+//                level of small fp32-MFMA GEMMs per launch, kept for the sweep
+//   k_pack       the compacted A, B (and transposes) in the activation dtype
+//                from the two half products and the live slices of D_s
 //   k_fwd        per 64-token tile: Z = x A^T with the K range split over the
 //                4 waves (unrolled, many loads in flight), Z summed in LDS and
 //                kept, then Y^T = B Z^T with the B fragments prefetched
@@ -55,81 +55,43 @@ struct ChainPtrs {
 // ------------------------------------------------------------------------------
 // merge
 // ------------------------------------------------------------------------------
-struct MergeArgs {
-  ChainPtrs c;
-  int d, s, rs, Rpad, in_first, max_rank;
-  int modes[kMaxCores];
-  int ranks[kMaxCores + 1];
-  int64_t item_off[kMaxCores + 1];
-  int64_t chain_off[kMaxCores];
-  int64_t N_in, N_out;
+// The products of the two halves are formed level by level as small GEMMs
+// (k_sweep, see the reverse sweep below):
+//   left   M_k = (M_{k-1} diag(D_{k-1})) G_k      (prod n_{<=k}) x r_{k+1}
+//   right  N_k = G_k diag(D_k) N_{k+1}            r_k x (prod n_{>=k})
+// The prefix / suffix products below the split stay in the chain area for the
+// backward sweep; the full halves L = M_{s-1} and R = N_s are then packed by
+// k_pack into the MFMA operands A = diag(D_s) R and B = L (roles swapped when
+// the chain starts with the input modes), keeping only the live slices of the
+// split link: entries of D_s that are exactly zero are dropped on the device.
+struct PackArgs {
+  const float* L;     // NL x rs (row-major)
+  const float* R;     // rs x NRt
+  const float* Ds;    // diagonal of the split link
+  const float* G0;    // copied into the chain area when the left half has more cores
+  const float* Gl;    // (last core) likewise for the right half
+  float* chain0;      // chain area of M_0, or null
+  float* chainl;      // chain area of N_{d-1}, or null
+  int64_t n0, nl;     // floats of G_0 / G_{d-1}
+  int rs, Rpad, in_first;
+  int64_t NL, NRt, N_in, N_out;
   int* meta;
   void* Ac;
   void* AcT;
   void* Bc;
   void* BcT;
-  float* chain;
 };
 
-// core slice G[:, dig, :] (r0 x rn) into LDS, eight independent loads per lane
-// per round
-__device__ __forceinline__ void stage_slice(float* gsl, const float* G, int r0, int rn, int n, int dig, int lane) {
-  const int tot = r0 * rn;
-  for (int e0 = lane; e0 < tot; e0 += 512) {
-    float vals[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + 64 * u;
-      const bool ok = e < tot;
-      const int aa = ok ? e / rn : 0, b = ok ? e % rn : 0;
-      vals[u] = G[((int64_t)aa * n + dig) * rn + b];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (e0 + 64 * u < tot) gsl[e0 + 64 * u] = vals[u];
-  }
-}
-
-// sum_i v[i] * m[i * stride] over LDS operands, eight terms per block so the
-// reads of a block are in flight together (fixed order: deterministic)
-__device__ __forceinline__ float dot_col(const float* v, const float* m, int len, int stride) {
-  float acc0 = 0.f, acc1 = 0.f;
-  int i = 0;
-  for (; i + 8 <= len; i += 8) {
-    float a[8], b[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      a[u] = v[i + u];
-      b[u] = m[(i + u) * stride];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; u += 2) {
-      acc0 += a[u] * b[u];
-      acc1 += a[u + 1] * b[u + 1];
-    }
-  }
-  for (; i < len; ++i) acc0 += v[i] * m[i * stride];
-  return acc0 + acc1;
-}
-
-// One wave (64 lanes) per item; vectors of length <= 128 live in LDS, each
-// step stages the core slice G_t[:, digit, :] in LDS and does one
-// vector-matrix product.
+// One wave per row of L (items [0, NL)) or column of R (the rest).
 template <typename T>
-__global__ __launch_bounds__(64) void k_merge(MergeArgs a) {
+__global__ __launch_bounds__(64) void k_pack(PackArgs a) {
   typedef typename Elem<T>::type E;
-  extern __shared__ float gsl[];  // max_rank x max_rank core slice
-  __shared__ float v[TTC_MAX_RANK];
-  __shared__ float w[TTC_MAX_RANK];
   __shared__ int live[TTC_MAX_RANK];
   const int lane = threadIdx.x;
   const int64_t item = blockIdx.x;
-  const int d = a.d, s = a.s;
-
   // live entries of the split link's diagonal, in increasing link index
-  const float* Ds = a.c.D[s - 1];
-  const bool f0 = lane < a.rs && Ds[lane] != 0.0f;
-  const bool f1 = lane + 64 < a.rs && Ds[lane + 64] != 0.0f;
+  const bool f0 = lane < a.rs && a.Ds[lane] != 0.0f;
+  const bool f1 = lane + 64 < a.rs && a.Ds[lane + 64] != 0.0f;
   const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int c0 = __popcll(m0);
@@ -148,104 +110,27 @@ __global__ __launch_bounds__(64) void k_merge(MergeArgs a) {
     __syncthreads();
     for (int j = lane; j < reff; j += 64) a.meta[kMetaPos + live[j]] = j;
     if (lane == 0) a.meta[kMetaReff] = reff;
+    if (a.chain0)
+      for (int64_t i = lane; i < a.n0; i += 64) a.chain0[i] = a.G0[i];
+    if (a.chainl)
+      for (int64_t i = lane; i < a.nl; i += 64) a.chainl[i] = a.Gl[i];
   }
-
-  // which core's item range holds this item
-  int k = -1;
-  for (int kk = 0; kk < d; ++kk) {
-    int64_t hi;
-    if (kk < s)
-      hi = (kk + 1 < s) ? a.item_off[kk + 1] : a.item_off[d - 1];
-    else
-      hi = (kk - 1 >= s) ? a.item_off[kk - 1] : a.item_off[d];
-    if (item >= a.item_off[kk] && item < hi) k = kk;
-  }
-  if (k < 0) return;
-  const int64_t idx = item - a.item_off[k];
-
-  if (k < s) {
-    // row idx of the prefix product M_k = G_0 D_0 G_1 ... G_k (digits j_0..j_k)
-    int dig[kMaxCores];
-    int64_t rem = idx;
-    for (int t = k; t >= 0; --t) {
-      dig[t] = (int)(rem % a.modes[t]);
-      rem /= a.modes[t];
-    }
-    const int r1 = a.ranks[1];
-    for (int b = lane; b < r1; b += 64) v[b] = a.c.G[0][(int64_t)dig[0] * r1 + b];
-    for (int t = 1; t <= k; ++t) {
-      const int r0 = a.ranks[t], rn = a.ranks[t + 1], n = a.modes[t];
-      const float* G = a.c.G[t];
-      const float* D = a.c.D[t - 1];
-      stage_slice(gsl, G, r0, rn, n, dig[t], lane);
-      for (int aa = lane; aa < r0; aa += 64) v[aa] *= D[aa];
-      __syncthreads();
-      for (int b = lane; b < rn; b += 64) w[b] = dot_col(v, gsl + b, r0, rn);
-      __syncthreads();
-      for (int b = lane; b < rn; b += 64) v[b] = w[b];
-      __syncthreads();
-    }
-    __syncthreads();
-    const int rk = a.ranks[k + 1];
-    if (k < s - 1) {
-      for (int b = lane; b < rk; b += 64) a.chain[a.chain_off[k] + idx * rk + b] = v[b];
-      return;
-    }
-    // a row of L (length rs)
-    for (int j = lane; j < a.Rpad; j += 64) {
-      const int b = j < reff ? live[j] : -1;
-      if (!a.in_first) {  // B row idx
-        const E val = (E)Mma<T>::from_f32(b >= 0 ? v[b] : 0.f);
-        ((E*)a.Bc)[idx * a.Rpad + j] = val;
-        ((E*)a.BcT)[(int64_t)j * a.N_out + idx] = val;
-      } else {  // A column idx
-        const E val = (E)Mma<T>::from_f32(b >= 0 ? Ds[b] * v[b] : 0.f);
-        ((E*)a.Ac)[(int64_t)j * a.N_in + idx] = val;
-        ((E*)a.AcT)[idx * a.Rpad + j] = val;
-      }
-    }
-  } else {
-    // column idx of the suffix product N_k = G_k D_k ... G_{d-1} (digits j_k..j_{d-1})
-    int dig[kMaxCores];
-    int64_t rem = idx;
-    for (int t = d - 1; t >= k; --t) {
-      dig[t] = (int)(rem % a.modes[t]);
-      rem /= a.modes[t];
-    }
-    const int rl = a.ranks[d - 1];
-    for (int b = lane; b < rl; b += 64) v[b] = a.c.G[d - 1][(int64_t)b * a.modes[d - 1] + dig[d - 1]];
-    for (int t = d - 2; t >= k; --t) {
-      const int r0 = a.ranks[t], rn = a.ranks[t + 1], n = a.modes[t];
-      const float* G = a.c.G[t];
-      const float* D = a.c.D[t];
-      stage_slice(gsl, G, r0, rn, n, dig[t], lane);
-      for (int b = lane; b < rn; b += 64) v[b] *= D[b];
-      __syncthreads();
-      for (int aa = lane; aa < r0; aa += 64) w[aa] = dot_col(v, gsl + aa * rn, rn, 1);
-      __syncthreads();
-      for (int aa = lane; aa < r0; aa += 64) v[aa] = w[aa];
-      __syncthreads();
-    }
-    __syncthreads();
-    const int rk = a.ranks[k];
-    if (k > s) {
-      int64_t cols = 1;
-      for (int t = k; t < d; ++t) cols *= a.modes[t];
-      for (int b = lane; b < rk; b += 64) a.chain[a.chain_off[k] + (int64_t)b * cols + idx] = v[b];
-      return;
-    }
-    // a column of R (length rs)
-    for (int j = lane; j < a.Rpad; j += 64) {
-      const int b = j < reff ? live[j] : -1;
-      if (!a.in_first) {  // A column idx
-        const E val = (E)Mma<T>::from_f32(b >= 0 ? Ds[b] * v[b] : 0.f);
-        ((E*)a.Ac)[(int64_t)j * a.N_in + idx] = val;
-        ((E*)a.AcT)[idx * a.Rpad + j] = val;
-      } else {  // B row idx
-        const E val = (E)Mma<T>::from_f32(b >= 0 ? v[b] : 0.f);
-        ((E*)a.Bc)[idx * a.Rpad + j] = val;
-        ((E*)a.BcT)[(int64_t)j * a.N_out + idx] = val;
-      }
+  const bool left = item < a.NL;
+  const int64_t idx = left ? item : item - a.NL;
+  // left rows are B rows unless the chain starts with the input modes
+  const bool is_b = left != (a.in_first != 0);
+  for (int j = lane; j < a.Rpad; j += 64) {
+    const int b = j < reff ? live[j] : -1;
+    float v = 0.f;
+    if (b >= 0) v = left ? a.L[idx * a.rs + b] : a.R[(int64_t)b * a.NRt + idx];
+    if (is_b) {
+      const E val = (E)Mma<T>::from_f32(v);
+      ((E*)a.Bc)[idx * a.Rpad + j] = val;
+      ((E*)a.BcT)[(int64_t)j * a.N_out + idx] = val;
+    } else {
+      const E val = (E)Mma<T>::from_f32(b >= 0 ? a.Ds[b] * v : 0.f);
+      ((E*)a.Ac)[(int64_t)j * a.N_in + idx] = val;
+      ((E*)a.AcT)[idx * a.Rpad + j] = val;
     }
   }
 }
@@ -363,7 +248,7 @@ __device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename 
 // ------------------------------------------------------------------------------
 // LDS of the forward: the Z reduction area (4 waves x 16*TT tokens x Rpad
 // fp32) is dead once Z is summed; the Z tile (16*TT tokens, act dtype) then
-// sits at offset 0 and two staged Y chunks of 16*TT rows x 256 columns
+// sits at offset 0 and two staged Y chunks of 16*TT rows x (at most) 256 columns
 // follow it, overlaying the rest of the reduction area.
 template <typename T, int NR, int TT>
 constexpr int kFwdStageOff() {
@@ -391,9 +276,13 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   constexpr int Rpad = 16 * NR;
   constexpr int EPV = Mma<T>::EPV, KSTEP = Mma<T>::KSTEP;
   constexpr int ZLD = Rpad + 16 / (int)sizeof(E);
-  constexpr int UNR = NR <= 2 ? 4 : (NR <= 4 ? 2 : 1);  // k-steps per batch of loads
+  // k-steps per batch of loads and output tiles per wave and step: fewer for
+  // the wider rank tiles, so that two batches in flight, the accumulators
+  // and three batches of B fragments stay within about 128 registers
+  constexpr int UNR = NR <= 2 ? 4 : 1;
   constexpr int KS = Rpad / KSTEP;
-  constexpr int UO = 4;                                  // output tiles per batch
+  constexpr int UO = NR <= 2 ? 4 : 2;
+  constexpr int TPS = 4 * UO;                            // output tiles per step (all waves)
   extern __shared__ __align__(16) char smem[];
   constexpr int TM = 16 * TT;                     // tokens per work-group
   float* zred = reinterpret_cast<float*>(smem);  // [4 waves][TM tokens][Rpad]
@@ -423,13 +312,17 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
       for (int ks = 0; ks < KS; ++ks)
         f[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + 4 * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
   };
-  // Likewise for B: work-group b visits the 256-column steps of the output
+  // Likewise for B: work-group b visits the output steps (TPS tiles each)
   // starting at step b mod nsteps.
-  const int nsteps = (not_ + 15) / 16;
+  const int nsteps = (not_ + TPS - 1) / TPS;
   const int rot2 = (int)(blockIdx.x % (unsigned)nsteps);
-  auto ostep = [&](int sidx) { return ((sidx + rot2) % nsteps) * 16; };
-  fetch_b(fo0, ostep(0) + w);
-  if (nsteps > 1) fetch_b(fo1, ostep(1) + w);
+  auto ostep = [&](int sidx) { return ((sidx + rot2) % nsteps) * TPS; };
+  // with one rank tile pair the first B batches are requested right away;
+  // wider ranks wait for phase 2 (register budget)
+  if constexpr (NR <= 2) {
+    fetch_b(fo0, ostep(0) + w);
+    if (nsteps > 1) fetch_b(fo1, ostep(1) + w);
+  }
 
   // Z = x A^T: M = token, N = rank, K = input column; wave w takes the
   // k-steps w, w+4, ... so the four waves read adjacent 64-byte pieces.
@@ -496,9 +389,13 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   lds_barrier();
 
   // Y^T = B Z^T: M = output column, N = token, K = rank.  The four waves
-  // cover 16 output tiles (256 columns) per step; the step's Y tile goes
-  // through LDS so that it leaves as whole-row 16-byte stores.
-  constexpr int CW = 256;                       // columns per step
+  // cover TPS output tiles per step; the step's Y tile goes through LDS so
+  // that it leaves as whole-row 16-byte stores.
+  if constexpr (NR > 2) {
+    fetch_b(fo0, ostep(0) + w);
+    if (nsteps > 1) fetch_b(fo1, ostep(1) + w);
+  }
+  constexpr int CW = 16 * TPS;                  // columns per step
   constexpr int YLD = CW + 16 / (int)sizeof(E);  // staged row stride
   E* ys0 = reinterpret_cast<E*>(smem + kFwdStageOff<T, NR, TT>());
   E* ys1 = ys0 + TM * YLD;
@@ -992,6 +889,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
 struct Gemm {
   const float* A;
   int64_t sAi, sAk;
+  const float* ks_;  // optional scale of A's columns (the reduction index), e.g. a link diagonal
   const float* B;
   int64_t sBk, sBj;
   const float* rs_;
@@ -1013,6 +911,7 @@ constexpr int kGStage = kGKC * kGShort > 32 * kGLong ? kGKC * kGShort : 32 * kGL
 // global reads coalesced (strides chosen so that neither the staging writes nor
 // the fragment reads conflict on LDS banks); the four waves split the k-steps
 // of a chunk and their partial tiles are summed in wave order at the end.
+template <bool KS>
 __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, c = lane & 15;
@@ -1036,7 +935,7 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
       const int k = a_kfast ? le % kGKC : le / 32;
       const bool ok = i0 + i < g.M && k0 + k < g.K;
       const float v = g.A[ok ? (i0 + i) * g.sAi + (k0 + k) * g.sAk : 0];
-      ra[e] = ok ? v : 0.f;
+      ra[e] = ok ? (KS ? v * g.ks_[k0 + k] : v) : 0.f;
       const int j = b_jfast ? le % 32 : le / kGKC;
       const int k2 = b_jfast ? le / 32 : le % kGKC;
       const bool ok2 = j0 + j < g.N && k0 + k2 < g.K;
@@ -1105,6 +1004,9 @@ struct SweepArgs {
   int ng;
 };
 
+// KS: the GEMMs scale A's columns by ks_ (the merge levels); the sweep's
+// GEMMs do not, and keep the register budget of the plain tile
+template <bool KS>
 __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
   __shared__ __align__(16) float lds[2 * kGStage];
   int t = blockIdx.x, q = 0;
@@ -1112,7 +1014,7 @@ __global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
     t -= a.tiles[q];
     ++q;
   }
-  gemm_tile32(a.g[q], t, lds);
+  gemm_tile32<KS>(a.g[q], t, lds);
 }
 
 // Left core k, gradient dM_k of the prefix M_k (rows prod_{j<=k} n_j, r_{k+1}
@@ -1123,6 +1025,7 @@ static Gemm left_dG(const LinearPlan& P, const float* chain, const float* const*
                     const float* dMk, int64_t rows) {
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   Gemm g;
+  g.ks_ = nullptr;
   g.A = chain + P.chain_off[k - 1];
   g.sAi = 1;
   g.sAk = r0;
@@ -1143,6 +1046,7 @@ static Gemm left_dM(const LinearPlan& P, const float* const* G, const float* con
                     int64_t rows, float* out) {
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   Gemm g;
+  g.ks_ = nullptr;
   g.A = dMk;
   g.sAi = (int64_t)n * r1;
   g.sAk = 1;
@@ -1168,6 +1072,7 @@ static Gemm right_dG(const LinearPlan& P, const float* chain, const float* const
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   const int64_t be = cols / n;
   Gemm g;
+  g.ks_ = nullptr;
   g.A = dNk;
   g.sAi = be;
   g.sAk = 1;
@@ -1189,6 +1094,7 @@ static Gemm right_dN(const LinearPlan& P, const float* const* G, const float* co
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   const int64_t be = cols / n;
   Gemm g;
+  g.ks_ = nullptr;
   g.A = G[k];
   g.sAi = 1;
   g.sAk = r1;
@@ -1396,23 +1302,82 @@ extern "C" ttc_status tt_linear_workspace(const tt_linear_desc* desc, int64_t T,
 
 namespace ttc {
 static void launch_merge(const LinearPlan& P, const float* const* G, const float* const* D, char* sv, hipStream_t s) {
-  MergeArgs m;
+  float* chain = reinterpret_cast<float*>(sv + P.sv_chain);
+  float* Lf = reinterpret_cast<float*>(sv + P.sv_Lf);
+  float* Rf = reinterpret_cast<float*>(sv + P.sv_Rf);
+  const int d = P.d, S = P.s;
+  const int nlev = std::max(S - 1, d - 1 - S);
+  for (int lvl = 0; lvl < nlev; ++lvl) {
+    SweepArgs a;
+    memset(&a, 0, sizeof(a));
+    int total = 0;
+    auto add = [&](const Gemm& g) {
+      a.g[a.ng] = g;
+      a.tiles[a.ng] = gemm_tiles(g);
+      total += a.tiles[a.ng];
+      ++a.ng;
+    };
+    const int kL = 1 + lvl;  // left: M_kL = (M_{kL-1} D_{kL-1}) G_kL
+    if (kL <= S - 1) {
+      int64_t rows = 1;
+      for (int t = 0; t < kL; ++t) rows *= P.modes[t];
+      Gemm g;
+      memset(&g, 0, sizeof(g));
+      g.A = kL == 1 ? G[0] : chain + P.chain_off[kL - 1];
+      g.sAi = P.ranks[kL];
+      g.sAk = 1;
+      g.ks_ = D[kL - 1];
+      g.B = G[kL];
+      g.sBk = (int64_t)P.modes[kL] * P.ranks[kL + 1];
+      g.sBj = 1;
+      g.C = kL == S - 1 ? Lf : chain + P.chain_off[kL];
+      g.sCi = (int64_t)P.modes[kL] * P.ranks[kL + 1];
+      g.sCj = 1;
+      g.M = (int)rows;
+      g.N = P.modes[kL] * P.ranks[kL + 1];
+      g.K = P.ranks[kL];
+      add(g);
+    }
+    const int kR = d - 2 - lvl;  // right: N_kR = G_kR D_kR N_{kR+1}
+    if (kR >= S) {
+      int64_t cols = 1;
+      for (int t = kR + 1; t < d; ++t) cols *= P.modes[t];
+      Gemm g;
+      memset(&g, 0, sizeof(g));
+      g.A = G[kR];
+      g.sAi = P.ranks[kR + 1];
+      g.sAk = 1;
+      g.ks_ = D[kR];
+      g.B = kR + 1 == d - 1 ? G[d - 1] : chain + P.chain_off[kR + 1];
+      g.sBk = cols;
+      g.sBj = 1;
+      g.C = kR == S ? Rf : chain + P.chain_off[kR];
+      g.sCi = cols;
+      g.sCj = 1;
+      g.M = P.ranks[kR] * P.modes[kR];
+      g.N = (int)cols;
+      g.K = P.ranks[kR + 1];
+      add(g);
+    }
+    TraceScope ts("merge_level", s);
+    TTC_LAUNCH(k_sweep<true>, dim3(total), dim3(256), 0, s, a);
+  }
+  PackArgs m;
   memset(&m, 0, sizeof(m));
-  m.c = chain_ptrs(P, G, D);
-  m.d = P.d;
-  m.s = P.s;
+  m.L = S == 1 ? G[0] : Lf;
+  m.R = d - S == 1 ? G[d - 1] : Rf;
+  m.Ds = D[S - 1];
+  m.G0 = G[0];
+  m.Gl = G[d - 1];
+  m.chain0 = S >= 2 ? chain + P.chain_off[0] : nullptr;
+  m.chainl = d - 1 > S ? chain + P.chain_off[d - 1] : nullptr;
+  m.n0 = (int64_t)P.modes[0] * P.ranks[1];
+  m.nl = (int64_t)P.ranks[d - 1] * P.modes[d - 1];
   m.rs = P.rs;
   m.Rpad = P.Rpad;
   m.in_first = P.in_first;
-  m.max_rank = P.max_rank;
-  for (int k = 0; k < P.d; ++k) {
-    m.modes[k] = P.modes[k];
-    m.chain_off[k] = P.chain_off[k];
-  }
-  for (int k = 0; k <= P.d; ++k) {
-    m.ranks[k] = P.ranks[k];
-    m.item_off[k] = P.item_off[k];
-  }
+  m.NL = P.NL;
+  m.NRt = P.NRt;
   m.N_in = P.N_in;
   m.N_out = P.N_out;
   m.meta = reinterpret_cast<int*>(sv + P.sv_meta);
@@ -1420,13 +1385,11 @@ static void launch_merge(const LinearPlan& P, const float* const* G, const float
   m.AcT = sv + P.sv_AcT;
   m.Bc = sv + P.sv_Bc;
   m.BcT = sv + P.sv_BcT;
-  m.chain = reinterpret_cast<float*>(sv + P.sv_chain);
-  const size_t lds = size_t(P.max_rank) * P.max_rank * sizeof(float);
   TraceScope ts("merge", s);
   if (P.act == TTC_BF16)
-    TTC_LAUNCH(k_merge<bf16_t>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
+    TTC_LAUNCH(k_pack<bf16_t>, dim3((unsigned)(P.NL + P.NRt)), dim3(64), 0, s, m);
   else
-    TTC_LAUNCH(k_merge<float>, dim3((unsigned)P.item_off[P.d]), dim3(64), lds, s, m);
+    TTC_LAUNCH(k_pack<float>, dim3((unsigned)(P.NL + P.NRt)), dim3(64), 0, s, m);
 }
 
 // one event orders the two streams of a split backward; a wait captures the
@@ -1577,7 +1540,7 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
       for (int q = 0; q < a.ng; ++q) total += (a.tiles[q] = gemm_tiles(a.g[q]));
       {
         TraceScope ts("core", s);
-        TTC_LAUNCH(k_sweep, dim3(total), dim3(256), 0, s, a);
+        TTC_LAUNCH(k_sweep<false>, dim3(total), dim3(256), 0, s, a);
       }
       if (hasL) {
         curL = outL;
