@@ -226,6 +226,37 @@ __device__ __forceinline__ void rank_fetch(typename Mma<T>::frag* r, const typen
   }
 }
 
+// Buffer-load forms of the two prefetches (16-byte rows only).  `src` covers
+// the work-group's token range from its first token; `row0` is the slab's
+// first row in that range.  Rows past the last token lie beyond the resource
+// and read as zero; a dead fetch (`live` false) issues the same loads at
+// kNoOff, which return zero without touching memory.
+template <typename T, int NR>
+__device__ __forceinline__ void slab_fetch_b(typename Mma<T>::frag* r, rsrc_t src, int row0, int64_t c0,
+                                             int64_t ncols, bool live) {
+  typedef Bwd<T, NR> B;
+#pragma unroll
+  for (int q = 0; q < B::PER; ++q) {
+    const int gi = threadIdx.x + 256 * q;
+    const int row = gi >> 4, part = gi & 15;
+    const int64_t col = c0 + part * B::EPV;
+    const uint32_t o = (uint32_t)(((int64_t)(row0 + row) * ncols + col) * B::ES);
+    r[q] = buf_frag<T>(src, (live & (col < ncols)) ? o : kNoOff);
+  }
+}
+
+template <typename T, int NR>
+__device__ __forceinline__ void rank_fetch_b(typename Mma<T>::frag* r, rsrc_t src, int row0, bool live) {
+  typedef Bwd<T, NR> B;
+#pragma unroll
+  for (int q = 0; q < B::ZPER; ++q) {
+    const int gi = threadIdx.x + 256 * q;
+    const int row = gi / B::ZG, part = gi % B::ZG;
+    const uint32_t o = (uint32_t)(((row0 + row) * B::Rpad + part * B::EPV) * B::ES);
+    r[q] = buf_frag<T>(src, (live & (gi < 64 * B::ZG)) ? o : kNoOff);
+  }
+}
+
 // write a prefetched rank tile rank-major (transposed) and optionally token-major
 template <typename T, int NR>
 __device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename Elem<T>::type* rm,
@@ -246,7 +277,7 @@ __device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename 
 // ------------------------------------------------------------------------------
 // forward
 // ------------------------------------------------------------------------------
-// LDS of the forward: the Z reduction area (4 waves x 16*TT tokens x Rpad
+// LDS of the forward: the Z reduction area (NW waves x 16*TT tokens x Rpad
 // fp32) is dead once Z is summed; the Z tile (16*TT tokens, act dtype) then
 // sits at offset 0 and two staged Y chunks of 16*TT rows x (at most) 256 columns
 // follow it, overlaying the rest of the reduction area.
@@ -255,17 +286,22 @@ constexpr int kFwdStageOff() {
   return ((16 * TT) * (16 * NR + 16 / (int)sizeof(typename Elem<T>::type)) * (int)sizeof(typename Elem<T>::type) +
           255) / 256 * 256;
 }
-template <typename T, int NR, int TT>
+template <typename T, int NR, int TT, int NW>
 constexpr size_t kFwdLdsBytes() {
-  constexpr size_t red = (size_t)4 * 16 * TT * 16 * NR * 4;
+  constexpr size_t red = (size_t)NW * 16 * TT * 16 * NR * 4;
   constexpr size_t stg = (size_t)kFwdStageOff<T, NR, TT>() + 2 * (size_t)(16 * TT) *
                                                                 (256 + 16 / sizeof(typename Elem<T>::type)) *
                                                                 sizeof(typename Elem<T>::type);
   return red > stg ? red : stg;
 }
 
-template <typename T, int NR, bool VEC, int TT>
-__global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __restrict__ x,
+// NW waves per work-group split the input columns of the first product and
+// the output tiles of the second.  Every work-group reads all of A and B, and
+// those reads (L2 hits) count against the same per-CU load throughput as the
+// reads of x, so the wide variant (NW = 8, 64 tokens, one work-group per CU)
+// reads A and B half as often per token as two 32-token work-groups.
+template <typename T, int NR, bool VEC, int TT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* __restrict__ x,
                                              const typename Elem<T>::type* __restrict__ Ac,
                                              const typename Elem<T>::type* __restrict__ Bc,
                                              typename Elem<T>::type* __restrict__ Z,
@@ -279,13 +315,14 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   // k-steps per batch of loads and output tiles per wave and step: fewer for
   // the wider rank tiles, so that two batches in flight, the accumulators
   // and three batches of B fragments stay within about 128 registers
-  constexpr int UNR = NR <= 2 ? 4 : 1;
+  constexpr int NT = 64 * NW;                           // threads
+  constexpr int UNR = NW == 8 ? (NR <= 2 ? 2 : 1) : (NR <= 2 ? 4 : 1);
   constexpr int KS = Rpad / KSTEP;
-  constexpr int UO = NR <= 2 ? 4 : 2;
-  constexpr int TPS = 4 * UO;                            // output tiles per step (all waves)
+  constexpr int UO = NW == 8 ? 2 : (NR <= 2 ? 4 : 2);
+  constexpr int TPS = NW * UO;                           // output tiles per step (all waves)
   extern __shared__ __align__(16) char smem[];
   constexpr int TM = 16 * TT;                     // tokens per work-group
-  float* zred = reinterpret_cast<float*>(smem);  // [4 waves][TM tokens][Rpad]
+  float* zred = reinterpret_cast<float*>(smem);  // [NW waves][TM tokens][Rpad]
   E* zl = reinterpret_cast<E*>(smem);            // [TM][ZLD], reuses zred after the sum
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -310,7 +347,7 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     for (int uo = 0; uo < UO; ++uo)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        f[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + 4 * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
+        f[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + NW * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
   };
   // Likewise for B: work-group b visits the output steps (TPS tiles each)
   // starting at step b mod nsteps.
@@ -325,15 +362,15 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   }
 
   // Z = x A^T: M = token, N = rank, K = input column; wave w takes the
-  // k-steps w, w+4, ... so the four waves read adjacent 64-byte pieces.
+  // k-steps w, w+NW, ... so the waves read adjacent 64-byte pieces.
   // Two register buffers, unrolled by two so that both stay in registers.
   const int nks = (int)((N_in + KSTEP - 1) / KSTEP);
-  constexpr int KB = 4 * UNR;
+  constexpr int KB = NW * UNR;
   frag fa0[UNR][TT], fb0[UNR][NR], fa1[UNR][TT], fb1[UNR][NR];
   auto fetch_x = [&](frag (&xa)[UNR][TT], frag (&xb)[UNR][NR], int kb) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t col = (int64_t)(kb + 4 * u + w) * KSTEP + g * EPV;
+      const int64_t col = (int64_t)(kb + NW * u + w) * KSTEP + g * EPV;
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) xa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
 #pragma unroll
@@ -370,17 +407,20 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
 #pragma unroll
       for (int vv = 0; vv < 4; ++vv) zred[(w * TM + 16 * u + 4 * g + vv) * Rpad + 16 * n + c] = acc[u][n][vv];
   lds_barrier();
-  constexpr int PER = TM * Rpad / 256;
+  constexpr int PER = TM * Rpad / NT;
   float zs[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    zs[i] = ((zred[idx] + zred[TM * Rpad + idx]) + zred[2 * TM * Rpad + idx]) + zred[3 * TM * Rpad + idx];
+    const int idx = threadIdx.x + NT * i;
+    float z = zred[idx];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) z += zred[v * TM * Rpad + idx];
+    zs[i] = z;
   }
   lds_barrier();
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + 256 * i;
+    const int idx = threadIdx.x + NT * i;
     const int tt = idx / Rpad, j = idx % Rpad;
     const E e = (E)Mma<T>::from_f32(zs[i]);
     if (t0 + tt < T_) Z[(t0 + tt) * Rpad + j] = e;
@@ -388,7 +428,7 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
   }
   lds_barrier();
 
-  // Y^T = B Z^T: M = output column, N = token, K = rank.  The four waves
+  // Y^T = B Z^T: M = output column, N = token, K = rank.  The waves
   // cover TPS output tiles per step; the step's Y tile goes through LDS so
   // that it leaves as whole-row 16-byte stores.
   if constexpr (NR > 2) {
@@ -404,7 +444,7 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     const int ob0 = ostep(sidx);
 #pragma unroll
     for (int uo = 0; uo < UO; ++uo) {
-      const int lt = w + 4 * uo;
+      const int lt = w + NW * uo;
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         f32x4 a2 = zero4();
@@ -427,14 +467,14 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
     const int64_t ncol = std::min<int64_t>(CW, N_out - c0);
     if (vout && (ncol % (16 / (int)sizeof(E))) == 0) {
       const int ngr = (int)(ncol * (int64_t)sizeof(E) / 16);
-      for (int idx = threadIdx.x; idx < TM * GPR; idx += 256) {
+      for (int idx = threadIdx.x; idx < TM * GPR; idx += NT) {
         const int row = idx / GPR, gr = idx - row * GPR;
         if (gr < ngr && t0 + row < T_)
           *reinterpret_cast<uint4*>(y + (t0 + row) * N_out + c0 + gr * (16 / (int)sizeof(E))) =
               *reinterpret_cast<const uint4*>(ys + row * YLD + gr * (16 / (int)sizeof(E)));
       }
     } else {
-      for (int idx = threadIdx.x; idx < TM * CW; idx += 256) {
+      for (int idx = threadIdx.x; idx < TM * CW; idx += NT) {
         const int row = idx / CW, col = idx - row * CW;
         if (col < ncol && t0 + row < T_) y[(t0 + row) * N_out + c0 + col] = ys[row * YLD + col];
       }
@@ -456,6 +496,14 @@ __global__ __launch_bounds__(256) void k_fwd(const typename Elem<T>::type* __res
 // ------------------------------------------------------------------------------
 // backward, dY pass
 // ------------------------------------------------------------------------------
+// Items (slabs) in flight per work-group in the two backward passes: one
+// register set per item, the slab of item it + depth requested while item it
+// is computed from LDS.
+#ifndef TTC_BWD_DEPTH
+#define TTC_BWD_DEPTH 2
+#endif
+constexpr int kBwdDepth = TTC_BWD_DEPTH;
+static_assert(kBwdDepth == 2 || kBwdDepth == 3, "two or three items in flight");
 template <typename T>
 struct DyArgs {
   const typename Elem<T>::type* dy;
@@ -488,16 +536,11 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
   const int64_t c0 = (int64_t)gc * a.nsl * B::SW;
   const int nsl = (int)std::min<int64_t>(a.nsl, (a.N_out - c0 + B::SW - 1) / B::SW);
   const int reff = a.meta[kMetaReff];
-
-  // B^T rows for this column range
-  {
-    const int gpr = nsl * B::SW / B::EPV;
-    for (int gi = tid; gi < B::Rpad * gpr; gi += 256) {
-      const int j = gi / gpr, part = gi % gpr;
-      *reinterpret_cast<frag*>(btl + j * BLD + part * B::EPV) =
-          ld_frag<T, VEC>(a.BcT, j, B::Rpad, c0 + part * B::EPV, a.N_out, a.N_out);
-    }
-  }
+  const int tt0 = gt * a.tpg;
+  const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
+  const int nitems = ntt * nsl;
+  const int64_t tb = (int64_t)tt0 * 64;
+  const int64_t nrow = std::min<int64_t>(a.T_ - tb, (int64_t)ntt * 64);
 
   f32x4 accB[NSM][B::CTW][NR];
 #pragma unroll
@@ -508,22 +551,73 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
       for (int n = 0; n < NR; ++n) accB[s][ct][n] = zero4();
   f32x4 accZ[NR];
 
-  const int tt0 = gt * a.tpg;
-  const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
-  const int nitems = ntt * nsl;
-  // two register sets: the slab (and, at a tile start, the Z tile) of item
-  // it+2 is fetched while item it is computed from LDS
-  frag srA[B::PER], srB[B::PER], zrA[B::ZPER], zrB[B::ZPER];
+  // one register set per item in flight: the slab (and, at a tile start,
+  // the Z tile) of item it + depth is requested while item it is computed
+  // from LDS
+  frag srA[B::PER], srB[B::PER], srC[B::PER], zrA[B::ZPER], zrB[B::ZPER], zrC[B::ZPER];
+  // With 16-byte rows every fetch, store and item is unconditional (buffer
+  // accesses, dead ones at kNoOff), so the count of memory operations between
+  // a fetch and its use is the same on every path and the wait before an item
+  // leaves the later fetches in flight.
+  const rsrc_t rsl = make_rsrc(a.dy + tb * a.N_out, nrow * a.N_out * B::ES);
+  const rsrc_t rzt = make_rsrc(a.Z + tb * B::Rpad, nrow * B::Rpad * B::ES);
+  const rsrc_t rdz = a.gc_n == 1 ? make_rsrc(a.dZ + tb * B::Rpad, nrow * B::Rpad * B::ES)
+                                 : make_rsrc(a.dZp + ((int64_t)gc * a.T_ + tb) * B::Rpad, nrow * B::Rpad * 4);
   auto fetch = [&](int it, frag* sr, frag* zr) {
-    if (it < nitems) {
+    if constexpr (VEC) {
+      const bool live = it < nitems;
+      const int itc = live ? it : 0;
+      const int tn = itc / nsl, sn = itc - tn * nsl;
+      slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_out, live);
+      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0));
+    } else if (it < nitems) {
       const int tn = tt0 + it / nsl, sn = it % nsl;
       slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_out);
       if (sn == 0) rank_fetch<T, NR>(zr, a.Z, (int64_t)tn * 64, a.T_);
     }
   };
+
+  // B^T rows of this column range; with 16-byte rows a fixed number of loads
+  // per thread, requested before the first two items so that the latencies
+  // overlap
+  {
+    const int gpr = nsl * B::SW / B::EPV;
+    if constexpr (VEC) {
+      constexpr int BPER = (B::Rpad * NSM * B::SW / B::EPV + 255) / 256;
+      const rsrc_t rb = make_rsrc(a.BcT, (int64_t)B::Rpad * a.N_out * B::ES);
+      frag bt[BPER];
+#pragma unroll
+      for (int q = 0; q < BPER; ++q) {
+        const int gi = tid + 256 * q;
+        const int j = gi / gpr, part = gi - j * gpr;
+        const int64_t col = c0 + part * B::EPV;
+        const uint32_t o = (uint32_t)(((int64_t)j * a.N_out + col) * B::ES);
+        bt[q] = buf_frag<T>(rb, ((gi < B::Rpad * gpr) & (col < a.N_out)) ? o : kNoOff);
+      }
+      fetch(0, srA, zrA);
+      fetch(1, srB, zrB);
+      if constexpr (kBwdDepth == 3) fetch(2, srC, zrC);
+#pragma unroll
+      for (int q = 0; q < BPER; ++q) {
+        const int gi = tid + 256 * q;
+        const int j = gi / gpr, part = gi - j * gpr;
+        if (gi < B::Rpad * gpr) *reinterpret_cast<frag*>(btl + j * BLD + part * B::EPV) = bt[q];
+      }
+    } else {
+      for (int gi = tid; gi < B::Rpad * gpr; gi += 256) {
+        const int j = gi / gpr, part = gi % gpr;
+        *reinterpret_cast<frag*>(btl + j * BLD + part * B::EPV) =
+            ld_frag<T, VEC>(a.BcT, j, B::Rpad, c0 + part * B::EPV, a.N_out, a.N_out);
+      }
+      fetch(0, srA, zrA);
+      fetch(1, srB, zrB);
+      if constexpr (kBwdDepth == 3) fetch(2, srC, zrC);
+    }
+  }
+
   auto body = [&](int it, frag* sr, frag* zr, int buf) {
-    const int tt = tt0 + it / nsl, sb = it % nsl;
-    const int64_t t0 = (int64_t)tt * 64;
+    const bool live = it < nitems;
+    const int tn = it / nsl, sb = it - tn * nsl;
     if (sb == 0) {
       lds_barrier();  // readers of the previous tile's Z^T are done
       rank_store<T, NR>(ztl, nullptr, zr);
@@ -532,39 +626,62 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
-    fetch(it + 2, sr, zr);
+    fetch(it + kBwdDepth, sr, zr);
     lds_barrier();
-    // dZ: M = token (16-row tile w), N = rank, K = column of the slab
+    if (live) {
+      // dZ: M = token (16-row tile w), N = rank, K = column of the slab
 #pragma unroll
-    for (int ks = 0; ks < B::SW / B::KSTEP; ++ks) {
-      const int kc = ks * B::KSTEP + g * B::EPV;
-      const frag fa = lds_frag<T>(sl + (16 * w + c) * B::SLD + kc);
+      for (int ks = 0; ks < B::SW / B::KSTEP; ++ks) {
+        const int kc = ks * B::KSTEP + g * B::EPV;
+        const frag fa = lds_frag<T>(sl + (16 * w + c) * B::SLD + kc);
 #pragma unroll
-      for (int n = 0; n < NR; ++n)
-        accZ[n] = Mma<T>::mma(fa, lds_frag<T>(btl + (16 * n + c) * BLD + sb * B::SW + kc), accZ[n]);
-    }
-    // dB^T: M = rank, N = column (tiles ct*4+w of the slab), K = token
+        for (int n = 0; n < NR; ++n)
+          accZ[n] = Mma<T>::mma(fa, lds_frag<T>(btl + (16 * n + c) * BLD + sb * B::SW + kc), accZ[n]);
+      }
+      // dB^T: M = rank, N = column (tiles ct*4+w of the slab), K = token
 #pragma unroll
-    for (int s = 0; s < NSM; ++s) {
-      if (s == sb) {
+      for (int s = 0; s < NSM; ++s) {
+        if (s == sb) {
 #pragma unroll
-        for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
-          const int kt = ks * B::KSTEP + g * B::EPV;
-          frag fb[B::CTW];
+          for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
+            const int kt = ks * B::KSTEP + g * B::EPV;
+            frag fb[B::CTW];
 #pragma unroll
-          for (int ct = 0; ct < B::CTW; ++ct)
-            fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
+            for (int ct = 0; ct < B::CTW; ++ct)
+              fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
 #pragma unroll
-          for (int n = 0; n < NR; ++n) {
-            const frag fa = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
+            for (int n = 0; n < NR; ++n) {
+              const frag fa = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
-            for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fa, fb[ct], accB[s][ct][n]);
+              for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fa, fb[ct], accB[s][ct][n]);
+            }
           }
         }
       }
     }
-    if (sb == nsl - 1) {
-      // tokens t0+16w+4g+v, rank column 16n+c
+    // dZ (or this column group's partial) once the tile's last slab is in:
+    // tokens 64 tn + 16w+4g+v of the group, rank column 16n+c
+    if constexpr (VEC) {
+      const bool st = live & (sb == nsl - 1);
+      if (a.gc_n == 1) {
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const uint32_t o = (uint32_t)(((64 * tn + 16 * w + 4 * g + vv) * B::Rpad + 16 * n + c) * B::ES);
+            buf_store(rdz, st ? o : kNoOff, (E)Mma<T>::from_f32(accZ[n][vv]));
+          }
+      } else {
+#pragma unroll
+        for (int n = 0; n < NR; ++n)
+#pragma unroll
+          for (int vv = 0; vv < 4; ++vv) {
+            const uint32_t o = (uint32_t)(((64 * tn + 16 * w + 4 * g + vv) * B::Rpad + 16 * n + c) * 4);
+            buf_store(rdz, st ? o : kNoOff, accZ[n][vv]);
+          }
+      }
+    } else if (live && sb == nsl - 1) {
+      const int64_t t0 = tb + 64 * (int64_t)tn;
       if (a.gc_n == 1) {
 #pragma unroll
         for (int n = 0; n < NR; ++n)
@@ -584,11 +701,11 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
       }
     }
   };
-  fetch(0, srA, zrA);
-  fetch(1, srB, zrB);
-  for (int it = 0; it < nitems; it += 2) {
-    body(it, srA, zrA, 0);
-    if (it + 1 < nitems) body(it + 1, srB, zrB, 1);
+  for (int it = 0; it < nitems; it += kBwdDepth) {
+    body(it, srA, zrA, it & 1);
+    if (VEC || it + 1 < nitems) body(it + 1, srB, zrB, (it + 1) & 1);
+    if constexpr (kBwdDepth == 3)
+      if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1);
   }
   // dB^T partial of this token group: rank 16n+4g+v, column c0+s*SW+(ct*4+w)*16+c
 #pragma unroll
@@ -658,15 +775,11 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
   const int64_t c0 = (int64_t)gc * a.nsl * B::SW;
   const int nsl = (int)std::min<int64_t>(a.nsl, (a.N_in - c0 + B::SW - 1) / B::SW);
   const int reff = a.meta[kMetaReff];
-
-  {
-    constexpr int gpr = B::Rpad / B::EPV;
-    for (int gi = tid; gi < nsl * B::SW * gpr; gi += 256) {
-      const int i = gi / gpr, part = gi % gpr;
-      *reinterpret_cast<frag*>(atl + i * B::RLD + part * B::EPV) =
-          load_frag_v<T>(a.AcT, c0 + i, a.N_in, part * B::EPV, B::Rpad, B::Rpad);
-    }
-  }
+  const int tt0 = gt * a.tpg;
+  const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
+  const int nitems = ntt * nsl;
+  const int64_t tb = (int64_t)tt0 * 64;
+  const int64_t nrow = std::min<int64_t>(a.T_ - tb, (int64_t)ntt * 64);
 
   f32x4 accA[NSM][B::CTW][NR];
 #pragma unroll
@@ -676,51 +789,89 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
 #pragma unroll
       for (int n = 0; n < NR; ++n) accA[s][ct][n] = zero4();
 
-  const int tt0 = gt * a.tpg;
-  const int ntt = std::min(a.ntiles, tt0 + a.tpg) - tt0;
-  const int nitems = ntt * nsl;
-  frag srA[B::PER], srB[B::PER], zrA[B::ZPER], zrB[B::ZPER];
+  // one register set per item in flight; with 16-byte rows every fetch,
+  // store and item is unconditional (buffer accesses, dead ones at kNoOff), so
+  // the wait before an item leaves the later fetches in flight
+  frag srA[B::PER], srB[B::PER], srC[B::PER], zrA[B::ZPER], zrB[B::ZPER], zrC[B::ZPER];
+  const rsrc_t rsl = make_rsrc(a.x + tb * a.N_in, nrow * a.N_in * B::ES);
+  const rsrc_t rzt = make_rsrc(a.dZ + tb * B::Rpad, nrow * B::Rpad * B::ES);
+  const rsrc_t rdx = make_rsrc(a.dx ? a.dx + tb * a.N_in : a.x, a.dx ? nrow * a.N_in * B::ES : 0);
   auto fetch = [&](int it, frag* sr, frag* zr) {
-    if (it < nitems) {
+    if constexpr (VEC) {
+      const bool live = it < nitems;
+      const int itc = live ? it : 0;
+      const int tn = itc / nsl, sn = itc - tn * nsl;
+      slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_in, live);
+      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0));
+    } else if (it < nitems) {
       const int tn = tt0 + it / nsl, sn = it % nsl;
       slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_in);
       if (sn == 0) rank_fetch<T, NR>(zr, a.dZ, (int64_t)tn * 64, a.T_);
     }
   };
-  auto body = [&](int it, frag* sr, frag* zr, int buf) {
 
-    const int tt = tt0 + it / nsl, sb = it % nsl;
-    const int64_t t0 = (int64_t)tt * 64;
+  // A^T rows of this column range (16-byte rows): a fixed number of loads per
+  // thread, requested before the first two items so that the latencies overlap
+  {
+    constexpr int gpr = B::Rpad / B::EPV;
+    constexpr int APER = (NSM * B::SW * gpr + 255) / 256;
+    const rsrc_t ra = make_rsrc(a.AcT + c0 * B::Rpad, (std::min<int64_t>(a.N_in, c0 + (int64_t)nsl * B::SW) - c0) * B::Rpad * B::ES);
+    frag at[APER];
+#pragma unroll
+    for (int q = 0; q < APER; ++q) {
+      const int gi = tid + 256 * q;
+      at[q] = buf_frag<T>(ra, gi < nsl * B::SW * gpr ? (uint32_t)(gi * B::EPV * B::ES) : kNoOff);
+    }
+    fetch(0, srA, zrA);
+    fetch(1, srB, zrB);
+    if constexpr (kBwdDepth == 3) fetch(2, srC, zrC);
+#pragma unroll
+    for (int q = 0; q < APER; ++q) {
+      const int gi = tid + 256 * q;
+      const int i = gi / gpr, part = gi % gpr;
+      if (gi < nsl * B::SW * gpr) *reinterpret_cast<frag*>(atl + i * B::RLD + part * B::EPV) = at[q];
+    }
+  }
+
+  auto body = [&](int it, frag* sr, frag* zr, int buf) {
+    const bool live = it < nitems;
+    const int tn = it / nsl, sb = it - tn * nsl;
+    const int64_t t0 = tb + 64 * (int64_t)tn;
     if (sb == 0) {
       lds_barrier();
       rank_store<T, NR>(dztl, dzl, zr);
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
-    fetch(it + 2, sr, zr);
+    fetch(it + kBwdDepth, sr, zr);
     lds_barrier();
-    // dA: M = rank, N = input column, K = token (reads the x slab first, so
-    // that the slab buffer can then stage this slab's dX)
+    if (live) {
+      // dA: M = rank, N = input column, K = token (reads the x slab first, so
+      // that the slab buffer can then stage this slab's dX)
 #pragma unroll
-    for (int s = 0; s < NSM; ++s) {
-      if (s == sb) {
+      for (int s = 0; s < NSM; ++s) {
+        if (s == sb) {
 #pragma unroll
-        for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
-          const int kt = ks * B::KSTEP + g * B::EPV;
-          frag fb[B::CTW];
+          for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
+            const int kt = ks * B::KSTEP + g * B::EPV;
+            frag fb[B::CTW];
 #pragma unroll
-          for (int ct = 0; ct < B::CTW; ++ct)
-            fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
+            for (int ct = 0; ct < B::CTW; ++ct)
+              fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
 #pragma unroll
-          for (int n = 0; n < NR; ++n) {
-            const frag fa = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
+            for (int n = 0; n < NR; ++n) {
+              const frag fa = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
-            for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fa, fb[ct], accA[s][ct][n]);
+              for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fa, fb[ct], accA[s][ct][n]);
+            }
           }
         }
       }
     }
-    if (a.dx) {
+    // without dX (a null pointer) the 16-byte-row form still runs the stores,
+    // all of them dropped by an empty resource, to keep the memory operations
+    // the same on every path
+    if (VEC || a.dx) {
       // dX^T = A^T dZ^T: M = input column (tiles ct*4+w of the slab), N = token, K = rank
       f32x4 accX[B::CTW][4];
 #pragma unroll
@@ -741,7 +892,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
       if constexpr (VEC) {
         // the slab's dX leaves through the slab buffer as whole 16-byte row
         // pieces: every wave is done reading the x slab, the tile is staged,
-        // then stored row by row
+        // then stored row by row (dead rows, columns and items at kNoOff)
         lds_barrier();
 #pragma unroll
         for (int ct = 0; ct < B::CTW; ++ct) {
@@ -766,11 +917,11 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
           const int idx = tid + 256 * k;
           const int row = idx / GPR, q = idx % GPR;
           const int64_t col = cs0 + q * EPG;
-          if (t0 + row < a.T_ && col < a.N_in)
-            *reinterpret_cast<uint4*>(a.dx + (t0 + row) * a.N_in + col) =
-                *reinterpret_cast<const uint4*>(sl + row * B::SLD + q * EPG);
+          const uint32_t o = (uint32_t)(((int64_t)(64 * tn + row) * a.N_in + col) * B::ES);
+          buf_store16(rdx, (live & (col < a.N_in)) ? o : kNoOff,
+                      *reinterpret_cast<const uint4*>(sl + row * B::SLD + q * EPG));
         }
-      } else {
+      } else if (live) {
 #pragma unroll
         for (int ct = 0; ct < B::CTW; ++ct) {
           const int64_t i0 = cs0 + (ct * 4 + w) * 16 + 4 * g;
@@ -784,11 +935,11 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
       }
     }
   };
-  fetch(0, srA, zrA);
-  fetch(1, srB, zrB);
-  for (int it = 0; it < nitems; it += 2) {
-    body(it, srA, zrA, 0);
-    if (it + 1 < nitems) body(it + 1, srB, zrB, 1);
+  for (int it = 0; it < nitems; it += kBwdDepth) {
+    body(it, srA, zrA, it & 1);
+    if (VEC || it + 1 < nitems) body(it + 1, srB, zrB, (it + 1) & 1);
+    if constexpr (kBwdDepth == 3)
+      if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1);
   }
 #pragma unroll
   for (int s = 0; s < NSM; ++s) {
@@ -1151,11 +1302,11 @@ static void allow_lds(const void* kern, size_t bytes) {
   if (bytes > 65536) (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <typename T, int NR, bool VEC, int TT>
+template <typename T, int NR, bool VEC, int TT, int NW>
 static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
   typedef typename Elem<T>::type E;
-  const size_t lds = kFwdLdsBytes<T, NR, TT>();
-  auto kern = k_fwd<T, NR, VEC, TT>;
+  const size_t lds = kFwdLdsBytes<T, NR, TT, NW>();
+  auto kern = k_fwd<T, NR, VEC, TT, NW>;
   static bool lds_set = false;
   if (!lds_set) {
     allow_lds((const void*)kern, lds);
@@ -1164,22 +1315,28 @@ static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* 
   const int vout = (P.N_out % 4) == 0 && aligned16(y);
   const unsigned grid = (unsigned)((P.T + 16 * TT - 1) / (16 * TT));
   TraceScope ts("fwd", st);
-  TTC_LAUNCH(kern, dim3(grid), dim3(256), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
+  TTC_LAUNCH(kern, dim3(grid), dim3(64 * NW), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
                      (const E*)(saved + P.sv_Bc), (E*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, (int)VEC, vout);
 }
 
-// 32-token work-groups until there are enough 64-token ones to give every CU two
+// 2-byte activations up to rank 64: 64-token work-groups of eight waves once
+// there are enough tiles to give every CU one; otherwise 32-token
+// work-groups of four waves.
 template <typename T, int NR>
 static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
   const bool vec = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x);
-#ifndef TTC_FWD_BIG_TILES
-#define TTC_FWD_BIG_TILES 512
+#ifndef TTC_FWD_WIDE_TILES
+#define TTC_FWD_WIDE_TILES 256
 #endif
-  const bool big = P.ntiles >= TTC_FWD_BIG_TILES && sizeof(typename Elem<T>::type) == 2;
-  if (vec && big) launch_fwd_v<T, NR, true, 4>(P, x, saved, y, st);
-  else if (vec) launch_fwd_v<T, NR, true, 2>(P, x, saved, y, st);
-  else if (big) launch_fwd_v<T, NR, false, 4>(P, x, saved, y, st);
-  else launch_fwd_v<T, NR, false, 2>(P, x, saved, y, st);
+  if constexpr (sizeof(typename Elem<T>::type) == 2 && NR <= 4) {
+    if (P.ntiles >= TTC_FWD_WIDE_TILES) {
+      if (vec) launch_fwd_v<T, NR, true, 4, 8>(P, x, saved, y, st);
+      else launch_fwd_v<T, NR, false, 4, 8>(P, x, saved, y, st);
+      return;
+    }
+  }
+  if (vec) launch_fwd_v<T, NR, true, 2, 4>(P, x, saved, y, st);
+  else launch_fwd_v<T, NR, false, 2, 4>(P, x, saved, y, st);
 }
 
 template <typename T, int NR, bool VY, bool VX>

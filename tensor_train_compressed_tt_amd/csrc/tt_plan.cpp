@@ -110,40 +110,49 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   // token tiles.  Splitting the columns of the dY pass costs partial sums of
   // the T x r intermediate dZ (and the dX pass re-reads dZ once per column
   // group); splitting the tokens costs partial sums of the r x N weight-side
-  // gradients.  Pick the split with the fewest extra bytes that still gives
-  // about one work-group per CU.
+  // gradients.  The passes are bound by each CU's share of the memory
+  // traffic, so the time of a shape is the bytes of the busiest CU: the
+  // work-groups per CU (rounded up) times the bytes of one work-group.  The
+  // partials that the reductions read back later run beside the streaming
+  // passes and weigh half.
   P->ntiles = (int)((T + kTileT - 1) / kTileT);
   const int nt = std::max(1, P->ntiles);
   P->sw = slab_cols(P->es);
-  const int target = 512;  // two work-groups per CU
+#ifndef TTC_BWD_CUS
+#define TTC_BWD_CUS 256  // compute units of an MI355X
+#endif
+  const double ncu = TTC_BWD_CUS;
   auto choose = [&](int64_t ncols, int maxs, bool dy, int* gc, int* gt, int* nsl, int* tpg) {
     const int chunks = (int)std::max<int64_t>(1, (ncols + P->sw - 1) / P->sw);
     const int gc_min = (chunks + maxs - 1) / maxs;
     double best = 1e300;
-    int bgc = gc_min, bgt = 1;
+    int bsl = (chunks + gc_min - 1) / gc_min, bper = nt;
     for (int g = gc_min; g <= chunks; ++g) {
-      int t_groups = std::max(1, std::min(nt, (target + g - 1) / g));
-      const int per = (nt + t_groups - 1) / t_groups;
-      t_groups = (nt + per - 1) / per;
-      const double wgs = double(g) * t_groups;
-      double extra = 8.0 * t_groups * ncols * P->rs;  // weight-side partials, written and read
-      if (dy)
-        extra += (g > 1 ? 8.0 * g * double(T) * P->Rpad : 0.0);
-      else
-        extra += double(g) * T * P->Rpad * P->es;  // dZ re-read per column group
-      const double stream = double(T) * ncols * P->es * (dy ? 1.0 : 2.0);
-      const double fill = std::min(1.0, wgs / target);
-      const double cost = stream / fill + extra;
-      if (cost < best) {
-        best = cost;
-        bgc = g;
-        bgt = t_groups;
+      const int sl = (chunks + g - 1) / g;
+      if ((chunks + sl - 1) / sl != g) continue;  // same shape as a smaller g
+      for (int per = 1; per <= nt; ++per) {
+        const int tg = (nt + per - 1) / per;
+        if ((nt + tg - 1) / tg != per) continue;
+        const double cols = double(sl) * P->sw, toks = double(per) * kTileT;
+        double wg = toks * cols * P->es * (dy ? 1.0 : 2.0);  // streamed activations
+        wg += 4.0 * P->rs * cols;                             // weight-side partial
+        if (dy)
+          wg += (g > 1 ? 4.0 : 0.0) * toks * P->Rpad + toks * P->Rpad * P->es;  // dZ partial, Z tile
+        else
+          wg += toks * P->Rpad * P->es;  // dZ tile
+        const double later = 4.0 * tg * P->rs * double(ncols) + (dy && g > 1 ? 4.0 * g * double(T) * P->Rpad : 0.0);
+        const double cost = std::ceil(double(g) * tg / ncu) * wg + 0.5 * later / ncu;
+        if (cost < best * (1 - 1e-9)) {
+          best = cost;
+          bsl = sl;
+          bper = per;
+        }
       }
     }
-    *nsl = (chunks + bgc - 1) / bgc;
-    *gc = (chunks + *nsl - 1) / *nsl;  // no empty column groups
-    *tpg = (nt + bgt - 1) / bgt;
-    *gt = (nt + *tpg - 1) / *tpg;
+    *nsl = bsl;
+    *gc = (chunks + bsl - 1) / bsl;
+    *tpg = bper;
+    *gt = (nt + bper - 1) / bper;
   };
   choose(nout, bwd_max_slabs(P->es, P->NR), true, &P->dy_gc, &P->dy_gt, &P->dy_nsl, &P->dy_tpg);
   choose(nin, dx_max_slabs(P->es, P->NR), false, &P->dx_gc, &P->dx_gt, &P->dx_nsl, &P->dx_tpg);

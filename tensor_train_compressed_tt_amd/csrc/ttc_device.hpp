@@ -129,6 +129,40 @@ __device__ __forceinline__ typename Mma<T>::frag ld_frag(const typename Elem<T>:
     return load_frag<T>(base, row, nrows, col, ncols, ld, false);
 }
 
+// Buffer loads.  A raw buffer resource over `bytes` bytes returns zero, with no
+// memory access, for a load at a byte offset at or beyond `bytes`.  A guarded
+// load is then one unconditional instruction whose offset is swapped for
+// kNoOff when the element is out of range: no branch, so the compiler knows
+// how many loads were issued after any other and waits for exactly the one
+// it needs instead of draining all outstanding loads.  Resources are at most
+// 2^31 - 1 bytes, so kNoOff plus any instruction offset is out of range.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kNoOff = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  // third descriptor word of an untyped 32-bit-format buffer on gfx9-class GPUs
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag buf_frag(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Stores through a buffer resource: a store at an out-of-range offset is
+// dropped, so guarded stores need no branch either.
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, unsigned short v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
+}
+
 // Same from LDS (always in range, 16-byte aligned).
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag lds_frag(const typename Elem<T>::type* p) {
