@@ -339,15 +339,32 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   // after a store cannot be waited for before that store completes.  Every
   // batch of operands is therefore requested one step ahead, before the
   // stores of the current step: the first B fragments at the very start,
-  // the next x / A batch before the current batch's MFMAs.
+  // the next x / A batch before the current batch's MFMAs.  With 16-byte
+  // rows (VEC) every load and store is a buffer access and every batch and
+  // output step runs, dead ones at kNoOff, so the count of memory operations
+  // between a request and its use is the same on every path and each wait
+  // leaves the later requests in flight.
+  const int64_t nrows = std::min<int64_t>(TM, T_ - t0);
+  const rsrc_t rx = make_rsrc(x + t0 * N_in, nrows * N_in * (int64_t)sizeof(E));
+  const rsrc_t ra = make_rsrc(Ac, (int64_t)Rpad * N_in * (int64_t)sizeof(E));
+  const rsrc_t rb = make_rsrc(Bc, N_out * Rpad * (int64_t)sizeof(E));
+  const rsrc_t rz = make_rsrc(Z + t0 * Rpad, nrows * Rpad * (int64_t)sizeof(E));
+  const rsrc_t ry = make_rsrc(y + t0 * N_out, nrows * N_out * (int64_t)sizeof(E));
   const int not_ = (int)((N_out + 15) / 16);
   frag fo0[UO][KS], fo1[UO][KS], fo2[UO][KS];
-  auto fetch_b = [&](frag (&f)[UO][KS], int ob) {
+  auto fetch_b = [&](frag (&f)[UO][KS], int ob, bool live) {
 #pragma unroll
     for (int uo = 0; uo < UO; ++uo)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        f[uo][ks] = load_frag_v<T>(Bc, (int64_t)(ob + NW * uo) * 16 + c, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int64_t row = (int64_t)(ob + NW * uo) * 16 + c;
+        if constexpr (VEC) {
+          const uint32_t o = (uint32_t)((row * Rpad + ks * KSTEP + g * EPV) * (int64_t)sizeof(E));
+          f[uo][ks] = buf_frag<T>(rb, (live & (row < N_out)) ? o : kNoOff);
+        } else {
+          f[uo][ks] = load_frag_v<T>(Bc, row, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
+        }
+      }
   };
   // Likewise for B: work-group b visits the output steps (TPS tiles each)
   // starting at step b mod nsteps.
@@ -357,8 +374,8 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   // with one rank tile pair the first B batches are requested right away;
   // wider ranks wait for phase 2 (register budget)
   if constexpr (NR <= 2) {
-    fetch_b(fo0, ostep(0) + w);
-    if (nsteps > 1) fetch_b(fo1, ostep(1) + w);
+    fetch_b(fo0, ostep(0) + w, true);
+    fetch_b(fo1, ostep(1) + w, nsteps > 1);
   }
 
   // Z = x A^T: M = token, N = rank, K = input column; wave w takes the
@@ -367,14 +384,25 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   const int nks = (int)((N_in + KSTEP - 1) / KSTEP);
   constexpr int KB = NW * UNR;
   frag fa0[UNR][TT], fb0[UNR][NR], fa1[UNR][TT], fb1[UNR][NR];
-  auto fetch_x = [&](frag (&xa)[UNR][TT], frag (&xb)[UNR][NR], int kb) {
+  auto fetch_x = [&](frag (&xa)[UNR][TT], frag (&xb)[UNR][NR], int kb, bool live) {
+    if (!VEC && !live) return;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t col = (int64_t)(kb + NW * u + w) * KSTEP + g * EPV;
+      if constexpr (VEC) {
+        const bool ok = live & (col < N_in);
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) xa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
+        for (int tt = 0; tt < TT; ++tt)
+          xa[u][tt] = buf_frag<T>(rx, ok ? (uint32_t)(((16 * tt + c) * N_in + col) * (int64_t)sizeof(E)) : kNoOff);
 #pragma unroll
-      for (int n = 0; n < NR; ++n) xb[u][n] = ld_frag<T, VEC>(Ac, 16 * n + c, Rpad, col, N_in, N_in);
+        for (int n = 0; n < NR; ++n)
+          xb[u][n] = buf_frag<T>(ra, ok ? (uint32_t)(((16 * n + c) * N_in + col) * (int64_t)sizeof(E)) : kNoOff);
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) xa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
+#pragma unroll
+        for (int n = 0; n < NR; ++n) xb[u][n] = ld_frag<T, VEC>(Ac, 16 * n + c, Rpad, col, N_in, N_in);
+      }
     }
   };
   auto mma_x = [&](const frag (&xa)[UNR][TT], const frag (&xb)[UNR][NR]) {
@@ -391,13 +419,13 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   const int nkb = (nks + KB - 1) / KB;
   const int rot1 = (int)(blockIdx.x % (unsigned)nkb);
   auto kbat = [&](int j) { return ((j + rot1) % nkb) * KB; };
-  fetch_x(fa0, fb0, kbat(0));
+  fetch_x(fa0, fb0, kbat(0), true);
   for (int j = 0; j < nkb; j += 2) {
-    if (j + 1 < nkb) fetch_x(fa1, fb1, kbat(j + 1));
+    fetch_x(fa1, fb1, kbat(j + 1), j + 1 < nkb);
     mma_x(fa0, fb0);
-    if (j + 1 >= nkb) break;
-    if (j + 2 < nkb) fetch_x(fa0, fb0, kbat(j + 2));
-    mma_x(fa1, fb1);
+    if (!VEC && j + 1 >= nkb) break;
+    fetch_x(fa0, fb0, kbat(j + 2), j + 2 < nkb);
+    mma_x(fa1, fb1);  // a dead batch is zeros and adds nothing
   }
   // lane (g, c) holds Z rows 4g+v of token tile u, rank column 16n+c
 #pragma unroll
@@ -423,7 +451,10 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
     const int idx = threadIdx.x + NT * i;
     const int tt = idx / Rpad, j = idx % Rpad;
     const E e = (E)Mma<T>::from_f32(zs[i]);
-    if (t0 + tt < T_) Z[(t0 + tt) * Rpad + j] = e;
+    if constexpr (VEC)
+      buf_store(rz, (uint32_t)((tt * Rpad + j) * (int)sizeof(E)), e);
+    else if (t0 + tt < T_)
+      Z[(t0 + tt) * Rpad + j] = e;
     zl[tt * ZLD + j] = e;
   }
   lds_barrier();
@@ -432,8 +463,8 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   // cover TPS output tiles per step; the step's Y tile goes through LDS so
   // that it leaves as whole-row 16-byte stores.
   if constexpr (NR > 2) {
-    fetch_b(fo0, ostep(0) + w);
-    if (nsteps > 1) fetch_b(fo1, ostep(1) + w);
+    fetch_b(fo0, ostep(0) + w, true);
+    fetch_b(fo1, ostep(1) + w, nsteps > 1);
   }
   constexpr int CW = 16 * TPS;                  // columns per step
   constexpr int YLD = CW + 16 / (int)sizeof(E);  // staged row stride
@@ -441,6 +472,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   E* ys1 = ys0 + TM * YLD;
   constexpr int GPR = CW * (int)sizeof(E) / 16;  // 16-byte groups per staged row
   auto out_step = [&](const frag (&f)[UO][KS], frag (&fn)[UO][KS], int sidx, E* ys) {
+    const bool live = sidx < nsteps;
     const int ob0 = ostep(sidx);
 #pragma unroll
     for (int uo = 0; uo < UO; ++uo) {
@@ -461,11 +493,22 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
         }
       }
     }
-    if (sidx + 2 < nsteps) fetch_b(fn, ostep(sidx + 2) + w);
+    if (VEC || sidx + 2 < nsteps) fetch_b(fn, ostep(sidx + 2) + w, sidx + 2 < nsteps);
     lds_barrier();
     const int64_t c0 = (int64_t)ob0 * 16;
     const int64_t ncol = std::min<int64_t>(CW, N_out - c0);
-    if (vout && (ncol % (16 / (int)sizeof(E))) == 0) {
+    if constexpr (VEC) {
+      constexpr int EPG = 16 / (int)sizeof(E);
+      static_assert(TM * GPR % NT == 0, "whole 16-byte groups per thread");
+#pragma unroll
+      for (int k = 0; k < TM * GPR / NT; ++k) {
+        const int idx = threadIdx.x + NT * k;
+        const int row = idx / GPR, gr = idx - row * GPR;
+        const int64_t col = c0 + gr * EPG;
+        const uint32_t o = (uint32_t)((row * N_out + col) * (int64_t)sizeof(E));
+        buf_store16(ry, (live & (col < N_out)) ? o : kNoOff, *reinterpret_cast<const uint4*>(ys + row * YLD + gr * EPG));
+      }
+    } else if (vout && (ncol % (16 / (int)sizeof(E))) == 0) {
       const int ngr = (int)(ncol * (int64_t)sizeof(E) / 16);
       for (int idx = threadIdx.x; idx < TM * GPR; idx += NT) {
         const int row = idx / GPR, gr = idx - row * GPR;
@@ -486,9 +529,9 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   // steps later, after the barrier of the step in between
   for (int sidx = 0; sidx < nsteps; sidx += 3) {
     out_step(fo0, fo2, sidx, (sidx & 1) ? ys1 : ys0);
-    if (sidx + 1 >= nsteps) break;
+    if (!VEC && sidx + 1 >= nsteps) break;
     out_step(fo1, fo0, sidx + 1, (sidx & 1) ? ys0 : ys1);
-    if (sidx + 2 >= nsteps) break;
+    if (!VEC && sidx + 2 >= nsteps) break;
     out_step(fo2, fo1, sidx + 2, (sidx & 1) ? ys1 : ys0);
   }
 }
@@ -1324,7 +1367,8 @@ static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* 
 // work-groups of four waves.
 template <typename T, int NR>
 static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
-  const bool vec = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x);
+  // 16-byte rows of both x and Y: the buffer-access form
+  const bool vec = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x) && (P.N_out % Mma<T>::EPV) == 0 && aligned16(y);
 #ifndef TTC_FWD_WIDE_TILES
 #define TTC_FWD_WIDE_TILES 256
 #endif
