@@ -238,29 +238,35 @@ def main():
                               scratch=scratch)
         ttm_bwd()
 
+    mods = [L["mod"] for L in layers]
+    all_cores = [L["cores"] for L in layers]
+    all_D = [L["D"] for L in layers]
+
     def step_overlap():
         # The merges depend only on the cores and D, the core-gradient tails
-        # produce only dG: both go to a side stream.  The main stream carries
-        # the dependent chain of streaming passes (embedding lookup, forward
-        # over the layers, dX backward through them in reverse order, then the
-        # embedding's backward).
+        # produce only dG: both go to a side stream, each as one batched call
+        # for all layers.  The main stream carries the dependent chain of
+        # streaming passes (embedding lookup, forward over the layers, dX
+        # backward through them in reverse order, then the embedding's
+        # backward).  The merges run beside the embedding lookup; the tails
+        # start after the last dX pass, beside the embedding's backward, so no
+        # side-stream work sits between two streaming passes.
         main = torch.cuda.current_stream()
         side.wait_stream(main)
-        ttm_fwd()
-        ready = []
         with torch.cuda.stream(side):
-            for L in layers:
-                L["mod"].prepare(T, L["cores"], L["D"], saved=L["saved"])
-                e = torch.cuda.Event()
-                e.record(side)
-                ready.append(e)
-        for L, e in zip(layers, ready):
-            main.wait_event(e)
+            ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
+        ttm_fwd()
+        main.wait_stream(side)
+        for L in layers:
             L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"], prepared=True)
         for L in reversed(layers):
-            L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
-                              scratch=L["scratch"], grad_stream=side)
+            L["mod"].backward_data(L["x"], L["dy"], L["cores"], L["D"], L["saved"], L["scratch"], dx=L["dx"])
+        side.wait_stream(main)
         ttm_bwd()
+        with torch.cuda.stream(side):
+            ttc.backward_cores_batch(mods[::-1], T, all_cores[::-1], all_D[::-1],
+                                     [L["saved"] for L in layers][::-1], [L["scratch"] for L in layers][::-1],
+                                     [L["dG"] for L in layers][::-1])
         main.wait_stream(side)
 
     step = step_single if args.single_stream else step_overlap
@@ -308,44 +314,24 @@ def main():
     ttc.trace_stop()
     recs = ttc.trace_records()
     per = {}
-    # launch order of one step: per layer merge, fwd; then per layer (reversed)
-    # bwd_dy, bwd_dx, reduce, core_step x n
-    expect = []
-    nlev = 0 if ttm is None else ttm["d"] - 1
-    ttm_f = [] if ttm is None else ([("ttm_sort", "ttm"), ("ttm_lists", "ttm")] + [("ttm_level", "ttm")] * nlev
-                                    + [("ttm_gather", "ttm")])
-    ttm_b = [] if ttm is None else [("ttm_seg", "ttm")] + [("ttm_bwd_level", "ttm")] * nlev + [("ttm_reduce", "ttm")]
-    expect += ttm_f
-    def merge_launches(li):
-        # one GEMM launch per level of the longer half, then the packing launch
-        s = layers[li]["spec"]
-        split = len(s.in_modes) if s.in_first else len(s.out_modes)
-        d = len(s.in_modes) + len(s.out_modes)
-        return [("merge_level", li)] * max(split - 1, d - 1 - split) + [("merge", li)]
-
-    if args.single_stream:
-        for li in range(len(layers)):
-            expect += merge_launches(li) + [("fwd", li)]
-    else:
-        for li in range(len(layers)):
-            expect += merge_launches(li)
-        expect += [("fwd", li) for li in range(len(layers))]
-    for li in reversed(range(len(layers))):
-        s = layers[li]["spec"]
-        plan = dict(kv.split("=") for kv in ttc.tt_linear_explain(layers[li]["mod"].desc, T).split())
-        ndy = int(plan["dy_grid"].split("x")[0])
-        halves = [len(s.out_modes), len(s.in_modes)]
-        expect += [("bwd_dy", li)] + ([("dz_sum", li)] if ndy > 1 else []) + [("bwd_dx", li), ("reduce", li)]
-        expect += [("core", li)] * (max(halves) - 1)
-    expect += ttm_b
-    assert len(recs) == len(expect) * args.steps, (len(recs), len(expect))
-    for i, (name, ms) in enumerate(recs):
-        ename, li = expect[i % len(expect)]
-        assert name == ename, (i, name, ename)
+    # layer of the k-th launch of a streaming kernel within one step: the
+    # forward runs over the layers in order, the backward passes in reverse
+    nl = len(layers)
+    layer_of = {"fwd": list(range(nl)), "bwd_dy": list(range(nl))[::-1], "bwd_dx": list(range(nl))[::-1]}
+    ttm_names = {"ttm_sort", "ttm_lists", "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level", "ttm_reduce"}
+    counts = {}
+    for name, ms in recs:
         d = per.setdefault(name, {"ms": 0.0, "bytes": 0.0, "launches": 0})
         d["ms"] += ms
+        k = counts.get(name, 0)
+        counts[name] = k + 1
         d["launches"] += 1
-        d["bytes"] += (ttm_sizes if li == "ttm" else sizes[li]).get(name, 0)
+        if name in layer_of:
+            d["bytes"] += sizes[layer_of[name][k % nl]].get(name, 0)
+        elif name in ttm_names:
+            d["bytes"] += ttm_sizes.get(name, 0)
+    for name in layer_of:
+        assert counts.get(name, 0) == nl * args.steps, (name, counts.get(name))
     for d in per.values():
         d["avg_us"] = 1e3 * d["ms"] / d["launches"]
         d["gbps"] = d["bytes"] / (d["ms"] / 1e3) / 1e9 if d["bytes"] else None

@@ -173,6 +173,68 @@ ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
                                ttc_stream_t grad_stream);
 
 /*
+ * The backward in two calls, for callers that schedule the core-gradient
+ * work themselves (e.g. the tails of many layers together, after every
+ * layer's dX is done).  The split follows the merged contraction order of the
+ * project page (section "Making small tensor operations fast on GPUs"): the
+ * passes over the T-sized activations, then the T-independent sweep back
+ * through the two half products of the chain.
+ *
+ * tt_linear_bwd_data: the passes over dY and x on `stream`.  Writes dX
+ *   (skipped when dx == NULL) and leaves the partial sums of the half-product
+ *   gradients in `scratch`.  Arguments as for tt_linear_bwd.
+ * tt_linear_bwd_cores: reduces those partial sums and sweeps back through
+ *   the chain on `stream`; writes dG (fp32, shapes of the cores, overwritten).
+ *   It must run after the tt_linear_bwd_data call with the same desc, T,
+ *   saved and scratch has completed on the device (same stream, or an event);
+ *   scratch must not be reused in between.  x and dy are not read.
+ * Results are bitwise identical to tt_linear_bwd.  T == 0: bwd_data does
+ * nothing, bwd_cores zeroes dG.  Errors are returned before any launch.
+ */
+ttc_status tt_linear_bwd_data(const tt_linear_desc* desc, int64_t T,
+                              const void* x, const void* dy,
+                              const float* const* G, const float* const* D,
+                              const void* saved, size_t saved_bytes, void* dx,
+                              void* scratch, size_t scratch_bytes,
+                              ttc_stream_t stream);
+ttc_status tt_linear_bwd_cores(const tt_linear_desc* desc, int64_t T,
+                               const float* const* G, const float* const* D,
+                               const void* saved, size_t saved_bytes,
+                               float* const* dG, void* scratch,
+                               size_t scratch_bytes, ttc_stream_t stream);
+
+/*
+ * Batched forms of tt_linear_prepare and tt_linear_bwd_cores for n layers
+ * (arrays of n entries, entry i exactly the arguments of the single-layer
+ * call).  Every layer's merge level (or sweep level) goes into one launch
+ * with the other layers', so n layers cost about as many launches as one;
+ * these T-independent steps are small and bound by launch latency.  Results
+ * are bitwise those of the single-layer calls.  All arguments of all layers
+ * are checked before anything is launched; n == 0 does nothing; n < 0 gives
+ * TTC_ERR_SHAPE.  The layers must not share saved or scratch buffers.
+ *   descs[i]  - descriptor of layer i
+ *   T[i]      - tokens of layer i (sizes its buffers)
+ *   G[i], D[i] - host arrays of layer i's core / diagonal device pointers
+ *   dG[i]     - host array of layer i's core-gradient device pointers
+ */
+ttc_status tt_linear_prepare_batch(int32_t n, const tt_linear_desc* const* descs,
+                                   const int64_t* T,
+                                   const float* const* const* G,
+                                   const float* const* const* D,
+                                   void* const* saved, const size_t* saved_bytes,
+                                   ttc_stream_t stream);
+ttc_status tt_linear_bwd_cores_batch(int32_t n, const tt_linear_desc* const* descs,
+                                     const int64_t* T,
+                                     const float* const* const* G,
+                                     const float* const* const* D,
+                                     const void* const* saved,
+                                     const size_t* saved_bytes,
+                                     float* const* const* dG,
+                                     void* const* scratch,
+                                     const size_t* scratch_bytes,
+                                     ttc_stream_t stream);
+
+/*
  * Planner report (host-only): writes a NUL-terminated text into buf (at most
  * n bytes) with the chosen path and the modelled flops / bytes of the merged,
  * sequential and dense paths for T tokens.

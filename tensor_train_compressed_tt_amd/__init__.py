@@ -41,6 +41,10 @@ EXPORTS = [
     "tt_linear_explain",
     "tt_linear_prepare",
     "tt_linear_bwd_split",
+    "tt_linear_bwd_data",
+    "tt_linear_bwd_cores",
+    "tt_linear_prepare_batch",
+    "tt_linear_bwd_cores_batch",
     "tt_linear_path_cost",
     "ttm_embed_workspace",
     "ttm_embed_fwd",
@@ -109,7 +113,14 @@ def lib() -> ctypes.CDLL:
         "tt_linear_fwd": [D, _I64, _P, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
         "tt_linear_bwd": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P],
         "tt_linear_bwd_split": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P, _P],
+        "tt_linear_bwd_data": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, _P, _SZ, _P],
+        "tt_linear_bwd_cores": [D, _I64, pp, pp, _P, _SZ, pp, _P, _SZ, _P],
         "tt_linear_prepare": [D, _I64, pp, pp, _P, _SZ, _P],
+        "tt_linear_prepare_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), ctypes.POINTER(pp),
+                                    ctypes.POINTER(pp), pp, ctypes.POINTER(_SZ), _P],
+        "tt_linear_bwd_cores_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), ctypes.POINTER(pp),
+                                      ctypes.POINTER(pp), pp, ctypes.POINTER(_SZ), ctypes.POINTER(pp), pp,
+                                      ctypes.POINTER(_SZ), _P],
         "tt_linear_explain": [D, _I64, ctypes.c_char_p, _SZ],
         "tt_linear_path_cost": [D, _I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                 ctypes.POINTER(ctypes.c_double)],
@@ -211,10 +222,68 @@ def tt_linear_bwd_split(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, scratc
     _check("tt_linear_bwd_split", code)
 
 
+def tt_linear_bwd_data(desc, T, x, dy, G, D, saved, saved_bytes, dx, scratch, scratch_bytes, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    code = lib().tt_linear_bwd_data(ctypes.byref(desc), T, x, dy, g, dd, saved, saved_bytes, dx, scratch,
+                                    scratch_bytes, stream)
+    _check("tt_linear_bwd_data", code)
+
+
+def tt_linear_bwd_cores(desc, T, G, D, saved, saved_bytes, dG, scratch, scratch_bytes, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    dg, _dga = _ptrs(dG)
+    code = lib().tt_linear_bwd_cores(ctypes.byref(desc), T, g, dd, saved, saved_bytes, dg, scratch, scratch_bytes,
+                                     stream)
+    _check("tt_linear_bwd_cores", code)
+
+
 def tt_linear_prepare(desc, T, G, D, saved, saved_bytes, stream=0):
     g, _ga = _ptrs(G)
     dd, _da = _ptrs(D) if D is not None else (None, None)
     _check("tt_linear_prepare", lib().tt_linear_prepare(ctypes.byref(desc), T, g, dd, saved, saved_bytes, stream))
+
+
+def _batch_args(descs, T, lists):
+    """ctypes arrays for a batched call: descriptor pointers, token counts and,
+    per entry of `lists`, a host array of n host arrays of device pointers.
+    Returns the arrays and a list that keeps every ctypes object alive."""
+    n = len(descs)
+    keep = []
+    dp = (ctypes.POINTER(TTLinearDesc) * max(1, n))(*[ctypes.pointer(d) for d in descs])
+    ta = (_I64 * max(1, n))(*[int(t) for t in T])
+    outs = []
+    for lst in lists:
+        inner = [_ptrs(x) for x in lst]
+        keep.append(inner)
+        outs.append((ctypes.POINTER(ctypes.c_void_p) * max(1, n))(*[p for p, _ in inner]))
+    keep += [dp, ta, outs]
+    return dp, ta, outs, keep
+
+
+def _addr_array(addrs):
+    return (ctypes.c_void_p * max(1, len(addrs)))(*[ctypes.c_void_p(None if a is None else int(a)) for a in addrs])
+
+
+def tt_linear_prepare_batch(descs, T, G, D, saved, saved_bytes, stream=0):
+    dp, ta, (ga, da), _keep = _batch_args(descs, T, [G, D])
+    sv = _addr_array(saved)
+    sb = (_SZ * max(1, len(descs)))(*saved_bytes)
+    code = lib().tt_linear_prepare_batch(len(descs), dp, ta, ga, da, ctypes.cast(sv, ctypes.POINTER(ctypes.c_void_p)),
+                                         sb, stream)
+    _check("tt_linear_prepare_batch", code)
+
+
+def tt_linear_bwd_cores_batch(descs, T, G, D, saved, saved_bytes, dG, scratch, scratch_bytes, stream=0):
+    dp, ta, (ga, da, gg), _keep = _batch_args(descs, T, [G, D, dG])
+    sv = _addr_array(saved)
+    sc = _addr_array(scratch)
+    n = max(1, len(descs))
+    code = lib().tt_linear_bwd_cores_batch(len(descs), dp, ta, ga, da, ctypes.cast(sv, ctypes.POINTER(ctypes.c_void_p)),
+                                           (_SZ * n)(*saved_bytes), gg, ctypes.cast(sc, ctypes.POINTER(ctypes.c_void_p)),
+                                           (_SZ * n)(*scratch_bytes), stream)
+    _check("tt_linear_bwd_cores_batch", code)
 
 
 def tt_linear_explain(desc: TTLinearDesc, T: int) -> str:
@@ -278,4 +347,4 @@ def version() -> str:
     return lib().ttc_version().decode()
 
 
-from .torch_api import TTLinear, TTMEmbedding  # noqa: E402,F401
+from .torch_api import TTLinear, TTMEmbedding, backward_cores_batch, prepare_batch  # noqa: E402,F401

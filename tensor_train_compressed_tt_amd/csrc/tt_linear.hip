@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "tt_plan.hpp"
 #include "ttc_device.hpp"
@@ -82,13 +83,25 @@ struct PackArgs {
   void* BcT;
 };
 
+// Layers packed by one launch; work-group i belongs to the layer q with
+// first[q] <= i < first[q + 1].
+constexpr int kMaxBatch = 8;
+struct PackBatch {
+  PackArgs p[kMaxBatch];
+  int64_t first[kMaxBatch + 1];
+  int n;
+};
+
 // One wave per row of L (items [0, NL)) or column of R (the rest).
 template <typename T>
-__global__ __launch_bounds__(64) void k_pack(PackArgs a) {
+__global__ __launch_bounds__(64) void k_pack(PackBatch pb) {
   typedef typename Elem<T>::type E;
   __shared__ int live[TTC_MAX_RANK];
   const int lane = threadIdx.x;
-  const int64_t item = blockIdx.x;
+  int q = 0;
+  while (q < pb.n - 1 && (int64_t)blockIdx.x >= pb.first[q + 1]) ++q;
+  const PackArgs& a = pb.p[q];
+  const int64_t item = (int64_t)blockIdx.x - pb.first[q];
   // live entries of the split link's diagonal, in increasing link index
   const bool f0 = lane < a.rs && a.Ds[lane] != 0.0f;
   const bool f1 = lane + 64 < a.rs && a.Ds[lane + 64] != 0.0f;
@@ -1019,57 +1032,94 @@ struct ReduceArgs {
   int rs, Rpad, in_first;
 };
 
-// Each thread sums four consecutive columns of one rank row over all token
-// groups (float4 loads when aligned) and scatters them into the layout of the
-// half product's gradient.
-__global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
-  const int64_t qB = (a.N_out + 3) / 4, qA = (a.N_in + 3) / 4;
-  const int64_t nB = (int64_t)a.rs * qB, nA = (int64_t)a.rs * qA;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nB + nA;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const bool isB = idx < nB;
-    const int64_t id = isB ? idx : idx - nB;
-    const int64_t N = isB ? a.N_out : a.N_in;
-    const int64_t nq = isB ? qB : qA;
-    const int b = (int)(id / nq);
-    const int64_t r0 = (id % nq) * 4;
-    const int j = a.meta[kMetaPos + b];
-    const float* src = isB ? a.dBp : a.dAp;
-    const int gtn = isB ? a.gtB : a.gtA;
-    f32x4 acc = zero4();
-    if (j >= 0) {
-      if ((N & 3) == 0) {
-        f32x4 acc1 = zero4();
-        int q = 0;
-        for (; q + 16 <= gtn; q += 16) {
-          f32x4 v[16];
+// Layers reduced by one launch.  A work-group owns 64 consecutive 4-column
+// groups of one rank row of one side (B or A) of one layer; its four waves
+// sum contiguous quarters of the token groups (float4 loads, eight in flight)
+// and the quarters are added in wave order through LDS, so the order of every
+// sum is fixed.  The result is scattered into the layout of the half
+// product's gradient.
+struct ReduceBatch {
+  ReduceArgs r[kMaxBatch];
+  int64_t first[kMaxBatch + 1];  // first work-group of each layer
+  int n;
+};
+
+static_assert(sizeof(ReduceBatch) <= 2048, "ReduceBatch too large for a kernel argument");
+
+__device__ __forceinline__ int64_t reduce_strips(int64_t N) { return ((N + 3) / 4 + 63) / 64; }
+
+__global__ __launch_bounds__(256) void k_reduce(ReduceBatch rb) {
+  __shared__ f32x4 part[3][64];
+  int q = 0;
+  while (q < rb.n - 1 && (int64_t)blockIdx.x >= rb.first[q + 1]) ++q;
+  const ReduceArgs& a = rb.r[q];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int64_t item = (int64_t)blockIdx.x - rb.first[q];
+  const int64_t sB = reduce_strips(a.N_out), sA = reduce_strips(a.N_in);
+  const bool isB = item < (int64_t)a.rs * sB;
+  if (!isB) item -= (int64_t)a.rs * sB;
+  const int64_t ns = isB ? sB : sA;
+  const int b = (int)(item / ns);
+  const int64_t N = isB ? a.N_out : a.N_in;
+  const int64_t r0 = ((item % ns) * 64 + lane) * 4;
+  const int j = a.meta[kMetaPos + b];
+  const float* src = isB ? a.dBp : a.dAp;
+  const int gtn = isB ? a.gtB : a.gtA;
+  const int per = (gtn + 3) / 4;
+  const int qb = min(gtn, w * per), qe = min(gtn, qb + per);
+  f32x4 acc = zero4();
+  if (j >= 0 && r0 < N) {
+    const float* col = src + (int64_t)j * N + r0;
+    const int64_t qstride = (int64_t)a.Rpad * N;
+    if ((N & 3) == 0) {
+      f32x4 acc1 = zero4();
+      int qq = qb;
+      for (; qq + 8 <= qe; qq += 8) {
+        f32x4 v[8];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + ((int64_t)(q + u) * a.Rpad + j) * N + r0);
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(col + (int64_t)(qq + u) * qstride);
 #pragma unroll
-          for (int u = 0; u < 16; u += 2) {
-            acc += v[u];
-            acc1 += v[u + 1];
-          }
+        for (int u = 0; u < 8; u += 2) {
+          acc += v[u];
+          acc1 += v[u + 1];
         }
-        for (; q < gtn; ++q) acc += *reinterpret_cast<const f32x4*>(src + ((int64_t)q * a.Rpad + j) * N + r0);
-        acc += acc1;
-      } else {
-        for (int q = 0; q < gtn; ++q)
-          for (int e = 0; e < 4; ++e)
-            if (r0 + e < N) acc[e] += src[((int64_t)q * a.Rpad + j) * N + r0 + e];
       }
-      if (!isB) acc *= a.Ds[b];
+      for (; qq < qe; ++qq) acc += *reinterpret_cast<const f32x4*>(col + (int64_t)qq * qstride);
+      acc += acc1;
+    } else {
+      for (int qq = qb; qq < qe; ++qq)
+        for (int e = 0; e < 4; ++e)
+          if (r0 + e < N) acc[e] += col[(int64_t)qq * qstride + e];
     }
-    // B side feeds L (out first) or R (in first); A side the other one
-    const bool toL = isB != (a.in_first != 0);
+  }
+  if (w > 0) part[w - 1][lane] = acc;
+  __syncthreads();
+  if (w != 0 || j < 0 || r0 >= N) {
+    // dead slice: its gradient rows / columns are exactly zero
+    if (w == 0 && r0 < N) {
+      const bool toL = isB != (a.in_first != 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (r0 + e < N) {
-        if (toL)
-          a.dL[(r0 + e) * a.rs + b] = acc[e];
-        else
-          a.dR[(int64_t)b * N + r0 + e] = acc[e];
-      }
+      for (int e = 0; e < 4; ++e)
+        if (r0 + e < N) {
+          if (toL)
+            a.dL[(r0 + e) * a.rs + b] = 0.f;
+          else
+            a.dR[(int64_t)b * N + r0 + e] = 0.f;
+        }
+    }
+    return;
+  }
+  acc = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
+  if (!isB) acc *= a.Ds[b];
+  // B side feeds L (out first) or R (in first); A side the other one
+  const bool toL = isB != (a.in_first != 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (r0 + e < N) {
+      if (toL)
+        a.dL[(r0 + e) * a.rs + b] = acc[e];
+      else
+        a.dR[(int64_t)b * N + r0 + e] = acc[e];
     }
   }
 }
@@ -1189,14 +1239,19 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
   }
 }
 
-// One level of the reverse sweep: up to four independent GEMMs (per half, the
-// core gradient and the gradient passed on to the next core), one 32 x 32
-// tile per work-group.
+// One level of the reverse sweep (or of the merge) for one or more layers:
+// up to kMaxGemm independent GEMMs (per half and layer, the core gradient and
+// the gradient passed on to the next core), one 32 x 32 tile per work-group.
+constexpr int kMaxGemm = 16;
 struct SweepArgs {
-  Gemm g[4];
-  int tiles[4];
+  Gemm g[kMaxGemm];
+  int tiles[kMaxGemm];
   int ng;
 };
+
+// kernel arguments stay well inside the 4 KB argument segment
+static_assert(sizeof(SweepArgs) <= 2048, "SweepArgs too large for a kernel argument");
+static_assert(sizeof(PackBatch) <= 2048, "PackBatch too large for a kernel argument");
 
 // KS: the GEMMs scale A's columns by ks_ (the merge levels); the sweep's
 // GEMMs do not, and keep the register budget of the plain tile
@@ -1502,71 +1557,101 @@ extern "C" ttc_status tt_linear_workspace(const tt_linear_desc* desc, int64_t T,
 }
 
 namespace ttc {
-static void launch_merge(const LinearPlan& P, const float* const* G, const float* const* D, char* sv, hipStream_t s) {
-  float* chain = reinterpret_cast<float*>(sv + P.sv_chain);
-  float* Lf = reinterpret_cast<float*>(sv + P.sv_Lf);
-  float* Rf = reinterpret_cast<float*>(sv + P.sv_Rf);
-  const int d = P.d, S = P.s;
-  const int nlev = std::max(S - 1, d - 1 - S);
-  for (int lvl = 0; lvl < nlev; ++lvl) {
+// One layer of a batched merge or core-gradient launch.
+struct LayerJob {
+  LinearPlan P;
+  ChainPtrs c;
+  char* sv;
+  char* sc;
+  float* dG[kMaxCores];
+};
+
+// Independent GEMMs in launches of at most kMaxGemm.
+template <bool KS>
+static void launch_gemm_list(const Gemm* gs, int n, const char* name, hipStream_t s) {
+  for (int i = 0; i < n; i += kMaxGemm) {
     SweepArgs a;
     memset(&a, 0, sizeof(a));
     int total = 0;
-    auto add = [&](const Gemm& g) {
-      a.g[a.ng] = g;
-      a.tiles[a.ng] = gemm_tiles(g);
-      total += a.tiles[a.ng];
+    for (int q = 0; q < std::min(kMaxGemm, n - i); ++q) {
+      a.g[q] = gs[i + q];
+      a.tiles[q] = gemm_tiles(gs[i + q]);
+      total += a.tiles[q];
       ++a.ng;
-    };
-    const int kL = 1 + lvl;  // left: M_kL = (M_{kL-1} D_{kL-1}) G_kL
-    if (kL <= S - 1) {
-      int64_t rows = 1;
-      for (int t = 0; t < kL; ++t) rows *= P.modes[t];
-      Gemm g;
-      memset(&g, 0, sizeof(g));
-      g.A = kL == 1 ? G[0] : chain + P.chain_off[kL - 1];
-      g.sAi = P.ranks[kL];
-      g.sAk = 1;
-      g.ks_ = D[kL - 1];
-      g.B = G[kL];
-      g.sBk = (int64_t)P.modes[kL] * P.ranks[kL + 1];
-      g.sBj = 1;
-      g.C = kL == S - 1 ? Lf : chain + P.chain_off[kL];
-      g.sCi = (int64_t)P.modes[kL] * P.ranks[kL + 1];
-      g.sCj = 1;
-      g.M = (int)rows;
-      g.N = P.modes[kL] * P.ranks[kL + 1];
-      g.K = P.ranks[kL];
-      add(g);
     }
-    const int kR = d - 2 - lvl;  // right: N_kR = G_kR D_kR N_{kR+1}
-    if (kR >= S) {
-      int64_t cols = 1;
-      for (int t = kR + 1; t < d; ++t) cols *= P.modes[t];
-      Gemm g;
-      memset(&g, 0, sizeof(g));
-      g.A = G[kR];
-      g.sAi = P.ranks[kR + 1];
-      g.sAk = 1;
-      g.ks_ = D[kR];
-      g.B = kR + 1 == d - 1 ? G[d - 1] : chain + P.chain_off[kR + 1];
-      g.sBk = cols;
-      g.sBj = 1;
-      g.C = kR == S ? Rf : chain + P.chain_off[kR];
-      g.sCi = cols;
-      g.sCj = 1;
-      g.M = P.ranks[kR] * P.modes[kR];
-      g.N = (int)cols;
-      g.K = P.ranks[kR + 1];
-      add(g);
-    }
-    TraceScope ts("merge_level", s);
-    TTC_LAUNCH(k_sweep<true>, dim3(total), dim3(256), 0, s, a);
+    TraceScope ts(name, s);
+    TTC_LAUNCH(k_sweep<KS>, dim3(total), dim3(256), 0, s, a);
   }
+}
+
+static int merge_levels(const LinearPlan& P) { return std::max(P.s - 1, P.d - 1 - P.s); }
+
+// The GEMMs of merge level `lvl` of one layer (at most two: one per half).
+static int merge_gemms(const LayerJob& j, int lvl, Gemm* out) {
+  const LinearPlan& P = j.P;
+  const float* const* G = j.c.G;
+  const float* const* D = j.c.D;
+  float* chain = reinterpret_cast<float*>(j.sv + P.sv_chain);
+  float* Lf = reinterpret_cast<float*>(j.sv + P.sv_Lf);
+  float* Rf = reinterpret_cast<float*>(j.sv + P.sv_Rf);
+  const int d = P.d, S = P.s;
+  int ng = 0;
+  const int kL = 1 + lvl;  // left: M_kL = (M_{kL-1} D_{kL-1}) G_kL
+  if (kL <= S - 1) {
+    int64_t rows = 1;
+    for (int t = 0; t < kL; ++t) rows *= P.modes[t];
+    Gemm g;
+    memset(&g, 0, sizeof(g));
+    g.A = kL == 1 ? G[0] : chain + P.chain_off[kL - 1];
+    g.sAi = P.ranks[kL];
+    g.sAk = 1;
+    g.ks_ = D[kL - 1];
+    g.B = G[kL];
+    g.sBk = (int64_t)P.modes[kL] * P.ranks[kL + 1];
+    g.sBj = 1;
+    g.C = kL == S - 1 ? Lf : chain + P.chain_off[kL];
+    g.sCi = (int64_t)P.modes[kL] * P.ranks[kL + 1];
+    g.sCj = 1;
+    g.M = (int)rows;
+    g.N = P.modes[kL] * P.ranks[kL + 1];
+    g.K = P.ranks[kL];
+    out[ng++] = g;
+  }
+  const int kR = d - 2 - lvl;  // right: N_kR = G_kR D_kR N_{kR+1}
+  if (kR >= S) {
+    int64_t cols = 1;
+    for (int t = kR + 1; t < d; ++t) cols *= P.modes[t];
+    Gemm g;
+    memset(&g, 0, sizeof(g));
+    g.A = G[kR];
+    g.sAi = P.ranks[kR + 1];
+    g.sAk = 1;
+    g.ks_ = D[kR];
+    g.B = kR + 1 == d - 1 ? G[d - 1] : chain + P.chain_off[kR + 1];
+    g.sBk = cols;
+    g.sBj = 1;
+    g.C = kR == S ? Rf : chain + P.chain_off[kR];
+    g.sCi = cols;
+    g.sCj = 1;
+    g.M = P.ranks[kR] * P.modes[kR];
+    g.N = (int)cols;
+    g.K = P.ranks[kR + 1];
+    out[ng++] = g;
+  }
+  return ng;
+}
+
+static PackArgs pack_args(const LayerJob& j) {
+  const LinearPlan& P = j.P;
+  const float* const* G = j.c.G;
+  const float* const* D = j.c.D;
+  char* sv = j.sv;
+  float* chain = reinterpret_cast<float*>(sv + P.sv_chain);
+  const int d = P.d, S = P.s;
   PackArgs m;
   memset(&m, 0, sizeof(m));
-  m.L = S == 1 ? G[0] : Lf;
-  m.R = d - S == 1 ? G[d - 1] : Rf;
+  m.L = S == 1 ? G[0] : reinterpret_cast<float*>(sv + P.sv_Lf);
+  m.R = d - S == 1 ? G[d - 1] : reinterpret_cast<float*>(sv + P.sv_Rf);
   m.Ds = D[S - 1];
   m.G0 = G[0];
   m.Gl = G[d - 1];
@@ -1586,11 +1671,54 @@ static void launch_merge(const LinearPlan& P, const float* const* G, const float
   m.AcT = sv + P.sv_AcT;
   m.Bc = sv + P.sv_Bc;
   m.BcT = sv + P.sv_BcT;
-  TraceScope ts("merge", s);
-  if (P.act == TTC_BF16)
-    TTC_LAUNCH(k_pack<bf16_t>, dim3((unsigned)(P.NL + P.NRt)), dim3(64), 0, s, m);
-  else
-    TTC_LAUNCH(k_pack<float>, dim3((unsigned)(P.NL + P.NRt)), dim3(64), 0, s, m);
+  return m;
+}
+
+// Merge of n layers: one launch per level for all of them, then the packing
+// launches (one per activation dtype and kMaxBatch layers).
+static void launch_merge_batch(const LayerJob* jobs, int n, hipStream_t s) {
+  int nlev = 0;
+  for (int i = 0; i < n; ++i) nlev = std::max(nlev, merge_levels(jobs[i].P));
+  std::vector<Gemm> gs;
+  for (int lvl = 0; lvl < nlev; ++lvl) {
+    gs.clear();
+    for (int i = 0; i < n; ++i) {
+      Gemm g[2];
+      const int k = lvl < merge_levels(jobs[i].P) ? merge_gemms(jobs[i], lvl, g) : 0;
+      for (int q = 0; q < k; ++q) gs.push_back(g[q]);
+    }
+    launch_gemm_list<true>(gs.data(), (int)gs.size(), "merge_level", s);
+  }
+  for (int act = 0; act < 2; ++act) {
+    const int want = act == 0 ? TTC_BF16 : TTC_F32;
+    PackBatch pb;
+    memset(&pb, 0, sizeof(pb));
+    auto flush = [&]() {
+      if (pb.n == 0) return;
+      TraceScope ts("merge", s);
+      if (want == TTC_BF16)
+        TTC_LAUNCH(k_pack<bf16_t>, dim3((unsigned)pb.first[pb.n]), dim3(64), 0, s, pb);
+      else
+        TTC_LAUNCH(k_pack<float>, dim3((unsigned)pb.first[pb.n]), dim3(64), 0, s, pb);
+      memset(&pb, 0, sizeof(pb));
+    };
+    for (int i = 0; i < n; ++i) {
+      if (jobs[i].P.act != want) continue;
+      pb.p[pb.n] = pack_args(jobs[i]);
+      pb.first[pb.n + 1] = pb.first[pb.n] + jobs[i].P.NL + jobs[i].P.NRt;
+      if (++pb.n == kMaxBatch) flush();
+    }
+    flush();
+  }
+}
+
+static void launch_merge(const LinearPlan& P, const float* const* G, const float* const* D, char* sv, hipStream_t s) {
+  LayerJob j;
+  memset(&j, 0, sizeof(j));
+  j.P = P;
+  j.c = chain_ptrs(P, G, D);
+  j.sv = sv;
+  launch_merge_batch(&j, 1, s);
 }
 
 // one event orders the two streams of a split backward; a wait captures the
@@ -1643,6 +1771,134 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   return hip_status();
 }
 
+namespace ttc {
+// Partial sums left in scratch by the streaming passes -> gradients of the two
+// half products (a half made of one core receives its gradient directly) ->
+// reverse sweep through both halves; for n layers, the reductions in launches
+// of kMaxBatch layers and one launch per sweep level for all of them.
+static void launch_cores_batch(const LayerJob* jobs, int n, hipStream_t s) {
+  struct Walk {
+    const float* curL;
+    const float* curR;
+    int64_t rowsL, colsR;
+  };
+  std::vector<Walk> wk(n);
+  ReduceBatch rb;
+  memset(&rb, 0, sizeof(rb));
+  auto flush = [&]() {
+    if (rb.n == 0) return;
+    TraceScope ts("reduce", s);
+    TTC_LAUNCH(k_reduce, dim3((unsigned)rb.first[rb.n]), dim3(256), 0, s, rb);
+    memset(&rb, 0, sizeof(rb));
+  };
+  for (int i = 0; i < n; ++i) {
+    const LinearPlan& P = jobs[i].P;
+    const char* sv = jobs[i].sv;
+    char* sc = jobs[i].sc;
+    float* const* dG = jobs[i].dG;
+    float* dL = P.s == 1 ? dG[0] : (float*)(sc + P.sc_dL);
+    float* dR = P.d - P.s == 1 ? dG[P.d - 1] : (float*)(sc + P.sc_dR);
+    ReduceArgs& r = rb.r[rb.n];
+    r.dBp = (const float*)(sc + P.sc_dBp);
+    r.dAp = (const float*)(sc + P.sc_dAp);
+    r.gtB = P.dy_gt;
+    r.gtA = P.dx_gt;
+    r.meta = (const int*)(sv + P.sv_meta);
+    r.Ds = jobs[i].c.D[P.s - 1];
+    r.dL = dL;
+    r.dR = dR;
+    r.N_out = P.N_out;
+    r.N_in = P.N_in;
+    r.rs = P.rs;
+    r.Rpad = P.Rpad;
+    r.in_first = P.in_first;
+    rb.first[rb.n + 1] =
+        rb.first[rb.n] + (int64_t)P.rs * (((P.N_out + 3) / 4 + 63) / 64 + ((P.N_in + 3) / 4 + 63) / 64);
+    if (++rb.n == kMaxBatch) flush();
+    wk[i] = Walk{dL, dR, P.NL, P.NRt};
+  }
+  flush();
+  std::vector<Gemm> gs;
+  for (int lvl = 0;; ++lvl) {
+    gs.clear();
+    for (int i = 0; i < n; ++i) {
+      const LinearPlan& P = jobs[i].P;
+      const float* const* G = jobs[i].c.G;
+      const float* const* D = jobs[i].c.D;
+      float* const* dG = jobs[i].dG;
+      char* sc = jobs[i].sc;
+      const float* chain = reinterpret_cast<const float*>(jobs[i].sv + P.sv_chain);
+      float* wL = (float*)(sc + ((lvl & 1) ? P.sc_w1 : P.sc_w0));
+      float* wR = wL + P.wl_floats;
+      const int kL = P.s - 1 - lvl, kR = P.s + lvl;
+      const bool hasL = kL >= 1, hasR = kR <= P.d - 2;
+      Walk& w = wk[i];
+      if (hasL) {
+        float* outL = kL - 1 == 0 ? dG[0] : wL;
+        gs.push_back(left_dG(P, chain, D, dG[kL], kL, w.curL, w.rowsL));
+        gs.push_back(left_dM(P, G, D, kL, w.curL, w.rowsL, outL));
+        w.curL = outL;
+        w.rowsL /= P.modes[kL];
+      }
+      if (hasR) {
+        float* outR = kR + 1 == P.d - 1 ? dG[P.d - 1] : wR;
+        gs.push_back(right_dG(P, chain, D, dG[kR], kR, w.curR, w.colsR));
+        gs.push_back(right_dN(P, G, D, kR, w.curR, w.colsR, outR));
+        w.curR = outR;
+        w.colsR /= P.modes[kR];
+      }
+    }
+    if (gs.empty()) break;
+    launch_gemm_list<false>(gs.data(), (int)gs.size(), "core", s);
+  }
+}
+
+static void launch_bwd_cores(const LinearPlan& P, const float* const* G, const float* const* D, const char* sv,
+                             char* sc, float* const* dG, hipStream_t s) {
+  LayerJob j;
+  memset(&j, 0, sizeof(j));
+  j.P = P;
+  j.c = chain_ptrs(P, G, D);
+  j.sv = const_cast<char*>(sv);
+  j.sc = sc;
+  for (int k = 0; k < P.d; ++k) j.dG[k] = dG[k];
+  launch_cores_batch(&j, 1, s);
+}
+
+static void launch_zero_grads(const LinearPlan& P, float* const* dG, hipStream_t s) {
+  for (int k = 0; k < P.d; ++k) {
+    const int64_t n = (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
+    TraceScope ts("zero", s);
+    TTC_LAUNCH(k_zero, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, dG[k], n);
+  }
+}
+
+// argument checks shared by the backward entry points; *P is the plan
+static ttc_status bwd_checks(const tt_linear_desc* desc, int64_t T, const float* const* G, const float* const* D,
+                             LinearPlan* P) {
+  ttc_status st = make_linear_plan(desc, T, P);
+  if (st != TTC_OK) return st;
+  return check_chain(*P, G, D);
+}
+static ttc_status grads_checks(const LinearPlan& P, float* const* dG) {
+  if (!dG) return TTC_ERR_NULL;
+  for (int k = 0; k < P.d; ++k)
+    if (!dG[k]) return TTC_ERR_NULL;
+  return TTC_OK;
+}
+// null pointers first, then alignment, then sizes; x and dy are checked
+// when `data` is set (the streaming passes read them)
+static ttc_status buffer_checks(const LinearPlan& P, bool data, const void* x, const void* dy, const void* dx,
+                                const void* saved, size_t saved_bytes, const void* scratch, size_t scratch_bytes) {
+  if ((data && (!x || !dy)) || !saved || !scratch) return TTC_ERR_NULL;
+  if ((data && (!aligned16(x) || !aligned16(dy) || (dx && !aligned16(dx)))) || !aligned16(saved) ||
+      !aligned16(scratch))
+    return TTC_ERR_ALIGN;
+  if (saved_bytes < P.sv_total || scratch_bytes < P.sc_total) return TTC_ERR_WORKSPACE;
+  return TTC_OK;
+}
+}  // namespace ttc
+
 extern "C" ttc_status tt_linear_bwd(const tt_linear_desc* desc, int64_t T, const void* x, const void* dy,
                                     const float* const* G, const float* const* D, const void* saved,
                                     size_t saved_bytes, void* dx, float* const* dG, void* scratch,
@@ -1656,27 +1912,17 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
                                           size_t saved_bytes, void* dx, float* const* dG, void* scratch,
                                           size_t scratch_bytes, ttc_stream_t stream, ttc_stream_t grad_stream) {
   LinearPlan P;
-  ttc_status st = make_linear_plan(desc, T, &P);
+  ttc_status st = bwd_checks(desc, T, G, D, &P);
   if (st != TTC_OK) return st;
-  if ((st = check_chain(P, G, D)) != TTC_OK) return st;
-  if (!dG) return TTC_ERR_NULL;
-  for (int k = 0; k < P.d; ++k)
-    if (!dG[k]) return TTC_ERR_NULL;
+  if ((st = grads_checks(P, dG)) != TTC_OK) return st;
   hipStream_t s_main = reinterpret_cast<hipStream_t>(stream);
   hipStream_t s = reinterpret_cast<hipStream_t>(grad_stream);  // the core-gradient tail
   (void)hipGetLastError();
   if (T == 0) {
-    for (int k = 0; k < P.d; ++k) {
-      const int64_t n = (int64_t)P.ranks[k] * P.modes[k] * P.ranks[k + 1];
-      TraceScope ts("zero", s);
-      TTC_LAUNCH(k_zero, dim3(grid_for(n, 256, 1024)), dim3(256), 0, s, dG[k], n);
-    }
+    launch_zero_grads(P, dG, s);
     return hip_status();
   }
-  if (!x || !dy || !saved || !scratch) return TTC_ERR_NULL;
-  if (!aligned16(x) || !aligned16(dy) || !aligned16(saved) || !aligned16(scratch) || (dx && !aligned16(dx)))
-    return TTC_ERR_ALIGN;
-  if (saved_bytes < P.sv_total || scratch_bytes < P.sc_total) return TTC_ERR_WORKSPACE;
+  if ((st = buffer_checks(P, true, x, dy, dx, saved, saved_bytes, scratch, scratch_bytes)) != TTC_OK) return st;
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
   const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s_main)
@@ -1688,71 +1934,114 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
     std::lock_guard<std::mutex> lk(g_split_mu);
     if (hipEventRecord(ev, s_main) != hipSuccess || hipStreamWaitEvent(s, ev, 0) != hipSuccess) return TTC_ERR_HIP;
   }
-  // partial sums -> gradients of the two half products; a half made of one
-  // core receives its gradient directly
-  float* dL = P.s == 1 ? dG[0] : (float*)(sc + P.sc_dL);
-  float* dR = P.d - P.s == 1 ? dG[P.d - 1] : (float*)(sc + P.sc_dR);
-  {
-    ReduceArgs r;
-    r.dBp = (const float*)(sc + P.sc_dBp);
-    r.dAp = (const float*)(sc + P.sc_dAp);
-    r.gtB = P.dy_gt;
-    r.gtA = P.dx_gt;
-    r.meta = (const int*)(sv + P.sv_meta);
-    r.Ds = D[P.s - 1];
-    r.dL = dL;
-    r.dR = dR;
-    r.N_out = P.N_out;
-    r.N_in = P.N_in;
-    r.rs = P.rs;
-    r.Rpad = P.Rpad;
-    r.in_first = P.in_first;
-    const int64_t n = (int64_t)P.rs * ((P.N_out + 3) / 4 + (P.N_in + 3) / 4);
-    TraceScope ts("reduce", s);
-    TTC_LAUNCH(k_reduce, dim3(grid_for(n, 256, 4096)), dim3(256), 0, s, r);
+  launch_bwd_cores(P, G, D, sv, sc, dG, s);
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_bwd_data(const tt_linear_desc* desc, int64_t T, const void* x, const void* dy,
+                                         const float* const* G, const float* const* D, const void* saved,
+                                         size_t saved_bytes, void* dx, void* scratch, size_t scratch_bytes,
+                                         ttc_stream_t stream) {
+  LinearPlan P;
+  ttc_status st = bwd_checks(desc, T, G, D, &P);
+  if (st != TTC_OK) return st;
+  if (T == 0) return TTC_OK;
+  if ((st = buffer_checks(P, true, x, dy, dx, saved, saved_bytes, scratch, scratch_bytes)) != TTC_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const char* sv = static_cast<const char*>(saved);
+  char* sc = static_cast<char*>(scratch);
+  const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s)
+                                    : dispatch_bwd<float>(P, x, dy, sv, dx, sc, s);
+  if (!ok) return TTC_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_bwd_cores(const tt_linear_desc* desc, int64_t T, const float* const* G,
+                                          const float* const* D, const void* saved, size_t saved_bytes,
+                                          float* const* dG, void* scratch, size_t scratch_bytes,
+                                          ttc_stream_t stream) {
+  LinearPlan P;
+  ttc_status st = bwd_checks(desc, T, G, D, &P);
+  if (st != TTC_OK) return st;
+  if ((st = grads_checks(P, dG)) != TTC_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (T == 0) {
+    launch_zero_grads(P, dG, s);
+    return hip_status();
   }
-  // reverse sweep through both halves, one launch per level
-  {
-    const float* chain = reinterpret_cast<const float*>(sv + P.sv_chain);
-    float* wL[2] = {(float*)(sc + P.sc_w0), (float*)(sc + P.sc_w1)};
-    float* wR[2] = {(float*)(sc + P.sc_w0) + P.wl_floats, (float*)(sc + P.sc_w1) + P.wl_floats};
-    const float* curL = dL;
-    const float* curR = dR;
-    int64_t rowsL = P.NL, colsR = P.NRt;
-    for (int lvl = 0;; ++lvl) {
-      const int kL = P.s - 1 - lvl, kR = P.s + lvl;
-      const bool hasL = kL >= 1, hasR = kR <= P.d - 2;
-      if (!hasL && !hasR) break;
-      SweepArgs a;
-      memset(&a, 0, sizeof(a));
-      float* outL = nullptr;
-      float* outR = nullptr;
-      if (hasL) {
-        outL = kL - 1 == 0 ? dG[0] : wL[lvl & 1];
-        a.g[a.ng++] = left_dG(P, chain, D, dG[kL], kL, curL, rowsL);
-        a.g[a.ng++] = left_dM(P, G, D, kL, curL, rowsL, outL);
-      }
-      if (hasR) {
-        outR = kR + 1 == P.d - 1 ? dG[P.d - 1] : wR[lvl & 1];
-        a.g[a.ng++] = right_dG(P, chain, D, dG[kR], kR, curR, colsR);
-        a.g[a.ng++] = right_dN(P, G, D, kR, curR, colsR, outR);
-      }
-      int total = 0;
-      for (int q = 0; q < a.ng; ++q) total += (a.tiles[q] = gemm_tiles(a.g[q]));
-      {
-        TraceScope ts("core", s);
-        TTC_LAUNCH(k_sweep<false>, dim3(total), dim3(256), 0, s, a);
-      }
-      if (hasL) {
-        curL = outL;
-        rowsL /= P.modes[kL];
-      }
-      if (hasR) {
-        curR = outR;
-        colsR /= P.modes[kR];
-      }
+  if ((st = buffer_checks(P, false, nullptr, nullptr, nullptr, saved, saved_bytes, scratch, scratch_bytes)) !=
+      TTC_OK)
+    return st;
+  launch_bwd_cores(P, G, D, static_cast<const char*>(saved), static_cast<char*>(scratch), dG, s);
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_prepare_batch(int32_t n, const tt_linear_desc* const* descs, const int64_t* T,
+                                              const float* const* const* G, const float* const* const* D,
+                                              void* const* saved, const size_t* saved_bytes, ttc_stream_t stream) {
+  if (n < 0) return TTC_ERR_SHAPE;
+  if (n == 0) return TTC_OK;
+  if (!descs || !T || !G || !D || !saved || !saved_bytes) return TTC_ERR_NULL;
+  std::vector<LayerJob> jobs(n);
+  for (int i = 0; i < n; ++i) {
+    LayerJob& j = jobs[i];
+    memset(&j, 0, sizeof(j));
+    if (!descs[i]) return TTC_ERR_NULL;
+    ttc_status st = make_linear_plan(descs[i], T[i], &j.P);
+    if (st != TTC_OK) return st;
+    if ((st = check_chain(j.P, G[i], D[i])) != TTC_OK) return st;
+    if (!saved[i]) return TTC_ERR_NULL;
+    if (!aligned16(saved[i])) return TTC_ERR_ALIGN;
+    if (saved_bytes[i] < j.P.sv_total) return TTC_ERR_WORKSPACE;
+    j.c = chain_ptrs(j.P, G[i], D[i]);
+    j.sv = static_cast<char*>(saved[i]);
+  }
+  (void)hipGetLastError();
+  launch_merge_batch(jobs.data(), n, reinterpret_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_bwd_cores_batch(int32_t n, const tt_linear_desc* const* descs, const int64_t* T,
+                                                const float* const* const* G, const float* const* const* D,
+                                                const void* const* saved, const size_t* saved_bytes,
+                                                float* const* const* dG, void* const* scratch,
+                                                const size_t* scratch_bytes, ttc_stream_t stream) {
+  if (n < 0) return TTC_ERR_SHAPE;
+  if (n == 0) return TTC_OK;
+  if (!descs || !T || !G || !D || !saved || !saved_bytes || !dG || !scratch || !scratch_bytes) return TTC_ERR_NULL;
+  std::vector<LayerJob> jobs;
+  jobs.reserve(n);
+  std::vector<int> empty;
+  for (int i = 0; i < n; ++i) {
+    LayerJob j;
+    memset(&j, 0, sizeof(j));
+    if (!descs[i]) return TTC_ERR_NULL;
+    ttc_status st = bwd_checks(descs[i], T[i], G[i], D[i], &j.P);
+    if (st != TTC_OK) return st;
+    if ((st = grads_checks(j.P, dG[i])) != TTC_OK) return st;
+    if (T[i] == 0) {
+      empty.push_back(i);
+      continue;
     }
+    if ((st = buffer_checks(j.P, false, nullptr, nullptr, nullptr, saved[i], saved_bytes[i], scratch[i],
+                            scratch_bytes[i])) != TTC_OK)
+      return st;
+    j.c = chain_ptrs(j.P, G[i], D[i]);
+    j.sv = const_cast<char*>(static_cast<const char*>(saved[i]));
+    j.sc = static_cast<char*>(scratch[i]);
+    for (int k = 0; k < j.P.d; ++k) j.dG[k] = dG[i][k];
+    jobs.push_back(j);
   }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  for (int i : empty) {
+    LinearPlan P;
+    make_linear_plan(descs[i], 0, &P);
+    launch_zero_grads(P, dG[i], s);
+  }
+  if (!jobs.empty()) launch_cores_batch(jobs.data(), (int)jobs.size(), s);
   return hip_status();
 }
 

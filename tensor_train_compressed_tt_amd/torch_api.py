@@ -15,9 +15,13 @@ from . import (
     TTC_PATH_AUTO,
     make_linear_desc,
     make_ttm_desc,
+    tt_linear_bwd_cores,
+    tt_linear_bwd_cores_batch,
+    tt_linear_bwd_data,
     tt_linear_bwd_split,
     tt_linear_fwd,
     tt_linear_prepare,
+    tt_linear_prepare_batch,
     tt_linear_workspace,
     ttm_embed_bwd,
     ttm_embed_fwd,
@@ -129,6 +133,50 @@ class TTLinear:
                             scratch.numel(), main, gs)
         return (dx if want_dx else None), dG
 
+
+    def backward_data(self, x, dy, cores, D, saved, scratch, want_dx=True, dx=None):
+        """dX on the current stream; the partial sums for backward_cores stay in `scratch`."""
+        T = int(x.shape[0])
+        _need(x, "x", self.dtype, (T, self.n_in))
+        _need(dy, "dy", self.dtype, (T, self.n_out))
+        self._check_chain(cores, D)
+        if want_dx and dx is None:
+            dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
+        tt_linear_bwd_data(self.desc, T, x.data_ptr(), dy.data_ptr(), [c.data_ptr() for c in cores],
+                           [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
+                           dx.data_ptr() if want_dx else None, scratch.data_ptr(), scratch.numel(), _stream())
+        return dx if want_dx else None
+
+    def backward_cores(self, T, cores, D, saved, scratch, dG=None):
+        """dG on the current stream from the partial sums backward_data left in `scratch`."""
+        self._check_chain(cores, D)
+        if dG is None:
+            dG = [torch.empty(s, dtype=torch.float32, device=cores[0].device) for s in self.core_shapes]
+        tt_linear_bwd_cores(self.desc, int(T), [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
+                            saved.data_ptr(), saved.numel(), [g.data_ptr() for g in dG], scratch.data_ptr(),
+                            scratch.numel(), _stream())
+        return dG
+
+def prepare_batch(mods, T, cores, D, saved):
+    """TTLinear.prepare for several layers in one batched call on the current
+    stream (lists with one entry per layer; `saved` buffers are required)."""
+    for m, c, d in zip(mods, cores, D):
+        m._check_chain(c, d)
+    tt_linear_prepare_batch([m.desc for m in mods], [T] * len(mods),
+                            [[t.data_ptr() for t in c] for c in cores], [[v.data_ptr() for v in d] for d in D],
+                            [b.data_ptr() for b in saved], [b.numel() for b in saved], _stream())
+
+
+def backward_cores_batch(mods, T, cores, D, saved, scratch, dG):
+    """TTLinear.backward_cores for several layers in one batched call on the
+    current stream; each layer's backward_data must have run before."""
+    for m, c, d in zip(mods, cores, D):
+        m._check_chain(c, d)
+    tt_linear_bwd_cores_batch([m.desc for m in mods], [T] * len(mods),
+                              [[t.data_ptr() for t in c] for c in cores], [[v.data_ptr() for v in d] for d in D],
+                              [b.data_ptr() for b in saved], [b.numel() for b in saved],
+                              [[g.data_ptr() for g in gl] for gl in dG],
+                              [b.data_ptr() for b in scratch], [b.numel() for b in scratch], _stream())
 
 class TTMEmbedding:
     """A TTM embedding table: cores F_k (r_{k-1}, m_k, n_k, r_k) fp32."""

@@ -117,6 +117,65 @@ def test_bwd_errors_before_launch():
     assert e.value.code == 1
 
 
+
+def test_bwd_data_and_cores_errors_before_launch():
+    d = _desc()
+    sb, cb = ttc.tt_linear_workspace(d, 64)
+    G = [16] * 6
+    D = [16] * 5
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_data(d, 64, 16, 16, G, D, 16, sb, 16, 16, cb - 1)
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_data(d, 64, None, 16, G, D, 16, sb, 16, 16, cb)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_data(d, 64, 16, 24, G, D, 16, sb, 16, 16, cb)
+    assert e.value.code == 5
+    # T = 0: the data pass has nothing to do and touches nothing
+    ttc.tt_linear_bwd_data(d, 0, None, None, G, D, None, 0, None, None, 0)
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_cores(d, 64, G, D, 16, sb - 1, [16] * 6, 16, cb)
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_cores(d, 64, G, D, 16, sb, [16] * 5 + [0], 16, cb)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_cores(d, 64, G, D, None, sb, [16] * 6, 16, cb)
+    assert e.value.code == 1
+
+
+def test_batch_calls_check_every_layer_before_launch():
+    d = _desc()
+    d2 = _desc(out_modes=(12, 16, 16))
+    sb, cb = ttc.tt_linear_workspace(d, 64)
+    sb2, cb2 = ttc.tt_linear_workspace(d2, 64)
+    G = [[16] * 6, [16] * 6]
+    D = [[16] * 5, [16] * 5]
+    # the second layer's saved buffer is too small (sized for the first layer)
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_prepare_batch([d, d2], [64, 64], G, D, [16, 32], [sb, sb])
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_prepare_batch([d, d2], [64, 64], G, D, [16, None], [sb, sb2])
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_prepare_batch([d, d2], [64, 64], G, [[16] * 5, [16] * 4 + [0]], [16, 32], [sb, sb2])
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_cores_batch([d, d2], [64, 64], G, D, [16, 32], [sb, sb2], [[16] * 6, [16] * 6],
+                                      [16, 32], [cb, cb2 - 1])
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_cores_batch([d, d2], [64, 64], G, D, [16, 32], [sb, sb2], [[16] * 6, [16] * 5 + [0]],
+                                      [16, 32], [cb, cb2])
+    assert e.value.code == 1
+    # nothing to do
+    ttc.tt_linear_prepare_batch([], [], [], [], [], [])
+    ttc.tt_linear_bwd_cores_batch([], [], [], [], [], [], [], [], [])
+    code = ttc.lib().tt_linear_prepare_batch(-1, None, None, None, None, None, None, None)
+    assert code == 2
+
 def _merged_macs(out_modes, in_modes, r, T):
     """Independent count: skinny GEMMs of the merged order plus the half merges."""
     n_out, n_in = 1, 1

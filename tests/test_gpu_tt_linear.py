@@ -217,10 +217,96 @@ def test_prepared_and_split_stream_match_single_stream():
         assert np.array_equal(f(g), r)
 
 
-def test_graph_replay_two_streams_matches_eager():
+def test_backward_in_two_calls_matches_single_call():
+    """tt_linear_bwd_data followed (on another stream, after an event) by
+    tt_linear_bwd_cores gives bitwise the results of tt_linear_bwd, for an
+    output-side and an input-side FFN layer; T = 0 zeroes dG."""
+    ttc = _ttc()
+    for li in (4, 5):
+        spec = synth.config_layers(2, 30)[li]
+        layer = synth.make_tt_layer(2, 90 + li, spec, 333, 0.40, "bf16")
+        ref = _run(spec, layer, "bf16")
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, torch.bfloat16, spec.in_first)
+        cores, D, x, dy = _to_dev(layer, "bf16")
+        y, saved = mod.forward(x, cores, D)
+        _, cb = mod.workspace(333)
+        scratch = torch.empty(cb, dtype=torch.uint8, device="cuda")
+        dx = mod.backward_data(x, dy, cores, D, saved, scratch)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dG = mod.backward_cores(333, cores, D, saved, scratch)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        f = lambda t: t.float().cpu().numpy()
+        assert np.array_equal(f(y), ref[0]) and np.array_equal(f(dx), ref[1])
+        for g, r in zip(dG, ref[2]):
+            assert np.array_equal(f(g), r)
+    dG = [torch.full(s, 5.0, device="cuda") for s in mod.core_shapes]
+    mod.backward_cores(0, cores, D, saved, scratch, dG=dG)
+    torch.cuda.synchronize()
+    for g in dG:
+        assert torch.all(g == 0.0)
+
+def test_batched_prepare_and_core_gradients_match_single_layer_calls():
+    """tt_linear_prepare_batch and tt_linear_bwd_cores_batch over layers of
+    different shapes, chain orders and dtypes (and one with T = 0) give
+    bitwise the results of the single-layer calls."""
+    ttc = _ttc()
+    cases = [(synth.config_layers(2, 30)[0], "bf16", 257), (synth.config_layers(2, 30)[4], "bf16", 257),
+             (synth.config_layers(2, 16)[5], "bf16", 257), (synth.config_layers(1, 30)[4], "f32", 130),
+             (synth.config_layers(0)[0], "f32", 0)]
+    mods, data, refs = [], [], []
+    for i, (spec, dt, T) in enumerate(cases):
+        layer = synth.make_tt_layer(2, 300 + i, spec, T, 0.40, dt)
+        in_first = spec.in_first
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, in_first)
+        cores, D, x, dy = _to_dev(layer, dt)
+        y, saved = mod.forward(x, cores, D)
+        dx, dG = mod.backward(x, dy, cores, D, saved)
+        torch.cuda.synchronize()
+        refs.append((y.clone(), dx.clone(), [g.clone() for g in dG]))
+        sb, cb = mod.workspace(T)
+        mods.append(mod)
+        data.append(dict(cores=cores, D=D, x=x, dy=dy, T=T,
+                         saved=torch.empty(max(sb, 256), dtype=torch.uint8, device="cuda"),
+                         scratch=torch.empty(max(cb, 256), dtype=torch.uint8, device="cuda"),
+                         dG=[torch.full(sh, 9.0, device="cuda") for sh in mod.core_shapes]))
+    # per-layer T differs, so call the ctypes level directly
+    ttc.tt_linear_prepare_batch([m.desc for m in mods], [b["T"] for b in data],
+                                [[c.data_ptr() for c in b["cores"]] for b in data],
+                                [[v.data_ptr() for v in b["D"]] for b in data],
+                                [b["saved"].data_ptr() for b in data], [b["saved"].numel() for b in data],
+                                torch.cuda.current_stream().cuda_stream)
+    ys, dxs = [], []
+    for m, b in zip(mods, data):
+        y, _ = m.forward(b["x"], b["cores"], b["D"], saved=b["saved"], prepared=True)
+        dx = m.backward_data(b["x"], b["dy"], b["cores"], b["D"], b["saved"], b["scratch"])
+        ys.append(y)
+        dxs.append(dx)
+    ttc.tt_linear_bwd_cores_batch([m.desc for m in mods], [b["T"] for b in data],
+                                  [[c.data_ptr() for c in b["cores"]] for b in data],
+                                  [[v.data_ptr() for v in b["D"]] for b in data],
+                                  [b["saved"].data_ptr() for b in data], [b["saved"].numel() for b in data],
+                                  [[g.data_ptr() for g in b["dG"]] for b in data],
+                                  [b["scratch"].data_ptr() for b in data], [b["scratch"].numel() for b in data],
+                                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for (ry, rdx, rdG), y, dx, b in zip(refs, ys, dxs, data):
+        assert torch.equal(y, ry) and torch.equal(dx, rdx)
+        for g, r in zip(b["dG"], rdG):
+            assert torch.equal(g, r)
+        if b["T"] == 0:
+            for g in b["dG"]:
+                assert torch.all(g == 0.0)
+
+@pytest.mark.parametrize("deferred", [False, True])
+def test_graph_replay_two_streams_matches_eager(deferred):
     """A captured two-layer step (merges and core-gradient tails on a side
-    stream) replayed several times, with eager work and synchronisation in
-    between, reproduces the eager results every time."""
+    stream; the tails either per layer behind its data pass, or all together
+    after the last data pass) replayed several times, with eager work and
+    synchronisation in between, reproduces the eager results every time."""
     ttc = _ttc()
     specs = synth.config_layers(2, 16)[3:5]
     T = 300
@@ -244,16 +330,33 @@ def test_graph_replay_two_streams_matches_eager():
         side.wait_stream(main)
         evs = []
         with torch.cuda.stream(side):
-            for mod, (cores, D, x, dy, b) in zip(mods, data):
-                mod.prepare(T, cores, D, saved=b["saved"])
+            if deferred:
+                ttc.prepare_batch(mods, T, [d[0] for d in data], [d[1] for d in data],
+                                  [d[4]["saved"] for d in data])
                 e = torch.cuda.Event()
                 e.record(side)
-                evs.append(e)
+                evs = [e] * len(mods)
+            else:
+                for mod, (cores, D, x, dy, b) in zip(mods, data):
+                    mod.prepare(T, cores, D, saved=b["saved"])
+                    e = torch.cuda.Event()
+                    e.record(side)
+                    evs.append(e)
         for mod, e, (cores, D, x, dy, b) in zip(mods, evs, data):
             main.wait_event(e)
             mod.forward(x, cores, D, out=b["y"], saved=b["saved"], prepared=True)
-        for mod, (cores, D, x, dy, b) in reversed(list(zip(mods, data))):
-            mod.backward(x, dy, cores, D, b["saved"], dx=b["dx"], dG=b["dG"], scratch=b["scratch"], grad_stream=side)
+        if deferred:
+            for mod, (cores, D, x, dy, b) in reversed(list(zip(mods, data))):
+                mod.backward_data(x, dy, cores, D, b["saved"], b["scratch"], dx=b["dx"])
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                ttc.backward_cores_batch(mods, T, [d[0] for d in data], [d[1] for d in data],
+                                         [d[4]["saved"] for d in data], [d[4]["scratch"] for d in data],
+                                         [d[4]["dG"] for d in data])
+        else:
+            for mod, (cores, D, x, dy, b) in reversed(list(zip(mods, data))):
+                mod.backward(x, dy, cores, D, b["saved"], dx=b["dx"], dG=b["dG"], scratch=b["scratch"],
+                             grad_stream=side)
         main.wait_stream(side)
 
     def snapshot():
