@@ -227,13 +227,14 @@ __device__ void block_radix_sort(uint32_t* keys, uint16_t* vals, uint16_t* cnt, 
   }
 }
 
-// One stable counting-sort pass over keys < 2^nb, nb <= 8 (the last digits
-// of a level's nodes).  Wave w owns the contiguous range [w*L, (w+1)*L) and
-// walks it in rounds of 64 lanes; lanes holding equal keys in a round are
-// found with one ballot per key bit, which ranks each element among equal
-// keys of its wave in position order.  Counts per (key, wave), key-major,
-// are scanned once for the destinations.
-__device__ void block_multisplit(uint32_t* keys, uint16_t* vals, uint16_t* cnt, uint32_t* s_red, int n, int nb) {
+// One stable counting-sort pass over the digit (key >> shift) mod 2^nb,
+// nb <= 8.  Wave w owns the contiguous range [w*L, (w+1)*L) and walks it in
+// rounds of 64 lanes; lanes holding equal digits in a round are found with
+// one ballot per digit bit, which ranks each element among equal digits of
+// its wave in position order.  Counts per (digit, wave), digit-major, are
+// scanned once for the destinations.
+__device__ void block_multisplit(uint32_t* keys, uint16_t* vals, uint16_t* cnt, uint32_t* s_red, int n, int nb,
+                                 int shift = 0) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = ((n + kSortWaves - 1) / kSortWaves + 63) & ~63;
   const int rounds = L >> 6;
@@ -255,19 +256,20 @@ __device__ void block_multisplit(uint32_t* keys, uint16_t* vals, uint16_t* cnt, 
       const int i = w * L + r * 64 + lane;
       const bool valid = i < n;
       const uint32_t key = valid ? keys[kw + 68 * r] : 0u;
+      const uint32_t dg = (key >> shift) & ((1u << nb) - 1u);
       uint64_t mask = __ballot(valid);
       for (int b = 0; b < nb; ++b) {
-        const bool bit = (key >> b) & 1u;
+        const bool bit = (dg >> b) & 1u;
         const uint64_t bb = __ballot(valid && bit);
         mask &= bit ? bb : ~bb;
       }
       k[r] = key;
       if (valid) {
         vp[r >> 1] |= (uint32_t)vals[vw + 72 * r] << (16 * (r & 1));
-        const uint32_t pre = cnt[key * kSortWaves + w];
+        const uint32_t pre = cnt[dg * kSortWaves + w];
         const uint32_t mine = (uint32_t)__popcll(mask & below);
         rp[r >> 1] |= (pre + mine) << (16 * (r & 1));
-        if (mine == 0) cnt[key * kSortWaves + w] = (uint16_t)(pre + (uint32_t)__popcll(mask));
+        if (mine == 0) cnt[dg * kSortWaves + w] = (uint16_t)(pre + (uint32_t)__popcll(mask));
       }
     }
   }
@@ -293,12 +295,22 @@ __device__ void block_multisplit(uint32_t* keys, uint16_t* vals, uint16_t* cnt, 
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r < rounds && w * L + r * 64 + lane < n) {
-      const int dest = (int)cnt[k[r] * kSortWaves + w] + (int)((rp[r >> 1] >> (16 * (r & 1))) & 0xffffu);
+      const uint32_t dg = (k[r] >> shift) & ((1u << nb) - 1u);
+      const int dest = (int)cnt[dg * kSortWaves + w] + (int)((rp[r >> 1] >> (16 * (r & 1))) & 0xffffu);
       keys[KI(dest)] = k[r];
       vals[VI(dest)] = (uint16_t)(vp[r >> 1] >> (16 * (r & 1)));
     }
   }
   lds_barrier();
+}
+
+// Stable LSD radix sort of keys[0..n) < 2^kbits (16-bit payloads) in LDS:
+// passes of block_multisplit over 8-bit digits, lowest digit first (one
+// pass for the last digits of a level, which have at most 8 bits for
+// vocabulary modes up to 256).
+__device__ void block_radix_sort8(uint32_t* keys, uint16_t* vals, uint16_t* cnt, uint32_t* s_red, int n, int kbits) {
+  for (int shift = 0; shift < kbits; shift += 8)
+    block_multisplit(keys, vals, cnt, s_red, n, kbits - shift < 8 ? kbits - shift : 8, shift);
 }
 
 // first index i in [0, n) with keys[i] >= x (keys ascending), n if none
@@ -420,7 +432,8 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
     pp += __popcll(mp);
     if (i < n) {
       a.order[i] = val[e];
-      if (val[e] < n) a.inverse[val[e]] = i < Tv ? ui : -1;
+      // inverse staged in LDS (free after the sort), stored in token order below
+      if (val[e] < n) s_cnt[val[e]] = i < Tv ? (uint16_t)ui : (uint16_t)0xffffu;
     }
     if (fs) {
       a.uids[ui] = (int32_t)key[e];
@@ -441,6 +454,7 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
     s_ul[a.d - 1] = U;
   }
   lds_barrier();
+  for (int t = tid; t < n; t += kSortThreads) a.inverse[t] = s_cnt[t] == 0xffffu ? -1 : (int32_t)s_cnt[t];
 
   // e1 (levels): distinct prefixes of every level, from level d-2 down to 0;
   // s_val[u] holds the level-(l+1) node of distinct id u
@@ -544,10 +558,7 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_lists(SortArgs a) {
     }
   }
   lds_barrier();
-  if (a.dbits[l] <= 8)
-    block_multisplit(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
-  else
-    block_radix_sort(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
+  block_radix_sort8(s_key, s_val, s_cnt, s_red, Ul, a.dbits[l]);
   for (int j = tid; j < Ul; j += kSortThreads) a.list[l][j] = s_val[VI(j)];
   for (int v = tid; v <= (int)ml; v += kSortThreads) a.list_off[l][v] = lower_bound_lds(s_key, Ul, (uint32_t)v);
 }
