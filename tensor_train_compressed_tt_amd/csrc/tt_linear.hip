@@ -1169,23 +1169,29 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[p][q] = zero4();
-  for (int k0 = 0; k0 < g.K; k0 += kGKC) {
-    lds_barrier();
-    float ra[16], rb[16];
+  // the operands of chunk k0 + kGKC are requested before chunk k0 is
+  // multiplied, so the global latency of one chunk hides behind the MFMA
+  // work of the previous one
+  float ra[16], rb[16];
+  auto load_chunk = [&](int k0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int le = tid + 256 * e;
       const int i = a_kfast ? le / kGKC : le % 32;
       const int k = a_kfast ? le % kGKC : le / 32;
-      const bool ok = i0 + i < g.M && k0 + k < g.K;
+      const bool ok = k0 < g.K && i0 + i < g.M && k0 + k < g.K;
       const float v = g.A[ok ? (i0 + i) * g.sAi + (k0 + k) * g.sAk : 0];
       ra[e] = ok ? (KS ? v * g.ks_[k0 + k] : v) : 0.f;
       const int j = b_jfast ? le % 32 : le / kGKC;
       const int k2 = b_jfast ? le / 32 : le % kGKC;
-      const bool ok2 = j0 + j < g.N && k0 + k2 < g.K;
+      const bool ok2 = k0 < g.K && j0 + j < g.N && k0 + k2 < g.K;
       const float v2 = g.B[ok2 ? (k0 + k2) * g.sBk + (j0 + j) * g.sBj : 0];
       rb[e] = ok2 ? v2 : 0.f;
     }
+  };
+  load_chunk(0);
+  for (int k0 = 0; k0 < g.K; k0 += kGKC) {
+    lds_barrier();
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int le = tid + 256 * e;
@@ -1199,6 +1205,7 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
         Bs[(le / kGKC) * kGLong + le % kGKC] = rb[e];
     }
     lds_barrier();
+    if (k0 + kGKC < g.K) load_chunk(k0 + kGKC);
 #pragma unroll
     for (int st = 0; st < kGKC / 16; ++st) {
       const int kk = (4 * st + w) * 4 + gq;  // k-step 4*st+w of this wave
@@ -1242,15 +1249,15 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
 // One level of the reverse sweep (or of the merge) for one or more layers:
 // up to kMaxGemm independent GEMMs (per half and layer, the core gradient and
 // the gradient passed on to the next core), one 32 x 32 tile per work-group.
-constexpr int kMaxGemm = 16;
+constexpr int kMaxGemm = 24;
 struct SweepArgs {
   Gemm g[kMaxGemm];
   int tiles[kMaxGemm];
   int ng;
 };
 
-// kernel arguments stay well inside the 4 KB argument segment
-static_assert(sizeof(SweepArgs) <= 2048, "SweepArgs too large for a kernel argument");
+// kernel arguments stay inside the 4 KB argument segment
+static_assert(sizeof(SweepArgs) <= 3072, "SweepArgs too large for a kernel argument");
 static_assert(sizeof(PackBatch) <= 2048, "PackBatch too large for a kernel argument");
 
 // KS: the GEMMs scale A's columns by ks_ (the merge levels); the sweep's

@@ -122,6 +122,10 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
 #define TTC_BWD_CUS 256  // compute units of an MI355X
 #endif
   const double ncu = TTC_BWD_CUS;
+#ifndef TTC_LATER_WEIGHT
+#define TTC_LATER_WEIGHT 0.5
+#endif
+  const double kLaterWeight = TTC_LATER_WEIGHT;
   auto choose = [&](int64_t ncols, int maxs, bool dy, int* gc, int* gt, int* nsl, int* tpg) {
     const int chunks = (int)std::max<int64_t>(1, (ncols + P->sw - 1) / P->sw);
     const int gc_min = (chunks + maxs - 1) / maxs;
@@ -141,7 +145,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
         else
           wg += toks * P->Rpad * P->es;  // dZ tile
         const double later = 4.0 * tg * P->rs * double(ncols) + (dy && g > 1 ? 4.0 * g * double(T) * P->Rpad : 0.0);
-        const double cost = std::ceil(double(g) * tg / ncu) * wg + 0.5 * later / ncu;
+        const double cost = std::ceil(double(g) * tg / ncu) * wg + kLaterWeight * later / ncu;
         if (cost < best * (1 - 1e-9)) {
           best = cost;
           bsl = sl;

@@ -51,6 +51,11 @@ constexpr int kChunk = 32;          // sorted positions per piece chunk
 constexpr int kHdrWords = 32;
 constexpr int kTtmThreads = 256;
 constexpr int kLevelThreads = 128;  // per-node work-groups: many resident per CU
+// backward per-node work-groups (measured: 256 threads beat 128 and 512)
+#ifndef TTC_TTM_BWD_THREADS
+#define TTC_TTM_BWD_THREADS 256
+#endif
+constexpr int kLevelBwdThreads = TTC_TTM_BWD_THREADS;
 constexpr size_t kTtmMaxLds = 65536;
 
 // header words of `saved`
@@ -654,10 +659,6 @@ __device__ __forceinline__ float dot_lds(const float* x, int sx, const float* y,
   return acc;
 }
 
-// Sum of a node's source rows, elements [e, e + 4) of each row (float4-aligned
-// rows), in row order.  Rows are requested 8 at a time and the next 8 are in
-// flight while the current 8 are added, so a node with many rows costs about
-// one memory latency plus the issue time of its loads.
 __device__ __forceinline__ void add4(float4& acc, const float4& x) {
   acc.x += x.x;
   acc.y += x.y;
@@ -665,34 +666,44 @@ __device__ __forceinline__ void add4(float4& acc, const float4& x) {
   acc.w += x.w;
 }
 
+// Sum of a node's source rows, elements [e, e + 4) of each row (float4-aligned
+// rows).  Rows are added one at a time in increasing order (one accumulator), in
+// batches of kRowBatch loads with the next batch requested before the current
+// one is added, so a long run of rows costs about one memory latency per
+// kRowBatch rows.
+// (measured: 16 costs more registers than it saves in latency)
+#ifndef TTC_TTM_ROW_BATCH
+#define TTC_TTM_ROW_BATCH 8
+#endif
+constexpr int kRowBatch = TTC_TTM_ROW_BATCH;
 __device__ __forceinline__ float4 sum_rows4(const float* p, int64_t ld, int s0, int s1, int e) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   auto row = [&](int q) { return *reinterpret_cast<const float4*>(p + (int64_t)q * ld + e); };
   int q = s0;
-  if (q + 8 <= s1) {
-    float4 x0[8], x1[8];
+  if (q + kRowBatch <= s1) {
+    float4 x0[kRowBatch], x1[kRowBatch];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x0[k] = row(q + k);
-    q += 8;
+    for (int k = 0; k < kRowBatch; ++k) x0[k] = row(q + k);
+    q += kRowBatch;
     while (true) {
-      const bool more1 = q + 8 <= s1;
+      const bool more1 = q + kRowBatch <= s1;
       if (more1) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x1[k] = row(q + k);
+        for (int k = 0; k < kRowBatch; ++k) x1[k] = row(q + k);
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) add4(acc, x0[k]);
+      for (int k = 0; k < kRowBatch; ++k) add4(acc, x0[k]);
       if (!more1) break;
-      q += 8;
-      const bool more0 = q + 8 <= s1;
+      q += kRowBatch;
+      const bool more0 = q + kRowBatch <= s1;
       if (more0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x0[k] = row(q + k);
+        for (int k = 0; k < kRowBatch; ++k) x0[k] = row(q + k);
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) add4(acc, x1[k]);
+      for (int k = 0; k < kRowBatch; ++k) add4(acc, x1[k]);
       if (!more0) break;
-      q += 8;
+      q += kRowBatch;
     }
   }
   for (; q < s1; ++q) add4(acc, row(q));
@@ -752,7 +763,7 @@ __global__ __launch_bounds__(kLevelThreads) void k_ttm_level_fwd(LevelArgs a) {
 //   C_j[a, c_k, b] = sum_c Pd[c, a] G_j[(c, c_k), b],
 // and its contribution to the parent's gradient,
 //   Q_j[c, a] = D[a] sum_{c_k, b} G_j[(c, c_k), b] F[a, v, c_k, b].
-__global__ __launch_bounds__(kLevelThreads) void k_ttm_level_bwd(LevelArgs a) {
+__global__ __launch_bounds__(kLevelBwdThreads) void k_ttm_level_bwd(LevelArgs a) {
   extern __shared__ float lds[];
   const int np = a.R * a.ra;
   const int nw = a.ra * a.blk;
@@ -1106,7 +1117,15 @@ static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* 
 
 static ttc_status hip_ok() { return hipGetLastError() == hipSuccess ? TTC_OK : TTC_ERR_HIP; }
 
-static unsigned grid_nodes(int64_t cap) { return (unsigned)(cap < 1 ? 1 : (cap > 16384 ? 16384 : cap)); }
+// work-groups of a per-node level launch: the node count is known only on
+// the device, so the grid is capped and each work-group strides over nodes
+// (measured: a cap of 4096 beats launching one work-group per possible node)
+#ifndef TTC_TTM_NODE_GRID
+#define TTC_TTM_NODE_GRID 4096
+#endif
+static unsigned grid_nodes(int64_t cap) {
+  return (unsigned)(cap < 1 ? 1 : (cap > TTC_TTM_NODE_GRID ? TTC_TTM_NODE_GRID : cap));
+}
 
 template <typename Ptr>
 static Ptr at(void* base, size_t off) {
@@ -1301,7 +1320,7 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
     a.C = at<float*>(scratch, P.sc_C[l]);
     a.Q = at<float*>(scratch, P.sc_Q[l]);
     TraceScope ts("ttm_bwd_level", s);
-    TTC_LAUNCH(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelThreads), P.lds_bwd[l], s, a);
+    TTC_LAUNCH(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelBwdThreads), P.lds_bwd[l], s, a);
   }
   ReduceArgs ra;
   memset(&ra, 0, sizeof(ra));
