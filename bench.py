@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--single-stream", action="store_true",
                     help="run merges and core-gradient tails on the main stream too (no overlap)")
     ap.add_argument("--no-ttm", action="store_true", help="time the TT-linear layers only")
+    ap.add_argument("--no-qkv-batch", action="store_true",
+                    help="one launch per layer for the Q, K and V projections instead of one batched launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -241,6 +243,34 @@ def main():
     mods = [L["mod"] for L in layers]
     all_cores = [L["cores"] for L in layers]
     all_D = [L["D"] for L in layers]
+    # Launch groups of the streaming passes.  Within one encoder the Q, K and V
+    # projections are independent (same input, separate outputs), so each of
+    # their passes is one batched launch; O, FFN1 and FFN2 depend on what comes
+    # before them in the encoder and run one after another.
+    fwd_groups = []
+    for e in range(len(layers) // 6):
+        qkv = [6 * e, 6 * e + 1, 6 * e + 2]
+        fwd_groups += ([[i] for i in qkv] if args.no_qkv_batch else [qkv]) + [[6 * e + 3], [6 * e + 4], [6 * e + 5]]
+    bwd_groups = [g[::-1] for g in fwd_groups[::-1]]
+
+    def fwd_group(g):
+        if len(g) == 1:
+            L = layers[g[0]]
+            L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"], prepared=True)
+        else:
+            Ls = [layers[i] for i in g]
+            ttc.forward_batch([L["mod"] for L in Ls], [L["x"] for L in Ls], [L["cores"] for L in Ls],
+                              [L["D"] for L in Ls], [L["y"] for L in Ls], [L["saved"] for L in Ls], prepared=True)
+
+    def bwd_group(g):
+        if len(g) == 1:
+            L = layers[g[0]]
+            L["mod"].backward_data(L["x"], L["dy"], L["cores"], L["D"], L["saved"], L["scratch"], dx=L["dx"])
+        else:
+            Ls = [layers[i] for i in g]
+            ttc.backward_data_batch([L["mod"] for L in Ls], [L["x"] for L in Ls], [L["dy"] for L in Ls],
+                                    [L["cores"] for L in Ls], [L["D"] for L in Ls], [L["saved"] for L in Ls],
+                                    [L["scratch"] for L in Ls], [L["dx"] for L in Ls])
 
     def step_overlap():
         # The merges depend only on the cores and D, the core-gradient tails
@@ -257,10 +287,10 @@ def main():
             ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
         ttm_fwd()
         main.wait_stream(side)
-        for L in layers:
-            L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"], prepared=True)
-        for L in reversed(layers):
-            L["mod"].backward_data(L["x"], L["dy"], L["cores"], L["D"], L["saved"], L["scratch"], dx=L["dx"])
+        for g in fwd_groups:
+            fwd_group(g)
+        for g in bwd_groups:
+            bwd_group(g)
         side.wait_stream(main)
         ttm_bwd()
         with torch.cuda.stream(side):
@@ -314,10 +344,16 @@ def main():
     ttc.trace_stop()
     recs = ttc.trace_records()
     per = {}
-    # layer of the k-th launch of a streaming kernel within one step: the
-    # forward runs over the layers in order, the backward passes in reverse
+    # layers of the k-th launch of a streaming kernel within one step: the
+    # forward runs over the launch groups in order, the backward passes in
+    # reverse (one launch per layer in the single-stream step)
     nl = len(layers)
-    layer_of = {"fwd": list(range(nl)), "bwd_dy": list(range(nl))[::-1], "bwd_dx": list(range(nl))[::-1]}
+    if args.single_stream:
+        fg = [[i] for i in range(nl)]
+        bg = fg[::-1]
+    else:
+        fg, bg = fwd_groups, bwd_groups
+    layer_of = {"fwd": fg, "bwd_dy": bg, "bwd_dx": bg}
     ttm_names = {"ttm_sort", "ttm_lists", "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level", "ttm_reduce"}
     counts = {}
     for name, ms in recs:
@@ -327,11 +363,12 @@ def main():
         counts[name] = k + 1
         d["launches"] += 1
         if name in layer_of:
-            d["bytes"] += sizes[layer_of[name][k % nl]].get(name, 0)
+            grp = layer_of[name][k % len(layer_of[name])]
+            d["bytes"] += sum(sizes[i].get(name, 0) for i in grp)
         elif name in ttm_names:
             d["bytes"] += ttm_sizes.get(name, 0)
     for name in layer_of:
-        assert counts.get(name, 0) == nl * args.steps, (name, counts.get(name))
+        assert counts.get(name, 0) == len(layer_of[name]) * args.steps, (name, counts.get(name))
     for d in per.values():
         d["avg_us"] = 1e3 * d["ms"] / d["launches"]
         d["gbps"] = d["bytes"] / (d["ms"] / 1e3) / 1e9 if d["bytes"] else None
@@ -385,6 +422,7 @@ def main():
             "rank": rank,
             "layers": len(specs),
             "launch": "eager" if graph is None else "hip_graph_replay",
+            "qkv_batched": not (args.no_qkv_batch or args.single_stream),
             "streams": 1 if args.single_stream else 2,
             "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "
                                                   "fp32, Zipf(1.1) ids",

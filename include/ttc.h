@@ -235,6 +235,39 @@ ttc_status tt_linear_bwd_cores_batch(int32_t n, const tt_linear_desc* const* des
                                      ttc_stream_t stream);
 
 /*
+ * Batched forms of tt_linear_fwd and tt_linear_bwd_data for n independent
+ * layers (arrays of n entries, entry i exactly the arguments of the
+ * single-layer call; dx may be NULL as a whole or per entry).  Layers that
+ * share a kernel form (activation type, rank tile count, 16-byte rows and,
+ * for the forward, the token tile) run in common launches of up to four
+ * layers: each streaming pass then has one ramp-up and one tail for all of
+ * them, which matters for passes of a few tens of MB such as the Q, K and V
+ * projections of one encoder (project page, section "Making small tensor
+ * operations fast on GPUs": many small contractions cost more than their
+ * arithmetic).  The forward merges the cores of every layer whose descriptor
+ * lacks TTC_FLAG_PREPARED (batched as tt_linear_prepare_batch).  Results are
+ * bitwise those of the single-layer calls.  All arguments of all layers are
+ * checked before anything is launched; n == 0 does nothing; n < 0 gives
+ * TTC_ERR_SHAPE.  The layers must not share output, saved or scratch buffers.
+ */
+ttc_status tt_linear_fwd_batch(int32_t n, const tt_linear_desc* const* descs,
+                               const int64_t* T, const void* const* x,
+                               const float* const* const* G,
+                               const float* const* const* D, void* const* y,
+                               void* const* saved, const size_t* saved_bytes,
+                               ttc_stream_t stream);
+ttc_status tt_linear_bwd_data_batch(int32_t n, const tt_linear_desc* const* descs,
+                                    const int64_t* T, const void* const* x,
+                                    const void* const* dy,
+                                    const float* const* const* G,
+                                    const float* const* const* D,
+                                    const void* const* saved,
+                                    const size_t* saved_bytes, void* const* dx,
+                                    void* const* scratch,
+                                    const size_t* scratch_bytes,
+                                    ttc_stream_t stream);
+
+/*
  * Planner report (host-only): writes a NUL-terminated text into buf (at most
  * n bytes) with the chosen path and the modelled flops / bytes of the merged,
  * sequential and dense paths for T tokens.

@@ -45,6 +45,8 @@ EXPORTS = [
     "tt_linear_bwd_cores",
     "tt_linear_prepare_batch",
     "tt_linear_bwd_cores_batch",
+    "tt_linear_fwd_batch",
+    "tt_linear_bwd_data_batch",
     "tt_linear_path_cost",
     "ttm_embed_workspace",
     "ttm_embed_fwd",
@@ -118,6 +120,11 @@ def lib() -> ctypes.CDLL:
         "tt_linear_prepare": [D, _I64, pp, pp, _P, _SZ, _P],
         "tt_linear_prepare_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), ctypes.POINTER(pp),
                                     ctypes.POINTER(pp), pp, ctypes.POINTER(_SZ), _P],
+        "tt_linear_fwd_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), pp, ctypes.POINTER(pp),
+                                ctypes.POINTER(pp), pp, pp, ctypes.POINTER(_SZ), _P],
+        "tt_linear_bwd_data_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), pp, pp,
+                                     ctypes.POINTER(pp), ctypes.POINTER(pp), pp, ctypes.POINTER(_SZ), pp, pp,
+                                     ctypes.POINTER(_SZ), _P],
         "tt_linear_bwd_cores_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), ctypes.POINTER(pp),
                                       ctypes.POINTER(pp), pp, ctypes.POINTER(_SZ), ctypes.POINTER(pp), pp,
                                       ctypes.POINTER(_SZ), _P],
@@ -286,6 +293,28 @@ def tt_linear_bwd_cores_batch(descs, T, G, D, saved, saved_bytes, dG, scratch, s
     _check("tt_linear_bwd_cores_batch", code)
 
 
+def _vp(arr):
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+
+
+def tt_linear_fwd_batch(descs, T, x, G, D, y, saved, saved_bytes, stream=0):
+    dp, ta, (ga, da), _keep = _batch_args(descs, T, [G, D])
+    n = max(1, len(descs))
+    code = lib().tt_linear_fwd_batch(len(descs), dp, ta, _vp(_addr_array(x)), ga, da, _vp(_addr_array(y)),
+                                     _vp(_addr_array(saved)), (_SZ * n)(*saved_bytes), stream)
+    _check("tt_linear_fwd_batch", code)
+
+
+def tt_linear_bwd_data_batch(descs, T, x, dy, G, D, saved, saved_bytes, dx, scratch, scratch_bytes, stream=0):
+    dp, ta, (ga, da), _keep = _batch_args(descs, T, [G, D])
+    n = max(1, len(descs))
+    dxa = _vp(_addr_array(dx)) if dx is not None else None
+    code = lib().tt_linear_bwd_data_batch(len(descs), dp, ta, _vp(_addr_array(x)), _vp(_addr_array(dy)), ga, da,
+                                          _vp(_addr_array(saved)), (_SZ * n)(*saved_bytes), dxa,
+                                          _vp(_addr_array(scratch)), (_SZ * n)(*scratch_bytes), stream)
+    _check("tt_linear_bwd_data_batch", code)
+
+
 def tt_linear_explain(desc: TTLinearDesc, T: int) -> str:
     buf = ctypes.create_string_buffer(1024)
     _check("tt_linear_explain", lib().tt_linear_explain(ctypes.byref(desc), T, buf, 1024))
@@ -347,4 +376,11 @@ def version() -> str:
     return lib().ttc_version().decode()
 
 
-from .torch_api import TTLinear, TTMEmbedding, backward_cores_batch, prepare_batch  # noqa: E402,F401
+from .torch_api import (  # noqa: E402,F401
+    TTLinear,
+    TTMEmbedding,
+    backward_cores_batch,
+    backward_data_batch,
+    forward_batch,
+    prepare_batch,
+)

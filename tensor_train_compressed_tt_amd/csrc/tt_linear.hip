@@ -313,14 +313,47 @@ constexpr size_t kFwdLdsBytes() {
 // those reads (L2 hits) count against the same per-CU load throughput as the
 // reads of x, so the wide variant (NW = 8, 64 tokens, one work-group per CU)
 // reads A and B half as often per token as two 32-token work-groups.
+// Layers of one streaming launch: work-group i belongs to the layer q with
+// first[q] <= i < first[q + 1] and runs as work-group i - first[q] of that
+// layer's own grid (independent layers, e.g. the Q, K and V projections of an
+// encoder, share one launch: one ramp-up and one tail instead of three).
+constexpr int kMaxStream = 4;
+template <typename T>
+struct FwdArgs {
+  const typename Elem<T>::type* x;
+  const typename Elem<T>::type* Ac;
+  const typename Elem<T>::type* Bc;
+  typename Elem<T>::type* Z;
+  typename Elem<T>::type* y;
+  int64_t T_, N_in, N_out;
+  int vin, vout;
+};
+template <typename A>
+struct StreamBatch {
+  A a[kMaxStream];
+  int first[kMaxStream + 1];
+  int n;
+};
+template <typename A>
+__device__ __forceinline__ int batch_layer(const StreamBatch<A>& b, unsigned* local) {
+  int q = 0;
+  while (q < b.n - 1 && (int)blockIdx.x >= b.first[q + 1]) ++q;
+  *local = blockIdx.x - (unsigned)b.first[q];
+  return q;
+}
+
 template <typename T, int NR, bool VEC, int TT, int NW>
-__global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* __restrict__ x,
-                                             const typename Elem<T>::type* __restrict__ Ac,
-                                             const typename Elem<T>::type* __restrict__ Bc,
-                                             typename Elem<T>::type* __restrict__ Z,
-                                             typename Elem<T>::type* __restrict__ y, int64_t T_, int64_t N_in,
-                                             int64_t N_out, int vin, int vout) {
+__global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   typedef typename Elem<T>::type E;
+  unsigned bid;
+  const FwdArgs<T>& fa_ = fb.a[batch_layer(fb, &bid)];
+  const E* __restrict__ x = fa_.x;
+  const E* __restrict__ Ac = fa_.Ac;
+  const E* __restrict__ Bc = fa_.Bc;
+  E* __restrict__ Z = fa_.Z;
+  E* __restrict__ y = fa_.y;
+  const int64_t T_ = fa_.T_, N_in = fa_.N_in, N_out = fa_.N_out;
+  const int vin = fa_.vin, vout = fa_.vout;
   typedef typename Mma<T>::frag frag;
   constexpr int Rpad = 16 * NR;
   constexpr int EPV = Mma<T>::EPV, KSTEP = Mma<T>::KSTEP;
@@ -340,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t t0 = (int64_t)blockIdx.x * TM;
+  const int64_t t0 = (int64_t)bid * TM;
 
   f32x4 acc[TT][NR];
 #pragma unroll
@@ -382,7 +415,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   // Likewise for B: work-group b visits the output steps (TPS tiles each)
   // starting at step b mod nsteps.
   const int nsteps = (not_ + TPS - 1) / TPS;
-  const int rot2 = (int)(blockIdx.x % (unsigned)nsteps);
+  const int rot2 = (int)(bid % (unsigned)nsteps);
   auto ostep = [&](int sidx) { return ((sidx + rot2) % nsteps) * TPS; };
   // with one rank tile pair the first B batches are requested right away;
   // wider ranks wait for phase 2 (register budget)
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(const typename Elem<T>::type* _
   // that concurrent requests for A spread over the L2 channels instead of
   // queueing on the same lines.
   const int nkb = (nks + KB - 1) / KB;
-  const int rot1 = (int)(blockIdx.x % (unsigned)nkb);
+  const int rot1 = (int)(bid % (unsigned)nkb);
   auto kbat = [&](int j) { return ((j + rot1) % nkb) * KB; };
   fetch_x(fa0, fb0, kbat(0), true);
   for (int j = 0; j < nkb; j += 2) {
@@ -574,7 +607,9 @@ struct DyArgs {
 };
 
 template <typename T, int NR, bool VEC>
-__global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
+__global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
+  unsigned bid;
+  const DyArgs<T>& a = bb.a[batch_layer(bb, &bid)];
   typedef Bwd<T, NR> B;
   typedef typename B::E E;
   typedef typename Mma<T>::frag frag;
@@ -588,7 +623,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int gc = blockIdx.x, gt = blockIdx.y;
+  const int gc = (int)(bid % (unsigned)a.gc_n), gt = (int)(bid / (unsigned)a.gc_n);
   const int64_t c0 = (int64_t)gc * a.nsl * B::SW;
   const int nsl = (int)std::min<int64_t>(a.nsl, (a.N_out - c0 + B::SW - 1) / B::SW);
   const int reff = a.meta[kMetaReff];
@@ -784,16 +819,27 @@ __global__ __launch_bounds__(256) void k_bwd_dy(DyArgs<T> a) {
   }
 }
 
-// dZ = sum of the column groups' partials, in group order (deterministic)
+// dZ = sum of the column groups' partials, in group order (deterministic);
+// every layer of the batch strides over its own range of work-groups
 template <typename T>
-__global__ __launch_bounds__(256) void k_dz_sum(const float* __restrict__ dZp, typename Elem<T>::type* __restrict__ dZ,
-                                                int ngc, int64_t n4) {
+struct DzArgs {
+  const float* dZp;
+  typename Elem<T>::type* dZ;
+  int ngc;
+  int64_t n4;
+};
+template <typename T>
+__global__ __launch_bounds__(256) void k_dz_sum(StreamBatch<DzArgs<T>> zb) {
   typedef typename Elem<T>::type E;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+  unsigned bid;
+  const int q = batch_layer(zb, &bid);
+  const DzArgs<T>& a = zb.a[q];
+  const int64_t nb = zb.first[q + 1] - zb.first[q];
+  for (int64_t i = (int64_t)bid * blockDim.x + threadIdx.x; i < a.n4; i += nb * blockDim.x) {
     f32x4 sum = zero4();
-    for (int q = 0; q < ngc; ++q) sum += *reinterpret_cast<const f32x4*>(dZp + ((int64_t)q * n4 + i) * 4);
+    for (int g = 0; g < a.ngc; ++g) sum += *reinterpret_cast<const f32x4*>(a.dZp + ((int64_t)g * a.n4 + i) * 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dZ[i * 4 + e] = (E)Mma<T>::from_f32(sum[e]);
+    for (int e = 0; e < 4; ++e) a.dZ[i * 4 + e] = (E)Mma<T>::from_f32(sum[e]);
   }
 }
 
@@ -809,11 +855,13 @@ struct DxArgs {
   typename Elem<T>::type* dx;         // T x N_in or null
   const int* meta;
   int64_t T_, N_in;
-  int nsl, tpg, ntiles, vec;
+  int nsl, tpg, ntiles, vec, gcols;
 };
 
 template <typename T, int NR, bool VEC>
-__global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
+__global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
+  unsigned bid;
+  const DxArgs<T>& a = bb.a[batch_layer(bb, &bid)];
   typedef Bwd<T, NR> B;
   typedef typename B::E E;
   typedef typename Mma<T>::frag frag;
@@ -827,7 +875,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(DxArgs<T> a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int gc = blockIdx.x, gt = blockIdx.y;
+  const int gc = (int)(bid % (unsigned)a.gcols), gt = (int)(bid / (unsigned)a.gcols);
   const int64_t c0 = (int64_t)gc * a.nsl * B::SW;
   const int nsl = (int)std::min<int64_t>(a.nsl, (a.N_in - c0 + B::SW - 1) / B::SW);
   const int reff = a.meta[kMetaReff];
@@ -1407,8 +1455,19 @@ static void allow_lds(const void* kern, size_t bytes) {
   if (bytes > 65536) (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// One layer's share of a streaming launch.
+struct StreamJob {
+  const LinearPlan* P;
+  const void* x;
+  const void* dy;
+  char* sv;  // saved: the forward writes Z there, the backward reads it
+  void* y;   // forward output
+  void* dx;  // backward output, or null
+  char* sc;  // backward scratch
+};
+
 template <typename T, int NR, bool VEC, int TT, int NW>
-static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
+static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef typename Elem<T>::type E;
   const size_t lds = kFwdLdsBytes<T, NR, TT, NW>();
   auto kern = k_fwd<T, NR, VEC, TT, NW>;
@@ -1417,55 +1476,81 @@ static void launch_fwd_v(const LinearPlan& P, const void* x, char* saved, void* 
     allow_lds((const void*)kern, lds);
     lds_set = true;
   }
-  const int vout = (P.N_out % 4) == 0 && aligned16(y);
-  const unsigned grid = (unsigned)((P.T + 16 * TT - 1) / (16 * TT));
+  StreamBatch<FwdArgs<T>> b;
+  memset(&b, 0, sizeof(b));
+  for (int i = 0; i < n; ++i) {
+    const LinearPlan& P = *jobs[i].P;
+    FwdArgs<T>& a = b.a[i];
+    a.x = (const E*)jobs[i].x;
+    a.Ac = (const E*)(jobs[i].sv + P.sv_Ac);
+    a.Bc = (const E*)(jobs[i].sv + P.sv_Bc);
+    a.Z = (E*)(jobs[i].sv + P.sv_Z);
+    a.y = (E*)jobs[i].y;
+    a.T_ = P.T;
+    a.N_in = P.N_in;
+    a.N_out = P.N_out;
+    a.vin = (int)VEC;
+    a.vout = (P.N_out % 4) == 0 && aligned16(jobs[i].y);
+    b.first[i + 1] = b.first[i] + (int)((P.T + 16 * TT - 1) / (16 * TT));
+  }
+  b.n = n;
   TraceScope ts("fwd", st);
-  TTC_LAUNCH(kern, dim3(grid), dim3(64 * NW), lds, st, (const E*)x, (const E*)(saved + P.sv_Ac),
-                     (const E*)(saved + P.sv_Bc), (E*)(saved + P.sv_Z), (E*)y, P.T, P.N_in, P.N_out, (int)VEC, vout);
+  TTC_LAUNCH(kern, dim3((unsigned)b.first[n]), dim3(64 * NW), lds, st, b);
 }
 
 // 2-byte activations up to rank 64: 64-token work-groups of eight waves once
 // there are enough tiles to give every CU one; otherwise 32-token
 // work-groups of four waves.
-template <typename T, int NR>
-static void launch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
-  // 16-byte rows of both x and Y: the buffer-access form
-  const bool vec = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x) && (P.N_out % Mma<T>::EPV) == 0 && aligned16(y);
 #ifndef TTC_FWD_WIDE_TILES
 #define TTC_FWD_WIDE_TILES 256
 #endif
+template <typename T>
+static bool fwd_vec(const StreamJob& j) {
+  const LinearPlan& P = *j.P;
+  return (P.N_in % Mma<T>::EPV) == 0 && aligned16(j.x) && (P.N_out % Mma<T>::EPV) == 0 && aligned16(j.y);
+}
+template <typename T, int NR>
+static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, hipStream_t st) {
   if constexpr (sizeof(typename Elem<T>::type) == 2 && NR <= 4) {
-    if (P.ntiles >= TTC_FWD_WIDE_TILES) {
-      if (vec) launch_fwd_v<T, NR, true, 4, 8>(P, x, saved, y, st);
-      else launch_fwd_v<T, NR, false, 4, 8>(P, x, saved, y, st);
+    if (wide) {
+      if (vec) launch_fwd_v<T, NR, true, 4, 8>(jobs, n, st);
+      else launch_fwd_v<T, NR, false, 4, 8>(jobs, n, st);
       return;
     }
   }
-  if (vec) launch_fwd_v<T, NR, true, 2, 4>(P, x, saved, y, st);
-  else launch_fwd_v<T, NR, false, 2, 4>(P, x, saved, y, st);
+  if (vec) launch_fwd_v<T, NR, true, 2, 4>(jobs, n, st);
+  else launch_fwd_v<T, NR, false, 2, 4>(jobs, n, st);
 }
 
 template <typename T, int NR, bool VY, bool VX>
-static void launch_bwd_v(const LinearPlan& P, const void* x, const void* dy, const char* saved, void* dx,
-                            char* scratch, hipStream_t st) {
+static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef Bwd<T, NR> B;
   typedef typename B::E E;
   {
-    DyArgs<T> a;
-    a.dy = (const E*)dy;
-    a.BcT = (const E*)(saved + P.sv_BcT);
-    a.Z = (const E*)(saved + P.sv_Z);
-    a.dZp = (float*)(scratch + P.sc_dZp);
-    a.dZ = (E*)(scratch + P.sc_dZ);
-    a.dBp = (float*)(scratch + P.sc_dBp);
-    a.meta = (const int*)(saved + P.sv_meta);
-    a.T_ = P.T;
-    a.N_out = P.N_out;
-    a.nsl = P.dy_nsl;
-    a.tpg = P.dy_tpg;
-    a.ntiles = P.ntiles;
-    a.gc_n = P.dy_gc;
-    a.vec = (P.N_out % B::EPV) == 0 && aligned16(dy);
+    StreamBatch<DyArgs<T>> b;
+    memset(&b, 0, sizeof(b));
+    for (int i = 0; i < n; ++i) {
+      const LinearPlan& P = *jobs[i].P;
+      const char* saved = jobs[i].sv;
+      char* scratch = jobs[i].sc;
+      DyArgs<T>& a = b.a[i];
+      a.dy = (const E*)jobs[i].dy;
+      a.BcT = (const E*)(saved + P.sv_BcT);
+      a.Z = (const E*)(saved + P.sv_Z);
+      a.dZp = (float*)(scratch + P.sc_dZp);
+      a.dZ = (E*)(scratch + P.sc_dZ);
+      a.dBp = (float*)(scratch + P.sc_dBp);
+      a.meta = (const int*)(saved + P.sv_meta);
+      a.T_ = P.T;
+      a.N_out = P.N_out;
+      a.nsl = P.dy_nsl;
+      a.tpg = P.dy_tpg;
+      a.ntiles = P.ntiles;
+      a.gc_n = P.dy_gc;
+      a.vec = (P.N_out % B::EPV) == 0 && aligned16(jobs[i].dy);
+      b.first[i + 1] = b.first[i] + P.dy_gc * P.dy_gt;
+    }
+    b.n = n;
     constexpr int NSM = bwd_max_slabs(B::ES, NR);
     const size_t lds = size_t(B::Rpad) * (NSM * B::SW + 16 / B::ES) * B::ES + 2 * B::SLAB * B::ES +
                        size_t(B::Rpad) * B::ZLD * B::ES;
@@ -1475,28 +1560,52 @@ static void launch_bwd_v(const LinearPlan& P, const void* x, const void* dy, con
       lds_set = true;
     }
     TraceScope ts("bwd_dy", st);
-    TTC_LAUNCH((k_bwd_dy<T, NR, VY>), dim3(P.dy_gc, P.dy_gt), dim3(256), lds, st, a);
-  }
-  if (P.dy_gc > 1) {
-    const int64_t n4 = P.T * B::Rpad / 4;
-    TraceScope ts("dz_sum", st);
-    TTC_LAUNCH(k_dz_sum<T>, dim3((unsigned)std::min<int64_t>(4096, (n4 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)(scratch + P.sc_dZp), (E*)(scratch + P.sc_dZ), P.dy_gc, n4);
+    TTC_LAUNCH((k_bwd_dy<T, NR, VY>), dim3((unsigned)b.first[n]), dim3(256), lds, st, b);
   }
   {
-    DxArgs<T> a;
-    a.x = (const E*)x;
-    a.AcT = (const E*)(saved + P.sv_AcT);
-    a.dZ = (const E*)(scratch + P.sc_dZ);
-    a.dAp = (float*)(scratch + P.sc_dAp);
-    a.dx = (E*)dx;
-    a.meta = (const int*)(saved + P.sv_meta);
-    a.T_ = P.T;
-    a.N_in = P.N_in;
-    a.nsl = P.dx_nsl;
-    a.tpg = P.dx_tpg;
-    a.ntiles = P.ntiles;
-    a.vec = (P.N_in % B::EPV) == 0 && aligned16(x) && (dx == nullptr || aligned16(dx));
+    StreamBatch<DzArgs<T>> b;
+    memset(&b, 0, sizeof(b));
+    for (int i = 0; i < n; ++i) {
+      const LinearPlan& P = *jobs[i].P;
+      if (P.dy_gc <= 1) continue;
+      const int64_t n4 = P.T * B::Rpad / 4;
+      DzArgs<T>& a = b.a[b.n];
+      a.dZp = (const float*)(jobs[i].sc + P.sc_dZp);
+      a.dZ = (E*)(jobs[i].sc + P.sc_dZ);
+      a.ngc = P.dy_gc;
+      a.n4 = n4;
+      b.first[b.n + 1] = b.first[b.n] + (int)std::min<int64_t>(4096, (n4 + 255) / 256);
+      ++b.n;
+    }
+    if (b.n > 0) {
+      TraceScope ts("dz_sum", st);
+      TTC_LAUNCH(k_dz_sum<T>, dim3((unsigned)b.first[b.n]), dim3(256), 0, st, b);
+    }
+  }
+  {
+    StreamBatch<DxArgs<T>> b;
+    memset(&b, 0, sizeof(b));
+    for (int i = 0; i < n; ++i) {
+      const LinearPlan& P = *jobs[i].P;
+      const char* saved = jobs[i].sv;
+      char* scratch = jobs[i].sc;
+      DxArgs<T>& a = b.a[i];
+      a.x = (const E*)jobs[i].x;
+      a.AcT = (const E*)(saved + P.sv_AcT);
+      a.dZ = (const E*)(scratch + P.sc_dZ);
+      a.dAp = (float*)(scratch + P.sc_dAp);
+      a.dx = (E*)jobs[i].dx;
+      a.meta = (const int*)(saved + P.sv_meta);
+      a.T_ = P.T;
+      a.N_in = P.N_in;
+      a.nsl = P.dx_nsl;
+      a.tpg = P.dx_tpg;
+      a.ntiles = P.ntiles;
+      a.vec = (P.N_in % B::EPV) == 0 && aligned16(jobs[i].x) && (jobs[i].dx == nullptr || aligned16(jobs[i].dx));
+      a.gcols = P.dx_gc;
+      b.first[i + 1] = b.first[i] + P.dx_gc * P.dx_gt;
+    }
+    b.n = n;
     constexpr int NSM = dx_max_slabs(B::ES, NR);
     const size_t lds = size_t(NSM) * B::SW * B::RLD * B::ES + 2 * B::SLAB * B::ES + size_t(64) * B::RLD * B::ES +
                        size_t(B::Rpad) * B::ZLD * B::ES;
@@ -1506,42 +1615,75 @@ static void launch_bwd_v(const LinearPlan& P, const void* x, const void* dy, con
       lds_set = true;
     }
     TraceScope ts("bwd_dx", st);
-    TTC_LAUNCH((k_bwd_dx<T, NR, VX>), dim3(P.dx_gc, P.dx_gt), dim3(256), lds, st, a);
+    TTC_LAUNCH((k_bwd_dx<T, NR, VX>), dim3((unsigned)b.first[n]), dim3(256), lds, st, b);
   }
 }
 
+template <typename T>
+static bool bwd_vec(const StreamJob& j) {
+  const LinearPlan& P = *j.P;
+  const bool vy = (P.N_out % Mma<T>::EPV) == 0 && aligned16(j.dy);
+  const bool vx = (P.N_in % Mma<T>::EPV) == 0 && aligned16(j.x) && (j.dx == nullptr || aligned16(j.dx));
+  return vy && vx;
+}
 template <typename T, int NR>
-static void launch_bwd_main(const LinearPlan& P, const void* x, const void* dy, const char* saved, void* dx,
-                            char* scratch, hipStream_t st) {
-  const bool vy = (P.N_out % Mma<T>::EPV) == 0 && aligned16(dy);
-  const bool vx = (P.N_in % Mma<T>::EPV) == 0 && aligned16(x) && (dx == nullptr || aligned16(dx));
-  if (vy && vx)
-    launch_bwd_v<T, NR, true, true>(P, x, dy, saved, dx, scratch, st);
+static void launch_bwd_group(const StreamJob* jobs, int n, bool vec, hipStream_t st) {
+  if (vec)
+    launch_bwd_v<T, NR, true, true>(jobs, n, st);
   else
-    launch_bwd_v<T, NR, false, false>(P, x, dy, saved, dx, scratch, st);
+    launch_bwd_v<T, NR, false, false>(jobs, n, st);
 }
 
-template <typename T>
-static bool dispatch_fwd(const LinearPlan& P, const void* x, char* saved, void* y, hipStream_t st) {
-  switch (P.NR) {
-    case 2: launch_fwd<T, 2>(P, x, saved, y, st); return true;
-    case 4: launch_fwd<T, 4>(P, x, saved, y, st); return true;
-    case 6: launch_fwd<T, 6>(P, x, saved, y, st); return true;
-    case 8: launch_fwd<T, 8>(P, x, saved, y, st); return true;
-  }
-  return false;
-}
+static bool nr_supported(int NR) { return NR == 2 || NR == 4 || NR == 6 || NR == 8; }
 
-template <typename T>
-static bool dispatch_bwd(const LinearPlan& P, const void* x, const void* dy, const char* saved, void* dx,
-                         char* scratch, hipStream_t st) {
-  switch (P.NR) {
-    case 2: launch_bwd_main<T, 2>(P, x, dy, saved, dx, scratch, st); return true;
-    case 4: launch_bwd_main<T, 4>(P, x, dy, saved, dx, scratch, st); return true;
-    case 6: launch_bwd_main<T, 6>(P, x, dy, saved, dx, scratch, st); return true;
-    case 8: launch_bwd_main<T, 8>(P, x, dy, saved, dx, scratch, st); return true;
+// Streaming launches for a list of layers: layers that share a kernel
+// instantiation (activation type, rank tile count, 16-byte form and, for the
+// forward, the tile width) go into common launches of up to kMaxStream
+// layers, in list order; the others get launches of their own.  The caller
+// has checked nr_supported for every layer.
+template <bool FWD>
+static void launch_stream_jobs(const StreamJob* jobs, int n, hipStream_t st) {
+  auto key = [&](const StreamJob& j) {
+    const LinearPlan& P = *j.P;
+    const bool bf = P.act == TTC_BF16;
+    const bool vec = FWD ? (bf ? fwd_vec<bf16_t>(j) : fwd_vec<float>(j)) : (bf ? bwd_vec<bf16_t>(j) : bwd_vec<float>(j));
+    const bool wide = FWD && P.ntiles >= TTC_FWD_WIDE_TILES;
+    return (P.act << 8) | (P.NR << 2) | ((int)vec << 1) | (int)wide;
+  };
+  std::vector<char> done(n, 0);
+  std::vector<StreamJob> grp;
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const int k = key(jobs[i]);
+    grp.clear();
+    for (int j = i; j < n; ++j)
+      if (!done[j] && key(jobs[j]) == k) {
+        grp.push_back(jobs[j]);
+        done[j] = 1;
+      }
+    const bool bf = (k >> 8) == TTC_BF16;
+    const int NR = (k >> 2) & 63;
+    const bool vec = (k >> 1) & 1, wide = k & 1;
+    for (size_t g0 = 0; g0 < grp.size(); g0 += kMaxStream) {
+      const int m = (int)std::min<size_t>(kMaxStream, grp.size() - g0);
+      const StreamJob* js = grp.data() + g0;
+      if constexpr (FWD) {
+        switch (NR) {
+          case 2: bf ? launch_fwd_group<bf16_t, 2>(js, m, vec, wide, st) : launch_fwd_group<float, 2>(js, m, vec, wide, st); break;
+          case 4: bf ? launch_fwd_group<bf16_t, 4>(js, m, vec, wide, st) : launch_fwd_group<float, 4>(js, m, vec, wide, st); break;
+          case 6: bf ? launch_fwd_group<bf16_t, 6>(js, m, vec, wide, st) : launch_fwd_group<float, 6>(js, m, vec, wide, st); break;
+          case 8: bf ? launch_fwd_group<bf16_t, 8>(js, m, vec, wide, st) : launch_fwd_group<float, 8>(js, m, vec, wide, st); break;
+        }
+      } else {
+        switch (NR) {
+          case 2: bf ? launch_bwd_group<bf16_t, 2>(js, m, vec, st) : launch_bwd_group<float, 2>(js, m, vec, st); break;
+          case 4: bf ? launch_bwd_group<bf16_t, 4>(js, m, vec, st) : launch_bwd_group<float, 4>(js, m, vec, st); break;
+          case 6: bf ? launch_bwd_group<bf16_t, 6>(js, m, vec, st) : launch_bwd_group<float, 6>(js, m, vec, st); break;
+          case 8: bf ? launch_bwd_group<bf16_t, 8>(js, m, vec, st) : launch_bwd_group<float, 8>(js, m, vec, st); break;
+        }
+      }
+    }
   }
-  return false;
 }
 
 static unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
@@ -1772,9 +1914,10 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   char* sv = static_cast<char*>(saved);
+  if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
   if (!(desc->flags & TTC_FLAG_PREPARED)) launch_merge(P, G, D, sv, s);
-  const bool ok = P.act == TTC_BF16 ? dispatch_fwd<bf16_t>(P, x, sv, y, s) : dispatch_fwd<float>(P, x, sv, y, s);
-  if (!ok) return TTC_ERR_UNSUPPORTED;
+  StreamJob j{&P, x, nullptr, sv, y, nullptr, nullptr};
+  launch_stream_jobs<true>(&j, 1, s);
   return hip_status();
 }
 
@@ -1932,9 +2075,9 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
   if ((st = buffer_checks(P, true, x, dy, dx, saved, saved_bytes, scratch, scratch_bytes)) != TTC_OK) return st;
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
-  const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s_main)
-                                    : dispatch_bwd<float>(P, x, dy, sv, dx, sc, s_main);
-  if (!ok) return TTC_ERR_UNSUPPORTED;
+  if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
+  StreamJob job{&P, x, dy, const_cast<char*>(sv), nullptr, dx, sc};
+  launch_stream_jobs<false>(&job, 1, s_main);
   if (s != s_main) {
     hipEvent_t ev = split_event();
     if (!ev) return TTC_ERR_HIP;
@@ -1958,9 +2101,9 @@ extern "C" ttc_status tt_linear_bwd_data(const tt_linear_desc* desc, int64_t T, 
   (void)hipGetLastError();
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
-  const bool ok = P.act == TTC_BF16 ? dispatch_bwd<bf16_t>(P, x, dy, sv, dx, sc, s)
-                                    : dispatch_bwd<float>(P, x, dy, sv, dx, sc, s);
-  if (!ok) return TTC_ERR_UNSUPPORTED;
+  if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
+  StreamJob job{&P, x, dy, const_cast<char*>(sv), nullptr, dx, sc};
+  launch_stream_jobs<false>(&job, 1, s);
   return hip_status();
 }
 
@@ -2049,6 +2192,78 @@ extern "C" ttc_status tt_linear_bwd_cores_batch(int32_t n, const tt_linear_desc*
     launch_zero_grads(P, dG[i], s);
   }
   if (!jobs.empty()) launch_cores_batch(jobs.data(), (int)jobs.size(), s);
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_fwd_batch(int32_t n, const tt_linear_desc* const* descs, const int64_t* T,
+                                          const void* const* x, const float* const* const* G,
+                                          const float* const* const* D, void* const* y, void* const* saved,
+                                          const size_t* saved_bytes, ttc_stream_t stream) {
+  if (n < 0) return TTC_ERR_SHAPE;
+  if (n == 0) return TTC_OK;
+  if (!descs || !T || !x || !G || !D || !y || !saved || !saved_bytes) return TTC_ERR_NULL;
+  std::vector<LinearPlan> plans(n);
+  std::vector<LayerJob> merges;
+  std::vector<StreamJob> jobs;
+  for (int i = 0; i < n; ++i) {
+    if (!descs[i]) return TTC_ERR_NULL;
+    LinearPlan& P = plans[i];
+    ttc_status st = make_linear_plan(descs[i], T[i], &P);
+    if (st != TTC_OK) return st;
+    if ((st = check_chain(P, G[i], D[i])) != TTC_OK) return st;
+    if (T[i] == 0) continue;
+    if (!x[i] || !y[i] || !saved[i]) return TTC_ERR_NULL;
+    if (!aligned16(x[i]) || !aligned16(y[i]) || !aligned16(saved[i])) return TTC_ERR_ALIGN;
+    if (saved_bytes[i] < P.sv_total) return TTC_ERR_WORKSPACE;
+    if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
+    if (!(descs[i]->flags & TTC_FLAG_PREPARED)) {
+      LayerJob m;
+      memset(&m, 0, sizeof(m));
+      m.P = P;
+      m.c = chain_ptrs(P, G[i], D[i]);
+      m.sv = static_cast<char*>(saved[i]);
+      merges.push_back(m);
+    }
+    jobs.push_back(StreamJob{&P, x[i], nullptr, static_cast<char*>(saved[i]), y[i], nullptr, nullptr});
+  }
+  if (jobs.empty()) return TTC_OK;  // every layer has T == 0
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (!merges.empty()) launch_merge_batch(merges.data(), (int)merges.size(), s);
+  launch_stream_jobs<true>(jobs.data(), (int)jobs.size(), s);
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_bwd_data_batch(int32_t n, const tt_linear_desc* const* descs, const int64_t* T,
+                                               const void* const* x, const void* const* dy,
+                                               const float* const* const* G, const float* const* const* D,
+                                               const void* const* saved, const size_t* saved_bytes,
+                                               void* const* dx, void* const* scratch, const size_t* scratch_bytes,
+                                               ttc_stream_t stream) {
+  if (n < 0) return TTC_ERR_SHAPE;
+  if (n == 0) return TTC_OK;
+  if (!descs || !T || !x || !dy || !G || !D || !saved || !saved_bytes || !scratch || !scratch_bytes)
+    return TTC_ERR_NULL;
+  std::vector<LinearPlan> plans(n);
+  std::vector<StreamJob> jobs;
+  for (int i = 0; i < n; ++i) {
+    if (!descs[i]) return TTC_ERR_NULL;
+    LinearPlan& P = plans[i];
+    ttc_status st = bwd_checks(descs[i], T[i], G[i], D[i], &P);
+    if (st != TTC_OK) return st;
+    if (T[i] == 0) continue;
+    void* dxi = dx ? dx[i] : nullptr;
+    if ((st = buffer_checks(P, true, x[i], dy[i], dxi, saved[i], saved_bytes[i], scratch[i], scratch_bytes[i])) !=
+        TTC_OK)
+      return st;
+    if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
+    jobs.push_back(StreamJob{&P, x[i], dy[i], const_cast<char*>(static_cast<const char*>(saved[i])), nullptr, dxi,
+                             static_cast<char*>(scratch[i])});
+  }
+  if (jobs.empty()) return TTC_OK;  // every layer has T == 0
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_stream_jobs<false>(jobs.data(), (int)jobs.size(), s);
   return hip_status();
 }
 

@@ -18,8 +18,10 @@ from . import (
     tt_linear_bwd_cores,
     tt_linear_bwd_cores_batch,
     tt_linear_bwd_data,
+    tt_linear_bwd_data_batch,
     tt_linear_bwd_split,
     tt_linear_fwd,
+    tt_linear_fwd_batch,
     tt_linear_prepare,
     tt_linear_prepare_batch,
     tt_linear_workspace,
@@ -166,6 +168,35 @@ def prepare_batch(mods, T, cores, D, saved):
                             [[t.data_ptr() for t in c] for c in cores], [[v.data_ptr() for v in d] for d in D],
                             [b.data_ptr() for b in saved], [b.numel() for b in saved], _stream())
 
+
+def forward_batch(mods, xs, cores, D, outs, saved, prepared=False):
+    """TTLinear.forward of several independent layers in one batched call on
+    the current stream (lists with one entry per layer; outputs and saved
+    buffers are required)."""
+    for m, x, c, d, y in zip(mods, xs, cores, D, outs):
+        T = int(x.shape[0])
+        _need(x, "x", m.dtype, (T, m.n_in))
+        _need(y, "out", m.dtype, (T, m.n_out))
+        m._check_chain(c, d)
+    tt_linear_fwd_batch([m.desc_prepared if prepared else m.desc for m in mods], [int(x.shape[0]) for x in xs],
+                        [x.data_ptr() for x in xs], [[t.data_ptr() for t in c] for c in cores],
+                        [[v.data_ptr() for v in d] for d in D], [y.data_ptr() for y in outs],
+                        [b.data_ptr() for b in saved], [b.numel() for b in saved], _stream())
+
+
+def backward_data_batch(mods, xs, dys, cores, D, saved, scratch, dxs):
+    """TTLinear.backward_data of several independent layers in one batched
+    call on the current stream; dxs entries may be None (dX skipped)."""
+    for m, x, dy, c, d in zip(mods, xs, dys, cores, D):
+        T = int(x.shape[0])
+        _need(x, "x", m.dtype, (T, m.n_in))
+        _need(dy, "dy", m.dtype, (T, m.n_out))
+        m._check_chain(c, d)
+    tt_linear_bwd_data_batch([m.desc for m in mods], [int(x.shape[0]) for x in xs], [x.data_ptr() for x in xs],
+                             [dy.data_ptr() for dy in dys], [[t.data_ptr() for t in c] for c in cores],
+                             [[v.data_ptr() for v in d] for d in D], [b.data_ptr() for b in saved],
+                             [b.numel() for b in saved], [None if t is None else t.data_ptr() for t in dxs],
+                             [b.data_ptr() for b in scratch], [b.numel() for b in scratch], _stream())
 
 def backward_cores_batch(mods, T, cores, D, saved, scratch, dG):
     """TTLinear.backward_cores for several layers in one batched call on the

@@ -176,6 +176,36 @@ def test_batch_calls_check_every_layer_before_launch():
     code = ttc.lib().tt_linear_prepare_batch(-1, None, None, None, None, None, None, None)
     assert code == 2
 
+
+def test_batched_streaming_calls_check_every_layer_before_launch():
+    d = _desc()
+    d2 = _desc(out_modes=(12, 16, 16))
+    sb, cb = ttc.tt_linear_workspace(d, 64)
+    sb2, cb2 = ttc.tt_linear_workspace(d2, 64)
+    G = [[16] * 6, [16] * 6]
+    D = [[16] * 5, [16] * 5]
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd_batch([d, d2], [64, 64], [16, 32], G, D, [48, 64], [80, 96], [sb, sb])
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd_batch([d, d2], [64, 64], [16, 32], G, D, [48, 72], [80, 96], [sb, sb2])
+    assert e.value.code == 5
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_fwd_batch([d, d2], [64, 64], [16, None], G, D, [48, 64], [80, 96], [sb, sb2])
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_data_batch([d, d2], [64, 64], [16, 32], [48, 64], G, D, [80, 96], [sb, sb2], None,
+                                     [112, 128], [cb, cb2 - 1])
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_bwd_data_batch([d, d2], [64, 64], [16, 32], [48, None], G, D, [80, 96], [sb, sb2], None,
+                                     [112, 128], [cb, cb2])
+    assert e.value.code == 1
+    # T = 0 layers are skipped; nothing to do
+    ttc.tt_linear_fwd_batch([d], [0], [None], [[16] * 6], [[16] * 5], [None], [None], [0])
+    ttc.tt_linear_bwd_data_batch([], [], [], [], [], [], [], [], None, [], [])
+    assert ttc.lib().tt_linear_fwd_batch(-1, None, None, None, None, None, None, None, None, None) == 2
+
 def _merged_macs(out_modes, in_modes, r, T):
     """Independent count: skinny GEMMs of the merged order plus the half merges."""
     n_out, n_in = 1, 1

@@ -301,6 +301,55 @@ def test_batched_prepare_and_core_gradients_match_single_layer_calls():
             for g in b["dG"]:
                 assert torch.all(g == 0.0)
 
+def test_batched_streaming_passes_match_single_layer_calls():
+    """tt_linear_fwd_batch and tt_linear_bwd_data_batch (then the batched core
+    gradients) over five same-form bf16 layers (two launches: four layers and
+    one), an FFN layer, an fp32 layer and a zero-token layer in one call give
+    bitwise the outputs of the single-layer calls."""
+    ttc = _ttc()
+    c2 = synth.config_layers(2, 30)
+    cases = [(c2[i % 4], "bf16", 257) for i in range(5)] + [(c2[5], "bf16", 257),
+                                                           (synth.config_layers(1, 30)[4], "f32", 130),
+                                                           (c2[0], "bf16", 0)]
+    mods, data, refs = [], [], []
+    for i, (spec, dt, T) in enumerate(cases):
+        layer = synth.make_tt_layer(2, 400 + i, spec, T, 0.40, dt)
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
+        cores, D, x, dy = _to_dev(layer, dt)
+        y, saved = mod.forward(x, cores, D)
+        dx, dG = mod.backward(x, dy, cores, D, saved)
+        torch.cuda.synchronize()
+        refs.append((y.clone(), dx.clone(), [g.clone() for g in dG]))
+        sb, cb = mod.workspace(T)
+        mods.append(mod)
+        data.append(dict(cores=cores, D=D, x=x, dy=dy, T=T,
+                         y=torch.full((T, spec.n_out), 3.0, dtype=tdt, device="cuda"),
+                         dx=torch.full((T, spec.n_in), 3.0, dtype=tdt, device="cuda"),
+                         saved=torch.empty(max(sb, 256), dtype=torch.uint8, device="cuda"),
+                         scratch=torch.empty(max(cb, 256), dtype=torch.uint8, device="cuda"),
+                         dG=[torch.full(sh, 9.0, device="cuda") for sh in mod.core_shapes]))
+    cur = torch.cuda.current_stream().cuda_stream
+    Ts = [b["T"] for b in data]
+    Gp = [[c.data_ptr() for c in b["cores"]] for b in data]
+    Dp = [[v.data_ptr() for v in b["D"]] for b in data]
+    ttc.tt_linear_fwd_batch([m.desc for m in mods], Ts, [b["x"].data_ptr() for b in data], Gp, Dp,
+                            [b["y"].data_ptr() for b in data], [b["saved"].data_ptr() for b in data],
+                            [b["saved"].numel() for b in data], cur)
+    ttc.tt_linear_bwd_data_batch([m.desc for m in mods], Ts, [b["x"].data_ptr() for b in data],
+                                 [b["dy"].data_ptr() for b in data], Gp, Dp, [b["saved"].data_ptr() for b in data],
+                                 [b["saved"].numel() for b in data], [b["dx"].data_ptr() for b in data],
+                                 [b["scratch"].data_ptr() for b in data], [b["scratch"].numel() for b in data], cur)
+    ttc.tt_linear_bwd_cores_batch([m.desc for m in mods], Ts, Gp, Dp, [b["saved"].data_ptr() for b in data],
+                                  [b["saved"].numel() for b in data], [[g.data_ptr() for g in b["dG"]] for b in data],
+                                  [b["scratch"].data_ptr() for b in data], [b["scratch"].numel() for b in data], cur)
+    torch.cuda.synchronize()
+    for i, ((ry, rdx, rdG), b) in enumerate(zip(refs, data)):
+        assert torch.equal(b["y"], ry), i
+        assert torch.equal(b["dx"], rdx), i
+        for g, r in zip(b["dG"], rdG):
+            assert torch.equal(g, r), i
+
 @pytest.mark.parametrize("deferred", [False, True])
 def test_graph_replay_two_streams_matches_eager(deferred):
     """A captured two-layer step (merges and core-gradient tails on a side
@@ -342,12 +391,19 @@ def test_graph_replay_two_streams_matches_eager(deferred):
                     e = torch.cuda.Event()
                     e.record(side)
                     evs.append(e)
-        for mod, e, (cores, D, x, dy, b) in zip(mods, evs, data):
-            main.wait_event(e)
-            mod.forward(x, cores, D, out=b["y"], saved=b["saved"], prepared=True)
         if deferred:
-            for mod, (cores, D, x, dy, b) in reversed(list(zip(mods, data))):
-                mod.backward_data(x, dy, cores, D, b["saved"], b["scratch"], dx=b["dx"])
+            main.wait_event(evs[0])
+            ttc.forward_batch(mods, [d[2] for d in data], [d[0] for d in data], [d[1] for d in data],
+                              [d[4]["y"] for d in data], [d[4]["saved"] for d in data], prepared=True)
+        else:
+            for mod, e, (cores, D, x, dy, b) in zip(mods, evs, data):
+                main.wait_event(e)
+                mod.forward(x, cores, D, out=b["y"], saved=b["saved"], prepared=True)
+        if deferred:
+            ttc.backward_data_batch(mods[::-1], [d[2] for d in data][::-1], [d[3] for d in data][::-1],
+                                    [d[0] for d in data][::-1], [d[1] for d in data][::-1],
+                                    [d[4]["saved"] for d in data][::-1], [d[4]["scratch"] for d in data][::-1],
+                                    [d[4]["dx"] for d in data][::-1])
             side.wait_stream(main)
             with torch.cuda.stream(side):
                 ttc.backward_cores_batch(mods, T, [d[0] for d in data], [d[1] for d in data],
