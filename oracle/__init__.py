@@ -32,6 +32,9 @@ invariants).
 """
 
 from .tt_linear import (  # noqa: F401
+    chain_link_grads,
+    early_stage_grads,
+    tt_linear_link_grads,
     chain_tensor,
     chain_prefix,
     chain_suffix,

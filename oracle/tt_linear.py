@@ -149,3 +149,56 @@ def tt_linear_core_grads(x, dy, cores, D, in_first: bool = False) -> list:
     dW = _f64(dy).T @ _f64(x)
     dT = dW.T if in_first else dW           # back to the chain's own layout
     return chain_core_grads(dT.reshape(-1), cores, D)
+
+
+def chain_link_grads(dT, cores, D) -> list:
+    """Gradient of <dT, T(G, D)> with respect to every link diagonal D_k.
+
+    T is linear in each diagonal: T = P_k' diag(D_k) S_k' with P_k' the chain
+    product up to and including core k (its own left diagonals applied) and
+    S_k' the product from core k+1 on (its own right diagonals applied), so
+        dD_k[b] = sum_{alpha, beta} P_k'[alpha, b] dT[alpha, beta] S_k'[b, beta]
+    with dT viewed as (prod n_<=k, prod n_>k).  This is the exact gradient for
+    every entry, zero entries included.
+    """
+    _check_chain(cores, D)
+    dT = _f64(dT).reshape(-1)
+    d = len(cores)
+    grads = []
+    for k in range(d - 1):
+        G = _f64(cores[k])
+        r0, n, r1 = G.shape
+        P = (chain_prefix(cores, D, k) @ G.reshape(r0, n * r1)).reshape(-1, r1)
+        Gn = _f64(cores[k + 1])
+        q0, m, q1 = Gn.shape
+        S = (Gn.reshape(q0 * m, q1) @ chain_suffix(cores, D, k + 1)).reshape(q0, -1)
+        dTk = dT.reshape(P.shape[0], S.shape[1])
+        grads.append(np.einsum("xb,xy,by->b", P, dTk, S))
+    return grads
+
+
+def tt_linear_link_grads(x, dy, cores, D, in_first: bool = False) -> list:
+    """dL/dD_k for L = <dY, x W^T>: dW = dY^T x, then chain_link_grads."""
+    dW = _f64(dy).T @ _f64(x)
+    dT = dW.T if in_first else dW
+    return chain_link_grads(dT.reshape(-1), cores, D)
+
+
+def early_stage_grads(x, dy, cores, D, gamma: float, beta: float, in_first: bool = False):
+    """Gradients of the early-stage objective L + gamma * S^(D) + beta * ||G||^2
+    (project page, section "Learn the ranks while training").
+
+    Readings (listed in the design doc): S^(D) is the l1 norm of all link diagonals,
+    sum_k |D_k|_1, and ||G||^2 the squared Frobenius norm of all cores.  An
+    entry with D_k[b] == 0 is a pruned slice: its diagonal gradient is reported
+    as 0 (the l1 subgradient at 0 is taken as 0 as well).  Returns
+    (dG_k + 2 beta G_k for every core, dD_k for every link).
+    """
+    dG = tt_linear_core_grads(x, dy, cores, D, in_first)
+    dD = tt_linear_link_grads(x, dy, cores, D, in_first)
+    dG = [g + 2.0 * beta * _f64(c) for g, c in zip(dG, cores)]
+    out = []
+    for g, v in zip(dD, D):
+        v = _f64(v)
+        out.append(np.where(v != 0.0, g + gamma * np.sign(v), 0.0))
+    return dG, out

@@ -252,3 +252,89 @@ def test_hand_worked_golden():
     assert np.array_equal(dX, np.array(g["dX"]))
     for k in range(2):
         assert np.array_equal(dG[k], np.array(g["dG"][k]))
+
+
+# ---- link diagonals: dL/dD_k and the early-stage objective ---------------------
+
+@pytest.mark.parametrize("in_first", [False, True])
+def test_link_grads_by_unit_probes(in_first):
+    """f(D) = <dY, x W(G, D)^T> is linear in each diagonal: setting D_k to the
+    unit vector e_b (the other diagonals fixed) gives dL/dD_k[b] exactly, for
+    zero entries of D_k as well (the brute-force W is independent code)."""
+    rng = np.random.default_rng(17)
+    out_modes, in_modes = (2, 3), (3, 2)
+    modes = list(in_modes) + list(out_modes) if in_first else list(out_modes) + list(in_modes)
+    ranks = [1, 2, 4, 2, 1]
+    cores, D = _rand_chain(rng, modes, ranks, zero_frac=0.34)
+    x = rng.standard_normal((5, 6))
+    dy = rng.standard_normal((5, 6))
+    dD = oracle.tt_linear_link_grads(x, dy, cores, D, in_first)
+    assert len(dD) == len(D)
+    for k in range(len(D)):
+        for b in range(len(D[k])):
+            probe = [v.copy() for v in D]
+            probe[k][:] = 0.0
+            probe[k][b] = 1.0
+            want = _loss(x, dy, out_modes, in_modes, cores, probe, in_first)
+            assert abs(dD[k][b] - want) <= 1e-12 * (1.0 + abs(want)), (k, b)
+
+
+def test_link_grads_finite_difference_and_core_identity():
+    """Exact linear finite differences along a random direction, and the
+    identity sum_{a,m} G_k[a,m,b] dG_k[a,m,b] = D_k[b] dL/dD_k[b]: the core
+    gradient of core k carries D_k[b] as a factor of its slice b."""
+    rng = np.random.default_rng(18)
+    out_modes, in_modes = (3, 2, 2), (2, 3, 2)
+    ranks = [1, 3, 4, 3, 4, 3, 1]
+    cores, D = _rand_chain(rng, list(out_modes) + list(in_modes), ranks, zero_frac=0.25)
+    x = rng.standard_normal((6, 12))
+    dy = rng.standard_normal((6, 12))
+    _, dG = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D)
+    dD = oracle.tt_linear_link_grads(x, dy, cores, D)
+    f0 = _loss(x, dy, out_modes, in_modes, cores, D)
+    for k in range(len(D)):
+        E = rng.standard_normal(D[k].shape)
+        trial = [v.copy() for v in D]
+        trial[k] = D[k] + E
+        df = _loss(x, dy, out_modes, in_modes, cores, trial) - f0
+        assert abs(df - np.sum(dD[k] * E)) <= 1e-10 * (1.0 + abs(df))
+        lhs = np.einsum("amb,amb->b", cores[k], dG[k])
+        assert np.allclose(lhs, D[k] * dD[k], rtol=1e-12, atol=1e-12 * np.abs(lhs).max())
+
+
+def test_early_stage_grads_central_differences():
+    """Gradients of J = L + gamma * sum_k |D_k|_1 + beta * sum_k ||G_k||^2 by
+    central differences, which are exact here: L is linear in each core and
+    diagonal, the penalty on the cores is quadratic, and the l1 term is linear
+    as long as the step keeps every live entry's sign.  Dead entries (D = 0,
+    pruned slices) report 0."""
+    rng = np.random.default_rng(19)
+    out_modes, in_modes = (2, 3), (3, 2)
+    ranks = [1, 3, 2, 3, 1]
+    cores, D = _rand_chain(rng, list(out_modes) + list(in_modes), ranks, zero_frac=0.34)
+    x = rng.standard_normal((4, 6))
+    dy = rng.standard_normal((4, 6))
+    gamma, beta = 0.3, 0.05
+
+    def J(cs, ds):
+        return (_loss(x, dy, out_modes, in_modes, cs, ds) + gamma * sum(np.abs(v).sum() for v in ds)
+                + beta * sum((c * c).sum() for c in cs))
+
+    dG, dD = oracle.early_stage_grads(x, dy, cores, D, gamma, beta)
+    h = 1e-3
+    for k in range(len(cores)):
+        E = rng.standard_normal(cores[k].shape)
+        cp, cm = list(cores), list(cores)
+        cp[k] = cores[k] + h * E
+        cm[k] = cores[k] - h * E
+        df = (J(cp, D) - J(cm, D)) / (2 * h)
+        assert abs(df - np.sum(dG[k] * E)) <= 1e-8 * (1.0 + abs(df)), k
+    for k in range(len(D)):
+        live = D[k] != 0.0
+        E = rng.standard_normal(D[k].shape) * live  # dead entries stay at 0
+        dp, dm = [v.copy() for v in D], [v.copy() for v in D]
+        dp[k] = D[k] + h * E
+        dm[k] = D[k] - h * E
+        df = (J(cores, dp) - J(cores, dm)) / (2 * h)
+        assert abs(df - np.sum(dD[k] * E)) <= 1e-8 * (1.0 + abs(df)), k
+        assert np.all(dD[k][~live] == 0.0)
