@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "TT-linear fwd+bwd tokens/sec at d=768 r=30; achieved HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+RG_GAMMA, RG_BETA = 1e-3, 1e-5  # early-stage penalty weights for --rank-grads (values do not change the cost)
 
 
 def parse():
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--single-stream", action="store_true",
                     help="run merges and core-gradient tails on the main stream too (no overlap)")
     ap.add_argument("--no-ttm", action="store_true", help="time the TT-linear layers only")
+    ap.add_argument("--rank-grads", action="store_true",
+                    help="also compute every layer's early-stage gradients (diagonals dD, penalties) after its dG")
     ap.add_argument("--no-qkv-batch", action="store_true",
                     help="one launch per layer for the Q, K and V projections instead of one batched launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -189,6 +192,7 @@ def main():
             "y": torch.empty((T, spec.n_out), dtype=tdt, device=dev),
             "dx": torch.empty((T, spec.n_in), dtype=tdt, device=dev),
             "dG": [torch.empty(s, dtype=torch.float32, device=dev) for s in mod.core_shapes],
+            "dD": [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in D],
             "saved": torch.empty(sb, dtype=torch.uint8, device=dev),
         })
         keep = {"spec": spec, "cores": L["cores"], "D": L["D"]}
@@ -297,6 +301,9 @@ def main():
             ttc.backward_cores_batch(mods[::-1], T, all_cores[::-1], all_D[::-1],
                                      [L["saved"] for L in layers][::-1], [L["scratch"] for L in layers][::-1],
                                      [L["dG"] for L in layers][::-1])
+            if args.rank_grads:
+                ttc.rank_grads_batch(mods, all_cores, all_D, [L["dG"] for L in layers], [L["dD"] for L in layers],
+                                     RG_GAMMA, RG_BETA)
         main.wait_stream(side)
 
     step = step_single if args.single_stream else step_overlap
@@ -423,6 +430,7 @@ def main():
             "layers": len(specs),
             "launch": "eager" if graph is None else "hip_graph_replay",
             "qkv_batched": not (args.no_qkv_batch or args.single_stream),
+            "rank_grads": bool(args.rank_grads and not args.single_stream),
             "streams": 1 if args.single_stream else 2,
             "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "
                                                   "fp32, Zipf(1.1) ids",

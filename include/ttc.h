@@ -268,6 +268,38 @@ ttc_status tt_linear_bwd_data_batch(int32_t n, const tt_linear_desc* const* desc
                                     ttc_stream_t stream);
 
 /*
+ * Gradients of the early-stage objective of the project page (section "Learn
+ * the ranks while training"): L(G, D) + gamma * S(D) + beta * ||G||^2, read as
+ * S(D) = sum over the layer's links of |D_k|_1 (the l1 stand-in for the link
+ * ranks) and ||G||^2 = sum_k ||G_k||_F^2.
+ *   G, D - as for tt_linear_fwd (chain order)
+ *   dG   - in: dL/dG_k as written by tt_linear_bwd / tt_linear_bwd_cores for
+ *          these G and D; out: dL/dG_k + 2 beta G_k (in place)
+ *   dD   - host array of d-1 device pointers, fp32 vectors of length r_k,
+ *          overwritten: dL/dD_k[b] + gamma sign(D_k[b]); an entry with
+ *          D_k[b] == 0 is a pruned slice and gets exactly 0
+ * dL/dD_k[b] comes from dG_k: core k carries D_k[b] as a factor of its slice
+ * b, so sum_{a,m} G_k[a,m,b] dG_k[a,m,b] = D_k[b] dL/dD_k[b].  One small
+ * launch; fixed-order sums (bitwise reproducible).  Must run after the
+ * backward that wrote dG has completed on the device (same stream, or an
+ * event).  NaN gamma or beta gives TTC_ERR_SHAPE; errors are returned before
+ * any launch.
+ */
+ttc_status tt_linear_rank_grads(const tt_linear_desc* desc, const float* const* G,
+                                const float* const* D, float* const* dG,
+                                float* const* dD, float gamma, float beta,
+                                ttc_stream_t stream);
+/* The same for n layers in one launch (arrays of n entries, entry i the
+ * arguments of the single-layer call; same gamma and beta for all).  n == 0
+ * does nothing, n < 0 gives TTC_ERR_SHAPE; every layer is checked first. */
+ttc_status tt_linear_rank_grads_batch(int32_t n, const tt_linear_desc* const* descs,
+                                      const float* const* const* G,
+                                      const float* const* const* D,
+                                      float* const* const* dG,
+                                      float* const* const* dD, float gamma,
+                                      float beta, ttc_stream_t stream);
+
+/*
  * Planner report (host-only): writes a NUL-terminated text into buf (at most
  * n bytes) with the chosen path and the modelled flops / bytes of the merged,
  * sequential and dense paths for T tokens.

@@ -47,6 +47,8 @@ EXPORTS = [
     "tt_linear_bwd_cores_batch",
     "tt_linear_fwd_batch",
     "tt_linear_bwd_data_batch",
+    "tt_linear_rank_grads",
+    "tt_linear_rank_grads_batch",
     "tt_linear_path_cost",
     "ttm_embed_workspace",
     "ttm_embed_fwd",
@@ -120,6 +122,9 @@ def lib() -> ctypes.CDLL:
         "tt_linear_prepare": [D, _I64, pp, pp, _P, _SZ, _P],
         "tt_linear_prepare_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), ctypes.POINTER(pp),
                                     ctypes.POINTER(pp), pp, ctypes.POINTER(_SZ), _P],
+        "tt_linear_rank_grads": [D, pp, pp, pp, pp, ctypes.c_float, ctypes.c_float, _P],
+        "tt_linear_rank_grads_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(pp), ctypes.POINTER(pp),
+                                       ctypes.POINTER(pp), ctypes.POINTER(pp), ctypes.c_float, ctypes.c_float, _P],
         "tt_linear_fwd_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), pp, ctypes.POINTER(pp),
                                 ctypes.POINTER(pp), pp, pp, ctypes.POINTER(_SZ), _P],
         "tt_linear_bwd_data_batch": [ctypes.c_int32, ctypes.POINTER(D), ctypes.POINTER(_I64), pp, pp,
@@ -315,6 +320,21 @@ def tt_linear_bwd_data_batch(descs, T, x, dy, G, D, saved, saved_bytes, dx, scra
     _check("tt_linear_bwd_data_batch", code)
 
 
+def tt_linear_rank_grads(desc, G, D, dG, dD, gamma=0.0, beta=0.0, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    dg, _dga = _ptrs(dG) if dG is not None else (None, None)
+    ddd, _ddda = _ptrs(dD) if dD is not None else (None, None)
+    code = lib().tt_linear_rank_grads(ctypes.byref(desc), g, dd, dg, ddd, float(gamma), float(beta), stream)
+    _check("tt_linear_rank_grads", code)
+
+
+def tt_linear_rank_grads_batch(descs, G, D, dG, dD, gamma=0.0, beta=0.0, stream=0):
+    dp, _ta, (ga, da, gg, ddd), _keep = _batch_args(descs, [0] * len(descs), [G, D, dG, dD])
+    code = lib().tt_linear_rank_grads_batch(len(descs), dp, ga, da, gg, ddd, float(gamma), float(beta), stream)
+    _check("tt_linear_rank_grads_batch", code)
+
+
 def tt_linear_explain(desc: TTLinearDesc, T: int) -> str:
     buf = ctypes.create_string_buffer(1024)
     _check("tt_linear_explain", lib().tt_linear_explain(ctypes.byref(desc), T, buf, 1024))
@@ -382,5 +402,6 @@ from .torch_api import (  # noqa: E402,F401
     backward_cores_batch,
     backward_data_batch,
     forward_batch,
+    rank_grads_batch,
     prepare_batch,
 )

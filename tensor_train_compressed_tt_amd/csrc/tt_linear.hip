@@ -1416,6 +1416,78 @@ static Gemm right_dN(const LinearPlan& P, const float* const* G, const float* co
   return g;
 }
 
+// ------------------------------------------------------------------------------
+// gradients of the rank-control diagonals and the early-stage penalties
+// ------------------------------------------------------------------------------
+// Core k (chain position) carries the diagonal D_k of its right link as a
+// factor of its slice b, so sum_{a,m} G_k[a,m,b] dG_k[a,m,b] = D_k[b] dL/dD_k[b]
+// (project page, "Learn the ranks while training": a diagonal on every link).
+// One work-group per core of a list (cores of one or more layers): thread t
+// takes entry b = t mod r_k of row group t / r_k, so consecutive lanes read
+// consecutive floats of a row (a, m); the row groups' sums are added in group
+// order through LDS.  dD_k[b] = sum / D_k[b] + gamma sign(D_k[b]), and 0 for a
+// pruned entry (D_k[b] == 0).  Then, after every read of dG_k, the work-group
+// adds 2 beta G_k to dG_k.  The last core of a chain has no right link and
+// only takes the penalty.
+struct CoreJob {
+  const float* G;
+  const float* D;  // right link, or null
+  float* dG;
+  float* dD;       // right link, or null
+  int rows;        // r_{k-1} n_k
+  int r1;
+};
+constexpr int kMaxCoreJobs = 40;
+struct RankGradArgs {
+  CoreJob j[kMaxCoreJobs];
+  int n;
+  float gamma, beta;
+};
+static_assert(sizeof(RankGradArgs) <= 2048, "RankGradArgs too large for a kernel argument");
+
+constexpr int kRankGradThreads = 1024;
+__global__ __launch_bounds__(kRankGradThreads) void k_rank_grads(RankGradArgs a) {
+  __shared__ float part[kRankGradThreads];
+  const CoreJob& c = a.j[blockIdx.x];
+  const int r1 = c.r1, rows = c.rows;
+  if (c.D) {
+    const int ng = (int)blockDim.x / r1;  // row groups (r1 <= 128)
+    const int b = (int)threadIdx.x % r1, grp = (int)threadIdx.x / r1;
+    if (grp < ng) {
+      // eight rows in flight per thread, eight partial sums added in a fixed order
+      float acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+      int i = grp;
+      for (; i + 7 * ng < rows; i += 8 * ng) {
+        float gv[8], dv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          gv[u] = c.G[(int64_t)(i + u * ng) * r1 + b];
+          dv[u] = c.dG[(int64_t)(i + u * ng) * r1 + b];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(gv[u], dv[u], acc[u]);
+      }
+      for (; i < rows; i += ng) acc[0] = fmaf(c.G[(int64_t)i * r1 + b], c.dG[(int64_t)i * r1 + b], acc[0]);
+      part[threadIdx.x] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < r1) {
+      float sum = 0.f;
+      for (int g = 0; g < ng; ++g) sum += part[g * r1 + threadIdx.x];
+      const float dv = c.D[threadIdx.x];
+      c.dD[threadIdx.x] = dv != 0.f ? sum / dv + (dv > 0.f ? a.gamma : -a.gamma) : 0.f;
+    }
+  }
+  if (a.beta != 0.f) {
+    __syncthreads();
+    const int64_t ne = (int64_t)rows * r1;
+    const float tb = 2.f * a.beta;
+    for (int64_t i = threadIdx.x; i < ne; i += blockDim.x) c.dG[i] = fmaf(tb, c.G[i], c.dG[i]);
+  }
+}
+
 __global__ void k_zero(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -2265,6 +2337,69 @@ extern "C" ttc_status tt_linear_bwd_data_batch(int32_t n, const tt_linear_desc* 
   (void)hipGetLastError();
   launch_stream_jobs<false>(jobs.data(), (int)jobs.size(), s);
   return hip_status();
+}
+
+namespace ttc {
+static ttc_status rank_grads_checks(const tt_linear_desc* desc, const float* const* G, const float* const* D,
+                                    float* const* dG, float* const* dD, LinearPlan* P) {
+  ttc_status st = make_linear_plan(desc, 0, P);
+  if (st != TTC_OK) return st;
+  if ((st = check_chain(*P, G, D)) != TTC_OK) return st;
+  if ((st = grads_checks(*P, dG)) != TTC_OK) return st;
+  if (P->d > 1 && !dD) return TTC_ERR_NULL;
+  for (int k = 0; k < P->d - 1; ++k)
+    if (!dD[k]) return TTC_ERR_NULL;
+  return TTC_OK;
+}
+}  // namespace ttc
+
+extern "C" ttc_status tt_linear_rank_grads_batch(int32_t n, const tt_linear_desc* const* descs,
+                                                 const float* const* const* G, const float* const* const* D,
+                                                 float* const* const* dG, float* const* const* dD, float gamma,
+                                                 float beta, ttc_stream_t stream) {
+  if (n < 0) return TTC_ERR_SHAPE;
+  if (!(gamma == gamma) || !(beta == beta)) return TTC_ERR_SHAPE;  // NaN penalty weights
+  if (n == 0) return TTC_OK;
+  if (!descs || !G || !D || !dG || !dD) return TTC_ERR_NULL;
+  std::vector<CoreJob> jobs;
+  for (int i = 0; i < n; ++i) {
+    if (!descs[i]) return TTC_ERR_NULL;
+    LinearPlan P;
+    const ttc_status st = rank_grads_checks(descs[i], G[i], D[i], dG[i], dD[i], &P);
+    if (st != TTC_OK) return st;
+    for (int k = 0; k < P.d; ++k) {
+      const bool link = k < P.d - 1;
+      if (!link && beta == 0.f) continue;  // nothing to do for the last core
+      CoreJob c;
+      c.G = G[i][k];
+      c.D = link ? D[i][k] : nullptr;
+      c.dG = dG[i][k];
+      c.dD = link ? dD[i][k] : nullptr;
+      c.rows = P.ranks[k] * P.modes[k];
+      c.r1 = P.ranks[k + 1];
+      jobs.push_back(c);
+    }
+  }
+  if (jobs.empty()) return TTC_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  for (size_t j0 = 0; j0 < jobs.size(); j0 += kMaxCoreJobs) {
+    RankGradArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n = (int)std::min<size_t>(kMaxCoreJobs, jobs.size() - j0);
+    for (int q = 0; q < a.n; ++q) a.j[q] = jobs[j0 + q];
+    a.gamma = gamma;
+    a.beta = beta;
+    TraceScope ts("rank_grads", s);
+    TTC_LAUNCH(k_rank_grads, dim3((unsigned)a.n), dim3(kRankGradThreads), 0, s, a);
+  }
+  return hip_status();
+}
+
+extern "C" ttc_status tt_linear_rank_grads(const tt_linear_desc* desc, const float* const* G, const float* const* D,
+                                           float* const* dG, float* const* dD, float gamma, float beta,
+                                           ttc_stream_t stream) {
+  return tt_linear_rank_grads_batch(1, &desc, &G, &D, &dG, &dD, gamma, beta, stream);
 }
 
 extern "C" ttc_status tt_linear_explain(const tt_linear_desc* desc, int64_t T, char* buf, size_t n) {

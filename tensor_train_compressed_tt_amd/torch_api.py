@@ -24,6 +24,8 @@ from . import (
     tt_linear_fwd_batch,
     tt_linear_prepare,
     tt_linear_prepare_batch,
+    tt_linear_rank_grads,
+    tt_linear_rank_grads_batch,
     tt_linear_workspace,
     ttm_embed_bwd,
     ttm_embed_fwd,
@@ -159,6 +161,19 @@ class TTLinear:
                             scratch.numel(), _stream())
         return dG
 
+    def rank_grads(self, cores, D, dG, gamma=0.0, beta=0.0, dD=None):
+        """Early-stage gradients on the current stream: returns dD (one fp32
+        vector per link) and adds 2 beta G_k to dG in place (see
+        tt_linear_rank_grads)."""
+        self._check_chain(cores, D)
+        for g, s in zip(dG, self.core_shapes):
+            _need(g, "dG", torch.float32, s)
+        if dD is None:
+            dD = [torch.empty(v.shape, dtype=torch.float32, device=v.device) for v in D]
+        tt_linear_rank_grads(self.desc, [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
+                             [g.data_ptr() for g in dG], [v.data_ptr() for v in dD], gamma, beta, _stream())
+        return dD
+
 def prepare_batch(mods, T, cores, D, saved):
     """TTLinear.prepare for several layers in one batched call on the current
     stream (lists with one entry per layer; `saved` buffers are required)."""
@@ -167,6 +182,7 @@ def prepare_batch(mods, T, cores, D, saved):
     tt_linear_prepare_batch([m.desc for m in mods], [T] * len(mods),
                             [[t.data_ptr() for t in c] for c in cores], [[v.data_ptr() for v in d] for d in D],
                             [b.data_ptr() for b in saved], [b.numel() for b in saved], _stream())
+
 
 
 def forward_batch(mods, xs, cores, D, outs, saved, prepared=False):
@@ -266,3 +282,14 @@ class TTMEmbedding:
                       None if D is None else [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
                       [g.data_ptr() for g in dF], scratch.data_ptr(), scratch.numel(), _stream())
         return dF
+
+
+def rank_grads_batch(mods, cores, D, dG, dD, gamma=0.0, beta=0.0):
+    """TTLinear.rank_grads for several layers in one launch on the current stream."""
+    for m, c, d, g in zip(mods, cores, D, dG):
+        m._check_chain(c, d)
+        for t, s in zip(g, m.core_shapes):
+            _need(t, "dG", torch.float32, s)
+    tt_linear_rank_grads_batch([m.desc for m in mods], [[t.data_ptr() for t in c] for c in cores],
+                               [[v.data_ptr() for v in d] for d in D], [[t.data_ptr() for t in g] for g in dG],
+                               [[v.data_ptr() for v in dd] for dd in dD], gamma, beta, _stream())

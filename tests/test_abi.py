@@ -206,6 +206,21 @@ def test_batched_streaming_calls_check_every_layer_before_launch():
     ttc.tt_linear_bwd_data_batch([], [], [], [], [], [], [], [], None, [], [])
     assert ttc.lib().tt_linear_fwd_batch(-1, None, None, None, None, None, None, None, None, None) == 2
 
+
+def test_rank_grads_errors_before_launch():
+    d = _desc()
+    G = [16] * 6
+    D = [16] * 5
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_rank_grads(d, G, D, [16] * 6, [16] * 4 + [0], 0.1, 0.0)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_rank_grads(d, G, D, [16] * 5 + [0], [16] * 5, 0.1, 0.0)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_rank_grads(d, G, D, [16] * 6, [16] * 5, float("nan"), 0.0)
+    assert e.value.code == 2
+
 def _merged_macs(out_modes, in_modes, r, T):
     """Independent count: skinny GEMMs of the merged order plus the half merges."""
     n_out, n_in = 1, 1

@@ -476,3 +476,78 @@ def test_config4_full_tokens_sampled_rows():
     for k, v in enumerate(layer["D"]):
         dead = np.flatnonzero(v == 0)
         assert np.all(dG[k][:, :, dead] == 0.0) and np.all(dG[k + 1][dead, :, :] == 0.0)
+
+
+# ---- early-stage gradients: link diagonals and penalties -------------------------
+
+def _rank_grads_case(spec, layer, dtype, gamma, beta):
+    ttc = _ttc()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
+    cores, D, x, dy = _to_dev(layer, dtype)
+    y, saved = mod.forward(x, cores, D)
+    _, dG = mod.backward(x, dy, cores, D, saved)
+    dD = mod.rank_grads(cores, D, dG, gamma, beta)
+    torch.cuda.synchronize()
+    xr = layer["x"].astype(np.float64)
+    dyr = layer["dy"].astype(np.float64)
+    dGr, dDr = oracle.early_stage_grads(xr, dyr, layer["cores"], layer["D"], gamma, beta, spec.in_first)
+    tol = TOL[dtype]
+    errs = {f"dG{k}": _rel(g.cpu().numpy(), r) for k, (g, r) in enumerate(zip(dG, dGr))}
+    errs.update({f"dD{k}": _rel(v.cpu().numpy(), r) for k, (v, r) in enumerate(zip(dD, dDr))})
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"rel-L2 above {tol}: {bad} (all: {errs})"
+    for v, d in zip(dD, layer["D"]):
+        assert np.all(v.cpu().numpy()[d == 0] == 0.0), "pruned entry of dD not exactly 0"
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gamma,beta", [(0.0, 0.0), (0.02, 1e-3)])
+def test_rank_grads_config0(dtype, gamma, beta):
+    spec = synth.config_layers(0)[0]
+    layer = synth.make_tt_layer(0, 5, spec, 64, 0.25, dtype)
+    print(_rank_grads_case(spec, layer, dtype, gamma, beta))
+
+
+@pytest.mark.parametrize("in_first", [False, True])
+@pytest.mark.parametrize("modes", [((2, 3), (3, 2)), ((5,), (7,)), ((2, 2, 2, 2), (3,))])
+def test_rank_grads_chain_orders_and_lengths(in_first, modes):
+    spec = synth.LayerSpec("rg", modes[0], modes[1], 3, in_first)
+    layer = synth.make_tt_layer(105, 3 * len(modes[0]) + int(in_first), spec, 90, 0.34, "f32")
+    _rank_grads_case(spec, layer, "f32", 0.1, 0.01)
+
+
+@pytest.mark.parametrize("li", [0, 4, 5])
+def test_rank_grads_config2_layers(li):
+    spec = synth.config_layers(2, 30)[li]
+    layer = synth.make_tt_layer(2, 500 + li, spec, 512, 0.40, "bf16")
+    _rank_grads_case(spec, layer, "bf16", 0.01, 1e-4)
+
+
+def test_rank_grads_batch_matches_single_layer_calls():
+    """tt_linear_rank_grads_batch over six layers (two launches of core lists
+    would be needed above forty cores; here one) gives bitwise the results of
+    per-layer calls, penalties included."""
+    ttc = _ttc()
+    specs = synth.config_layers(2, 16)
+    mods, args, single = [], [], []
+    for i, spec in enumerate(specs):
+        layer = synth.make_tt_layer(2, 600 + i, spec, 200, 0.40, "bf16")
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, torch.bfloat16, spec.in_first)
+        cores, D, x, dy = _to_dev(layer, "bf16")
+        y, saved = mod.forward(x, cores, D)
+        _, dG = mod.backward(x, dy, cores, D, saved)
+        dG2 = [g.clone() for g in dG]
+        dD1 = mod.rank_grads(cores, D, dG, 0.05, 1e-3)
+        mods.append(mod)
+        args.append((cores, D, dG2, [torch.empty_like(v) for v in D]))
+        single.append((dG, dD1))
+    ttc.rank_grads_batch(mods, [a[0] for a in args], [a[1] for a in args], [a[2] for a in args],
+                         [a[3] for a in args], 0.05, 1e-3)
+    torch.cuda.synchronize()
+    for (dG, dD1), (_, _, dG2, dD2) in zip(single, args):
+        for a, b in zip(dG, dG2):
+            assert torch.equal(a, b)
+        for a, b in zip(dD1, dD2):
+            assert torch.equal(a, b)
