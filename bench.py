@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--single-stream", action="store_true",
                     help="run merges and core-gradient tails on the main stream too (no overlap)")
     ap.add_argument("--no-ttm", action="store_true", help="time the TT-linear layers only")
+    ap.add_argument("--ttm-mode", default="dedup", choices=["dedup", "unique", "plain"],
+                    help="embedding lookup mode: distinct ids and shared prefixes (default), distinct ids only, "
+                         "or every token on its own")
     ap.add_argument("--rank-grads", action="store_true",
                     help="also compute every layer's early-stage gradients (diagonals dD, penalties) after its dG")
     ap.add_argument("--no-qkv-batch", action="store_true",
@@ -210,7 +213,8 @@ def main():
     if not args.no_ttm:
         w = synth.make_ttm(3, T=T)
         sp = w["spec"]
-        emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks)
+        emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks,
+                               mode={"dedup": 0, "unique": 1, "plain": 2}[args.ttm_mode])
         tsb, tcb = emb.workspace(T)
         ttm = {"emb": emb, "F": [torch.from_numpy(c).to(dev) for c in w["cores"]],
                "ids": torch.from_numpy(w["ids"]).to(dev), "dout": torch.from_numpy(w["dout"]).to(dev),
@@ -433,7 +437,7 @@ def main():
             "rank_grads": bool(args.rank_grads and not args.single_stream),
             "streams": 1 if args.single_stream else 2,
             "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "
-                                                  "fp32, Zipf(1.1) ids",
+                                                  f"fp32, Zipf(1.1) ids, lookup mode {args.ttm_mode}",
         },
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),

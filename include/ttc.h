@@ -321,7 +321,21 @@ typedef struct {
   int32_t dim_modes[TTC_TTM_MAX_MODES];   /* n_k; embedding dim = prod n_k <= 2^24   */
   int32_t ranks[TTC_TTM_MAX_MODES + 1];   /* r_0..r_d, r_0 = r_d = 1, r_k <= 128     */
   int32_t accumulate;                     /* bwd: 1 = add into dF, 0 = overwrite     */
+  int32_t mode;                           /* TTC_TTM_DEDUP (0), _UNIQUE or _PLAIN    */
 } ttm_embed_desc;
+
+/* Lookup modes (project page, section "Making small tensor operations fast on
+ * GPUs", and its figure comparing lookup variants): DEDUP evaluates every
+ * distinct id once and every distinct digit prefix once, shared by the ids
+ * that carry it (the proposed lookup); UNIQUE evaluates every distinct id
+ * once but shares no prefixes; PLAIN evaluates every token's row on its own.
+ * All three give bitwise the same rows and, within rounding, the same core
+ * gradients; they differ in work, in saved / scratch bytes (workspace query)
+ * and in speed.  The mode must be the same for the workspace query, the
+ * forward and the backward of one lookup.  Any other value: TTC_ERR_SHAPE. */
+#define TTC_TTM_DEDUP 0
+#define TTC_TTM_UNIQUE 1
+#define TTC_TTM_PLAIN 2
 
 /*
  * Bytes of the saved / scratch buffers for a lookup of T ids (host-only).

@@ -92,7 +92,11 @@ class TTMEmbedDesc(ctypes.Structure):
         ("dim_modes", ctypes.c_int32 * TTM_MAX_MODES),
         ("ranks", ctypes.c_int32 * (TTM_MAX_MODES + 1)),
         ("accumulate", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
     ]
+
+
+TTC_TTM_DEDUP, TTC_TTM_UNIQUE, TTC_TTM_PLAIN = 0, 1, 2
 
 
 _lib = None
@@ -187,7 +191,7 @@ def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=Fal
     return d
 
 
-def make_ttm_desc(vocab_modes, dim_modes, ranks, accumulate=False):
+def make_ttm_desc(vocab_modes, dim_modes, ranks, accumulate=False, mode=TTC_TTM_DEDUP):
     d = TTMEmbedDesc()
     d.d = len(vocab_modes)
     for i, n in enumerate(vocab_modes):
@@ -197,6 +201,7 @@ def make_ttm_desc(vocab_modes, dim_modes, ranks, accumulate=False):
     for i, r in enumerate(ranks):
         d.ranks[i] = int(r)
     d.accumulate = int(bool(accumulate))
+    d.mode = int(mode)
     return d
 
 

@@ -70,6 +70,7 @@ struct TtmPlan {
   int m[TTC_TTM_MAX_MODES], n[TTC_TTM_MAX_MODES], r[TTC_TTM_MAX_MODES + 1];
   int64_t V, N, T, nch;
   int kbits;                        // bits of the sort key (ids and the out-of-range marker V)
+  int mode;                         // TTC_TTM_DEDUP / _UNIQUE / _PLAIN
   int dbits[TTC_TTM_MAX_MODES];     // bits of the last digit of level l
   uint32_t Mgt[TTC_TTM_MAX_MODES];  // prod m_{>l}: prefix of level l = id / Mgt[l]
   int64_t cap[TTC_TTM_MAX_MODES];   // max nodes at level l = min(T, prod m_{<=l})
@@ -102,6 +103,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f) {
 struct SortArgs {
   const int64_t* ids;
   int n;
+  int mode;  // TTC_TTM_DEDUP / _UNIQUE / _PLAIN
   uint32_t V;
   int kbits;
   int d;
@@ -399,7 +401,8 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
     key[e] = i < n ? s_key[kb + 68 * e] : 0u;
     val[e] = i < n ? s_val[vb + 72 * e] : (uint16_t)0;
     const uint32_t kp = (i > 0 && i - 1 < n) ? s_key[kbm + 68 * e] : 0xffffffffu;
-    const bool fs = i < Tv && (i == 0 || key[e] != kp);
+    // a segment per distinct id, or (PLAIN) per valid token
+    const bool fs = i < Tv && (i == 0 || key[e] != kp || a.mode == TTC_TTM_PLAIN);
     const bool ps = i < Tv && (fs || (i & (kChunk - 1)) == 0);
     fsm |= (uint32_t)fs << e;
     psm |= (uint32_t)ps << e;
@@ -478,8 +481,11 @@ __global__ __launch_bounds__(kSortThreads) void k_ttm_sort(SortArgs a) {
       const bool prev = u > 0 && u - 1 < U;
       const uint32_t pp2 = prev ? fdiv(s_key[kbm + 68 * e], M) : 0xffffffffu;
       const uint32_t nxp = prev ? (uint32_t)s_val[vbm + 72 * e] : 0xffffffffu;
-      const bool ns = in && (u == 0 || pre[e] != pp2);
-      const bool cs = in && (u == 0 || (uint32_t)nx[e] != nxp);
+      // a new node per distinct prefix; without prefix sharing, a node per
+      // node of the level below
+      const bool share = a.mode == TTC_TTM_DEDUP;
+      const bool ns = in && (u == 0 || pre[e] != pp2 || !share);
+      const bool cs = in && (u == 0 || (uint32_t)nx[e] != nxp || !share);
       nsm |= (uint32_t)ns << e;
       csm |= (uint32_t)cs << e;
       cnt += (uint32_t)__popcll(__ballot(ns));
@@ -1050,6 +1056,8 @@ static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* 
   if (P->r[0] != 1 || P->r[d] != 1) return TTC_ERR_RANK;
   P->V = V;
   P->N = N;
+  if (desc->mode < TTC_TTM_DEDUP || desc->mode > TTC_TTM_PLAIN) return TTC_ERR_SHAPE;
+  P->mode = desc->mode;
   P->kbits = bit_length((uint64_t)V);
   P->nch = (T + kChunk - 1) / kChunk;
   {
@@ -1065,7 +1073,10 @@ static ttc_status make_ttm_plan(const ttm_embed_desc* desc, int64_t T, TtmPlan* 
     P->R[l] = nprod;
     mprod *= P->m[l];
     nprod *= P->n[l];
-    P->cap[l] = mprod < T ? mprod : T;
+    // most nodes of level l: distinct prefixes (DEDUP), distinct ids (UNIQUE)
+    // or tokens (PLAIN)
+    const int64_t lim = P->mode == TTC_TTM_DEDUP ? mprod : (P->mode == TTC_TTM_UNIQUE ? V : T);
+    P->cap[l] = lim < T ? lim : T;
     P->psz[l] = nprod * P->r[l + 1];
     const size_t blk = (size_t)P->n[l] * P->r[l + 1];
     P->lds_fwd[l] = 4 * ((size_t)P->R[l] * P->r[l] + (size_t)P->r[l] * (blk + 1));
@@ -1216,6 +1227,7 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
   sa.n = (int)T;
   sa.V = (uint32_t)P.V;
   sa.kbits = P.kbits;
+  sa.mode = P.mode;
   sa.d = P.d;
   sa.nch = (int)P.nch;
   for (int l = 0; l < P.d; ++l) {

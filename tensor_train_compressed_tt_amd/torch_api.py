@@ -228,7 +228,7 @@ def backward_cores_batch(mods, T, cores, D, saved, scratch, dG):
 class TTMEmbedding:
     """A TTM embedding table: cores F_k (r_{k-1}, m_k, n_k, r_k) fp32."""
 
-    def __init__(self, vocab_modes, dim_modes, ranks):
+    def __init__(self, vocab_modes, dim_modes, ranks, mode=0):
         self.vocab_modes = tuple(int(n) for n in vocab_modes)
         self.dim_modes = tuple(int(n) for n in dim_modes)
         self.ranks = tuple(int(r) for r in ranks)
@@ -236,9 +236,10 @@ class TTMEmbedding:
         self.dim = math.prod(self.dim_modes)
         self.core_shapes = [(self.ranks[k], self.vocab_modes[k], self.dim_modes[k], self.ranks[k + 1])
                             for k in range(len(self.vocab_modes))]
+        self.mode = int(mode)  # TTC_TTM_DEDUP / _UNIQUE / _PLAIN
 
     def desc(self, accumulate=False):
-        return make_ttm_desc(self.vocab_modes, self.dim_modes, self.ranks, accumulate)
+        return make_ttm_desc(self.vocab_modes, self.dim_modes, self.ranks, accumulate, self.mode)
 
     def workspace(self, T: int):
         return ttm_embed_workspace(self.desc(), T)

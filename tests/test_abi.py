@@ -326,6 +326,19 @@ def test_ttm_limits():
     assert e.value.code == 7
 
 
+def test_ttm_lookup_modes_size_their_workspace():
+    """Without shared prefixes every level can hold as many nodes as there are
+    distinct ids (UNIQUE) or tokens (PLAIN): the saved buffer grows; an
+    unknown mode is rejected."""
+    sizes = []
+    for mode in (0, 1, 2):
+        d = ttc.make_ttm_desc((32, 32, 32), (12, 8, 8), (1, 16, 16, 1), mode=mode)
+        sizes.append(ttc.ttm_embed_workspace(d, 16384))
+    assert sizes[0][0] < sizes[1][0] <= sizes[2][0]
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_workspace(ttc.make_ttm_desc((32, 32, 32), (12, 8, 8), (1, 16, 16, 1), mode=3), 64)
+    assert e.value.code == 2
+
 def test_ttm_errors_before_launch():
     d = _ttm()
     sb, cb = ttc.ttm_embed_workspace(d, 64)

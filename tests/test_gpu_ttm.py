@@ -267,3 +267,39 @@ def test_backward_is_bitwise_deterministic():
     assert torch.equal(out1, out2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+# ---- lookup modes: distinct ids and prefixes shared (default), distinct ids
+# only, every token on its own -------------------------------------------------
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("T", [700, 16384])
+def test_lookup_modes_match_default_and_oracle(mode, T):
+    """The UNIQUE and PLAIN modes give bitwise the rows of the default lookup
+    (same arithmetic per row), core gradients within tolerance of the oracle,
+    and node counts of a tree without shared prefixes: every level has U nodes
+    (UNIQUE: U distinct ids; PLAIN: U = valid tokens)."""
+    ttc = _ttc()
+    m = synth.make_ttm(3, T=T)
+    sp = m["spec"]
+    F = [_dev(c) for c in m["cores"]]
+    ids = _dev(m["ids"])
+    dout = _dev(m["dout"])
+    outs, grads, heads = [], [], []
+    for md in (0, mode):
+        emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks, mode=md)
+        out, saved = emb.forward(ids, F)
+        dF = emb.backward(ids, dout, F, None, saved)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        grads.append([g.cpu().numpy() for g in dF])
+        heads.append(_head(saved, T, len(sp.vocab_modes)))
+    assert np.array_equal(outs[0], outs[1])
+    dFr = oracle.ttm_backward(m["ids"], m["dout"], m["cores"])
+    for g, r in zip(grads[1], dFr):
+        assert _rel(g, r) <= TOL
+    h0, h1 = heads
+    U = h0["U"] if mode == 1 else h0["Tv"]
+    assert h1["U"] == U
+    assert all(int(c) == U for c in h1["levels"]), (h1["levels"], U)
+    assert int(h0["levels"][0]) < U  # the default shares prefixes
