@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--ttm-mode", default="dedup", choices=["dedup", "unique", "plain"],
                     help="embedding lookup mode: distinct ids and shared prefixes (default), distinct ids only, "
                          "or every token on its own")
+    ap.add_argument("--no-index-ahead", action="store_true",
+                    help="build the embedding index inside the step's forward instead of one step ahead")
     ap.add_argument("--rank-grads", action="store_true",
                     help="also compute every layer's early-stage gradients (diagonals dD, penalties) after its dG")
     ap.add_argument("--no-qkv-batch", action="store_true",
@@ -221,6 +223,8 @@ def main():
                "out": torch.empty((T, sp.dim), dtype=torch.float32, device=dev),
                "dF": [torch.empty(c.shape, dtype=torch.float32, device=dev) for c in w["cores"]],
                "saved": torch.empty(tsb, dtype=torch.uint8, device=dev),
+               # the index of the next step's ids is built into the other buffer
+               "saved2": [torch.empty(tsb, dtype=torch.uint8, device=dev) for _ in range(2)],
                "scratch": torch.empty(tcb, dtype=torch.uint8, device=dev), "d": len(sp.vocab_modes),
                "dim": sp.dim}
         if not args.no_cpu_baseline:
@@ -228,14 +232,29 @@ def main():
                         "cores": w["cores"]}
         del w
 
+    ahead = ttm is not None and not args.no_index_ahead and not args.single_stream
+    phase = [0]  # which of the two index buffers the current step looks up
+
+    def ttm_saved():
+        return ttm["saved2"][phase[0]] if ahead else ttm["saved"]
+
     def ttm_fwd():
-        if ttm is not None:
+        if ttm is None:
+            return
+        if ahead:
+            ttm["emb"].lookup(T, ttm["F"], None, ttm_saved(), out=ttm["out"], scratch=ttm["scratch"])
+        else:
             ttm["emb"].forward(ttm["ids"], ttm["F"], None, out=ttm["out"], saved=ttm["saved"],
                                scratch=ttm["scratch"])
 
+    def ttm_index_next():
+        # the next step's ids are known before it starts (this synthetic
+        # workload repeats the same batch)
+        ttm["emb"].index(ttm["ids"], saved=ttm["saved2"][1 - phase[0]])
+
     def ttm_bwd():
         if ttm is not None:
-            ttm["emb"].backward(ttm["ids"], ttm["dout"], ttm["F"], None, ttm["saved"], dF=ttm["dF"],
+            ttm["emb"].backward(ttm["ids"], ttm["dout"], ttm["F"], None, ttm_saved(), dF=ttm["dF"],
                                 scratch=ttm["scratch"])
     side = torch.cuda.Stream()  # default priority
 
@@ -291,10 +310,16 @@ def main():
         # side-stream work sits between two streaming passes.
         main = torch.cuda.current_stream()
         side.wait_stream(main)
+        merged = torch.cuda.Event()
         with torch.cuda.stream(side):
             ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
+            merged.record(side)
+            if ahead:
+                # the index of the next batch (sort, distinct ids, prefix tree)
+                # runs beside this step's streaming passes
+                ttm_index_next()
         ttm_fwd()
-        main.wait_stream(side)
+        main.wait_event(merged)
         for g in fwd_groups:
             fwd_group(g)
         for g in bwd_groups:
@@ -309,23 +334,38 @@ def main():
                 ttc.rank_grads_batch(mods, all_cores, all_D, [L["dG"] for L in layers], [L["dD"] for L in layers],
                                      RG_GAMMA, RG_BETA)
         main.wait_stream(side)
+        phase[0] = 1 - phase[0]
 
     step = step_single if args.single_stream else step_overlap
 
     # ---- warm-up, optional graph capture --------------------------------------------
+    if ahead:
+        ttm["emb"].index(ttm["ids"], saved=ttm["saved2"][0])  # the first step's index
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
     graph = None
     if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
+        # with the index built one step ahead, the step alternates between two
+        # index buffers: one graph per phase, replayed in turn
+        graphs = []
+        for _ in range(2 if ahead else 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            graphs.append(g)
         torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup)):
-            graph.replay()
+        turn = [0]
+
+        def replay():
+            graphs[turn[0]].replay()
+            turn[0] = (turn[0] + 1) % len(graphs)
+
+        graph = graphs[0]
+        for _ in range(max(1, args.warmup) * len(graphs)):
+            replay()
         torch.cuda.synchronize()
-    run = graph.replay if graph is not None else step
+    run = replay if graph is not None else step
 
     # ---- timed region -----------------------------------------------------------------
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,6 +474,8 @@ def main():
             "layers": len(specs),
             "launch": "eager" if graph is None else "hip_graph_replay",
             "qkv_batched": not (args.no_qkv_batch or args.single_stream),
+            "embedding_index": None if ttm is None else ("built one step ahead on the side stream" if ahead
+                                                         else "built in the step's forward"),
             "rank_grads": bool(args.rank_grads and not args.single_stream),
             "streams": 1 if args.single_stream else 2,
             "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "

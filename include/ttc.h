@@ -384,6 +384,32 @@ ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T,
                          ttc_stream_t stream);
 
 /*
+ * The forward in two calls, for callers that build the index of a batch
+ * ahead of its lookup (e.g. the next batch's ids beside the current step's
+ * work, since the index depends on the ids only).  The split follows the
+ * lookup of the project page (section "Making small tensor operations fast on
+ * GPUs"): first find the distinct ids and shared digit prefixes, then
+ * contract the cores once per distinct prefix and assemble the rows.
+ * ttm_embed_index: sort, distinct ids, segments and the per-level prefix
+ *   tree into `saved` (the head documented above and the private index
+ *   arrays).  Reads only ids.
+ * ttm_embed_lookup: from an index built in `saved` for the same desc and T,
+ *   the prefix products (into the rest of `saved`) and out.  The index stays
+ *   valid, so the same saved then serves ttm_embed_bwd.
+ * ttm_embed_fwd is exactly index then lookup.  The caller orders the two
+ * (same stream or an event); two batches in flight need two saved buffers.
+ * Errors are returned before any launch.
+ */
+ttc_status ttm_embed_index(const ttm_embed_desc* desc, int64_t T,
+                           const int64_t* ids, void* saved, size_t saved_bytes,
+                           ttc_stream_t stream);
+ttc_status ttm_embed_lookup(const ttm_embed_desc* desc, int64_t T,
+                            const float* const* F, const float* const* D,
+                            float* out, void* saved, size_t saved_bytes,
+                            void* scratch, size_t scratch_bytes,
+                            ttc_stream_t stream);
+
+/*
  * Backward: dF_k = d( sum_t <dout[t], E[ids[t]]> ) / dF_k, D held fixed.
  * The output gradients of equal ids are summed along their sorted segment
  * (no floating-point atomics; the result is bitwise reproducible).

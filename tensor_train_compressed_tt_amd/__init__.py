@@ -52,6 +52,8 @@ EXPORTS = [
     "tt_linear_path_cost",
     "ttm_embed_workspace",
     "ttm_embed_fwd",
+    "ttm_embed_index",
+    "ttm_embed_lookup",
     "ttm_embed_bwd",
     "ttc_status_str",
     "ttc_version",
@@ -142,6 +144,8 @@ def lib() -> ctypes.CDLL:
                                 ctypes.POINTER(ctypes.c_double)],
         "ttm_embed_workspace": [E, _I64, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
         "ttm_embed_fwd": [E, _I64, _P, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
+        "ttm_embed_index": [E, _I64, _P, _P, _SZ, _P],
+        "ttm_embed_lookup": [E, _I64, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
         "ttm_embed_bwd": [E, _I64, _P, _P, pp, pp, _P, _SZ, pp, _P, _SZ, _P],
     }
     for name, args in sig.items():
@@ -365,6 +369,18 @@ def ttm_embed_fwd(desc, T, ids, F, D, out, saved, saved_bytes, scratch, scratch_
     code = lib().ttm_embed_fwd(ctypes.byref(desc), T, ids, f, dd, out, saved, saved_bytes, scratch, scratch_bytes,
                                stream)
     _check("ttm_embed_fwd", code)
+
+
+def ttm_embed_index(desc, T, ids, saved, saved_bytes, stream=0):
+    _check("ttm_embed_index", lib().ttm_embed_index(ctypes.byref(desc), T, ids, saved, saved_bytes, stream))
+
+
+def ttm_embed_lookup(desc, T, F, D, out, saved, saved_bytes, scratch, scratch_bytes, stream=0):
+    f, _fa = _ptrs(F)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    code = lib().ttm_embed_lookup(ctypes.byref(desc), T, f, dd, out, saved, saved_bytes, scratch, scratch_bytes,
+                                  stream)
+    _check("ttm_embed_lookup", code)
 
 
 def ttm_embed_bwd(desc, T, ids, dout, F, D, saved, saved_bytes, dF, scratch, scratch_bytes, stream=0):

@@ -1207,20 +1207,10 @@ extern "C" ttc_status ttm_embed_workspace(const ttm_embed_desc* desc, int64_t T,
   return TTC_OK;
 }
 
-extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const int64_t* ids,
-                                    const float* const* F, const float* const* D, float* out, void* saved,
-                                    size_t saved_bytes, void* scratch, size_t scratch_bytes, ttc_stream_t stream) {
-  TtmPlan P;
-  ttc_status st = make_ttm_plan(desc, T, &P);
-  if (st != TTC_OK) return st;
-  if ((st = check_cores(P, F, D)) != TTC_OK) return st;
-  if (T == 0) return TTC_OK;
-  if (!ids || !out || !saved || (P.d >= 2 && !scratch)) return TTC_ERR_NULL;
-  if (!al16(out) || !al16(saved) || (scratch && !al16(scratch))) return TTC_ERR_ALIGN;
-  if (saved_bytes < P.sv_total || (P.d >= 2 && scratch_bytes < P.sc_fwd)) return TTC_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();
-
+namespace ttc {
+// The index of a lookup (depends on the ids only): sort, distinct ids,
+// segments, pieces, distinct digit prefixes per level and the digit lists.
+static void launch_index(const TtmPlan& P, int64_t T, const int64_t* ids, void* saved, hipStream_t s) {
   SortArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.ids = ids;
@@ -1257,6 +1247,12 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
     TraceScope ts("ttm_lists", s);
     TTC_LAUNCH(k_ttm_lists, dim3((unsigned)P.d), dim3(kSortThreads), 0, s, sa);
   }
+}
+
+// The rows of a lookup from its index: prefix products level by level, the
+// distinct-id rows, and the token gather.
+static void launch_lookup(const TtmPlan& P, int64_t T, const float* const* F, const float* const* D, float* out,
+                          void* saved, void* scratch, hipStream_t s) {
   // prefix products, level 1 .. d-1 (level 0 is a slice of F_1)
   for (int l = 1; l < P.d; ++l) {
     LevelArgs a;
@@ -1269,16 +1265,62 @@ extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const
   const float* rows = P.d >= 2 ? at<const float*>(scratch, P.sc_urow) : F[0];
   const int32_t* map = P.d >= 2 ? nullptr : at<const int32_t*>(saved, P.sv_uids);
   const int32_t* inv = at<const int32_t*>(saved, P.sv_inverse);
-  {
-    const bool vec = (P.N % 4) == 0 && al16(rows);
-    const int64_t per_block = (kTtmThreads / 64) * kRowsPerWave;
-    const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
-    TraceScope ts("ttm_gather", s);
-    if (vec)
-      TTC_LAUNCH(k_ttm_gather<true>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
-    else
-      TTC_LAUNCH(k_ttm_gather<false>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
-  }
+  const bool vec = (P.N % 4) == 0 && al16(rows);
+  const int64_t per_block = (kTtmThreads / 64) * kRowsPerWave;
+  const unsigned grid = (unsigned)((T + per_block - 1) / per_block);
+  TraceScope ts("ttm_gather", s);
+  if (vec)
+    TTC_LAUNCH(k_ttm_gather<true>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
+  else
+    TTC_LAUNCH(k_ttm_gather<false>, dim3(grid), dim3(kTtmThreads), 0, s, inv, map, rows, out, T, P.N);
+}
+}  // namespace ttc
+
+extern "C" ttc_status ttm_embed_index(const ttm_embed_desc* desc, int64_t T, const int64_t* ids, void* saved,
+                                      size_t saved_bytes, ttc_stream_t stream) {
+  TtmPlan P;
+  ttc_status st = make_ttm_plan(desc, T, &P);
+  if (st != TTC_OK) return st;
+  if (T == 0) return TTC_OK;
+  if (!ids || !saved) return TTC_ERR_NULL;
+  if (!al16(saved)) return TTC_ERR_ALIGN;
+  if (saved_bytes < P.sv_total) return TTC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  launch_index(P, T, ids, saved, (hipStream_t)stream);
+  return hip_ok();
+}
+
+extern "C" ttc_status ttm_embed_lookup(const ttm_embed_desc* desc, int64_t T, const float* const* F,
+                                       const float* const* D, float* out, void* saved, size_t saved_bytes,
+                                       void* scratch, size_t scratch_bytes, ttc_stream_t stream) {
+  TtmPlan P;
+  ttc_status st = make_ttm_plan(desc, T, &P);
+  if (st != TTC_OK) return st;
+  if ((st = check_cores(P, F, D)) != TTC_OK) return st;
+  if (T == 0) return TTC_OK;
+  if (!out || !saved || (P.d >= 2 && !scratch)) return TTC_ERR_NULL;
+  if (!al16(out) || !al16(saved) || (scratch && !al16(scratch))) return TTC_ERR_ALIGN;
+  if (saved_bytes < P.sv_total || (P.d >= 2 && scratch_bytes < P.sc_fwd)) return TTC_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  launch_lookup(P, T, F, D, out, saved, scratch, (hipStream_t)stream);
+  return hip_ok();
+}
+
+extern "C" ttc_status ttm_embed_fwd(const ttm_embed_desc* desc, int64_t T, const int64_t* ids,
+                                    const float* const* F, const float* const* D, float* out, void* saved,
+                                    size_t saved_bytes, void* scratch, size_t scratch_bytes, ttc_stream_t stream) {
+  TtmPlan P;
+  ttc_status st = make_ttm_plan(desc, T, &P);
+  if (st != TTC_OK) return st;
+  if ((st = check_cores(P, F, D)) != TTC_OK) return st;
+  if (T == 0) return TTC_OK;
+  if (!ids || !out || !saved || (P.d >= 2 && !scratch)) return TTC_ERR_NULL;
+  if (!al16(out) || !al16(saved) || (scratch && !al16(scratch))) return TTC_ERR_ALIGN;
+  if (saved_bytes < P.sv_total || (P.d >= 2 && scratch_bytes < P.sc_fwd)) return TTC_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  launch_index(P, T, ids, saved, s);
+  launch_lookup(P, T, F, D, out, saved, scratch, s);
   return hip_ok();
 }
 

@@ -29,6 +29,8 @@ from . import (
     tt_linear_workspace,
     ttm_embed_bwd,
     ttm_embed_fwd,
+    ttm_embed_index,
+    ttm_embed_lookup,
     ttm_embed_workspace,
 )
 
@@ -268,6 +270,31 @@ class TTMEmbedding:
                       None if D is None else [v.data_ptr() for v in D], out.data_ptr(), saved.data_ptr(),
                       saved.numel(), scratch.data_ptr(), scratch.numel(), _stream())
         return out, saved
+
+    def index(self, ids, saved=None):
+        """The index of a lookup of `ids` into `saved` on the current stream
+        (see ttm_embed_index); returns saved."""
+        T = int(ids.shape[0])
+        _need(ids, "ids", torch.int64, (T,))
+        sb, _ = self.workspace(T)
+        if saved is None:
+            saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=ids.device)
+        ttm_embed_index(self.desc(), T, ids.data_ptr(), saved.data_ptr(), saved.numel(), _stream())
+        return saved
+
+    def lookup(self, T, cores, D, saved, out=None, scratch=None):
+        """The rows of the lookup whose index `saved` holds (see ttm_embed_lookup)."""
+        self._check(cores, D)
+        _, cb = self.workspace(T)
+        dev = cores[0].device
+        if out is None:
+            out = torch.empty((T, self.dim), dtype=torch.float32, device=dev)
+        if scratch is None:
+            scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=dev)
+        ttm_embed_lookup(self.desc(), int(T), [c.data_ptr() for c in cores],
+                         None if D is None else [v.data_ptr() for v in D], out.data_ptr(), saved.data_ptr(),
+                         saved.numel(), scratch.data_ptr(), scratch.numel(), _stream())
+        return out
 
     def backward(self, ids, dout, cores, D, saved, dF=None, accumulate=False, scratch=None):
         T = int(ids.shape[0])

@@ -339,6 +339,25 @@ def test_ttm_lookup_modes_size_their_workspace():
         ttc.ttm_embed_workspace(ttc.make_ttm_desc((32, 32, 32), (12, 8, 8), (1, 16, 16, 1), mode=3), 64)
     assert e.value.code == 2
 
+def test_ttm_index_and_lookup_errors_before_launch():
+    d = ttc.make_ttm_desc((32, 32, 32), (12, 8, 8), (1, 16, 16, 1))
+    sb, cb = ttc.ttm_embed_workspace(d, 64)
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_index(d, 64, None, 16, sb)
+    assert e.value.code == 1
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_index(d, 64, 16, 16, sb - 1)
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_lookup(d, 64, [16, 16, 16], None, 16, 16, sb, 16, 16)  # scratch far too small
+    assert e.value.code == 6
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.ttm_embed_lookup(d, 64, [16, 16, 0], None, 16, 16, sb, 16, cb)
+    assert e.value.code == 1
+    # T = 0: nothing to do
+    ttc.ttm_embed_index(d, 0, None, None, 0)
+    ttc.ttm_embed_lookup(d, 0, [16, 16, 16], None, None, None, 0, None, 0)
+
 def test_ttm_errors_before_launch():
     d = _ttm()
     sb, cb = ttc.ttm_embed_workspace(d, 64)

@@ -303,3 +303,40 @@ def test_lookup_modes_match_default_and_oracle(mode, T):
     assert h1["U"] == U
     assert all(int(c) == U for c in h1["levels"]), (h1["levels"], U)
     assert int(h0["levels"][0]) < U  # the default shares prefixes
+
+
+def test_index_then_lookup_is_the_forward_and_pipelines():
+    """ttm_embed_index then ttm_embed_lookup gives bitwise the rows of
+    ttm_embed_fwd; and with two saved buffers, the index of a second batch
+    built on a side stream while the first batch is looked up and
+    back-propagated leaves both batches exact against the oracle."""
+    ttc = _ttc()
+    a = synth.make_ttm(3, T=5000)
+    b = synth.make_ttm(3, T=3000, base=20241203)  # other ids and row gradients; a's cores are used
+    sp = a["spec"]
+    emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks)
+    F = [_dev(c) for c in a["cores"]]
+    ids_a, ids_b = _dev(a["ids"]), _dev(b["ids"])
+    ref_out, _ = emb.forward(ids_a, F)
+    sv_a = emb.index(ids_a)
+    out_a = emb.lookup(len(a["ids"]), F, None, sv_a)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, ref_out)
+    # pipelined: index of batch b on a side stream beside batch a's lookup and backward
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    sv_a = emb.index(ids_a)
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        sv_b = emb.index(ids_b)
+    out_a = emb.lookup(len(a["ids"]), F, None, sv_a)
+    dF_a = emb.backward(ids_a, _dev(a["dout"]), F, None, sv_a)
+    main.wait_stream(side)
+    out_b = emb.lookup(len(b["ids"]), F, None, sv_b)
+    dF_b = emb.backward(ids_b, _dev(b["dout"]), F, None, sv_b)
+    torch.cuda.synchronize()
+    for m, out, dF in ((a, out_a, dF_a), (b, out_b, dF_b)):
+        assert _rel(out.cpu().numpy(), oracle.ttm_forward(m["ids"], a["cores"])) <= TOL
+        for g, r in zip(dF, oracle.ttm_backward(m["ids"], m["dout"], a["cores"])):
+            assert _rel(g.cpu().numpy(), r) <= TOL
+    _check_integer(sv_b, b["ids"], sp.vocab_modes)
