@@ -13,8 +13,8 @@ with 40% of every link diagonal zeroed; the embedding is fp32.  Inputs are
 seeded synthetic data already resident in HBM.  --no-ttm drops the
 embedding from the step.
 
-Prints one JSON line (see the design doc for every field).  Only rank 0 of a single
-GPU runs; --gpus above 1 is refused.
+Prints one JSON line: the metric, the roofline of the dominant kernel and the
+oracle's CPU baseline.  One GPU only: --gpus above 1 is refused.
 """
 
 from __future__ import annotations
@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 4])
     ap.add_argument("--rank", type=int, default=None)
-    ap.add_argument("--layers", type=int, default=None, help="config 4 only: number of encoder layers")
+    ap.add_argument("--layers", type=int, default=None, help="with --config 4: number of encoder layers")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens per step instead of the config's (batch x 128-token sequences, e.g. 128 for batch 1)")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--single-stream", action="store_true",
                     help="run merges and core-gradient tails on the main stream too (no overlap)")
@@ -54,6 +56,10 @@ def parse():
                     help="build the embedding index inside the step's forward instead of one step ahead")
     ap.add_argument("--rank-grads", action="store_true",
                     help="also compute every layer's early-stage gradients (diagonals dD, penalties) after its dG")
+    ap.add_argument("--graph-steps", type=int, default=2, choices=[1, 2],
+                    help="steps per captured graph (2 needs an even --steps; otherwise 1)")
+    ap.add_argument("--merge-side", action="store_true",
+                    help="run the merges on the side stream and the embedding lookup on the main one")
     ap.add_argument("--no-qkv-batch", action="store_true",
                     help="one launch per layer for the Q, K and V projections instead of one batched launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -164,7 +170,9 @@ def main():
 
     cfg = args.config
     rank = args.rank if args.rank is not None else (64 if cfg == 4 else 30)
-    T = synth.CONFIG_TOKENS[cfg]
+    T = args.tokens if args.tokens is not None else synth.CONFIG_TOKENS[cfg]
+    if not 1 <= T <= 16384:
+        sys.exit("--tokens must be in [1, 16384] (the embedding sorts at most 16384 ids per call)")
     zf = synth.CONFIG_ZERO_FRAC[cfg]
     dt = synth.CONFIG_DTYPE[cfg]
     specs = synth.config_layers(cfg, rank)
@@ -301,25 +309,39 @@ def main():
 
     def step_overlap():
         # The merges depend only on the cores and D, the core-gradient tails
-        # produce only dG: both go to a side stream, each as one batched call
-        # for all layers.  The main stream carries the dependent chain of
-        # streaming passes (embedding lookup, forward over the layers, dX
-        # backward through them in reverse order, then the embedding's
-        # backward).  The merges run beside the embedding lookup; the tails
-        # start after the last dX pass, beside the embedding's backward, so no
-        # side-stream work sits between two streaming passes.
+        # produce only dG; each is one batched call for all layers.  The main
+        # stream carries the merges and then the dependent chain of streaming
+        # passes (forward over the layers, dX backward through them in reverse
+        # order, then the embedding's backward).  The side stream carries the
+        # embedding lookup beside the merges (the forwards wait for it), the
+        # next batch's index beside the forwards, and the tails after the last
+        # dX pass, beside the embedding's backward, so no side-stream work sits
+        # between two streaming passes.  With the index built in the step
+        # (no index ahead) the lookup is the longer of the two and runs on the
+        # main stream, the merges beside it.
         main = torch.cuda.current_stream()
         side.wait_stream(main)
-        merged = torch.cuda.Event()
-        with torch.cuda.stream(side):
-            ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
-            merged.record(side)
-            if ahead:
-                # the index of the next batch (sort, distinct ids, prefix tree)
-                # runs beside this step's streaming passes
+        if ahead and not args.merge_side:
+            # the lookup of the already indexed batch (shorter than the merges)
+            # on the side stream, then the index of the next batch (sort,
+            # distinct ids, prefix tree) beside this step's streaming passes;
+            # the forwards follow the merges on the main stream
+            looked = torch.cuda.Event()
+            with torch.cuda.stream(side):
+                ttm_fwd()
+                looked.record(side)
                 ttm_index_next()
-        ttm_fwd()
-        main.wait_event(merged)
+            ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
+            main.wait_event(looked)
+        else:
+            merged = torch.cuda.Event()
+            with torch.cuda.stream(side):
+                ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
+                merged.record(side)
+                if ahead:
+                    ttm_index_next()
+            ttm_fwd()
+            main.wait_event(merged)
         for g in fwd_groups:
             fwd_group(g)
         for g in bwd_groups:
@@ -347,12 +369,16 @@ def main():
     graph = None
     if not args.eager:
         # with the index built one step ahead, the step alternates between two
-        # index buffers: one graph per phase, replayed in turn
+        # index buffers: one graph per phase, replayed in turn, or one graph of
+        # both steps (no drain between the two)
+        pair = args.graph_steps == 2 and args.steps % 2 == 0
         graphs = []
-        for _ in range(2 if ahead else 1):
+        for _ in range(1 if pair else 2 if ahead else 1):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step()
+                if pair:
+                    step()
             graphs.append(g)
         torch.cuda.synchronize()
         turn = [0]
@@ -366,13 +392,14 @@ def main():
             replay()
         torch.cuda.synchronize()
     run = replay if graph is not None else step
+    launches = args.steps // 2 if graph is not None and pair else args.steps
 
     # ---- timed region -----------------------------------------------------------------
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
+    for _ in range(launches):
         run()
     end.record()
     torch.cuda.synchronize()
@@ -448,9 +475,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host[:6], args.cpu_tokens, ttm_host)
+        cpu = cpu_baseline(host[:6], min(args.cpu_tokens, T), ttm_host)
 
-    wl = {1: "config 1", 2: "config 2", 4: "config 4"}[cfg]
+    wl = {1: "one encoder's TT-linear set, fp32", 2: "one encoder's TT-linear set, bf16",
+          4: "CodeBERT-large-sized encoder stack"}[cfg]
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -465,7 +493,7 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": f"{wl}{'' if ttm is None else ' + config 3 embedding'}: {len(specs)} TT-linear layers (fwd then bwd in reverse), "
+            "workload": f"{wl}{'' if ttm is None else ' + TTM embedding lookup of the same tokens'}: {len(specs)} TT-linear layers (fwd then bwd in reverse), "
                         f"{'4x 768->768, 768->3072, 3072->768' if cfg != 4 else '24x (4x 1024->1024, 1024->4096, 4096->1024)'}, "
                         f"{dt} activations, fp32 accumulate, T={T} tokens, TT rank {rank}, "
                         f"{int(zf * 100)}% of each link diagonal zeroed",
@@ -473,9 +501,12 @@ def main():
             "rank": rank,
             "layers": len(specs),
             "launch": "eager" if graph is None else "hip_graph_replay",
+            "steps_per_graph": None if graph is None else (2 if pair else 1),
             "qkv_batched": not (args.no_qkv_batch or args.single_stream),
             "embedding_index": None if ttm is None else ("built one step ahead on the side stream" if ahead
                                                          else "built in the step's forward"),
+            "merges": "side stream, beside the embedding lookup" if (args.merge_side or not ahead)
+                      else "main stream, the embedding lookup beside them on the side stream",
             "rank_grads": bool(args.rank_grads and not args.single_stream),
             "streams": 1 if args.single_stream else 2,
             "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "

@@ -15,7 +15,7 @@ poster page, figure caption on the TT / TTM network structures):
   first in the chain, W = T.reshape(N_out, N_in); with the input modes first,
   W = T.reshape(N_in, N_out)^T.  Y = x W^T (no bias).
 
-Readings where the pages are silent (each is listed in the design doc): the order
+Readings where the pages are silent: the order
 of the modes in the chain is a parameter (``in_first``); index linearisation
 is row-major mixed radix; D is a real-valued scale, not only a 0/1 mask.
 """
@@ -188,7 +188,7 @@ def early_stage_grads(x, dy, cores, D, gamma: float, beta: float, in_first: bool
     """Gradients of the early-stage objective L + gamma * S^(D) + beta * ||G||^2
     (project page, section "Learn the ranks while training").
 
-    Readings (listed in the design doc): S^(D) is the l1 norm of all link diagonals,
+    Readings: S^(D) is the l1 norm of all link diagonals,
     sum_k |D_k|_1, and ||G||^2 the squared Frobenius norm of all cores.  An
     entry with D_k[b] == 0 is a pruned slice: its diagonal gradient is reported
     as 0 (the l1 subgradient at 0 is taken as 0 as well).  Returns

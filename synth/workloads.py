@@ -9,7 +9,7 @@ shapes, value distributions and rank-mask structure of those layers.
 Seeds: numpy PCG64 seeded with SeedSequence([config, layer, tensor_id,
 BASE_SEED]), so any layer of any configuration can be regenerated on its own.
 
-Readings of the workload descriptions (each listed in the design doc):
+Readings of the workload descriptions:
 
 * the link diagonals draw U(0.5, 1.5) and then exactly floor(p * r) entries
   per link, picked by a seeded permutation, are set to 0;
