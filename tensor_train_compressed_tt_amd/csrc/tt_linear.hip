@@ -299,6 +299,8 @@ constexpr int kFwdStageOff() {
   return ((16 * TT) * (16 * NR + 16 / (int)sizeof(typename Elem<T>::type)) * (int)sizeof(typename Elem<T>::type) +
           255) / 256 * 256;
 }
+// output tiles per wave and step of the forward's second product
+constexpr int kFwdUO(int NR, int NW) { return NW == 8 ? 2 : (NR <= 2 ? 4 : 2); }
 template <typename T, int NR, int TT, int NW>
 constexpr size_t kFwdLdsBytes() {
   constexpr size_t red = (size_t)NW * 16 * TT * 16 * NR * 4;
@@ -327,6 +329,7 @@ struct FwdArgs {
   typename Elem<T>::type* y;
   int64_t T_, N_in, N_out;
   int vin, vout;
+  int cg_n;  // column groups per token tile (>= 1, at most the tile's output steps)
 };
 template <typename A>
 struct StreamBatch {
@@ -354,6 +357,13 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   E* __restrict__ y = fa_.y;
   const int64_t T_ = fa_.T_, N_in = fa_.N_in, N_out = fa_.N_out;
   const int vin = fa_.vin, vout = fa_.vout;
+  // With few token tiles the output steps of a tile are split over cg_n
+  // work-groups: work-group (tile, cg) computes the tile's Z and writes the
+  // output steps cg, cg + cg_n, ...; only group 0 stores Z.  The wide
+  // variant runs only with a tile for every CU and never splits.
+  const int cg_n = NW == 8 ? 1 : fa_.cg_n;
+  const int cg = (int)(bid % (unsigned)cg_n);
+  bid /= (unsigned)cg_n;
   typedef typename Mma<T>::frag frag;
   constexpr int Rpad = 16 * NR;
   constexpr int EPV = Mma<T>::EPV, KSTEP = Mma<T>::KSTEP;
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   constexpr int NT = 64 * NW;                           // threads
   constexpr int UNR = NW == 8 ? (NR <= 2 ? 2 : 1) : (NR <= 2 ? 4 : 1);
   constexpr int KS = Rpad / KSTEP;
-  constexpr int UO = NW == 8 ? 2 : (NR <= 2 ? 4 : 2);
+  constexpr int UO = kFwdUO(NR, NW);
   constexpr int TPS = NW * UO;                           // output tiles per step (all waves)
   extern __shared__ __align__(16) char smem[];
   constexpr int TM = 16 * TT;                     // tokens per work-group
@@ -412,11 +422,11 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
         }
       }
   };
-  // Likewise for B: work-group b visits the output steps (TPS tiles each)
-  // starting at step b mod nsteps.
-  const int nsteps = (not_ + TPS - 1) / TPS;
+  // Likewise for B: work-group b visits its column group's output steps (TPS
+  // tiles each) starting at its step b mod nsteps.
+  const int nsteps = ((not_ + TPS - 1) / TPS - cg + cg_n - 1) / cg_n;  // this group's steps
   const int rot2 = (int)(bid % (unsigned)nsteps);
-  auto ostep = [&](int sidx) { return ((sidx + rot2) % nsteps) * TPS; };
+  auto ostep = [&](int sidx) { return (cg + cg_n * ((sidx + rot2) % nsteps)) * TPS; };
   // with one rank tile pair the first B batches are requested right away;
   // wider ranks wait for phase 2 (register budget)
   if constexpr (NR <= 2) {
@@ -498,8 +508,8 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
     const int tt = idx / Rpad, j = idx % Rpad;
     const E e = (E)Mma<T>::from_f32(zs[i]);
     if constexpr (VEC)
-      buf_store(rz, (uint32_t)((tt * Rpad + j) * (int)sizeof(E)), e);
-    else if (t0 + tt < T_)
+      buf_store(rz, cg == 0 ? (uint32_t)((tt * Rpad + j) * (int)sizeof(E)) : kNoOff, e);
+    else if (cg == 0 && t0 + tt < T_)
       Z[(t0 + tt) * Rpad + j] = e;
     zl[tt * ZLD + j] = e;
   }
@@ -1538,6 +1548,10 @@ struct StreamJob {
   char* sc;  // backward scratch
 };
 
+#ifndef TTC_FWD_CUS
+#define TTC_FWD_CUS 256  // compute units of an MI355X
+#endif
+constexpr int64_t kFwdCUs = TTC_FWD_CUS;
 template <typename T, int NR, bool VEC, int TT, int NW>
 static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef typename Elem<T>::type E;
@@ -1550,9 +1564,18 @@ static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   }
   StreamBatch<FwdArgs<T>> b;
   memset(&b, 0, sizeof(b));
+  // fewer token tiles than CUs: split each tile's output steps over column
+  // groups so that the launch still covers the chip
+  int64_t tiles_all = 0;
+  for (int i = 0; i < n; ++i) tiles_all += (jobs[i].P->T + 16 * TT - 1) / (16 * TT);
   for (int i = 0; i < n; ++i) {
     const LinearPlan& P = *jobs[i].P;
     FwdArgs<T>& a = b.a[i];
+    const int64_t tiles = (P.T + 16 * TT - 1) / (16 * TT);
+    const int nst = (int)(((P.N_out + 15) / 16 + NW * kFwdUO(NR, NW) - 1) / (NW * kFwdUO(NR, NW)));
+    a.cg_n = (NW == 8 || tiles_all == 0 || tiles_all >= kFwdCUs)
+                 ? 1
+                 : (int)std::min<int64_t>(nst, std::max<int64_t>(1, kFwdCUs / tiles_all));
     a.x = (const E*)jobs[i].x;
     a.Ac = (const E*)(jobs[i].sv + P.sv_Ac);
     a.Bc = (const E*)(jobs[i].sv + P.sv_Bc);
@@ -1563,7 +1586,7 @@ static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     a.N_out = P.N_out;
     a.vin = (int)VEC;
     a.vout = (P.N_out % 4) == 0 && aligned16(jobs[i].y);
-    b.first[i + 1] = b.first[i] + (int)((P.T + 16 * TT - 1) / (16 * TT));
+    b.first[i + 1] = b.first[i] + (int)(tiles * a.cg_n);
   }
   b.n = n;
   TraceScope ts("fwd", st);
