@@ -112,6 +112,22 @@ def test_rank_range(rank):
     _check(spec, layer, "f32")
 
 
+@pytest.mark.parametrize("dtype,li,T,rank", [
+    ("bf16", 3, 2000, 30),  # 63 tiles of 32 tokens, 3 output steps: 3 column groups of one step
+    ("f32", 3, 1000, 30),   # 32 tiles, 3 column groups
+    ("bf16", 3, 1000, 64),  # rank 64: 6 output steps, 6 column groups
+    ("bf16", 4, 100, 30),   # 4 tiles, 768 -> 3072: 12 column groups of one step
+    ("bf16", 4, 1500, 30),  # 47 tiles: 5 column groups over 12 steps (3, 3, 2, 2, 2)
+])
+def test_forward_column_groups(dtype, li, T, rank):
+    """With fewer token tiles than CUs the forward splits each tile's output
+    steps over column groups (uneven ones included); Y, dX and every dG
+    (through the saved Z, stored by the first group only) match the oracle."""
+    spec = synth.config_layers(2, rank)[li]
+    layer = synth.make_tt_layer(2, 500 + li, spec, T, 0.40, dtype)
+    _check(spec, layer, dtype)
+
+
 @pytest.mark.parametrize("li", range(6))
 def test_config1_layers_fp32(li):
     spec = synth.config_layers(1)[li]
