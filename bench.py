@@ -82,14 +82,26 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 2, "copies": 3}), flush=True)
 
 
+# the sources that decide what the TT-linear kernels do and how they are launched
+KERNEL_SOURCES = ("tt_linear.hip", "ttc_device.hpp", "tt_plan.cpp", "tt_plan.hpp")
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources, in KERNEL_SOURCES order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_train_compressed_tt_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from its committed counter summary
     (profiles/<kernel>_hbm_traffic.md), or None when that summary was taken on
-    a different version of the kernel source."""
-    import hashlib
-
+    a different version of the kernel sources."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_hbm_traffic.md")
-    src = os.path.join(ROOT, "tensor_train_compressed_tt_amd", "csrc", "tt_linear.hip")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -97,8 +109,7 @@ def measured_traffic(kernel):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != digest or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_sources_sha256") != kernel_source_digest() or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
 

@@ -158,9 +158,14 @@ __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, unsigned short
 __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
 }
+// 16-byte store of a streamed output (a layer's Y or dX): written once and not
+// read again by the pass that follows, so it carries the non-temporal cache
+// policy bit and does not displace the operands the next kernels re-read
+// from the caches.
+constexpr int kStreamStorePolicy = 2;  // nt
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
   typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, kStreamStorePolicy);
 }
 
 // Same from LDS (always in range, 16-byte aligned).
