@@ -254,7 +254,7 @@ __device__ __forceinline__ void slab_fetch_b(typename Mma<T>::frag* r, rsrc_t sr
     const int row = gi >> 4, part = gi & 15;
     const int64_t col = c0 + part * B::EPV;
     const uint32_t o = (uint32_t)(((int64_t)(row0 + row) * ncols + col) * B::ES);
-    r[q] = buf_frag<T>(src, (live & (col < ncols)) ? o : kNoOff);
+    r[q] = buf_frag_last<T>(src, (live & (col < ncols)) ? o : kNoOff);
   }
 }
 

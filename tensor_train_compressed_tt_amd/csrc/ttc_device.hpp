@@ -149,6 +149,13 @@ template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag buf_frag(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// The same load for the last read of a streamed activation in the step (dY in
+// the dY pass, x in the dX pass): non-temporal, so that the lines need not
+// stay in the caches after this read.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag buf_frag_last(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
 
 // Stores through a buffer resource: a store at an out-of-range offset is
 // dropped, so guarded stores need no branch either.
