@@ -805,6 +805,19 @@ __global__ __launch_bounds__(kLevelBwdThreads) void k_ttm_level_bwd(LevelArgs a)
   }
 }
 
+// 16-byte accesses of data the step touches once (the token rows written by the
+// gather, the row gradients read by the segment sums): non-temporal, so that
+// they do not displace the cores, products and partial sums that are re-read.
+typedef float stream_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream4(const float* p) {
+  const stream_f4 t = __builtin_nontemporal_load(reinterpret_cast<const stream_f4*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_stream4(float* p, float4 v) {
+  const stream_f4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<stream_f4*>(p));
+}
+
 // out[t] = row of inverse[t] (through `map` when given: the row index of a
 // distinct id); zero for an id that was out of range.  Each wave copies
 // kRowsPerWave rows, loading all of them before storing.
@@ -835,7 +848,7 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_gather(const int32_t* __res
                          : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int k = 0; k < kRowsPerWave; ++k)
-        if (t0 + k < T) reinterpret_cast<float4*>(out + (t0 + k) * N)[c] = v[k];
+        if (t0 + k < T) st_stream4(out + (t0 + k) * N + 4 * (int64_t)c, v[k]);
     }
   } else {
     for (int64_t c = lane; c < N; c += 64) {
@@ -884,7 +897,7 @@ __global__ __launch_bounds__(kTtmThreads) void k_ttm_seg(const int32_t* __restri
         float4 x[B];
 #pragma unroll
         for (int q = 0; q < B; ++q)
-          x[q] = ib + q < i1 ? reinterpret_cast<const float4*>(dout + (int64_t)s_ord[ib + q - i0] * N)[col]
+          x[q] = ib + q < i1 ? ld_stream4(dout + (int64_t)s_ord[ib + q - i0] * N + 4 * (int64_t)col)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int q = 0; q < B; ++q) {
