@@ -99,9 +99,10 @@ def kernel_source_digest():
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from its committed counter summary
-    (profiles/<kernel>_hbm_traffic.md), or None when that summary was taken on
-    a different version of the kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_hbm_traffic.md")
+    on the default workload (profiles/<kernel>_tt6_bf16_t16384_rank30_hbm_traffic.md),
+    or None when that summary was taken on a different version of the kernel
+    sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_tt6_bf16_t16384_rank30_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
