@@ -123,7 +123,9 @@ def chain_core_grads(dT, cores, D) -> list:
         P = chain_prefix(cores, D, k)
         S = chain_suffix(cores, D, k)
         dTk = dT.reshape(P.shape[0], G.shape[1], S.shape[1])
-        grads.append(np.einsum("xa,xmy,by->amb", P, dTk, S))
+        # one sum over alpha and beta; numpy picks the pairwise order
+        # (P^T dT first, then S^T), which changes nothing but the rounding order
+        grads.append(np.einsum("xa,xmy,by->amb", P, dTk, S, optimize=True))
     return grads
 
 
