@@ -2435,11 +2435,11 @@ extern "C" ttc_status tt_linear_explain(const tt_linear_desc* desc, int64_t T, c
   snprintf(buf, n,
            "path=merged split=%d rank=%d rpad=%d N_out=%lld N_in=%lld T=%lld "
            "merged_macs=%.6g merged_bytes=%.6g sequential_macs=%.6g sequential_bytes=%.6g "
-           "dense_macs=%.6g dense_bytes=%.6g dy_grid=%dx%d dy_slabs=%d dx_grid=%dx%d dx_slabs=%d saved=%zu "
-           "scratch=%zu",
+           "dense_macs=%.6g dense_bytes=%.6g dy_grid=%dx%d dy_slabs=%d dy_tiles=%d dx_grid=%dx%d dx_slabs=%d "
+           "dx_tiles=%d saved=%zu scratch=%zu",
            P.s, P.rs, P.Rpad, (long long)P.N_out, (long long)P.N_in, (long long)T, macs[1], bytes[1], macs[2],
-           bytes[2], macs[3], bytes[3], P.dy_gc, P.dy_gt, P.dy_nsl, P.dx_gc, P.dx_gt, P.dx_nsl, P.sv_total,
-           P.sc_total);
+           bytes[2], macs[3], bytes[3], P.dy_gc, P.dy_gt, P.dy_nsl, P.dy_tpg, P.dx_gc, P.dx_gt, P.dx_nsl, P.dx_tpg,
+           P.sv_total, P.sc_total);
   return TTC_OK;
 }
 

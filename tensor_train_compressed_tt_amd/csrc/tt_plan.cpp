@@ -1,14 +1,12 @@
 // Validation, contraction-path cost model and buffer layout of a TT-linear call.
 //
-// The merged path follows the CoMERA project page, section "Making small
-// tensor operations fast on GPUs" (one contraction order for both passes):
-// the cores on the output side of the chain are multiplied into one matrix,
-// the cores on the input side into another, the input is contracted through
-// them and the rank-r intermediate is kept for the backward pass.  The page
-// states (Proposition 4.1 of the paper) that for large batches this order is
-// close to the fewest operations; the model below also prices the
-// core-by-core sweep and the dense weight so the claim can be checked for any
-// shape, batch and rank.
+// The merged path is the contraction order of the CoMERA project page, section
+// "Making small tensor operations fast on GPUs" (Proposition 4.1): both halves
+// of the chain are multiplied out first, the tokens then pass through two
+// skinny products, and the rank-sized intermediate is kept for the backward.
+// The page argues that this order costs close to the minimum once the batch is
+// large; the model below prices it next to a core-by-core sweep and the dense
+// weight, so the crossover can be computed for any shape, batch and rank.
 #include "tt_plan.hpp"
 
 #include <string.h>
@@ -19,6 +17,10 @@
 namespace ttc {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// largest extent of one buffer resource of the streaming kernels
+constexpr int64_t kRsrcMax = 0x7fffffff;
+static bool fits_rsrc(int64_t bytes) { return bytes <= kRsrcMax; }
 
 ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P) {
   if (!desc || !P) return TTC_ERR_NULL;
@@ -68,6 +70,13 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->NRt = desc->in_first ? nout : nin;
   P->T = T;
   P->es = desc->act_dtype == TTC_BF16 ? 2 : 4;
+  // The streaming kernels address their operands through buffer resources of
+  // at most 2^31 - 1 bytes with 32-bit offsets: the merged operands
+  // (Rpad x N activation elements each) and a 64-token slab of any activation
+  // must fit, or the call is refused instead of reading zeros past the range.
+  if (!fits_rsrc(int64_t(P->Rpad) * nin * P->es) || !fits_rsrc(int64_t(P->Rpad) * nout * P->es) ||
+      !fits_rsrc(int64_t(kTileT) * nin * P->es) || !fits_rsrc(int64_t(kTileT) * nout * P->es))
+    return TTC_ERR_UNSUPPORTED;
   P->max_rank = 1;
   for (int k = 0; k <= d; ++k) P->max_rank = std::max(P->max_rank, P->ranks[k]);
 
@@ -130,13 +139,17 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
     const int chunks = (int)std::max<int64_t>(1, (ncols + P->sw - 1) / P->sw);
     const int gc_min = (chunks + maxs - 1) / maxs;
     double best = 1e300;
-    int bsl = (chunks + gc_min - 1) / gc_min, bper = nt;
+    int bsl = (chunks + gc_min - 1) / gc_min, bper = 1;
     for (int g = gc_min; g <= chunks; ++g) {
       const int sl = (chunks + g - 1) / g;
       if ((chunks + sl - 1) / sl != g) continue;  // same shape as a smaller g
       for (int per = 1; per <= nt; ++per) {
         const int tg = (nt + per - 1) / per;
         if ((nt + tg - 1) / tg != per) continue;
+        // a work-group's token range of the streamed activation, of its rank
+        // tile and of the fp32 dZ partials are each one buffer resource
+        const int64_t toks64 = int64_t(per) * kTileT;
+        if (!fits_rsrc(toks64 * ncols * P->es) || !fits_rsrc(toks64 * P->Rpad * 4)) break;
         const double cols = double(sl) * P->sw, toks = double(per) * kTileT;
         double wg = toks * cols * P->es * (dy ? 1.0 : 2.0);  // streamed activations
         wg += 4.0 * P->rs * cols;                             // weight-side partial

@@ -41,6 +41,24 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_buf(t: torch.Tensor, name: str):
+    """A caller-supplied workspace: any contiguous device tensor; its size in
+    bytes is what the C entry points receive."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _need_grads(dG, shapes, name="dG"):
+    if len(dG) != len(shapes):
+        raise ValueError(f"{name} needs {len(shapes)} tensors, got {len(dG)}")
+    for k, (g, s) in enumerate(zip(dG, shapes)):
+        _need(g, f"{name}[{k}]", torch.float32, s)
+
+
 def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -98,7 +116,7 @@ class TTLinear:
         if saved is None:
             saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=cores[0].device)
         tt_linear_prepare(self.desc, T, [c.data_ptr() for c in cores], [v.data_ptr() for v in D], saved.data_ptr(),
-                          saved.numel(), _stream())
+                          _nbytes(saved), _stream())
         return saved
 
     def forward(self, x, cores, D, out=None, saved=None, prepared=False):
@@ -115,7 +133,7 @@ class TTLinear:
             saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=x.device)
         desc = self.desc_prepared if prepared else self.desc
         tt_linear_fwd(desc, T, x.data_ptr(), [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
-                      out.data_ptr(), saved.data_ptr(), saved.numel(), None, 0, _stream())
+                      out.data_ptr(), saved.data_ptr(), _nbytes(saved), None, 0, _stream())
         return out, saved
 
     def backward(self, x, dy, cores, D, saved, want_dx=True, dx=None, dG=None, scratch=None, grad_stream=None):
@@ -124,19 +142,35 @@ class TTLinear:
         _need(x, "x", self.dtype, (T, self.n_in))
         _need(dy, "dy", self.dtype, (T, self.n_out))
         self._check_chain(cores, D)
+        _need_buf(saved, "saved")
         _, cb = self.workspace(T)
-        if scratch is None:
+        own_scratch = scratch is None
+        if own_scratch:
             scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=x.device)
-        if want_dx and dx is None:
-            dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
-        if dG is None:
+        _need_buf(scratch, "scratch")
+        if want_dx:
+            if dx is None:
+                dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
+            _need(dx, "dx", self.dtype, (T, self.n_in))
+        own_dG = dG is None
+        if own_dG:
             dG = [torch.empty(s, dtype=torch.float32, device=x.device) for s in self.core_shapes]
+        _need_grads(dG, self.core_shapes)
         main = _stream()
         gs = main if grad_stream is None else grad_stream.cuda_stream
         tt_linear_bwd_split(self.desc, T, x.data_ptr(), dy.data_ptr(), [c.data_ptr() for c in cores],
-                            [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
+                            [v.data_ptr() for v in D], saved.data_ptr(), _nbytes(saved),
                             dx.data_ptr() if want_dx else None, [g.data_ptr() for g in dG], scratch.data_ptr(),
-                            scratch.numel(), main, gs)
+                            _nbytes(scratch), main, gs)
+        if grad_stream is not None and gs != main:
+            # the core-gradient tail on grad_stream still reads scratch and
+            # writes dG after this call returns: keep the allocator from
+            # handing their blocks to work on the current stream before then
+            if own_scratch:
+                scratch.record_stream(grad_stream)
+            if own_dG:
+                for g in dG:
+                    g.record_stream(grad_stream)
         return (dx if want_dx else None), dG
 
 
@@ -146,21 +180,28 @@ class TTLinear:
         _need(x, "x", self.dtype, (T, self.n_in))
         _need(dy, "dy", self.dtype, (T, self.n_out))
         self._check_chain(cores, D)
-        if want_dx and dx is None:
-            dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
+        _need_buf(saved, "saved")
+        _need_buf(scratch, "scratch")
+        if want_dx:
+            if dx is None:
+                dx = torch.empty((T, self.n_in), dtype=self.dtype, device=x.device)
+            _need(dx, "dx", self.dtype, (T, self.n_in))
         tt_linear_bwd_data(self.desc, T, x.data_ptr(), dy.data_ptr(), [c.data_ptr() for c in cores],
-                           [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
-                           dx.data_ptr() if want_dx else None, scratch.data_ptr(), scratch.numel(), _stream())
+                           [v.data_ptr() for v in D], saved.data_ptr(), _nbytes(saved),
+                           dx.data_ptr() if want_dx else None, scratch.data_ptr(), _nbytes(scratch), _stream())
         return dx if want_dx else None
 
     def backward_cores(self, T, cores, D, saved, scratch, dG=None):
         """dG on the current stream from the partial sums backward_data left in `scratch`."""
         self._check_chain(cores, D)
+        _need_buf(saved, "saved")
+        _need_buf(scratch, "scratch")
         if dG is None:
             dG = [torch.empty(s, dtype=torch.float32, device=cores[0].device) for s in self.core_shapes]
+        _need_grads(dG, self.core_shapes)
         tt_linear_bwd_cores(self.desc, int(T), [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
-                            saved.data_ptr(), saved.numel(), [g.data_ptr() for g in dG], scratch.data_ptr(),
-                            scratch.numel(), _stream())
+                            saved.data_ptr(), _nbytes(saved), [g.data_ptr() for g in dG], scratch.data_ptr(),
+                            _nbytes(scratch), _stream())
         return dG
 
     def rank_grads(self, cores, D, dG, gamma=0.0, beta=0.0, dD=None):
@@ -168,8 +209,7 @@ class TTLinear:
         vector per link) and adds 2 beta G_k to dG in place (see
         tt_linear_rank_grads)."""
         self._check_chain(cores, D)
-        for g, s in zip(dG, self.core_shapes):
-            _need(g, "dG", torch.float32, s)
+        _need_grads(dG, self.core_shapes)
         if dD is None:
             dD = [torch.empty(v.shape, dtype=torch.float32, device=v.device) for v in D]
         tt_linear_rank_grads(self.desc, [c.data_ptr() for c in cores], [v.data_ptr() for v in D],
@@ -183,7 +223,7 @@ def prepare_batch(mods, T, cores, D, saved):
         m._check_chain(c, d)
     tt_linear_prepare_batch([m.desc for m in mods], [T] * len(mods),
                             [[t.data_ptr() for t in c] for c in cores], [[v.data_ptr() for v in d] for d in D],
-                            [b.data_ptr() for b in saved], [b.numel() for b in saved], _stream())
+                            [b.data_ptr() for b in saved], [_nbytes(b) for b in saved], _stream())
 
 
 
@@ -199,7 +239,7 @@ def forward_batch(mods, xs, cores, D, outs, saved, prepared=False):
     tt_linear_fwd_batch([m.desc_prepared if prepared else m.desc for m in mods], [int(x.shape[0]) for x in xs],
                         [x.data_ptr() for x in xs], [[t.data_ptr() for t in c] for c in cores],
                         [[v.data_ptr() for v in d] for d in D], [y.data_ptr() for y in outs],
-                        [b.data_ptr() for b in saved], [b.numel() for b in saved], _stream())
+                        [b.data_ptr() for b in saved], [_nbytes(b) for b in saved], _stream())
 
 
 def backward_data_batch(mods, xs, dys, cores, D, saved, scratch, dxs):
@@ -210,22 +250,30 @@ def backward_data_batch(mods, xs, dys, cores, D, saved, scratch, dxs):
         _need(x, "x", m.dtype, (T, m.n_in))
         _need(dy, "dy", m.dtype, (T, m.n_out))
         m._check_chain(c, d)
+    for m, x, dx in zip(mods, xs, dxs):
+        if dx is not None:
+            _need(dx, "dx", m.dtype, (int(x.shape[0]), m.n_in))
+    for b in list(saved) + list(scratch):
+        _need_buf(b, "saved/scratch")
     tt_linear_bwd_data_batch([m.desc for m in mods], [int(x.shape[0]) for x in xs], [x.data_ptr() for x in xs],
                              [dy.data_ptr() for dy in dys], [[t.data_ptr() for t in c] for c in cores],
                              [[v.data_ptr() for v in d] for d in D], [b.data_ptr() for b in saved],
-                             [b.numel() for b in saved], [None if t is None else t.data_ptr() for t in dxs],
-                             [b.data_ptr() for b in scratch], [b.numel() for b in scratch], _stream())
+                             [_nbytes(b) for b in saved], [None if t is None else t.data_ptr() for t in dxs],
+                             [b.data_ptr() for b in scratch], [_nbytes(b) for b in scratch], _stream())
 
 def backward_cores_batch(mods, T, cores, D, saved, scratch, dG):
     """TTLinear.backward_cores for several layers in one batched call on the
     current stream; each layer's backward_data must have run before."""
-    for m, c, d in zip(mods, cores, D):
+    for m, c, d, g in zip(mods, cores, D, dG):
         m._check_chain(c, d)
+        _need_grads(g, m.core_shapes)
+    for b in list(saved) + list(scratch):
+        _need_buf(b, "saved/scratch")
     tt_linear_bwd_cores_batch([m.desc for m in mods], [T] * len(mods),
                               [[t.data_ptr() for t in c] for c in cores], [[v.data_ptr() for v in d] for d in D],
-                              [b.data_ptr() for b in saved], [b.numel() for b in saved],
+                              [b.data_ptr() for b in saved], [_nbytes(b) for b in saved],
                               [[g.data_ptr() for g in gl] for gl in dG],
-                              [b.data_ptr() for b in scratch], [b.numel() for b in scratch], _stream())
+                              [b.data_ptr() for b in scratch], [_nbytes(b) for b in scratch], _stream())
 
 class TTMEmbedding:
     """A TTM embedding table: cores F_k (r_{k-1}, m_k, n_k, r_k) fp32."""
@@ -262,13 +310,16 @@ class TTMEmbedding:
         sb, cb = self.workspace(T)
         if out is None:
             out = torch.empty((T, self.dim), dtype=torch.float32, device=ids.device)
+        _need(out, "out", torch.float32, (T, self.dim))
         if saved is None:
             saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=ids.device)
         if scratch is None:
             scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=ids.device)
+        _need_buf(saved, "saved")
+        _need_buf(scratch, "scratch")
         ttm_embed_fwd(self.desc(), T, ids.data_ptr(), [c.data_ptr() for c in cores],
                       None if D is None else [v.data_ptr() for v in D], out.data_ptr(), saved.data_ptr(),
-                      saved.numel(), scratch.data_ptr(), scratch.numel(), _stream())
+                      _nbytes(saved), scratch.data_ptr(), _nbytes(scratch), _stream())
         return out, saved
 
     def index(self, ids, saved=None):
@@ -279,7 +330,7 @@ class TTMEmbedding:
         sb, _ = self.workspace(T)
         if saved is None:
             saved = torch.empty(max(sb, 256), dtype=torch.uint8, device=ids.device)
-        ttm_embed_index(self.desc(), T, ids.data_ptr(), saved.data_ptr(), saved.numel(), _stream())
+        ttm_embed_index(self.desc(), T, ids.data_ptr(), saved.data_ptr(), _nbytes(saved), _stream())
         return saved
 
     def lookup(self, T, cores, D, saved, out=None, scratch=None):
@@ -289,11 +340,14 @@ class TTMEmbedding:
         dev = cores[0].device
         if out is None:
             out = torch.empty((T, self.dim), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, (int(T), self.dim))
         if scratch is None:
             scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=dev)
+        _need_buf(saved, "saved")
+        _need_buf(scratch, "scratch")
         ttm_embed_lookup(self.desc(), int(T), [c.data_ptr() for c in cores],
                          None if D is None else [v.data_ptr() for v in D], out.data_ptr(), saved.data_ptr(),
-                         saved.numel(), scratch.data_ptr(), scratch.numel(), _stream())
+                         _nbytes(saved), scratch.data_ptr(), _nbytes(scratch), _stream())
         return out
 
     def backward(self, ids, dout, cores, D, saved, dF=None, accumulate=False, scratch=None):
@@ -306,18 +360,21 @@ class TTMEmbedding:
             scratch = torch.empty(max(cb, 256), dtype=torch.uint8, device=ids.device)
         if dF is None:
             dF = [torch.empty(s, dtype=torch.float32, device=ids.device) for s in self.core_shapes]
+        _need_grads(dF, self.core_shapes, "dF")
+        _need_buf(saved, "saved")
+        _need_buf(scratch, "scratch")
         ttm_embed_bwd(self.desc(accumulate), T, ids.data_ptr(), dout.data_ptr(), [c.data_ptr() for c in cores],
-                      None if D is None else [v.data_ptr() for v in D], saved.data_ptr(), saved.numel(),
-                      [g.data_ptr() for g in dF], scratch.data_ptr(), scratch.numel(), _stream())
+                      None if D is None else [v.data_ptr() for v in D], saved.data_ptr(), _nbytes(saved),
+                      [g.data_ptr() for g in dF], scratch.data_ptr(), _nbytes(scratch), _stream())
         return dF
 
 
 def rank_grads_batch(mods, cores, D, dG, dD, gamma=0.0, beta=0.0):
     """TTLinear.rank_grads for several layers in one launch on the current stream."""
-    for m, c, d, g in zip(mods, cores, D, dG):
+    for m, c, d, g, dd in zip(mods, cores, D, dG, dD):
         m._check_chain(c, d)
-        for t, s in zip(g, m.core_shapes):
-            _need(t, "dG", torch.float32, s)
+        _need_grads(g, m.core_shapes)
+        _need_grads(dd, [(s[2],) for s in m.core_shapes[:-1]], "dD")
     tt_linear_rank_grads_batch([m.desc for m in mods], [[t.data_ptr() for t in c] for c in cores],
                                [[v.data_ptr() for v in d] for d in D], [[t.data_ptr() for t in g] for g in dG],
                                [[v.data_ptr() for v in dd] for dd in dD], gamma, beta, _stream())

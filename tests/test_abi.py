@@ -379,3 +379,38 @@ def test_ttm_errors_before_launch():
     assert e.value.code == 6
     # T = 0 forward is a no-op
     ttc.ttm_embed_fwd(d, 0, None, F, None, None, None, 0, None, 0)
+
+
+def _explain_fields(d, T):
+    return dict(kv.split("=", 1) for kv in ttc.tt_linear_explain(d, T).split())
+
+
+@pytest.mark.parametrize("act,rank,in_modes,ok", [
+    (ttc.TTC_F32, 128, (2048, 2048), False),   # fp32 A operand: 128 x 2^22 x 4 B = 2^31 B
+    (ttc.TTC_BF16, 128, (2048, 2048), True),   # the same in bf16: 2^30 B
+    (ttc.TTC_F32, 32, (4096, 4096), False),    # fp32 A operand 32 x 2^24 x 4 B = 2^31 B
+    (ttc.TTC_BF16, 32, (4096, 4096), False),   # a 64-token bf16 slab of 2^24 columns = 2^31 B
+    (ttc.TTC_BF16, 32, (4096, 2048), True),
+])
+def test_buffer_resource_extents_are_bounded(act, rank, in_modes, ok):
+    """Every operand a streaming kernel reaches through a buffer resource is at
+    most 2^31 - 1 bytes: shapes beyond that are refused before any launch
+    instead of reading zeros past the resource's end."""
+    d = ttc.make_linear_desc((4,), in_modes, [1, rank, rank, 1], act)
+    if not ok:
+        with pytest.raises(ttc.TTCError) as e:
+            ttc.tt_linear_workspace(d, 64)
+        assert e.value.code == 7
+        return
+    ttc.tt_linear_workspace(d, 64)
+    # many tokens: the planner's token groups keep each work-group's slab of
+    # x, dY, its rank tile and the fp32 dZ partials within one resource
+    es = 2 if act == ttc.TTC_BF16 else 4
+    n_in = in_modes[0] * in_modes[1]
+    for T in (1 << 16, 1 << 20):
+        f = _explain_fields(d, T)
+        rpad = int(f["rpad"])
+        for pas, ncols in (("dy", 4), ("dx", n_in)):
+            toks = int(f[f"{pas}_tiles"]) * 64
+            assert toks * ncols * es <= 2**31 - 1, (pas, T, toks)
+            assert toks * rpad * 4 <= 2**31 - 1, (pas, T, toks)
