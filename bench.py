@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
 """TT-linear fwd+bwd throughput on one MI355X.
 
-One step = a TTM embedding lookup of the step's T ids (vocabulary 32^3 with
-modes (32,32,32), rows of 768 = (12,8,8), ranks (1,16,16,1), Zipf(1.1) ids),
-the forward pass of six TT-linear layers shaped like one encoder of the
-CoMERA pages' six-encoder transformer (Q, K, V, O 768->768 with modes
-(12,8,8)x(12,8,8); FFN 768->3072 and 3072->768 with 3072 = (12,16,16)),
-their backward passes in reverse order (input gradients and core gradients)
-and the embedding's backward into its core gradients, over T = 128 x 128 =
-16384 tokens; TT-linear activations bf16 with fp32 accumulation, TT rank 30
-with 40% of every link diagonal zeroed; the embedding is fp32.  Inputs are
-seeded synthetic data already resident in HBM.  --no-ttm drops the
-embedding from the step.
+One step = the forward pass of six TT-linear layers shaped like one encoder
+of the CoMERA pages' six-encoder transformer (Q, K, V, O 768->768 with modes
+(12,8,8)x(12,8,8); FFN 768->3072 and 3072->768 with 3072 = (12,16,16)) and
+their backward passes in reverse order (input gradients and core gradients),
+over T = 128 x 128 = 16384 tokens; activations bf16 with fp32 accumulation,
+TT rank 30 with 40% of every link diagonal zeroed.  That step is the headline
+(`value`).  The same run also times the step with a TTM embedding lookup of
+the step's T ids in front and its backward at the end (vocabulary 32^3 with
+modes (32,32,32), rows of 768 = (12,8,8), ranks (1,16,16,1), Zipf(1.1) ids,
+fp32), reported under `with_embedding` (--no-ttm skips it).
+
+Inputs are seeded synthetic data resident in HBM.  Consecutive steps read two
+different input sets (activations, output gradients, ids), so no step finds
+the previous step's inputs in the 256 MB memory-side cache.
 
 Prints one JSON line: the metric, the roofline of the dominant kernel and the
 oracle's CPU baseline.  One GPU only: --gpus above 1 is refused.
+
+The module-level helpers (make_layers, make_ttm, make_step) are the step the
+benchmark times; the full-size parity tests drive the same code.
 """
 
 from __future__ import annotations
@@ -22,9 +28,9 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import statistics
 import sys
 import time
+from dataclasses import dataclass
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -33,22 +39,23 @@ if ROOT not in sys.path:
 METRIC = "TT-linear fwd+bwd tokens/sec at d=768 r=30; achieved HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 RG_GAMMA, RG_BETA = 1e-3, 1e-5  # early-stage penalty weights for --rank-grads (values do not change the cost)
+N_SETS = 2  # input sets read by alternating steps
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 4])
     ap.add_argument("--rank", type=int, default=None)
-    ap.add_argument("--layers", type=int, default=None, help="with --config 4: number of encoder layers")
+    ap.add_argument("--layers", type=int, default=None, help="with --config 4: number of encoder layers (default 24)")
     ap.add_argument("--tokens", type=int, default=None,
                     help="tokens per step instead of the config's (batch x 128-token sequences, e.g. 128 for batch 1)")
     ap.add_argument("--eager", action="store_true", help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--single-stream", action="store_true",
                     help="run merges and core-gradient tails on the main stream too (no overlap)")
-    ap.add_argument("--no-ttm", action="store_true", help="time the TT-linear layers only")
+    ap.add_argument("--no-ttm", action="store_true", help="do not time the step with the embedding lookup")
     ap.add_argument("--ttm-mode", default="dedup", choices=["dedup", "unique", "plain"],
                     help="embedding lookup mode: distinct ids and shared prefixes (default), distinct ids only, "
                          "or every token on its own")
@@ -62,11 +69,15 @@ def parse():
                     help="run the merges on the side stream and the embedding lookup on the main one")
     ap.add_argument("--no-qkv-batch", action="store_true",
                     help="one launch per layer for the Q, K and V projections instead of one batched launch")
+    ap.add_argument("--one-input-set", action="store_true",
+                    help="every step reads the same inputs (they may then hit in the memory-side cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens of the CPU-baseline sample (default: the whole step for configs 1 and 2, "
+                         "2048 for config 4)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device three times (scale for the HBM byte counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def copy_calibration(mib):
@@ -115,7 +126,7 @@ def measured_traffic(kernel):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def step_bytes(layers, T, es):
+def step_bytes(specs, Ds, T, es):
     """Algorithmic HBM bytes of one fwd+bwd per layer (kernel-level split).
 
     fwd:    read x, write Y, write Z (T x r_eff fp32)
@@ -123,9 +134,9 @@ def step_bytes(layers, T, es):
     bwd_dx: read x, write dX
     """
     out = []
-    for L in layers:
-        s = L["spec"]
-        r_eff = int((L["D"][len(s.out_modes) - 1 if not s.in_first else len(s.in_modes) - 1] != 0).sum())
+    for s, D in zip(specs, Ds):
+        split = len(s.in_modes) if s.in_first else len(s.out_modes)
+        r_eff = int((D[split - 1] != 0).sum())
         out.append({
             "fwd": T * (s.n_in + s.n_out) * es + T * r_eff * 4,
             "bwd_dy": T * s.n_out * es + T * r_eff * 4,
@@ -135,191 +146,231 @@ def step_bytes(layers, T, es):
     return out
 
 
-def cpu_baseline(layers_host, T_cpu, ttm_host=None):
-    """The fp64 oracle, as it stands, on the first T_cpu tokens of every layer
-    (and of the embedding lookup when the step has one)."""
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover
+        blas = []
+    if not blas:
+        return "unknown", 1
+    p = blas[0]
+    return f"{p.get('internal_api', '?')} {p.get('version', '')}".strip(), int(p.get("num_threads", 1))
+
+
+def cpu_baseline(host, T_cpu):
+    """The fp64 oracle, as it stands, on the first T_cpu tokens of every given
+    layer; also the time of the same calls on 0 tokens (the work that does not
+    depend on the token count: weight reconstruction, core gradients)."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
+    def run(Tn):
+        t0 = time.perf_counter()
+        for L in host:
+            s = L["spec"]
+            x = L["x"][:Tn].astype(np.float64)
+            dy = L["dy"][:Tn].astype(np.float64)
+            oracle.tt_linear_forward(x, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
+            oracle.tt_linear_backward(x, dy, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
+        return time.perf_counter() - t0
 
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    t0 = time.perf_counter()
-    for L in layers_host:
-        s = L["spec"]
-        x = L["x"][:T_cpu].astype(np.float64)
-        dy = L["dy"][:T_cpu].astype(np.float64)
-        oracle.tt_linear_forward(x, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
-        oracle.tt_linear_backward(x, dy, s.out_modes, s.in_modes, L["cores"], L["D"], s.in_first)
-    what = f"all {len(layers_host)} TT-linear layers"
-    if ttm_host is not None:
-        oracle.ttm_forward(ttm_host["ids"][:T_cpu], ttm_host["cores"])
-        oracle.ttm_backward(ttm_host["ids"][:T_cpu], ttm_host["dout"][:T_cpu], ttm_host["cores"])
-        what = "the TTM embedding lookup and " + what
-    dt = time.perf_counter() - t0
-    return {"value": T_cpu / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd of {what} on the first {T_cpu} tokens "
-                      f"({dt:.1f} s wall)"}
+    t_fixed = run(0)
+    dt = run(T_cpu)
+    blas, threads = _blas_info()
+    return {"value": round(T_cpu / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd of {len(host)} TT-linear layers on the first {T_cpu} tokens "
+                      f"({dt:.1f} s wall; the same calls on 0 tokens take {t_fixed:.2f} s)",
+            "blas": blas, "blas_threads": threads, "affinity_cores": len(os.sched_getaffinity(0)),
+            "token_independent_s": round(t_fixed, 3), "wall_s": round(dt, 3)}
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+# ---- the step -------------------------------------------------------------------------
+
+@dataclass
+class StepOptions:
+    single_stream: bool = False   # merges and core-gradient tails on the main stream
+    qkv_batch: bool = True        # Q, K, V passes of an encoder in one launch each
+    index_ahead: bool = True      # embedding index built one step ahead, beside the step
+    merge_side: bool = False      # merges on the side stream, lookup on the main one
+    rank_grads: bool = False      # early-stage gradients after the core gradients
+
+
+def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None, clone_encoders=False):
+    """Device buffers of the step's TT-linear layers, in execution order.
+
+    Every layer has its own seeded cores, diagonals, x and dY (synth), uploaded
+    once and copied to n_sets device buffers (step s reads set s mod n_sets).
+    With clone_encoders the activations of encoder e > 0 are device copies of
+    encoder 0's (same shapes and values, separate memory; the cores are still
+    drawn per layer).  keep_host keeps the fp32 host arrays for the oracle.
+    """
     import numpy as np
     import torch
 
     import synth
     import tensor_train_compressed_tt_amd as ttc
 
-    cfg = args.config
-    rank = args.rank if args.rank is not None else (64 if cfg == 4 else 30)
-    T = args.tokens if args.tokens is not None else synth.CONFIG_TOKENS[cfg]
-    if not 1 <= T <= 16384:
-        sys.exit("--tokens must be in [1, 16384] (the embedding sorts at most 16384 ids per call)")
     zf = synth.CONFIG_ZERO_FRAC[cfg]
     dt = synth.CONFIG_DTYPE[cfg]
     specs = synth.config_layers(cfg, rank)
-    if cfg == 4 and args.layers is not None:
-        specs = specs[: 6 * args.layers]
+    if n_layers is not None:
+        specs = specs[:n_layers]
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-    es = 2 if dt == "bf16" else 4
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    # ---- inputs, resident in HBM ------------------------------------------------
     layers, host = [], []
-    max_scratch = 0
     for li, spec in enumerate(specs):
-        L = synth.make_tt_layer(cfg, li, spec, T, zf, dt)
+        fresh = not (clone_encoders and li >= 6)
+        L = synth.make_tt_layer(cfg, li, spec, T, zf, dt, acts=fresh)
         mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
-        cores = [torch.from_numpy(c).to(dev) for c in L["cores"]]
-        D = [torch.from_numpy(v).to(dev) for v in L["D"]]
-        if dt == "bf16":
-            x = torch.from_numpy(L["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
-            dy = torch.from_numpy(L["dy_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        if fresh:
+            if dt == "bf16":
+                x = torch.from_numpy(L["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+                dy = torch.from_numpy(L["dy_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+            else:
+                x = torch.from_numpy(L["x"]).to(dev)
+                dy = torch.from_numpy(L["dy"]).to(dev)
         else:
-            x = torch.from_numpy(L["x"]).to(dev)
-            dy = torch.from_numpy(L["dy"]).to(dev)
+            x, dy = layers[li % 6]["x"][0], layers[li % 6]["dy"][0]
         sb, cb = mod.workspace(T)
-        max_scratch = max(max_scratch, cb)
         layers.append({
-            "scratch": torch.empty(cb, dtype=torch.uint8, device=dev) if not args.single_stream else None,
-            "spec": spec, "mod": mod, "cores": cores, "D": D, "x": x, "dy": dy,
+            "spec": spec, "mod": mod,
+            "cores": [torch.from_numpy(c).to(dev) for c in L["cores"]],
+            "D": [torch.from_numpy(v).to(dev) for v in L["D"]],
+            "x": [x if (s == 0 and fresh) else x.clone() for s in range(n_sets)],
+            "dy": [dy if (s == 0 and fresh) else dy.clone() for s in range(n_sets)],
             "y": torch.empty((T, spec.n_out), dtype=tdt, device=dev),
             "dx": torch.empty((T, spec.n_in), dtype=tdt, device=dev),
             "dG": [torch.empty(s, dtype=torch.float32, device=dev) for s in mod.core_shapes],
-            "dD": [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in D],
+            "dD": [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in L["D"]],
             "saved": torch.empty(sb, dtype=torch.uint8, device=dev),
+            "scratch": torch.empty(cb, dtype=torch.uint8, device=dev),
         })
         keep = {"spec": spec, "cores": L["cores"], "D": L["D"]}
-        if not args.no_cpu_baseline and len(host) < 6:
-            keep["x"] = L["x"][: args.cpu_tokens].copy()
-            keep["dy"] = L["dy"][: args.cpu_tokens].copy()
+        if keep_host and fresh:
+            keep["x"], keep["dy"] = L["x"], L["dy"]
         host.append(keep)
         del L
-    scratch = torch.empty(max_scratch, dtype=torch.uint8, device=dev) if args.single_stream else None
-    sizes = step_bytes(host, T, es)
+    return layers, host
 
-    # ---- the embedding lookup of the step's T ids ------------------------------
-    ttm = None
-    ttm_host = None
-    if not args.no_ttm:
-        w = synth.make_ttm(3, T=T)
-        sp = w["spec"]
-        emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks,
-                               mode={"dedup": 0, "unique": 1, "plain": 2}[args.ttm_mode])
-        tsb, tcb = emb.workspace(T)
-        ttm = {"emb": emb, "F": [torch.from_numpy(c).to(dev) for c in w["cores"]],
-               "ids": torch.from_numpy(w["ids"]).to(dev), "dout": torch.from_numpy(w["dout"]).to(dev),
-               "out": torch.empty((T, sp.dim), dtype=torch.float32, device=dev),
-               "dF": [torch.empty(c.shape, dtype=torch.float32, device=dev) for c in w["cores"]],
-               "saved": torch.empty(tsb, dtype=torch.uint8, device=dev),
-               # the index of the next step's ids is built into the other buffer
-               "saved2": [torch.empty(tsb, dtype=torch.uint8, device=dev) for _ in range(2)],
-               "scratch": torch.empty(tcb, dtype=torch.uint8, device=dev), "d": len(sp.vocab_modes),
-               "dim": sp.dim}
-        if not args.no_cpu_baseline:
-            ttm_host = {"ids": w["ids"][: args.cpu_tokens].copy(), "dout": w["dout"][: args.cpu_tokens].copy(),
-                        "cores": w["cores"]}
-        del w
 
-    ahead = ttm is not None and not args.no_index_ahead and not args.single_stream
-    phase = [0]  # which of the two index buffers the current step looks up
+def make_ttm(T, dev, mode="dedup", n_sets=N_SETS, keep_host=False):
+    """The embedding of the step: one set of cores, n_sets id batches and row
+    gradients (set 0 from the base seed, set s from the base seed + s)."""
+    import torch
 
-    def ttm_saved():
-        return ttm["saved2"][phase[0]] if ahead else ttm["saved"]
+    import synth
+    import tensor_train_compressed_tt_amd as ttc
 
-    def ttm_fwd():
-        if ttm is None:
-            return
-        if ahead:
-            ttm["emb"].lookup(T, ttm["F"], None, ttm_saved(), out=ttm["out"], scratch=ttm["scratch"])
-        else:
-            ttm["emb"].forward(ttm["ids"], ttm["F"], None, out=ttm["out"], saved=ttm["saved"],
-                               scratch=ttm["scratch"])
+    sets = [synth.make_ttm(3, T=T, base=synth.BASE_SEED + s) for s in range(n_sets)]
+    sp = sets[0]["spec"]
+    emb = ttc.TTMEmbedding(sp.vocab_modes, sp.dim_modes, sp.ranks,
+                           mode={"dedup": 0, "unique": 1, "plain": 2}[mode])
+    tsb, tcb = emb.workspace(T)
+    ttm = {"emb": emb, "F": [torch.from_numpy(c).to(dev) for c in sets[0]["cores"]],
+           "ids": [torch.from_numpy(w["ids"]).to(dev) for w in sets],
+           "dout": [torch.from_numpy(w["dout"]).to(dev) for w in sets],
+           "out": torch.empty((T, sp.dim), dtype=torch.float32, device=dev),
+           "dF": [torch.empty(c.shape, dtype=torch.float32, device=dev) for c in sets[0]["cores"]],
+           "saved": torch.empty(tsb, dtype=torch.uint8, device=dev),
+           # one index buffer per phase: the next step's index is built into the other
+           "saved2": [torch.empty(tsb, dtype=torch.uint8, device=dev) for _ in range(2)],
+           "scratch": torch.empty(tcb, dtype=torch.uint8, device=dev), "dim": sp.dim}
+    host = None
+    if keep_host:
+        host = {"cores": sets[0]["cores"], "ids": [w["ids"] for w in sets], "dout": [w["dout"] for w in sets]}
+    return ttm, host
 
-    def ttm_index_next():
-        # the next step's ids are known before it starts (this synthetic
-        # workload repeats the same batch)
-        ttm["emb"].index(ttm["ids"], saved=ttm["saved2"][1 - phase[0]])
 
-    def ttm_bwd():
-        if ttm is not None:
-            ttm["emb"].backward(ttm["ids"], ttm["dout"], ttm["F"], None, ttm_saved(), dF=ttm["dF"],
-                                scratch=ttm["scratch"])
+def launch_groups(n_layers, qkv_batch=True):
+    """Launch groups of the streaming passes.  Within one encoder the Q, K and
+    V projections are independent (separate outputs), so each of their passes
+    is one batched launch; O, FFN1 and FFN2 depend on what comes before them
+    in the encoder and run one after another."""
+    fwd = []
+    for e in range(n_layers // 6):
+        qkv = [6 * e, 6 * e + 1, 6 * e + 2]
+        fwd += ([qkv] if qkv_batch else [[i] for i in qkv]) + [[6 * e + 3], [6 * e + 4], [6 * e + 5]]
+    fwd += [[i] for i in range(6 * (n_layers // 6), n_layers)]
+    return fwd, [g[::-1] for g in fwd[::-1]]
+
+
+def make_step(layers, T, ttm=None, opts=StepOptions()):
+    """step(ph): one fwd+bwd pass over every layer (and the embedding) reading
+    input set ph mod n_sets.  Consecutive steps must alternate ph = 0, 1, ...
+    when the embedding index is built ahead (call ttm_first_index first).
+    Returns (step, fwd_groups, bwd_groups)."""
+    import torch
+
+    import tensor_train_compressed_tt_amd as ttc
+
+    n_sets = len(layers[0]["x"])
+    fwd_groups, bwd_groups = launch_groups(len(layers), opts.qkv_batch and not opts.single_stream)
+    mods = [L["mod"] for L in layers]
+    col = lambda k: [L[k] for L in layers]
+    ahead = ttm is not None and opts.index_ahead and not opts.single_stream
     side = torch.cuda.Stream()  # default priority
 
-    def step_single():
-        ttm_fwd()
-        for L in layers:
-            L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"])
-        for L in reversed(layers):
-            L["mod"].backward(L["x"], L["dy"], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
-                              scratch=scratch)
-        ttm_bwd()
-
-    mods = [L["mod"] for L in layers]
-    all_cores = [L["cores"] for L in layers]
-    all_D = [L["D"] for L in layers]
-    # Launch groups of the streaming passes.  Within one encoder the Q, K and V
-    # projections are independent (same input, separate outputs), so each of
-    # their passes is one batched launch; O, FFN1 and FFN2 depend on what comes
-    # before them in the encoder and run one after another.
-    fwd_groups = []
-    for e in range(len(layers) // 6):
-        qkv = [6 * e, 6 * e + 1, 6 * e + 2]
-        fwd_groups += ([[i] for i in qkv] if args.no_qkv_batch else [qkv]) + [[6 * e + 3], [6 * e + 4], [6 * e + 5]]
-    bwd_groups = [g[::-1] for g in fwd_groups[::-1]]
-
-    def fwd_group(g):
-        if len(g) == 1:
-            L = layers[g[0]]
-            L["mod"].forward(L["x"], L["cores"], L["D"], out=L["y"], saved=L["saved"], prepared=True)
+    def ttm_fwd(ph):
+        if ttm is None:
+            return
+        s = ph % len(ttm["ids"])
+        if ahead:
+            ttm["emb"].lookup(T, ttm["F"], None, ttm["saved2"][ph % 2], out=ttm["out"], scratch=ttm["scratch"])
         else:
-            Ls = [layers[i] for i in g]
-            ttc.forward_batch([L["mod"] for L in Ls], [L["x"] for L in Ls], [L["cores"] for L in Ls],
+            ttm["emb"].forward(ttm["ids"][s], ttm["F"], None, out=ttm["out"], saved=ttm["saved"],
+                               scratch=ttm["scratch"])
+
+    def ttm_index_next(ph):
+        nxt = ph + 1
+        ttm["emb"].index(ttm["ids"][nxt % len(ttm["ids"])], saved=ttm["saved2"][nxt % 2])
+
+    def ttm_bwd(ph):
+        if ttm is not None:
+            s = ph % len(ttm["ids"])
+            ttm["emb"].backward(ttm["ids"][s], ttm["dout"][s], ttm["F"], None,
+                                ttm["saved2"][ph % 2] if ahead else ttm["saved"], dF=ttm["dF"],
+                                scratch=ttm["scratch"])
+
+    def fwd_group(g, s):
+        Ls = [layers[i] for i in g]
+        if len(Ls) == 1:
+            L = Ls[0]
+            L["mod"].forward(L["x"][s], L["cores"], L["D"], out=L["y"], saved=L["saved"], prepared=True)
+        else:
+            ttc.forward_batch([L["mod"] for L in Ls], [L["x"][s] for L in Ls], [L["cores"] for L in Ls],
                               [L["D"] for L in Ls], [L["y"] for L in Ls], [L["saved"] for L in Ls], prepared=True)
 
-    def bwd_group(g):
-        if len(g) == 1:
-            L = layers[g[0]]
-            L["mod"].backward_data(L["x"], L["dy"], L["cores"], L["D"], L["saved"], L["scratch"], dx=L["dx"])
+    def bwd_group(g, s):
+        Ls = [layers[i] for i in g]
+        if len(Ls) == 1:
+            L = Ls[0]
+            L["mod"].backward_data(L["x"][s], L["dy"][s], L["cores"], L["D"], L["saved"], L["scratch"], dx=L["dx"])
         else:
-            Ls = [layers[i] for i in g]
-            ttc.backward_data_batch([L["mod"] for L in Ls], [L["x"] for L in Ls], [L["dy"] for L in Ls],
+            ttc.backward_data_batch([L["mod"] for L in Ls], [L["x"][s] for L in Ls], [L["dy"][s] for L in Ls],
                                     [L["cores"] for L in Ls], [L["D"] for L in Ls], [L["saved"] for L in Ls],
                                     [L["scratch"] for L in Ls], [L["dx"] for L in Ls])
 
-    def step_overlap():
+    def cores_tail():
+        ttc.backward_cores_batch(mods[::-1], T, col("cores")[::-1], col("D")[::-1], col("saved")[::-1],
+                                 col("scratch")[::-1], col("dG")[::-1])
+        if opts.rank_grads:
+            ttc.rank_grads_batch(mods, col("cores"), col("D"), col("dG"), col("dD"), RG_GAMMA, RG_BETA)
+
+    def step_single(ph):
+        s = ph % n_sets
+        ttm_fwd(ph)
+        for L in layers:
+            L["mod"].forward(L["x"][s], L["cores"], L["D"], out=L["y"], saved=L["saved"])
+        for L in reversed(layers):
+            L["mod"].backward(L["x"][s], L["dy"][s], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
+                              scratch=L["scratch"])
+        if opts.rank_grads:
+            ttc.rank_grads_batch(mods, col("cores"), col("D"), col("dG"), col("dD"), RG_GAMMA, RG_BETA)
+        ttm_bwd(ph)
+
+    def step_overlap(ph):
         # The merges depend only on the cores and D, the core-gradient tails
         # produce only dG; each is one batched call for all layers.  The main
         # stream carries the merges and then the dependent chain of streaming
@@ -331,121 +382,141 @@ def main():
         # between two streaming passes.  With the index built in the step
         # (no index ahead) the lookup is the longer of the two and runs on the
         # main stream, the merges beside it.
+        s = ph % n_sets
         main = torch.cuda.current_stream()
         side.wait_stream(main)
-        if ahead and not args.merge_side:
-            # the lookup of the already indexed batch (shorter than the merges)
-            # on the side stream, then the index of the next batch (sort,
-            # distinct ids, prefix tree) beside this step's streaming passes;
-            # the forwards follow the merges on the main stream
+        if ttm is None:
+            ttc.prepare_batch(mods, T, col("cores"), col("D"), col("saved"))
+        elif ahead and not opts.merge_side:
             looked = torch.cuda.Event()
             with torch.cuda.stream(side):
-                ttm_fwd()
+                ttm_fwd(ph)
                 looked.record(side)
-                ttm_index_next()
-            ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
+                ttm_index_next(ph)
+            ttc.prepare_batch(mods, T, col("cores"), col("D"), col("saved"))
             main.wait_event(looked)
         else:
             merged = torch.cuda.Event()
             with torch.cuda.stream(side):
-                ttc.prepare_batch(mods, T, all_cores, all_D, [L["saved"] for L in layers])
+                ttc.prepare_batch(mods, T, col("cores"), col("D"), col("saved"))
                 merged.record(side)
                 if ahead:
-                    ttm_index_next()
-            ttm_fwd()
+                    ttm_index_next(ph)
+            ttm_fwd(ph)
             main.wait_event(merged)
         for g in fwd_groups:
-            fwd_group(g)
+            fwd_group(g, s)
         for g in bwd_groups:
-            bwd_group(g)
+            bwd_group(g, s)
         side.wait_stream(main)
-        ttm_bwd()
+        ttm_bwd(ph)
         with torch.cuda.stream(side):
-            ttc.backward_cores_batch(mods[::-1], T, all_cores[::-1], all_D[::-1],
-                                     [L["saved"] for L in layers][::-1], [L["scratch"] for L in layers][::-1],
-                                     [L["dG"] for L in layers][::-1])
-            if args.rank_grads:
-                ttc.rank_grads_batch(mods, all_cores, all_D, [L["dG"] for L in layers], [L["dD"] for L in layers],
-                                     RG_GAMMA, RG_BETA)
+            cores_tail()
         main.wait_stream(side)
-        phase[0] = 1 - phase[0]
 
-    step = step_single if args.single_stream else step_overlap
-
-    # ---- warm-up, optional graph capture --------------------------------------------
+    step = step_single if opts.single_stream else step_overlap
     if ahead:
-        ttm["emb"].index(ttm["ids"], saved=ttm["saved2"][0])  # the first step's index
-    for _ in range(max(1, args.warmup)):
-        step()
-    torch.cuda.synchronize()
-    graph = None
-    if not args.eager:
-        # with the index built one step ahead, the step alternates between two
-        # index buffers: one graph per phase, replayed in turn, or one graph of
-        # both steps (no drain between the two)
-        pair = args.graph_steps == 2 and args.steps % 2 == 0
-        graphs = []
-        for _ in range(1 if pair else 2 if ahead else 1):
+        step.first_index = lambda: ttm["emb"].index(ttm["ids"][0], saved=ttm["saved2"][0])
+    else:
+        step.first_index = lambda: None
+    return step, fwd_groups, bwd_groups
+
+
+class Runner:
+    """Runs a step eagerly or from captured HIP graphs, keeping the phase
+    (input set and index buffer) alternating from one step to the next."""
+
+    def __init__(self, step, eager=False, graph_steps=2):
+        self.step, self.eager, self.graph_steps = step, eager, graph_steps
+        self.ph = 0
+        self.graphs = None
+        step.first_index()
+
+    def eager_steps(self, n):
+        for _ in range(n):
+            self.step(self.ph)
+            self.ph ^= 1
+
+    def capture(self, pair):
+        import torch
+
+        assert self.ph == 0
+        self.pair = pair
+        self.graphs = []
+        for k in range(1 if pair else 2):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step()
                 if pair:
-                    step()
-            graphs.append(g)
+                    self.step(0)
+                    self.step(1)
+                else:
+                    self.step(k)
+            self.graphs.append(g)
         torch.cuda.synchronize()
-        turn = [0]
 
-        def replay():
-            graphs[turn[0]].replay()
-            turn[0] = (turn[0] + 1) % len(graphs)
+    def replay_steps(self, n):
+        """n steps from the graphs (n even with a two-step graph)."""
+        if self.pair:
+            assert n % 2 == 0 and self.ph == 0
+            for _ in range(n // 2):
+                self.graphs[0].replay()
+        else:
+            for _ in range(n):
+                self.graphs[self.ph].replay()
+                self.ph ^= 1
 
-        graph = graphs[0]
-        for _ in range(max(1, args.warmup) * len(graphs)):
-            replay()
+
+def time_step(step, steps, warmup, eager=False, graph_steps=2):
+    """ms per step over exactly `steps` timed steps (HIP events around the whole
+    run, after `warmup` untimed steps)."""
+    import torch
+
+    r = Runner(step, eager, graph_steps)
+    w = max(2, warmup + (warmup & 1))  # even: the timed run starts at phase 0
+    r.eager_steps(w)
+    torch.cuda.synchronize()
+    run = r.eager_steps
+    pair = graph_steps == 2 and steps % 2 == 0
+    if not eager:
+        r.capture(pair)
+        r.replay_steps(w)
         torch.cuda.synchronize()
-    run = replay if graph is not None else step
-    launches = args.steps // 2 if graph is not None and pair else args.steps
-
-    # ---- timed region -----------------------------------------------------------------
+        run = r.replay_steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(launches):
-        run()
+    run(steps)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
-    tokens_per_s = T / (ms_per_step / 1e3)
-    bytes_per_step = sum(s["fwd"] + s["bwd_dy"] + s["bwd_dx"] for s in sizes)
-    # embedding: read the ids, write the rows; read the row gradients
-    ttm_sizes = {} if ttm is None else {"ttm_sort": T * 8, "ttm_gather": T * ttm["dim"] * 4,
-                                        "ttm_seg": T * ttm["dim"] * 4}
-    bytes_per_step += sum(ttm_sizes.values())
-    step_gbps = bytes_per_step / (ms_per_step / 1e3) / 1e9
+    info = {"launch": "eager" if eager else "hip_graph_replay",
+            "steps_per_graph": None if eager else (2 if pair else 1)}
+    return start.elapsed_time(end) / steps, wall, info, r
 
-    # ---- per-kernel durations: the same steps, launched eagerly with HIP events
-    # recorded by the library around every kernel on its launch stream -----------------
+
+def trace_kernels(runner, steps):
+    """Per-kernel HIP-event durations of `steps` eager steps (the library
+    records a start and a stop event around every kernel on its stream)."""
+    import torch
+
+    import tensor_train_compressed_tt_amd as ttc
+
+    if runner.ph:
+        runner.eager_steps(1)
+    torch.cuda.synchronize()
     ttc.trace_start()
-    for _ in range(args.steps):
-        step()
+    runner.eager_steps(steps)
     torch.cuda.synchronize()
     ttc.trace_stop()
-    recs = ttc.trace_records()
-    per = {}
-    # layers of the k-th launch of a streaming kernel within one step: the
-    # forward runs over the launch groups in order, the backward passes in
-    # reverse (one launch per layer in the single-stream step)
-    nl = len(layers)
-    if args.single_stream:
-        fg = [[i] for i in range(nl)]
-        bg = fg[::-1]
-    else:
-        fg, bg = fwd_groups, bwd_groups
+    return ttc.trace_records()
+
+
+def kernel_table(recs, steps, sizes, groups, ttm_sizes):
+    """Per-kernel totals from trace records: ms, launches, algorithmic bytes."""
+    fg, bg = groups
     layer_of = {"fwd": fg, "bwd_dy": bg, "bwd_dx": bg}
-    ttm_names = {"ttm_sort", "ttm_lists", "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level", "ttm_reduce"}
-    counts = {}
+    per, counts = {}, {}
     for name, ms in recs:
         d = per.setdefault(name, {"ms": 0.0, "bytes": 0.0, "launches": 0})
         d["ms"] += ms
@@ -455,14 +526,59 @@ def main():
         if name in layer_of:
             grp = layer_of[name][k % len(layer_of[name])]
             d["bytes"] += sum(sizes[i].get(name, 0) for i in grp)
-        elif name in ttm_names:
-            d["bytes"] += ttm_sizes.get(name, 0)
+        elif name in ttm_sizes:
+            d["bytes"] += ttm_sizes[name]
     for name in layer_of:
-        assert counts.get(name, 0) == len(layer_of[name]) * args.steps, (name, counts.get(name))
+        assert counts.get(name, 0) == len(layer_of[name]) * steps, (name, counts.get(name))
     for d in per.values():
         d["avg_us"] = 1e3 * d["ms"] / d["launches"]
         d["gbps"] = d["bytes"] / (d["ms"] / 1e3) / 1e9 if d["bytes"] else None
-        d["ms_per_step"] = d["ms"] / args.steps
+        d["ms_per_step"] = d["ms"] / steps
+    return per
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    cfg = args.config
+    rank = args.rank if args.rank is not None else (64 if cfg == 4 else 30)
+    T = args.tokens if args.tokens is not None else synth.CONFIG_TOKENS[cfg]
+    if not 1 <= T <= 16384:
+        sys.exit("--tokens must be in [1, 16384] (the embedding sorts at most 16384 ids per call)")
+    dt = synth.CONFIG_DTYPE[cfg]
+    es = 2 if dt == "bf16" else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_layers = 6 * (args.layers if args.layers is not None else 24) if cfg == 4 else None
+    cpu_T = None if args.no_cpu_baseline else min(T, args.cpu_tokens or (2048 if cfg == 4 else T))
+    n_sets = 1 if args.one_input_set else N_SETS
+
+    # ---- inputs, resident in HBM ----------------------------------------------------
+    t_setup = time.perf_counter()
+    layers, host = make_layers(cfg, rank, T, dev, n_sets=n_sets, keep_host=cpu_T is not None, n_layers=n_layers,
+                               clone_encoders=(cfg == 4))
+    print(f"# {len(layers)} layers ready in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    specs = [L["spec"] for L in layers]
+    sizes = step_bytes(specs, [h["D"] for h in host], T, es)
+    opts = StepOptions(single_stream=args.single_stream, qkv_batch=not args.no_qkv_batch,
+                       index_ahead=not args.no_index_ahead, merge_side=args.merge_side, rank_grads=args.rank_grads)
+    tt_bytes = sum(s["fwd"] + s["bwd_dy"] + s["bwd_dx"] for s in sizes)
+
+    # ---- headline: the TT-linear layers alone -----------------------------------------
+    step, fg, bg = make_step(layers, T, None, opts)
+    ms_per_step, wall, launch, runner = time_step(step, args.steps, args.warmup, args.eager, args.graph_steps)
+    tokens_per_s = T / (ms_per_step / 1e3)
+    step_gbps = tt_bytes / (ms_per_step / 1e3) / 1e9
+    per = kernel_table(trace_kernels(runner, args.steps), args.steps, sizes, (fg, bg), {})
     stream_kernels = ["fwd", "bwd_dy", "bwd_dx"]
     dom = max(stream_kernels, key=lambda k: per[k]["ms"])
     roof = {
@@ -473,25 +589,45 @@ def main():
         "unit": "GB/s",
         "frac": round(per[dom]["gbps"] / HBM_PEAK_GBPS, 4),
         # the counter summaries were taken on the default workload only
-        "traffic": measured_traffic(dom) if (cfg, rank, T, args.rank_grads) == (2, 30, 16384, False) else None,
+        "traffic": measured_traffic(dom) if (cfg, rank, T, args.rank_grads, n_sets) == (2, 30, 16384, False, 2)
+        else None,
         "avg_launch_us": round(per[dom]["avg_us"], 2),
         "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
     }
 
-    ttm_summary = None
-    if ttm is not None:
-        tk = [k for k in per if k.startswith("ttm_")]
-        t_ms = sum(per[k]["ms_per_step"] for k in tk)
+    # ---- the same step with the embedding lookup and its backward ----------------------
+    with_emb = None
+    if not args.no_ttm:
+        ttm, _ = make_ttm(T, dev, args.ttm_mode, n_sets=n_sets)
+        stepe, fge, bge = make_step(layers, T, ttm, opts)
+        ms_e, _, _, runner_e = time_step(stepe, args.steps, args.warmup, args.eager, args.graph_steps)
+        ttm_sizes = {"ttm_sort": T * 8, "ttm_gather": T * ttm["dim"] * 4, "ttm_seg": T * ttm["dim"] * 4}
+        pere = kernel_table(trace_kernels(runner_e, args.steps), args.steps, sizes, (fge, bge), ttm_sizes)
+        tk = [k for k in pere if k.startswith("ttm_")]
+        t_ms = sum(pere[k]["ms_per_step"] for k in tk)
         tb = sum(ttm_sizes.values())
-        ttm_summary = {"kernel_us_per_step": round(1e3 * t_ms, 2), "algorithmic_bytes": tb,
-                       "gbps": round(tb / (t_ms / 1e3) / 1e9, 1)}
+        eb = tt_bytes + tb
+        with_emb = {
+            "ms_per_step": round(ms_e, 5), "tokens_per_s": round(T / (ms_e / 1e3), 1),
+            "algorithmic_bytes_per_step": eb, "hbm_gbps_step": round(eb / (ms_e / 1e3) / 1e9, 1),
+            "hbm_frac_step": round(eb / (ms_e / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "embedding_kernel_us_per_step": round(1e3 * t_ms, 2), "embedding_algorithmic_bytes": tb,
+            "embedding_gbps": round(tb / (t_ms / 1e3) / 1e9, 1),
+            "embedding_index": "built one step ahead on the side stream"
+            if (opts.index_ahead and not opts.single_stream) else "built in the step's forward",
+            "embedding": "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), fp32, Zipf(1.1) ids, "
+                         f"lookup mode {args.ttm_mode}",
+            "kernels_us_per_step": {k: round(1e3 * v["ms_per_step"], 2) for k, v in pere.items()},
+        }
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host[:6], min(args.cpu_tokens, T), ttm_host)
+    if cpu_T is not None:
+        cpu = cpu_baseline(host[:6], cpu_T)
 
     wl = {1: "one encoder's TT-linear set, fp32", 2: "one encoder's TT-linear set, bf16",
-          4: "CodeBERT-large-sized encoder stack"}[cfg]
+          4: "CodeBERT-large-sized encoder stack, bf16"}[cfg]
+    shapes = "4x 768->768, 768->3072, 3072->768" if cfg != 4 else \
+        f"{len(layers) // 6}x (4x 1024->1024, 1024->4096, 4096->1024)"
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -506,31 +642,24 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": f"{wl}{'' if ttm is None else ' + TTM embedding lookup of the same tokens'}: {len(specs)} TT-linear layers (fwd then bwd in reverse), "
-                        f"{'4x 768->768, 768->3072, 3072->768' if cfg != 4 else '24x (4x 1024->1024, 1024->4096, 4096->1024)'}, "
+            "workload": f"{wl}: {len(specs)} TT-linear layers (fwd then bwd in reverse), {shapes}, "
                         f"{dt} activations, fp32 accumulate, T={T} tokens, TT rank {rank}, "
-                        f"{int(zf * 100)}% of each link diagonal zeroed",
+                        f"{int(synth.CONFIG_ZERO_FRAC[cfg] * 100)}% of each link diagonal zeroed",
             "tokens": T,
             "rank": rank,
             "layers": len(specs),
-            "launch": "eager" if graph is None else "hip_graph_replay",
-            "steps_per_graph": None if graph is None else (2 if pair else 1),
+            "input_sets": n_sets,
             "qkv_batched": not (args.no_qkv_batch or args.single_stream),
-            "embedding_index": None if ttm is None else ("built one step ahead on the side stream" if ahead
-                                                         else "built in the step's forward"),
-            "merges": "side stream, beside the embedding lookup" if (args.merge_side or not ahead)
-                      else "main stream, the embedding lookup beside them on the side stream",
-            "rank_grads": bool(args.rank_grads and not args.single_stream),
+            "rank_grads": bool(args.rank_grads),
             "streams": 1 if args.single_stream else 2,
-            "embedding": None if ttm is None else "TTM 32^3 x 768, modes (32,32,32)x(12,8,8), ranks (1,16,16,1), "
-                                                  f"fp32, Zipf(1.1) ids, lookup mode {args.ttm_mode}",
+            **launch,
         },
         "hbm_gbps_step": round(step_gbps, 1),
         "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_step": bytes_per_step,
+        "algorithmic_bytes_per_step": tt_bytes,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in per.items()},
-        "embedding": ttm_summary,
+        "with_embedding": with_emb,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
