@@ -173,6 +173,30 @@ ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
                                ttc_stream_t grad_stream);
 
 /*
+ * tt_linear_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture that may not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the same computation, bitwise the same
+ * results, with the scratch buffer taken from a device array the library
+ * holds in each GPU's memory from its load to the end of the process, of
+ * TTC_NOALLOC_SCRATCH_BYTES bytes per GPU.  The caller still passes every
+ * input and output.  A shape whose scratch (tt_linear_workspace) is larger
+ * gives TTC_ERR_WORKSPACE before anything is enqueued; a failure to look the
+ * array up on the current device gives TTC_ERR_HIP.  Calls on one GPU share
+ * that array: two calls whose work overlaps on the device (different
+ * streams, or one call's stream not ordered after the other's) race and give
+ * wrong gradients; order them on one stream or with events.  This call itself
+ * allocates nothing and enqueues no memset; its first call on a device looks
+ * up the array's address (a host-side query, outside any stream).
+ */
+#define TTC_NOALLOC_SCRATCH_BYTES (64u << 20)
+ttc_status tt_linear_bwd_noalloc(const tt_linear_desc* desc, int64_t T,
+                                 const void* x, const void* dy,
+                                 const float* const* G, const float* const* D,
+                                 const void* saved, size_t saved_bytes,
+                                 void* dx, float* const* dG,
+                                 ttc_stream_t stream);
+
+/*
  * The backward in two calls, for callers that schedule the core-gradient
  * work themselves (e.g. the tails of many layers together, after every
  * layer's dX is done).  The split follows the merged contraction order of the

@@ -41,6 +41,7 @@ EXPORTS = [
     "tt_linear_explain",
     "tt_linear_prepare",
     "tt_linear_bwd_split",
+    "tt_linear_bwd_noalloc",
     "tt_linear_bwd_data",
     "tt_linear_bwd_cores",
     "tt_linear_prepare_batch",
@@ -123,6 +124,7 @@ def lib() -> ctypes.CDLL:
         "tt_linear_fwd": [D, _I64, _P, pp, pp, _P, _P, _SZ, _P, _SZ, _P],
         "tt_linear_bwd": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P],
         "tt_linear_bwd_split": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P, _SZ, _P, _P],
+        "tt_linear_bwd_noalloc": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, pp, _P],
         "tt_linear_bwd_data": [D, _I64, _P, _P, pp, pp, _P, _SZ, _P, _P, _SZ, _P],
         "tt_linear_bwd_cores": [D, _I64, pp, pp, _P, _SZ, pp, _P, _SZ, _P],
         "tt_linear_prepare": [D, _I64, pp, pp, _P, _SZ, _P],
@@ -241,6 +243,17 @@ def tt_linear_bwd_split(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, scratc
     code = lib().tt_linear_bwd_split(ctypes.byref(desc), T, x, dy, g, dd, saved, saved_bytes, dx, dg, scratch,
                                      scratch_bytes, stream, grad_stream)
     _check("tt_linear_bwd_split", code)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TTC_NOALLOC_SCRATCH_BYTES
+
+
+def tt_linear_bwd_noalloc(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, stream=0):
+    g, _ga = _ptrs(G)
+    dd, _da = _ptrs(D) if D is not None else (None, None)
+    dg, _dga = _ptrs(dG)
+    code = lib().tt_linear_bwd_noalloc(ctypes.byref(desc), T, x, dy, g, dd, saved, saved_bytes, dx, dg, stream)
+    _check("tt_linear_bwd_noalloc", code)
 
 
 def tt_linear_bwd_data(desc, T, x, dy, G, D, saved, saved_bytes, dx, scratch, scratch_bytes, stream=0):

@@ -2183,6 +2183,56 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
   return hip_status();
 }
 
+// ------------------------------------------------------------------------------
+// backward without a caller-provided scratch buffer
+// ------------------------------------------------------------------------------
+// For callers that cannot allocate device memory: the partial sums of the
+// backward live in one file-scope device array.  Every GPU the library runs
+// on holds its own copy until the process ends; calls on one GPU share it.
+namespace ttc {
+namespace noalloc {
+static __device__ __align__(256) unsigned char scratch[TTC_NOALLOC_SCRATCH_BYTES];
+}  // namespace noalloc
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_noalloc_mu;
+static void* g_noalloc_ptr[kMaxDevices];
+
+// Device address of the current device's copy of noalloc::scratch, looked up
+// once per device (with that device current).  In host code the array's name
+// is only a stand-in: kernels get this address, never the name.
+static ttc_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TTC_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc::scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return TTC_ERR_HIP;
+    }
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return TTC_OK;
+}
+}  // namespace ttc
+
+extern "C" ttc_status tt_linear_bwd_noalloc(const tt_linear_desc* desc, int64_t T, const void* x, const void* dy,
+                                            const float* const* G, const float* const* D, const void* saved,
+                                            size_t saved_bytes, void* dx, float* const* dG, ttc_stream_t stream) {
+  LinearPlan P;
+  ttc_status st = bwd_checks(desc, T, G, D, &P);
+  if (st != TTC_OK) return st;
+  if ((st = grads_checks(P, dG)) != TTC_OK) return st;
+  if (P.sc_total > (size_t)TTC_NOALLOC_SCRATCH_BYTES) return TTC_ERR_WORKSPACE;
+  void* sc = nullptr;
+  if ((st = noalloc_scratch(&sc)) != TTC_OK) return st;
+  // every byte the backward reads from its scratch is written earlier in the
+  // same call, so the array needs no clearing between calls
+  return tt_linear_bwd(desc, T, x, dy, G, D, saved, saved_bytes, dx, dG, sc, TTC_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 extern "C" ttc_status tt_linear_bwd_data(const tt_linear_desc* desc, int64_t T, const void* x, const void* dy,
                                          const float* const* G, const float* const* D, const void* saved,
                                          size_t saved_bytes, void* dx, void* scratch, size_t scratch_bytes,
