@@ -17,12 +17,12 @@
 // multiplication, which keeps dead-slice gradients exactly 0.
 //
 // Kernels (one stream, no host synchronisation, no allocation):
-//   k_sweep      (merge) the prefix / suffix products of both halves, one
-//                level of small fp32-MFMA GEMMs per launch, kept for the sweep
-//   k_pack       the compacted A, B (and transposes) in the activation dtype
-//                from the two half products and the live slices of D_s
+//   k_merge      both halves of the chain multiplied out, one prefix of the
+//                walk from each chain end per work-group: the prefix products
+//                kept for the sweep, the compacted A, B (and transposes) in
+//                the activation dtype
 //   k_fwd        per 64-token tile: Z = x A^T with the K range split over the
-//                4 waves (unrolled, many loads in flight), Z summed in LDS and
+//                waves (unrolled, many loads in flight), Z summed in LDS and
 //                kept, then Y^T = B Z^T with the B fragments prefetched
 //   k_bwd_dy     per (column group, token group): 64 x 256-byte slabs of dY
 //                stream through LDS with register prefetch; dZ (or its
@@ -56,95 +56,226 @@ struct ChainPtrs {
 // ------------------------------------------------------------------------------
 // merge
 // ------------------------------------------------------------------------------
-// The products of the two halves are formed level by level as small GEMMs
-// (k_sweep, see the reverse sweep below):
-//   left   M_k = (M_{k-1} diag(D_{k-1})) G_k      (prod n_{<=k}) x r_{k+1}
-//   right  N_k = G_k diag(D_k) N_{k+1}            r_k x (prod n_{>=k})
-// The prefix / suffix products below the split stay in the chain area for the
-// backward sweep; the full halves L = M_{s-1} and R = N_s are then packed by
-// k_pack into the MFMA operands A = diag(D_s) R and B = L (roles swapped when
-// the chain starts with the input modes), keeping only the live slices of the
-// split link: entries of D_s that are exactly zero are dropped on the device.
-struct PackArgs {
-  const float* L;     // NL x rs (row-major)
-  const float* R;     // rs x NRt
-  const float* Ds;    // diagonal of the split link
-  const float* G0;    // copied into the chain area when the left half has more cores
-  const float* Gl;    // (last core) likewise for the right half
-  float* chain0;      // chain area of M_0, or null
-  float* chainl;      // chain area of N_{d-1}, or null
-  int64_t n0, nl;     // floats of G_0 / G_{d-1}
-  int rs, Rpad, in_first;
-  int64_t NL, NRt, N_in, N_out;
-  int* meta;
+// Each half of the chain is multiplied out one row (left half) or one column
+// (right half) at a time, walking from the chain's end towards the split
+// link s:
+//   left   v_0 = G_0[0, i_0, :],     v_t = (v_{t-1} diag(D_{t-1})) G_t[:, i_t, :]
+//   right  w_0 = G_{d-1}[:, j, 0],   w_t = G_k[:, j_k, :] diag(D_k) w_{t-1}   (k = d-1-t)
+// The walk's last step is the core next to the split; every other step
+// belongs to a prefix (the digits of the cores before it).  A work-group owns
+// kMergePG consecutive prefixes: it forms their prefix products once (the
+// chain area the backward sweep reads: rows M_t of the left half, columns N_k
+// of the right half, each written by exactly one work-group), then loops over
+// the last core's mode with that core's slices staged in LDS.  The rows and
+// columns of the two half products go straight into the MFMA operands in the
+// activation dtype, keeping only the live slices of the split link:
+// B = L and A = diag(D_s) R (roles swapped when the chain starts with the
+// input modes), each also transposed, zero-padded to Rpad.  One launch per
+// activation dtype for up to kMaxMerge layers.
+// Layers per launch of the batched reductions.
+constexpr int kMaxBatch = 8;
+
+struct MergeLayer {
+  const float* G[kMaxCores];
+  const float* D[kMaxCores];  // D[k] on the link between cores k and k+1
+  float* chain;               // prefix / suffix products (fp32)
+  int64_t chain_off[kMaxCores];
+  int modes[kMaxCores];
+  int ranks[kMaxCores + 1];
   void* Ac;
   void* AcT;
   void* Bc;
   void* BcT;
+  int* meta;
+  int64_t N_in, N_out;
+  int64_t npl, npr;  // prefixes of the left and the right half
+  int64_t wgl;       // work-groups of the left half (the rest: right half)
+  int d, s, in_first, rs, Rpad;
 };
-
-// Layers packed by one launch; work-group i belongs to the layer q with
-// first[q] <= i < first[q + 1].
-constexpr int kMaxBatch = 8;
-struct PackBatch {
-  PackArgs p[kMaxBatch];
-  int64_t first[kMaxBatch + 1];
+constexpr int kMaxMerge = 6;
+struct MergeBatch {
+  MergeLayer l[kMaxMerge];
+  int64_t first[kMaxMerge + 1];
   int n;
 };
+static_assert(sizeof(MergeBatch) <= 4000, "MergeBatch too large for a kernel argument");
 
-// One wave per row of L (items [0, NL)) or column of R (the rest).
+constexpr int kMergeThreads = 512;
+constexpr int kMergePG = 8;      // prefixes per work-group
+constexpr int kMergeOut = 8192;  // floats of staged outputs ([pg][mode chunk][rank])
+constexpr int kMergeX = 32;      // core values per thread loaded before they are used
+
+// One output of a walk step for up to kMergePG prefixes at once:
+//   acc[pg] += sum_x v[pg][x] * G(x), x < rin,
+// with the rin core values G(x) = g[x * sx] requested in batches of kMergeX
+// (a plain loop would wait for each load in turn) and v read from LDS.
+__device__ __forceinline__ void merge_dot(float (&acc)[kMergePG], const float* __restrict__ g, int64_t sx,
+                                          int rin, const float* v) {
+  for (int x0 = 0; x0 < rin; x0 += kMergeX) {
+    float gv[kMergeX];
+#pragma unroll
+    for (int u = 0; u < kMergeX; ++u) gv[u] = x0 + u < rin ? g[(int64_t)(x0 + u) * sx] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kMergeX; ++u) {
+      if (x0 + u < rin) {
+#pragma unroll
+        for (int pg = 0; pg < kMergePG; ++pg) acc[pg] = fmaf(v[pg * TTC_MAX_RANK + x0 + u], gv[u], acc[pg]);
+      }
+    }
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(64) void k_pack(PackBatch pb) {
+__global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   typedef typename Elem<T>::type E;
-  __shared__ int live[TTC_MAX_RANK];
-  const int lane = threadIdx.x;
+  __shared__ float ob[kMergeOut];                          // [pg][ii][rout] outputs of the last step
+  __shared__ float vb[2][kMergePG * TTC_MAX_RANK];         // prefix vectors (D applied)
+  __shared__ int live[TTC_MAX_RANK], pos[TTC_MAX_RANK];
+  __shared__ int s_reff;
   int q = 0;
-  while (q < pb.n - 1 && (int64_t)blockIdx.x >= pb.first[q + 1]) ++q;
-  const PackArgs& a = pb.p[q];
-  const int64_t item = (int64_t)blockIdx.x - pb.first[q];
+  while (q < mb.n - 1 && (int64_t)blockIdx.x >= mb.first[q + 1]) ++q;
+  const MergeLayer& a = mb.l[q];
+  const int tid = threadIdx.x;
+  int64_t wg = (int64_t)blockIdx.x - mb.first[q];
+  const bool left = wg < a.wgl;
+  if (!left) wg -= a.wgl;
+  const int d = a.d, s = a.s;
+  const int S = left ? s : d - s;  // cores in this half
+  const int64_t NP = left ? a.npl : a.npr;
+  const int64_t p0 = wg * kMergePG;
+  const int npg = (int)(NP - p0 < kMergePG ? NP - p0 : kMergePG);
+  const float* Ds = a.D[s - 1];
   // live entries of the split link's diagonal, in increasing link index
-  const bool f0 = lane < a.rs && a.Ds[lane] != 0.0f;
-  const bool f1 = lane + 64 < a.rs && a.Ds[lane + 64] != 0.0f;
-  const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  const int c0 = __popcll(m0);
-  const int reff = c0 + __popcll(m1);
-  live[lane] = -1;
-  live[lane + 64] = -1;
+  if (tid < 64) {
+    const int lane = tid;
+    const bool f0 = lane < a.rs && Ds[lane] != 0.0f;
+    const bool f1 = lane + 64 < a.rs && Ds[lane + 64] != 0.0f;
+    const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int c0 = __popcll(m0);
+    const int i0 = __popcll(m0 & below), i1 = c0 + __popcll(m1 & below);
+    pos[lane] = f0 ? i0 : -1;
+    pos[lane + 64] = f1 ? i1 : -1;
+    live[lane] = -1;
+    live[lane + 64] = -1;
+    __builtin_amdgcn_wave_barrier();
+    if (f0) live[i0] = lane;
+    if (f1) live[i1] = lane + 64;
+    if (lane == 0) s_reff = c0 + __popcll(m1);
+  }
+  for (int e = tid; e < kMergePG; e += kMergeThreads) vb[0][e * TTC_MAX_RANK] = 1.0f;
   __syncthreads();
-  if (f0) live[__popcll(m0 & below)] = lane;
-  if (f1) live[c0 + __popcll(m1 & below)] = lane + 64;
-  __syncthreads();
-  if (item == 0) {
-    for (int j = lane; j < TTC_MAX_RANK; j += 64) {
+  const int reff = s_reff;
+  if (left && wg == 0) {
+    for (int j = tid; j < TTC_MAX_RANK; j += kMergeThreads) {
       a.meta[kMetaLive + j] = live[j];
-      a.meta[kMetaPos + j] = -1;
+      a.meta[kMetaPos + j] = pos[j];
+    }
+    if (tid == 0) a.meta[kMetaReff] = reff;
+  }
+
+  // Prefix walk, steps 0..S-2: thread (y, pg-group) forms output y of the
+  // step for every prefix of the work-group; the digit of step t of prefix p
+  // has step 0 most significant on the left and least significant on the
+  // right.  The next step's input is this output times the link diagonal.
+  int cur = 0;
+  int64_t divL = 1;  // left: product of the modes of steps t+1..S-2
+  for (int t = 1; t <= S - 2; ++t) divL *= a.modes[t];
+  int64_t mulR = 1;  // right: product of the modes of steps 0..t
+  for (int t = 0; t < S - 1; ++t) {
+    const int k = left ? t : d - 1 - t;
+    const int n = a.modes[k];
+    const int rin = left ? a.ranks[k] : a.ranks[k + 1];
+    const int rout = left ? a.ranks[k + 1] : a.ranks[k];
+    if (!left) mulR *= n;
+    const float* G = a.G[k];
+    // diagonal applied to this step's output before the next step
+    const float* Dn = left ? a.D[k] : a.D[k - 1];
+    float* ch = a.chain + a.chain_off[k];
+    for (int e = tid; e < npg * rout; e += kMergeThreads) {
+      const int pg = e / rout, y = e - pg * rout;
+      const int64_t p = p0 + pg;
+      const int dg = left ? (int)((p / divL) % n) : (int)((p / (mulR / n)) % n);
+      const float* g = left ? G + (int64_t)dg * rout + y : G + ((int64_t)y * n + dg) * rin;
+      const int64_t sx = left ? (int64_t)n * rout : 1;
+      const float* v = vb[cur] + pg * TTC_MAX_RANK;
+      float acc = 0.f;
+      for (int x0 = 0; x0 < rin; x0 += kMergeX) {
+        float gv[kMergeX];
+#pragma unroll
+        for (int u = 0; u < kMergeX; ++u) gv[u] = x0 + u < rin ? g[(int64_t)(x0 + u) * sx] : 0.f;
+#pragma unroll
+        for (int u = 0; u < kMergeX; ++u)
+          if (x0 + u < rin) acc = fmaf(v[x0 + u], gv[u], acc);
+      }
+      vb[cur ^ 1][pg * TTC_MAX_RANK + y] = acc * Dn[y];
+      // one writer per chain row: the prefix whose later digits are all 0
+      if (left) {
+        if (p % divL == 0) ch[(p / divL) * rout + y] = acc;
+      } else if (p < mulR) {
+        ch[(int64_t)y * mulR + p] = acc;
+      }
     }
     __syncthreads();
-    for (int j = lane; j < reff; j += 64) a.meta[kMetaPos + live[j]] = j;
-    if (lane == 0) a.meta[kMetaReff] = reff;
-    if (a.chain0)
-      for (int64_t i = lane; i < a.n0; i += 64) a.chain0[i] = a.G0[i];
-    if (a.chainl)
-      for (int64_t i = lane; i < a.nl; i += 64) a.chainl[i] = a.Gl[i];
+    cur ^= 1;
+    if (left && t + 1 <= S - 2) divL /= a.modes[t + 1];
   }
-  const bool left = item < a.NL;
-  const int64_t idx = left ? item : item - a.NL;
-  // left rows are B rows unless the chain starts with the input modes
+
+  // Last step: the core next to the split, all its mode indices for all the
+  // prefixes, in chunks of ci mode indices; outputs staged in LDS, then
+  // written as rows of the packed operand and of its transpose.
+  const int kf = left ? s - 1 : s;
+  const int n = a.modes[kf];
+  const int rin = left ? a.ranks[kf] : a.ranks[kf + 1];
+  const int rout = a.rs;
+  const float* G = a.G[kf];
   const bool is_b = left != (a.in_first != 0);
-  for (int j = lane; j < a.Rpad; j += 64) {
-    const int b = j < reff ? live[j] : -1;
-    float v = 0.f;
-    if (b >= 0) v = left ? a.L[idx * a.rs + b] : a.R[(int64_t)b * a.NRt + idx];
-    if (is_b) {
-      const E val = (E)Mma<T>::from_f32(v);
-      ((E*)a.Bc)[idx * a.Rpad + j] = val;
-      ((E*)a.BcT)[(int64_t)j * a.N_out + idx] = val;
-    } else {
-      const E val = (E)Mma<T>::from_f32(b >= 0 ? a.Ds[b] * v : 0.f);
-      ((E*)a.Ac)[(int64_t)j * a.N_in + idx] = val;
-      ((E*)a.AcT)[idx * a.Rpad + j] = val;
+  // B is kept as [N_out][Rpad] (Bc) and [Rpad][N_out] (BcT), A as [Rpad][N_in]
+  // (Ac) and [N_in][Rpad] (AcT): `out` is the [N][Rpad] one, `outT` the other
+  E* out = reinterpret_cast<E*>(is_b ? a.Bc : a.AcT);
+  E* outT = reinterpret_cast<E*>(is_b ? a.BcT : a.Ac);
+  const int64_t Nlong = is_b ? a.N_out : a.N_in;
+  const int Rpad = a.Rpad;
+  int ci = kMergeOut / (kMergePG * rout);
+  if (ci > n) ci = n;
+  const float* v = vb[cur];
+  for (int i0 = 0; i0 < n; i0 += ci) {
+    const int ni = n - i0 < ci ? n - i0 : ci;
+    for (int e = tid; e < ni * rout; e += kMergeThreads) {
+      const int ii = e / rout, y = e - ii * rout;
+      const float* g = left ? G + (int64_t)(i0 + ii) * rout + y : G + ((int64_t)y * n + i0 + ii) * rin;
+      float acc[kMergePG];
+#pragma unroll
+      for (int pg = 0; pg < kMergePG; ++pg) acc[pg] = 0.f;
+      merge_dot(acc, g, left ? (int64_t)n * rout : 1, rin, v);
+#pragma unroll
+      for (int pg = 0; pg < kMergePG; ++pg)
+        if (pg < npg) ob[(pg * ci + ii) * rout + y] = acc[pg];
     }
+    __syncthreads();
+    // packed operand rows [idx][Rpad] and the transpose [Rpad][Nlong]
+    for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
+      const int pg = e / (ni * Rpad);
+      const int r = e - pg * ni * Rpad;
+      const int ii = r / Rpad, j = r - ii * Rpad;
+      const int b = j < reff ? live[j] : -1;
+      const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
+      const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? Ds[b] * val : val);
+      const int64_t idx = left ? (p0 + pg) * n + i0 + ii : (int64_t)(i0 + ii) * NP + p0 + pg;
+      out[idx * Rpad + j] = ev;
+    }
+    for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
+      const int j = e / (npg * ni);
+      const int r = e - j * npg * ni;
+      const int pg = left ? r / ni : r % npg;
+      const int ii = left ? r % ni : r / npg;
+      const int b = j < reff ? live[j] : -1;
+      const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
+      const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? Ds[b] * val : val);
+      const int64_t idx = left ? (p0 + pg) * n + i0 + ii : (int64_t)(i0 + ii) * NP + p0 + pg;
+      outT[(int64_t)j * Nlong + idx] = ev;
+    }
+    __syncthreads();
   }
 }
 
@@ -1191,7 +1322,6 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceBatch rb) {
 struct Gemm {
   const float* A;
   int64_t sAi, sAk;
-  const float* ks_;  // optional scale of A's columns (the reduction index), e.g. a link diagonal
   const float* B;
   int64_t sBk, sBj;
   const float* rs_;
@@ -1203,100 +1333,70 @@ struct Gemm {
 
 __host__ __device__ inline int gemm_tiles(const Gemm& g) { return ((g.M + 31) / 32) * ((g.N + 31) / 32); }
 
-constexpr int kGKC = 128;          // k-chunk staged per round
-constexpr int kGLong = kGKC + 4;   // row stride when a whole chunk of k is contiguous
-constexpr int kGShort = 48;        // row stride when 32 tile entries are contiguous
-constexpr int kGStage = kGKC * kGShort > 32 * kGLong ? kGKC * kGShort : 32 * kGLong;
+// One 32 x 32 output tile per work-group of kSweepWaves waves with fp32 MFMA
+// 16x16x4.  These GEMMs are small (K up to a few hundred), so the time of a
+// tile is the latency of its loads: wave w takes the k-steps w, w + 16, ...
+// and requests kSweepBatch of them (all its loads for K <= 512) straight into
+// registers before multiplying, so a tile costs about one memory round trip.
+// The waves' partial tiles are then added in wave order through LDS (fixed
+// order, bitwise reproducible).
+constexpr int kSweepWaves = 16;
+constexpr int kSweepThreads = 64 * kSweepWaves;
+constexpr int kSweepBatch = 8;
+constexpr int kSweepRedLd = 33;
+constexpr size_t kSweepLds = (size_t)kSweepWaves * 32 * kSweepRedLd * 4;
 
-// One 32 x 32 output tile by 256 threads with fp32 MFMA 16x16x4: operands
-// staged in 128-deep k-chunks in LDS, each in the orientation that keeps its
-// global reads coalesced (strides chosen so that neither the staging writes nor
-// the fragment reads conflict on LDS banks); the four waves split the k-steps
-// of a chunk and their partial tiles are summed in wave order at the end.
-template <bool KS>
-__device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
+__device__ void gemm_tile32(const Gemm& g, int tile, float* red) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, c = lane & 15;
   const int ntj = (g.N + 31) / 32;
   const int64_t i0 = (int64_t)(tile / ntj) * 32, j0 = (int64_t)(tile % ntj) * 32;
-  float* As = lds;
-  float* Bs = lds + kGStage;
-  const bool a_kfast = g.sAk == 1, b_jfast = g.sBj == 1;
   f32x4 acc[2][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[p][q] = zero4();
-  // the operands of chunk k0 + kGKC are requested before chunk k0 is
-  // multiplied, so the global latency of one chunk hides behind the MFMA
-  // work of the previous one
-  float ra[16], rb[16];
-  auto load_chunk = [&](int k0) {
+  const int nks = (g.K + 3) / 4;  // k-steps of four
+  for (int kb = w; kb < nks; kb += kSweepWaves * kSweepBatch) {
+    float fa[kSweepBatch][2], fb[kSweepBatch][2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int le = tid + 256 * e;
-      const int i = a_kfast ? le / kGKC : le % 32;
-      const int k = a_kfast ? le % kGKC : le / 32;
-      const bool ok = k0 < g.K && i0 + i < g.M && k0 + k < g.K;
-      const float v = g.A[ok ? (i0 + i) * g.sAi + (k0 + k) * g.sAk : 0];
-      ra[e] = ok ? (KS ? v * g.ks_[k0 + k] : v) : 0.f;
-      const int j = b_jfast ? le % 32 : le / kGKC;
-      const int k2 = b_jfast ? le / 32 : le % kGKC;
-      const bool ok2 = k0 < g.K && j0 + j < g.N && k0 + k2 < g.K;
-      const float v2 = g.B[ok2 ? (k0 + k2) * g.sBk + (j0 + j) * g.sBj : 0];
-      rb[e] = ok2 ? v2 : 0.f;
-    }
-  };
-  load_chunk(0);
-  for (int k0 = 0; k0 < g.K; k0 += kGKC) {
-    lds_barrier();
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int le = tid + 256 * e;
-      if (a_kfast)
-        As[(le / kGKC) * kGLong + le % kGKC] = ra[e];
-      else
-        As[(le / 32) * kGShort + le % 32] = ra[e];
-      if (b_jfast)
-        Bs[(le / 32) * kGShort + le % 32] = rb[e];
-      else
-        Bs[(le / kGKC) * kGLong + le % kGKC] = rb[e];
-    }
-    lds_barrier();
-    if (k0 + kGKC < g.K) load_chunk(k0 + kGKC);
-#pragma unroll
-    for (int st = 0; st < kGKC / 16; ++st) {
-      const int kk = (4 * st + w) * 4 + gq;  // k-step 4*st+w of this wave
-      float fa[2], fb[2];
+    for (int u = 0; u < kSweepBatch; ++u) {
+      const int64_t k = (int64_t)(kb + u * kSweepWaves) * 4 + gq;
+      const bool kok = k < g.K;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const int i = 16 * p + c;
-        fa[p] = a_kfast ? As[i * kGLong + kk] : As[kk * kGShort + i];
-        fb[p] = b_jfast ? Bs[kk * kGShort + i] : Bs[i * kGLong + kk];
+        const int64_t i = i0 + 16 * p + c;
+        const bool ok = kok && i < g.M;
+        const float v = g.A[ok ? i * g.sAi + k * g.sAk : 0];
+        fa[u][p] = ok ? v : 0.f;
+        const int64_t j = j0 + 16 * p + c;
+        const bool ok2 = kok && j < g.N;
+        const float v2 = g.B[ok2 ? k * g.sBk + j * g.sBj : 0];
+        fb[u][p] = ok2 ? v2 : 0.f;
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kSweepBatch; ++u)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[p], fb[q], acc[p][q], 0, 0, 0);
-    }
+        for (int q = 0; q < 2; ++q) acc[p][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[u][p], fb[u][q], acc[p][q], 0, 0, 0);
   }
-  lds_barrier();
   // lane (gq, c) of sub-tile (p, q) holds rows 16p+4gq+v, column 16q+c
-  float* red = lds;  // [4 waves][32][33]
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[(w * 32 + 16 * p + 4 * gq + v) * 33 + 16 * q + c] = acc[p][q][v];
+      for (int v = 0; v < 4; ++v) red[(w * 32 + 16 * p + 4 * gq + v) * kSweepRedLd + 16 * q + c] = acc[p][q][v];
   lds_barrier();
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int idx = tid + 256 * e;
-    const int i = idx >> 5, j = idx & 31;
+  {
+    const int i = tid >> 5, j = tid & 31;
     const int64_t gi = i0 + i, gj = j0 + j;
     if (gi < g.M && gj < g.N) {
-      const float sum = ((red[i * 33 + j] + red[(32 + i) * 33 + j]) + red[(64 + i) * 33 + j]) + red[(96 + i) * 33 + j];
+      float sum = red[i * kSweepRedLd + j];
+#pragma unroll
+      for (int v = 1; v < kSweepWaves; ++v) sum += red[(v * 32 + i) * kSweepRedLd + j];
       const float rsc = g.rs_ ? g.rs_[gi] : 1.f;
       const float csc = g.cs_ ? g.cs_[gj] : 1.f;
       g.C[gi * g.sCi + gj * g.sCj] = (sum * rsc) * csc;
@@ -1304,9 +1404,9 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* lds) {
   }
 }
 
-// One level of the reverse sweep (or of the merge) for one or more layers:
-// up to kMaxGemm independent GEMMs (per half and layer, the core gradient and
-// the gradient passed on to the next core), one 32 x 32 tile per work-group.
+// One level of the reverse sweep for one or more layers: up to kMaxGemm
+// independent GEMMs (per half and layer, the core gradient and the gradient
+// passed on to the next core), one 32 x 32 tile per work-group.
 constexpr int kMaxGemm = 24;
 struct SweepArgs {
   Gemm g[kMaxGemm];
@@ -1316,19 +1416,15 @@ struct SweepArgs {
 
 // kernel arguments stay inside the 4 KB argument segment
 static_assert(sizeof(SweepArgs) <= 3072, "SweepArgs too large for a kernel argument");
-static_assert(sizeof(PackBatch) <= 2048, "PackBatch too large for a kernel argument");
 
-// KS: the GEMMs scale A's columns by ks_ (the merge levels); the sweep's
-// GEMMs do not, and keep the register budget of the plain tile
-template <bool KS>
-__global__ __launch_bounds__(256) void k_sweep(SweepArgs a) {
-  __shared__ __align__(16) float lds[2 * kGStage];
+__global__ __launch_bounds__(kSweepThreads) void k_sweep(SweepArgs a) {
+  extern __shared__ __align__(16) char smem[];
   int t = blockIdx.x, q = 0;
   while (q < a.ng - 1 && t >= a.tiles[q]) {
     t -= a.tiles[q];
     ++q;
   }
-  gemm_tile32<KS>(a.g[q], t, lds);
+  gemm_tile32(a.g[q], t, reinterpret_cast<float*>(smem));
 }
 
 // Left core k, gradient dM_k of the prefix M_k (rows prod_{j<=k} n_j, r_{k+1}
@@ -1339,7 +1435,6 @@ static Gemm left_dG(const LinearPlan& P, const float* chain, const float* const*
                     const float* dMk, int64_t rows) {
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   Gemm g;
-  g.ks_ = nullptr;
   g.A = chain + P.chain_off[k - 1];
   g.sAi = 1;
   g.sAk = r0;
@@ -1360,7 +1455,6 @@ static Gemm left_dM(const LinearPlan& P, const float* const* G, const float* con
                     int64_t rows, float* out) {
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   Gemm g;
-  g.ks_ = nullptr;
   g.A = dMk;
   g.sAi = (int64_t)n * r1;
   g.sAk = 1;
@@ -1386,7 +1480,6 @@ static Gemm right_dG(const LinearPlan& P, const float* chain, const float* const
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   const int64_t be = cols / n;
   Gemm g;
-  g.ks_ = nullptr;
   g.A = dNk;
   g.sAi = be;
   g.sAk = 1;
@@ -1408,7 +1501,6 @@ static Gemm right_dN(const LinearPlan& P, const float* const* G, const float* co
   const int n = P.modes[k], r0 = P.ranks[k], r1 = P.ranks[k + 1];
   const int64_t be = cols / n;
   Gemm g;
-  g.ks_ = nullptr;
   g.A = G[k];
   g.sAi = 1;
   g.sAk = r1;
@@ -1811,8 +1903,12 @@ struct LayerJob {
 };
 
 // Independent GEMMs in launches of at most kMaxGemm.
-template <bool KS>
 static void launch_gemm_list(const Gemm* gs, int n, const char* name, hipStream_t s) {
+  static bool lds_set = false;
+  if (!lds_set) {
+    allow_lds((const void*)k_sweep, kSweepLds);
+    lds_set = true;
+  }
   for (int i = 0; i < n; i += kMaxGemm) {
     SweepArgs a;
     memset(&a, 0, sizeof(a));
@@ -1824,133 +1920,63 @@ static void launch_gemm_list(const Gemm* gs, int n, const char* name, hipStream_
       ++a.ng;
     }
     TraceScope ts(name, s);
-    TTC_LAUNCH(k_sweep<KS>, dim3(total), dim3(256), 0, s, a);
+    TTC_LAUNCH(k_sweep, dim3(total), dim3(kSweepThreads), kSweepLds, s, a);
   }
 }
 
-static int merge_levels(const LinearPlan& P) { return std::max(P.s - 1, P.d - 1 - P.s); }
-
-// The GEMMs of merge level `lvl` of one layer (at most two: one per half).
-static int merge_gemms(const LayerJob& j, int lvl, Gemm* out) {
+static MergeLayer merge_layer(const LayerJob& j) {
   const LinearPlan& P = j.P;
-  const float* const* G = j.c.G;
-  const float* const* D = j.c.D;
-  float* chain = reinterpret_cast<float*>(j.sv + P.sv_chain);
-  float* Lf = reinterpret_cast<float*>(j.sv + P.sv_Lf);
-  float* Rf = reinterpret_cast<float*>(j.sv + P.sv_Rf);
-  const int d = P.d, S = P.s;
-  int ng = 0;
-  const int kL = 1 + lvl;  // left: M_kL = (M_{kL-1} D_{kL-1}) G_kL
-  if (kL <= S - 1) {
-    int64_t rows = 1;
-    for (int t = 0; t < kL; ++t) rows *= P.modes[t];
-    Gemm g;
-    memset(&g, 0, sizeof(g));
-    g.A = kL == 1 ? G[0] : chain + P.chain_off[kL - 1];
-    g.sAi = P.ranks[kL];
-    g.sAk = 1;
-    g.ks_ = D[kL - 1];
-    g.B = G[kL];
-    g.sBk = (int64_t)P.modes[kL] * P.ranks[kL + 1];
-    g.sBj = 1;
-    g.C = kL == S - 1 ? Lf : chain + P.chain_off[kL];
-    g.sCi = (int64_t)P.modes[kL] * P.ranks[kL + 1];
-    g.sCj = 1;
-    g.M = (int)rows;
-    g.N = P.modes[kL] * P.ranks[kL + 1];
-    g.K = P.ranks[kL];
-    out[ng++] = g;
-  }
-  const int kR = d - 2 - lvl;  // right: N_kR = G_kR D_kR N_{kR+1}
-  if (kR >= S) {
-    int64_t cols = 1;
-    for (int t = kR + 1; t < d; ++t) cols *= P.modes[t];
-    Gemm g;
-    memset(&g, 0, sizeof(g));
-    g.A = G[kR];
-    g.sAi = P.ranks[kR + 1];
-    g.sAk = 1;
-    g.ks_ = D[kR];
-    g.B = kR + 1 == d - 1 ? G[d - 1] : chain + P.chain_off[kR + 1];
-    g.sBk = cols;
-    g.sBj = 1;
-    g.C = kR == S ? Rf : chain + P.chain_off[kR];
-    g.sCi = cols;
-    g.sCj = 1;
-    g.M = P.ranks[kR] * P.modes[kR];
-    g.N = (int)cols;
-    g.K = P.ranks[kR + 1];
-    out[ng++] = g;
-  }
-  return ng;
-}
-
-static PackArgs pack_args(const LayerJob& j) {
-  const LinearPlan& P = j.P;
-  const float* const* G = j.c.G;
-  const float* const* D = j.c.D;
   char* sv = j.sv;
-  float* chain = reinterpret_cast<float*>(sv + P.sv_chain);
-  const int d = P.d, S = P.s;
-  PackArgs m;
+  MergeLayer m;
   memset(&m, 0, sizeof(m));
-  m.L = S == 1 ? G[0] : reinterpret_cast<float*>(sv + P.sv_Lf);
-  m.R = d - S == 1 ? G[d - 1] : reinterpret_cast<float*>(sv + P.sv_Rf);
-  m.Ds = D[S - 1];
-  m.G0 = G[0];
-  m.Gl = G[d - 1];
-  m.chain0 = S >= 2 ? chain + P.chain_off[0] : nullptr;
-  m.chainl = d - 1 > S ? chain + P.chain_off[d - 1] : nullptr;
-  m.n0 = (int64_t)P.modes[0] * P.ranks[1];
-  m.nl = (int64_t)P.ranks[d - 1] * P.modes[d - 1];
-  m.rs = P.rs;
-  m.Rpad = P.Rpad;
-  m.in_first = P.in_first;
-  m.NL = P.NL;
-  m.NRt = P.NRt;
-  m.N_in = P.N_in;
-  m.N_out = P.N_out;
-  m.meta = reinterpret_cast<int*>(sv + P.sv_meta);
+  for (int k = 0; k < P.d; ++k) {
+    m.G[k] = j.c.G[k];
+    m.modes[k] = P.modes[k];
+    m.chain_off[k] = P.chain_off[k] < 0 ? 0 : P.chain_off[k];
+  }
+  for (int k = 0; k < P.d - 1; ++k) m.D[k] = j.c.D[k];
+  for (int k = 0; k <= P.d; ++k) m.ranks[k] = P.ranks[k];
+  m.chain = reinterpret_cast<float*>(sv + P.sv_chain);
   m.Ac = sv + P.sv_Ac;
   m.AcT = sv + P.sv_AcT;
   m.Bc = sv + P.sv_Bc;
   m.BcT = sv + P.sv_BcT;
+  m.meta = reinterpret_cast<int*>(sv + P.sv_meta);
+  m.N_in = P.N_in;
+  m.N_out = P.N_out;
+  m.npl = P.NL / P.modes[P.s - 1];
+  m.npr = P.NRt / P.modes[P.s];
+  m.wgl = (m.npl + kMergePG - 1) / kMergePG;
+  m.d = P.d;
+  m.s = P.s;
+  m.in_first = P.in_first;
+  m.rs = P.rs;
+  m.Rpad = P.Rpad;
   return m;
 }
 
-// Merge of n layers: one launch per level for all of them, then the packing
-// launches (one per activation dtype and kMaxBatch layers).
+// Merge of n layers: one launch per activation dtype and kMaxMerge layers.
 static void launch_merge_batch(const LayerJob* jobs, int n, hipStream_t s) {
-  int nlev = 0;
-  for (int i = 0; i < n; ++i) nlev = std::max(nlev, merge_levels(jobs[i].P));
-  std::vector<Gemm> gs;
-  for (int lvl = 0; lvl < nlev; ++lvl) {
-    gs.clear();
-    for (int i = 0; i < n; ++i) {
-      Gemm g[2];
-      const int k = lvl < merge_levels(jobs[i].P) ? merge_gemms(jobs[i], lvl, g) : 0;
-      for (int q = 0; q < k; ++q) gs.push_back(g[q]);
-    }
-    launch_gemm_list<true>(gs.data(), (int)gs.size(), "merge_level", s);
-  }
   for (int act = 0; act < 2; ++act) {
     const int want = act == 0 ? TTC_BF16 : TTC_F32;
-    PackBatch pb;
-    memset(&pb, 0, sizeof(pb));
+    MergeBatch mb;
+    memset(&mb, 0, sizeof(mb));
     auto flush = [&]() {
-      if (pb.n == 0) return;
+      if (mb.n == 0) return;
       TraceScope ts("merge", s);
-      if (want == TTC_BF16)
-        TTC_LAUNCH(k_pack<bf16_t>, dim3((unsigned)pb.first[pb.n]), dim3(64), 0, s, pb);
-      else
-        TTC_LAUNCH(k_pack<float>, dim3((unsigned)pb.first[pb.n]), dim3(64), 0, s, pb);
-      memset(&pb, 0, sizeof(pb));
+      if (want == TTC_BF16) {
+        TTC_LAUNCH(k_merge<bf16_t>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
+      } else {
+        TTC_LAUNCH(k_merge<float>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
+      }
+      memset(&mb, 0, sizeof(mb));
     };
     for (int i = 0; i < n; ++i) {
       if (jobs[i].P.act != want) continue;
-      pb.p[pb.n] = pack_args(jobs[i]);
-      pb.first[pb.n + 1] = pb.first[pb.n] + jobs[i].P.NL + jobs[i].P.NRt;
-      if (++pb.n == kMaxBatch) flush();
+      MergeLayer& m = mb.l[mb.n];
+      m = merge_layer(jobs[i]);
+      mb.first[mb.n + 1] = mb.first[mb.n] + m.wgl + (m.npr + kMergePG - 1) / kMergePG;
+      if (++mb.n == kMaxMerge) flush();
     }
     flush();
   }
@@ -2094,7 +2120,7 @@ static void launch_cores_batch(const LayerJob* jobs, int n, hipStream_t s) {
       }
     }
     if (gs.empty()) break;
-    launch_gemm_list<false>(gs.data(), (int)gs.size(), "core", s);
+    launch_gemm_list(gs.data(), (int)gs.size(), "core", s);
   }
 }
 

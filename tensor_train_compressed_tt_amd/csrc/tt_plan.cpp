@@ -189,11 +189,6 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   o = align256(o + size_t(P->Rpad) * nout * es);
   P->sv_chain = o;
   o = align256(o + size_t(P->chain_floats) * 4);
-  // the two half products in fp32 before packing: L (NL x rs), R (rs x NRt)
-  P->sv_Lf = o;
-  o = align256(o + size_t(P->NL) * P->rs * 4);
-  P->sv_Rf = o;
-  o = align256(o + size_t(P->NRt) * P->rs * 4);
   P->sv_Z = o;
   o = align256(o + size_t(T) * P->Rpad * es);
   P->sv_total = o;

@@ -56,7 +56,7 @@ struct LinearPlan {
   int dy_gc, dy_gt, dy_nsl, dy_tpg;  // dY pass: column groups, token groups, slabs/group, tiles/group
   int dx_gc, dx_gt, dx_nsl, dx_tpg;  // dX pass
   // ---- saved layout (bytes) ----------------------------------------------------
-  size_t sv_meta, sv_Ac, sv_AcT, sv_Bc, sv_BcT, sv_chain, sv_Lf, sv_Rf, sv_Z, sv_total;
+  size_t sv_meta, sv_Ac, sv_AcT, sv_Bc, sv_BcT, sv_chain, sv_Z, sv_total;
   // ---- scratch layout (bytes) ----------------------------------------------------
   size_t sc_dZp, sc_dZ, sc_dBp, sc_dAp, sc_dL, sc_dR, sc_w0, sc_w1, sc_total;
   int64_t wl_floats, wr_floats;  // size of one left / right ping-pong buffer
