@@ -69,6 +69,8 @@ def parse(argv=None):
                     help="run the merges on the side stream and the embedding lookup on the main one")
     ap.add_argument("--no-qkv-batch", action="store_true",
                     help="one launch per layer for the Q, K and V projections instead of one batched launch")
+    ap.add_argument("--path", default="auto", choices=["auto", "merged", "sequential"],
+                    help="contraction order of every layer (default: the planner's pick for the batch)")
     ap.add_argument("--one-input-set", action="store_true",
                     help="every step reads the same inputs (they may then hit in the memory-side cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,7 +200,11 @@ class StepOptions:
     rank_grads: bool = False      # early-stage gradients after the core gradients
 
 
-def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None, clone_encoders=False):
+PATHS = {"auto": 0, "merged": 1, "sequential": 2}
+
+
+def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None, clone_encoders=False,
+                path="auto"):
     """Device buffers of the step's TT-linear layers, in execution order.
 
     Every layer has its own seeded cores, diagonals, x and dY (synth), uploaded
@@ -223,7 +229,7 @@ def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None
     for li, spec in enumerate(specs):
         fresh = not (clone_encoders and li >= 6)
         L = synth.make_tt_layer(cfg, li, spec, T, zf, dt, acts=fresh)
-        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, PATHS[path])
         if fresh:
             if dt == "bf16":
                 x = torch.from_numpy(L["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -528,8 +534,8 @@ def kernel_table(recs, steps, sizes, groups, ttm_sizes):
             d["bytes"] += sum(sizes[i].get(name, 0) for i in grp)
         elif name in ttm_sizes:
             d["bytes"] += ttm_sizes[name]
-    for name in layer_of:
-        assert counts.get(name, 0) == len(layer_of[name]) * steps, (name, counts.get(name))
+    for name in layer_of:  # layers on the sequential order launch none of these
+        assert counts.get(name, 0) in (0, len(layer_of[name]) * steps), (name, counts.get(name))
     for d in per.values():
         d["avg_us"] = 1e3 * d["ms"] / d["launches"]
         d["gbps"] = d["bytes"] / (d["ms"] / 1e3) / 1e9 if d["bytes"] else None
@@ -565,7 +571,7 @@ def main():
     # ---- inputs, resident in HBM ----------------------------------------------------
     t_setup = time.perf_counter()
     layers, host = make_layers(cfg, rank, T, dev, n_sets=n_sets, keep_host=cpu_T is not None, n_layers=n_layers,
-                               clone_encoders=(cfg == 4))
+                               clone_encoders=(cfg == 4), path=args.path)
     print(f"# {len(layers)} layers ready in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     specs = [L["spec"] for L in layers]
     sizes = step_bytes(specs, [h["D"] for h in host], T, es)
@@ -579,21 +585,23 @@ def main():
     tokens_per_s = T / (ms_per_step / 1e3)
     step_gbps = tt_bytes / (ms_per_step / 1e3) / 1e9
     per = kernel_table(trace_kernels(runner, args.steps), args.steps, sizes, (fg, bg), {})
-    stream_kernels = ["fwd", "bwd_dy", "bwd_dx"]
-    dom = max(stream_kernels, key=lambda k: per[k]["ms"])
-    roof = {
-        "bound": "hbm",
-        "kernel": dom,
-        "achieved": round(per[dom]["gbps"], 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(per[dom]["gbps"] / HBM_PEAK_GBPS, 4),
-        # the counter summaries were taken on the default workload only
-        "traffic": measured_traffic(dom) if (cfg, rank, T, args.rank_grads, n_sets) == (2, 30, 16384, False, 2)
-        else None,
-        "avg_launch_us": round(per[dom]["avg_us"], 2),
-        "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
-    }
+    stream_kernels = [k for k in ("fwd", "bwd_dy", "bwd_dx") if k in per]
+    roof = None  # every layer on the sequential order: latency-bound, no streaming kernel
+    if stream_kernels:
+        dom = max(stream_kernels, key=lambda k: per[k]["ms"])
+        roof = {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(per[dom]["gbps"], 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(per[dom]["gbps"] / HBM_PEAK_GBPS, 4),
+            # the counter summaries were taken on the default workload only
+            "traffic": measured_traffic(dom) if (cfg, rank, T, args.rank_grads, n_sets) == (2, 30, 16384, False, 2)
+            else None,
+            "avg_launch_us": round(per[dom]["avg_us"], 2),
+            "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
+        }
 
     # ---- the same step with the embedding lookup and its backward ----------------------
     with_emb = None
@@ -649,6 +657,9 @@ def main():
             "rank": rank,
             "layers": len(specs),
             "input_sets": n_sets,
+            "path": args.path,
+            "planned": sorted({__import__("tensor_train_compressed_tt_amd").tt_linear_explain(L["mod"].desc, T).split()[0][5:]
+                               for L in layers}),
             "qkv_batched": not (args.no_qkv_batch or args.single_stream),
             "rank_grads": bool(args.rank_grads),
             "streams": 1 if args.single_stream else 2,

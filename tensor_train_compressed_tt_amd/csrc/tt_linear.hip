@@ -1590,6 +1590,246 @@ __global__ __launch_bounds__(kRankGradThreads) void k_rank_grads(RankGradArgs a)
   }
 }
 
+// ------------------------------------------------------------------------------
+// sequential order (small batches)
+// ------------------------------------------------------------------------------
+// The core-by-core order of the project page's Proposition 4.1 comparison
+// (section "Making small tensor operations fast on GPUs"): for few tokens it
+// needs far fewer multiply-adds than merging the halves of the chain, whose
+// cost does not shrink with the batch.  One work-group per token carries the
+// token's state through the steps of the plan in LDS: the input modes are
+// contracted one core at a time from the input half's chain end to the
+// split, then the output modes are produced one core at a time.  The forward
+// keeps the states between steps in `saved`; the backward walks the steps in
+// reverse and writes, per token, the input gradient and one partial of every
+// core gradient (fixed-order sums; the partials are added over the tokens by
+// k_seq_reduce in token order).
+struct SeqArgs {
+  SeqStep st[kMaxCores];
+  const float* G[kMaxCores];
+  const float* D[kMaxCores];
+  const void* x;
+  const void* dy;
+  void* y;
+  void* dx;
+  float* states;
+  float* part;
+  int64_t N_in, N_out, state_floats, part_floats, max_state, max_core;
+  int d;
+};
+static_assert(sizeof(SeqArgs) <= 3072, "SeqArgs too large for a kernel argument");
+constexpr int kSeqThreads = 1024;
+
+// element (x, i, y) of a step's core in the core's own layout
+__device__ __forceinline__ int seq_gidx(const SeqStep& st, int x, int i, int y) {
+  return st.rightward ? (x * st.n + i) * st.rout + y : (y * st.n + i) * st.rin + x;
+}
+
+// the step's core and link diagonal into LDS (all of a thread's loads in flight
+// at once: a core has at most 16384 entries)
+__device__ __forceinline__ void seq_stage(const SeqArgs& a, const SeqStep& st, float* gsm, float* dv) {
+  const float* G = a.G[st.core];
+  const int csz = st.rin * st.n * st.rout;
+  constexpr int U = 16;
+  for (int e0 = threadIdx.x; e0 < csz; e0 += U * kSeqThreads) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = e0 + u * kSeqThreads < csz ? G[e0 + u * kSeqThreads] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (e0 + u * kSeqThreads < csz) gsm[e0 + u * kSeqThreads] = v[u];
+  }
+  for (int x = threadIdx.x; x < st.rin; x += kSeqThreads) dv[x] = st.dlink >= 0 ? a.D[st.dlink][x] : 1.0f;
+}
+
+// lanes per output when `outs` outputs share the work-group: a power of two
+// up to 16, so that small steps still spread their sums over the threads
+__device__ __forceinline__ int seq_group(int64_t outs) {
+  int g = 1;
+  while (g < 16 && (int64_t)(2 * g) * outs <= kSeqThreads) g *= 2;
+  return g;
+}
+
+// sum_{k < K} term(k) by the G lanes of a group (lane j takes k = j, j+G, ...,
+// four partial sums), then a fixed butterfly over the group; every lane of
+// the group returns the total
+template <typename F>
+__device__ __forceinline__ float seq_group_sum(int K, int j, int G, F term) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int k = j;
+  for (; k + 3 * G < K; k += 4 * G) {
+    a0 += term(k);
+    a1 += term(k + G);
+    a2 += term(k + 2 * G);
+    a3 += term(k + 3 * G);
+  }
+  for (; k < K; k += G) a0 += term(k);
+  float sum = (a0 + a1) + (a2 + a3);
+  for (int o = G >> 1; o > 0; o >>= 1) sum += __shfl_xor(sum, o, G);
+  return sum;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSeqThreads) void k_seq_fwd(SeqArgs a) {
+  typedef typename Elem<T>::type E;
+  extern __shared__ __align__(16) float sm[];
+  const int tid = threadIdx.x;
+  const int64_t tok = blockIdx.x;
+  float* in = sm;
+  float* out = sm + a.max_state;
+  float* gsm = sm + 2 * a.max_state;
+  float* dv = gsm + a.max_core;
+  const E* x = reinterpret_cast<const E*>(a.x) + tok * a.N_in;
+  for (int i = tid; i < (int)a.N_in; i += kSeqThreads) in[i] = elem_to_f32<T>(x[i]);
+  for (int t = 0; t < a.d; ++t) {
+    const SeqStep& st = a.st[t];
+    seq_stage(a, st, gsm, dv);
+    __syncthreads();
+    const int n = st.n, rin = st.rin, rout = st.rout;
+    const int B = (int)st.B;
+    const int outs = (int)st.out_size;
+    const int G = seq_group(outs);
+    const int j = tid % G;
+    for (int e = tid / G; e < outs; e += kSeqThreads / G) {
+      const int y = e % rout;
+      float sum;
+      if (!st.expand) {  // out[a][b][y] = sum_{i, x} in[a][i][b][x] dv[x] g(x, i, y)
+        const int ab = e / rout;
+        const int aa = ab / B, bb = ab - aa * B;
+        const float* iv = in + (aa * n * B + bb) * rin;
+        sum = seq_group_sum(n * rin, j, G, [&](int k) {
+          const int i = k / rin, xx = k - i * rin;
+          return iv[i * B * rin + xx] * dv[xx] * gsm[seq_gidx(st, xx, i, y)];
+        });
+      } else {  // out[a][i][b][y] = sum_x in[a][b][x] dv[x] g(x, i, y)
+        const int r = e / rout;
+        const int bb = r % B, ai = r / B;
+        const int i = ai % n, aa = ai / n;
+        const float* iv = in + (aa * B + bb) * rin;
+        sum = seq_group_sum(rin, j, G, [&](int xx) { return iv[xx] * dv[xx] * gsm[seq_gidx(st, xx, i, y)]; });
+      }
+      if (j == 0) out[e] = sum;
+    }
+    __syncthreads();
+    if (st.out_off >= 0) {
+      float* sv = a.states + tok * a.state_floats + st.out_off;
+      for (int e = tid; e < outs; e += kSeqThreads) sv[e] = out[e];
+    } else {
+      E* y = reinterpret_cast<E*>(a.y) + tok * a.N_out;
+      for (int e = tid; e < (int)a.N_out; e += kSeqThreads) y[e] = (E)Mma<T>::from_f32(out[e]);
+    }
+    float* tmp = in;
+    in = out;
+    out = tmp;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSeqThreads) void k_seq_bwd(SeqArgs a) {
+  typedef typename Elem<T>::type E;
+  extern __shared__ __align__(16) float sm[];
+  const int tid = threadIdx.x;
+  const int64_t tok = blockIdx.x;
+  float* sin = sm;
+  float* gout = sm + a.max_state;
+  float* gin = sm + 2 * a.max_state;
+  float* gsm = sm + 3 * a.max_state;
+  float* dv = gsm + a.max_core;
+  const E* dy = reinterpret_cast<const E*>(a.dy) + tok * a.N_out;
+  for (int i = tid; i < (int)a.N_out; i += kSeqThreads) gout[i] = elem_to_f32<T>(dy[i]);
+  float* part = a.part + tok * a.part_floats;
+  for (int t = a.d - 1; t >= 0; --t) {
+    const SeqStep& st = a.st[t];
+    if (st.in_off >= 0) {
+      const float* sv = a.states + tok * a.state_floats + st.in_off;
+      for (int e = tid; e < (int)st.in_size; e += kSeqThreads) sin[e] = sv[e];
+    } else {
+      const E* x = reinterpret_cast<const E*>(a.x) + tok * a.N_in;
+      for (int e = tid; e < (int)a.N_in; e += kSeqThreads) sin[e] = elem_to_f32<T>(x[e]);
+    }
+    seq_stage(a, st, gsm, dv);
+    __syncthreads();
+    const int n = st.n, rin = st.rin, rout = st.rout;
+    const int A = (int)st.A, B = (int)st.B;
+    const int csz = rin * n * rout;
+    // this token's share of the core gradient, in the core's own layout
+    {
+      const int G = seq_group(csz);
+      const int j = tid % G;
+      for (int ge = tid / G; ge < csz; ge += kSeqThreads / G) {
+        int xx, i, y;
+        if (st.rightward) {
+          xx = ge / (n * rout);
+          i = (ge / rout) % n;
+          y = ge % rout;
+        } else {
+          y = ge / (n * rin);
+          i = (ge / rin) % n;
+          xx = ge % rin;
+        }
+        const float sum = seq_group_sum(A * B, j, G, [&](int k) {
+          const int aa = k / B, bb = k - aa * B;
+          return st.expand ? sin[(aa * B + bb) * rin + xx] * gout[((aa * n + i) * B + bb) * rout + y]
+                           : sin[((aa * n + i) * B + bb) * rin + xx] * gout[(aa * B + bb) * rout + y];
+        });
+        if (j == 0) part[st.gp_off + ge] = sum * dv[xx];
+      }
+    }
+    // gradient of the step's input state
+    if (t > 0 || a.dx) {
+      const int ins = (int)st.in_size;
+      const int G = seq_group(ins);
+      const int j = tid % G;
+      for (int e = tid / G; e < ins; e += kSeqThreads / G) {
+        const int xx = e % rin;
+        float sum;
+        if (!st.expand) {  // e = [a][i][b][x]
+          const int r = e / rin;
+          const int bb = r % B, ai = r / B;
+          const int i = ai % n, aa = ai / n;
+          const float* go = gout + (aa * B + bb) * rout;
+          sum = seq_group_sum(rout, j, G, [&](int y) { return go[y] * gsm[seq_gidx(st, xx, i, y)]; });
+        } else {  // e = [a][b][x]
+          const int ab = e / rin;
+          const int bb = ab % B, aa = ab / B;
+          sum = seq_group_sum(n * rout, j, G, [&](int k) {
+            const int i = k / rout, y = k - i * rout;
+            return gout[((aa * n + i) * B + bb) * rout + y] * gsm[seq_gidx(st, xx, i, y)];
+          });
+        }
+        if (j == 0) gin[e] = sum * dv[xx];
+      }
+    }
+    __syncthreads();
+    float* tmp = gout;
+    gout = gin;
+    gin = tmp;
+  }
+  if (a.dx) {
+    E* dx = reinterpret_cast<E*>(a.dx) + tok * a.N_in;
+    for (int e = tid; e < (int)a.N_in; e += kSeqThreads) dx[e] = (E)Mma<T>::from_f32(gout[e]);
+  }
+}
+
+// dG_k = sum over the tokens of the partials, in token order
+struct SeqRedArgs {
+  const float* part;
+  float* dG[kMaxCores];   // indexed by walk step
+  int64_t off[kMaxCores + 1];
+  int64_t T, part_floats;
+  int d;
+};
+__global__ __launch_bounds__(256) void k_seq_reduce(SeqRedArgs a) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < a.part_floats;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    int t = 0;
+    while (t < a.d - 1 && e >= a.off[t + 1]) ++t;
+    float acc = 0.f;
+    for (int64_t k = 0; k < a.T; ++k) acc += a.part[k * a.part_floats + e];
+    a.dG[t][e - a.off[t]] = acc;
+  }
+}
+
 __global__ void k_zero(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -1873,6 +2113,78 @@ static void launch_stream_jobs(const StreamJob* jobs, int n, hipStream_t st) {
   }
 }
 
+static SeqArgs seq_args(const LinearPlan& P, const float* const* G, const float* const* D, const void* x,
+                        const void* dy, void* y, void* dx, const char* sv, char* sc) {
+  SeqArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int t = 0; t < P.d; ++t) a.st[t] = P.seq[t];
+  for (int k = 0; k < P.d; ++k) a.G[k] = G[k];
+  for (int k = 0; k < P.d - 1; ++k) a.D[k] = D[k];
+  a.x = x;
+  a.dy = dy;
+  a.y = y;
+  a.dx = dx;
+  a.states = reinterpret_cast<float*>(const_cast<char*>(sv));
+  a.part = reinterpret_cast<float*>(sc);
+  a.N_in = P.N_in;
+  a.N_out = P.N_out;
+  a.state_floats = P.seq_state_floats;
+  a.part_floats = P.seq_part_floats;
+  a.max_state = P.seq_max_state;
+  a.max_core = P.seq_max_core;
+  a.d = P.d;
+  return a;
+}
+
+// dynamic LDS above 64 KB for the sequential kernels, once per kernel
+template <int WHICH>
+static void seq_allow_lds(const void* kern) {
+  static bool done = false;
+  if (!done) {
+    allow_lds(kern, kSeqMaxLds);
+    done = true;
+  }
+}
+
+static void launch_seq_fwd(const LinearPlan& P, const SeqArgs& a, hipStream_t st) {
+  TraceScope ts("seq_fwd", st);
+  if (P.act == TTC_BF16) {
+    seq_allow_lds<0>((const void*)k_seq_fwd<bf16_t>);
+    TTC_LAUNCH(k_seq_fwd<bf16_t>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_fwd, st, a);
+  } else {
+    seq_allow_lds<1>((const void*)k_seq_fwd<float>);
+    TTC_LAUNCH(k_seq_fwd<float>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_fwd, st, a);
+  }
+}
+
+static void launch_seq_bwd(const LinearPlan& P, const SeqArgs& a, hipStream_t st) {
+  TraceScope ts("seq_bwd", st);
+  if (P.act == TTC_BF16) {
+    seq_allow_lds<2>((const void*)k_seq_bwd<bf16_t>);
+    TTC_LAUNCH(k_seq_bwd<bf16_t>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_bwd, st, a);
+  } else {
+    seq_allow_lds<3>((const void*)k_seq_bwd<float>);
+    TTC_LAUNCH(k_seq_bwd<float>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_bwd, st, a);
+  }
+}
+
+static void launch_seq_reduce(const LinearPlan& P, const char* sc, float* const* dG, hipStream_t st) {
+  SeqRedArgs r;
+  memset(&r, 0, sizeof(r));
+  r.part = reinterpret_cast<const float*>(sc);
+  for (int t = 0; t < P.d; ++t) {
+    r.dG[t] = dG[P.seq[t].core];
+    r.off[t] = P.seq[t].gp_off;
+  }
+  r.off[P.d] = P.seq_part_floats;
+  r.T = P.T;
+  r.part_floats = P.seq_part_floats;
+  r.d = P.d;
+  TraceScope ts("seq_reduce", st);
+  TTC_LAUNCH(k_seq_reduce, dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, (P.seq_part_floats + 255) / 256))),
+             dim3(256), 0, st, r);
+}
+
 static unsigned grid_for(int64_t n, int64_t per_block, int64_t cap) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(cap, (n + per_block - 1) / per_block));
 }
@@ -2014,6 +2326,7 @@ extern "C" ttc_status tt_linear_prepare(const tt_linear_desc* desc, int64_t T, c
   if (!saved) return TTC_ERR_NULL;
   if (!aligned16(saved)) return TTC_ERR_ALIGN;
   if (saved_bytes < P.sv_total) return TTC_ERR_WORKSPACE;
+  if (P.path == TTC_PATH_SEQUENTIAL) return TTC_OK;  // nothing to merge
   (void)hipGetLastError();
   launch_merge(P, G, D, static_cast<char*>(saved), reinterpret_cast<hipStream_t>(stream));
   return hip_status();
@@ -2035,6 +2348,10 @@ extern "C" ttc_status tt_linear_fwd(const tt_linear_desc* desc, int64_t T, const
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   char* sv = static_cast<char*>(saved);
+  if (P.path == TTC_PATH_SEQUENTIAL) {
+    launch_seq_fwd(P, seq_args(P, G, D, x, nullptr, y, nullptr, sv, nullptr), s);
+    return hip_status();
+  }
   if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
   if (!(desc->flags & TTC_FLAG_PREPARED)) launch_merge(P, G, D, sv, s);
   StreamJob j{&P, x, nullptr, sv, y, nullptr, nullptr};
@@ -2196,16 +2513,23 @@ extern "C" ttc_status tt_linear_bwd_split(const tt_linear_desc* desc, int64_t T,
   if ((st = buffer_checks(P, true, x, dy, dx, saved, saved_bytes, scratch, scratch_bytes)) != TTC_OK) return st;
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
-  if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
-  StreamJob job{&P, x, dy, const_cast<char*>(sv), nullptr, dx, sc};
-  launch_stream_jobs<false>(&job, 1, s_main);
+  if (P.path == TTC_PATH_SEQUENTIAL) {
+    launch_seq_bwd(P, seq_args(P, G, D, x, dy, nullptr, dx, sv, sc), s_main);
+  } else {
+    if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
+    StreamJob job{&P, x, dy, const_cast<char*>(sv), nullptr, dx, sc};
+    launch_stream_jobs<false>(&job, 1, s_main);
+  }
   if (s != s_main) {
     hipEvent_t ev = split_event();
     if (!ev) return TTC_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_split_mu);
     if (hipEventRecord(ev, s_main) != hipSuccess || hipStreamWaitEvent(s, ev, 0) != hipSuccess) return TTC_ERR_HIP;
   }
-  launch_bwd_cores(P, G, D, sv, sc, dG, s);
+  if (P.path == TTC_PATH_SEQUENTIAL)
+    launch_seq_reduce(P, sc, dG, s);
+  else
+    launch_bwd_cores(P, G, D, sv, sc, dG, s);
   return hip_status();
 }
 
@@ -2272,6 +2596,10 @@ extern "C" ttc_status tt_linear_bwd_data(const tt_linear_desc* desc, int64_t T, 
   (void)hipGetLastError();
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
+  if (P.path == TTC_PATH_SEQUENTIAL) {
+    launch_seq_bwd(P, seq_args(P, G, D, x, dy, nullptr, dx, sv, sc), s);
+    return hip_status();
+  }
   if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
   StreamJob job{&P, x, dy, const_cast<char*>(sv), nullptr, dx, sc};
   launch_stream_jobs<false>(&job, 1, s);
@@ -2295,7 +2623,10 @@ extern "C" ttc_status tt_linear_bwd_cores(const tt_linear_desc* desc, int64_t T,
   if ((st = buffer_checks(P, false, nullptr, nullptr, nullptr, saved, saved_bytes, scratch, scratch_bytes)) !=
       TTC_OK)
     return st;
-  launch_bwd_cores(P, G, D, static_cast<const char*>(saved), static_cast<char*>(scratch), dG, s);
+  if (P.path == TTC_PATH_SEQUENTIAL)
+    launch_seq_reduce(P, static_cast<const char*>(scratch), dG, s);
+  else
+    launch_bwd_cores(P, G, D, static_cast<const char*>(saved), static_cast<char*>(scratch), dG, s);
   return hip_status();
 }
 
@@ -2319,8 +2650,12 @@ extern "C" ttc_status tt_linear_prepare_batch(int32_t n, const tt_linear_desc* c
     j.c = chain_ptrs(j.P, G[i], D[i]);
     j.sv = static_cast<char*>(saved[i]);
   }
+  // layers on the sequential path have nothing to merge
+  jobs.erase(std::remove_if(jobs.begin(), jobs.end(), [](const LayerJob& j) { return j.P.path == TTC_PATH_SEQUENTIAL; }),
+             jobs.end());
+  if (jobs.empty()) return TTC_OK;
   (void)hipGetLastError();
-  launch_merge_batch(jobs.data(), n, reinterpret_cast<hipStream_t>(stream));
+  if (!jobs.empty()) launch_merge_batch(jobs.data(), (int)jobs.size(), reinterpret_cast<hipStream_t>(stream));
   return hip_status();
 }
 
@@ -2362,7 +2697,14 @@ extern "C" ttc_status tt_linear_bwd_cores_batch(int32_t n, const tt_linear_desc*
     make_linear_plan(descs[i], 0, &P);
     launch_zero_grads(P, dG[i], s);
   }
-  if (!jobs.empty()) launch_cores_batch(jobs.data(), (int)jobs.size(), s);
+  std::vector<LayerJob> merged;
+  for (const LayerJob& j : jobs) {
+    if (j.P.path == TTC_PATH_SEQUENTIAL)
+      launch_seq_reduce(j.P, j.sc, j.dG, s);
+    else
+      merged.push_back(j);
+  }
+  if (!merged.empty()) launch_cores_batch(merged.data(), (int)merged.size(), s);
   return hip_status();
 }
 
@@ -2376,6 +2718,8 @@ extern "C" ttc_status tt_linear_fwd_batch(int32_t n, const tt_linear_desc* const
   std::vector<LinearPlan> plans(n);
   std::vector<LayerJob> merges;
   std::vector<StreamJob> jobs;
+  std::vector<SeqArgs> seqs;
+  std::vector<const LinearPlan*> seq_plans;
   for (int i = 0; i < n; ++i) {
     if (!descs[i]) return TTC_ERR_NULL;
     LinearPlan& P = plans[i];
@@ -2386,6 +2730,11 @@ extern "C" ttc_status tt_linear_fwd_batch(int32_t n, const tt_linear_desc* const
     if (!x[i] || !y[i] || !saved[i]) return TTC_ERR_NULL;
     if (!aligned16(x[i]) || !aligned16(y[i]) || !aligned16(saved[i])) return TTC_ERR_ALIGN;
     if (saved_bytes[i] < P.sv_total) return TTC_ERR_WORKSPACE;
+    if (P.path == TTC_PATH_SEQUENTIAL) {
+      seqs.push_back(seq_args(P, G[i], D[i], x[i], nullptr, y[i], nullptr, static_cast<char*>(saved[i]), nullptr));
+      seq_plans.push_back(&P);
+      continue;
+    }
     if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
     if (!(descs[i]->flags & TTC_FLAG_PREPARED)) {
       LayerJob m;
@@ -2397,9 +2746,11 @@ extern "C" ttc_status tt_linear_fwd_batch(int32_t n, const tt_linear_desc* const
     }
     jobs.push_back(StreamJob{&P, x[i], nullptr, static_cast<char*>(saved[i]), y[i], nullptr, nullptr});
   }
-  if (jobs.empty()) return TTC_OK;  // every layer has T == 0
+  if (jobs.empty() && seqs.empty()) return TTC_OK;  // every layer has T == 0
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  for (size_t i = 0; i < seqs.size(); ++i) launch_seq_fwd(*seq_plans[i], seqs[i], s);
+  if (jobs.empty()) return hip_status();  // every layer is sequential or has T == 0
   if (!merges.empty()) launch_merge_batch(merges.data(), (int)merges.size(), s);
   launch_stream_jobs<true>(jobs.data(), (int)jobs.size(), s);
   return hip_status();
@@ -2417,6 +2768,8 @@ extern "C" ttc_status tt_linear_bwd_data_batch(int32_t n, const tt_linear_desc* 
     return TTC_ERR_NULL;
   std::vector<LinearPlan> plans(n);
   std::vector<StreamJob> jobs;
+  std::vector<SeqArgs> seqs;
+  std::vector<const LinearPlan*> seq_plans;
   for (int i = 0; i < n; ++i) {
     if (!descs[i]) return TTC_ERR_NULL;
     LinearPlan& P = plans[i];
@@ -2427,13 +2780,21 @@ extern "C" ttc_status tt_linear_bwd_data_batch(int32_t n, const tt_linear_desc* 
     if ((st = buffer_checks(P, true, x[i], dy[i], dxi, saved[i], saved_bytes[i], scratch[i], scratch_bytes[i])) !=
         TTC_OK)
       return st;
+    if (P.path == TTC_PATH_SEQUENTIAL) {
+      seqs.push_back(seq_args(P, G[i], D[i], x[i], dy[i], nullptr, dxi, static_cast<const char*>(saved[i]),
+                              static_cast<char*>(scratch[i])));
+      seq_plans.push_back(&P);
+      continue;
+    }
     if (!nr_supported(P.NR)) return TTC_ERR_UNSUPPORTED;
     jobs.push_back(StreamJob{&P, x[i], dy[i], const_cast<char*>(static_cast<const char*>(saved[i])), nullptr, dxi,
                              static_cast<char*>(scratch[i])});
   }
-  if (jobs.empty()) return TTC_OK;  // every layer has T == 0
+  if (jobs.empty() && seqs.empty()) return TTC_OK;  // every layer has T == 0
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  for (size_t i = 0; i < seqs.size(); ++i) launch_seq_bwd(*seq_plans[i], seqs[i], s);
+  if (jobs.empty()) return hip_status();  // every layer is sequential or has T == 0
   launch_stream_jobs<false>(jobs.data(), (int)jobs.size(), s);
   return hip_status();
 }
@@ -2506,15 +2867,18 @@ extern "C" ttc_status tt_linear_explain(const tt_linear_desc* desc, int64_t T, c
   LinearPlan P;
   const ttc_status st = make_linear_plan(desc, T, &P);
   if (st != TTC_OK) return st;
-  double macs[4], bytes[4];
+  double macs[4], bytes[4], usec[4];
   linear_path_costs(P, macs, bytes);
+  linear_path_times(P, macs, bytes, usec);
   snprintf(buf, n,
-           "path=merged split=%d rank=%d rpad=%d N_out=%lld N_in=%lld T=%lld "
-           "merged_macs=%.6g merged_bytes=%.6g sequential_macs=%.6g sequential_bytes=%.6g "
+           "path=%s split=%d rank=%d rpad=%d N_out=%lld N_in=%lld T=%lld "
+           "merged_macs=%.6g merged_bytes=%.6g merged_us=%.4g sequential_macs=%.6g sequential_bytes=%.6g "
+           "sequential_us=%.4g "
            "dense_macs=%.6g dense_bytes=%.6g dy_grid=%dx%d dy_slabs=%d dy_tiles=%d dx_grid=%dx%d dx_slabs=%d "
            "dx_tiles=%d saved=%zu scratch=%zu",
-           P.s, P.rs, P.Rpad, (long long)P.N_out, (long long)P.N_in, (long long)T, macs[1], bytes[1], macs[2],
-           bytes[2], macs[3], bytes[3], P.dy_gc, P.dy_gt, P.dy_nsl, P.dy_tpg, P.dx_gc, P.dx_gt, P.dx_nsl, P.dx_tpg,
+           P.path == TTC_PATH_SEQUENTIAL ? "sequential" : "merged", P.s, P.rs, P.Rpad, (long long)P.N_out,
+           (long long)P.N_in, (long long)T, macs[1], bytes[1], usec[1], macs[2], bytes[2], usec[2], macs[3],
+           bytes[3], P.dy_gc, P.dy_gt, P.dy_nsl, P.dy_tpg, P.dx_gc, P.dx_gt, P.dx_nsl, P.dx_tpg,
            P.sv_total, P.sc_total);
   return TTC_OK;
 }

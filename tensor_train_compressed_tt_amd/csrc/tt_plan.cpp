@@ -31,7 +31,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   if (desc->act_dtype != TTC_F32 && desc->act_dtype != TTC_BF16) return TTC_ERR_DTYPE;
   if (desc->in_first != 0 && desc->in_first != 1) return TTC_ERR_SHAPE;
   if (desc->path < TTC_PATH_AUTO || desc->path > TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
-  if (desc->path == TTC_PATH_SEQUENTIAL || desc->path == TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
+  if (desc->path == TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
   if (desc->flags & ~TTC_FLAG_PREPARED) return TTC_ERR_UNSUPPORTED;
   const int d = p + q;
   P->p = p;
@@ -113,6 +113,95 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
     items += cols;
   }
   P->item_off[d] = items;
+
+  // ---- the sequential order's steps ---------------------------------------------------
+  {
+    // chain position -> (input mode?, listed index)
+    int is_in[kMaxCores], lidx[kMaxCores];
+    for (int k = 0; k < d; ++k) {
+      const bool in = desc->in_first ? k < q : k >= p;
+      is_in[k] = in;
+      lidx[k] = desc->in_first ? (in ? k : k - q) : (in ? k - p : k);
+    }
+    const int s = P->s;
+    const bool in_left = desc->in_first != 0;  // the input half is left of the split
+    int order[kMaxCores], nst = 0;
+    if (in_left)
+      for (int k = 0; k < s; ++k) order[nst++] = k;
+    else
+      for (int k = d - 1; k >= s; --k) order[nst++] = k;
+    if (in_left)
+      for (int k = s; k < d; ++k) order[nst++] = k;
+    else
+      for (int k = s - 1; k >= 0; --k) order[nst++] = k;
+    bool remaining[TTC_MAX_HALF_MODES], produced[TTC_MAX_HALF_MODES];
+    for (int m = 0; m < TTC_MAX_HALF_MODES; ++m) {
+      remaining[m] = m < q;
+      produced[m] = false;
+    }
+    int64_t soff = 0, goff = 0, prev_size = nin;
+    P->seq_max_state = std::max(nin, nout);
+    P->seq_max_core = 0;
+    for (int t = 0; t < d; ++t) {
+      SeqStep& st = P->seq[t];
+      const int k = order[t];
+      // both halves are walked leftwards when the input half is on the
+      // right (its chain end first, then the output half from the split to
+      // its end) and rightwards otherwise
+      const bool rightward = in_left;
+      st.core = k;
+      st.n = P->modes[k];
+      st.rightward = rightward;
+      st.rin = rightward ? P->ranks[k] : P->ranks[k + 1];
+      st.rout = rightward ? P->ranks[k + 1] : P->ranks[k];
+      st.expand = t >= q;
+      // link between this core and the previous one of the walk (the split
+      // link for the first output step); none at the input half's chain end
+      st.dlink = t == 0 ? -1 : (rightward ? k - 1 : k);
+      const int m = lidx[k];
+      const int* md = st.expand ? desc->out_modes : desc->in_modes;
+      bool* set = st.expand ? produced : remaining;
+      int64_t A = 1, B = 1;
+      for (int u = 0; u < (st.expand ? p : q); ++u) {
+        if (!set[u] || u == m) continue;
+        if (u < m) A *= md[u];
+        else B *= md[u];
+      }
+      st.A = A;
+      st.B = B;
+      if (st.expand) produced[m] = true;
+      else remaining[m] = false;
+      st.in_size = prev_size;
+      st.out_size = st.expand ? A * st.n * B * st.rout : A * B * st.rout;
+      st.in_off = t == 0 ? -1 : soff - prev_size;
+      st.out_off = t == d - 1 ? -1 : soff;
+      if (t < d - 1) soff += st.out_size;
+      prev_size = st.out_size;
+      st.gp_off = goff;
+      goff += (int64_t)st.rin * st.n * st.rout;
+      P->seq_max_state = std::max(P->seq_max_state, st.out_size);
+      P->seq_max_core = std::max<int64_t>(P->seq_max_core, (int64_t)st.rin * st.n * st.rout);
+      (void)is_in;
+    }
+    P->seq_state_floats = soff;
+    P->seq_part_floats = goff;
+    P->seq_lds_fwd = size_t(2 * P->seq_max_state + P->seq_max_core + TTC_MAX_RANK) * 4;
+    P->seq_lds_bwd = size_t(3 * P->seq_max_state + P->seq_max_core + TTC_MAX_RANK) * 4;
+    P->seq_ok = P->seq_lds_bwd <= kSeqMaxLds && T <= kSeqMaxTokens;
+  }
+  {
+    double macs[4], bytes[4], usec[4];
+    linear_path_costs(*P, macs, bytes);
+    linear_path_times(*P, macs, bytes, usec);
+    if (desc->path == TTC_PATH_SEQUENTIAL) {
+      if (!P->seq_ok) return TTC_ERR_UNSUPPORTED;
+      P->path = TTC_PATH_SEQUENTIAL;
+    } else if (desc->path == TTC_PATH_MERGED) {
+      P->path = TTC_PATH_MERGED;
+    } else {
+      P->path = (P->seq_ok && usec[2] < usec[1]) ? TTC_PATH_SEQUENTIAL : TTC_PATH_MERGED;
+    }
+  }
 
   // ---- launch shapes of the two backward streaming passes ---------------------
   // A work-group owns a range of columns (whole 256-byte slabs) and a range of
@@ -227,6 +316,12 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->sc_w1 = o;
   o = align256(o + size_t(wl + wr) * 4);
   P->sc_total = o;
+  if (P->path == TTC_PATH_SEQUENTIAL) {
+    // saved: every token's states between the steps; scratch: every token's
+    // core-gradient partials
+    P->sv_total = align256(size_t(T) * P->seq_state_floats * 4);
+    P->sc_total = align256(size_t(T) * P->seq_part_floats * 4);
+  }
   return TTC_OK;
 }
 
@@ -264,32 +359,16 @@ void linear_path_costs(const LinearPlan& P, double macs[4], double bytes[4]) {
   // merged: 3 skinny GEMM pairs plus merge and its reverse sweep (about 2x)
   macs[1] = 3.0 * T * r * double(P.N_in + P.N_out) + 3.0 * merge;
   bytes[1] = act_bytes + 2.0 * T * r * 4.0 + 2.0 * core_elems * 4.0;
-  // sequential: sweep the input-side cores from the far end of the chain
-  // towards the split over x, then the output-side cores from the split
-  // outwards; forward cost f, backward about 2 f
+  // sequential: the steps of the core-by-core order; each step costs
+  // (state entries around its mode) x rin x rout per token; the backward
+  // (input and core gradients) about twice the forward
   {
-    const int p = P.p, q = P.q;
-    int in_pos[kMaxCores], out_pos[kMaxCores];
-    for (int k = 0; k < q; ++k) in_pos[k] = P.in_first ? k : d - 1 - k;   // far end first
-    for (int k = 0; k < p; ++k) out_pos[k] = P.in_first ? q + k : p - 1 - k;  // split first
     double f = 0.0, inter = 0.0;
-    double lead = double(P.N_in);
-    for (int k = 0; k < q; ++k) {
-      const int c = in_pos[k];
-      const double far = P.in_first ? P.ranks[c] : P.ranks[c + 1];
-      const double near = P.in_first ? P.ranks[c + 1] : P.ranks[c];
-      f += T * lead * far * near;  // lead still includes this core's mode
-      lead /= P.modes[c];
-      inter += T * lead * near;
-    }
-    double trail = 1.0;
-    for (int k = 0; k < p; ++k) {
-      const int c = out_pos[k];
-      const double near = P.in_first ? P.ranks[c] : P.ranks[c + 1];
-      const double far = P.in_first ? P.ranks[c + 1] : P.ranks[c];
-      trail *= P.modes[c];
-      f += T * trail * near * far;
-      inter += T * trail * far;
+    for (int t = 0; t < d; ++t) {
+      const SeqStep& st = P.seq[t];
+      const double around = double(st.A) * st.n * double(st.B);
+      f += T * around * st.rin * st.rout;
+      if (t < d - 1) inter += T * double(st.out_size);
     }
     macs[2] = 3.0 * f;
     bytes[2] = act_bytes + 4.0 * 3.0 * inter + 2.0 * core_elems * 4.0;
@@ -298,6 +377,33 @@ void linear_path_costs(const LinearPlan& P, double macs[4], double bytes[4]) {
   const double w = double(P.N_out) * double(P.N_in);
   macs[3] = 3.0 * T * w + 3.0 * w * r + 3.0 * merge;
   bytes[3] = act_bytes + 3.0 * w * 4.0 + 2.0 * core_elems * 4.0;
+}
+
+// Modelled time of one forward+backward.  At the sizes where the two orders
+// compete (a few tokens) both are bound by latency, not by multiply-adds:
+// the time is a count of dependent launches and in-kernel steps, each about
+// one memory round trip plus its barrier, with the multiply-adds and bytes
+// at the MI355X's fp32 MFMA and HBM rates on top.  Constants measured on one
+// MI355X with the six config-2 layer shapes at 1 to 128 tokens:
+//   a dependent launch of the merged order      ~7 us (six layers at one
+//                                                 token: 158 us per step)
+//   one step of the sequential kernels           ~14 us forward, ~23 us backward
+//                                                 (86 and 136 us per six-core layer)
+// so the sequential order, d dependent steps in each pass, is slower there
+// even where it needs fewer multiply-adds (below ~10 tokens).
+void linear_path_times(const LinearPlan& P, const double macs[4], const double bytes[4], double usec[4]) {
+  constexpr double kLaunch = 7.0, kSeqFwdStep = 14.0, kSeqBwdStep = 23.0;
+  constexpr double kMacPerUs = 157.3e6 / 2, kBytePerUs = 8.0e6;  // fp32 MFMA, HBM
+  const int levels = std::max(P.s - 1, P.d - 1 - P.s);
+  usec[0] = usec[3] = -1.0;
+  // merge, forward, dY pass, dZ sum, dX pass, reduction, one launch per sweep level
+  usec[1] = kLaunch * (6 + levels) + macs[1] / kMacPerUs + bytes[1] / kBytePerUs;
+  // forward, backward and reduction launches; one token per work-group, so
+  // more tokens than CUs add rounds of steps
+  const double rounds = std::ceil(double(std::max<int64_t>(1, P.T)) / 256.0);
+  usec[2] = P.seq_ok ? kLaunch * 3 + rounds * P.d * (kSeqFwdStep + kSeqBwdStep) + macs[2] / kMacPerUs +
+                           bytes[2] / kBytePerUs
+                     : -1.0;
 }
 
 }  // namespace ttc

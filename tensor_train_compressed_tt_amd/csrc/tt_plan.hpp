@@ -11,6 +11,11 @@
 namespace ttc {
 
 constexpr int kMaxCores = 2 * TTC_MAX_HALF_MODES;
+// most dynamic LDS the sequential kernels may use (one work-group per CU)
+constexpr size_t kSeqMaxLds = 152 * 1024;
+// most tokens of a sequential-path call (one work-group per token; meant for
+// small batches, where it needs fewer multiply-adds than the merged order)
+constexpr int64_t kSeqMaxTokens = 65536;
 constexpr int kTileT = 64;  // tokens per tile of the streaming kernels
 
 // Streaming kernels move 64-token x 256-byte slabs: 128 bf16 or 64 fp32 columns.
@@ -27,6 +32,25 @@ constexpr int bwd_max_slabs(int act_bytes, int NR) {
 constexpr int dx_max_slabs(int act_bytes, int NR) {
   return bwd_max_slabs(act_bytes, NR) / 2 < 1 ? 1 : bwd_max_slabs(act_bytes, NR) / 2;
 }
+
+// One step of the core-by-core (sequential) contraction order: the input
+// modes are contracted one core at a time from the input half's chain end
+// towards the split, then the output modes are produced one core at a time
+// from the split outwards.  A token's state before and after the step is a
+// row-major array [A][n][B][rank] around the step's mode (the mode is absent
+// from the contracted / not yet produced side).
+struct SeqStep {
+  int core;        // chain position of the core
+  int n, rin, rout;
+  int rightward;   // walk direction: element (x, i, y) of the core at
+                   // (x n + i) rout + y when rightward, else (y n + i) rin + x
+  int expand;      // 0: contracts an input mode, 1: produces an output mode
+  int64_t A, B;
+  int dlink;       // index of the link diagonal applied to the input state's rank, -1: none
+  int64_t in_off, out_off;    // state offsets in a token's state area (floats), -1: x / y
+  int64_t in_size, out_size;  // state sizes (floats)
+  int64_t gp_off;  // offset of this core's gradient partial in a token's partial area (floats)
+};
 
 struct LinearPlan {
   // ---- shape, chain order -------------------------------------------------
@@ -55,6 +79,14 @@ struct LinearPlan {
   int sw;                  // slab width in elements
   int dy_gc, dy_gt, dy_nsl, dy_tpg;  // dY pass: column groups, token groups, slabs/group, tiles/group
   int dx_gc, dx_gt, dx_nsl, dx_tpg;  // dX pass
+  // ---- path ------------------------------------------------------------------------
+  int path;                // resolved: TTC_PATH_MERGED or TTC_PATH_SEQUENTIAL
+  int seq_ok;              // the sequential path fits the device limits
+  SeqStep seq[kMaxCores];  // d steps: q contractions, then p expansions
+  int64_t seq_state_floats;  // per token: states 1 .. d-1
+  int64_t seq_part_floats;   // per token: one gradient partial per core
+  int64_t seq_max_state, seq_max_core;
+  size_t seq_lds_fwd, seq_lds_bwd;  // dynamic LDS bytes of the two sequential kernels
   // ---- saved layout (bytes) ----------------------------------------------------
   size_t sv_meta, sv_Ac, sv_AcT, sv_Bc, sv_BcT, sv_chain, sv_Z, sv_total;
   // ---- scratch layout (bytes) ----------------------------------------------------
@@ -70,7 +102,12 @@ constexpr size_t kMetaBytes = 1088;
 
 ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P);
 
+
+
 // multiply-adds and bytes of one forward+backward for each path (planner model)
 void linear_path_costs(const LinearPlan& P, double macs[4], double bytes[4]);
+// modelled time (microseconds) of one forward+backward per path on an
+// MI355X, -1 where the path does not apply (see tt_plan.cpp)
+void linear_path_times(const LinearPlan& P, const double macs[4], const double bytes[4], double usec[4]);
 
 }  // namespace ttc

@@ -53,7 +53,6 @@ def test_workspace_sizes_scale_with_tokens():
         (dict(act_dtype=7), 4),
         (dict(out_modes=(12, 0, 8)), 2),
         (dict(path=ttc.TTC_PATH_DENSE), 7),
-        (dict(path=ttc.TTC_PATH_SEQUENTIAL), 7),
     ],
 )
 def test_bad_descriptors_are_rejected(kw, code):
@@ -221,66 +220,189 @@ def test_rank_grads_errors_before_launch():
         ttc.tt_linear_rank_grads(d, G, D, [16] * 6, [16] * 5, float("nan"), 0.0)
     assert e.value.code == 2
 
-def _merged_macs(out_modes, in_modes, r, T):
-    """Independent count: skinny GEMMs of the merged order plus the half merges."""
-    n_out, n_in = 1, 1
-    for n in out_modes:
-        n_out *= n
-    for n in in_modes:
-        n_in *= n
-
-    def half(modes):
-        # chain product built one core at a time: (rows x r) (r x n r)
-        tot, rows = 0, modes[0]
-        for n in modes[1:]:
-            tot += rows * r * n * r
-            rows *= n
-        return tot
-
-    merge = half(list(out_modes)) + half(list(reversed(in_modes)))
-    return 3 * T * r * (n_in + n_out) + 3 * merge
+# ---- planner: contraction orders ----------------------------------------------------
+#
+# The forward pass is the tensor network {x, G_1, ..., G_d} contracted down to
+# Y (project page, "Making small tensor operations fast on GPUs": the order of
+# the pairwise contractions decides the cost; Proposition 4.1 compares the
+# merged order with the core-by-core one).  Contracting two tensors costs the
+# product of the sizes of all indices they carry.  These helpers count that
+# for every order of a small chain, independently of the library.
 
 
-def _sequential_macs(out_modes, in_modes, r, T):
-    """Independent count of the core-by-core sweep over x (forward f, total 3 f)."""
-    f = 0
-    lead = 1
-    for n in in_modes:
-        lead *= n
-    ranks_in = [r] * len(in_modes) + [1]  # rank left of each input core, then the end
-    for k in range(len(in_modes) - 1, -1, -1):
-        f += T * lead * ranks_in[k + 1] * ranks_in[k]
-        lead //= in_modes[k]
-    ranks_out = [1] + [r] * len(out_modes)
-    trail = 1
-    for k in range(len(out_modes) - 1, -1, -1):
-        trail *= out_modes[k]
-        f += T * trail * ranks_out[k + 1] * ranks_out[k]
-    return 3 * f
+def _network(out_modes, in_modes, ranks, in_first, T):
+    p, q = len(out_modes), len(in_modes)
+    d = p + q
+    chain = ([("i", m) for m in range(q)] + [("o", m) for m in range(p)]) if in_first else \
+        ([("o", m) for m in range(p)] + [("i", m) for m in range(q)])
+    dims = {"T": T}
+    for m in range(p):
+        dims[f"o{m}"] = out_modes[m]
+    for m in range(q):
+        dims[f"i{m}"] = in_modes[m]
+    for k in range(1, d):
+        dims[f"r{k}"] = ranks[k]
+    tensors = [frozenset(["T"] + [f"i{m}" for m in range(q)])]  # x
+    for k, (side, m) in enumerate(chain):
+        idx = {f"{side}{m}"}
+        if k > 0:
+            idx.add(f"r{k}")
+        if k < d - 1:
+            idx.add(f"r{k + 1}")
+        tensors.append(frozenset(idx))
+    out = frozenset(["T"] + [f"o{m}" for m in range(p)])
+    return tensors, dims, out, chain
 
 
-@pytest.mark.parametrize("T", [1, 64, 4096])
-@pytest.mark.parametrize("shape", [((12, 8, 8), (12, 8, 8)), ((12, 16, 16), (12, 8, 8)), ((2, 3), (3, 2))])
-def test_planner_cost_model_matches_independent_count(T, shape):
-    out_modes, in_modes = shape
-    r = 30 if len(out_modes) == 3 else 3
-    ranks = [1] + [r] * (len(out_modes) + len(in_modes) - 1) + [1]
-    d = ttc.make_linear_desc(out_modes, in_modes, ranks, ttc.TTC_F32)
+def _free(tensors, sub, out):
+    """Indices a group of tensors still carries after contracting it."""
+    inside = set().union(*(tensors[i] for i in sub))
+    outside = set().union(*(tensors[i] for i in range(len(tensors)) if i not in sub)) if len(sub) < len(tensors) else set()
+    return frozenset(i for i in inside if i in outside or i in out)
+
+
+def _pair_cost(a, b, dims):
+    c = 1
+    for i in a | b:
+        c *= dims[i]
+    return c
+
+
+def _optimal_cost(tensors, dims, out):
+    """Fewest multiply-adds over every pairwise contraction order (exhaustive)."""
+    n = len(tensors)
+    full = (1 << n) - 1
+    best = {}
+    for mask in range(1, full + 1):
+        sub = [i for i in range(n) if mask >> i & 1]
+        if len(sub) == 1:
+            best[mask] = 0
+            continue
+        b = None
+        part = (mask - 1) & mask
+        while part:
+            rest = mask ^ part
+            if part < rest:  # each split once
+                fa = _free(tensors, [i for i in range(n) if part >> i & 1], out)
+                fb = _free(tensors, [i for i in range(n) if rest >> i & 1], out)
+                c = best[part] + best[rest] + _pair_cost(fa, fb, dims)
+                b = c if b is None else min(b, c)
+            part = (part - 1) & mask
+        best[mask] = b
+    return best[full]
+
+
+def _order_cost(tensors, dims, out, steps):
+    """Cost of one given order: `steps` is a list of (group, group) pairs of
+    tensor-index tuples, each group already contracted."""
+    tot = 0
+    for ga, gb in steps:
+        tot += _pair_cost(_free(tensors, list(ga), out), _free(tensors, list(gb), out), dims)
+    return tot
+
+
+def _merged_order(d, s):
+    """Each half of the chain multiplied out from its end, then x through the
+    input half, then the output half (tensor 0 is x, core k is k + 1)."""
+    return s, d - s
+
+
+def _chain_orders(out_modes, in_modes, in_first, T, ranks):
+    tensors, dims, out, chain = _network(out_modes, in_modes, ranks, in_first, T)
+    p, q = len(out_modes), len(in_modes)
+    d = p + q
+    s = q if in_first else p
+    left = list(range(1, s + 1))          # cores of the left half (tensor ids)
+    right = list(range(s + 1, d + 1))
+    steps = []
+    # merged: left half from core 1 rightwards, right half from core d leftwards
+    g = (left[0],)
+    for c in left[1:]:
+        steps.append((g, (c,)))
+        g = g + (c,)
+    Lg = g
+    g = (right[-1],)
+    for c in reversed(right[:-1]):
+        steps.append(((c,), g))
+        g = (c,) + g
+    Rg = g
+    inp, outp = (Lg, Rg) if in_first else (Rg, Lg)
+    steps.append(((0,), inp))
+    steps.append(((0,) + inp, outp))
+    merged = _order_cost(tensors, dims, out, steps)
+    # sequential: x through the input half from its chain end, then the
+    # output half from the split outwards
+    walk = (left + right) if in_first else (right[::-1] + left[::-1])
+    g, steps = (0,), []
+    for c in walk:
+        steps.append((g, (c,)))
+        g = g + (c,)
+    sequential = _order_cost(tensors, dims, out, steps)
+    return merged, sequential, _optimal_cost(tensors, dims, out)
+
+
+CHAINS = [
+    ((2, 3), (3, 2), [1, 2, 3, 4, 1]),
+    ((2, 3), (3, 2), [1, 3, 2, 3, 1]),
+    ((2, 3, 2), (2, 2, 3), [1, 2, 3, 4, 3, 2, 1]),
+    ((4,), (2, 3, 2), [1, 3, 4, 2, 1]),
+    ((2, 2, 3), (5,), [1, 2, 3, 2, 1]),
+    ((3, 4), (4, 3), [1, 5, 5, 5, 1]),
+]
+
+
+@pytest.mark.parametrize("in_first", [False, True])
+@pytest.mark.parametrize("chain", CHAINS)
+@pytest.mark.parametrize("T", [1, 4, 64, 4096])
+def test_planner_costs_match_exhaustive_contraction_orders(chain, in_first, T):
+    """The planner's multiply-add counts of the merged and the core-by-core
+    orders equal the counts of those two orders in the network (forward;
+    the planner's totals are forward + backward = 3x), no order of the network
+    beats the merged order at a large batch, and AUTO picks the order with the
+    smaller modelled time."""
+    out_modes, in_modes, ranks = chain
+    d = ttc.make_linear_desc(out_modes, in_modes, ranks, ttc.TTC_F32, in_first)
+    merged, sequential, best = _chain_orders(out_modes, in_modes, in_first, T, ranks)
     m1, _ = ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_MERGED)
     m2, _ = ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_SEQUENTIAL)
-    assert m1 == pytest.approx(_merged_macs(out_modes, in_modes, r, T), rel=1e-12)
-    assert m2 == pytest.approx(_sequential_macs(out_modes, in_modes, r, T), rel=1e-12)
+    assert m1 == 3 * merged
+    assert m2 == 3 * sequential
+    assert best <= min(merged, sequential)
+    if T >= 4096:
+        assert best >= 0.99 * merged  # Proposition 4.1: near the fewest operations for large batches
+    f = _explain_fields(d, T)
+    assert f["path"] == ("sequential" if float(f["sequential_us"]) < float(f["merged_us"]) else "merged")
 
 
 def test_merged_order_wins_at_large_batch_and_loses_at_batch_one():
     """Project page, one contraction order for both passes: close to the fewest
     operations for large batches (Proposition 4.1); at batch 1 the core-by-core
-    sweep is cheaper, so a crossover exists."""
+    sweep needs fewer multiply-adds, so a crossover exists.  On this GPU both
+    orders are latency-bound at a few tokens and the modelled time of the
+    merged one is lower, so AUTO keeps it there too."""
     d = ttc.make_linear_desc((12, 8, 8), (12, 8, 8), [1, 30, 30, 30, 30, 30, 1], ttc.TTC_F32)
     for T in (64, 4096, 16384):
         assert ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_MERGED)[0] < ttc.tt_linear_path_cost(d, T, ttc.TTC_PATH_SEQUENTIAL)[0]
+        assert ttc.tt_linear_explain(d, T).startswith("path=merged")
     assert ttc.tt_linear_path_cost(d, 1, ttc.TTC_PATH_SEQUENTIAL)[0] < ttc.tt_linear_path_cost(d, 1, ttc.TTC_PATH_MERGED)[0]
-    assert "path=merged" in ttc.tt_linear_explain(d, 4096)
+    f = _explain_fields(d, 1)
+    assert float(f["merged_us"]) < float(f["sequential_us"]) and f["path"] == "merged"
+
+
+def test_forced_paths():
+    d = _desc(path=ttc.TTC_PATH_MERGED)
+    assert ttc.tt_linear_explain(d, 1).startswith("path=merged")
+    d = _desc(path=ttc.TTC_PATH_SEQUENTIAL)
+    assert ttc.tt_linear_explain(d, 4096).startswith("path=sequential")
+    # the sequential kernels keep a token's states and one core in LDS: a
+    # rank-64 core of mode 16 (256 KB) does not fit, so forcing it is refused
+    big = ttc.make_linear_desc((16, 16, 16), (16, 8, 8), [1] + [64] * 5 + [1], ttc.TTC_BF16, False,
+                               ttc.TTC_PATH_SEQUENTIAL)
+    with pytest.raises(ttc.TTCError) as e:
+        ttc.tt_linear_workspace(big, 8)
+    assert e.value.code == 7
+    auto = ttc.make_linear_desc((16, 16, 16), (16, 8, 8), [1] + [64] * 5 + [1], ttc.TTC_BF16)
+    assert ttc.tt_linear_explain(auto, 1).startswith("path=merged")
 
 
 # ---- TTM embedding -------------------------------------------------------------

@@ -4,7 +4,9 @@ Every case draws seeded inputs (synth), runs the HIP path through the C ABI
 and compares each output tensor with the oracle by relative L2 error
 ||gpu - ref|| / ||ref||: at most 1e-5 for fp32 activations, 2e-2 for bf16
 storage with fp32 accumulation.  Gradient slices whose link diagonal entry is
-zero must be exactly 0.0.
+zero must be exactly 0.0.  Unless a test says otherwise the layers are forced
+onto the merged contraction order (the sequential order has its own tests in
+test_gpu_sequential.py).
 """
 
 import numpy as np
@@ -46,10 +48,13 @@ def _to_dev(layer, dtype):
     return cores, D, x, dy
 
 
-def _run(spec, layer, dtype, want_dx=True):
+MERGED, SEQUENTIAL = 1, 2  # TTC_PATH_MERGED, TTC_PATH_SEQUENTIAL
+
+
+def _run(spec, layer, dtype, want_dx=True, path=MERGED):
     ttc = _ttc()
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first)
+    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, path)
     cores, D, x, dy = _to_dev(layer, dtype)
     y, saved = mod.forward(x, cores, D)
     dx, dG = mod.backward(x, dy, cores, D, saved, want_dx=want_dx)
@@ -58,8 +63,8 @@ def _run(spec, layer, dtype, want_dx=True):
     return f(y), (f(dx) if dx is not None else None), [f(g) for g in dG]
 
 
-def _check(spec, layer, dtype, want_dx=True):
-    y, dx, dG = _run(spec, layer, dtype, want_dx)
+def _check(spec, layer, dtype, want_dx=True, path=MERGED):
+    y, dx, dG = _run(spec, layer, dtype, want_dx, path)
     x = layer["x"].astype(np.float64)
     dy = layer["dy"].astype(np.float64)
     Yr = oracle.tt_linear_forward(x, spec.out_modes, spec.in_modes, layer["cores"], layer["D"], spec.in_first)
