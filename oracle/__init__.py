@@ -32,6 +32,7 @@ invariants).
 """
 
 from .tt_linear import (  # noqa: F401
+    chain_layout,
     chain_link_grads,
     early_stage_grads,
     tt_linear_link_grads,

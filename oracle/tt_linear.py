@@ -92,18 +92,53 @@ def chain_tensor(cores, D) -> np.ndarray:
     return (M @ G.reshape(r0, n)).reshape(-1)
 
 
-def dense_weight(out_modes, in_modes, cores, D, in_first: bool = False) -> np.ndarray:
-    """Dense W (N_out x N_in) reconstructed from the cores in fp64."""
+def chain_layout(out_modes, in_modes, in_first: bool = False, chain_perm=None):
+    """Where each mode sits in the chain.
+
+    Modes are listed output modes first, then input modes (mode m < p is
+    output mode m, mode p + j is input mode j).  ``chain_perm[m]`` is the
+    chain position of mode m; without it the chain holds the output modes
+    then the input modes in listed order, or the input modes first when
+    ``in_first``.  Returns (perm, chain_modes) with chain_modes[k] the size of
+    the mode at position k.  Any permutation is a valid chain order for the
+    weight itself (the pages leave the order of the modes in the chain open).
+    """
+    p, q = len(out_modes), len(in_modes)
+    listed = list(out_modes) + list(in_modes)
+    if chain_perm is None:
+        perm = [q + m for m in range(p)] + list(range(q)) if in_first else list(range(p + q))
+    else:
+        perm = [int(k) for k in chain_perm]
+    if sorted(perm) != list(range(p + q)):
+        raise ValueError(f"chain_perm {perm} is not a permutation of 0..{p + q - 1}")
+    chain_modes = [0] * (p + q)
+    for m, k in enumerate(perm):
+        chain_modes[k] = int(listed[m])
+    return perm, chain_modes
+
+
+def dense_weight(out_modes, in_modes, cores, D, in_first: bool = False, chain_perm=None) -> np.ndarray:
+    """Dense W (N_out x N_in) reconstructed from the cores in fp64: the chain
+    tensor with its axes put in listed mode order (output modes, then input
+    modes) and reshaped row-major."""
     n_out = int(np.prod(out_modes))
     n_in = int(np.prod(in_modes))
-    modes = list(in_modes) + list(out_modes) if in_first else list(out_modes) + list(in_modes)
+    perm, modes = chain_layout(out_modes, in_modes, in_first, chain_perm)
     got = [int(_f64(c).shape[1]) for c in cores]
     if got != modes:
         raise ValueError(f"core modes {got} do not match the chain {modes}")
-    T = chain_tensor(cores, D)
-    if in_first:
-        return T.reshape(n_in, n_out).T.copy()
-    return T.reshape(n_out, n_in)
+    T = chain_tensor(cores, D).reshape(modes)
+    return np.transpose(T, perm).reshape(n_out, n_in)
+
+
+def _dW_to_chain(dW, out_modes, in_modes, in_first, chain_perm):
+    """A gradient with respect to W, laid out as the chain tensor (flat)."""
+    perm, _ = chain_layout(out_modes, in_modes, in_first, chain_perm)
+    listed = list(out_modes) + list(in_modes)
+    inv = [0] * len(perm)
+    for m, k in enumerate(perm):
+        inv[k] = m
+    return np.transpose(_f64(dW).reshape(listed), inv).reshape(-1)
 
 
 def chain_core_grads(dT, cores, D) -> list:
@@ -129,28 +164,40 @@ def chain_core_grads(dT, cores, D) -> list:
     return grads
 
 
-def tt_linear_forward(x, out_modes, in_modes, cores, D, in_first: bool = False) -> np.ndarray:
+def tt_linear_forward(x, out_modes, in_modes, cores, D, in_first: bool = False, chain_perm=None) -> np.ndarray:
     """Y = x W^T for a batch of tokens x (T x N_in)."""
-    W = dense_weight(out_modes, in_modes, cores, D, in_first)
+    W = dense_weight(out_modes, in_modes, cores, D, in_first, chain_perm)
     return _f64(x) @ W.T
 
 
-def tt_linear_backward(x, dy, out_modes, in_modes, cores, D, in_first: bool = False):
+def tt_linear_backward(x, dy, out_modes, in_modes, cores, D, in_first: bool = False, chain_perm=None):
     """Input gradient and core gradients of the TT-linear layer.
 
     dX = dY W, dW = dY^T x, and dG_k = d<dW, W>/dG_k, i.e. the gradient of
     <dY, x W^T> with respect to each core with D fixed.  Returns (dX, [dG_k]).
     """
-    W = dense_weight(out_modes, in_modes, cores, D, in_first)
+    W = dense_weight(out_modes, in_modes, cores, D, in_first, chain_perm)
     dX = _f64(dy) @ W
-    return dX, tt_linear_core_grads(x, dy, cores, D, in_first)
+    return dX, tt_linear_core_grads(x, dy, cores, D, in_first, chain_perm, out_modes, in_modes)
 
 
-def tt_linear_core_grads(x, dy, cores, D, in_first: bool = False) -> list:
+def _modes_of(cores, in_first, chain_perm, out_modes, in_modes):
+    if out_modes is not None:
+        return out_modes, in_modes
+    if chain_perm is not None:
+        raise ValueError("a chain_perm needs out_modes and in_modes")
+    return None, None
+
+
+def tt_linear_core_grads(x, dy, cores, D, in_first: bool = False, chain_perm=None, out_modes=None,
+                         in_modes=None) -> list:
     """The core gradients alone: dW = dY^T x, then dG_k = d<dW, W>/dG_k."""
     dW = _f64(dy).T @ _f64(x)
-    dT = dW.T if in_first else dW           # back to the chain's own layout
-    return chain_core_grads(dT.reshape(-1), cores, D)
+    out_modes, in_modes = _modes_of(cores, in_first, chain_perm, out_modes, in_modes)
+    if out_modes is None:
+        dT = dW.T if in_first else dW           # back to the chain's own layout
+        return chain_core_grads(dT.reshape(-1), cores, D)
+    return chain_core_grads(_dW_to_chain(dW, out_modes, in_modes, in_first, chain_perm), cores, D)
 
 
 def chain_link_grads(dT, cores, D) -> list:
@@ -179,11 +226,15 @@ def chain_link_grads(dT, cores, D) -> list:
     return grads
 
 
-def tt_linear_link_grads(x, dy, cores, D, in_first: bool = False) -> list:
+def tt_linear_link_grads(x, dy, cores, D, in_first: bool = False, chain_perm=None, out_modes=None,
+                         in_modes=None) -> list:
     """dL/dD_k for L = <dY, x W^T>: dW = dY^T x, then chain_link_grads."""
     dW = _f64(dy).T @ _f64(x)
-    dT = dW.T if in_first else dW
-    return chain_link_grads(dT.reshape(-1), cores, D)
+    out_modes, in_modes = _modes_of(cores, in_first, chain_perm, out_modes, in_modes)
+    if out_modes is None:
+        dT = dW.T if in_first else dW
+        return chain_link_grads(dT.reshape(-1), cores, D)
+    return chain_link_grads(_dW_to_chain(dW, out_modes, in_modes, in_first, chain_perm), cores, D)
 
 
 def early_stage_grads(x, dy, cores, D, gamma: float, beta: float, in_first: bool = False):

@@ -9,7 +9,9 @@
   tensors gives every gradient entry exactly;
 * a zero D entry is the same as deleting the matching slices of both
   neighbouring cores (project page, "Learn the ranks while training");
-* a hand-worked two-core example under tests/golden/.
+* a hand-worked two-core example under tests/golden/;
+* a chain whose modes sit in any order (chain_perm): the brute-force sum
+  with each listed digit placed at its chain position.
 """
 
 import itertools
@@ -338,3 +340,93 @@ def test_early_stage_grads_central_differences():
         df = (J(cores, dp) - J(cores, dm)) / (2 * h)
         assert abs(df - np.sum(dD[k] * E)) <= 1e-8 * (1.0 + abs(df)), k
         assert np.all(dD[k][~live] == 0.0)
+
+
+# ---- modes in any chain order ----------------------------------------------------
+
+def _brute_W_perm(out_modes, in_modes, cores, D, perm):
+    """W[i, j]: the listed digits of (i, j), each put at its chain position."""
+    p = len(out_modes)
+    n_out, n_in = int(np.prod(out_modes)), int(np.prod(in_modes))
+    W = np.zeros((n_out, n_in))
+    for i in range(n_out):
+        for j in range(n_in):
+            listed = _digits(i, out_modes) + _digits(j, in_modes)
+            js = [0] * len(perm)
+            for m, k in enumerate(perm):
+                js[k] = listed[m]
+            W[i, j] = _brute_entry(cores, D, js)
+    return W
+
+
+PERMS = [
+    # out (2,3) in (3,2): mirrored input block, output block first
+    [0, 1, 3, 2],
+    # input block first, both blocks permuted
+    [3, 2, 1, 0],
+    # interleaved (the weight is still defined; the GPU's orders need blocks)
+    [0, 2, 1, 3],
+]
+
+
+@pytest.mark.parametrize("perm", PERMS)
+def test_W_chain_perm_matches_brute_force(perm):
+    rng = np.random.default_rng(11)
+    out_modes, in_modes = (2, 3), (3, 2)
+    listed = list(out_modes) + list(in_modes)
+    modes = [0] * 4
+    for m, k in enumerate(perm):
+        modes[k] = listed[m]
+    cores, D = _rand_chain(rng, modes, [1, 2, 3, 2, 1], zero_frac=0.34)
+    W = oracle.dense_weight(out_modes, in_modes, cores, D, chain_perm=perm)
+    Wb = _brute_W_perm(out_modes, in_modes, cores, D, perm)
+    assert np.max(np.abs(W - Wb)) <= 1e-13 * max(1.0, np.max(np.abs(Wb)))
+
+
+@pytest.mark.parametrize("in_first", [False, True])
+def test_default_chain_perm_is_the_listed_order(in_first):
+    rng = np.random.default_rng(12)
+    out_modes, in_modes = (2, 3, 2), (3, 2)
+    perm, modes = oracle.chain_layout(out_modes, in_modes, in_first)
+    assert perm == ([2, 3, 4, 0, 1] if in_first else [0, 1, 2, 3, 4])
+    cores, D = _rand_chain(rng, modes, [1, 2, 3, 2, 3, 1], zero_frac=0.3)
+    W1 = oracle.dense_weight(out_modes, in_modes, cores, D, in_first)
+    W2 = oracle.dense_weight(out_modes, in_modes, cores, D, chain_perm=perm)
+    assert np.array_equal(W1, W2)
+    np.testing.assert_allclose(W1, _brute_W(out_modes, in_modes, cores, D, in_first), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("perm", PERMS)
+def test_core_and_link_grads_chain_perm_by_unit_probes(perm):
+    """The loss is linear in each core and in each diagonal: unit probes give
+    every gradient entry, for modes in any chain order."""
+    rng = np.random.default_rng(13)
+    out_modes, in_modes = (2, 3), (3, 2)
+    listed = list(out_modes) + list(in_modes)
+    modes = [0] * 4
+    for m, k in enumerate(perm):
+        modes[k] = listed[m]
+    cores, D = _rand_chain(rng, modes, [1, 2, 3, 2, 1], zero_frac=0.0)
+    x = rng.standard_normal((3, 6))
+    dy = rng.standard_normal((3, 6))
+
+    def loss(cs, Ds):
+        return float(np.sum(dy * (x @ _brute_W_perm(out_modes, in_modes, cs, Ds, perm).T)))
+
+    _, dG = oracle.tt_linear_backward(x, dy, out_modes, in_modes, cores, D, chain_perm=perm)
+    for k in range(len(cores)):
+        for idx in np.ndindex(*cores[k].shape):
+            probe = np.zeros_like(cores[k])
+            probe[idx] = 1.0
+            trial = list(cores)
+            trial[k] = probe
+            want = loss(trial, D)
+            assert abs(dG[k][idx] - want) <= 1e-12 * (1.0 + abs(want)), (k, idx)
+    dD = oracle.tt_linear_link_grads(x, dy, cores, D, chain_perm=perm, out_modes=out_modes, in_modes=in_modes)
+    for k in range(len(D)):
+        for b in range(len(D[k])):
+            probe = [v.copy() for v in D]
+            probe[k][:] = 0.0
+            probe[k][b] = 1.0
+            want = loss(cores, probe)
+            assert abs(dD[k][b] - want) <= 1e-12 * (1.0 + abs(want)), (k, b)
