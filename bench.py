@@ -137,8 +137,7 @@ def step_bytes(specs, Ds, T, es):
     """
     out = []
     for s, D in zip(specs, Ds):
-        split = len(s.in_modes) if s.in_first else len(s.out_modes)
-        r_eff = int((D[split - 1] != 0).sum())
+        r_eff = int((D[s.split - 1] != 0).sum())
         out.append({
             "fwd": T * (s.n_in + s.n_out) * es + T * r_eff * 4,
             "bwd_dy": T * s.n_out * es + T * r_eff * 4,
@@ -229,7 +228,8 @@ def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None
     for li, spec in enumerate(specs):
         fresh = not (clone_encoders and li >= 6)
         L = synth.make_tt_layer(cfg, li, spec, T, zf, dt, acts=fresh)
-        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, PATHS[path])
+        mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, PATHS[path],
+                           spec.chain_perm)
         if fresh:
             if dt == "bf16":
                 x = torch.from_numpy(L["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)

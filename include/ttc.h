@@ -90,6 +90,30 @@ typedef struct {
   int32_t act_dtype;                      /* ttc_dtype of x, y, dy, dx              */
   int32_t path;                           /* ttc_path                               */
   int32_t flags;                          /* TTC_FLAG_* bits, 0 by default          */
+  /* Chain order of the modes.  Listing the modes as the p output modes, then
+   * the q input modes (mode m < p is out_modes[m], mode p + j is in_modes[j]),
+   * chain_perm[m] is the chain position (0 .. p+q-1) of mode m, i.e. core m'
+   * with chain_perm[m] == m' carries that mode; the cores, ranks and diagonals
+   * are given in chain order.  The row and column indices of W stay the
+   * listed mixed-radix indices whatever the chain order.  All entries -1 (or
+   * all 0) for the first p+q: the default order set by in_first, which is
+   * then ignored otherwise.  The output modes must fill one end of the chain
+   * and the input modes the other (any order inside each block), so that
+   * one link joins the two kinds (TTC_ERR_UNSUPPORTED otherwise: the weight
+   * is still defined, but neither contraction order here takes it);
+   * TTC_ERR_SHAPE when the entries are not a permutation.  Example: the
+   * mirrored layout whose end cores carry the largest modes (project page,
+   * results, rank table of the compressed encoder: ranks (12,30,30,30,12) for
+   * modes (12,8,8) x (12,8,8)) is out (12,8,8), in (12,8,8) with
+   * chain_perm = {0,1,2,5,4,3}. */
+  int32_t chain_perm[2 * TTC_MAX_HALF_MODES];
+  /* The link at which the merged order cuts the chain into the two products
+   * it multiplies out (project page, "Making small tensor operations fast on
+   * GPUs"): -1 for the link between the output and the input modes, the only
+   * link where each product holds modes of one kind, which the skinny
+   * token products need; that link's index (s = number of modes in the first
+   * block) is accepted too, any other value gives TTC_ERR_UNSUPPORTED. */
+  int32_t split;
 } tt_linear_desc;
 
 /* tt_linear_fwd: `saved` already holds the merged halves written by
@@ -450,6 +474,19 @@ ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T,
                          const void* saved, size_t saved_bytes,
                          float* const* dF, void* scratch, size_t scratch_bytes,
                          ttc_stream_t stream);
+
+/*
+ * Device-side error of a TTM lookup, for tests and diagnostics: waits for
+ * `stream` (a host synchronisation: not for use under graph capture), then
+ * sets *code to the flag the lookup keeps in word 1 of its `saved` buffer:
+ * 1 if some id of the batch was outside [0, prod m_k) (such ids give zero
+ * rows and no gradient), 0 otherwise.  `saved` is the buffer passed to
+ * ttm_embed_fwd / ttm_embed_index.  The TT-linear entry points check every
+ * argument on the host before enqueuing anything, so they have no
+ * device-side error to report.  TTC_ERR_NULL for a NULL pointer,
+ * TTC_ERR_HIP if the copy or the wait fails.
+ */
+ttc_status ttc_device_error(const void* saved, ttc_stream_t stream, int32_t* code);
 
 /* Human-readable name of a status code (static storage). */
 const char* ttc_status_str(ttc_status s);

@@ -66,6 +66,7 @@ class LayerSpec:
     in_modes: tuple
     rank: int
     in_first: bool = False
+    chain_perm: tuple | None = None  # chain position of each mode (outputs, then inputs)
 
     @property
     def n_out(self) -> int:
@@ -77,9 +78,23 @@ class LayerSpec:
 
     @property
     def chain_modes(self) -> list:
+        if self.chain_perm is not None:
+            listed = list(self.out_modes) + list(self.in_modes)
+            modes = [0] * len(listed)
+            for m, k in enumerate(self.chain_perm):
+                modes[k] = listed[m]
+            return modes
         if self.in_first:
             return list(self.in_modes) + list(self.out_modes)
         return list(self.out_modes) + list(self.in_modes)
+
+    @property
+    def split(self) -> int:
+        """Chain link between the output and the input modes (cores before it)."""
+        if self.chain_perm is not None:
+            first_out = min(self.chain_perm[: len(self.out_modes)])
+            return len(self.out_modes) if first_out == 0 else len(self.in_modes)
+        return len(self.in_modes) if self.in_first else len(self.out_modes)
 
     @property
     def ranks(self) -> list:

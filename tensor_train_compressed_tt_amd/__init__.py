@@ -56,6 +56,7 @@ EXPORTS = [
     "ttm_embed_index",
     "ttm_embed_lookup",
     "ttm_embed_bwd",
+    "ttc_device_error",
     "ttc_status_str",
     "ttc_version",
     "ttc_trace_start",
@@ -82,6 +83,8 @@ class TTLinearDesc(ctypes.Structure):
         ("act_dtype", ctypes.c_int32),
         ("path", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("chain_perm", ctypes.c_int32 * (2 * MAX_HALF_MODES)),
+        ("split", ctypes.c_int32),
     ]
 
 
@@ -154,6 +157,8 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    L.ttc_device_error.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)]
+    L.ttc_device_error.restype = ctypes.c_int
     L.ttc_status_str.argtypes = [ctypes.c_int]
     L.ttc_status_str.restype = ctypes.c_char_p
     L.ttc_version.argtypes = []
@@ -181,7 +186,11 @@ def _ptrs(addrs: Sequence[int] | None):
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), arr
 
 
-def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=False, path=TTC_PATH_AUTO, flags=0):
+def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=False, path=TTC_PATH_AUTO, flags=0,
+                     chain_perm=None, split=-1):
+    """chain_perm: chain position of each mode (output modes, then input
+    modes), or None for the order given by in_first; split: -1 or the link
+    between the two kinds of modes."""
     d = TTLinearDesc()
     d.p, d.q = len(out_modes), len(in_modes)
     for i, n in enumerate(out_modes):
@@ -194,6 +203,12 @@ def make_linear_desc(out_modes, in_modes, ranks, act_dtype=TTC_F32, in_first=Fal
     d.act_dtype = int(act_dtype)
     d.path = int(path)
     d.flags = int(flags)
+    for i in range(2 * MAX_HALF_MODES):
+        d.chain_perm[i] = -1
+    if chain_perm is not None:
+        for i, k in enumerate(chain_perm):
+            d.chain_perm[i] = int(k)
+    d.split = int(split)
     return d
 
 
@@ -355,6 +370,13 @@ def tt_linear_rank_grads_batch(descs, G, D, dG, dD, gamma=0.0, beta=0.0, stream=
     dp, _ta, (ga, da, gg, ddd), _keep = _batch_args(descs, [0] * len(descs), [G, D, dG, dD])
     code = lib().tt_linear_rank_grads_batch(len(descs), dp, ga, da, gg, ddd, float(gamma), float(beta), stream)
     _check("tt_linear_rank_grads_batch", code)
+
+
+def ttc_device_error(saved: int, stream=0) -> int:
+    """The device-side error flag of a TTM lookup's saved buffer (syncs the stream)."""
+    code = ctypes.c_int32(0)
+    _check("ttc_device_error", lib().ttc_device_error(saved, stream, ctypes.byref(code)))
+    return int(code.value)
 
 
 def tt_linear_explain(desc: TTLinearDesc, T: int) -> str:

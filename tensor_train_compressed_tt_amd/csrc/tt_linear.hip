@@ -79,7 +79,8 @@ struct MergeLayer {
   const float* G[kMaxCores];
   const float* D[kMaxCores];  // D[k] on the link between cores k and k+1
   float* chain;               // prefix / suffix products (fp32)
-  int64_t chain_off[kMaxCores];
+  int chain_off[kMaxCores];   // float offsets (the plan keeps them below 2^31)
+  int lstride[kMaxCores];     // stride of each position's mode in its kind's listed index
   int modes[kMaxCores];
   int ranks[kMaxCores + 1];
   void* Ac;
@@ -239,6 +240,29 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   int ci = kMergeOut / (kMergePG * rout);
   if (ci > n) ci = n;
   const float* v = vb[cur];
+  // the operand row of (prefix, mode index i) is its listed index: the sum of
+  // every chain digit times that mode's stride in the listed order (the chain
+  // index itself when each half lists its modes in chain order)
+  __shared__ int64_t lbase[kMergePG];
+  if (tid < npg) {
+    const int64_t p = p0 + tid;
+    int64_t rem = p, b = 0;
+    if (left) {
+      for (int t = S - 2; t >= 0; --t) {
+        b += (rem % a.modes[t]) * a.lstride[t];
+        rem /= a.modes[t];
+      }
+    } else {
+      for (int t = 0; t <= S - 2; ++t) {
+        const int k = d - 1 - t;
+        b += (rem % a.modes[k]) * a.lstride[k];
+        rem /= a.modes[k];
+      }
+    }
+    lbase[tid] = b;
+  }
+  const int64_t lsf = a.lstride[kf];
+  __syncthreads();
   for (int i0 = 0; i0 < n; i0 += ci) {
     const int ni = n - i0 < ci ? n - i0 : ci;
     for (int e = tid; e < ni * rout; e += kMergeThreads) {
@@ -261,7 +285,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
       const int b = j < reff ? live[j] : -1;
       const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
       const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? Ds[b] * val : val);
-      const int64_t idx = left ? (p0 + pg) * n + i0 + ii : (int64_t)(i0 + ii) * NP + p0 + pg;
+      const int64_t idx = lbase[pg] + (int64_t)(i0 + ii) * lsf;
       out[idx * Rpad + j] = ev;
     }
     for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
       const int b = j < reff ? live[j] : -1;
       const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
       const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? Ds[b] * val : val);
-      const int64_t idx = left ? (p0 + pg) * n + i0 + ii : (int64_t)(i0 + ii) * NP + p0 + pg;
+      const int64_t idx = lbase[pg] + (int64_t)(i0 + ii) * lsf;
       outT[(int64_t)j * Nlong + idx] = ev;
     }
     __syncthreads();
@@ -1219,7 +1243,22 @@ struct ReduceArgs {
   float* dR;
   int64_t N_out, N_in;
   int rs, Rpad, in_first;
+  // chain order inside the halves differing from the listed order: the
+  // listed modes of each side and the chain stride of each (B: output, A: input)
+  int perm, nmB, nmA;
+  int szB[TTC_MAX_HALF_MODES], csB[TTC_MAX_HALF_MODES];
+  int szA[TTC_MAX_HALF_MODES], csA[TTC_MAX_HALF_MODES];
 };
+
+// listed (mixed-radix) index -> index in the half's chain order
+__device__ __forceinline__ int64_t listed_to_chain(int64_t li, int nm, const int* sz, const int* cs) {
+  int64_t c = 0;
+  for (int m = nm - 1; m >= 0; --m) {
+    c += (li % sz[m]) * cs[m];
+    li /= sz[m];
+  }
+  return c;
+}
 
 // Layers reduced by one launch.  A work-group owns 64 consecutive 4-column
 // groups of one rank row of one side (B or A) of one layer; its four waves
@@ -1283,6 +1322,9 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceBatch rb) {
   }
   if (w > 0) part[w - 1][lane] = acc;
   __syncthreads();
+  auto row = [&](int64_t li) {
+    return a.perm ? (isB ? listed_to_chain(li, a.nmB, a.szB, a.csB) : listed_to_chain(li, a.nmA, a.szA, a.csA)) : li;
+  };
   if (w != 0 || j < 0 || r0 >= N) {
     // dead slice: its gradient rows / columns are exactly zero
     if (w == 0 && r0 < N) {
@@ -1291,9 +1333,9 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceBatch rb) {
       for (int e = 0; e < 4; ++e)
         if (r0 + e < N) {
           if (toL)
-            a.dL[(r0 + e) * a.rs + b] = 0.f;
+            a.dL[row(r0 + e) * a.rs + b] = 0.f;
           else
-            a.dR[(int64_t)b * N + r0 + e] = 0.f;
+            a.dR[(int64_t)b * N + row(r0 + e)] = 0.f;
         }
     }
     return;
@@ -1306,9 +1348,9 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceBatch rb) {
   for (int e = 0; e < 4; ++e) {
     if (r0 + e < N) {
       if (toL)
-        a.dL[(r0 + e) * a.rs + b] = acc[e];
+        a.dL[row(r0 + e) * a.rs + b] = acc[e];
       else
-        a.dR[(int64_t)b * N + r0 + e] = acc[e];
+        a.dR[(int64_t)b * N + row(r0 + e)] = acc[e];
     }
   }
 }
@@ -2244,7 +2286,8 @@ static MergeLayer merge_layer(const LayerJob& j) {
   for (int k = 0; k < P.d; ++k) {
     m.G[k] = j.c.G[k];
     m.modes[k] = P.modes[k];
-    m.chain_off[k] = P.chain_off[k] < 0 ? 0 : P.chain_off[k];
+    m.chain_off[k] = P.chain_off[k] < 0 ? 0 : (int)P.chain_off[k];
+    m.lstride[k] = P.lstride[k];
   }
   for (int k = 0; k < P.d - 1; ++k) m.D[k] = j.c.D[k];
   for (int k = 0; k <= P.d; ++k) m.ranks[k] = P.ranks[k];
@@ -2400,6 +2443,18 @@ static void launch_cores_batch(const LayerJob* jobs, int n, hipStream_t s) {
     r.rs = P.rs;
     r.Rpad = P.Rpad;
     r.in_first = P.in_first;
+    r.perm = !P.perm_trivial;
+    r.nmB = P.p;
+    r.nmA = P.q;
+    for (int k = 0; k < P.d; ++k) {
+      if (P.is_in[k]) {
+        r.szA[P.lidx[k]] = P.modes[k];
+        r.csA[P.lidx[k]] = P.cstride[k];
+      } else {
+        r.szB[P.lidx[k]] = P.modes[k];
+        r.csB[P.lidx[k]] = P.cstride[k];
+      }
+    }
     rb.first[rb.n + 1] =
         rb.first[rb.n] + (int64_t)P.rs * (((P.N_out + 3) / 4 + 63) / 64 + ((P.N_in + 3) / 4 + 63) / 64);
     if (++rb.n == kMaxBatch) flush();

@@ -30,14 +30,42 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   if (T < 0 || T > (int64_t(1) << 31) - 1) return TTC_ERR_SHAPE;
   if (desc->act_dtype != TTC_F32 && desc->act_dtype != TTC_BF16) return TTC_ERR_DTYPE;
   if (desc->in_first != 0 && desc->in_first != 1) return TTC_ERR_SHAPE;
+  int in_first = desc->in_first;
   if (desc->path < TTC_PATH_AUTO || desc->path > TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
   if (desc->path == TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
   if (desc->flags & ~TTC_FLAG_PREPARED) return TTC_ERR_UNSUPPORTED;
   const int d = p + q;
+  // chain position of each listed mode (output modes, then input modes)
+  int pos_of[kMaxCores];
+  {
+    bool all_m1 = true, all_0 = true;
+    for (int m = 0; m < d; ++m) {
+      all_m1 = all_m1 && desc->chain_perm[m] == -1;
+      all_0 = all_0 && desc->chain_perm[m] == 0;
+    }
+    if (all_m1 || all_0) {
+      for (int m = 0; m < d; ++m) pos_of[m] = in_first ? (m < p ? q + m : m - p) : m;
+    } else {
+      bool seen[kMaxCores] = {};
+      for (int m = 0; m < d; ++m) {
+        const int k = desc->chain_perm[m];
+        if (k < 0 || k >= d || seen[k]) return TTC_ERR_SHAPE;
+        seen[k] = true;
+        pos_of[m] = k;
+      }
+      // one link between the kinds: the output modes fill one end of the chain
+      int lo = d;
+      for (int m = 0; m < p; ++m) lo = std::min(lo, pos_of[m]);
+      if (lo != 0 && lo != q) return TTC_ERR_UNSUPPORTED;
+      for (int m = 0; m < p; ++m)
+        if (pos_of[m] >= lo + p) return TTC_ERR_UNSUPPORTED;
+      in_first = lo == q;
+    }
+  }
   P->p = p;
   P->q = q;
   P->d = d;
-  P->in_first = desc->in_first;
+  P->in_first = in_first;
   P->act = desc->act_dtype;
   int64_t nout = 1, nin = 1;
   for (int k = 0; k < p; ++k) {
@@ -51,23 +79,40 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   if (nout > (1 << 24) || nin > (1 << 24)) return TTC_ERR_SHAPE;
   P->N_out = nout;
   P->N_in = nin;
-  for (int k = 0; k < d; ++k) {
-    if (!desc->in_first)
-      P->modes[k] = k < p ? desc->out_modes[k] : desc->in_modes[k - p];
-    else
-      P->modes[k] = k < q ? desc->in_modes[k] : desc->out_modes[k - q];
+  for (int m = 0; m < d; ++m) {
+    const int k = pos_of[m];
+    P->is_in[k] = m >= p;
+    P->lidx[k] = m < p ? m : m - p;
+    P->modes[k] = m < p ? desc->out_modes[m] : desc->in_modes[m - p];
+  }
+  // strides of each position: in its kind's listed index, in its half's chain index
+  {
+    const int sp = in_first ? q : p;
+    for (int k = 0; k < d; ++k) {
+      const int* md = P->is_in[k] ? desc->in_modes : desc->out_modes;
+      const int nk = P->is_in[k] ? q : p;
+      int64_t ls = 1;
+      for (int u = P->lidx[k] + 1; u < nk; ++u) ls *= md[u];
+      int64_t cs = 1;
+      for (int u = k + 1; u < (k < sp ? sp : d); ++u) cs *= P->modes[u];
+      P->lstride[k] = (int)ls;
+      P->cstride[k] = (int)cs;
+    }
+    P->perm_trivial = 1;
+    for (int k = 0; k < d; ++k) P->perm_trivial &= P->lstride[k] == P->cstride[k];
   }
   if (desc->ranks[0] != 1 || desc->ranks[d] != 1) return TTC_ERR_RANK;
   for (int k = 0; k <= d; ++k) {
     if (desc->ranks[k] < 1 || desc->ranks[k] > TTC_MAX_RANK) return TTC_ERR_RANK;
     P->ranks[k] = desc->ranks[k];
   }
-  P->s = desc->in_first ? q : p;
+  P->s = in_first ? q : p;
+  if (desc->split != -1 && desc->split != P->s) return TTC_ERR_UNSUPPORTED;
   P->rs = P->ranks[P->s];
   P->Rpad = ((P->rs + 31) / 32) * 32;
   P->NR = P->Rpad / 16;
-  P->NL = desc->in_first ? nin : nout;
-  P->NRt = desc->in_first ? nout : nin;
+  P->NL = in_first ? nin : nout;
+  P->NRt = in_first ? nout : nin;
   P->T = T;
   P->es = desc->act_dtype == TTC_BF16 ? 2 : 4;
   // The streaming kernels address their operands through buffer resources of
@@ -97,6 +142,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
     off += cols * P->ranks[k];
   }
   P->chain_floats = off;
+  if (off > 0x7fffffff) return TTC_ERR_UNSUPPORTED;  // offsets are 32-bit in the merge kernel
   // merge work items: one per row of every left prefix M_k (k < s) and one per
   // column of every right suffix N_k (k >= s)
   int64_t items = 0;
@@ -116,15 +162,9 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
 
   // ---- the sequential order's steps ---------------------------------------------------
   {
-    // chain position -> (input mode?, listed index)
-    int is_in[kMaxCores], lidx[kMaxCores];
-    for (int k = 0; k < d; ++k) {
-      const bool in = desc->in_first ? k < q : k >= p;
-      is_in[k] = in;
-      lidx[k] = desc->in_first ? (in ? k : k - q) : (in ? k - p : k);
-    }
+    const int* lidx = P->lidx;
     const int s = P->s;
-    const bool in_left = desc->in_first != 0;  // the input half is left of the split
+    const bool in_left = in_first != 0;  // the input half is left of the split
     int order[kMaxCores], nst = 0;
     if (in_left)
       for (int k = 0; k < s; ++k) order[nst++] = k;
@@ -181,7 +221,6 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
       goff += (int64_t)st.rin * st.n * st.rout;
       P->seq_max_state = std::max(P->seq_max_state, st.out_size);
       P->seq_max_core = std::max<int64_t>(P->seq_max_core, (int64_t)st.rin * st.n * st.rout);
-      (void)is_in;
     }
     P->seq_state_floats = soff;
     P->seq_part_floats = goff;

@@ -60,6 +60,11 @@ struct LinearPlan {
   int es;                  // bytes per activation element
   int modes[kMaxCores];    // n_k in chain order
   int ranks[kMaxCores + 1];
+  int lidx[kMaxCores];     // listed index (within its kind) of the mode at each chain position
+  int is_in[kMaxCores];    // the mode at each chain position is an input mode
+  int lstride[kMaxCores];  // stride of that mode in the listed index of its kind
+  int cstride[kMaxCores];  // stride of that position in its half's chain-order index
+  int perm_trivial;        // each half's chain order is its kind's listed order
   int s;                   // cores in the left half of the chain
   int rs;                  // rank of the link between the halves
   int Rpad;                // rs rounded up to 32 (MFMA tile multiple)

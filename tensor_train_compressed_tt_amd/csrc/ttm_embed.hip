@@ -1209,6 +1209,19 @@ static ttc_status check_cores(const TtmPlan& P, const float* const* F, const flo
 
 using namespace ttc;
 
+extern "C" ttc_status ttc_device_error(const void* saved, ttc_stream_t stream, int32_t* code) {
+  if (!saved || !code) return TTC_ERR_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  (void)hipGetLastError();
+  if (hipMemcpyAsync(&word, static_cast<const char*>(saved) + 4, sizeof(word), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return TTC_ERR_HIP;
+  *code = word;
+  return TTC_OK;
+}
+
 extern "C" ttc_status ttm_embed_workspace(const ttm_embed_desc* desc, int64_t T, size_t* saved_bytes,
                                           size_t* scratch_bytes) {
   if (!saved_bytes || !scratch_bytes) return TTC_ERR_NULL;

@@ -78,18 +78,29 @@ class TTLinear:
     vectors; activations are fp32 or bf16.
     """
 
-    def __init__(self, out_modes, in_modes, ranks, dtype=torch.float32, in_first=False, path=TTC_PATH_AUTO):
+    def __init__(self, out_modes, in_modes, ranks, dtype=torch.float32, in_first=False, path=TTC_PATH_AUTO,
+                 chain_perm=None):
         self.out_modes = tuple(int(n) for n in out_modes)
         self.in_modes = tuple(int(n) for n in in_modes)
         self.ranks = tuple(int(r) for r in ranks)
         self.in_first = bool(in_first)
+        self.chain_perm = None if chain_perm is None else tuple(int(k) for k in chain_perm)
         self.dtype = dtype
         self.n_out = math.prod(self.out_modes)
         self.n_in = math.prod(self.in_modes)
-        self.desc = make_linear_desc(self.out_modes, self.in_modes, self.ranks, _ACT[dtype], in_first, path)
+        self.desc = make_linear_desc(self.out_modes, self.in_modes, self.ranks, _ACT[dtype], in_first, path,
+                                     chain_perm=self.chain_perm)
         self.desc_prepared = make_linear_desc(self.out_modes, self.in_modes, self.ranks, _ACT[dtype], in_first, path,
-                                              TTC_FLAG_PREPARED)
-        modes = list(self.in_modes) + list(self.out_modes) if in_first else list(self.out_modes) + list(self.in_modes)
+                                              TTC_FLAG_PREPARED, chain_perm=self.chain_perm)
+        listed = list(self.out_modes) + list(self.in_modes)
+        if self.chain_perm is not None:
+            modes = [0] * len(listed)
+            for m, k in enumerate(self.chain_perm):
+                modes[k] = listed[m]
+        elif in_first:
+            modes = list(self.in_modes) + list(self.out_modes)
+        else:
+            modes = listed
         self.core_shapes = [(self.ranks[k], modes[k], self.ranks[k + 1]) for k in range(len(modes))]
 
     def workspace(self, T: int):

@@ -536,3 +536,40 @@ def test_buffer_resource_extents_are_bounded(act, rank, in_modes, ok):
             toks = int(f[f"{pas}_tiles"]) * 64
             assert toks * ncols * es <= 2**31 - 1, (pas, T, toks)
             assert toks * rpad * 4 <= 2**31 - 1, (pas, T, toks)
+
+
+# ---- chain order (chain_perm) and split ----------------------------------------------
+
+def test_chain_perm_and_split_validation():
+    base = dict(out_modes=(12, 8, 8), in_modes=(12, 8, 8), ranks=[1, 30, 30, 30, 30, 30, 1], act_dtype=ttc.TTC_BF16)
+
+    def desc(**kw):
+        b = dict(base)
+        b.update(kw)
+        return ttc.make_linear_desc(**b)
+
+    def code(d):
+        try:
+            ttc.tt_linear_workspace(d, 64)
+            return 0
+        except ttc.TTCError as e:
+            return e.code
+
+    assert code(desc(chain_perm=(0, 1, 2, 5, 4, 3))) == 0           # mirrored input block
+    assert code(desc(chain_perm=(5, 4, 3, 0, 1, 2))) == 0           # inputs first, outputs reversed
+    assert code(desc(chain_perm=(0, 1, 2, 3, 4, 4))) == 2           # not a permutation
+    assert code(desc(chain_perm=(0, 1, 2, 3, 4, 6))) == 2           # out of range
+    assert code(desc(chain_perm=(0, 3, 1, 2, 4, 5))) == 7           # interleaved kinds: two links between them
+    assert code(desc(split=3)) == 0 and code(desc(split=-1)) == 0
+    assert code(desc(split=2)) == 7 and code(desc(split=4)) == 7
+    assert code(desc(chain_perm=(3, 4, 5, 0, 1, 2), split=3)) == 0  # inputs first: s = 3 as well
+    # the explicit identity and all-zero entries both mean the default order
+    for perm in ((0, 1, 2, 3, 4, 5), None):
+        assert ttc.tt_linear_explain(desc(chain_perm=perm), 64) == ttc.tt_linear_explain(desc(), 64)
+    d0 = desc()
+    for i in range(16):
+        d0.chain_perm[i] = 0
+    assert ttc.tt_linear_explain(d0, 64) == ttc.tt_linear_explain(desc(), 64)
+    # inputs-first permutation ignores in_first
+    assert ttc.tt_linear_explain(desc(chain_perm=(3, 4, 5, 0, 1, 2), in_first=False), 64) == \
+        ttc.tt_linear_explain(desc(in_first=True), 64)

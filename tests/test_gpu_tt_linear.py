@@ -54,7 +54,7 @@ MERGED, SEQUENTIAL = 1, 2  # TTC_PATH_MERGED, TTC_PATH_SEQUENTIAL
 def _run(spec, layer, dtype, want_dx=True, path=MERGED):
     ttc = _ttc()
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, path)
+    mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, path, spec.chain_perm)
     cores, D, x, dy = _to_dev(layer, dtype)
     y, saved = mod.forward(x, cores, D)
     dx, dG = mod.backward(x, dy, cores, D, saved, want_dx=want_dx)
@@ -67,9 +67,10 @@ def _check(spec, layer, dtype, want_dx=True, path=MERGED):
     y, dx, dG = _run(spec, layer, dtype, want_dx, path)
     x = layer["x"].astype(np.float64)
     dy = layer["dy"].astype(np.float64)
-    Yr = oracle.tt_linear_forward(x, spec.out_modes, spec.in_modes, layer["cores"], layer["D"], spec.in_first)
+    Yr = oracle.tt_linear_forward(x, spec.out_modes, spec.in_modes, layer["cores"], layer["D"], spec.in_first,
+                                  spec.chain_perm)
     dXr, dGr = oracle.tt_linear_backward(x, dy, spec.out_modes, spec.in_modes, layer["cores"], layer["D"],
-                                         spec.in_first)
+                                         spec.in_first, spec.chain_perm)
     tol = TOL[dtype]
     errs = {"Y": _rel(y, Yr)}
     if want_dx:

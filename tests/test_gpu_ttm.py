@@ -222,6 +222,13 @@ def test_out_of_range_ids_flagged_and_zero():
     out, dF, saved = _run(vocab, dims, ranks, cores, D, ids, dout)
     _check_integer(saved, ids, vocab)
     _check_float(out, dF, ids, dout, cores, D, vocab)
+    # the same flag through the C ABI's device-error query
+    ttc = _ttc()
+    stream = torch.cuda.current_stream().cuda_stream
+    assert ttc.ttc_device_error(saved.data_ptr(), stream) == 1
+    ids = np.clip(ids, 0, 63)
+    _, _, saved = _run(vocab, dims, ranks, cores, D, ids, dout)
+    assert ttc.ttc_device_error(saved.data_ptr(), stream) == 0
 
 
 def test_accumulate_and_zero_tokens():
