@@ -69,6 +69,8 @@ def parse(argv=None):
                     help="run the merges on the side stream and the embedding lookup on the main one")
     ap.add_argument("--no-qkv-batch", action="store_true",
                     help="one launch per layer for the Q, K and V projections instead of one batched launch")
+    ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "fp8"],
+                    help="activation storage instead of the config's (fp8: OCP e4m3 activations and MFMA operands)")
     ap.add_argument("--path", default="auto", choices=["auto", "merged", "sequential"],
                     help="contraction order of every layer (default: the planner's pick for the batch)")
     ap.add_argument("--one-input-set", action="store_true",
@@ -202,8 +204,11 @@ class StepOptions:
 PATHS = {"auto": 0, "merged": 1, "sequential": 2}
 
 
+TORCH_DTYPES = {"f32": "float32", "bf16": "bfloat16", "fp8": "float8_e4m3fn"}
+
+
 def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None, clone_encoders=False,
-                path="auto"):
+                path="auto", dtype=None):
     """Device buffers of the step's TT-linear layers, in execution order.
 
     Every layer has its own seeded cores, diagonals, x and dY (synth), uploaded
@@ -219,11 +224,11 @@ def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None
     import tensor_train_compressed_tt_amd as ttc
 
     zf = synth.CONFIG_ZERO_FRAC[cfg]
-    dt = synth.CONFIG_DTYPE[cfg]
+    dt = dtype or synth.CONFIG_DTYPE[cfg]
     specs = synth.config_layers(cfg, rank)
     if n_layers is not None:
         specs = specs[:n_layers]
-    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    tdt = getattr(torch, TORCH_DTYPES[dt])
     layers, host = [], []
     for li, spec in enumerate(specs):
         fresh = not (clone_encoders and li >= 6)
@@ -234,6 +239,9 @@ def make_layers(cfg, rank, T, dev, n_sets=N_SETS, keep_host=False, n_layers=None
             if dt == "bf16":
                 x = torch.from_numpy(L["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
                 dy = torch.from_numpy(L["dy_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+            elif dt == "fp8":
+                x = torch.from_numpy(L["x_bits"]).to(dev).view(torch.float8_e4m3fn)
+                dy = torch.from_numpy(L["dy_bits"]).to(dev).view(torch.float8_e4m3fn)
             else:
                 x = torch.from_numpy(L["x"]).to(dev)
                 dy = torch.from_numpy(L["dy"]).to(dev)
@@ -560,8 +568,8 @@ def main():
     T = args.tokens if args.tokens is not None else synth.CONFIG_TOKENS[cfg]
     if not 1 <= T <= 16384:
         sys.exit("--tokens must be in [1, 16384] (the embedding sorts at most 16384 ids per call)")
-    dt = synth.CONFIG_DTYPE[cfg]
-    es = 2 if dt == "bf16" else 4
+    dt = args.dtype or synth.CONFIG_DTYPE[cfg]
+    es = {"f32": 4, "bf16": 2, "fp8": 1}[dt]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     n_layers = 6 * (args.layers if args.layers is not None else 24) if cfg == 4 else None
@@ -571,7 +579,7 @@ def main():
     # ---- inputs, resident in HBM ----------------------------------------------------
     t_setup = time.perf_counter()
     layers, host = make_layers(cfg, rank, T, dev, n_sets=n_sets, keep_host=cpu_T is not None, n_layers=n_layers,
-                               clone_encoders=(cfg == 4), path=args.path)
+                               clone_encoders=(cfg == 4), path=args.path, dtype=dt)
     print(f"# {len(layers)} layers ready in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     specs = [L["spec"] for L in layers]
     sizes = step_bytes(specs, [h["D"] for h in host], T, es)
@@ -597,8 +605,8 @@ def main():
             "unit": "GB/s",
             "frac": round(per[dom]["gbps"] / HBM_PEAK_GBPS, 4),
             # the counter summaries were taken on the default workload only
-            "traffic": measured_traffic(dom) if (cfg, rank, T, args.rank_grads, n_sets) == (2, 30, 16384, False, 2)
-            else None,
+            "traffic": measured_traffic(dom)
+            if (cfg, rank, T, args.rank_grads, n_sets, dt) == (2, 30, 16384, False, 2, "bf16") else None,
             "avg_launch_us": round(per[dom]["avg_us"], 2),
             "algorithmic_bytes_per_launch": round(per[dom]["bytes"] / per[dom]["launches"]),
         }
@@ -632,8 +640,8 @@ def main():
     if cpu_T is not None:
         cpu = cpu_baseline(host[:6], cpu_T)
 
-    wl = {1: "one encoder's TT-linear set, fp32", 2: "one encoder's TT-linear set, bf16",
-          4: "CodeBERT-large-sized encoder stack, bf16"}[cfg]
+    wl = {1: "one encoder's TT-linear set", 2: "one encoder's TT-linear set",
+          4: "CodeBERT-large-sized encoder stack"}[cfg] + f", {dt}"
     shapes = "4x 768->768, 768->3072, 3072->768" if cfg != 4 else \
         f"{len(layers) // 6}x (4x 1024->1024, 1024->4096, 4096->1024)"
     out = {

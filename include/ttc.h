@@ -67,7 +67,13 @@ typedef enum {
   TTC_ERR_HIP = 8          /* a HIP runtime call failed                            */
 } ttc_status;
 
-typedef enum { TTC_F32 = 0, TTC_BF16 = 1 } ttc_dtype;
+/* Activation dtypes.  TTC_FP8 (FP8 mixed precision; CoMERA poster page,
+ * tables and figures on FP8-mix products and FP8/FP32 training): x, y, dy, dx
+ * stored as OCP e4m3 bytes (largest finite 448), every MFMA operand of the
+ * merged order in e4m3 (the packed rank-side operands and the kept
+ * intermediates too), fp32 accumulation, cores, D and dG in fp32; ranks up
+ * to 64 on the merged order (the rank tile is padded to 64). */
+typedef enum { TTC_F32 = 0, TTC_BF16 = 1, TTC_FP8 = 2 } ttc_dtype;
 
 typedef enum {
   TTC_PATH_AUTO = 0,       /* planner picks                                        */

@@ -7,6 +7,8 @@ from .workloads import (  # noqa: F401
     LayerSpec,
     TTMSpec,
     bf16_bits,
+    fp8_bits,
+    fp8_decode,
     bf16_round,
     config_layers,
     make_tt_layer,

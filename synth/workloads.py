@@ -17,8 +17,10 @@ Readings of the workload descriptions:
   reconstructed W has entry variance 1 / N_in given the drawn D:
   E[W_ij^2] = sigma^(2d) * prod_k sum_a D_k[a]^2;
 * each layer gets its own independent x and dY, N(0, 1);
-* bf16 values are the fp32 draws rounded to nearest-even; cores and D stay
-  fp32 (master weights), only activations are stored in bf16;
+* bf16 values are the fp32 draws rounded to nearest-even; fp8 values the
+  fp32 draws rounded to the nearest OCP e4m3 value (ties to the even code);
+  cores and D stay fp32 (master weights), only activations are stored in
+  bf16 or fp8;
 * TTM ids follow a finite Zipf law P(k) ~ (k+1)^-s over the vocabulary,
   sampled by inverse CDF from seeded uniforms.
 """
@@ -52,6 +54,38 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
         bias = np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1))
         out[s:s + step] = (c + bias) >> np.uint32(16)
     return out.reshape(np.shape(a))
+
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the 127 non-negative finite OCP e4m3 codes 0x00..0x7E, ascending
+    (4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal;
+    0x7F is NaN, so 448 is the largest finite value)."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10))
+
+
+_E4M3 = _e4m3_table()
+
+
+def fp8_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP e4m3 codes (uint8), round to nearest, ties to the even code
+    (even mantissa), magnitudes above 448 saturated to 448."""
+    x = np.asarray(a, dtype=np.float64)
+    ax = np.minimum(np.abs(x), _E4M3[-1])
+    hi = np.clip(np.searchsorted(_E4M3, ax), 1, 126)
+    lo = hi - 1
+    dlo, dhi = ax - _E4M3[lo], _E4M3[hi] - ax
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(ax == _E4M3[hi], hi, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def fp8_decode(bits: np.ndarray) -> np.ndarray:
+    """OCP e4m3 codes -> fp32 values (no NaN codes are produced by fp8_bits)."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    v = _E4M3[np.minimum(b & 0x7F, 126)]
+    return np.where(b & 0x80, -v, v).astype(np.float32)
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
@@ -176,6 +210,11 @@ def make_tt_layer(config: int, layer: int, spec: LayerSpec, T: int, zero_frac: f
             out["dy_bits"] = bf16_bits(dy)
             x = (out["x_bits"].astype(np.uint32) << np.uint32(16)).view(np.float32)
             dy = (out["dy_bits"].astype(np.uint32) << np.uint32(16)).view(np.float32)
+        elif dtype == "fp8":
+            out["x_bits"] = fp8_bits(x)
+            out["dy_bits"] = fp8_bits(dy)
+            x = fp8_decode(out["x_bits"])
+            dy = fp8_decode(out["dy_bits"])
         out["x"], out["dy"] = x, dy
     return out
 

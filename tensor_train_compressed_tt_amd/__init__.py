@@ -16,7 +16,7 @@ from typing import Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libttc.so")
 
-TTC_F32, TTC_BF16 = 0, 1
+TTC_F32, TTC_BF16, TTC_FP8 = 0, 1, 2
 TTC_PATH_AUTO, TTC_PATH_MERGED, TTC_PATH_SEQUENTIAL, TTC_PATH_DENSE = 0, 1, 2, 3
 MAX_HALF_MODES = 8
 TTM_MAX_MODES = 8

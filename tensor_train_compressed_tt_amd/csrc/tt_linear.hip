@@ -329,6 +329,11 @@ __device__ __forceinline__ void store4<bf16_t>(unsigned short* p, f32x4 v, int v
   }
 }
 template <>
+__device__ __forceinline__ void store4<fp8_t>(unsigned char* p, f32x4 v, int valid, bool vec) {
+  (void)vec;
+  for (int e = 0; e < 4 && e < valid; ++e) p[e] = Mma<fp8_t>::from_f32(v[e]);
+}
+template <>
 __device__ __forceinline__ void store4<float>(float* p, f32x4 v, int valid, bool vec) {
   if (vec && valid >= 4) {
     *reinterpret_cast<f32x4*>(p) = v;
@@ -698,6 +703,8 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
         if constexpr (sizeof(E) == 2) {
           const uint2 pk = {f32x2_to_bf16x2(a2[0], a2[1]), f32x2_to_bf16x2(a2[2], a2[3])};
           *reinterpret_cast<uint2*>(d) = pk;
+        } else if constexpr (sizeof(E) == 1) {
+          *reinterpret_cast<unsigned*>(d) = f32x4_to_fp8x4(a2[0], a2[1], a2[2], a2[3]);
         } else {
 #pragma unroll
           for (int vv = 0; vv < 4; ++vv) d[vv] = (E)Mma<T>::from_f32(a2[vv]);
@@ -1173,6 +1180,9 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
               const uint2 pk = {f32x2_to_bf16x2(accX[ct][u][0], accX[ct][u][1]),
                                 f32x2_to_bf16x2(accX[ct][u][2], accX[ct][u][3])};
               *reinterpret_cast<uint2*>(d) = pk;
+            } else if constexpr (sizeof(E) == 1) {
+              *reinterpret_cast<unsigned*>(d) =
+                  f32x4_to_fp8x4(accX[ct][u][0], accX[ct][u][1], accX[ct][u][2], accX[ct][u][3]);
             } else {
               *reinterpret_cast<f32x4*>(d) = accX[ct][u];
             }
@@ -1980,7 +1990,7 @@ static bool fwd_vec(const StreamJob& j) {
 }
 template <typename T, int NR>
 static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, hipStream_t st) {
-  if constexpr (sizeof(typename Elem<T>::type) == 2 && NR <= 4) {
+  if constexpr (sizeof(typename Elem<T>::type) <= 2 && NR <= 4) {
     if (wide) {
       if (vec) launch_fwd_v<T, NR, true, 4, 8>(jobs, n, st);
       else launch_fwd_v<T, NR, false, 4, 8>(jobs, n, st);
@@ -2110,12 +2120,44 @@ static bool nr_supported(int NR) { return NR == 2 || NR == 4 || NR == 6 || NR ==
 // forward, the tile width) go into common launches of up to kMaxStream
 // layers, in list order; the others get launches of their own.  The caller
 // has checked nr_supported for every layer.
+template <bool FWD, typename T>
+static void launch_stream_group(const StreamJob* js, int m, int NR, bool vec, bool wide, hipStream_t st) {
+  if constexpr (sizeof(typename Elem<T>::type) == 1) {
+    // fp8: the plan pads the rank tile to 64 and takes ranks up to 64
+    if constexpr (FWD)
+      launch_fwd_group<T, 4>(js, m, vec, wide, st);
+    else
+      launch_bwd_group<T, 4>(js, m, vec, st);
+    return;
+  }
+  if constexpr (FWD) {
+    switch (NR) {
+      case 2: launch_fwd_group<T, 2>(js, m, vec, wide, st); break;
+      case 4: launch_fwd_group<T, 4>(js, m, vec, wide, st); break;
+      case 6: launch_fwd_group<T, 6>(js, m, vec, wide, st); break;
+      case 8: launch_fwd_group<T, 8>(js, m, vec, wide, st); break;
+    }
+  } else {
+    switch (NR) {
+      case 2: launch_bwd_group<T, 2>(js, m, vec, st); break;
+      case 4: launch_bwd_group<T, 4>(js, m, vec, st); break;
+      case 6: launch_bwd_group<T, 6>(js, m, vec, st); break;
+      case 8: launch_bwd_group<T, 8>(js, m, vec, st); break;
+    }
+  }
+}
+
 template <bool FWD>
 static void launch_stream_jobs(const StreamJob* jobs, int n, hipStream_t st) {
   auto key = [&](const StreamJob& j) {
     const LinearPlan& P = *j.P;
-    const bool bf = P.act == TTC_BF16;
-    const bool vec = FWD ? (bf ? fwd_vec<bf16_t>(j) : fwd_vec<float>(j)) : (bf ? bwd_vec<bf16_t>(j) : bwd_vec<float>(j));
+    bool vec;
+    if (P.act == TTC_BF16)
+      vec = FWD ? fwd_vec<bf16_t>(j) : bwd_vec<bf16_t>(j);
+    else if (P.act == TTC_FP8)
+      vec = FWD ? fwd_vec<fp8_t>(j) : bwd_vec<fp8_t>(j);
+    else
+      vec = FWD ? fwd_vec<float>(j) : bwd_vec<float>(j);
     const bool wide = FWD && P.ntiles >= TTC_FWD_WIDE_TILES;
     return (P.act << 8) | (P.NR << 2) | ((int)vec << 1) | (int)wide;
   };
@@ -2130,27 +2172,18 @@ static void launch_stream_jobs(const StreamJob* jobs, int n, hipStream_t st) {
         grp.push_back(jobs[j]);
         done[j] = 1;
       }
-    const bool bf = (k >> 8) == TTC_BF16;
+    const int act = k >> 8;
     const int NR = (k >> 2) & 63;
     const bool vec = (k >> 1) & 1, wide = k & 1;
     for (size_t g0 = 0; g0 < grp.size(); g0 += kMaxStream) {
       const int m = (int)std::min<size_t>(kMaxStream, grp.size() - g0);
       const StreamJob* js = grp.data() + g0;
-      if constexpr (FWD) {
-        switch (NR) {
-          case 2: bf ? launch_fwd_group<bf16_t, 2>(js, m, vec, wide, st) : launch_fwd_group<float, 2>(js, m, vec, wide, st); break;
-          case 4: bf ? launch_fwd_group<bf16_t, 4>(js, m, vec, wide, st) : launch_fwd_group<float, 4>(js, m, vec, wide, st); break;
-          case 6: bf ? launch_fwd_group<bf16_t, 6>(js, m, vec, wide, st) : launch_fwd_group<float, 6>(js, m, vec, wide, st); break;
-          case 8: bf ? launch_fwd_group<bf16_t, 8>(js, m, vec, wide, st) : launch_fwd_group<float, 8>(js, m, vec, wide, st); break;
-        }
-      } else {
-        switch (NR) {
-          case 2: bf ? launch_bwd_group<bf16_t, 2>(js, m, vec, st) : launch_bwd_group<float, 2>(js, m, vec, st); break;
-          case 4: bf ? launch_bwd_group<bf16_t, 4>(js, m, vec, st) : launch_bwd_group<float, 4>(js, m, vec, st); break;
-          case 6: bf ? launch_bwd_group<bf16_t, 6>(js, m, vec, st) : launch_bwd_group<float, 6>(js, m, vec, st); break;
-          case 8: bf ? launch_bwd_group<bf16_t, 8>(js, m, vec, st) : launch_bwd_group<float, 8>(js, m, vec, st); break;
-        }
-      }
+      if (act == TTC_BF16)
+        launch_stream_group<FWD, bf16_t>(js, m, NR, vec, wide, st);
+      else if (act == TTC_FP8)
+        launch_stream_group<FWD, fp8_t>(js, m, NR, vec, wide, st);
+      else
+        launch_stream_group<FWD, float>(js, m, NR, vec, wide, st);
     }
   }
 }
@@ -2193,6 +2226,9 @@ static void launch_seq_fwd(const LinearPlan& P, const SeqArgs& a, hipStream_t st
   if (P.act == TTC_BF16) {
     seq_allow_lds<0>((const void*)k_seq_fwd<bf16_t>);
     TTC_LAUNCH(k_seq_fwd<bf16_t>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_fwd, st, a);
+  } else if (P.act == TTC_FP8) {
+    seq_allow_lds<4>((const void*)k_seq_fwd<fp8_t>);
+    TTC_LAUNCH(k_seq_fwd<fp8_t>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_fwd, st, a);
   } else {
     seq_allow_lds<1>((const void*)k_seq_fwd<float>);
     TTC_LAUNCH(k_seq_fwd<float>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_fwd, st, a);
@@ -2204,6 +2240,9 @@ static void launch_seq_bwd(const LinearPlan& P, const SeqArgs& a, hipStream_t st
   if (P.act == TTC_BF16) {
     seq_allow_lds<2>((const void*)k_seq_bwd<bf16_t>);
     TTC_LAUNCH(k_seq_bwd<bf16_t>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_bwd, st, a);
+  } else if (P.act == TTC_FP8) {
+    seq_allow_lds<5>((const void*)k_seq_bwd<fp8_t>);
+    TTC_LAUNCH(k_seq_bwd<fp8_t>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_bwd, st, a);
   } else {
     seq_allow_lds<3>((const void*)k_seq_bwd<float>);
     TTC_LAUNCH(k_seq_bwd<float>, dim3((unsigned)P.T), dim3(kSeqThreads), P.seq_lds_bwd, st, a);
@@ -2312,18 +2351,19 @@ static MergeLayer merge_layer(const LayerJob& j) {
 
 // Merge of n layers: one launch per activation dtype and kMaxMerge layers.
 static void launch_merge_batch(const LayerJob* jobs, int n, hipStream_t s) {
-  for (int act = 0; act < 2; ++act) {
-    const int want = act == 0 ? TTC_BF16 : TTC_F32;
+  for (int act = 0; act < 3; ++act) {
+    const int want = act == 0 ? TTC_BF16 : (act == 1 ? TTC_F32 : TTC_FP8);
     MergeBatch mb;
     memset(&mb, 0, sizeof(mb));
     auto flush = [&]() {
       if (mb.n == 0) return;
       TraceScope ts("merge", s);
-      if (want == TTC_BF16) {
+      if (want == TTC_BF16)
         TTC_LAUNCH(k_merge<bf16_t>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
-      } else {
+      else if (want == TTC_FP8)
+        TTC_LAUNCH(k_merge<fp8_t>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
+      else
         TTC_LAUNCH(k_merge<float>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
-      }
       memset(&mb, 0, sizeof(mb));
     };
     for (int i = 0; i < n; ++i) {

@@ -28,7 +28,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   const int p = desc->p, q = desc->q;
   if (p < 1 || q < 1 || p > TTC_MAX_HALF_MODES || q > TTC_MAX_HALF_MODES) return TTC_ERR_SHAPE;
   if (T < 0 || T > (int64_t(1) << 31) - 1) return TTC_ERR_SHAPE;
-  if (desc->act_dtype != TTC_F32 && desc->act_dtype != TTC_BF16) return TTC_ERR_DTYPE;
+  if (desc->act_dtype != TTC_F32 && desc->act_dtype != TTC_BF16 && desc->act_dtype != TTC_FP8) return TTC_ERR_DTYPE;
   if (desc->in_first != 0 && desc->in_first != 1) return TTC_ERR_SHAPE;
   int in_first = desc->in_first;
   if (desc->path < TTC_PATH_AUTO || desc->path > TTC_PATH_DENSE) return TTC_ERR_UNSUPPORTED;
@@ -109,12 +109,15 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->s = in_first ? q : p;
   if (desc->split != -1 && desc->split != P->s) return TTC_ERR_UNSUPPORTED;
   P->rs = P->ranks[P->s];
-  P->Rpad = ((P->rs + 31) / 32) * 32;
+  // rank tile: a multiple of the MFMA k-step of the rank-side products (32
+  // k-values for fp32 and bf16, 64 for fp8)
+  const int rstep = desc->act_dtype == TTC_FP8 ? 64 : 32;
+  P->Rpad = ((P->rs + rstep - 1) / rstep) * rstep;
   P->NR = P->Rpad / 16;
   P->NL = in_first ? nin : nout;
   P->NRt = in_first ? nout : nin;
   P->T = T;
-  P->es = desc->act_dtype == TTC_BF16 ? 2 : 4;
+  P->es = desc->act_dtype == TTC_BF16 ? 2 : (desc->act_dtype == TTC_FP8 ? 1 : 4);
   // The streaming kernels address their operands through buffer resources of
   // at most 2^31 - 1 bytes with 32-bit offsets: the merged operands
   // (Rpad x N activation elements each) and a 64-token slab of any activation
@@ -232,11 +235,17 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
     double macs[4], bytes[4], usec[4];
     linear_path_costs(*P, macs, bytes);
     linear_path_times(*P, macs, bytes, usec);
+    // the fp8 merged kernels hold one rank tile of 64 (accumulator registers)
+    const bool merged_ok = !(desc->act_dtype == TTC_FP8 && P->Rpad > 64);
     if (desc->path == TTC_PATH_SEQUENTIAL) {
       if (!P->seq_ok) return TTC_ERR_UNSUPPORTED;
       P->path = TTC_PATH_SEQUENTIAL;
     } else if (desc->path == TTC_PATH_MERGED) {
+      if (!merged_ok) return TTC_ERR_UNSUPPORTED;
       P->path = TTC_PATH_MERGED;
+    } else if (!merged_ok) {
+      if (!P->seq_ok) return TTC_ERR_UNSUPPORTED;
+      P->path = TTC_PATH_SEQUENTIAL;
     } else {
       P->path = (P->seq_ok && usec[2] < usec[1]) ? TTC_PATH_SEQUENTIAL : TTC_PATH_MERGED;
     }
@@ -374,7 +383,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
 //       from dW.
 void linear_path_costs(const LinearPlan& P, double macs[4], double bytes[4]) {
   const double T = double(P.T);
-  const double es = P.act == TTC_BF16 ? 2.0 : 4.0;
+  const double es = P.act == TTC_BF16 ? 2.0 : (P.act == TTC_FP8 ? 1.0 : 4.0);
   const int d = P.d, s = P.s;
   const double r = P.rs;
   // chain products of the two halves (prefix rows built left to right,

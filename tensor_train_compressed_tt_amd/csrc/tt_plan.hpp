@@ -24,7 +24,9 @@ constexpr int slab_cols(int act_bytes) { return 256 / act_bytes; }
 // for: bounded so that the per-lane accumulators stay within 64 registers
 // and the work-group's LDS within ~80 KB (two work-groups per CU).
 constexpr int bwd_max_slabs(int act_bytes, int NR) {
-  return (2048 / (NR * act_bytes)) / slab_cols(act_bytes) < 1
+  // one-byte activations: a 256-column slab already needs 4 column tiles per
+  // wave, i.e. 64 accumulator registers at a rank tile of 64
+  return act_bytes == 1 ? 1 : (2048 / (NR * act_bytes)) / slab_cols(act_bytes) < 1
              ? 1
              : ((2048 / (NR * act_bytes)) / slab_cols(act_bytes) > 8 ? 8
                                                                      : (2048 / (NR * act_bytes)) / slab_cols(act_bytes));

@@ -16,6 +16,14 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 struct bf16_t {
   unsigned short bits;
 };
+// fp8 activations: OCP e4m3 (4 exponent bits, bias 7, 3 mantissa bits,
+// largest finite 448), the format of gfx950's fp8 conversions and MFMAs,
+// carried as raw bytes.
+struct fp8_t {
+  unsigned char bits;
+};
+typedef unsigned char u8x16 __attribute__((ext_vector_type(16)));
+typedef long i64x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
   return __uint_as_float(((unsigned int)b) << 16);
@@ -73,10 +81,39 @@ struct Mma<float> {
   __device__ __forceinline__ static float from_f32(float f) { return f; }
 };
 
+// fp8: a k-step is 4 groups x 16 bytes = 64 k-values; the 16 bytes of a lane
+// feed two 16x16x32 fp8 MFMAs (elements 0..7, then 8..15), the same split
+// for both operands, so the dot products are those of the k-step.
+template <>
+struct Mma<fp8_t> {
+  static constexpr int EPV = 16;
+  static constexpr int KSTEP = 64;
+  typedef u8x16 frag;
+  __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    const i64x2 a2 = __builtin_bit_cast(i64x2, a), b2 = __builtin_bit_cast(i64x2, b);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], c, 0, 0, 0);
+    return c;
+  }
+  __device__ __forceinline__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
+  // round to nearest even (hardware conversion); values beyond the format's
+  // range are not expected (activations and operands are O(1))
+  __device__ __forceinline__ static unsigned char from_f32(float f) {
+    return (unsigned char)(__builtin_amdgcn_cvt_pk_fp8_f32(f, f, 0, false) & 0xff);
+  }
+};
+
+// four values -> four e4m3 bytes (little-endian order), round to nearest even
+__device__ __forceinline__ unsigned f32x4_to_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // storage element of an activation type
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> { typedef unsigned short type; };
 template <> struct Elem<float> { typedef float type; };
+template <> struct Elem<fp8_t> { typedef unsigned char type; };
 
 template <typename T>
 __device__ __forceinline__ float elem_to_f32(typename Elem<T>::type v);
@@ -84,6 +121,8 @@ template <>
 __device__ __forceinline__ float elem_to_f32<bf16_t>(unsigned short v) { return bf16_to_f32(v); }
 template <>
 __device__ __forceinline__ float elem_to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float elem_to_f32<fp8_t>(unsigned char v) { return __builtin_amdgcn_cvt_f32_fp8((int)v, 0); }
 
 // Load the 16-byte group of row `row` starting at column `col` of a row-major
 // matrix (leading dimension ld elements).  Elements outside [0,nrows) x
@@ -161,6 +200,9 @@ __device__ __forceinline__ typename Mma<T>::frag buf_frag_last(rsrc_t r, uint32_
 // dropped, so guarded stores need no branch either.
 __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, unsigned short v) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, unsigned char v) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, 0);
 }
 __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);

@@ -11,6 +11,7 @@ import torch
 from . import (
     TTC_BF16,
     TTC_F32,
+    TTC_FP8,
     TTC_FLAG_PREPARED,
     TTC_PATH_AUTO,
     make_linear_desc,
@@ -34,7 +35,7 @@ from . import (
     ttm_embed_workspace,
 )
 
-_ACT = {torch.float32: TTC_F32, torch.bfloat16: TTC_BF16}
+_ACT = {torch.float32: TTC_F32, torch.bfloat16: TTC_BF16, torch.float8_e4m3fn: TTC_FP8}
 
 
 def _stream() -> int:

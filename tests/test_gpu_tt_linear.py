@@ -18,7 +18,7 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 0.15}
 
 
 def _ttc():
@@ -42,6 +42,9 @@ def _to_dev(layer, dtype):
     if dtype == "bf16":
         x = torch.from_numpy(layer["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
         dy = torch.from_numpy(layer["dy_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    elif dtype == "fp8":
+        x = torch.from_numpy(layer["x_bits"]).to(dev).view(torch.float8_e4m3fn)
+        dy = torch.from_numpy(layer["dy_bits"]).to(dev).view(torch.float8_e4m3fn)
     else:
         x = torch.from_numpy(layer["x"]).to(dev)
         dy = torch.from_numpy(layer["dy"]).to(dev)
@@ -53,7 +56,7 @@ MERGED, SEQUENTIAL = 1, 2  # TTC_PATH_MERGED, TTC_PATH_SEQUENTIAL
 
 def _run(spec, layer, dtype, want_dx=True, path=MERGED):
     ttc = _ttc()
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "f32": torch.float32}[dtype]
     mod = ttc.TTLinear(spec.out_modes, spec.in_modes, spec.ranks, tdt, spec.in_first, path, spec.chain_perm)
     cores, D, x, dy = _to_dev(layer, dtype)
     y, saved = mod.forward(x, cores, D)
