@@ -162,10 +162,12 @@ def _blas_info():
     return f"{p.get('internal_api', '?')} {p.get('version', '')}".strip(), int(p.get("num_threads", 1))
 
 
-def cpu_baseline(host, T_cpu):
+def cpu_baseline(host, T_cpu, min_s=10.0, max_reps=64):
     """The fp64 oracle, as it stands, on the first T_cpu tokens of every given
-    layer; also the time of the same calls on 0 tokens (the work that does not
-    depend on the token count: weight reconstruction, core gradients)."""
+    layer, repeated until about min_s seconds of CPU work have run (the mean
+    over the repetitions is reported); also the time of the same calls on 0
+    tokens (the work that does not depend on the token count: weight
+    reconstruction, core gradients)."""
     import numpy as np
 
     import oracle
@@ -181,13 +183,17 @@ def cpu_baseline(host, T_cpu):
         return time.perf_counter() - t0
 
     t_fixed = run(0)
-    dt = run(T_cpu)
+    times = [run(T_cpu)]
+    while sum(times) < min_s and len(times) < max_reps:
+        times.append(run(T_cpu))
+    dt = sum(times) / len(times)
     blas, threads = _blas_info()
     return {"value": round(T_cpu / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd of {len(host)} TT-linear layers on the first {T_cpu} tokens "
-                      f"({dt:.1f} s wall; the same calls on 0 tokens take {t_fixed:.2f} s)",
+            "sample": f"fp64 oracle fwd+bwd of {len(host)} TT-linear layers on the first {T_cpu} tokens, "
+                      f"{len(times)} repetitions ({sum(times):.1f} s wall, {dt:.2f} s each; the same calls on "
+                      f"0 tokens take {t_fixed:.2f} s)",
             "blas": blas, "blas_threads": threads, "affinity_cores": len(os.sched_getaffinity(0)),
-            "token_independent_s": round(t_fixed, 3), "wall_s": round(dt, 3)}
+            "token_independent_s": round(t_fixed, 3), "wall_s": round(dt, 3), "repetitions": len(times)}
 
 
 # ---- the step -------------------------------------------------------------------------
