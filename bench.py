@@ -67,6 +67,9 @@ def parse(argv=None):
                     help="steps per captured graph (2 needs an even --steps; otherwise 1)")
     ap.add_argument("--merge-side", action="store_true",
                     help="run the merges on the side stream and the embedding lookup on the main one")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="merge only the first forward group's layers before it (the others beside it) and run "
+                         "each backward group's core-gradient tail beside the next group's passes")
     ap.add_argument("--no-qkv-batch", action="store_true",
                     help="one launch per layer for the Q, K and V projections instead of one batched launch")
     ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "fp8"],
@@ -205,6 +208,7 @@ class StepOptions:
     index_ahead: bool = True      # embedding index built one step ahead, beside the step
     merge_side: bool = False      # merges on the side stream, lookup on the main one
     rank_grads: bool = False      # early-stage gradients after the core gradients
+    pipeline: bool = False        # later layers' merges and earlier layers' gradient tails beside the passes
 
 
 PATHS = {"auto": 0, "merged": 1, "sequential": 2}
@@ -329,6 +333,11 @@ def make_step(layers, T, ttm=None, opts=StepOptions()):
     fwd_groups, bwd_groups = launch_groups(len(layers), opts.qkv_batch and not opts.single_stream)
     mods = [L["mod"] for L in layers]
     col = lambda k: [L[k] for L in layers]
+    pick = lambda k, idx: [layers[i][k] for i in idx]
+    every = [i for g in fwd_groups for i in g]
+    # merged on the main stream before the first forward; the others beside it
+    first = list(fwd_groups[0]) if opts.pipeline else every
+    rest = [i for i in every if i not in first]
     ahead = ttm is not None and opts.index_ahead and not opts.single_stream
     side = torch.cuda.Stream()  # default priority
 
@@ -372,11 +381,17 @@ def make_step(layers, T, ttm=None, opts=StepOptions()):
                                     [L["cores"] for L in Ls], [L["D"] for L in Ls], [L["saved"] for L in Ls],
                                     [L["scratch"] for L in Ls], [L["dx"] for L in Ls])
 
-    def cores_tail():
-        ttc.backward_cores_batch(mods[::-1], T, col("cores")[::-1], col("D")[::-1], col("saved")[::-1],
-                                 col("scratch")[::-1], col("dG")[::-1])
+    def cores_tail(idx):
+        ttc.backward_cores_batch([mods[i] for i in idx], T, pick("cores", idx), pick("D", idx), pick("saved", idx),
+                                 pick("scratch", idx), pick("dG", idx))
+
+    def rank_grads():
         if opts.rank_grads:
             ttc.rank_grads_batch(mods, col("cores"), col("D"), col("dG"), col("dD"), RG_GAMMA, RG_BETA)
+
+    def merge(idx):
+        if idx:
+            ttc.prepare_batch([mods[i] for i in idx], T, pick("cores", idx), pick("D", idx), pick("saved", idx))
 
     def step_single(ph):
         s = ph % n_sets
@@ -386,52 +401,70 @@ def make_step(layers, T, ttm=None, opts=StepOptions()):
         for L in reversed(layers):
             L["mod"].backward(L["x"][s], L["dy"][s], L["cores"], L["D"], L["saved"], dx=L["dx"], dG=L["dG"],
                               scratch=L["scratch"])
-        if opts.rank_grads:
-            ttc.rank_grads_batch(mods, col("cores"), col("D"), col("dG"), col("dD"), RG_GAMMA, RG_BETA)
+        rank_grads()
         ttm_bwd(ph)
 
     def step_overlap(ph):
-        # The merges depend only on the cores and D, the core-gradient tails
-        # produce only dG; each is one batched call for all layers.  The main
-        # stream carries the merges and then the dependent chain of streaming
-        # passes (forward over the layers, dX backward through them in reverse
-        # order, then the embedding's backward).  The side stream carries the
-        # embedding lookup beside the merges (the forwards wait for it), the
-        # next batch's index beside the forwards, and the tails after the last
-        # dX pass, beside the embedding's backward, so no side-stream work sits
-        # between two streaming passes.  With the index built in the step
-        # (no index ahead) the lookup is the longer of the two and runs on the
-        # main stream, the merges beside it.
+        # Merges depend only on the cores and D, the core-gradient tails
+        # produce only dG.  The main stream carries the merges and then the
+        # dependent chain of streaming passes (forward over the layers, dX
+        # backward through them in reverse order, then the embedding's
+        # backward).  The side stream carries the embedding lookup beside the
+        # merges (the forwards wait for it), the next batch's index beside the
+        # forwards, and the core-gradient tails after the last dX pass, beside
+        # the embedding's backward.  With the index built in the step (no index
+        # ahead) the lookup is the longer of the two and runs on the main
+        # stream, the merges beside it.  Pipelined (an option, slower on
+        # MI355X: the streaming passes place one work-group per CU and lose
+        # whole CUs to the latency-bound tails beside them), only the first
+        # forward group's layers are merged on the main stream, the others
+        # beside that group's forward, and each backward group's tail runs as
+        # soon as its data pass is done, beside the next group's passes.
         s = ph % n_sets
         main = torch.cuda.current_stream()
         side.wait_stream(main)
+        merged = torch.cuda.Event()
         if ttm is None:
-            ttc.prepare_batch(mods, T, col("cores"), col("D"), col("saved"))
+            merge(first)
+            with torch.cuda.stream(side):
+                merge(rest)
+                merged.record(side)
         elif ahead and not opts.merge_side:
             looked = torch.cuda.Event()
             with torch.cuda.stream(side):
                 ttm_fwd(ph)
                 looked.record(side)
+                merge(rest)
+                merged.record(side)
                 ttm_index_next(ph)
-            ttc.prepare_batch(mods, T, col("cores"), col("D"), col("saved"))
+            merge(first)
             main.wait_event(looked)
         else:
-            merged = torch.cuda.Event()
             with torch.cuda.stream(side):
-                ttc.prepare_batch(mods, T, col("cores"), col("D"), col("saved"))
+                merge(every)
                 merged.record(side)
                 if ahead:
                     ttm_index_next(ph)
             ttm_fwd(ph)
             main.wait_event(merged)
+        waited = False
         for g in fwd_groups:
+            if not waited and any(i in rest for i in g):
+                main.wait_event(merged)
+                waited = True
             fwd_group(g, s)
         for g in bwd_groups:
             bwd_group(g, s)
+            if opts.pipeline:
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    cores_tail(g)
         side.wait_stream(main)
         ttm_bwd(ph)
         with torch.cuda.stream(side):
-            cores_tail()
+            if not opts.pipeline:
+                cores_tail([i for g in bwd_groups for i in g])
+            rank_grads()
         main.wait_stream(side)
 
     step = step_single if opts.single_stream else step_overlap
@@ -590,7 +623,8 @@ def main():
     specs = [L["spec"] for L in layers]
     sizes = step_bytes(specs, [h["D"] for h in host], T, es)
     opts = StepOptions(single_stream=args.single_stream, qkv_batch=not args.no_qkv_batch,
-                       index_ahead=not args.no_index_ahead, merge_side=args.merge_side, rank_grads=args.rank_grads)
+                       index_ahead=not args.no_index_ahead, merge_side=args.merge_side, rank_grads=args.rank_grads,
+                       pipeline=args.pipeline)
     tt_bytes = sum(s["fwd"] + s["bwd_dy"] + s["bwd_dx"] for s in sizes)
 
     # ---- headline: the TT-linear layers alone -----------------------------------------
@@ -677,6 +711,7 @@ def main():
             "qkv_batched": not (args.no_qkv_batch or args.single_stream),
             "rank_grads": bool(args.rank_grads),
             "streams": 1 if args.single_stream else 2,
+            "pipelined_merges_and_tails": bool(args.pipeline and not args.single_stream),
             **launch,
         },
         "hbm_gbps_step": round(step_gbps, 1),

@@ -342,6 +342,9 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v, int valid, bool
   }
 }
 
+#ifndef TTC_SLAB_PAD
+#define TTC_SLAB_PAD 16  // bytes of padding per LDS slab row
+#endif
 // Geometry shared by the two backward passes for activation type T and NR
 // rank tiles of 16.
 template <typename T, int NR>
@@ -352,7 +355,7 @@ struct Bwd {
   static constexpr int KSTEP = Mma<T>::KSTEP;
   static constexpr int Rpad = 16 * NR;
   static constexpr int SW = 256 / ES;        // slab columns
-  static constexpr int SLD = SW + 16 / ES;   // slab row stride (elements), 16-byte pad
+  static constexpr int SLD = SW + TTC_SLAB_PAD / ES;  // slab row stride (elements), padded
   static constexpr int CTW = SW / 64;        // 16-column tiles per wave per slab
   static constexpr int ZLD = 64 + 16 / ES;   // row stride of a rank-major 64-token tile
   static constexpr int RLD = Rpad + 16 / ES; // row stride of a token-major rank tile
@@ -911,7 +914,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
             frag fb[B::CTW];
 #pragma unroll
             for (int ct = 0; ct < B::CTW; ++ct)
-              fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
+              fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
               const frag fa = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
@@ -1133,7 +1136,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
             frag fb[B::CTW];
 #pragma unroll
             for (int ct = 0; ct < B::CTW; ++ct)
-              fb[ct] = lds_col_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16 + c, B::SLD);
+              fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
               const frag fa = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);

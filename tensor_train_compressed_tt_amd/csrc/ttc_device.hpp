@@ -232,6 +232,36 @@ __device__ __forceinline__ typename Mma<T>::frag lds_col_frag(const typename Ele
   return f;
 }
 
+// Column fragments of a 16-column tile of a row-major LDS tile, one per lane:
+// lane 16g + i gets EPV consecutive rows, from row EPV*g on, of column i.  `p`
+// is the tile's first column in its first row (row 0 of block g = 0; the
+// caller adds EPV*g rows).
+//
+// bf16 uses gfx950's transposing LDS read (ds_read_b64_tr_b16).  Inside each
+// block of 16 lanes it hands lane i, as its result j (j = 0..3), element
+// i mod 4 of the 64-bit word read by lane 4j + i/4.  So lane 4j + q of the
+// block reads row j at columns 4q..4q+3, and lane i ends up with rows 0..3
+// of column i; a second read four rows further down gives rows 4..7.  Two
+// LDS reads per fragment instead of eight 16-bit reads and the packing.
+#ifndef TTC_LDS_TR
+#define TTC_LDS_TR 1
+#endif
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag lds_colT_frag(const typename Elem<T>::type* p, int ld) {
+#if TTC_LDS_TR
+  if constexpr (sizeof(typename Elem<T>::type) == 2) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int i = threadIdx.x & 15;
+    const typename Elem<T>::type* q = p + (i >> 2) * ld + 4 * (i & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)q);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(q + 4 * ld));
+    return __builtin_bit_cast(typename Mma<T>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+#endif
+  return lds_col_frag<T>(p + (threadIdx.x & 15), ld);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Work-group barrier that orders LDS accesses only.  __syncthreads() is a

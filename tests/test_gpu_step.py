@@ -4,7 +4,8 @@ and a ragged tail.
 
 bench.make_layers / make_ttm / make_step build the step: the merges of six
 TT-linear layers, their forwards (Q, K and V in one launch), the backward data
-passes in reverse order and the batched core-gradient tails; with the
+passes in reverse order and the batched core-gradient tails (or, pipelined,
+each backward group's tail beside the next group's passes); with the
 embedding, its lookup of an already indexed id batch and the index of the next
 batch beside them (side stream) and its backward beside the tails.  Two steps
 run, one per input set (the two id batches differ).  The eager steps are
@@ -60,6 +61,7 @@ OPTIONS = {
     "index_in_step": bench.StepOptions(index_ahead=False),
     "merge_side": bench.StepOptions(merge_side=True),
     "qkv_unbatched": bench.StepOptions(qkv_batch=False),
+    "pipeline": bench.StepOptions(pipeline=True),
 }
 
 
