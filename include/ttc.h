@@ -78,7 +78,7 @@ typedef enum { TTC_F32 = 0, TTC_BF16 = 1, TTC_FP8 = 2 } ttc_dtype;
 typedef enum {
   TTC_PATH_AUTO = 0,       /* planner picks                                        */
   TTC_PATH_MERGED = 1,     /* merge each half of the chain, two skinny GEMMs       */
-  TTC_PATH_SEQUENTIAL = 2, /* core-by-core sweep (costed by the planner only)      */
+  TTC_PATH_SEQUENTIAL = 2, /* core-by-core sweep, one work-group per token         */
   TTC_PATH_DENSE = 3       /* materialise W (costed by the planner only)           */
 } ttc_path;
 

@@ -32,9 +32,10 @@ ttc_status ttc_trace_count(int32_t* n);
 
 /*
  * Record i (0-based, in launch order): the kernel's name (static storage, one
- * of "merge_level", "merge", "fwd", "bwd_dy", "dz_sum", "bwd_dx", "reduce", "core", "zero",
- * "ttm_sort", "ttm_lists", "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level",
- * "ttm_reduce") and its duration in
+ * of "merge", "fwd", "bwd_dy", "dz_sum", "bwd_dx", "reduce", "core", "zero",
+ * "rank_grads", "seq_fwd", "seq_bwd", "seq_reduce", "ttm_sort", "ttm_lists",
+ * "ttm_level", "ttm_gather", "ttm_seg", "ttm_bwd_level", "ttm_reduce") and its
+ * duration in
  * milliseconds.  Waits for the record's end event.
  */
 ttc_status ttc_trace_get(int32_t i, const char** name, float* ms);

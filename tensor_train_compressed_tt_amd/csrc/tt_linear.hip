@@ -508,8 +508,14 @@ __device__ __forceinline__ int batch_layer(const StreamBatch<A>& b, unsigned* lo
   return q;
 }
 
+#ifndef TTC_FWD_WIDE_UNR
+#define TTC_FWD_WIDE_UNR 2
+#endif
+#ifndef TTC_FWD_WIDE_WPE
+#define TTC_FWD_WIDE_WPE 1
+#endif
 template <typename T, int NR, bool VEC, int TT, int NW>
-__global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
+__global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   typedef typename Elem<T>::type E;
   unsigned bid;
   const FwdArgs<T>& fa_ = fb.a[batch_layer(fb, &bid)];
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(64 * NW) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   // the wider rank tiles, so that two batches in flight, the accumulators
   // and three batches of B fragments stay within about 128 registers
   constexpr int NT = 64 * NW;                           // threads
-  constexpr int UNR = NW == 8 ? (NR <= 2 ? 2 : 1) : (NR <= 2 ? 4 : 1);
+  constexpr int UNR = NW == 8 ? (NR <= 2 ? TTC_FWD_WIDE_UNR : 1) : (NR <= 2 ? 4 : 1);
   constexpr int KS = Rpad / KSTEP;
   constexpr int UO = kFwdUO(NR, NW);
   constexpr int TPS = NW * UO;                           // output tiles per step (all waves)
@@ -1983,6 +1989,9 @@ static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
 // 2-byte activations up to rank 64: 64-token work-groups of eight waves once
 // there are enough tiles to give every CU one; otherwise 32-token
 // work-groups of four waves.
+#ifndef TTC_FWD_WIDE_TT
+#define TTC_FWD_WIDE_TT 4
+#endif
 #ifndef TTC_FWD_WIDE_TILES
 #define TTC_FWD_WIDE_TILES 256
 #endif
@@ -1995,8 +2004,8 @@ template <typename T, int NR>
 static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, hipStream_t st) {
   if constexpr (sizeof(typename Elem<T>::type) <= 2 && NR <= 4) {
     if (wide) {
-      if (vec) launch_fwd_v<T, NR, true, 4, 8>(jobs, n, st);
-      else launch_fwd_v<T, NR, false, 4, 8>(jobs, n, st);
+      if (vec) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8>(jobs, n, st);
+      else launch_fwd_v<T, NR, false, TTC_FWD_WIDE_TT, 8>(jobs, n, st);
       return;
     }
   }

@@ -188,12 +188,17 @@ template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag buf_frag(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+#ifndef TTC_STREAM_HINTS
+#define TTC_STREAM_HINTS 1
+#endif
+constexpr int kStreamLoadPolicy = TTC_STREAM_HINTS ? 2 : 0;  // nt
 // The same load for the last read of a streamed activation in the step (dY in
 // the dY pass, x in the dX pass): non-temporal, so that the lines need not
 // stay in the caches after this read.
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag buf_frag_last(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(typename Mma<T>::frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+  return __builtin_bit_cast(typename Mma<T>::frag,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStreamLoadPolicy));
 }
 
 // Stores through a buffer resource: a store at an out-of-range offset is
@@ -211,7 +216,7 @@ __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, float v) {
 // read again by the pass that follows, so it carries the non-temporal cache
 // policy bit and does not displace the operands the next kernels re-read
 // from the caches.
-constexpr int kStreamStorePolicy = 2;  // nt
+constexpr int kStreamStorePolicy = TTC_STREAM_HINTS ? 2 : 0;  // nt
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
   typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
   __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{v.x, v.y, v.z, v.w}, r, (int)off, 0, kStreamStorePolicy);
