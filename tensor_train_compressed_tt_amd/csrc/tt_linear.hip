@@ -421,15 +421,16 @@ __device__ __forceinline__ void slab_fetch_b(typename Mma<T>::frag* r, rsrc_t sr
   }
 }
 
+// Rank columns at or past r_eff are zero in the tile and are not read.
 template <typename T, int NR>
-__device__ __forceinline__ void rank_fetch_b(typename Mma<T>::frag* r, rsrc_t src, int row0, bool live) {
+__device__ __forceinline__ void rank_fetch_b(typename Mma<T>::frag* r, rsrc_t src, int row0, bool live, int reff) {
   typedef Bwd<T, NR> B;
 #pragma unroll
   for (int q = 0; q < B::ZPER; ++q) {
     const int gi = threadIdx.x + 256 * q;
     const int row = gi / B::ZG, part = gi % B::ZG;
     const uint32_t o = (uint32_t)(((row0 + row) * B::Rpad + part * B::EPV) * B::ES);
-    r[q] = buf_frag<T>(src, (live & (gi < 64 * B::ZG)) ? o : kNoOff);
+    r[q] = buf_frag<T>(src, (live & (gi < 64 * B::ZG) & (part * B::EPV < reff)) ? o : kNoOff);
   }
 }
 
@@ -490,6 +491,7 @@ struct FwdArgs {
   const typename Elem<T>::type* Bc;
   typename Elem<T>::type* Z;
   typename Elem<T>::type* y;
+  const int* meta;  // live-slice map of the split link (r_eff)
   int64_t T_, N_in, N_out;
   int vin, vout;
   int cg_n;  // column groups per token tile (>= 1, at most the tile's output steps)
@@ -575,6 +577,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   const rsrc_t rb = make_rsrc(Bc, N_out * Rpad * (int64_t)sizeof(E));
   const rsrc_t rz = make_rsrc(Z + t0 * Rpad, nrows * Rpad * (int64_t)sizeof(E));
   const rsrc_t ry = make_rsrc(y + t0 * N_out, nrows * N_out * (int64_t)sizeof(E));
+  // rows of A and columns of B at or past the live rank r_eff are zero (the
+  // merge compacts the live slices of the split link to the front)
+  const int reff = fa_.meta[kMetaReff];
   const int not_ = (int)((N_out + 15) / 16);
   frag fo0[UO][KS], fo1[UO][KS], fo2[UO][KS];
   auto fetch_b = [&](frag (&f)[UO][KS], int ob, bool live) {
@@ -585,7 +590,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
         const int64_t row = (int64_t)(ob + NW * uo) * 16 + c;
         if constexpr (VEC) {
           const uint32_t o = (uint32_t)((row * Rpad + ks * KSTEP + g * EPV) * (int64_t)sizeof(E));
-          f[uo][ks] = buf_frag<T>(rb, (live & (row < N_out)) ? o : kNoOff);
+          // ranks at or past r_eff are zero in B: not read (a load at kNoOff is zero)
+          f[uo][ks] = buf_frag<T>(rb, (live & (row < N_out) & (ks * KSTEP + g * EPV < reff)) ? o : kNoOff);
         } else {
           f[uo][ks] = load_frag_v<T>(Bc, row, N_out, ks * KSTEP + g * EPV, Rpad, Rpad);
         }
@@ -621,7 +627,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
           xa[u][tt] = buf_frag<T>(rx, ok ? (uint32_t)(((16 * tt + c) * N_in + col) * (int64_t)sizeof(E)) : kNoOff);
 #pragma unroll
         for (int n = 0; n < NR; ++n)
-          xb[u][n] = buf_frag<T>(ra, ok ? (uint32_t)(((16 * n + c) * N_in + col) * (int64_t)sizeof(E)) : kNoOff);
+          xb[u][n] = buf_frag<T>(ra, (ok & (16 * n + c < reff)) ? (uint32_t)(((16 * n + c) * N_in + col) * (int64_t)sizeof(E))
+                                                               : kNoOff);
       } else {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) xa[u][tt] = ld_frag<T, VEC>(x, t0 + 16 * tt + c, T_, col, N_in, N_in);
@@ -841,7 +848,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
       const int itc = live ? it : 0;
       const int tn = itc / nsl, sn = itc - tn * nsl;
       slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_out, live);
-      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0));
+      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0), reff);
     } else if (it < nitems) {
       const int tn = tt0 + it / nsl, sn = it % nsl;
       slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_out);
@@ -864,7 +871,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
         const int j = gi / gpr, part = gi - j * gpr;
         const int64_t col = c0 + part * B::EPV;
         const uint32_t o = (uint32_t)(((int64_t)j * a.N_out + col) * B::ES);
-        bt[q] = buf_frag<T>(rb, ((gi < B::Rpad * gpr) & (col < a.N_out)) ? o : kNoOff);
+        bt[q] = buf_frag<T>(rb, ((gi < B::Rpad * gpr) & (col < a.N_out) & (j < reff)) ? o : kNoOff);
       }
       fetch(0, srA, zrA);
       fetch(1, srB, zrB);
@@ -1087,7 +1094,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
       const int itc = live ? it : 0;
       const int tn = itc / nsl, sn = itc - tn * nsl;
       slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_in, live);
-      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0));
+      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0), reff);
     } else if (it < nitems) {
       const int tn = tt0 + it / nsl, sn = it % nsl;
       slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_in);
@@ -1105,7 +1112,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
 #pragma unroll
     for (int q = 0; q < APER; ++q) {
       const int gi = tid + 256 * q;
-      at[q] = buf_frag<T>(ra, gi < nsl * B::SW * gpr ? (uint32_t)(gi * B::EPV * B::ES) : kNoOff);
+      at[q] = buf_frag<T>(ra, (gi < nsl * B::SW * gpr) & ((gi % gpr) * B::EPV < reff) ? (uint32_t)(gi * B::EPV * B::ES)
+                                                                                    : kNoOff);
     }
     fetch(0, srA, zrA);
     fetch(1, srB, zrB);
@@ -1977,6 +1985,7 @@ static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     a.T_ = P.T;
     a.N_in = P.N_in;
     a.N_out = P.N_out;
+    a.meta = (const int*)(jobs[i].sv + P.sv_meta);
     a.vin = (int)VEC;
     a.vout = (P.N_out % 4) == 0 && aligned16(jobs[i].y);
     b.first[i + 1] = b.first[i] + (int)(tiles * a.cg_n);
