@@ -345,6 +345,29 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v, int valid, bool
 #ifndef TTC_SLAB_PAD
 #define TTC_SLAB_PAD 16  // bytes of padding per LDS slab row
 #endif
+// four consecutive values of one row in the activation dtype, as one buffer
+// store (a dead store at kNoOff is dropped)
+template <typename T>
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, f32x4 v) {
+  if constexpr (sizeof(typename Elem<T>::type) == 2)
+    buf_store8(r, off, uint2{f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])});
+  else if constexpr (sizeof(typename Elem<T>::type) == 1)
+    buf_store32(r, off, f32x4_to_fp8x4(v[0], v[1], v[2], v[3]));
+  else
+    buf_store_f32x4(r, off, v);
+}
+
+// fp32 partial sums: four consecutive columns of one row, one 16-byte store
+// when the row is 16-byte aligned and the four are in range
+__device__ __forceinline__ void store_partial4(float* p, f32x4 v, int64_t col, int64_t ncols, bool vec) {
+  if (vec && col + 4 <= ncols) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  } else {
+    for (int e = 0; e < 4; ++e)
+      if (col + e < ncols) p[e] = v[e];
+  }
+}
+
 // Geometry shared by the two backward passes for activation type T and NR
 // rank tiles of 16.
 template <typename T, int NR>
@@ -908,16 +931,18 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
     fetch(it + kBwdDepth, sr, zr);
     lds_barrier();
     if (live) {
-      // dZ: M = token (16-row tile w), N = rank, K = column of the slab
+      // dZ^T: M = rank (tile n), N = token (16-row tile w), K = column of the
+      // slab; a lane ends with four consecutive ranks of one token
 #pragma unroll
       for (int ks = 0; ks < B::SW / B::KSTEP; ++ks) {
         const int kc = ks * B::KSTEP + g * B::EPV;
-        const frag fa = lds_frag<T>(sl + (16 * w + c) * B::SLD + kc);
+        const frag fy = lds_frag<T>(sl + (16 * w + c) * B::SLD + kc);
 #pragma unroll
         for (int n = 0; n < NR; ++n)
-          accZ[n] = Mma<T>::mma(fa, lds_frag<T>(btl + (16 * n + c) * BLD + sb * B::SW + kc), accZ[n]);
+          accZ[n] = Mma<T>::mma(lds_frag<T>(btl + (16 * n + c) * BLD + sb * B::SW + kc), fy, accZ[n]);
       }
-      // dB^T: M = rank, N = column (tiles ct*4+w of the slab), K = token
+      // dB: M = column (tiles ct*4+w of the slab), N = rank (tile n), K =
+      // token; a lane ends with four consecutive columns of one rank
 #pragma unroll
       for (int s = 0; s < NSM; ++s) {
         if (s == sb) {
@@ -930,52 +955,38 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
               fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-              const frag fa = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
+              const frag fz = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
-              for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fa, fb[ct], accB[s][ct][n]);
+              for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fb[ct], fz, accB[s][ct][n]);
             }
           }
         }
       }
     }
     // dZ (or this column group's partial) once the tile's last slab is in:
-    // tokens 64 tn + 16w+4g+v of the group, rank column 16n+c
+    // token 64 tn + 16w + c of the group, ranks 16n + 4g .. 16n + 4g + 3
     if constexpr (VEC) {
       const bool st = live & (sb == nsl - 1);
-      if (a.gc_n == 1) {
+      const int row = 64 * tn + 16 * w + c;
 #pragma unroll
-        for (int n = 0; n < NR; ++n)
-#pragma unroll
-          for (int vv = 0; vv < 4; ++vv) {
-            const uint32_t o = (uint32_t)(((64 * tn + 16 * w + 4 * g + vv) * B::Rpad + 16 * n + c) * B::ES);
-            buf_store(rdz, st ? o : kNoOff, (E)Mma<T>::from_f32(accZ[n][vv]));
-          }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NR; ++n)
-#pragma unroll
-          for (int vv = 0; vv < 4; ++vv) {
-            const uint32_t o = (uint32_t)(((64 * tn + 16 * w + 4 * g + vv) * B::Rpad + 16 * n + c) * 4);
-            buf_store(rdz, st ? o : kNoOff, accZ[n][vv]);
-          }
+      for (int n = 0; n < NR; ++n) {
+        if (a.gc_n == 1)
+          buf_store4<T>(rdz, st ? (uint32_t)((row * B::Rpad + 16 * n + 4 * g) * B::ES) : kNoOff, accZ[n]);
+        else
+          buf_store_f32x4(rdz, st ? (uint32_t)((row * B::Rpad + 16 * n + 4 * g) * 4) : kNoOff, accZ[n]);
       }
     } else if (live && sb == nsl - 1) {
-      const int64_t t0 = tb + 64 * (int64_t)tn;
-      if (a.gc_n == 1) {
+      const int64_t t = tb + 64 * (int64_t)tn + 16 * w + c;
+      if (t < a.T_) {
 #pragma unroll
         for (int n = 0; n < NR; ++n)
 #pragma unroll
           for (int vv = 0; vv < 4; ++vv) {
-            const int64_t t = t0 + 16 * w + 4 * g + vv;
-            if (t < a.T_) a.dZ[t * B::Rpad + 16 * n + c] = (E)Mma<T>::from_f32(accZ[n][vv]);
-          }
-      } else {
-#pragma unroll
-        for (int n = 0; n < NR; ++n)
-#pragma unroll
-          for (int vv = 0; vv < 4; ++vv) {
-            const int64_t t = t0 + 16 * w + 4 * g + vv;
-            if (t < a.T_) a.dZp[((int64_t)gc * a.T_ + t) * B::Rpad + 16 * n + c] = accZ[n][vv];
+            const int j = 16 * n + 4 * g + vv;
+            if (a.gc_n == 1)
+              a.dZ[t * B::Rpad + j] = (E)Mma<T>::from_f32(accZ[n][vv]);
+            else
+              a.dZp[((int64_t)gc * a.T_ + t) * B::Rpad + j] = accZ[n][vv];
           }
       }
     }
@@ -986,21 +997,20 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
     if constexpr (kBwdDepth == 3)
       if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1);
   }
-  // dB^T partial of this token group: rank 16n+4g+v, column c0+s*SW+(ct*4+w)*16+c
+  // dB^T partial of this token group: rank 16n + c, columns
+  // c0 + s*SW + (ct*4+w)*16 + 4g .. + 3
+  const bool pvec = (a.N_out & 3) == 0;
 #pragma unroll
   for (int s = 0; s < NSM; ++s) {
     if (s < nsl) {
 #pragma unroll
       for (int ct = 0; ct < B::CTW; ++ct) {
-        const int64_t o = c0 + (int64_t)s * B::SW + (ct * 4 + w) * 16 + c;
-        if (o < a.N_out) {
+        const int64_t o = c0 + (int64_t)s * B::SW + (ct * 4 + w) * 16 + 4 * g;
 #pragma unroll
-          for (int n = 0; n < NR; ++n)
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv) {
-              const int j = 16 * n + 4 * g + vv;
-              if (j < reff) a.dBp[((int64_t)gt * B::Rpad + j) * a.N_out + o] = accB[s][ct][n][vv];
-            }
+        for (int n = 0; n < NR; ++n) {
+          const int j = 16 * n + c;
+          if (j < reff && o < a.N_out)
+            store_partial4(a.dBp + ((int64_t)gt * B::Rpad + j) * a.N_out + o, accB[s][ct][n], o, a.N_out, pvec);
         }
       }
     }
@@ -1112,8 +1122,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
 #pragma unroll
     for (int q = 0; q < APER; ++q) {
       const int gi = tid + 256 * q;
-      at[q] = buf_frag<T>(ra, (gi < nsl * B::SW * gpr) & ((gi % gpr) * B::EPV < reff) ? (uint32_t)(gi * B::EPV * B::ES)
-                                                                                    : kNoOff);
+      at[q] = buf_frag<T>(ra, ((gi < nsl * B::SW * gpr) & ((gi % gpr) * B::EPV < reff)) ? (uint32_t)(gi * B::EPV * B::ES)
+                                                                                      : kNoOff);
     }
     fetch(0, srA, zrA);
     fetch(1, srB, zrB);
@@ -1139,8 +1149,9 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
     fetch(it + kBwdDepth, sr, zr);
     lds_barrier();
     if (live) {
-      // dA: M = rank, N = input column, K = token (reads the x slab first, so
-      // that the slab buffer can then stage this slab's dX)
+      // dA: M = input column, N = rank, K = token (reads the x slab first, so
+      // that the slab buffer can then stage this slab's dX); a lane ends with
+      // four consecutive columns of one rank
 #pragma unroll
       for (int s = 0; s < NSM; ++s) {
         if (s == sb) {
@@ -1153,9 +1164,9 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
               fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-              const frag fa = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
+              const frag fz = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
-              for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fa, fb[ct], accA[s][ct][n]);
+              for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fb[ct], fz, accA[s][ct][n]);
             }
           }
         }
@@ -1237,20 +1248,20 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
     if constexpr (kBwdDepth == 3)
       if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1);
   }
+  // dA partial of this token group: rank 16n + c, columns
+  // c0 + s*SW + (ct*4+w)*16 + 4g .. + 3
+  const bool pvec = (a.N_in & 3) == 0;
 #pragma unroll
   for (int s = 0; s < NSM; ++s) {
     if (s < nsl) {
 #pragma unroll
       for (int ct = 0; ct < B::CTW; ++ct) {
-        const int64_t i = c0 + (int64_t)s * B::SW + (ct * 4 + w) * 16 + c;
-        if (i < a.N_in) {
+        const int64_t i = c0 + (int64_t)s * B::SW + (ct * 4 + w) * 16 + 4 * g;
 #pragma unroll
-          for (int n = 0; n < NR; ++n)
-#pragma unroll
-            for (int vv = 0; vv < 4; ++vv) {
-              const int j = 16 * n + 4 * g + vv;
-              if (j < reff) a.dAp[((int64_t)gt * B::Rpad + j) * a.N_in + i] = accA[s][ct][n][vv];
-            }
+        for (int n = 0; n < NR; ++n) {
+          const int j = 16 * n + c;
+          if (j < reff && i < a.N_in)
+            store_partial4(a.dAp + ((int64_t)gt * B::Rpad + j) * a.N_in + i, accA[s][ct][n], i, a.N_in, pvec);
         }
       }
     }

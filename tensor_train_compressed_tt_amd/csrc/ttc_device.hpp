@@ -212,6 +212,17 @@ __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, unsigned char 
 __device__ __forceinline__ void buf_store(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store32(rsrc_t r, uint32_t off, unsigned v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 v) {
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_f32x4(rsrc_t r, uint32_t off, f32x4 v) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, 0);
+}
 // 16-byte store of a streamed output (a layer's Y or dX): written once and not
 // read again by the pass that follows, so it carries the non-temporal cache
 // policy bit and does not displace the operands the next kernels re-read
