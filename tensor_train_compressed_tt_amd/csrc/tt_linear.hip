@@ -382,6 +382,11 @@ struct Bwd {
   static constexpr int CTW = SW / 64;        // 16-column tiles per wave per slab
   static constexpr int ZLD = 64 + 16 / ES;   // row stride of a rank-major 64-token tile
   static constexpr int RLD = Rpad + 16 / ES; // row stride of a token-major rank tile
+  // 2-byte activations: the token-contracting products read the Z / dZ tile's
+  // columns with the transposing LDS read, so the tile is kept token-major
+  // only; other types keep a rank-major copy and read its rows
+  static constexpr bool ZT = ES == 2;
+  static constexpr int ZTILE = ZT ? 64 * RLD : Rpad * ZLD;  // elements of that tile
   static constexpr int SLAB = 64 * SLD;      // elements of one slab buffer
   static constexpr int PER = 4;              // 16-byte slab groups per thread
   static constexpr int ZG = Rpad * ES / 16;  // 16-byte groups per row of a rank tile
@@ -467,8 +472,10 @@ __device__ __forceinline__ void rank_store(typename Elem<T>::type* tr, typename 
     const int gi = threadIdx.x + 256 * q;
     if (gi < 64 * B::ZG) {
       const int row = gi / B::ZG, part = gi % B::ZG;
+      if (tr) {
 #pragma unroll
-      for (int e = 0; e < B::EPV; ++e) tr[(part * B::EPV + e) * B::ZLD + row] = r[q][e];
+        for (int e = 0; e < B::EPV; ++e) tr[(part * B::EPV + e) * B::ZLD + row] = r[q][e];
+      }
       if (rm) *reinterpret_cast<typename Mma<T>::frag*>(rm + row * B::RLD + part * B::EPV) = r[q];
     }
   }
@@ -829,7 +836,7 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
   extern __shared__ __align__(16) char smem[];
   E* btl = reinterpret_cast<E*>(smem);            // [Rpad][BLD]: B^T for the column range
   E* slab = btl + B::Rpad * BLD;                  // [2][64][SLD]
-  E* ztl = slab + 2 * B::SLAB;                    // [Rpad][ZLD]: Z^T of the current tile
+  E* ztl = slab + 2 * B::SLAB;  // Z of the current tile: [64][RLD] (ZT), else Z^T [Rpad][ZLD]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -922,7 +929,10 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
     const int tn = it / nsl, sb = it - tn * nsl;
     if (sb == 0) {
       lds_barrier();  // readers of the previous tile's Z^T are done
-      rank_store<T, NR>(ztl, nullptr, zr);
+      if constexpr (B::ZT)
+        rank_store<T, NR>(nullptr, ztl, zr);
+      else
+        rank_store<T, NR>(ztl, nullptr, zr);
 #pragma unroll
       for (int n = 0; n < NR; ++n) accZ[n] = zero4();
     }
@@ -955,7 +965,8 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
               fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-              const frag fz = lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
+              const frag fz = B::ZT ? lds_colT_frag<T>(ztl + (ks * B::KSTEP + g * B::EPV) * B::RLD + 16 * n, B::RLD)
+                                    : lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
               for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fb[ct], fz, accB[s][ct][n]);
             }
@@ -1068,7 +1079,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
   E* atl = reinterpret_cast<E*>(smem);            // [NSM*SW][RLD]: A^T rows of the column range
   E* slab = atl + NSM * B::SW * B::RLD;           // [2][64][SLD]
   E* dzl = slab + 2 * B::SLAB;                    // [64][RLD]: dZ, token-major
-  E* dztl = dzl + 64 * B::RLD;                    // [Rpad][ZLD]: dZ^T
+  E* dztl = dzl + 64 * B::RLD;                    // [Rpad][ZLD]: dZ^T (not with ZT)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -1142,7 +1153,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
     const int64_t t0 = tb + 64 * (int64_t)tn;
     if (sb == 0) {
       lds_barrier();
-      rank_store<T, NR>(dztl, dzl, zr);
+      rank_store<T, NR>(B::ZT ? nullptr : dztl, dzl, zr);
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
@@ -1164,7 +1175,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
               fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
-              const frag fz = lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
+              const frag fz = B::ZT ? lds_colT_frag<T>(dzl + (ks * B::KSTEP + g * B::EPV) * B::RLD + 16 * n, B::RLD)
+                                    : lds_frag<T>(dztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
               for (int ct = 0; ct < B::CTW; ++ct) accA[s][ct][n] = Mma<T>::mma(fb[ct], fz, accA[s][ct][n]);
             }
@@ -2064,7 +2076,7 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     b.n = n;
     constexpr int NSM = bwd_max_slabs(B::ES, NR);
     const size_t lds = size_t(B::Rpad) * (NSM * B::SW + 16 / B::ES) * B::ES + 2 * B::SLAB * B::ES +
-                       size_t(B::Rpad) * B::ZLD * B::ES;
+                       size_t(B::ZTILE) * B::ES;
     static bool lds_set = false;
     if (!lds_set) {
       allow_lds((const void*)k_bwd_dy<T, NR, VY>, lds);
@@ -2119,7 +2131,7 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     b.n = n;
     constexpr int NSM = dx_max_slabs(B::ES, NR);
     const size_t lds = size_t(NSM) * B::SW * B::RLD * B::ES + 2 * B::SLAB * B::ES + size_t(64) * B::RLD * B::ES +
-                       size_t(B::Rpad) * B::ZLD * B::ES;
+                       (B::ZT ? 0 : size_t(B::Rpad) * B::ZLD * B::ES);
     static bool lds_set = false;
     if (!lds_set) {
       allow_lds((const void*)k_bwd_dx<T, NR, VX>, lds);
