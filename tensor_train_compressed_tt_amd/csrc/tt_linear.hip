@@ -1427,14 +1427,13 @@ __host__ __device__ inline int gemm_tiles(const Gemm& g) { return ((g.M + 31) / 
 
 // One 32 x 32 output tile per work-group of kSweepWaves waves with fp32 MFMA
 // 16x16x4.  These GEMMs are small (K up to a few hundred), so the time of a
-// tile is the latency of its loads: wave w takes the k-steps w, w + 16, ...
-// and requests kSweepBatch of them (all its loads for K <= 512) straight into
-// registers before multiplying, so a tile costs about one memory round trip.
-// The waves' partial tiles are then added in wave order through LDS (fixed
-// order, bitwise reproducible).
+// tile is the latency of its loads: wave w takes the 32-wide chunks of K w,
+// w + 16, ... and requests a chunk's operands (all its loads for K <= 512)
+// straight into registers before multiplying, so a tile costs about one
+// memory round trip.  The waves' partial tiles are then added in wave order
+// through LDS (fixed order, bitwise reproducible).
 constexpr int kSweepWaves = 16;
 constexpr int kSweepThreads = 64 * kSweepWaves;
-constexpr int kSweepBatch = 8;
 constexpr int kSweepRedLd = 33;
 constexpr size_t kSweepLds = (size_t)kSweepWaves * 32 * kSweepRedLd * 4;
 
@@ -1448,27 +1447,60 @@ __device__ void gemm_tile32(const Gemm& g, int tile, float* red) {
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[p][q] = zero4();
-  const int nks = (g.K + 3) / 4;  // k-steps of four
-  for (int kb = w; kb < nks; kb += kSweepWaves * kSweepBatch) {
-    float fa[kSweepBatch][2], fb[kSweepBatch][2];
+  // Wave w takes the 32-wide chunks of K w, w + 16, ...; within a chunk lane
+  // group gq holds the 8 consecutive k = base + 8 gq + u (u = 0..7) and MFMA u
+  // takes value u of every lane: any assignment of k to (lane group, MFMA)
+  // gives the same sums as long as both operands use it.  An operand whose k
+  // index is contiguous in memory then comes as two 16-byte loads per lane
+  // (the lanes of one row share 64 contiguous bytes) instead of eight scalar
+  // loads that each touch 16 rows; an operand contiguous along its other
+  // index keeps the scalar loads, which are contiguous across the lanes.
+  const bool va = g.sAk == 1 && (g.sAi & 3) == 0 && (g.K & 3) == 0 && ((uintptr_t)g.A & 15) == 0;
+  const bool vb = g.sBk == 1 && (g.sBj & 3) == 0 && (g.K & 3) == 0 && ((uintptr_t)g.B & 15) == 0;
+  for (int64_t kb = (int64_t)w * 32; kb < g.K; kb += (int64_t)kSweepWaves * 32) {
+    const int64_t k0 = kb + 8 * gq;
+    float fa[8][2], fb[8][2];
 #pragma unroll
-    for (int u = 0; u < kSweepBatch; ++u) {
-      const int64_t k = (int64_t)(kb + u * kSweepWaves) * 4 + gq;
-      const bool kok = k < g.K;
+    for (int p = 0; p < 2; ++p) {
+      const int64_t i = i0 + 16 * p + c;
+      const bool iok = i < g.M;
+      if (va) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int64_t i = i0 + 16 * p + c;
-        const bool ok = kok && i < g.M;
-        const float v = g.A[ok ? i * g.sAi + k * g.sAk : 0];
-        fa[u][p] = ok ? v : 0.f;
-        const int64_t j = j0 + 16 * p + c;
-        const bool ok2 = kok && j < g.N;
-        const float v2 = g.B[ok2 ? k * g.sBk + j * g.sBj : 0];
-        fb[u][p] = ok2 ? v2 : 0.f;
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = iok && k0 + 4 * h < g.K;
+          const f32x4 v = ok ? *reinterpret_cast<const f32x4*>(g.A + i * g.sAi + k0 + 4 * h) : zero4();
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fa[4 * h + e][p] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool ok = iok && k0 + u < g.K;
+          const float v = g.A[ok ? i * g.sAi + (k0 + u) * g.sAk : 0];
+          fa[u][p] = ok ? v : 0.f;
+        }
+      }
+      const int64_t j = j0 + 16 * p + c;
+      const bool jok = j < g.N;
+      if (vb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = jok && k0 + 4 * h < g.K;
+          const f32x4 v = ok ? *reinterpret_cast<const f32x4*>(g.B + j * g.sBj + k0 + 4 * h) : zero4();
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fb[4 * h + e][p] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool ok = jok && k0 + u < g.K;
+          const float v = g.B[ok ? (k0 + u) * g.sBk + j * g.sBj : 0];
+          fb[u][p] = ok ? v : 0.f;
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSweepBatch; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
