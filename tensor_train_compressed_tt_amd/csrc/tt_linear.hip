@@ -106,6 +106,34 @@ constexpr int kMergePG = 8;      // prefixes per work-group
 constexpr int kMergeOut = 8192;  // floats of staged outputs ([pg][mode chunk][rank])
 constexpr int kMergeX = 32;      // core values per thread loaded before they are used
 
+// A batch of core values g[(x0 + u) * sx], u < kMergeX, zero past rin.  With
+// unit stride (the right half's walk: each lane reads its own contiguous run,
+// the lanes' runs far apart) the batch comes as 16- or 8-byte loads when the
+// run is aligned (rin a multiple of 4 or 2), not as kMergeX scalar loads that
+// each touch as many cache lines as there are lanes.
+__device__ __forceinline__ void merge_batch(float (&gv)[kMergeX], const float* __restrict__ g, int64_t sx, int x0,
+                                            int rin) {
+  const uintptr_t adr = (uintptr_t)(g + x0);
+  if (sx == 1 && (rin & 3) == 0 && (adr & 15) == 0) {
+#pragma unroll
+    for (int u = 0; u < kMergeX; u += 4) {
+      const f32x4 v = x0 + u < rin ? *reinterpret_cast<const f32x4*>(g + x0 + u) : zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gv[u + e] = v[e];
+    }
+  } else if (sx == 1 && (rin & 1) == 0 && (adr & 7) == 0) {
+#pragma unroll
+    for (int u = 0; u < kMergeX; u += 2) {
+      const f32x2 v = x0 + u < rin ? *reinterpret_cast<const f32x2*>(g + x0 + u) : f32x2{0.f, 0.f};
+      gv[u] = v[0];
+      gv[u + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kMergeX; ++u) gv[u] = x0 + u < rin ? g[(int64_t)(x0 + u) * sx] : 0.f;
+  }
+}
+
 // One output of a walk step for up to kMergePG prefixes at once:
 //   acc[pg] += sum_x v[pg][x] * G(x), x < rin,
 // with the rin core values G(x) = g[x * sx] requested in batches of kMergeX
@@ -114,8 +142,7 @@ __device__ __forceinline__ void merge_dot(float (&acc)[kMergePG], const float* _
                                           int rin, const float* v) {
   for (int x0 = 0; x0 < rin; x0 += kMergeX) {
     float gv[kMergeX];
-#pragma unroll
-    for (int u = 0; u < kMergeX; ++u) gv[u] = x0 + u < rin ? g[(int64_t)(x0 + u) * sx] : 0.f;
+    merge_batch(gv, g, sx, x0, rin);
 #pragma unroll
     for (int u = 0; u < kMergeX; ++u) {
       if (x0 + u < rin) {
@@ -203,8 +230,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
       float acc = 0.f;
       for (int x0 = 0; x0 < rin; x0 += kMergeX) {
         float gv[kMergeX];
-#pragma unroll
-        for (int u = 0; u < kMergeX; ++u) gv[u] = x0 + u < rin ? g[(int64_t)(x0 + u) * sx] : 0.f;
+        merge_batch(gv, g, sx, x0, rin);
 #pragma unroll
         for (int u = 0; u < kMergeX; ++u)
           if (x0 + u < rin) acc = fmaf(v[x0 + u], gv[u], acc);
