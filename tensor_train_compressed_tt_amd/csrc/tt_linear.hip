@@ -153,6 +153,10 @@ __device__ __forceinline__ void merge_dot(float (&acc)[kMergePG], const float* _
   }
 }
 
+// store 4 consecutive values of one row (defined with the streaming helpers)
+template <typename T>
+__device__ __forceinline__ void store4(typename Elem<T>::type* p, f32x4 v, int valid, bool vec);
+
 template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   typedef typename Elem<T>::type E;
@@ -303,18 +307,34 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
         if (pg < npg) ob[(pg * ci + ii) * rout + y] = acc[pg];
     }
     __syncthreads();
-    // packed operand rows [idx][Rpad] and the transpose [Rpad][Nlong]
-    for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
-      const int pg = e / (ni * Rpad);
-      const int r = e - pg * ni * Rpad;
-      const int ii = r / Rpad, j = r - ii * Rpad;
+    // packed operand rows [idx][Rpad] and the transpose [Rpad][Nlong], four
+    // consecutive entries of a row per thread and store where they are
+    // contiguous in memory
+    auto packed = [&](int pg, int ii, int j) {
       const int b = j < reff ? live[j] : -1;
       const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
-      const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? Ds[b] * val : val);
+      return b >= 0 && !is_b ? Ds[b] * val : val;
+    };
+    for (int e = 4 * tid; e < npg * ni * Rpad; e += 4 * kMergeThreads) {
+      const int pg = e / (ni * Rpad);
+      const int r = e - pg * ni * Rpad;
+      const int ii = r / Rpad, j = r - ii * Rpad;  // Rpad is a multiple of 4
       const int64_t idx = lbase[pg] + (int64_t)(i0 + ii) * lsf;
-      out[idx * Rpad + j] = ev;
+      const f32x4 v = {packed(pg, ii, j), packed(pg, ii, j + 1), packed(pg, ii, j + 2), packed(pg, ii, j + 3)};
+      store4<T>(out + idx * Rpad + j, v, 4, true);
     }
-    for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
+    // left half, last mode least significant in the listed order: four
+    // consecutive mode indices of one prefix are four consecutive columns
+    if (left && lsf == 1 && (ni & 3) == 0 && (i0 & 3) == 0 && (n & 3) == 0 && (Nlong & 3) == 0) {
+      for (int e = 4 * tid; e < npg * ni * Rpad; e += 4 * kMergeThreads) {
+        const int j = e / (npg * ni);
+        const int r = e - j * npg * ni;
+        const int pg = r / ni, ii = r % ni;
+        const int64_t idx = lbase[pg] + i0 + ii;
+        const f32x4 v = {packed(pg, ii, j), packed(pg, ii + 1, j), packed(pg, ii + 2, j), packed(pg, ii + 3, j)};
+        store4<T>(outT + (int64_t)j * Nlong + idx, v, 4, true);
+      }
+    } else for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
       const int j = e / (npg * ni);
       const int r = e - j * npg * ni;
       const int pg = left ? r / ni : r % npg;
