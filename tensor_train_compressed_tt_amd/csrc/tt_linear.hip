@@ -866,6 +866,7 @@ struct DyArgs {
   typename Elem<T>::type* dZ;         // T x Rpad
   float* dBp;                         // gt x Rpad x N_out partials (rows < r_eff)
   const int* meta;
+  int* gts;                           // [0] <- token groups of this launch (for the reduction)
   int64_t T_, N_out;
   int nsl, tpg, ntiles, gc_n, vec;
 };
@@ -1072,6 +1073,9 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
       }
     }
   }
+  // the token groups of this launch, for the reduction (one unconditional
+  // store instruction, kept by work-group 0's first lane only)
+  buf_store32(make_rsrc(a.gts, 8), (bid == 0 && tid == 0) ? 0u : kNoOff, (unsigned)((a.ntiles + a.tpg - 1) / a.tpg));
 }
 
 // dZ = sum of the column groups' partials, in group order (deterministic);
@@ -1109,6 +1113,7 @@ struct DxArgs {
   float* dAp;                         // gt x Rpad x N_in partials (rows < r_eff)
   typename Elem<T>::type* dx;         // T x N_in or null
   const int* meta;
+  int* gts;                           // [1] <- token groups of this launch (for the reduction)
   int64_t T_, N_in;
   int nsl, tpg, ntiles, vec, gcols;
 };
@@ -1324,6 +1329,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
       }
     }
   }
+  buf_store32(make_rsrc(a.gts, 8), (bid == 0 && tid == 0) ? 4u : kNoOff, (unsigned)((a.ntiles + a.tpg - 1) / a.tpg));
 }
 
 // ------------------------------------------------------------------------------
@@ -1332,7 +1338,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
 struct ReduceArgs {
   const float* dBp;
   const float* dAp;
-  int gtB, gtA;
+  const int* gts;  // token groups the data passes used (dY, dX)
+  int gtB, gtA;    // most token groups the partial buffers hold
   const int* meta;
   const float* Ds;
   float* dL;
@@ -1388,7 +1395,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceBatch rb) {
   const int64_t r0 = ((item % ns) * 64 + lane) * 4;
   const int j = a.meta[kMetaPos + b];
   const float* src = isB ? a.dBp : a.dAp;
-  const int gtn = isB ? a.gtB : a.gtA;
+  const int gtn = max(0, min(a.gts[isB ? 0 : 1], isB ? a.gtB : a.gtA));
   const int per = (gtn + 3) / 4;
   const int qb = min(gtn, w * per), qe = min(gtn, qb + per);
   f32x4 acc = zero4();
@@ -2127,6 +2134,31 @@ template <typename T, int NR, bool VY, bool VX>
 static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef Bwd<T, NR> B;
   typedef typename B::E E;
+  // With several layers in one launch, each layer gets a share of the CUs by
+  // its bytes and a grid shaped for that share (fewer, longer work-groups,
+  // so fewer partial sums).  The partial buffers hold the plan's own grid,
+  // which bounds the share's column groups (dY pass) and token groups.
+  BwdGrid gy[kMaxStream], gx[kMaxStream];
+  {
+    double ty = 0.0, tx = 0.0;
+    for (int i = 0; i < n; ++i) {
+      ty += double(jobs[i].P->T) * double(jobs[i].P->N_out);
+      tx += double(jobs[i].P->T) * double(jobs[i].P->N_in);
+    }
+    for (int i = 0; i < n; ++i) {
+      const LinearPlan& P = *jobs[i].P;
+      gy[i] = BwdGrid{P.dy_gc, P.dy_gt, P.dy_nsl, P.dy_tpg};
+      gx[i] = BwdGrid{P.dx_gc, P.dx_gt, P.dx_nsl, P.dx_tpg};
+      if (n > 1 && ty > 0.0 && tx > 0.0) {
+        BwdGrid g;
+        if (plan_bwd_grid(P, true, std::max(1.0, kPlanCUs * double(P.T) * double(P.N_out) / ty), P.dy_gc, P.dy_gt,
+                          &g))
+          gy[i] = g;
+        if (plan_bwd_grid(P, false, std::max(1.0, kPlanCUs * double(P.T) * double(P.N_in) / tx), 0, P.dx_gt, &g))
+          gx[i] = g;
+      }
+    }
+  }
   {
     StreamBatch<DyArgs<T>> b;
     memset(&b, 0, sizeof(b));
@@ -2142,14 +2174,15 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
       a.dZ = (E*)(scratch + P.sc_dZ);
       a.dBp = (float*)(scratch + P.sc_dBp);
       a.meta = (const int*)(saved + P.sv_meta);
+      a.gts = (int*)(scratch + P.sc_gts);
       a.T_ = P.T;
       a.N_out = P.N_out;
-      a.nsl = P.dy_nsl;
-      a.tpg = P.dy_tpg;
+      a.nsl = gy[i].nsl;
+      a.tpg = gy[i].tpg;
       a.ntiles = P.ntiles;
-      a.gc_n = P.dy_gc;
+      a.gc_n = gy[i].gc;
       a.vec = (P.N_out % B::EPV) == 0 && aligned16(jobs[i].dy);
-      b.first[i + 1] = b.first[i] + P.dy_gc * P.dy_gt;
+      b.first[i + 1] = b.first[i] + gy[i].gc * gy[i].gt;
     }
     b.n = n;
     constexpr int NSM = bwd_max_slabs(B::ES, NR);
@@ -2168,12 +2201,12 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     memset(&b, 0, sizeof(b));
     for (int i = 0; i < n; ++i) {
       const LinearPlan& P = *jobs[i].P;
-      if (P.dy_gc <= 1) continue;
+      if (gy[i].gc <= 1) continue;
       const int64_t n4 = P.T * B::Rpad / 4;
       DzArgs<T>& a = b.a[b.n];
       a.dZp = (const float*)(jobs[i].sc + P.sc_dZp);
       a.dZ = (E*)(jobs[i].sc + P.sc_dZ);
-      a.ngc = P.dy_gc;
+      a.ngc = gy[i].gc;
       a.n4 = n4;
       b.first[b.n + 1] = b.first[b.n] + (int)std::min<int64_t>(4096, (n4 + 255) / 256);
       ++b.n;
@@ -2197,14 +2230,15 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
       a.dAp = (float*)(scratch + P.sc_dAp);
       a.dx = (E*)jobs[i].dx;
       a.meta = (const int*)(saved + P.sv_meta);
+      a.gts = (int*)(scratch + P.sc_gts);
       a.T_ = P.T;
       a.N_in = P.N_in;
-      a.nsl = P.dx_nsl;
-      a.tpg = P.dx_tpg;
+      a.nsl = gx[i].nsl;
+      a.tpg = gx[i].tpg;
       a.ntiles = P.ntiles;
       a.vec = (P.N_in % B::EPV) == 0 && aligned16(jobs[i].x) && (jobs[i].dx == nullptr || aligned16(jobs[i].dx));
-      a.gcols = P.dx_gc;
-      b.first[i + 1] = b.first[i] + P.dx_gc * P.dx_gt;
+      a.gcols = gx[i].gc;
+      b.first[i + 1] = b.first[i] + gx[i].gc * gx[i].gt;
     }
     b.n = n;
     constexpr int NSM = dx_max_slabs(B::ES, NR);
@@ -2594,6 +2628,7 @@ static void launch_cores_batch(const LayerJob* jobs, int n, hipStream_t s) {
     ReduceArgs& r = rb.r[rb.n];
     r.dBp = (const float*)(sc + P.sc_dBp);
     r.dAp = (const float*)(sc + P.sc_dAp);
+    r.gts = (const int*)(sc + P.sc_gts);
     r.gtB = P.dy_gt;
     r.gtA = P.dx_gt;
     r.meta = (const int*)(sv + P.sv_meta);

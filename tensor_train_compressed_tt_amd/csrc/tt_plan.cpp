@@ -22,6 +22,63 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int64_t kRsrcMax = 0x7fffffff;
 static bool fits_rsrc(int64_t bytes) { return bytes <= kRsrcMax; }
 
+// Launch shape of a backward streaming pass.  A work-group owns a range of
+// columns (whole 256-byte slabs) and a range of token tiles.  Splitting the
+// columns of the dY pass costs partial sums of the T x r intermediate dZ (and
+// the dX pass re-reads dZ once per column group); splitting the tokens costs
+// partial sums of the r x N weight-side gradients.  The passes are bound by
+// each CU's share of the memory traffic, so the time of a shape is the bytes
+// of the busiest CU: the work-groups per CU (rounded up) times the bytes of
+// one work-group.  The partials that the reductions read back later run
+// beside the streaming passes and weigh half.
+#ifndef TTC_LATER_WEIGHT
+#define TTC_LATER_WEIGHT 0.5
+#endif
+bool plan_bwd_grid(const LinearPlan& P, bool dy, double ncu, int gc_max, int gt_max, BwdGrid* out) {
+  const double kLaterWeight = TTC_LATER_WEIGHT;
+  const int64_t ncols = dy ? P.N_out : P.N_in;
+  const int maxs = dy ? bwd_max_slabs(P.es, P.NR) : dx_max_slabs(P.es, P.NR);
+  const int nt = std::max(1, P.ntiles);
+  const int chunks = (int)std::max<int64_t>(1, (ncols + P.sw - 1) / P.sw);
+  const int gc_min = (chunks + maxs - 1) / maxs;
+  double best = 1e300;
+  int bsl = 0, bper = 0;
+  for (int g = gc_min; g <= chunks; ++g) {
+    const int sl = (chunks + g - 1) / g;
+    if ((chunks + sl - 1) / sl != g) continue;  // same shape as a smaller g
+    if (gc_max > 0 && g > gc_max) continue;
+    for (int per = 1; per <= nt; ++per) {
+      const int tg = (nt + per - 1) / per;
+      if ((nt + tg - 1) / tg != per) continue;
+      if (gt_max > 0 && tg > gt_max) continue;
+      // a work-group's token range of the streamed activation, of its rank
+      // tile and of the fp32 dZ partials are each one buffer resource
+      const int64_t toks64 = int64_t(per) * kTileT;
+      if (!fits_rsrc(toks64 * ncols * P.es) || !fits_rsrc(toks64 * P.Rpad * 4)) break;
+      const double cols = double(sl) * P.sw, toks = double(per) * kTileT;
+      double wg = toks * cols * P.es * (dy ? 1.0 : 2.0);  // streamed activations
+      wg += 4.0 * P.rs * cols;                           // weight-side partial
+      if (dy)
+        wg += (g > 1 ? 4.0 : 0.0) * toks * P.Rpad + toks * P.Rpad * P.es;  // dZ partial, Z tile
+      else
+        wg += toks * P.Rpad * P.es;  // dZ tile
+      const double later = 4.0 * tg * P.rs * double(ncols) + (dy && g > 1 ? 4.0 * g * double(P.T) * P.Rpad : 0.0);
+      const double cost = std::ceil(double(g) * tg / ncu) * wg + kLaterWeight * later / ncu;
+      if (cost < best * (1 - 1e-9)) {
+        best = cost;
+        bsl = sl;
+        bper = per;
+      }
+    }
+  }
+  if (bsl == 0) return false;
+  out->nsl = bsl;
+  out->gc = (chunks + bsl - 1) / bsl;
+  out->tpg = bper;
+  out->gt = (nt + bper - 1) / bper;
+  return true;
+}
+
 ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P) {
   if (!desc || !P) return TTC_ERR_NULL;
   memset(P, 0, sizeof(*P));
@@ -252,64 +309,19 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   }
 
   // ---- launch shapes of the two backward streaming passes ---------------------
-  // A work-group owns a range of columns (whole 256-byte slabs) and a range of
-  // token tiles.  Splitting the columns of the dY pass costs partial sums of
-  // the T x r intermediate dZ (and the dX pass re-reads dZ once per column
-  // group); splitting the tokens costs partial sums of the r x N weight-side
-  // gradients.  The passes are bound by each CU's share of the memory
-  // traffic, so the time of a shape is the bytes of the busiest CU: the
-  // work-groups per CU (rounded up) times the bytes of one work-group.  The
-  // partials that the reductions read back later run beside the streaming
-  // passes and weigh half.
   P->ntiles = (int)((T + kTileT - 1) / kTileT);
-  const int nt = std::max(1, P->ntiles);
   P->sw = slab_cols(P->es);
-#ifndef TTC_BWD_CUS
-#define TTC_BWD_CUS 256  // compute units of an MI355X
-#endif
-  const double ncu = TTC_BWD_CUS;
-#ifndef TTC_LATER_WEIGHT
-#define TTC_LATER_WEIGHT 0.5
-#endif
-  const double kLaterWeight = TTC_LATER_WEIGHT;
-  auto choose = [&](int64_t ncols, int maxs, bool dy, int* gc, int* gt, int* nsl, int* tpg) {
-    const int chunks = (int)std::max<int64_t>(1, (ncols + P->sw - 1) / P->sw);
-    const int gc_min = (chunks + maxs - 1) / maxs;
-    double best = 1e300;
-    int bsl = (chunks + gc_min - 1) / gc_min, bper = 1;
-    for (int g = gc_min; g <= chunks; ++g) {
-      const int sl = (chunks + g - 1) / g;
-      if ((chunks + sl - 1) / sl != g) continue;  // same shape as a smaller g
-      for (int per = 1; per <= nt; ++per) {
-        const int tg = (nt + per - 1) / per;
-        if ((nt + tg - 1) / tg != per) continue;
-        // a work-group's token range of the streamed activation, of its rank
-        // tile and of the fp32 dZ partials are each one buffer resource
-        const int64_t toks64 = int64_t(per) * kTileT;
-        if (!fits_rsrc(toks64 * ncols * P->es) || !fits_rsrc(toks64 * P->Rpad * 4)) break;
-        const double cols = double(sl) * P->sw, toks = double(per) * kTileT;
-        double wg = toks * cols * P->es * (dy ? 1.0 : 2.0);  // streamed activations
-        wg += 4.0 * P->rs * cols;                             // weight-side partial
-        if (dy)
-          wg += (g > 1 ? 4.0 : 0.0) * toks * P->Rpad + toks * P->Rpad * P->es;  // dZ partial, Z tile
-        else
-          wg += toks * P->Rpad * P->es;  // dZ tile
-        const double later = 4.0 * tg * P->rs * double(ncols) + (dy && g > 1 ? 4.0 * g * double(T) * P->Rpad : 0.0);
-        const double cost = std::ceil(double(g) * tg / ncu) * wg + kLaterWeight * later / ncu;
-        if (cost < best * (1 - 1e-9)) {
-          best = cost;
-          bsl = sl;
-          bper = per;
-        }
-      }
-    }
-    *nsl = bsl;
-    *gc = (chunks + bsl - 1) / bsl;
-    *tpg = bper;
-    *gt = (nt + bper - 1) / bper;
-  };
-  choose(nout, bwd_max_slabs(P->es, P->NR), true, &P->dy_gc, &P->dy_gt, &P->dy_nsl, &P->dy_tpg);
-  choose(nin, dx_max_slabs(P->es, P->NR), false, &P->dx_gc, &P->dx_gt, &P->dx_nsl, &P->dx_tpg);
+  BwdGrid gy, gx;
+  plan_bwd_grid(*P, true, kPlanCUs, 0, 0, &gy);
+  plan_bwd_grid(*P, false, kPlanCUs, 0, 0, &gx);
+  P->dy_gc = gy.gc;
+  P->dy_gt = gy.gt;
+  P->dy_nsl = gy.nsl;
+  P->dy_tpg = gy.tpg;
+  P->dx_gc = gx.gc;
+  P->dx_gt = gx.gt;
+  P->dx_nsl = gx.nsl;
+  P->dx_tpg = gx.tpg;
 
   // ---- saved layout -----------------------------------------------------------
   const size_t es = P->es;
@@ -347,6 +359,8 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->wl_floats = wl;
   P->wr_floats = wr;
   o = 0;
+  P->sc_gts = o;  // token groups the last data pass used: dY pass, dX pass (int32)
+  o = align256(o + 2 * 4);
   P->sc_dZp = o;
   o = align256(o + (P->dy_gc > 1 ? size_t(P->dy_gc) * T * P->Rpad * 4 : 0));
   P->sc_dZ = o;

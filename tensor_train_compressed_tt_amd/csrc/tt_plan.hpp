@@ -97,7 +97,7 @@ struct LinearPlan {
   // ---- saved layout (bytes) ----------------------------------------------------
   size_t sv_meta, sv_Ac, sv_AcT, sv_Bc, sv_BcT, sv_chain, sv_Z, sv_total;
   // ---- scratch layout (bytes) ----------------------------------------------------
-  size_t sc_dZp, sc_dZ, sc_dBp, sc_dAp, sc_dL, sc_dR, sc_w0, sc_w1, sc_total;
+  size_t sc_gts, sc_dZp, sc_dZ, sc_dBp, sc_dAp, sc_dL, sc_dR, sc_w0, sc_w1, sc_total;
   int64_t wl_floats, wr_floats;  // size of one left / right ping-pong buffer
 };
 
@@ -108,6 +108,21 @@ constexpr int kMetaReff = 256;  // r_eff
 constexpr size_t kMetaBytes = 1088;
 
 ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P);
+
+// compute units the plan's own backward grids are shaped for
+#ifndef TTC_BWD_CUS
+#define TTC_BWD_CUS 256  // compute units of an MI355X
+#endif
+constexpr double kPlanCUs = TTC_BWD_CUS;
+
+// Launch shape of one backward streaming pass (dY pass when dy, else dX) for
+// `ncu` compute units, with at most gc_max column groups and gt_max token
+// groups (0: no limit).  False when no shape qualifies.  make_linear_plan
+// takes it for all the CUs; a batched launch takes it for each layer's share.
+struct BwdGrid {
+  int gc, gt, nsl, tpg;
+};
+bool plan_bwd_grid(const LinearPlan& P, bool dy, double ncu, int gc_max, int gt_max, BwdGrid* out);
 
 
 
