@@ -157,12 +157,57 @@ __device__ __forceinline__ void merge_dot(float (&acc)[kMergePG], const float* _
 template <typename T>
 __device__ __forceinline__ void store4(typename Elem<T>::type* p, f32x4 v, int valid, bool vec);
 
-template <typename T>
+// Digit of walk step t of prefix p (step 0 most significant on the left,
+// least significant on the right).  Prefix counts are below 2^24 (the plan
+// bounds N_in and N_out), so the index arithmetic of the merge is 32-bit.
+__device__ __forceinline__ int merge_digit(const MergeLayer& a, bool left, int S, int t, int p) {
+  int div = 1;
+  if (left) {
+    for (int u = t + 1; u <= S - 2; ++u) div *= a.modes[u];
+    return (p / div) % a.modes[t];
+  }
+  for (int u = 0; u < t; ++u) div *= a.modes[a.d - 1 - u];
+  return (p / div) % a.modes[a.d - 1 - t];
+}
+
+// Eight core values g[(x0 + u) * sx], u < 8, zero at or past rin (16- or
+// 8-byte loads where the run is contiguous and aligned).
+__device__ __forceinline__ void merge_load8(float (&o)[8], const float* __restrict__ g, int64_t sx, int x0, int rin) {
+  const uintptr_t adr = (uintptr_t)(g + x0);
+  if (sx == 1 && (rin & 3) == 0 && (adr & 15) == 0) {
+#pragma unroll
+    for (int u = 0; u < 8; u += 4) {
+      const f32x4 v = x0 + u < rin ? *reinterpret_cast<const f32x4*>(g + x0 + u) : zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[u + e] = v[e];
+    }
+  } else if (sx == 1 && (rin & 1) == 0 && (adr & 7) == 0) {
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const f32x2 v = x0 + u < rin ? *reinterpret_cast<const f32x2*>(g + x0 + u) : f32x2{0.f, 0.f};
+      o[u] = v[0];
+      o[u + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = x0 + u < rin ? g[(int64_t)(x0 + u) * sx] : 0.f;
+  }
+}
+
+// FAST (every layer of the launch: at most three cores per half, ranks up to
+// kMergeX, a last core's mode times the split rank up to kMergeThreads): each
+// thread forms at most one output of every walk step, and the last step is
+// one fp32-MFMA product [prefix x rin] x [rin x (mode index, rank)], so every
+// core value and diagonal entry a thread reads is requested at the start and
+// the work-group waits for memory once instead of once or twice per step
+// (each wait is a round trip to memory beyond the L2).
+template <typename T, bool FAST>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   typedef typename Elem<T>::type E;
   __shared__ float ob[kMergeOut];                          // [pg][ii][rout] outputs of the last step
   __shared__ float vb[2][kMergePG * TTC_MAX_RANK];         // prefix vectors (D applied)
   __shared__ int live[TTC_MAX_RANK], pos[TTC_MAX_RANK];
+  __shared__ float dlive[TTC_MAX_RANK];  // D_s at the live entries, compacted
   __shared__ int s_reff;
   int q = 0;
   while (q < mb.n - 1 && (int64_t)blockIdx.x >= mb.first[q + 1]) ++q;
@@ -173,15 +218,65 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   if (!left) wg -= a.wgl;
   const int d = a.d, s = a.s;
   const int S = left ? s : d - s;  // cores in this half
-  const int64_t NP = left ? a.npl : a.npr;
-  const int64_t p0 = wg * kMergePG;
-  const int npg = (int)(NP - p0 < kMergePG ? NP - p0 : kMergePG);
+  const int NP = (int)(left ? a.npl : a.npr);
+  const int p0 = (int)wg * kMergePG;
+  const int npg = NP - p0 < kMergePG ? NP - p0 : kMergePG;
   const float* Ds = a.D[s - 1];
+  float gw0[kMergeX], gw1[kMergeX];
+  float bl[kMergeThreads / 128][8];  // FAST last step: B values of this lane's output tiles
+  float dn0 = 0.f, dn1 = 0.f;
+  // FAST: the walk steps' fields, read with the first loads
+  int wn[2] = {1, 1}, wrin[2] = {0, 0}, wrout[2] = {0, 0}, wls[2] = {0, 0};
+  float* wch[2] = {nullptr, nullptr};
+  const int lane = tid & 63, wv = tid >> 6;
+  if constexpr (FAST) {
+    // walk step t: output (pg, y) = (tid / rout, tid % rout)
+    auto walk_load = [&](int t, float (&gv)[kMergeX], float& dn) {
+      const int k = left ? t : d - 1 - t;
+      const int n = a.modes[k];
+      const int rin = left ? a.ranks[k] : a.ranks[k + 1];
+      const int rout = left ? a.ranks[k + 1] : a.ranks[k];
+      wn[t] = n;
+      wrin[t] = rin;
+      wrout[t] = rout;
+      wls[t] = a.lstride[k];
+      wch[t] = a.chain + a.chain_off[k];
+      if (tid < npg * rout) {
+        const int pg = tid / rout, y = tid - pg * rout;
+        const int dg = merge_digit(a, left, S, t, p0 + pg);
+        const float* g = left ? a.G[k] + (int64_t)dg * rout + y : a.G[k] + ((int64_t)y * n + dg) * rin;
+        merge_batch(gv, g, left ? (int64_t)n * rout : 1, 0, rin);
+        dn = (left ? a.D[k] : a.D[k - 1])[y];
+      }
+    };
+    if (S >= 2) walk_load(0, gw0, dn0);
+    if (S >= 3) walk_load(1, gw1, dn1);
+    // last step: the B operand of the product, column c = (mode index ii,
+    // rank y) = (c / rs, c % rs), row x; wave wv takes the 16-column tiles
+    // wv, wv + 8, ..., and lane group gq of a tile supplies rows 8gq .. 8gq+7
+    // (the same order of K for both operands)
+    const int kf = left ? s - 1 : s;
+    const int n = a.modes[kf];
+    const int rin = left ? a.ranks[kf] : a.ranks[kf + 1];
+    const int NC = n * a.rs;
+#pragma unroll
+    for (int u = 0; u < kMergeThreads / 128; ++u) {
+      const int c = 16 * (wv + 8 * u) + (lane & 15);
+      if (c < NC) {
+        const int ii = c / a.rs, y = c - ii * a.rs;
+        const float* g = left ? a.G[kf] + c : a.G[kf] + ((int64_t)y * n + ii) * rin;
+        merge_load8(bl[u], g, left ? (int64_t)NC : 1, 8 * (lane >> 4), rin);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bl[u][e] = 0.f;
+      }
+    }
+  }
   // live entries of the split link's diagonal, in increasing link index
   if (tid < 64) {
     const int lane = tid;
-    const bool f0 = lane < a.rs && Ds[lane] != 0.0f;
-    const bool f1 = lane + 64 < a.rs && Ds[lane + 64] != 0.0f;
+    const float d0 = lane < a.rs ? Ds[lane] : 0.f, d1 = lane + 64 < a.rs ? Ds[lane + 64] : 0.f;
+    const bool f0 = d0 != 0.0f, f1 = d1 != 0.0f;
     const uint64_t m0 = __ballot(f0), m1 = __ballot(f1);
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     const int c0 = __popcll(m0);
@@ -191,8 +286,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
     live[lane] = -1;
     live[lane + 64] = -1;
     __builtin_amdgcn_wave_barrier();
-    if (f0) live[i0] = lane;
-    if (f1) live[i1] = lane + 64;
+    if (f0) {
+      live[i0] = lane;
+      dlive[i0] = d0;
+    }
+    if (f1) {
+      live[i1] = lane + 64;
+      dlive[i1] = d1;
+    }
     if (lane == 0) s_reff = c0 + __popcll(m1);
   }
   for (int e = tid; e < kMergePG; e += kMergeThreads) vb[0][e * TTC_MAX_RANK] = 1.0f;
@@ -211,10 +312,37 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   // has step 0 most significant on the left and least significant on the
   // right.  The next step's input is this output times the link diagonal.
   int cur = 0;
-  int64_t divL = 1;  // left: product of the modes of steps t+1..S-2
+  int divL = 1;  // left: product of the modes of steps t+1..S-2
   for (int t = 1; t <= S - 2; ++t) divL *= a.modes[t];
-  int64_t mulR = 1;  // right: product of the modes of steps 0..t
-  for (int t = 0; t < S - 1; ++t) {
+  int mulR = 1;  // right: product of the modes of steps 0..t
+  if constexpr (FAST) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t < S - 1) {
+        const int rin = wrin[t], rout = wrout[t];
+        if (!left) mulR *= wn[t];
+        if (tid < npg * rout) {
+          const int pg = tid / rout, y = tid - pg * rout;
+          const float* v = vb[cur] + pg * TTC_MAX_RANK;
+          float acc = 0.f;
+#pragma unroll
+          for (int u = 0; u < kMergeX; ++u)
+            if (u < rin) acc = fmaf(v[u], t == 0 ? gw0[u] : gw1[u], acc);
+          vb[cur ^ 1][pg * TTC_MAX_RANK + y] = acc * (t == 0 ? dn0 : dn1);
+          // one writer per chain row: the prefix whose later digits are all 0
+          const int p = p0 + pg;
+          if (left) {
+            if (p % divL == 0) wch[t][(int64_t)(p / divL) * rout + y] = acc;
+          } else if (p < mulR) {
+            wch[t][(int64_t)y * mulR + p] = acc;
+          }
+        }
+        __syncthreads();
+        cur ^= 1;
+        if (left && t == 0 && S == 3) divL /= wn[1];
+      }
+    }
+  } else for (int t = 0; t < S - 1; ++t) {
     const int k = left ? t : d - 1 - t;
     const int n = a.modes[k];
     const int rin = left ? a.ranks[k] : a.ranks[k + 1];
@@ -224,10 +352,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
     // diagonal applied to this step's output before the next step
     const float* Dn = left ? a.D[k] : a.D[k - 1];
     float* ch = a.chain + a.chain_off[k];
+    // one writer per chain row: the prefix whose later digits are all 0
+    auto chain_put = [&](int p, int y, float acc) {
+      if (left) {
+        if (p % divL == 0) ch[(int64_t)(p / divL) * rout + y] = acc;
+      } else if (p < mulR) {
+        ch[(int64_t)y * mulR + p] = acc;
+      }
+    };
     for (int e = tid; e < npg * rout; e += kMergeThreads) {
       const int pg = e / rout, y = e - pg * rout;
-      const int64_t p = p0 + pg;
-      const int dg = left ? (int)((p / divL) % n) : (int)((p / (mulR / n)) % n);
+      const int p = p0 + pg;
+      const int dg = left ? (p / divL) % n : (p / (mulR / n)) % n;
       const float* g = left ? G + (int64_t)dg * rout + y : G + ((int64_t)y * n + dg) * rin;
       const int64_t sx = left ? (int64_t)n * rout : 1;
       const float* v = vb[cur] + pg * TTC_MAX_RANK;
@@ -240,12 +376,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
           if (x0 + u < rin) acc = fmaf(v[x0 + u], gv[u], acc);
       }
       vb[cur ^ 1][pg * TTC_MAX_RANK + y] = acc * Dn[y];
-      // one writer per chain row: the prefix whose later digits are all 0
-      if (left) {
-        if (p % divL == 0) ch[(p / divL) * rout + y] = acc;
-      } else if (p < mulR) {
-        ch[(int64_t)y * mulR + p] = acc;
-      }
+      chain_put(p, y, acc);
     }
     __syncthreads();
     cur ^= 1;
@@ -275,9 +406,20 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   // index itself when each half lists its modes in chain order)
   __shared__ int64_t lbase[kMergePG];
   if (tid < npg) {
-    const int64_t p = p0 + tid;
-    int64_t rem = p, b = 0;
-    if (left) {
+    int rem = p0 + tid;
+    int64_t b = 0;
+    if (FAST) {
+      // the walk's digits, least significant first
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = left ? S - 2 - u : u;
+        if (t >= 0 && t <= S - 2) {
+          const int mt = t == 0 ? wn[0] : wn[1], st = t == 0 ? wls[0] : wls[1];
+          b += (int64_t)(rem % mt) * st;
+          rem /= mt;
+        }
+      }
+    } else if (left) {
       for (int t = S - 2; t >= 0; --t) {
         b += (rem % a.modes[t]) * a.lstride[t];
         rem /= a.modes[t];
@@ -295,16 +437,45 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
   __syncthreads();
   for (int i0 = 0; i0 < n; i0 += ci) {
     const int ni = n - i0 < ci ? n - i0 : ci;
-    for (int e = tid; e < ni * rout; e += kMergeThreads) {
-      const int ii = e / rout, y = e - ii * rout;
-      const float* g = left ? G + (int64_t)(i0 + ii) * rout + y : G + ((int64_t)y * n + i0 + ii) * rin;
-      float acc[kMergePG];
+    if constexpr (FAST) {
+      // one chunk (ci = n): out[pg][c] = sum_x v[pg][x] B[x][c] as 16 x 16
+      // fp32-MFMA tiles (M = prefix, rows past npg zero; K = x in the lane
+      // groups' order of the B values loaded at the start; N = c)
+      const int NC = n * rout;
+      const int m = lane & 15, gq = lane >> 4;
+      f32x4 a0 = zero4(), a1 = zero4();
+      if (m < npg) {
 #pragma unroll
-      for (int pg = 0; pg < kMergePG; ++pg) acc[pg] = 0.f;
-      merge_dot(acc, g, left ? (int64_t)n * rout : 1, rin, v);
+        for (int e = 0; e < 4; ++e) {
+          a0[e] = 8 * gq + e < rin ? v[m * TTC_MAX_RANK + 8 * gq + e] : 0.f;
+          a1[e] = 8 * gq + 4 + e < rin ? v[m * TTC_MAX_RANK + 8 * gq + 4 + e] : 0.f;
+        }
+      }
 #pragma unroll
-      for (int pg = 0; pg < kMergePG; ++pg)
-        if (pg < npg) ob[(pg * ci + ii) * rout + y] = acc[pg];
+      for (int u = 0; u < kMergeThreads / 128; ++u) {
+        const int c = 16 * (wv + 8 * u) + m;
+        if (16 * (wv + 8 * u) < NC) {
+          f32x4 acc = zero4();
+          acc = Mma<float>::mma(a0, f32x4{bl[u][0], bl[u][1], bl[u][2], bl[u][3]}, acc);
+          acc = Mma<float>::mma(a1, f32x4{bl[u][4], bl[u][5], bl[u][6], bl[u][7]}, acc);
+          // lane (gq, m) holds rows 4gq .. 4gq+3 of column c
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * gq + e < npg && c < NC) ob[(4 * gq + e) * NC + c] = acc[e];
+        }
+      }
+    } else {
+      for (int e = tid; e < ni * rout; e += kMergeThreads) {
+        const int ii = e / rout, y = e - ii * rout;
+        const float* g = left ? G + (int64_t)(i0 + ii) * rout + y : G + ((int64_t)y * n + i0 + ii) * rin;
+        float acc[kMergePG];
+#pragma unroll
+        for (int pg = 0; pg < kMergePG; ++pg) acc[pg] = 0.f;
+        merge_dot(acc, g, left ? (int64_t)n * rout : 1, rin, v);
+#pragma unroll
+        for (int pg = 0; pg < kMergePG; ++pg)
+          if (pg < npg) ob[(pg * ci + ii) * rout + y] = acc[pg];
+      }
     }
     __syncthreads();
     // packed operand rows [idx][Rpad] and the transpose [Rpad][Nlong], four
@@ -313,12 +484,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
     auto packed = [&](int pg, int ii, int j) {
       const int b = j < reff ? live[j] : -1;
       const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
-      return b >= 0 && !is_b ? Ds[b] * val : val;
+      return b >= 0 && !is_b ? dlive[j] * val : val;
     };
+    // (left: rows of one prefix, consecutive mode indices adjacent; right:
+    // consecutive prefixes adjacent, the order in which their rows follow
+    // one another when the chain end's mode is least significant)
     for (int e = 4 * tid; e < npg * ni * Rpad; e += 4 * kMergeThreads) {
-      const int pg = e / (ni * Rpad);
-      const int r = e - pg * ni * Rpad;
-      const int ii = r / Rpad, j = r - ii * Rpad;  // Rpad is a multiple of 4
+      const int r = e / Rpad, j = e - r * Rpad;  // Rpad is a multiple of 4
+      const int pg = left ? r / ni : r % npg;
+      const int ii = left ? r - pg * ni : r / npg;
       const int64_t idx = lbase[pg] + (int64_t)(i0 + ii) * lsf;
       const f32x4 v = {packed(pg, ii, j), packed(pg, ii, j + 1), packed(pg, ii, j + 2), packed(pg, ii, j + 3)};
       store4<T>(out + idx * Rpad + j, v, 4, true);
@@ -334,6 +508,19 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
         const f32x4 v = {packed(pg, ii, j), packed(pg, ii + 1, j), packed(pg, ii + 2, j), packed(pg, ii + 3, j)};
         store4<T>(outT + (int64_t)j * Nlong + idx, v, 4, true);
       }
+    } else if (!left && S >= 2 && a.lstride[d - 1] == 1 && (a.modes[d - 1] & 3) == 0 && (npg & 3) == 0 &&
+               (Nlong & 3) == 0) {
+      // right half, its chain end's mode least significant in the listed
+      // order: four consecutive prefixes of one mode index are four
+      // consecutive columns
+      for (int e = 4 * tid; e < npg * ni * Rpad; e += 4 * kMergeThreads) {
+        const int j = e / (npg * ni);
+        const int r = e - j * npg * ni;
+        const int pg = r % npg, ii = r / npg;
+        const int64_t idx = lbase[pg] + (int64_t)(i0 + ii) * lsf;
+        const f32x4 v = {packed(pg, ii, j), packed(pg + 1, ii, j), packed(pg + 2, ii, j), packed(pg + 3, ii, j)};
+        store4<T>(outT + (int64_t)j * Nlong + idx, v, 4, true);
+      }
     } else for (int e = tid; e < npg * ni * Rpad; e += kMergeThreads) {
       const int j = e / (npg * ni);
       const int r = e - j * npg * ni;
@@ -341,7 +528,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeBatch mb) {
       const int ii = left ? r % ni : r / npg;
       const int b = j < reff ? live[j] : -1;
       const float val = b >= 0 ? ob[(pg * ci + ii) * rout + b] : 0.f;
-      const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? Ds[b] * val : val);
+      const E ev = (E)Mma<T>::from_f32(b >= 0 && !is_b ? dlive[j] * val : val);
       const int64_t idx = lbase[pg] + (int64_t)(i0 + ii) * lsf;
       outT[(int64_t)j * Nlong + idx] = ev;
     }
@@ -592,8 +779,13 @@ __device__ __forceinline__ int batch_layer(const StreamBatch<A>& b, unsigned* lo
 #ifndef TTC_FWD_WIDE_WPE
 #define TTC_FWD_WIDE_WPE 1
 #endif
-template <typename T, int NR, bool VEC, int TT, int NW>
+// PS passes of 16*TT tokens per work-group (PS > 1 with 16-byte rows only):
+// the first x batches of pass p + 1 and, with one rank tile pair, its first B
+// fragments are requested before the stores of pass p, so that they arrive
+// while pass p sums Z and writes Y.
+template <typename T, int NR, bool VEC, int TT, int NW, int PS>
 __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
+  static_assert(PS == 1 || (VEC && NW == 8), "passes need 16-byte rows and one work-group per tile");
   typedef typename Elem<T>::type E;
   unsigned bid;
   const FwdArgs<T>& fa_ = fb.a[batch_layer(fb, &bid)];
@@ -624,9 +816,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   constexpr int UO = kFwdUO(NR, NW);
   constexpr int TPS = NW * UO;                           // output tiles per step (all waves)
   extern __shared__ __align__(16) char smem[];
-  constexpr int TM = 16 * TT;                     // tokens per work-group
-  float* zred = reinterpret_cast<float*>(smem);  // [NW waves][TM tokens][Rpad]
-  E* zl = reinterpret_cast<E*>(smem);            // [TM][ZLD], reuses zred after the sum
+  constexpr int TP = 16 * TT;                     // tokens per pass
+  constexpr int TM = TP * PS;                     // tokens per work-group
+  float* zred = reinterpret_cast<float*>(smem);  // [NW waves][TP tokens][Rpad]
+  E* zl = reinterpret_cast<E*>(smem);            // [TP][ZLD], reuses zred after the sum
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -691,7 +884,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   const int nks = (int)((N_in + KSTEP - 1) / KSTEP);
   constexpr int KB = NW * UNR;
   frag fa0[UNR][TT], fb0[UNR][NR], fa1[UNR][TT], fb1[UNR][NR];
-  auto fetch_x = [&](frag (&xa)[UNR][TT], frag (&xb)[UNR][NR], int kb, bool live) {
+  auto fetch_x = [&](frag (&xa)[UNR][TT], frag (&xb)[UNR][NR], int p, int kb, bool live) {
     if (!VEC && !live) return;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
@@ -700,7 +893,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
         const bool ok = live & (col < N_in);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
-          xa[u][tt] = buf_frag<T>(rx, ok ? (uint32_t)(((16 * tt + c) * N_in + col) * (int64_t)sizeof(E)) : kNoOff);
+          xa[u][tt] = buf_frag<T>(rx, ok ? (uint32_t)(((p * TP + 16 * tt + c) * N_in + col) * (int64_t)sizeof(E)) : kNoOff);
 #pragma unroll
         for (int n = 0; n < NR; ++n)
           xb[u][n] = buf_frag<T>(ra, (ok & (16 * n + c < reff)) ? (uint32_t)(((16 * n + c) * N_in + col) * (int64_t)sizeof(E))
@@ -727,59 +920,31 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   const int nkb = (nks + KB - 1) / KB;
   const int rot1 = (int)(bid % (unsigned)nkb);
   auto kbat = [&](int j) { return ((j + rot1) % nkb) * KB; };
-  fetch_x(fa0, fb0, kbat(0), true);
-  for (int j = 0; j < nkb; j += 2) {
-    fetch_x(fa1, fb1, kbat(j + 1), j + 1 < nkb);
-    mma_x(fa0, fb0);
-    if (!VEC && j + 1 >= nkb) break;
-    fetch_x(fa0, fb0, kbat(j + 2), j + 2 < nkb);
-    mma_x(fa1, fb1);  // a dead batch is zeros and adds nothing
+  // with several passes the batch stream runs on across them: both buffers
+  // hold a batch in flight at every MFMA (the batch count of a pass rounded
+  // up to even, the extra batch dead), the last two of pass p being the first
+  // two of pass p + 1
+  const int nkb2 = PS > 1 ? (nkb + 1) & ~1 : nkb;
+  if constexpr (PS == 1) {
+    fetch_x(fa0, fb0, 0, kbat(0), true);
+  } else {
+    fetch_x(fa0, fb0, 0, kbat(0), true);
+    fetch_x(fa1, fb1, 0, kbat(1), 1 < nkb);
   }
-  // lane (g, c) holds Z rows 4g+v of token tile u, rank column 16n+c
-#pragma unroll
-  for (int u = 0; u < TT; ++u)
-#pragma unroll
-    for (int n = 0; n < NR; ++n)
-#pragma unroll
-      for (int vv = 0; vv < 4; ++vv) zred[(w * TM + 16 * u + 4 * g + vv) * Rpad + 16 * n + c] = acc[u][n][vv];
-  lds_barrier();
-  constexpr int PER = TM * Rpad / NT;
-  float zs[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + NT * i;
-    float z = zred[idx];
-#pragma unroll
-    for (int v = 1; v < NW; ++v) z += zred[v * TM * Rpad + idx];
-    zs[i] = z;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int idx = threadIdx.x + NT * i;
-    const int tt = idx / Rpad, j = idx % Rpad;
-    const E e = (E)Mma<T>::from_f32(zs[i]);
-    if constexpr (VEC)
-      buf_store(rz, cg == 0 ? (uint32_t)((tt * Rpad + j) * (int)sizeof(E)) : kNoOff, e);
-    else if (cg == 0 && t0 + tt < T_)
-      Z[(t0 + tt) * Rpad + j] = e;
-    zl[tt * ZLD + j] = e;
-  }
-  lds_barrier();
 
   // Y^T = B Z^T: M = output column, N = token, K = rank.  The waves
   // cover TPS output tiles per step; the step's Y tile goes through LDS so
-  // that it leaves as whole-row 16-byte stores.
-  if constexpr (NR > 2) {
-    fetch_b(fo0, ostep(0) + w, true);
-    fetch_b(fo1, ostep(1) + w, nsteps > 1);
-  }
+  // that it leaves as whole-row 16-byte stores.  Every out-step loop runs a
+  // multiple of three steps (the B buffers rotate by three); with several
+  // passes and one rank tile pair the fragment requests of the last two steps
+  // of pass p are the first two steps of pass p + 1.
   constexpr int CW = 16 * TPS;                  // columns per step
   constexpr int YLD = CW + 16 / (int)sizeof(E);  // staged row stride
   E* ys0 = reinterpret_cast<E*>(smem + kFwdStageOff<T, NR, TT>());
-  E* ys1 = ys0 + TM * YLD;
+  E* ys1 = ys0 + TP * YLD;
   constexpr int GPR = CW * (int)sizeof(E) / 16;  // 16-byte groups per staged row
-  auto out_step = [&](const frag (&f)[UO][KS], frag (&fn)[UO][KS], int sidx, E* ys) {
+  const int ns3 = (nsteps + 2) / 3 * 3;
+  auto out_step = [&](const frag (&f)[UO][KS], frag (&fn)[UO][KS], int p, int sidx, E* ys) {
     const bool live = sidx < nsteps;
     const int ob0 = ostep(sidx);
 #pragma unroll
@@ -803,46 +968,125 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
         }
       }
     }
-    if (VEC || sidx + 2 < nsteps) fetch_b(fn, ostep(sidx + 2) + w, sidx + 2 < nsteps);
+    if constexpr (PS > 1 && NR <= 2) {
+      const int nx = sidx + 2;
+      const bool wrap = nx >= ns3;
+      fetch_b(fn, ostep(wrap ? nx - ns3 : nx) + w, wrap ? (p + 1 < PS) & (nx - ns3 < nsteps) : nx < nsteps);
+    } else if (VEC || sidx + 2 < nsteps) {
+      fetch_b(fn, ostep(sidx + 2) + w, sidx + 2 < nsteps);
+    }
     lds_barrier();
     const int64_t c0 = (int64_t)ob0 * 16;
     const int64_t ncol = std::min<int64_t>(CW, N_out - c0);
     if constexpr (VEC) {
       constexpr int EPG = 16 / (int)sizeof(E);
-      static_assert(TM * GPR % NT == 0, "whole 16-byte groups per thread");
+      static_assert(TP * GPR % NT == 0, "whole 16-byte groups per thread");
 #pragma unroll
-      for (int k = 0; k < TM * GPR / NT; ++k) {
+      for (int k = 0; k < TP * GPR / NT; ++k) {
         const int idx = threadIdx.x + NT * k;
         const int row = idx / GPR, gr = idx - row * GPR;
         const int64_t col = c0 + gr * EPG;
-        const uint32_t o = (uint32_t)((row * N_out + col) * (int64_t)sizeof(E));
+        const uint32_t o = (uint32_t)(((p * TP + row) * N_out + col) * (int64_t)sizeof(E));
         buf_store16(ry, (live & (col < N_out)) ? o : kNoOff, *reinterpret_cast<const uint4*>(ys + row * YLD + gr * EPG));
       }
     } else if (vout && (ncol % (16 / (int)sizeof(E))) == 0) {
       const int ngr = (int)(ncol * (int64_t)sizeof(E) / 16);
-      for (int idx = threadIdx.x; idx < TM * GPR; idx += NT) {
+      for (int idx = threadIdx.x; idx < TP * GPR; idx += NT) {
         const int row = idx / GPR, gr = idx - row * GPR;
         if (gr < ngr && t0 + row < T_)
           *reinterpret_cast<uint4*>(y + (t0 + row) * N_out + c0 + gr * (16 / (int)sizeof(E))) =
               *reinterpret_cast<const uint4*>(ys + row * YLD + gr * (16 / (int)sizeof(E)));
       }
     } else {
-      for (int idx = threadIdx.x; idx < TM * CW; idx += NT) {
+      for (int idx = threadIdx.x; idx < TP * CW; idx += NT) {
         const int row = idx / CW, col = idx - row * CW;
         if (col < ncol && t0 + row < T_) y[(t0 + row) * N_out + c0 + col] = ys[row * YLD + col];
       }
     }
   };
-  // three fragment buffers: the fragments of step s + 2 are requested in
-  // step s, so waiting for them never waits for the stores of step s + 1
-  // staging buffers alternate by step parity: a buffer is rewritten two
-  // steps later, after the barrier of the step in between
-  for (int sidx = 0; sidx < nsteps; sidx += 3) {
-    out_step(fo0, fo2, sidx, (sidx & 1) ? ys1 : ys0);
-    if (!VEC && sidx + 1 >= nsteps) break;
-    out_step(fo1, fo0, sidx + 1, (sidx & 1) ? ys0 : ys1);
-    if (!VEC && sidx + 2 >= nsteps) break;
-    out_step(fo2, fo1, sidx + 2, (sidx & 1) ? ys1 : ys0);
+
+#pragma unroll
+  for (int p = 0; p < PS; ++p) {
+    if (p > 0) {
+#pragma unroll
+      for (int u = 0; u < TT; ++u)
+#pragma unroll
+        for (int n = 0; n < NR; ++n) acc[u][n] = zero4();
+    }
+    if constexpr (PS == 1) {
+      for (int j = 0; j < nkb; j += 2) {
+        fetch_x(fa1, fb1, 0, kbat(j + 1), j + 1 < nkb);
+        mma_x(fa0, fb0);
+        if (!VEC && j + 1 >= nkb) break;
+        fetch_x(fa0, fb0, 0, kbat(j + 2), j + 2 < nkb);
+        mma_x(fa1, fb1);  // a dead batch is zeros and adds nothing
+      }
+    } else {
+      for (int j = 0; j < nkb2; j += 2) {
+        mma_x(fa0, fb0);
+        {
+          const int k = j + 2;
+          const bool nx = k >= nkb2;
+          fetch_x(fa0, fb0, nx ? p + 1 : p, kbat(nx ? k - nkb2 : k), nx ? (p + 1 < PS) : k < nkb);
+        }
+        mma_x(fa1, fb1);  // a dead batch is zeros and adds nothing
+        {
+          const int k = j + 3;
+          const bool nx = k >= nkb2;
+          fetch_x(fa1, fb1, nx ? p + 1 : p, kbat(nx ? k - nkb2 : k), nx ? (p + 1 < PS) & (k - nkb2 < nkb) : k < nkb);
+        }
+      }
+      // the previous pass's out steps are done with the Z tile and the
+      // staging buffers that the reduction area overlays
+      if (p > 0) lds_barrier();
+    }
+    // lane (g, c) holds Z rows 4g+v of token tile u, rank column 16n+c
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+#pragma unroll
+      for (int n = 0; n < NR; ++n)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) zred[(w * TP + 16 * u + 4 * g + vv) * Rpad + 16 * n + c] = acc[u][n][vv];
+    lds_barrier();
+    constexpr int PER = TP * Rpad / NT;
+    float zs[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      float z = zred[idx];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) z += zred[v * TP * Rpad + idx];
+      zs[i] = z;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      const int tt = idx / Rpad, j = idx % Rpad;
+      const E e = (E)Mma<T>::from_f32(zs[i]);
+      if constexpr (VEC)
+        buf_store(rz, cg == 0 ? (uint32_t)(((p * TP + tt) * Rpad + j) * (int)sizeof(E)) : kNoOff, e);
+      else if (cg == 0 && t0 + tt < T_)
+        Z[(t0 + tt) * Rpad + j] = e;
+      zl[tt * ZLD + j] = e;
+    }
+    lds_barrier();
+
+    if constexpr (NR > 2) {
+      fetch_b(fo0, ostep(0) + w, true);
+      fetch_b(fo1, ostep(1) + w, nsteps > 1);
+    }
+    // three fragment buffers: the fragments of step s + 2 are requested in
+    // step s, so waiting for them never waits for the stores of step s + 1
+    // staging buffers alternate by step parity: a buffer is rewritten two
+    // steps later, after the barrier of the step in between
+    for (int sidx = 0; sidx < nsteps; sidx += 3) {
+      out_step(fo0, fo2, p, sidx, (sidx & 1) ? ys1 : ys0);
+      if (!VEC && sidx + 1 >= nsteps) break;
+      out_step(fo1, fo0, p, sidx + 1, (sidx & 1) ? ys0 : ys1);
+      if (!VEC && sidx + 2 >= nsteps) break;
+      out_step(fo2, fo1, p, sidx + 2, (sidx & 1) ? ys1 : ys0);
+    }
   }
 }
 
@@ -2061,11 +2305,12 @@ struct StreamJob {
 #define TTC_FWD_CUS 256  // compute units of an MI355X
 #endif
 constexpr int64_t kFwdCUs = TTC_FWD_CUS;
-template <typename T, int NR, bool VEC, int TT, int NW>
+template <typename T, int NR, bool VEC, int TT, int NW, int PS>
 static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef typename Elem<T>::type E;
+  constexpr int TM = 16 * TT * PS;  // tokens per work-group
   const size_t lds = kFwdLdsBytes<T, NR, TT, NW>();
-  auto kern = k_fwd<T, NR, VEC, TT, NW>;
+  auto kern = k_fwd<T, NR, VEC, TT, NW, PS>;
   static bool lds_set = false;
   if (!lds_set) {
     allow_lds((const void*)kern, lds);
@@ -2076,11 +2321,11 @@ static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   // fewer token tiles than CUs: split each tile's output steps over column
   // groups so that the launch still covers the chip
   int64_t tiles_all = 0;
-  for (int i = 0; i < n; ++i) tiles_all += (jobs[i].P->T + 16 * TT - 1) / (16 * TT);
+  for (int i = 0; i < n; ++i) tiles_all += (jobs[i].P->T + TM - 1) / TM;
   for (int i = 0; i < n; ++i) {
     const LinearPlan& P = *jobs[i].P;
     FwdArgs<T>& a = b.a[i];
-    const int64_t tiles = (P.T + 16 * TT - 1) / (16 * TT);
+    const int64_t tiles = (P.T + TM - 1) / TM;
     const int nst = (int)(((P.N_out + 15) / 16 + NW * kFwdUO(NR, NW) - 1) / (NW * kFwdUO(NR, NW)));
     a.cg_n = (NW == 8 || tiles_all == 0 || tiles_all >= kFwdCUs)
                  ? 1
@@ -2104,10 +2349,17 @@ static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
 }
 
 // 2-byte activations up to rank 64: 64-token work-groups of eight waves once
-// there are enough tiles to give every CU one; otherwise 32-token
-// work-groups of four waves.
+// there are enough tiles to give every CU one (with 16-byte rows in passes of
+// 64 / TTC_FWD_PASSES tokens); otherwise 32-token work-groups of four waves.
 #ifndef TTC_FWD_WIDE_TT
 #define TTC_FWD_WIDE_TT 4
+#endif
+#ifndef TTC_FWD_PASSES
+#define TTC_FWD_PASSES 1
+#endif
+static_assert(TTC_FWD_WIDE_TT % TTC_FWD_PASSES == 0, "whole 16-token tiles per pass");
+#ifndef TTC_FWD_PASS_NIN
+#define TTC_FWD_PASS_NIN 1024
 #endif
 #ifndef TTC_FWD_WIDE_TILES
 #define TTC_FWD_WIDE_TILES 256
@@ -2121,13 +2373,20 @@ template <typename T, int NR>
 static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, hipStream_t st) {
   if constexpr (sizeof(typename Elem<T>::type) <= 2 && NR <= 4) {
     if (wide) {
-      if (vec) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8>(jobs, n, st);
-      else launch_fwd_v<T, NR, false, TTC_FWD_WIDE_TT, 8>(jobs, n, st);
+      // passes for one layer per launch with a short input side (one round of
+      // work-groups, little x per pass); otherwise one pass
+      // (one-byte rows: at most two passes, so that a pass's Y chunk is a
+      // whole number of 16-byte stores per thread)
+      constexpr int PS = sizeof(typename Elem<T>::type) == 1 && TTC_FWD_PASSES > 2 ? 2 : TTC_FWD_PASSES;
+      const bool passes = PS > 1 && n == 1 && jobs[0].P->N_in <= TTC_FWD_PASS_NIN;
+      if (vec && passes) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT / PS, 8, PS>(jobs, n, st);
+      else if (vec) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1>(jobs, n, st);
+      else launch_fwd_v<T, NR, false, TTC_FWD_WIDE_TT, 8, 1>(jobs, n, st);
       return;
     }
   }
-  if (vec) launch_fwd_v<T, NR, true, 2, 4>(jobs, n, st);
-  else launch_fwd_v<T, NR, false, 2, 4>(jobs, n, st);
+  if (vec) launch_fwd_v<T, NR, true, 2, 4, 1>(jobs, n, st);
+  else launch_fwd_v<T, NR, false, 2, 4, 1>(jobs, n, st);
 }
 
 template <typename T, int NR, bool VY, bool VX>
@@ -2473,6 +2732,16 @@ static void launch_gemm_list(const Gemm* gs, int n, const char* name, hipStream_
   }
 }
 
+// the FAST merge's limits (one layer): at most three cores per half, every
+// rank at most kMergeX, each half's last core mode times the split rank at
+// most one output per thread
+static bool merge_fast_ok(const LinearPlan& P) {
+  if (P.s > 3 || P.d - P.s > 3) return false;
+  for (int k = 0; k <= P.d; ++k)
+    if (P.ranks[k] > kMergeX) return false;
+  return P.modes[P.s - 1] * P.rs <= kMergeThreads && P.modes[P.s] * P.rs <= kMergeThreads;
+}
+
 static MergeLayer merge_layer(const LayerJob& j) {
   const LinearPlan& P = j.P;
   char* sv = j.sv;
@@ -2506,26 +2775,37 @@ static MergeLayer merge_layer(const LayerJob& j) {
 }
 
 // Merge of n layers: one launch per activation dtype and kMaxMerge layers.
+#ifndef TTC_MERGE_FAST
+#define TTC_MERGE_FAST 1
+#endif
 static void launch_merge_batch(const LayerJob* jobs, int n, hipStream_t s) {
   for (int act = 0; act < 3; ++act) {
     const int want = act == 0 ? TTC_BF16 : (act == 1 ? TTC_F32 : TTC_FP8);
     MergeBatch mb;
     memset(&mb, 0, sizeof(mb));
+    bool fast = true;
     auto flush = [&]() {
       if (mb.n == 0) return;
       TraceScope ts("merge", s);
-      if (want == TTC_BF16)
-        TTC_LAUNCH(k_merge<bf16_t>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
-      else if (want == TTC_FP8)
-        TTC_LAUNCH(k_merge<fp8_t>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
-      else
-        TTC_LAUNCH(k_merge<float>, dim3((unsigned)mb.first[mb.n]), dim3(kMergeThreads), 0, s, mb);
+      const dim3 grid((unsigned)mb.first[mb.n]);
+      if (want == TTC_BF16) {
+        if (fast) TTC_LAUNCH((k_merge<bf16_t, true>), grid, dim3(kMergeThreads), 0, s, mb);
+        else TTC_LAUNCH((k_merge<bf16_t, false>), grid, dim3(kMergeThreads), 0, s, mb);
+      } else if (want == TTC_FP8) {
+        if (fast) TTC_LAUNCH((k_merge<fp8_t, true>), grid, dim3(kMergeThreads), 0, s, mb);
+        else TTC_LAUNCH((k_merge<fp8_t, false>), grid, dim3(kMergeThreads), 0, s, mb);
+      } else {
+        if (fast) TTC_LAUNCH((k_merge<float, true>), grid, dim3(kMergeThreads), 0, s, mb);
+        else TTC_LAUNCH((k_merge<float, false>), grid, dim3(kMergeThreads), 0, s, mb);
+      }
       memset(&mb, 0, sizeof(mb));
+      fast = true;
     };
     for (int i = 0; i < n; ++i) {
       if (jobs[i].P.act != want) continue;
       MergeLayer& m = mb.l[mb.n];
       m = merge_layer(jobs[i]);
+      fast = fast && TTC_MERGE_FAST && merge_fast_ok(jobs[i].P);
       mb.first[mb.n + 1] = mb.first[mb.n] + m.wgl + (m.npr + kMergePG - 1) / kMergePG;
       if (++mb.n == kMaxMerge) flush();
     }
