@@ -622,10 +622,25 @@ struct LevelArgs {
   float* Q;               // backward: R * ra per level-l node
 };
 
-// the parent's product with D applied, R x ra
+// the parent's product with D applied, R x ra (16-byte loads when ra is a
+// multiple of 4 and the product is aligned)
 __device__ __forceinline__ void stage_pd(const LevelArgs& a, int p, float* sPd) {
   const int np = a.R * a.ra;
   const float* Pp = a.l == 1 ? a.F0 + (int64_t)((uint32_t)a.ppref[p]) * np : a.Ppar + (int64_t)p * np;
+  if ((a.ra & 3) == 0 && ((uintptr_t)Pp & 15) == 0) {
+    Walk wk(4 * threadIdx.x, 4 * blockDim.x, a.ra);
+#pragma unroll 4
+    for (int e = 4 * threadIdx.x; e < np; e += 4 * blockDim.x) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(Pp + e);
+      if (a.Dpar) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] *= a.Dpar[wk.r + u];
+      }
+      *reinterpret_cast<f32x4*>(sPd + e) = v;
+      wk.next();
+    }
+    return;
+  }
   Walk wk(threadIdx.x, blockDim.x, a.ra);
 #pragma unroll 4
   for (int e = threadIdx.x; e < np; e += blockDim.x) {
@@ -636,9 +651,21 @@ __device__ __forceinline__ void stage_pd(const LevelArgs& a, int p, float* sPd) 
 
 // the core slice F[:, v, :, :] of node j, ra x blk, rows padded to blk + 1
 // floats so that lanes reading one column of different rows do not collide
+// (16-byte loads when blk is a multiple of 4 and the core is aligned)
 __device__ __forceinline__ void stage_w(const LevelArgs& a, int j, float* sW) {
   const int v = (int)((uint32_t)a.pref[j] % (uint32_t)a.m);
   const int nw = a.ra * a.blk;
+  if ((a.blk & 3) == 0 && ((uintptr_t)a.F & 15) == 0) {
+    Walk wk(4 * threadIdx.x, 4 * blockDim.x, a.blk);
+#pragma unroll 4
+    for (int e = 4 * threadIdx.x; e < nw; e += 4 * blockDim.x) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(a.F + ((int64_t)wk.q * a.m + v) * a.blk + wk.r);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sW[wk.q * (a.blk + 1) + wk.r + u] = x[u];
+      wk.next();
+    }
+    return;
+  }
   Walk wk(threadIdx.x, blockDim.x, a.blk);
 #pragma unroll 4
   for (int e = threadIdx.x; e < nw; e += blockDim.x) {
@@ -646,6 +673,9 @@ __device__ __forceinline__ void stage_w(const LevelArgs& a, int j, float* sW) {
     wk.next();
   }
 }
+
+// ranks a forward thread keeps its core column of in registers
+constexpr int kTtmRegRank = 32;
 
 // dot product of n terms x[i * sx] * y[i * sy] in order, loads issued 8 ahead
 __device__ __forceinline__ float dot_lds(const float* x, int sx, const float* y, int sy, int n) {
@@ -756,10 +786,33 @@ __global__ __launch_bounds__(kLevelThreads) void k_ttm_level_fwd(LevelArgs a) {
     stage_w(a, j, sW);
     lds_barrier();
     float* o = a.out + (int64_t)j * nout;
-    Walk wk(threadIdx.x, blockDim.x, a.blk);
-    for (int e = threadIdx.x; e < nout; e += blockDim.x) {
-      o[e] = dot_lds(sPd + wk.q * a.ra, 1, sW + wk.r, ldw, a.ra);
-      wk.next();
+    if (kLevelThreads % a.blk == 0 && (a.ra & 3) == 0 && a.ra <= kTtmRegRank) {
+      // blk divides the work-group: every output of this thread is in column
+      // r of the slice, which it keeps in registers; the rows of Pd come as
+      // 16-byte LDS reads (same terms, same order as the general form)
+      const int r = (int)threadIdx.x % a.blk;
+      float w[kTtmRegRank];
+#pragma unroll
+      for (int x = 0; x < kTtmRegRank; ++x) w[x] = x < a.ra ? sW[x * ldw + r] : 0.f;
+      for (int q = (int)threadIdx.x / a.blk; q < a.R; q += kLevelThreads / a.blk) {
+        const float* pr = sPd + q * a.ra;
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < kTtmRegRank; x += 4) {
+          if (x < a.ra) {
+            const f32x4 pv = *reinterpret_cast<const f32x4*>(pr + x);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc = fmaf(pv[u], w[x + u], acc);
+          }
+        }
+        o[q * a.blk + r] = acc;
+      }
+    } else {
+      Walk wk(threadIdx.x, blockDim.x, a.blk);
+      for (int e = threadIdx.x; e < nout; e += blockDim.x) {
+        o[e] = dot_lds(sPd + wk.q * a.ra, 1, sW + wk.r, ldw, a.ra);
+        wk.next();
+      }
     }
     lds_barrier();
   }
