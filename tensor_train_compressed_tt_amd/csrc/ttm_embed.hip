@@ -822,6 +822,9 @@ __global__ __launch_bounds__(kLevelThreads) void k_ttm_level_fwd(LevelArgs a) {
 //   C_j[a, c_k, b] = sum_c Pd[c, a] G_j[(c, c_k), b],
 // and its contribution to the parent's gradient,
 //   Q_j[c, a] = D[a] sum_{c_k, b} G_j[(c, c_k), b] F[a, v, c_k, b].
+// C4: the grouped form of C (host's choice per level, a separate instance so
+// that the other form keeps its smaller register count)
+template <bool C4>
 __global__ __launch_bounds__(kLevelBwdThreads) void k_ttm_level_bwd(LevelArgs a) {
   extern __shared__ float lds[];
   const int np = a.R * a.ra;
@@ -838,21 +841,51 @@ __global__ __launch_bounds__(kLevelBwdThreads) void k_ttm_level_bwd(LevelArgs a)
     stage_g(a.src, j, ng, sG);
     lds_barrier();
     float* C = a.C + (int64_t)j * nw;
-    {
+    if (C4 && ((uintptr_t)sG & 15) == 0) {
+      // four adjacent outputs C[a][r..r+3] per thread: one read of Pd[c][a]
+      // and one 16-byte read of G[c][r..r+3] per term (each output sums its
+      // terms in the same order as the general form)
+      const int nb4 = a.blk / 4;
+      Walk wk(threadIdx.x, blockDim.x, nb4);
+      for (int e = threadIdx.x; e < a.ra * nb4; e += blockDim.x) {
+        const int x = wk.q, r = 4 * wk.r;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        int c = 0;
+        for (; c + 8 <= a.R; c += 8) {  // eight terms' reads issued together
+          float p[8];
+          f32x4 g[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            p[k] = sPd[(c + k) * a.ra + x];
+            g[k] = *reinterpret_cast<const f32x4*>(sG + (c + k) * a.blk + r);
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] = fmaf(p[k], g[k][u], acc[u]);
+        }
+        for (; c < a.R; ++c) {
+          const float p = sPd[c * a.ra + x];
+          const f32x4 g = *reinterpret_cast<const f32x4*>(sG + c * a.blk + r);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[u] = fmaf(p, g[u], acc[u]);
+        }
+        *reinterpret_cast<f32x4*>(C + x * a.blk + r) = acc;
+        wk.next();
+      }
+    } else {
       Walk wk(threadIdx.x, blockDim.x, a.blk);
       for (int e = threadIdx.x; e < nw; e += blockDim.x) {
         C[e] = dot_lds(sPd + wk.q, a.ra, sG + wk.r, a.blk, a.R);
         wk.next();
       }
     }
-    {
-      Walk wk(threadIdx.x, blockDim.x, a.ra);
-      float* Q = a.Q + (int64_t)j * np;
-      for (int e = threadIdx.x; e < np; e += blockDim.x) {
-        const float acc = dot_lds(sG + wk.q * a.blk, 1, sW + wk.r * ldw, 1, a.blk);
-        Q[e] = acc * (a.Dpar ? a.Dpar[wk.r] : 1.f);
-        wk.next();
-      }
+    float* Q = a.Q + (int64_t)j * np;
+    Walk wk(threadIdx.x, blockDim.x, a.ra);
+    for (int e = threadIdx.x; e < np; e += blockDim.x) {
+      const float acc = dot_lds(sG + wk.q * a.blk, 1, sW + wk.r * ldw, 1, a.blk);
+      Q[e] = acc * (a.Dpar ? a.Dpar[wk.r] : 1.f);
+      wk.next();
     }
     lds_barrier();
   }
@@ -1453,7 +1486,14 @@ extern "C" ttc_status ttm_embed_bwd(const ttm_embed_desc* desc, int64_t T, const
     a.C = at<float*>(scratch, P.sc_C[l]);
     a.Q = at<float*>(scratch, P.sc_Q[l]);
     TraceScope ts("ttm_bwd_level", s);
-    TTC_LAUNCH(k_ttm_level_bwd, dim3(grid_nodes(P.cap[l])), dim3(kLevelBwdThreads), P.lds_bwd[l], s, a);
+    // the grouped C form only with a group of four outputs for every thread
+    // (fewer, longer sums measured slower: the last level of a 32x32x32
+    // vocabulary has 16 x 2 groups of 96 terms)
+    const bool c4 = (a.blk & 3) == 0 && a.ra * (a.blk / 4) >= kLevelBwdThreads;
+    if (c4)
+      TTC_LAUNCH(k_ttm_level_bwd<true>, dim3(grid_nodes(P.cap[l])), dim3(kLevelBwdThreads), P.lds_bwd[l], s, a);
+    else
+      TTC_LAUNCH(k_ttm_level_bwd<false>, dim3(grid_nodes(P.cap[l])), dim3(kLevelBwdThreads), P.lds_bwd[l], s, a);
   }
   ReduceArgs ra;
   memset(&ra, 0, sizeof(ra));
