@@ -706,10 +706,12 @@ __device__ __forceinline__ void add4(float4& acc, const float4& x) {
 // rows).  Rows are added one at a time in increasing order (one accumulator), in
 // batches of kRowBatch loads with the next batch requested before the current
 // one is added, so a long run of rows costs about one memory latency per
-// kRowBatch rows.
-// (measured: 16 costs more registers than it saves in latency)
+// kRowBatch rows.  (Measured on the 32x32x32 table's backward levels: 4 beats
+// 8, 86 -> 54 registers, five -> eight waves per SIMD, the last level 28.5 ->
+// 25.7 us, since most nodes have one or two rows and the launch runs in rounds
+// of resident work-groups; 16 costs more registers than it saves.)
 #ifndef TTC_TTM_ROW_BATCH
-#define TTC_TTM_ROW_BATCH 8
+#define TTC_TTM_ROW_BATCH 4
 #endif
 constexpr int kRowBatch = TTC_TTM_ROW_BATCH;
 __device__ __forceinline__ float4 sum_rows4(const float* p, int64_t ld, int s0, int s1, int e) {
