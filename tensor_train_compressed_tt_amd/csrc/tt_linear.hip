@@ -610,6 +610,9 @@ struct Bwd {
   static constexpr int EPV = Mma<T>::EPV;
   static constexpr int KSTEP = Mma<T>::KSTEP;
   static constexpr int Rpad = 16 * NR;
+  // rank tile narrower than the k-step (e4m3 at 32): the rank-contracting
+  // product takes one 32-wide k-step on the fragments' low halves
+  static constexpr bool HALF = Rpad % KSTEP != 0;
   static constexpr int SW = 256 / ES;        // slab columns
   static constexpr int SLD = SW + TTC_SLAB_PAD / ES;  // slab row stride (elements), padded
   static constexpr int CTW = SW / 64;        // 16-column tiles per wave per slab
@@ -812,7 +815,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   // and three batches of B fragments stay within about 128 registers
   constexpr int NT = 64 * NW;                           // threads
   constexpr int UNR = NW == 8 ? (NR <= 2 ? TTC_FWD_WIDE_UNR : 1) : (NR <= 2 ? 4 : 1);
-  constexpr int KS = Rpad / KSTEP;
+  // a rank tile narrower than the k-step (e4m3 at 32): one 32-wide k-step
+  // on the low halves of the fragments
+  constexpr bool HALF = Rpad % KSTEP != 0;
+  constexpr int KS = HALF ? 1 : Rpad / KSTEP;
   constexpr int UO = kFwdUO(NR, NW);
   constexpr int TPS = NW * UO;                           // output tiles per step (all waves)
   extern __shared__ __align__(16) char smem[];
@@ -857,7 +863,14 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int64_t row = (int64_t)(ob + NW * uo) * 16 + c;
-        if constexpr (VEC) {
+        if constexpr (HALF) {
+          if constexpr (VEC)
+            f[uo][0] = buf_frag_lo8<T>(rb, (live & (row < N_out) & (8 * g < reff))
+                                               ? (uint32_t)((row * Rpad + 8 * g) * (int64_t)sizeof(E))
+                                               : kNoOff);
+          else
+            f[uo][0] = load_frag_lo8<T>(Bc, row, N_out, 8 * g, Rpad);
+        } else if constexpr (VEC) {
           const uint32_t o = (uint32_t)((row * Rpad + ks * KSTEP + g * EPV) * (int64_t)sizeof(E));
           // ranks at or past r_eff are zero in B: not read (a load at kNoOff is zero)
           f[uo][ks] = buf_frag<T>(rb, (live & (row < N_out) & (ks * KSTEP + g * EPV < reff)) ? o : kNoOff);
@@ -953,9 +966,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         f32x4 a2 = zero4();
+        if constexpr (HALF) {
+          a2 = Mma<T>::mma_k32(f[uo][0], lds_frag_lo8<T>(zl + (16 * u + c) * ZLD + 8 * g), a2);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          a2 = Mma<T>::mma(f[uo][ks], lds_frag<T>(zl + (16 * u + c) * ZLD + ks * KSTEP + g * EPV), a2);
+          for (int ks = 0; ks < KS; ++ks)
+            a2 = Mma<T>::mma(f[uo][ks], lds_frag<T>(zl + (16 * u + c) * ZLD + ks * KSTEP + g * EPV), a2);
+        }
         E* d = ys + (16 * u + c) * YLD + lt * 16 + 4 * g;
         if constexpr (sizeof(E) == 2) {
           const uint2 pk = {f32x2_to_bf16x2(a2[0], a2[1]), f32x2_to_bf16x2(a2[2], a2[3])};
@@ -1490,13 +1507,20 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
         const int colt = (ct * 4 + w) * 16;
 #pragma unroll
         for (int u = 0; u < 4; ++u) accX[ct][u] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < B::Rpad / B::KSTEP; ++ks) {
-          const int kc = ks * B::KSTEP + g * B::EPV;
-          const frag fa = lds_frag<T>(atl + (sb * B::SW + colt + c) * B::RLD + kc);
+        if constexpr (B::HALF) {
+          const frag fa = lds_frag_lo8<T>(atl + (sb * B::SW + colt + c) * B::RLD + 8 * g);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            accX[ct][u] = Mma<T>::mma(fa, lds_frag<T>(dzl + (16 * u + c) * B::RLD + kc), accX[ct][u]);
+            accX[ct][u] = Mma<T>::mma_k32(fa, lds_frag_lo8<T>(dzl + (16 * u + c) * B::RLD + 8 * g), accX[ct][u]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < B::Rpad / B::KSTEP; ++ks) {
+            const int kc = ks * B::KSTEP + g * B::EPV;
+            const frag fa = lds_frag<T>(atl + (sb * B::SW + colt + c) * B::RLD + kc);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              accX[ct][u] = Mma<T>::mma(fa, lds_frag<T>(dzl + (16 * u + c) * B::RLD + kc), accX[ct][u]);
+          }
         }
       }
       const int64_t cs0 = c0 + (int64_t)sb * B::SW;
@@ -2538,11 +2562,14 @@ static bool nr_supported(int NR) { return NR == 2 || NR == 4 || NR == 6 || NR ==
 template <bool FWD, typename T>
 static void launch_stream_group(const StreamJob* js, int m, int NR, bool vec, bool wide, hipStream_t st) {
   if constexpr (sizeof(typename Elem<T>::type) == 1) {
-    // fp8: the plan pads the rank tile to 64 and takes ranks up to 64
-    if constexpr (FWD)
-      launch_fwd_group<T, 4>(js, m, vec, wide, st);
-    else
-      launch_bwd_group<T, 4>(js, m, vec, st);
+    // e4m3: rank tiles of 32 (one 32-wide k-step) and 64
+    if constexpr (FWD) {
+      if (NR == 2) launch_fwd_group<T, 2>(js, m, vec, wide, st);
+      else launch_fwd_group<T, 4>(js, m, vec, wide, st);
+    } else {
+      if (NR == 2) launch_bwd_group<T, 2>(js, m, vec, st);
+      else launch_bwd_group<T, 4>(js, m, vec, st);
+    }
     return;
   }
   if constexpr (FWD) {

@@ -166,9 +166,10 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
   P->s = in_first ? q : p;
   if (desc->split != -1 && desc->split != P->s) return TTC_ERR_UNSUPPORTED;
   P->rs = P->ranks[P->s];
-  // rank tile: a multiple of the MFMA k-step of the rank-side products (32
-  // k-values for fp32 and bf16, 64 for fp8)
-  const int rstep = desc->act_dtype == TTC_FP8 ? 64 : 32;
+  // rank tile: a multiple of 32 (the k-step of the rank-contracting products:
+  // one MFMA k-step for bf16, two for fp32, and for e4m3 either one 32-wide
+  // step on half fragments or whole 64-wide steps)
+  const int rstep = 32;
   P->Rpad = ((P->rs + rstep - 1) / rstep) * rstep;
   P->NR = P->Rpad / 16;
   P->NL = in_first ? nin : nout;

@@ -95,6 +95,13 @@ struct Mma<fp8_t> {
     c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], c, 0, 0, 0);
     return c;
   }
+  // one 32-wide k-step: the MFMA on the low eight bytes of each lane only
+  // (lane group g holds k = 8g .. 8g + 7); the rank-contracting products of a
+  // rank tile of 32
+  __device__ __forceinline__ static f32x4 mma_k32(frag a, frag b, f32x4 c) {
+    const i64x2 a2 = __builtin_bit_cast(i64x2, a), b2 = __builtin_bit_cast(i64x2, b);
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], c, 0, 0, 0);
+  }
   __device__ __forceinline__ static frag zero() { return frag{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}; }
   // round to nearest even (hardware conversion); values beyond the format's
   // range are not expected (activations and operands are O(1))
@@ -237,6 +244,31 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag lds_frag(const typename Elem<T>::type* p) {
   return *reinterpret_cast<const typename Mma<T>::frag*>(p);
+}
+
+// Eight e4m3 values in the low half of a fragment, the upper half zero: the
+// operand of one 32-wide k-step (Mma::mma_k32), 8-byte aligned.
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag lds_frag_lo8(const typename Elem<T>::type* p) {
+  static_assert(sizeof(typename Elem<T>::type) == 1, "one-byte activations only");
+  const u32x2v v = *reinterpret_cast<const u32x2v*>(p);
+  return __builtin_bit_cast(typename Mma<T>::frag, u32x4v{v.x, v.y, 0u, 0u});
+}
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag buf_frag_lo8(rsrc_t r, uint32_t off) {
+  static_assert(sizeof(typename Elem<T>::type) == 1, "one-byte activations only");
+  const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return __builtin_bit_cast(typename Mma<T>::frag, u32x4v{v.x, v.y, 0u, 0u});
+}
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag load_frag_lo8(const typename Elem<T>::type* __restrict__ base,
+                                                               int64_t row, int64_t nrows, int64_t col, int64_t ld) {
+  static_assert(sizeof(typename Elem<T>::type) == 1, "one-byte activations only");
+  const bool ok = row < nrows;
+  const u32x2v v = *reinterpret_cast<const u32x2v*>(base + (ok ? row * ld + col : 0));
+  return ok ? __builtin_bit_cast(typename Mma<T>::frag, u32x4v{v.x, v.y, 0u, 0u}) : Mma<T>::zero();
 }
 
 // Column fragment from LDS: EPV consecutive rows of one column.

@@ -576,14 +576,19 @@ def test_chain_perm_and_split_validation():
 
 
 def test_fp8_descriptor_limits():
+    # e4m3 rank tiles are 32 (one 32-wide k-step) or 64; wider ones take the
+    # sequential order
     d = ttc.make_linear_desc((12, 8, 8), (12, 8, 8), [1] + [30] * 5 + [1], ttc.TTC_FP8)
     f = _explain_fields(d, 16384)
-    assert f["path"] == "merged" and f["rpad"] == "64"  # the fp8 rank tile is a multiple of 64
-    big = ttc.make_linear_desc((12, 8, 8), (12, 8, 8), [1] + [100] * 5 + [1], ttc.TTC_FP8, False, ttc.TTC_PATH_MERGED)
+    assert f["path"] == "merged" and f["rpad"] == "32"
+    d64 = ttc.make_linear_desc((12, 8, 8), (12, 8, 8), [1] + [40] * 5 + [1], ttc.TTC_FP8)
+    f = _explain_fields(d64, 16384)
+    assert f["path"] == "merged" and f["rpad"] == "64"
+    big = ttc.make_linear_desc((12, 8, 8), (12, 8, 8), [1] + [65] * 5 + [1], ttc.TTC_FP8, False, ttc.TTC_PATH_MERGED)
     with pytest.raises(ttc.TTCError) as e:
         ttc.tt_linear_workspace(big, 64)
     assert e.value.code == 7
-    # activations take one byte each: Z is T x 64 bytes
+    # activations take one byte each: Z is T x 32 bytes
     s0, _ = ttc.tt_linear_workspace(d, 0)
     s1, _ = ttc.tt_linear_workspace(d, 16384)
-    assert s1 - s0 == 16384 * 64
+    assert s1 - s0 == 16384 * 32
