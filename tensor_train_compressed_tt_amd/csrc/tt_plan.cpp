@@ -293,7 +293,7 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
     double macs[4], bytes[4], usec[4];
     linear_path_costs(*P, macs, bytes);
     linear_path_times(*P, macs, bytes, usec);
-    // the fp8 merged kernels hold one rank tile of 64 (accumulator registers)
+    // the e4m3 merged kernels are built for rank tiles of 32 and 64
     const bool merged_ok = !(desc->act_dtype == TTC_FP8 && P->Rpad > 64);
     if (desc->path == TTC_PATH_SEQUENTIAL) {
       if (!P->seq_ok) return TTC_ERR_UNSUPPORTED;
