@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "tt_plan.hpp"
@@ -1132,14 +1133,31 @@ struct DyArgs {
   int nsl, tpg, ntiles, gc_n, vec;
 };
 
-template <typename T, int NR, bool VEC>
+// calls f(integral_constant<int, I>) for I = B_ .. E_-1
+template <int B_, int E_, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B_ < E_) {
+    f(std::integral_constant<int, B_>{});
+    static_for<B_ + 1, E_>(f);
+  }
+}
+
+// NSL > 0 (16-byte rows, two items in flight): the launch's work-groups own
+// at most NSL slabs and the item loop is unrolled over them, so that every
+// item's slab, and with it its dB^T accumulators, is known at compile time
+// (a slab chosen at run time among NSM accumulator sets makes the compiler
+// copy the sets at every item); a work-group with fewer slabs runs the
+// missing ones on zeros (dead loads), and with NSL odd the tile count is
+// rounded up to even the same way.  NSL = 0: the slab of an item at run time.
+template <typename T, int NR, bool VEC, int NSL>
 __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
   unsigned bid;
   const DyArgs<T>& a = bb.a[batch_layer(bb, &bid)];
   typedef Bwd<T, NR> B;
   typedef typename B::E E;
   typedef typename Mma<T>::frag frag;
-  constexpr int NSM = bwd_max_slabs(B::ES, NR);
+  static_assert(NSL == 0 || (VEC && kBwdDepth == 2), "static slabs need 16-byte rows and two items in flight");
+  constexpr int NSM = NSL > 0 ? NSL : bwd_max_slabs(B::ES, NR);
   constexpr int BLD = NSM * B::SW + 16 / B::ES;
   extern __shared__ __align__(16) char smem[];
   E* btl = reinterpret_cast<E*>(smem);            // [Rpad][BLD]: B^T for the column range
@@ -1158,6 +1176,11 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
   const int nitems = ntt * nsl;
   const int64_t tb = (int64_t)tt0 * 64;
   const int64_t nrow = std::min<int64_t>(a.T_ - tb, (int64_t)ntt * 64);
+  // items per tile and items run (static slabs: NSL per tile, an even tile
+  // count when NSL is odd; the extra items are dead)
+  const int ipt = NSL > 0 ? NSL : nsl;
+  const int ntt_run = (NSL & 1) ? (ntt + 1) & ~1 : ntt;
+  const int nit = NSL > 0 ? ntt_run * NSL : nitems;
 
   f32x4 accB[NSM][B::CTW][NR];
 #pragma unroll
@@ -1182,11 +1205,11 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
                                  : make_rsrc(a.dZp + ((int64_t)gc * a.T_ + tb) * B::Rpad, nrow * B::Rpad * 4);
   auto fetch = [&](int it, frag* sr, frag* zr) {
     if constexpr (VEC) {
-      const bool live = it < nitems;
-      const int itc = live ? it : 0;
-      const int tn = itc / nsl, sn = itc - tn * nsl;
-      slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_out, live);
-      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0), reff);
+      const int itc = it < nit ? it : 0;
+      const int tn = itc / ipt, sn = itc - tn * ipt;
+      const bool tile = (it < nit) & (tn < ntt);
+      slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_out, tile & (sn < nsl));
+      rank_fetch_b<T, NR>(zr, rzt, tn * 64, tile & (sn == 0), reff);
     } else if (it < nitems) {
       const int tn = tt0 + it / nsl, sn = it % nsl;
       slab_fetch<T, NR, VEC>(sr, a.dy, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_out);
@@ -1198,7 +1221,8 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
   // per thread, requested before the first two items so that the latencies
   // overlap
   {
-    const int gpr = nsl * B::SW / B::EPV;
+    // (static slabs: all NSL slabs' columns, zero past the work-group's own)
+    const int gpr = (NSL > 0 ? NSL : nsl) * B::SW / B::EPV;
     if constexpr (VEC) {
       constexpr int BPER = (B::Rpad * NSM * B::SW / B::EPV + 255) / 256;
       const rsrc_t rb = make_rsrc(a.BcT, (int64_t)B::Rpad * a.N_out * B::ES);
@@ -1232,9 +1256,13 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
     }
   }
 
-  auto body = [&](int it, frag* sr, frag* zr, int buf) {
-    const bool live = it < nitems;
-    const int tn = it / nsl, sb = it - tn * nsl;
+  // sc: integral_constant of the item's slab (static slabs) or of -1
+  auto body = [&](int it, frag* sr, frag* zr, int buf, auto sc) __attribute__((always_inline)) {
+    constexpr int SS = decltype(sc)::value;
+    const int tn = it / ipt;
+    const int sb = SS >= 0 ? SS : it - tn * ipt;
+    // static slabs: dead items hold zeros, so every item runs its products
+    const bool live = SS >= 0 || it < nitems;
     if (sb == 0) {
       lds_barrier();  // readers of the previous tile's Z^T are done
       if constexpr (B::ZT)
@@ -1261,31 +1289,35 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
       }
       // dB: M = column (tiles ct*4+w of the slab), N = rank (tile n), K =
       // token; a lane ends with four consecutive columns of one rank
+      auto dB_products = [&](f32x4 (&acc)[B::CTW][NR]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < NSM; ++s) {
-        if (s == sb) {
+        for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
+          const int kt = ks * B::KSTEP + g * B::EPV;
+          frag fb[B::CTW];
 #pragma unroll
-          for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
-            const int kt = ks * B::KSTEP + g * B::EPV;
-            frag fb[B::CTW];
+          for (int ct = 0; ct < B::CTW; ++ct)
+            fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
 #pragma unroll
-            for (int ct = 0; ct < B::CTW; ++ct)
-              fb[ct] = lds_colT_frag<T>(sl + kt * B::SLD + (ct * 4 + w) * 16, B::SLD);
+          for (int n = 0; n < NR; ++n) {
+            const frag fz = B::ZT ? lds_colT_frag<T>(ztl + (ks * B::KSTEP + g * B::EPV) * B::RLD + 16 * n, B::RLD)
+                                  : lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
 #pragma unroll
-            for (int n = 0; n < NR; ++n) {
-              const frag fz = B::ZT ? lds_colT_frag<T>(ztl + (ks * B::KSTEP + g * B::EPV) * B::RLD + 16 * n, B::RLD)
-                                    : lds_frag<T>(ztl + (16 * n + c) * B::ZLD + kt);
-#pragma unroll
-              for (int ct = 0; ct < B::CTW; ++ct) accB[s][ct][n] = Mma<T>::mma(fb[ct], fz, accB[s][ct][n]);
-            }
+            for (int ct = 0; ct < B::CTW; ++ct) acc[ct][n] = Mma<T>::mma(fb[ct], fz, acc[ct][n]);
           }
         }
+      };
+      if constexpr (SS >= 0) {
+        dB_products(accB[SS]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < NSM; ++s)
+          if (s == sb) dB_products(accB[s]);
       }
     }
     // dZ (or this column group's partial) once the tile's last slab is in:
     // token 64 tn + 16w + c of the group, ranks 16n + 4g .. 16n + 4g + 3
     if constexpr (VEC) {
-      const bool st = live & (sb == nsl - 1);
+      const bool st = live & (sb == ipt - 1) & (tn < ntt);
       const int row = 64 * tn + 16 * w + c;
 #pragma unroll
       for (int n = 0; n < NR; ++n) {
@@ -1310,11 +1342,27 @@ __global__ __launch_bounds__(256) void k_bwd_dy(StreamBatch<DyArgs<T>> bb) {
       }
     }
   };
-  for (int it = 0; it < nitems; it += kBwdDepth) {
-    body(it, srA, zrA, it & 1);
-    if (VEC || it + 1 < nitems) body(it + 1, srB, zrB, (it + 1) & 1);
-    if constexpr (kBwdDepth == 3)
-      if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1);
+  if constexpr (NSL > 0) {
+    // item it = tn * NSL + s; its register set and slab buffer follow the
+    // parity of it, which each unrolled item knows
+    for (int tn = 0; tn < ntt_run; tn += (NSL & 1) ? 2 : 1) {
+      static_for<0, ((NSL & 1) ? 2 : 1) * NSL>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int s = u % NSL;
+        const int it = tn * NSL + u;
+        if constexpr ((u & 1) == 0)
+          body(it, srA, zrA, 0, std::integral_constant<int, s>{});
+        else
+          body(it, srB, zrB, 1, std::integral_constant<int, s>{});
+      });
+    }
+  } else {
+    for (int it = 0; it < nitems; it += kBwdDepth) {
+      body(it, srA, zrA, it & 1, std::integral_constant<int, -1>{});
+      if (VEC || it + 1 < nitems) body(it + 1, srB, zrB, (it + 1) & 1, std::integral_constant<int, -1>{});
+      if constexpr (kBwdDepth == 3)
+        if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1, std::integral_constant<int, -1>{});
+    }
   }
   // dB^T partial of this token group: rank 16n + c, columns
   // c0 + s*SW + (ct*4+w)*16 + 4g .. + 3
@@ -2413,6 +2461,35 @@ static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, 
   else launch_fwd_v<T, NR, false, 2, 4, 1>(jobs, n, st);
 }
 
+// one dY-pass launch; NSL = 0: the slab of an item at run time, else the
+// static-slab form for work-groups of at most NSL slabs
+#ifndef TTC_DY_STATIC_SLABS
+#define TTC_DY_STATIC_SLABS 1
+#endif
+template <typename T, int NR, bool VY, int NSL>
+static void launch_dy(const StreamBatch<DyArgs<T>>& b, hipStream_t st) {
+  typedef Bwd<T, NR> B;
+  constexpr int NSM = NSL > 0 ? NSL : bwd_max_slabs(B::ES, NR);
+  const size_t lds = size_t(B::Rpad) * (NSM * B::SW + 16 / B::ES) * B::ES + 2 * B::SLAB * B::ES +
+                     size_t(B::ZTILE) * B::ES;
+  static bool lds_set = false;
+  if (!lds_set) {
+    allow_lds((const void*)k_bwd_dy<T, NR, VY, NSL>, lds);
+    lds_set = true;
+  }
+  TTC_LAUNCH((k_bwd_dy<T, NR, VY, NSL>), dim3((unsigned)b.first[b.n]), dim3(256), lds, st, b);
+}
+// the static-slab form for K = nsl (K <= MAX), else the run-time form
+template <typename T, int NR, bool VY, int K, int MAX>
+static void launch_dy_n(int nsl, const StreamBatch<DyArgs<T>>& b, hipStream_t st) {
+  if constexpr (K > MAX)
+    launch_dy<T, NR, VY, 0>(b, st);
+  else if (nsl == K)
+    launch_dy<T, NR, VY, K>(b, st);
+  else
+    launch_dy_n<T, NR, VY, K + 1, MAX>(nsl, b, st);
+}
+
 template <typename T, int NR, bool VY, bool VX>
 static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef Bwd<T, NR> B;
@@ -2469,15 +2546,13 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     }
     b.n = n;
     constexpr int NSM = bwd_max_slabs(B::ES, NR);
-    const size_t lds = size_t(B::Rpad) * (NSM * B::SW + 16 / B::ES) * B::ES + 2 * B::SLAB * B::ES +
-                       size_t(B::ZTILE) * B::ES;
-    static bool lds_set = false;
-    if (!lds_set) {
-      allow_lds((const void*)k_bwd_dy<T, NR, VY>, lds);
-      lds_set = true;
-    }
+    int nsl_max = 1;
+    for (int i = 0; i < n; ++i) nsl_max = std::max(nsl_max, gy[i].nsl);
     TraceScope ts("bwd_dy", st);
-    TTC_LAUNCH((k_bwd_dy<T, NR, VY>), dim3((unsigned)b.first[n]), dim3(256), lds, st, b);
+    if constexpr (VY && kBwdDepth == 2 && TTC_DY_STATIC_SLABS)
+      launch_dy_n<T, NR, VY, 1, (NSM < 4 ? NSM : 4)>(nsl_max, b, st);
+    else
+      launch_dy<T, NR, VY, 0>(b, st);
   }
   {
     StreamBatch<DzArgs<T>> b;
