@@ -1519,13 +1519,16 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
     slab_store<T, NR>(sl, sr);
     fetch(it + kBwdDepth, sr, zr);
     lds_barrier();
-    if (live) {
+    // (16-byte rows: a dead item's x slab holds zeros, so its products add
+    // nothing and run unconditionally; a condition around the accumulators'
+    // updates makes the compiler copy them)
+    if (VEC || live) {
       // dA: M = input column, N = rank, K = token (reads the x slab first, so
       // that the slab buffer can then stage this slab's dX); a lane ends with
       // four consecutive columns of one rank
 #pragma unroll
       for (int s = 0; s < NSM; ++s) {
-        if (s == sb) {
+        if (NSM == 1 || s == sb) {
 #pragma unroll
           for (int ks = 0; ks < 64 / B::KSTEP; ++ks) {
             const int kt = ks * B::KSTEP + g * B::EPV;
