@@ -114,6 +114,11 @@ ttc_status make_linear_plan(const tt_linear_desc* desc, int64_t T, LinearPlan* P
 #define TTC_BWD_CUS 256  // compute units of an MI355X
 #endif
 constexpr double kPlanCUs = TTC_BWD_CUS;
+// the backward passes of a batched launch (long work-groups) shaped for two
+// work-groups per CU
+#ifndef TTC_BWD_TWO_PER_CU
+#define TTC_BWD_TWO_PER_CU 1
+#endif
 
 // Launch shape of one backward streaming pass (dY pass when dy, else dX) for
 // `ncu` compute units, with at most gc_max column groups and gt_max token
