@@ -2515,11 +2515,14 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
       if (n > 1 && ty > 0.0 && tx > 0.0) {
         BwdGrid g;
         // (a batch's work-groups run long: shaped for two per CU; measured on
-        // the batched Q, K, V passes: dY 27.6 -> 25.0 us, dX 35.4 -> 32.9 us)
-        const double cus = (TTC_BWD_TWO_PER_CU ? 2.0 : 1.0) * kPlanCUs;
-        if (plan_bwd_grid(P, true, std::max(1.0, cus * double(P.T) * double(P.N_out) / ty), P.dy_gc, P.dy_gt, &g))
+        // the batched Q, K, V passes: dY 27.6 -> 25.0 us, bf16 dX 35.4 -> 32.9
+        // us; the e4m3 dX work-groups move half the bytes and lose, 24.2 ->
+        // 31.8 us, so they stay at one per CU)
+        const double cy = (TTC_BWD_TWO_PER_CU ? 2.0 : 1.0) * kPlanCUs;
+        const double cx = (TTC_BWD_TWO_PER_CU && B::ES >= 2 ? 2.0 : 1.0) * kPlanCUs;
+        if (plan_bwd_grid(P, true, std::max(1.0, cy * double(P.T) * double(P.N_out) / ty), P.dy_gc, P.dy_gt, &g))
           gy[i] = g;
-        if (plan_bwd_grid(P, false, std::max(1.0, cus * double(P.T) * double(P.N_in) / tx), 0, P.dx_gt, &g))
+        if (plan_bwd_grid(P, false, std::max(1.0, cx * double(P.T) * double(P.N_in) / tx), 0, P.dx_gt, &g))
           gx[i] = g;
       }
     }
