@@ -738,7 +738,10 @@ constexpr size_t kFwdLdsBytes() {
   constexpr size_t stg = (size_t)kFwdStageOff<T, NR, TT>() + 2 * (size_t)(16 * TT) *
                                                                 (256 + 16 / sizeof(typename Elem<T>::type)) *
                                                                 sizeof(typename Elem<T>::type);
-  return red > stg ? red : stg;
+  // the x batch of the row-pattern loads: 16*TT rows of NW*UNR k-steps
+  // (64 bytes each) plus a 16-byte pad
+  constexpr size_t xs = (size_t)(16 * TT) * (NW * (NR <= 2 ? 2 : 1) * 64 + 16);
+  return red > stg ? (red > xs ? red : xs) : (stg > xs ? stg : xs);
 }
 
 // NW waves per work-group split the input columns of the first product and
@@ -783,11 +786,33 @@ __device__ __forceinline__ int batch_layer(const StreamBatch<A>& b, unsigned* lo
 #ifndef TTC_FWD_WIDE_WPE
 #define TTC_FWD_WIDE_WPE 1
 #endif
+// XR: x read in whole 256-byte row pieces (a wave instruction covers four
+// rows) and staged through LDS, instead of straight into the fragment layout
+// (a wave instruction there covers 16 rows x 64 bytes).  With the operand A
+// read alongside from the L2, the row pieces stream at 5.2 against 3.7 TB/s
+// (100 MB over 256 work-groups, a 3072-wide x); the launch takes this path
+// for 2-byte rows of at least TTC_FWD_XROWS_BYTES (long k loops; with one
+// or two batches per work-group the staging barriers cost more than the
+// pattern gains).
+#ifndef TTC_FWD_XROWS
+#define TTC_FWD_XROWS 1
+#endif
+#ifndef TTC_FWD_XROWS_BYTES
+#define TTC_FWD_XROWS_BYTES 4096
+#endif
+// the row pieces with the streaming (non-temporal) hint.  Measured on the
+// six-layer step: the dX pass of FFN2, which follows its forward, then reads
+// its x from HBM (36.5 -> 43 us), but the passes after it gain more (O and
+// FFN1 dX 15.5 -> 13.8 us, Q, K, V dX 33 -> 30.5 us): 0.3527 against
+// 0.3452 ms per step without and with the hint
+#ifndef TTC_FWD_XR_NT
+#define TTC_FWD_XR_NT 1
+#endif
 // PS passes of 16*TT tokens per work-group (PS > 1 with 16-byte rows only):
 // the first x batches of pass p + 1 and, with one rank tile pair, its first B
 // fragments are requested before the stores of pass p, so that they arrive
 // while pass p sums Z and writes Y.
-template <typename T, int NR, bool VEC, int TT, int NW, int PS>
+template <typename T, int NR, bool VEC, int TT, int NW, int PS, bool XRW>
 __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   static_assert(PS == 1 || (VEC && NW == 8), "passes need 16-byte rows and one work-group per tile");
   typedef typename Elem<T>::type E;
@@ -939,7 +964,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   // up to even, the extra batch dead), the last two of pass p being the first
   // two of pass p + 1
   const int nkb2 = PS > 1 ? (nkb + 1) & ~1 : nkb;
-  if constexpr (PS == 1) {
+  // the row-pattern path (16-byte rows, one pass, 64-token work-groups)
+  constexpr bool XR = XRW && VEC && PS == 1 && NW == 8 && TT == 4;
+  constexpr int RB = KB * 64;            // bytes of a row in one batch
+  constexpr int CPR = RB / 256;          // 256-byte pieces per row and batch
+  constexpr int XI = XR ? 16 * TT * CPR / 4 / NW : 1;  // wave instructions per batch
+  constexpr int XLD = RB + 16;           // staged row stride (bytes)
+  static_assert(!XR || (KSTEP * (int)sizeof(E) == 64 && RB % 256 == 0 && XI == UNR * TT), "row-pattern geometry");
+  static_assert(!XR || (size_t)(16 * TT) * XLD <= kFwdLdsBytes<T, NR, TT, NW>(), "the staged batch fits");
+  char* xs = smem;
+  if constexpr (XR) {
+  } else if constexpr (PS == 1) {
     fetch_x(fa0, fb0, 0, kbat(0), true);
   } else {
     fetch_x(fa0, fb0, 0, kbat(0), true);
@@ -1031,7 +1066,88 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
 #pragma unroll
         for (int n = 0; n < NR; ++n) acc[u][n] = zero4();
     }
-    if constexpr (PS == 1) {
+    if constexpr (XR) {
+      // batch kb: rows 0..TM-1, bytes [kb*64, kb*64 + RB) of each row; wave
+      // instruction i = q*NW + w covers rows 4(i / CPR) .. +3, piece i % CPR
+      frag xr0[XI], xr1[XI];
+      auto fetch_xr = [&](frag (&r)[XI], int kb, bool live) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < XI; ++q) {
+          const int i = q * NW + w;
+          const int row = 4 * (i / CPR) + (lane >> 4);
+          const int64_t cb = (int64_t)kb * 64 + (i % CPR) * 256 + (lane & 15) * 16;
+          const uint32_t o = (live & (cb < N_in * (int64_t)sizeof(E))) ? (uint32_t)(row * N_in * (int64_t)sizeof(E) + cb)
+                                                                       : kNoOff;
+          r[q] = TTC_FWD_XR_NT ? buf_frag_last<T>(rx, o) : buf_frag<T>(rx, o);
+        }
+      };
+      // every wave is done with the previous batch before the store, and the
+      // batch is in LDS before any wave reads it
+      auto stage = [&](const frag (&r)[XI]) __attribute__((always_inline)) {
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < XI; ++q) {
+          const int i = q * NW + w;
+          const int row = 4 * (i / CPR) + (lane >> 4);
+          *reinterpret_cast<frag*>(xs + row * XLD + (i % CPR) * 256 + (lane & 15) * 16) = r[q];
+        }
+        lds_barrier();
+      };
+      // Z += x A^T over the wave's k-steps NW*u + w of the staged batch
+      auto mma_s = [&](const frag (&xb)[UNR][NR]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            const frag xa = *reinterpret_cast<const frag*>(xs + (16 * tt + c) * XLD + (NW * u + w) * 64 + g * 16);
+#pragma unroll
+            for (int n = 0; n < NR; ++n) acc[tt][n] = Mma<T>::mma(xa, xb[u][n], acc[tt][n]);
+          }
+      };
+      // the A fragments of a batch: rows 16n + c, the wave's k-steps
+      auto fetch_a = [&](frag (&xb)[UNR][NR], int kb, bool live) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int64_t col = (int64_t)(kb + NW * u + w) * KSTEP + g * EPV;
+          const bool ok = live & (col < N_in);
+#pragma unroll
+          for (int n = 0; n < NR; ++n)
+            xb[u][n] = buf_frag<T>(ra, (ok & (16 * n + c < reff)) ? (uint32_t)(((16 * n + c) * N_in + col) * (int64_t)sizeof(E))
+                                                                 : kNoOff);
+        }
+      };
+      // two batches in flight; the scheduling barriers keep every request
+      // ahead of the products that do not need it
+      // (in the order the loop's waits assume: x then A of batch 0, then of
+      // batch 1; each wait then leaves the younger batch in flight)
+      fetch_xr(xr0, kbat(0), true);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_a(fb0, kbat(0), true);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_xr(xr1, kbat(1), 1 < nkb);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_a(fb1, kbat(1), 1 < nkb);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < nkb; j += 2) {
+        stage(xr0);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_xr(xr0, kbat(j + 2), j + 2 < nkb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_s(fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_a(fb0, kbat(j + 2), j + 2 < nkb);
+        __builtin_amdgcn_sched_barrier(0);
+        stage(xr1);  // a dead batch is zeros and adds nothing
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_xr(xr1, kbat(j + 3), j + 3 < nkb);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_s(fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_a(fb1, kbat(j + 3), j + 3 < nkb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lds_barrier();  // the reduction area overlays the staged batch
+    } else if constexpr (PS == 1) {
       for (int j = 0; j < nkb; j += 2) {
         fetch_x(fa1, fb1, 0, kbat(j + 1), j + 1 < nkb);
         mma_x(fa0, fb0);
@@ -2380,12 +2496,12 @@ struct StreamJob {
 #define TTC_FWD_CUS 256  // compute units of an MI355X
 #endif
 constexpr int64_t kFwdCUs = TTC_FWD_CUS;
-template <typename T, int NR, bool VEC, int TT, int NW, int PS>
+template <typename T, int NR, bool VEC, int TT, int NW, int PS, bool XRW = false>
 static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef typename Elem<T>::type E;
   constexpr int TM = 16 * TT * PS;  // tokens per work-group
   const size_t lds = kFwdLdsBytes<T, NR, TT, NW>();
-  auto kern = k_fwd<T, NR, VEC, TT, NW, PS>;
+  auto kern = k_fwd<T, NR, VEC, TT, NW, PS, XRW>;
   static bool lds_set = false;
   if (!lds_set) {
     allow_lds((const void*)kern, lds);
@@ -2454,7 +2570,10 @@ static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, 
       // whole number of 16-byte stores per thread)
       constexpr int PS = sizeof(typename Elem<T>::type) == 1 && TTC_FWD_PASSES > 2 ? 2 : TTC_FWD_PASSES;
       const bool passes = PS > 1 && n == 1 && jobs[0].P->N_in <= TTC_FWD_PASS_NIN;
+      bool xr = TTC_FWD_XROWS && sizeof(typename Elem<T>::type) == 2 && TTC_FWD_WIDE_TT == 4;
+      for (int i = 0; i < n; ++i) xr = xr && jobs[i].P->N_in * 2 >= TTC_FWD_XROWS_BYTES;
       if (vec && passes) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT / PS, 8, PS>(jobs, n, st);
+      else if (vec && xr) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1, true>(jobs, n, st);
       else if (vec) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1>(jobs, n, st);
       else launch_fwd_v<T, NR, false, TTC_FWD_WIDE_TT, 8, 1>(jobs, n, st);
       return;
