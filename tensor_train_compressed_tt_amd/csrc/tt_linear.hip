@@ -793,7 +793,7 @@ __device__ __forceinline__ int batch_layer(const StreamBatch<A>& b, unsigned* lo
 // (100 MB over 256 work-groups, a 3072-wide x); the launch takes this path
 // for 2-byte rows of at least TTC_FWD_XROWS_BYTES (long k loops; with one
 // or two batches per work-group the staging barriers cost more than the
-// pattern gains).
+// pattern gains: 768-wide inputs, Q+K+V 37.5 -> 42 us, FFN1 28.8 -> 30 us).
 #ifndef TTC_FWD_XROWS
 #define TTC_FWD_XROWS 1
 #endif
@@ -808,11 +808,14 @@ __device__ __forceinline__ int batch_layer(const StreamBatch<A>& b, unsigned* lo
 #ifndef TTC_FWD_XR_NT
 #define TTC_FWD_XR_NT 1
 #endif
+#ifndef TTC_FWD_XR_NT_BYTES
+#define TTC_FWD_XR_NT_BYTES 4096
+#endif
 // PS passes of 16*TT tokens per work-group (PS > 1 with 16-byte rows only):
 // the first x batches of pass p + 1 and, with one rank tile pair, its first B
 // fragments are requested before the stores of pass p, so that they arrive
 // while pass p sums Z and writes Y.
-template <typename T, int NR, bool VEC, int TT, int NW, int PS, bool XRW>
+template <typename T, int NR, bool VEC, int TT, int NW, int PS, int XRW>
 __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_fwd(StreamBatch<FwdArgs<T>> fb) {
   static_assert(PS == 1 || (VEC && NW == 8), "passes need 16-byte rows and one work-group per tile");
   typedef typename Elem<T>::type E;
@@ -965,7 +968,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   // two of pass p + 1
   const int nkb2 = PS > 1 ? (nkb + 1) & ~1 : nkb;
   // the row-pattern path (16-byte rows, one pass, 64-token work-groups)
-  constexpr bool XR = XRW && VEC && PS == 1 && NW == 8 && TT == 4;
+  constexpr bool XR = XRW > 0 && VEC && PS == 1 && NW == 8 && TT == 4;
   constexpr int RB = KB * 64;            // bytes of a row in one batch
   constexpr int CPR = RB / 256;          // 256-byte pieces per row and batch
   constexpr int XI = XR ? 16 * TT * CPR / 4 / NW : 1;  // wave instructions per batch
@@ -1078,7 +1081,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
           const int64_t cb = (int64_t)kb * 64 + (i % CPR) * 256 + (lane & 15) * 16;
           const uint32_t o = (live & (cb < N_in * (int64_t)sizeof(E))) ? (uint32_t)(row * N_in * (int64_t)sizeof(E) + cb)
                                                                        : kNoOff;
-          r[q] = TTC_FWD_XR_NT ? buf_frag_last<T>(rx, o) : buf_frag<T>(rx, o);
+          r[q] = XRW == 2 ? buf_frag_last<T>(rx, o) : buf_frag<T>(rx, o);
         }
       };
       // every wave is done with the previous batch before the store, and the
@@ -2496,7 +2499,7 @@ struct StreamJob {
 #define TTC_FWD_CUS 256  // compute units of an MI355X
 #endif
 constexpr int64_t kFwdCUs = TTC_FWD_CUS;
-template <typename T, int NR, bool VEC, int TT, int NW, int PS, bool XRW = false>
+template <typename T, int NR, bool VEC, int TT, int NW, int PS, int XRW = 0>
 static void launch_fwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef typename Elem<T>::type E;
   constexpr int TM = 16 * TT * PS;  // tokens per work-group
@@ -2570,10 +2573,14 @@ static void launch_fwd_group(const StreamJob* jobs, int n, bool vec, bool wide, 
       // whole number of 16-byte stores per thread)
       constexpr int PS = sizeof(typename Elem<T>::type) == 1 && TTC_FWD_PASSES > 2 ? 2 : TTC_FWD_PASSES;
       const bool passes = PS > 1 && n == 1 && jobs[0].P->N_in <= TTC_FWD_PASS_NIN;
-      bool xr = TTC_FWD_XROWS && sizeof(typename Elem<T>::type) == 2 && TTC_FWD_WIDE_TT == 4;
-      for (int i = 0; i < n; ++i) xr = xr && jobs[i].P->N_in * 2 >= TTC_FWD_XROWS_BYTES;
+      bool xr = TTC_FWD_XROWS && sizeof(typename Elem<T>::type) == 2 && TTC_FWD_WIDE_TT == 4, nt = TTC_FWD_XR_NT;
+      for (int i = 0; i < n; ++i) {
+        xr = xr && jobs[i].P->N_in * 2 >= TTC_FWD_XROWS_BYTES;
+        nt = nt && jobs[i].P->N_in * 2 >= TTC_FWD_XR_NT_BYTES;
+      }
       if (vec && passes) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT / PS, 8, PS>(jobs, n, st);
-      else if (vec && xr) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1, true>(jobs, n, st);
+      else if (vec && xr && nt) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1, 2>(jobs, n, st);
+      else if (vec && xr) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1, 1>(jobs, n, st);
       else if (vec) launch_fwd_v<T, NR, true, TTC_FWD_WIDE_TT, 8, 1>(jobs, n, st);
       else launch_fwd_v<T, NR, false, TTC_FWD_WIDE_TT, 8, 1>(jobs, n, st);
       return;
