@@ -1538,6 +1538,7 @@ struct DxArgs {
   const typename Elem<T>::type* x;
   const typename Elem<T>::type* AcT;  // N_in x Rpad
   const typename Elem<T>::type* dZ;   // T x Rpad
+  const float* dZp;                   // ZS x T x Rpad partials of the dY pass (ZS > 0)
   float* dAp;                         // gt x Rpad x N_in partials (rows < r_eff)
   typename Elem<T>::type* dx;         // T x N_in or null
   const int* meta;
@@ -1546,7 +1547,11 @@ struct DxArgs {
   int nsl, tpg, ntiles, vec, gcols;
 };
 
-template <typename T, int NR, bool VEC>
+// ZS > 0 (16-byte rows): dZ is the sum of the dY pass's ZS fp32 column-group
+// partials, formed here per tile in group order and rounded to the activation
+// type as the separate sum would (the same values bit for bit), so that
+// layers whose dY pass splits its columns in two need no launch for the sum.
+template <typename T, int NR, bool VEC, int ZS>
 __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
   unsigned bid;
   const DxArgs<T>& a = bb.a[batch_layer(bb, &bid)];
@@ -1584,17 +1589,42 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
   // one register set per item in flight; with 16-byte rows every fetch,
   // store and item is unconditional (buffer accesses, dead ones at kNoOff), so
   // the wait before an item leaves the later fetches in flight
+  static_assert(ZS == 0 || VEC, "dZ partials with 16-byte rows only");
+  constexpr int ZQ = B::EPV / 4;  // float4 per fragment of a partial
   frag srA[B::PER], srB[B::PER], srC[B::PER], zrA[B::ZPER], zrB[B::ZPER], zrC[B::ZPER];
+  f32x4 zpA[ZS > 0 ? ZS * B::ZPER * ZQ : 1], zpB[ZS > 0 ? ZS * B::ZPER * ZQ : 1], zpC[ZS > 0 ? ZS * B::ZPER * ZQ : 1];
   const rsrc_t rsl = make_rsrc(a.x + tb * a.N_in, nrow * a.N_in * B::ES);
   const rsrc_t rzt = make_rsrc(a.dZ + tb * B::Rpad, nrow * B::Rpad * B::ES);
   const rsrc_t rdx = make_rsrc(a.dx ? a.dx + tb * a.N_in : a.x, a.dx ? nrow * a.N_in * B::ES : 0);
-  auto fetch = [&](int it, frag* sr, frag* zr) {
+  rsrc_t rzp[ZS > 0 ? ZS : 1];
+#pragma unroll
+  for (int g2 = 0; g2 < ZS; ++g2) rzp[g2] = make_rsrc(a.dZp + ((int64_t)g2 * a.T_ + tb) * B::Rpad, nrow * B::Rpad * 4);
+  auto fetch = [&](int it, frag* sr, frag* zr, f32x4* zp) {
     if constexpr (VEC) {
       const bool live = it < nitems;
       const int itc = live ? it : 0;
       const int tn = itc / nsl, sn = itc - tn * nsl;
       slab_fetch_b<T, NR>(sr, rsl, tn * 64, c0 + (int64_t)sn * B::SW, a.N_in, live);
-      rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0), reff);
+      if constexpr (ZS == 0) {
+        rank_fetch_b<T, NR>(zr, rzt, tn * 64, live & (sn == 0), reff);
+      } else {
+        // the rank tile's pieces of every partial (the layout of rank_fetch_b,
+        // in fp32); rank columns at or past r_eff are zero and not read
+#pragma unroll
+        for (int q = 0; q < B::ZPER; ++q) {
+          const int gi = tid + 256 * q;
+          const int row = gi / B::ZG, part = gi % B::ZG;
+          const bool ok = live & (sn == 0) & (gi < 64 * B::ZG) & (part * B::EPV < reff);
+#pragma unroll
+          for (int g2 = 0; g2 < ZS; ++g2)
+#pragma unroll
+            for (int e4 = 0; e4 < ZQ; ++e4)
+              zp[(g2 * B::ZPER + q) * ZQ + e4] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             rzp[g2], ok ? (int)(((tn * 64 + row) * B::Rpad + part * B::EPV + 4 * e4) * 4) : (int)kNoOff, 0,
+                             0));
+        }
+      }
     } else if (it < nitems) {
       const int tn = tt0 + it / nsl, sn = it % nsl;
       slab_fetch<T, NR, VEC>(sr, a.x, (int64_t)tn * 64, a.T_, c0 + (int64_t)sn * B::SW, a.N_in);
@@ -1615,9 +1645,9 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
       at[q] = buf_frag<T>(ra, ((gi < nsl * B::SW * gpr) & ((gi % gpr) * B::EPV < reff)) ? (uint32_t)(gi * B::EPV * B::ES)
                                                                                       : kNoOff);
     }
-    fetch(0, srA, zrA);
-    fetch(1, srB, zrB);
-    if constexpr (kBwdDepth == 3) fetch(2, srC, zrC);
+    fetch(0, srA, zrA, zpA);
+    fetch(1, srB, zrB, zpB);
+    if constexpr (kBwdDepth == 3) fetch(2, srC, zrC, zpC);
 #pragma unroll
     for (int q = 0; q < APER; ++q) {
       const int gi = tid + 256 * q;
@@ -1626,17 +1656,33 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
     }
   }
 
-  auto body = [&](int it, frag* sr, frag* zr, int buf) {
+  auto body = [&](int it, frag* sr, frag* zr, f32x4* zp, int buf) {
     const bool live = it < nitems;
     const int tn = it / nsl, sb = it - tn * nsl;
     const int64_t t0 = tb + 64 * (int64_t)tn;
     if (sb == 0) {
       lds_barrier();
-      rank_store<T, NR>(B::ZT ? nullptr : dztl, dzl, zr);
+      if constexpr (ZS == 0) {
+        rank_store<T, NR>(B::ZT ? nullptr : dztl, dzl, zr);
+      } else {
+        // dZ = the partials summed in group order, rounded once
+        frag zc[B::ZPER];
+#pragma unroll
+        for (int q = 0; q < B::ZPER; ++q)
+#pragma unroll
+          for (int e4 = 0; e4 < ZQ; ++e4) {
+            f32x4 v = zero4();
+#pragma unroll
+            for (int g2 = 0; g2 < ZS; ++g2) v += zp[(g2 * B::ZPER + q) * ZQ + e4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zc[q][4 * e4 + e] = Mma<T>::from_f32(v[e]);
+          }
+        rank_store<T, NR>(B::ZT ? nullptr : dztl, dzl, zc);
+      }
     }
     E* sl = slab + buf * B::SLAB;
     slab_store<T, NR>(sl, sr);
-    fetch(it + kBwdDepth, sr, zr);
+    fetch(it + kBwdDepth, sr, zr, zp);
     lds_barrier();
     // (16-byte rows: a dead item's x slab holds zeros, so its products add
     // nothing and run unconditionally; a condition around the accumulators'
@@ -1744,10 +1790,10 @@ __global__ __launch_bounds__(256) void k_bwd_dx(StreamBatch<DxArgs<T>> bb) {
     }
   };
   for (int it = 0; it < nitems; it += kBwdDepth) {
-    body(it, srA, zrA, it & 1);
-    if (VEC || it + 1 < nitems) body(it + 1, srB, zrB, (it + 1) & 1);
+    body(it, srA, zrA, zpA, it & 1);
+    if (VEC || it + 1 < nitems) body(it + 1, srB, zrB, zpB, (it + 1) & 1);
     if constexpr (kBwdDepth == 3)
-      if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, (it + 2) & 1);
+      if (VEC || it + 2 < nitems) body(it + 2, srC, zrC, zpC, (it + 2) & 1);
   }
   // dA partial of this token group: rank 16n + c, columns
   // c0 + s*SW + (ct*4+w)*16 + 4g .. + 3
@@ -2619,6 +2665,9 @@ static void launch_dy_n(int nsl, const StreamBatch<DyArgs<T>>& b, hipStream_t st
     launch_dy_n<T, NR, VY, K + 1, MAX>(nsl, b, st);
 }
 
+#ifndef TTC_DX_DZ_FOLD
+#define TTC_DX_DZ_FOLD 1
+#endif
 template <typename T, int NR, bool VY, bool VX>
 static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
   typedef Bwd<T, NR> B;
@@ -2688,7 +2737,15 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
     else
       launch_dy<T, NR, VY, 0>(b, st);
   }
-  {
+  // every layer's dY pass in two column groups and every dX work-group over
+  // two slabs or more: the dX pass sums the two partials itself (one launch
+  // fewer).  Measured: FFN2 (dX work-groups of two slabs) 4.2 us of sum
+  // saved, its dX pass unchanged; the one-slab dX passes of O and Q, K, V
+  // read four times the dZ bytes per slab and lose more than the sum costs
+  // (O 14.5 -> 17.3 us, Q+K+V 29.7 -> 36.1 us)
+  bool fold = VX && TTC_DX_DZ_FOLD;
+  for (int i = 0; i < n; ++i) fold = fold && gy[i].gc == 2 && gx[i].nsl >= 2;
+  if (!fold) {
     StreamBatch<DzArgs<T>> b;
     memset(&b, 0, sizeof(b));
     for (int i = 0; i < n; ++i) {
@@ -2719,6 +2776,7 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
       a.x = (const E*)jobs[i].x;
       a.AcT = (const E*)(saved + P.sv_AcT);
       a.dZ = (const E*)(scratch + P.sc_dZ);
+      a.dZp = (const float*)(scratch + P.sc_dZp);
       a.dAp = (float*)(scratch + P.sc_dAp);
       a.dx = (E*)jobs[i].dx;
       a.meta = (const int*)(saved + P.sv_meta);
@@ -2738,11 +2796,18 @@ static void launch_bwd_v(const StreamJob* jobs, int n, hipStream_t st) {
                        (B::ZT ? 0 : size_t(B::Rpad) * B::ZLD * B::ES);
     static bool lds_set = false;
     if (!lds_set) {
-      allow_lds((const void*)k_bwd_dx<T, NR, VX>, lds);
+      allow_lds((const void*)k_bwd_dx<T, NR, VX, 0>, lds);
+      if constexpr (VX) allow_lds((const void*)k_bwd_dx<T, NR, VX, 2>, lds);
       lds_set = true;
     }
     TraceScope ts("bwd_dx", st);
-    TTC_LAUNCH((k_bwd_dx<T, NR, VX>), dim3((unsigned)b.first[n]), dim3(256), lds, st, b);
+    if constexpr (VX) {
+      if (fold) {
+        TTC_LAUNCH((k_bwd_dx<T, NR, VX, 2>), dim3((unsigned)b.first[n]), dim3(256), lds, st, b);
+        return;
+      }
+    }
+    TTC_LAUNCH((k_bwd_dx<T, NR, VX, 0>), dim3((unsigned)b.first[n]), dim3(256), lds, st, b);
   }
 }
 
