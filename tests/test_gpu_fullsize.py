@@ -110,14 +110,16 @@ def test_config2_full_step_bench_launches(rank):
     _check_step(layers, host, "bf16", _rows(T, seed=rank))
 
 
-def test_config2_ragged_tokens_bench_launches():
-    """Config 2 at T = 16424, rank 30: 257 token tiles, the last of 40
-    tokens, so the benchmark's launch forms (the eight-wave forward, the
+@pytest.mark.parametrize("T", [16360, 16424])
+def test_config2_ragged_tokens_bench_launches(T):
+    """Config 2 at rank 30 with a ragged last tile of 40 tokens: 256 tiles
+    (T = 16360; FFN2's dY pass in two column groups and its two-slab dX pass
+    summing the dZ partials itself) and 257 tiles (T = 16424; three column
+    groups), so the benchmark's launch forms (the eight-wave forward, the
     row-piece x loads of the 3072-wide input, the batched Q, K, V passes, the
     backward grids the planner picks for this T) all meet a ragged tail."""
-    T = synth.CONFIG_TOKENS[2] + 40
     layers, host, _ = _run_bench_step(2, 30, T)
-    _check_step(layers, host, "bf16", _rows(T, seed=40))
+    _check_step(layers, host, "bf16", _rows(T, seed=T))
 
 
 def test_config2_full_step_graph_replay_bitwise():
