@@ -22,13 +22,16 @@
 //                kept for the sweep, the compacted A, B (and transposes) in
 //                the activation dtype
 //   k_fwd        per 64-token tile: Z = x A^T with the K range split over the
-//                waves (unrolled, many loads in flight), Z summed in LDS and
-//                kept, then Y^T = B Z^T with the B fragments prefetched
+//                waves (two load batches in flight; x of wide inputs read as
+//                whole 256-byte row pieces and staged through LDS), Z summed
+//                in LDS and kept, then Y^T = B Z^T with the B fragments
+//                prefetched
 //   k_bwd_dy     per (column group, token group): 64 x 256-byte slabs of dY
 //                stream through LDS with register prefetch; dZ (or its
 //                partials over the column groups), dB^T partials over the
 //                token group
 //   k_dz_sum     sums the dZ partials of the column groups in group order
+//                (skipped where the dX pass sums two partials itself)
 //   k_bwd_dx     per (column group, token group): slabs of x stream through
 //                LDS; dX^T = A^T dZ^T written per slab, dA partials
 //   k_reduce     sums the partials into the gradients of the two half products
