@@ -979,10 +979,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 8 ? TTC_FWD_WIDE_WPE : 1)) void k_f
   static_assert(!XR || (KSTEP * (int)sizeof(E) == 64 && RB % 256 == 0 && XI == UNR * TT), "row-pattern geometry");
   static_assert(!XR || (size_t)(16 * TT) * XLD <= kFwdLdsBytes<T, NR, TT, NW>(), "the staged batch fits");
   char* xs = smem;
-  if constexpr (XR) {
-  } else if constexpr (PS == 1) {
+  // (the row-piece path requests its first batches in its own loop)
+  if constexpr (!XR && PS == 1) {
     fetch_x(fa0, fb0, 0, kbat(0), true);
-  } else {
+  } else if constexpr (!XR) {
     fetch_x(fa0, fb0, 0, kbat(0), true);
     fetch_x(fa1, fb1, 0, kbat(1), 1 < nkb);
   }
