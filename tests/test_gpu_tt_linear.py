@@ -164,6 +164,16 @@ def test_config2_full_tokens_ffn1_r30():
     print(_check(spec, layer, "bf16"))
 
 
+@pytest.mark.parametrize("T", [16384, 16392])
+def test_wide_input_row_pieces(T):
+    """A 2304 -> 768 layer at the full token count and with a ragged last
+    tile: its 4.5 KB rows take the forward's row-piece x loads (staged through
+    LDS, the last batch of each row half past its end); bf16, rank 30."""
+    spec = synth.LayerSpec("w2304", (12, 8, 8), (12, 12, 16), 30)
+    layer = synth.make_tt_layer(2, 700, spec, T, 0.40, "bf16")
+    print(_check(spec, layer, "bf16"))
+
+
 def test_skip_dx():
     spec = synth.config_layers(0)[0]
     layer = synth.make_tt_layer(0, 1, spec, 100, 0.25, "f32")
