@@ -2488,8 +2488,18 @@ __global__ __launch_bounds__(256) void k_seq_reduce(SeqRedArgs a) {
        e += (int64_t)gridDim.x * blockDim.x) {
     int t = 0;
     while (t < a.d - 1 && e >= a.off[t + 1]) ++t;
+    // eight tokens' partials requested together, added in token order
+    const float* p = a.part + e;
     float acc = 0.f;
-    for (int64_t k = 0; k < a.T; ++k) acc += a.part[k * a.part_floats + e];
+    int64_t k = 0;
+    for (; k + 8 <= a.T; k += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p[(k + u) * a.part_floats];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; k < a.T; ++k) acc += p[k * a.part_floats];
     a.dG[t][e - a.off[t]] = acc;
   }
 }
